@@ -1,0 +1,209 @@
+"""Pins of the oracle's ProbePlan / score / estimate / update (oracle/zo.py).
+
+What the pages fix and the tests check:
+* the factorized side state equals explicit dense mutation of the weights
+  (arXiv abstract of "Inference-Native Zeroth-Order Optimization"), both in
+  the oracle (fp64, 1e-12) and against the transformers library run on the
+  mutated weights;
+* eps = 0 makes S+ and S- bitwise equal; swapping the signs negates c
+  exactly ("Zeroth-Order Fine-Tuning Was an Inference Workload All Along",
+  equations for L+, L- and c);
+* c converges to the analytic directional derivative at rate O(eps^2) on a
+  single linear + log-softmax layer with a closed-form gradient;
+* the 1/r flag divides c by r (section "The System Reorganization");
+* the lazy update U_{t+1} = U_t - eta c_t G_t and the m-step identity
+  Delta W = (U_t - eta sum c_s G_s) V^T (same section);
+* packing: a batch scores the same as its sequences scored one by one.
+"""
+import numpy as np
+import pytest
+import torch
+
+from oracle import model as om
+from oracle import params, zo
+from oracle.zo import Bank, Plan, Weights
+from synth import configs, inputs
+from synth.configs import ModelCfg
+
+from .test_oracle_model import OPT_SMALL, QWEN_SMALL, _opt_hf, _qwen_hf, T
+
+
+def _small_wl(cfg, targets, n_prompts=3, rank=2, dirs=(0,), n_fg=0, mode="last_label"):
+    return configs.Workload("t", cfg, n_prompts, 6, 11, "uniform", mode, rank, 1e-2, dirs, targets,
+                            nu=4, n_fg=n_fg, model_seed=2, data_seed=5)
+
+
+def _bank_after_updates(cfg, wl, steps=2, c=(0.7, -1.3)):
+    bank = Bank(4, wl.rank, wl.targets)
+    for t in range(steps):
+        plan = zo.plan_from_workload(wl, t)
+        zo.update(cfg, plan, bank, np.array([c[t % 2]] * wl.n_dirs), 0.5)
+    return bank
+
+
+@pytest.mark.parametrize("cfg,targets", [(OPT_SMALL, configs.KIND_NAMES_OPT),
+                                         (QWEN_SMALL, configs.KIND_NAMES_QWEN3),
+                                         (OPT_SMALL, ("q", "v"))])
+def test_factorized_equals_dense_mutation(cfg, targets):
+    wl = _small_wl(cfg, targets, dirs=(0, 5), n_fg=1)
+    bank = _bank_after_updates(cfg, wl)
+    batch = inputs.make_batch(wl)
+    W = Weights(cfg, wl.model_seed, cache_layers=True)
+    plan = zo.plan_from_workload(wl, 2)
+    a = zo.score(cfg, W, plan, bank, batch)
+    b = zo.score(cfg, W, plan, bank, batch, dense=True)
+    assert np.allclose(a["seq_logp"], b["seq_logp"], rtol=1e-12, atol=0)
+    assert np.allclose(a["S"], b["S"], rtol=1e-12, atol=0)
+    # the perturbation is actually visible
+    assert np.ptp(a["S"]) > 0
+
+
+@pytest.mark.parametrize("cfg,build", [(OPT_SMALL, _opt_hf), (QWEN_SMALL, _qwen_hf)])
+def test_candidate_state_matches_library_on_mutated_weights(cfg, build):
+    targets = cfg.kind_names
+    wl = _small_wl(cfg, targets, n_prompts=1)
+    bank = _bank_after_updates(cfg, wl, steps=1)
+    batch = inputs.make_batch(wl)
+    plan = zo.plan_from_workload(wl, 1)
+    Wbase = Weights(cfg, wl.model_seed, cache_layers=True)
+    got = zo.score(cfg, Wbase, plan, bank, batch)
+    for cand in range(2):
+        side = zo.side_terms(cfg, plan, bank, cand)
+        Wm = Weights(cfg, wl.model_seed, cache_layers=True)
+        names = {"q": "wq", "k": "wk", "v": "wv", "o": "wo", "fc1": "w_fc1", "fc2": "w_fc2",
+                 "gate": "w_gate", "up": "w_up", "down": "w_down"}
+        for l in range(cfg.n_layers):
+            Wl = Wm.get_layer(l)
+            for kind in targets:
+                for V, B in side(l, kind):
+                    Wl[names[kind]] = Wl[names[kind]] + B @ V.T
+        m = build(cfg, Wm)
+        toks = batch.tokens[0]
+        with torch.no_grad():
+            logits = m(input_ids=torch.tensor(toks, dtype=torch.long)[None]).logits[0]
+        ref = torch.log_softmax(logits, -1)[len(toks) - 2, int(toks[-1])].item()
+        p = [i for i, (li, c) in enumerate(got["phys"]) if c == cand][0]
+        assert abs(got["seq_logp"][p] - ref) < 1e-6
+
+
+def test_eps_zero_gives_equal_scores():
+    cfg = OPT_SMALL
+    wl = _small_wl(cfg, ("q", "v", "fc1"))
+    bank = _bank_after_updates(cfg, wl)
+    plan = zo.plan_from_workload(wl, 2)
+    plan.eps, plan.allow_zero_eps = 0.0, True
+    out = zo.score(cfg, Weights(cfg, 2, True), plan, bank, inputs.make_batch(wl))
+    assert out["S"][0] == out["S"][1]
+    with pytest.raises(ValueError):
+        Plan(0, 1, 2, 0.0, (0,), ((0, 1), (0, -1)), ("q",)).validate()
+
+
+def test_swapping_signs_negates_c_exactly():
+    S = np.array([-12.25, -12.875, -3.1, -2.9])
+    p1 = Plan(0, 1, 2, 1e-3, (0, 1), ((0, 1), (0, -1), (1, 1), (1, -1)), ("q",))
+    p2 = Plan(0, 1, 2, 1e-3, (0, 1), ((0, -1), (0, 1), (1, -1), (1, 1)), ("q",))
+    c1, c2 = zo.estimate(p1, S), zo.estimate(p2, S)
+    assert np.array_equal(c1, -c2)
+    # closed form: L = -S
+    assert c1[0] == ((-S[0]) - (-S[1])) / (2 * 1e-3)
+
+
+def test_inv_rank_and_mean_flags():
+    S = np.array([-10.0, -10.5])
+    p = Plan(0, 1, 4, 1e-2, (0,), ((0, 1), (0, -1)), ("q",))
+    c = zo.estimate(p, S)
+    cr = zo.estimate(p, S, zo.EST_INV_RANK)
+    assert abs(cr[0] * 4 - c[0]) <= np.spacing(abs(c[0]))
+    cm = zo.estimate(p, S, zo.EST_MEAN, n_scored=np.array([5, 5]))
+    # (L+/5 - L-/5) rounds the two quotients before the difference: bound relative to |L|
+    assert abs(cm[0] * 5 - c[0]) <= 1e-12 * abs(S).max() / 1e-2
+    with pytest.raises(FloatingPointError):
+        zo.estimate(p, np.array([np.nan, 1.0]))
+
+
+def test_c_converges_to_directional_derivative():
+    """L(W) = -sum log softmax(x W^T)_y; grad = (P - Y)^T X; D = <grad, G V^T>."""
+    r = np.random.default_rng(9)
+    n, din, V, rank = 6, 24, 40, 2
+    X, W = r.normal(size=(n, din)), r.normal(size=(V, din)) * 0.3
+    y = r.integers(0, V, size=n)
+    G, Vf = params.factor(3, 0, 0, 0, 0, V, rank), params.factor(3, 0, 0, 1, 0, din, rank)
+    logits = X @ W.T
+    P = np.exp(logits - logits.max(1, keepdims=True))
+    P /= P.sum(1, keepdims=True)
+    Y = np.zeros_like(P)
+    Y[np.arange(n), y] = 1
+    D = np.sum(((P - Y).T @ X) * (G @ Vf.T))
+    errs = []
+    for eps in (4e-3, 2e-3, 1e-3):
+        plan = Plan(0, 1, rank, eps, (3,), ((0, 1), (0, -1)), ("q",))
+        S = np.array([om.log_softmax_gather(om.linear(X, W, None, [(Vf, s * eps * G)], False), y).sum()
+                      for s in (1, -1)])
+        errs.append(abs(zo.estimate(plan, S)[0] - D))
+    assert errs[-1] / abs(D) < 5e-5
+    assert 3.0 < errs[0] / errs[1] < 5.0 and 3.0 < errs[1] / errs[2] < 5.0
+
+
+def test_update_closed_form_and_m_step_identity():
+    cfg = OPT_SMALL
+    wl = _small_wl(cfg, ("q", "fc2"), dirs=(4, 9))
+    bank = Bank(2, wl.rank, wl.targets)
+    cs = [np.array([0.8, -0.3]), np.array([-1.1, 0.6]), np.array([0.25, 0.4])]
+    lr = 0.05
+    for t, c in enumerate(cs):
+        zo.update(cfg, zo.plan_from_workload(wl, t), bank, c, lr)
+        if t == 0:
+            for d, e in enumerate(bank.active()):
+                G = params.factor(wl.dir_seeds[d], 1, 0, 0, 0, cfg.d_model, wl.rank)
+                exact = (0.0 - ((lr / 2) * c[d]) * G).astype(np.float32)
+                assert np.array_equal(e.U[(1, "q")], exact.astype(np.float64))
+    assert len(bank.active()) == 2          # nu = 4: all three steps in window 0
+    for d, e in enumerate(bank.active()):
+        n_out, n_in = cfg.linear_shape("fc2")
+        kid = cfg.kind_names.index("fc2")
+        dense = np.zeros((n_out, n_in))
+        V = params.factor(wl.dir_seeds[d], 0, kid, 1, 0, n_in, wl.rank)
+        for t, c in enumerate(cs):
+            G = params.factor(wl.dir_seeds[d], 0, kid, 0, t, n_out, wl.rank)
+            dense = dense - (lr / 2) * c[d] * (G @ V.T)       # three explicit dense updates
+        lazy = e.U[(0, "fc2")] @ V.T
+        assert np.allclose(lazy, dense, rtol=0, atol=1e-6 * np.abs(dense).max())
+
+
+def test_window_rollover_makes_new_entry():
+    cfg = OPT_SMALL
+    wl = _small_wl(cfg, ("v",))
+    bank = Bank(2, wl.rank, wl.targets)
+    for t in range(6):                                       # nu = 4: windows 0 and 1
+        zo.update(cfg, zo.plan_from_workload(wl, t), bank, np.array([1.0]), 0.1)
+    keys = sorted((e.seed, e.window) for e in bank.active())
+    assert keys == [(0, 0), (0, 1)]
+    with pytest.raises(RuntimeError):
+        for t in range(8, 9):
+            zo.update(cfg, zo.plan_from_workload(wl, t), bank, np.array([1.0]), 0.1)
+
+
+def test_packing_order_and_batch_equals_single():
+    cfg = OPT_SMALL
+    wl = _small_wl(cfg, ("q", "v"), n_fg=2, n_prompts=2)
+    batch = inputs.make_batch(wl)
+    plan = zo.plan_from_workload(wl, 0)
+    phys = zo.pack(batch, plan)
+    assert phys == [(0, -1), (1, -1), (2, 0), (3, 0), (2, 1), (3, 1)]
+    W = Weights(cfg, 2, True)
+    full = zo.score(cfg, W, plan, None, batch)
+    for li in range(batch.n_seq):
+        one = zo.score(cfg, W, plan, None, batch.subset([li]))
+        for p1, (l1, c1) in enumerate(one["phys"]):
+            p = phys.index((li, c1))
+            assert full["seq_logp"][p] == one["seq_logp"][p1]
+
+
+def test_all_next_scores_every_position():
+    toks = np.array([4, 8, 15, 16, 23])
+    pos, lab = zo.scored_positions(toks, zo.MODE_ALL_NEXT)
+    assert list(pos) == [0, 1, 2, 3] and list(lab) == [8, 15, 16, 23]
+    pos, lab = zo.scored_positions(toks, zo.MODE_LAST_LABEL)
+    assert list(pos) == [3] and list(lab) == [23]
+    with pytest.raises(ValueError):
+        zo.scored_positions(np.array([3]), zo.MODE_LAST_LABEL)
