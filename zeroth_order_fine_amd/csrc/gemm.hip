@@ -1,0 +1,424 @@
+// Shared-weight projection GEMM with the factorized side path and fused epilogues.
+//
+// C = A . B^T with A [M x K] activations and B [N x K] the frozen weight
+// (row-major, K contiguous, i.e. exactly the nn.Linear layout).  The per-row
+// side path of a candidate state theta + s*eps*G V^T + sum_j U_j V_j^T
+// ("Inference-Native Zeroth-Order Optimization", arXiv abstract: factorized
+// side states, LoRA banks; "Zeroth-Order Fine-Tuning Was an Inference Workload
+// All Along", section "The System Reorganization") is folded into the same
+// accumulation as an extended K: the tile's last K-steps read
+// As [M x ks] = per-row [t_j | s*eps*t_d] and Bs [N x ks] = [U_j | G_d], so W
+// is never written and rows without a candidate carry zeros.
+//
+// bf16 path: v_mfma_f32_16x16x32_bf16, 64-wide wavefronts, LDS double buffer
+// with an XOR swizzle on 16-byte chunks, one barrier per K-step, XCD-aware
+// mapping of workgroups to tiles.  fp32 path: VALU FMA with the same
+// accumulator layout (lane l holds rows 4*(l/16)+j, column l%16 of every
+// 16x16 block), so both share the epilogues.
+//
+// The tile shape depends only on the call site (N and K), never on M: a row's
+// result does not depend on what else is in the batch.
+#include "common.h"
+#include <math.h>
+#include <type_traits>
+
+namespace {
+
+// compile-time loop: f(integral_constant<int, 0>) ... f(integral_constant<int, N-1>)
+template <int I, int N, typename F>
+__device__ __forceinline__ void static_for(F&& f) {
+  if constexpr (I < N) {
+    f(std::integral_constant<int, I>{});
+    static_for<I + 1, N>(f);
+  }
+}
+
+constexpr int BK_BF16 = 64;
+constexpr int BK_F32 = 16;
+
+__device__ __forceinline__ float gelu_erf(float x) { return 0.5f * x * (1.0f + erff(x * 0.70710678118654752f)); }
+__device__ __forceinline__ float silu(float x) { return x / (1.0f + expf(-x)); }
+
+__device__ __forceinline__ int tile_swizzle(int bid, int total, int& logical) {
+  // Workgroups are dispatched round-robin over the 8 XCDs; give each XCD a
+  // contiguous range of logical tiles so neighbouring tiles share its L2.
+  int xcd = bid & 7, local = bid >> 3;
+  int per = total >> 3, rem = total & 7;
+  logical = (xcd < rem) ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
+  return logical;
+}
+
+// ------------------------------------------------------------------------------
+// epilogue, shared by both paths.  acc[i][j][q]: row r0 + i*16 + 4*(lane>>4) + q,
+// column c0 + j*16 + (lane&15).
+template <int EPI, int TM, int TN, int BM, int BN, int WM, int WN, typename TAct>
+__device__ __forceinline__ void epilogue(const GemmParams& p, floatx4_t (&acc)[TM][TN], int m0, int n0, int nt,
+                                         int wm, int wn, int lane, float* red) {
+  const int rbase = m0 + wm * WM + 4 * (lane >> 4);
+  const int cbase = n0 + wn * WN + (lane & 15);
+  constexpr int epi = EPI;
+  if constexpr (epi == EPI_STORE || epi == EPI_GELU || epi == EPI_RESID || epi == EPI_TPROJ) {
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = rbase + i * 16 + q;
+        if (r >= p.M) continue;
+        int cand = -1, cdir = -1;
+        float cscale = 0.f;
+        if constexpr (epi == EPI_TPROJ) {
+          cand = p.row_cand[r];
+          if (cand >= 0) { cdir = p.cand_dir[cand]; cscale = p.cand_scale[cand]; }
+        }
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int c = cbase + j * 16;
+          if (c >= p.N) continue;
+          float v = acc[i][j][q];
+          if constexpr (epi == EPI_TPROJ) {
+            int w = c % p.tp_ks;
+            float o = 0.f;
+            if (cand >= 0 && w < p.tp_used) {
+              int slot = w / p.tp_rank;
+              if (slot < p.tp_entries) o = v;
+              else if (slot - p.tp_entries == cdir) o = cscale * v;
+            }
+            ((TAct*)p.C)[(int64_t)r * p.ldc + c] = from_f32<TAct>(o);
+          } else {
+            if (p.bias) v += p.bias[c];
+            if constexpr (epi == EPI_RESID) {
+              float* hp = p.H + (int64_t)r * p.ldh + c;
+              *hp = *hp + v;
+            } else {
+              if constexpr (epi == EPI_GELU) v = gelu_erf(v);
+              ((TAct*)p.C)[(int64_t)r * p.ldc + c] = from_f32<TAct>(v);
+            }
+          }
+        }
+      }
+    return;
+  }
+  if constexpr (epi == EPI_SWIGLU) {
+    // packed rows: 16 gate rows then 16 up rows; output column = gate index
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = rbase + i * 16 + q;
+        if (r >= p.M) continue;
+#pragma unroll
+        for (int jp = 0; jp < TN / 2; ++jp) {
+          const int cg = cbase + (2 * jp) * 16;
+          if (cg >= p.N) continue;
+          const int oc = (n0 + wn * WN) / 2 + jp * 16 + (lane & 15);
+          float g = acc[i][2 * jp][q], u = acc[i][2 * jp + 1][q];
+          ((TAct*)p.C)[(int64_t)r * p.ldc + oc] = from_f32<TAct>(silu(g) * u);
+        }
+      }
+    return;
+  }
+  if constexpr (epi == EPI_LMHEAD) {
+    constexpr int NWN = BN / WN;
+    // red: [2][NWN][BM] floats
+    float* rmax = red;
+    float* rsum = red + NWN * BM;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        float m = -INFINITY;
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          if (cbase + j * 16 < p.N) m = fmaxf(m, acc[i][j][q]);
+#pragma unroll
+        for (int s = 1; s < 16; s <<= 1) m = fmaxf(m, __shfl_xor(m, s, 64));
+        if ((lane & 15) == 0) rmax[wn * BM + wm * WM + i * 16 + 4 * (lane >> 4) + q] = m;
+      }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int rl = wm * WM + i * 16 + 4 * (lane >> 4) + q;
+        float m = rmax[rl];
+#pragma unroll
+        for (int w = 1; w < NWN; ++w) m = fmaxf(m, rmax[w * BM + rl]);
+        float s = 0.f;
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          if (cbase + j * 16 < p.N) s += expf(acc[i][j][q] - m);
+#pragma unroll
+        for (int sh = 1; sh < 16; sh <<= 1) s += __shfl_xor(s, sh, 64);
+        if ((lane & 15) == 0) rsum[wn * BM + rl] = s;
+        const int r = m0 + rl;
+        if (r < p.M) {
+          const int lab = p.labels[r];
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+            if (cbase + j * 16 == lab) p.lab_logit[r] = acc[i][j][q];
+        }
+      }
+    __syncthreads();
+    const int tid = threadIdx.x;
+    for (int rl = tid; rl < BM; rl += blockDim.x) {
+      const int r = m0 + rl;
+      if (r >= p.M) continue;
+      float m = rmax[rl], s = 0.f;
+      for (int w = 1; w < NWN; ++w) m = fmaxf(m, rmax[w * BM + rl]);
+      for (int w = 0; w < NWN; ++w) s += rsum[w * BM + rl];
+      p.part[(int64_t)r * p.n_ntiles + nt] = make_float2(m, s);
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------
+// bf16 MFMA kernel
+template <int BM, int BN, int WM, int WN, int EPI>
+__global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
+gemm_bf16_kernel(GemmParams p) {
+  constexpr int NWM = BM / WM, NWN = BN / WN, NT = NWM * NWN * 64;
+  constexpr int TM = WM / 16, TN = WN / 16;
+  constexpr int BK = BK_BF16;
+  constexpr int CA = BM * BK / 8 / NT, CB = BN * BK / 8 / NT;
+  static_assert(CA * NT * 8 == BM * BK && CB * NT * 8 == BN * BK, "tile/threads mismatch");
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  bf16_t* sm = (bf16_t*)smem_raw;
+  constexpr int STAGE = (BM + BN) * BK;
+
+  const int n_mt = (p.M + BM - 1) / BM, n_nt = (p.N + BN - 1) / BN;
+  int logical;
+  tile_swizzle(blockIdx.x, n_mt * n_nt, logical);
+  const int mt = logical % n_mt, nt = logical / n_mt;
+  const int m0 = mt * BM, n0 = nt * BN;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / NWN, wn = wave % NWN;
+
+  const int grp = (p.n_bounds > 0 && n0 >= p.bounds[0]) + (p.n_bounds > 1 && n0 >= p.bounds[1]) +
+                  (p.n_bounds > 2 && n0 >= p.bounds[2]);
+  const int a_side_off = grp * p.ks_tile;
+  const int nkb = p.K / BK, nk = nkb + p.ks_tile / BK;
+
+  const bf16_t* Ab = (const bf16_t*)p.A;
+  const bf16_t* Bb = (const bf16_t*)p.B;
+  const bf16_t* Asb = (const bf16_t*)p.As;
+  const bf16_t* Bsb = (const bf16_t*)p.Bs;
+
+  // Thread t loads 16-byte chunk (t & 7) of tile rows (t >> 3) + i * NT/8.
+  // Offsets are 32-bit element offsets (the host checks every operand fits).
+  constexpr int RSTEP = NT / 8;
+  const int ch = tid & 7, r0 = tid >> 3;
+  int arow[CA], brow[CB];
+#pragma unroll
+  for (int i = 0; i < CA; ++i) arow[i] = min(m0 + r0 + i * RSTEP, p.M - 1);
+#pragma unroll
+  for (int i = 0; i < CB; ++i) brow[i] = min(n0 + r0 + i * RSTEP, p.N - 1);
+  const int lda = (int)p.lda, ldb = (int)p.ldb, ldas = (int)p.ldas, ldbs = (int)p.ldbs;
+
+  u32x4_t ra[CA], rb[CB];
+#define ZO_GLOAD(kt_)                                                              \
+  do {                                                                            \
+    const int kt__ = (kt_);                                                       \
+    const bool side__ = kt__ >= nkb;                                              \
+    const bf16_t* ga__ = side__ ? Asb : Ab;                                       \
+    const bf16_t* gb__ = side__ ? Bsb : Bb;                                       \
+    const int la__ = side__ ? ldas : lda, lb__ = side__ ? ldbs : ldb;             \
+    const int kb__ = (side__ ? (kt__ - nkb) : kt__) * BK + ch * 8;                \
+    const int ka__ = kb__ + (side__ ? a_side_off : 0);                            \
+    static_for<0, CA>([&](auto i) { ra[i] = *(const u32x4_t*)(ga__ + (arow[i] * la__ + ka__)); }); \
+    static_for<0, CB>([&](auto i) { rb[i] = *(const u32x4_t*)(gb__ + (brow[i] * lb__ + kb__)); }); \
+  } while (0)
+#define ZO_SSTORE(buf_)                                                           \
+  do {                                                                            \
+    bf16_t* sA_ = sm + (buf_) * STAGE;                                            \
+    bf16_t* sB_ = sA_ + BM * BK;                                                  \
+    static_for<0, CA>([&](auto i) {                                               \
+      const int rr = r0 + i * RSTEP;                                              \
+      *(u32x4_t*)(sA_ + rr * BK + ((ch ^ ((rr >> 1) & 7)) << 3)) = ra[i];           \
+    });                                                                           \
+    static_for<0, CB>([&](auto i) {                                               \
+      const int rr = r0 + i * RSTEP;                                              \
+      *(u32x4_t*)(sB_ + rr * BK + ((ch ^ ((rr >> 1) & 7)) << 3)) = rb[i];           \
+    });                                                                           \
+  } while (0)
+
+  floatx4_t acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+
+  if (nk > 0) {
+    ZO_GLOAD(0);
+    ZO_SSTORE(0);
+    __syncthreads();
+  }
+  const int lr = lane & 15, lk = lane >> 4;
+  const int sw = (lr >> 1) & 7;
+  for (int kt = 0; kt < nk; ++kt) {
+    const int cur = kt & 1;
+    if (kt + 1 < nk) ZO_GLOAD(kt + 1);
+    const bf16_t* sA = sm + cur * STAGE;
+    const bf16_t* sB = sA + BM * BK;
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int ch = ((kk * 4 + lk) ^ sw) << 3;
+      bf16x8_t a[TM], b[TN];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) a[i] = *(const bf16x8_t*)(sA + (wm * WM + i * 16 + lr) * BK + ch);
+#pragma unroll
+      for (int j = 0; j < TN; ++j) b[j] = *(const bf16x8_t*)(sB + (wn * WN + j * 16 + lr) * BK + ch);
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i], b[j], acc[i][j], 0, 0, 0);
+    }
+    if (kt + 1 < nk) ZO_SSTORE(cur ^ 1);
+    __syncthreads();
+  }
+  epilogue<EPI, TM, TN, BM, BN, WM, WN, bf16_t>(p, acc, m0, n0, nt, wm, wn, lane, (float*)smem_raw);
+#undef ZO_GLOAD
+#undef ZO_SSTORE
+}
+
+// ------------------------------------------------------------------------------
+// fp32 VALU kernel (fp32 models); same accumulator layout as the MFMA path.
+template <int BM, int BN, int WM, int WN, int EPI>
+__global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
+gemm_f32_kernel(GemmParams p) {
+  constexpr int NWM = BM / WM, NWN = BN / WN, NT = NWM * NWN * 64;
+  constexpr int TM = WM / 16, TN = WN / 16;
+  constexpr int BK = BK_F32;
+  __shared__ float sA[BM][BK + 1];
+  __shared__ float sB[BN][BK + 1];
+  __shared__ float red[2 * NWN * BM];
+  const int n_mt = (p.M + BM - 1) / BM, n_nt = (p.N + BN - 1) / BN;
+  int logical;
+  tile_swizzle(blockIdx.x, n_mt * n_nt, logical);
+  const int mt = logical % n_mt, nt = logical / n_mt;
+  const int m0 = mt * BM, n0 = nt * BN;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / NWN, wn = wave % NWN;
+  const int grp = (p.n_bounds > 0 && n0 >= p.bounds[0]) + (p.n_bounds > 1 && n0 >= p.bounds[1]) +
+                  (p.n_bounds > 2 && n0 >= p.bounds[2]);
+  const int a_side_off = grp * p.ks_tile;
+  const int nkb = p.K / BK, nk = nkb + p.ks_tile / BK;
+  const float* Af = (const float*)p.A;
+  const float* Bf = (const float*)p.B;
+  const float* Asf = (const float*)p.As;
+  const float* Bsf = (const float*)p.Bs;
+
+  floatx4_t acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+
+  for (int kt = 0; kt < nk; ++kt) {
+    for (int e = tid; e < BM * BK; e += NT) {
+      int r = e / BK, k = e % BK;
+      int gr = min(m0 + r, p.M - 1);
+      sA[r][k] = kt < nkb ? Af[(int64_t)gr * p.lda + kt * BK + k]
+                          : Asf[(int64_t)gr * p.ldas + a_side_off + (kt - nkb) * BK + k];
+    }
+    for (int e = tid; e < BN * BK; e += NT) {
+      int r = e / BK, k = e % BK;
+      int gr = min(n0 + r, p.N - 1);
+      sB[r][k] = kt < nkb ? Bf[(int64_t)gr * p.ldb + kt * BK + k]
+                          : Bsf[(int64_t)gr * p.ldbs + (kt - nkb) * BK + k];
+    }
+    __syncthreads();
+#pragma unroll 4
+    for (int k = 0; k < BK; ++k) {
+      float bv[TN];
+#pragma unroll
+      for (int j = 0; j < TN; ++j) bv[j] = sB[wn * WN + j * 16 + (lane & 15)][k];
+#pragma unroll
+      for (int i = 0; i < TM; ++i)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          float av = sA[wm * WM + i * 16 + 4 * (lane >> 4) + q][k];
+#pragma unroll
+          for (int j = 0; j < TN; ++j) acc[i][j][q] += av * bv[j];
+        }
+    }
+    __syncthreads();
+  }
+  epilogue<EPI, TM, TN, BM, BN, WM, WN, float>(p, acc, m0, n0, nt, wm, wn, lane, red);
+}
+
+template <int BM, int BN, int WM, int WN, int EPI>
+hipError_t launch_bf16(const GemmParams& p, hipStream_t s) {
+  constexpr int NT = (BM / WM) * (BN / WN) * 64;
+  const size_t stage = (size_t)(BM + BN) * BK_BF16 * sizeof(bf16_t);
+  size_t smem = 2 * stage;
+  const size_t red = (size_t)2 * (BN / WN) * BM * sizeof(float);
+  if (smem < red) smem = red;
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)gemm_bf16_kernel<BM, BN, WM, WN, EPI>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const int tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
+  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, EPI>), dim3(tiles), dim3(NT), smem, s, p);
+  return hipGetLastError();
+}
+
+template <int BM, int BN, int WM, int WN, int EPI>
+hipError_t launch_f32(const GemmParams& p, hipStream_t s) {
+  constexpr int NT = (BM / WM) * (BN / WN) * 64;
+  const int tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
+  hipLaunchKernelGGL((gemm_f32_kernel<BM, BN, WM, WN, EPI>), dim3(tiles), dim3(NT), 0, s, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+// Tile shapes per call site.  BIG: the shared-weight projections; NARROW: the
+// side-input projection (N = a few kind blocks); HEAD: the vocabulary head
+// (few rows, many columns).
+int gemm_cfg_bm(int cfg, bool bf16) {
+  if (!bf16) return 64;
+  return cfg == GEMM_CFG_HEAD ? 128 : 256;
+}
+int gemm_cfg_bn(int cfg, bool bf16) {
+  if (!bf16) return 64;
+  return cfg == GEMM_CFG_BIG ? 256 : (cfg == GEMM_CFG_NARROW ? 64 : 128);
+}
+int gemm_bk(bool bf16) { return bf16 ? BK_BF16 : BK_F32; }
+
+hipError_t gemm_launch_bf16(const GemmParams& p, int cfg, hipStream_t s) {
+  if (p.M <= 0 || p.N <= 0) return hipSuccess;
+  if (cfg == GEMM_CFG_BIG) {
+    switch (p.epi) {
+      case EPI_STORE: return launch_bf16<256, 256, 128, 128, EPI_STORE>(p, s);
+      case EPI_GELU: return launch_bf16<256, 256, 128, 128, EPI_GELU>(p, s);
+      case EPI_SWIGLU: return launch_bf16<256, 256, 128, 128, EPI_SWIGLU>(p, s);
+      case EPI_RESID: return launch_bf16<256, 256, 128, 128, EPI_RESID>(p, s);
+      default: return hipErrorInvalidValue;
+    }
+  }
+  if (cfg == GEMM_CFG_NARROW) {
+    if (p.epi == EPI_TPROJ) return launch_bf16<256, 64, 64, 64, EPI_TPROJ>(p, s);
+    if (p.epi == EPI_STORE) return launch_bf16<256, 64, 64, 64, EPI_STORE>(p, s);
+    return hipErrorInvalidValue;
+  }
+  if (p.epi == EPI_LMHEAD) return launch_bf16<128, 128, 64, 64, EPI_LMHEAD>(p, s);
+  return hipErrorInvalidValue;
+}
+
+hipError_t gemm_launch_f32(const GemmParams& p, int cfg, hipStream_t s) {
+  if (p.M <= 0 || p.N <= 0) return hipSuccess;
+  (void)cfg;
+  switch (p.epi) {
+    case EPI_STORE: return launch_f32<64, 64, 32, 32, EPI_STORE>(p, s);
+    case EPI_GELU: return launch_f32<64, 64, 32, 32, EPI_GELU>(p, s);
+    case EPI_SWIGLU: return launch_f32<64, 64, 32, 32, EPI_SWIGLU>(p, s);
+    case EPI_RESID: return launch_f32<64, 64, 32, 32, EPI_RESID>(p, s);
+    case EPI_TPROJ: return launch_f32<64, 64, 32, 32, EPI_TPROJ>(p, s);
+    case EPI_LMHEAD: return launch_f32<64, 64, 32, 32, EPI_LMHEAD>(p, s);
+    default: return hipErrorInvalidValue;
+  }
+}

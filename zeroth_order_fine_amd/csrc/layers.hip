@@ -1,0 +1,217 @@
+// Row-wise transformer pieces: embedding, LayerNorm / RMSNorm (optionally on a
+// gathered row list), per-head QK RMSNorm + rotate-half RoPE, and the final
+// log-prob combine.  All are HBM-bound: one row per workgroup, the row kept in
+// registers between the statistics and the write.
+#include "common.h"
+#include <math.h>
+
+namespace {
+
+constexpr int NORM_THREADS = 256;
+constexpr int NORM_MAXV = 24;      // d <= 256 * 24 = 6144
+
+__device__ __forceinline__ float block_sum(float v, float* sh) {
+#pragma unroll
+  for (int s = 32; s >= 1; s >>= 1) v += __shfl_xor(v, s, 64);
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  __syncthreads();
+  if (l == 0) sh[w] = v;
+  __syncthreads();
+  float t = 0.f;
+  const int nw = blockDim.x >> 6;
+  for (int i = 0; i < nw; ++i) t += sh[i];
+  return t;
+}
+
+template <typename TW>
+__global__ void embed_kernel(const TW* __restrict__ E, const TW* __restrict__ P, const int32_t* __restrict__ tokens,
+                             const int32_t* __restrict__ row_src, const int32_t* __restrict__ row_pos, int d,
+                             int vocab, float* __restrict__ h) {
+  const int m = blockIdx.x;
+  const int tok = min(max(tokens[row_src[m]], 0), vocab - 1);   // ids outside the vocabulary are clamped
+  const int pos = row_pos[m];
+  const TW* e = E + (int64_t)tok * d;
+  const TW* pp = P ? P + (int64_t)pos * d : nullptr;
+  float* out = h + (int64_t)m * d;
+  for (int i = threadIdx.x; i < d; i += blockDim.x) {
+    float v = to_f32<TW>(e[i]);
+    if (pp) v = v + to_f32<TW>(pp[i]);
+    out[i] = v;
+  }
+}
+
+// out[m] = norm(h[rows ? rows[m] : m]); LayerNorm (affine) or RMSNorm (gain only)
+template <typename T>
+__global__ void __launch_bounds__(NORM_THREADS)
+norm_kernel(const float* __restrict__ h, const int32_t* __restrict__ rows, int d, const float* __restrict__ w,
+            const float* __restrict__ b, float eps, int rms, T* __restrict__ out) {
+  __shared__ float sh[NORM_THREADS / 64];
+  const int m = blockIdx.x;
+  const int src = rows ? rows[m] : m;
+  const float* x = h + (int64_t)src * d;
+  float v[NORM_MAXV];
+  float s = 0.f;
+#pragma unroll
+  for (int k = 0; k < NORM_MAXV; ++k) {
+    const int i = threadIdx.x + k * NORM_THREADS;
+    v[k] = i < d ? x[i] : 0.f;
+    s += v[k];
+  }
+  float mean = 0.f, scale;
+  if (!rms) {
+    mean = block_sum(s, sh) / (float)d;
+    float q = 0.f;
+#pragma unroll
+    for (int k = 0; k < NORM_MAXV; ++k) {
+      const int i = threadIdx.x + k * NORM_THREADS;
+      const float c = v[k] - mean;
+      q += i < d ? c * c : 0.f;
+    }
+    const float var = block_sum(q, sh) / (float)d;
+    scale = 1.0f / sqrtf(var + eps);
+  } else {
+    float q = 0.f;
+#pragma unroll
+    for (int k = 0; k < NORM_MAXV; ++k) q += v[k] * v[k];
+    const float ms = block_sum(q, sh) / (float)d;
+    scale = 1.0f / sqrtf(ms + eps);
+  }
+  T* o = out + (int64_t)m * d;
+#pragma unroll
+  for (int k = 0; k < NORM_MAXV; ++k) {
+    const int i = threadIdx.x + k * NORM_THREADS;
+    if (i < d) {
+      float y = (v[k] - mean) * scale * w[i];
+      if (b) y += b[i];
+      o[i] = from_f32<T>(y);
+    }
+  }
+}
+
+// In place on the packed q|k|v row: per-head RMSNorm of q and k, then RoPE
+// with pairs (i, i + hd/2) and the position of the row within its sequence.
+template <typename T>
+__global__ void qknorm_rope_kernel(T* __restrict__ qkv, int ld, int hq, int hkv, int hd,
+                                   const float* __restrict__ qw, const float* __restrict__ kw, float eps,
+                                   const float2* __restrict__ cs, const int32_t* __restrict__ row_pos) {
+  const int m = blockIdx.x;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63, nw = blockDim.x >> 6;
+  const int half = hd >> 1;
+  const int pos = row_pos[m];
+  T* row = qkv + (int64_t)m * ld;
+  for (int head = wave; head < hq + hkv; head += nw) {
+    T* x = row + head * hd;
+    const float* g = head < hq ? qw : kw;
+    float a[2], c[2];
+    float ss = 0.f;
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int i = lane + 64 * t;
+      a[t] = i < half ? to_f32<T>(x[i]) : 0.f;
+      c[t] = i < half ? to_f32<T>(x[i + half]) : 0.f;
+      ss += a[t] * a[t] + c[t] * c[t];
+    }
+#pragma unroll
+    for (int s = 32; s >= 1; s >>= 1) ss += __shfl_xor(ss, s, 64);
+    const float sc = 1.0f / sqrtf(ss / (float)hd + eps);
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int i = lane + 64 * t;
+      if (i < half) {
+        const float x1 = a[t] * sc * g[i], x2 = c[t] * sc * g[i + half];
+        const float2 r = cs[(int64_t)pos * half + i];
+        x[i] = from_f32<T>(x1 * r.x - x2 * r.y);
+        x[i + half] = from_f32<T>(x2 * r.x + x1 * r.y);
+      }
+    }
+  }
+}
+
+// Per physical sequence: combine the vocabulary-tile partials of each scored
+// row into log p(label) = z_label - (max + log sum exp) in fp64, then sum the
+// sequence's rows in order.
+__global__ void logp_reduce_kernel(const float2* __restrict__ part, int n_tiles, const float* __restrict__ lab,
+                                   const int32_t* __restrict__ seq_first, double* __restrict__ tok64,
+                                   float* __restrict__ tok32, double* __restrict__ seq_logp) {
+  const int s = blockIdx.x;
+  const int r0 = seq_first[s], r1 = seq_first[s + 1];
+  for (int r = r0 + threadIdx.x; r < r1; r += blockDim.x) {
+    const float2* pr = part + (int64_t)r * n_tiles;
+    double M = -INFINITY;
+    for (int t = 0; t < n_tiles; ++t) M = fmax(M, (double)pr[t].x);
+    double S = 0.0;
+    for (int t = 0; t < n_tiles; ++t) S += (double)pr[t].y * exp((double)pr[t].x - M);
+    const double lp = (double)lab[r] - (M + log(S));
+    tok64[r] = lp;
+    if (tok32) tok32[r] = (float)lp;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    double acc = 0.0;
+    for (int r = r0; r < r1; ++r) acc += tok64[r];
+    seq_logp[s] = acc;
+  }
+}
+
+__global__ void gather_i32_kernel(const int32_t* __restrict__ src, const int32_t* __restrict__ idx, int n,
+                                  int32_t* __restrict__ dst) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) dst[i] = src[idx[i]];
+}
+
+}  // namespace
+
+hipError_t launch_gather_i32(const int32_t* src, const int32_t* idx, int n, int32_t* dst, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(gather_i32_kernel, dim3((n + 255) / 256), dim3(256), 0, s, src, idx, n, dst);
+  return hipGetLastError();
+}
+
+template <typename TW>
+hipError_t launch_embed_t(const TW* E, const TW* P, const int32_t* tokens, const int32_t* row_src,
+                          const int32_t* row_pos, int M, int d, int vocab, float* h, hipStream_t s) {
+  if (M <= 0) return hipSuccess;
+  hipLaunchKernelGGL(embed_kernel<TW>, dim3(M), dim3(256), 0, s, E, P, tokens, row_src, row_pos, d, vocab, h);
+  return hipGetLastError();
+}
+template hipError_t launch_embed_t<float>(const float*, const float*, const int32_t*, const int32_t*,
+                                          const int32_t*, int, int, int, float*, hipStream_t);
+template hipError_t launch_embed_t<bf16_t>(const bf16_t*, const bf16_t*, const int32_t*, const int32_t*,
+                                           const int32_t*, int, int, int, float*, hipStream_t);
+
+template <typename T>
+hipError_t launch_norm(const float* h, const int32_t* rows, int M, int d, const float* w, const float* b,
+                       float eps, bool rms, T* out, hipStream_t s) {
+  if (M <= 0) return hipSuccess;
+  if (d > NORM_THREADS * NORM_MAXV) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(norm_kernel<T>, dim3(M), dim3(NORM_THREADS), 0, s, h, rows, d, w, b, eps, rms ? 1 : 0, out);
+  return hipGetLastError();
+}
+template hipError_t launch_norm<float>(const float*, const int32_t*, int, int, const float*, const float*, float,
+                                       bool, float*, hipStream_t);
+template hipError_t launch_norm<bf16_t>(const float*, const int32_t*, int, int, const float*, const float*, float,
+                                        bool, bf16_t*, hipStream_t);
+
+template <typename T>
+hipError_t launch_qknorm_rope(T* qkv, int M, int ld, int hq, int hkv, int hd, const float* qw, const float* kw,
+                              float eps, const float2* rope_cs, const int32_t* row_pos, hipStream_t s) {
+  if (M <= 0) return hipSuccess;
+  if (hd > 256 || (hd & 1)) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(qknorm_rope_kernel<T>, dim3(M), dim3(256), 0, s, qkv, ld, hq, hkv, hd, qw, kw, eps, rope_cs,
+                     row_pos);
+  return hipGetLastError();
+}
+template hipError_t launch_qknorm_rope<float>(float*, int, int, int, int, int, const float*, const float*, float,
+                                              const float2*, const int32_t*, hipStream_t);
+template hipError_t launch_qknorm_rope<bf16_t>(bf16_t*, int, int, int, int, int, const float*, const float*, float,
+                                               const float2*, const int32_t*, hipStream_t);
+
+hipError_t launch_logp_reduce(const float2* part, int n_tiles, const float* lab_logit, int n_scored,
+                              const int32_t* seq_first, int n_phys, double* tok_logp64, float* tok_logp32,
+                              double* seq_logp, hipStream_t s) {
+  (void)n_scored;
+  if (n_phys <= 0) return hipSuccess;
+  hipLaunchKernelGGL(logp_reduce_kernel, dim3(n_phys), dim3(256), 0, s, part, n_tiles, lab_logit, seq_first,
+                     tok_logp64, tok_logp32, seq_logp);
+  return hipGetLastError();
+}

@@ -1,0 +1,1084 @@
+// Host runtime of libzo: the C-ABI declared in include/zo.h.
+//
+// Plans, packing and the bank's keys are host objects; every step of the path
+// runs in the HIP kernels of this library, launched on the caller's stream.
+// The query process follows the arXiv abstract of "Inference-Native
+// Zeroth-Order Optimization" (ProbePlan -> candidate evaluation -> estimation ->
+// update) and the estimator and lazy update of "Zeroth-Order Fine-Tuning Was an
+// Inference Workload All Along" (sections "Why ZO Fine-Tuning Is Really
+// Scoring" and "The System Reorganization").
+#include "../../include/zo.h"
+#include "common.h"
+
+#include <algorithm>
+#include <array>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <new>
+#include <string>
+#include <vector>
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof buf, fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return code;
+}
+
+#define ZO_HIP(expr)                                                                             \
+  do {                                                                                           \
+    hipError_t e_ = (expr);                                                                      \
+    if (e_ != hipSuccess) return fail(ZO_E_DEVICE, "%s: %s", #expr, hipGetErrorString(e_));      \
+  } while (0)
+
+#define ZO_CHECK(cond, code, ...)                 \
+  do {                                            \
+    if (!(cond)) return fail(code, __VA_ARGS__);  \
+  } while (0)
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+inline int64_t round_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
+
+// ---- parameters and layout -----------------------------------------------------
+enum { G_TOK = 0, G_POS = 1, G_FNW = 2, G_FNB = 3, G_HEAD = 4, N_GLOBAL = 5 };
+enum {
+  P_LN1W = 0, P_LN1B, P_WQ, P_BQ, P_WK, P_BK, P_WV, P_BV, P_WO, P_BO, P_LN2W, P_LN2B,
+  P_W1, P_B1, P_W2, P_B2, P_WDOWN, P_QNW, P_KNW, N_LAYER_PARAMS
+};
+
+struct TLoc {
+  bool present = false;
+  size_t off = 0;
+  int64_t rows = 0, cols = 0;
+  int32_t dtype = ZO_DTYPE_F32;
+  int32_t layout = 0;   // 0 plain, 1 gate / 2 up of a 16-row interleave
+  bool gain = false;    // initialised as 1 + 0.02 z
+};
+
+struct Layout {
+  size_t bytes = 0;
+  std::array<TLoc, N_GLOBAL> g;
+  std::vector<std::array<TLoc, N_LAYER_PARAMS>> L;
+};
+
+bool is_opt(const zo_model_desc& d) { return d.arch == ZO_ARCH_OPT; }
+int n_kinds_of(const zo_model_desc& d) { return is_opt(d) ? 6 : 7; }
+
+int validate_desc(const zo_model_desc* d) {
+  ZO_CHECK(d, ZO_E_INVAL, "null model descriptor");
+  ZO_CHECK(d->abi_version == ZO_ABI_VERSION, ZO_E_ABI, "descriptor ABI %d, library ABI %d", d->abi_version,
+           ZO_ABI_VERSION);
+  ZO_CHECK(d->arch == ZO_ARCH_OPT || d->arch == ZO_ARCH_QWEN3, ZO_E_INVAL, "unknown arch %d", d->arch);
+  ZO_CHECK(d->dtype == ZO_DTYPE_F32 || d->dtype == ZO_DTYPE_BF16, ZO_E_INVAL, "unknown dtype %d", d->dtype);
+  ZO_CHECK(d->n_layers >= 1 && d->d_model >= 1 && d->n_heads >= 1 && d->n_kv_heads >= 1 && d->head_dim >= 1 &&
+               d->d_ffn >= 1 && d->vocab >= 2 && d->max_pos >= 1,
+           ZO_E_INVAL, "model sizes must be positive");
+  ZO_CHECK(d->n_heads % d->n_kv_heads == 0, ZO_E_INVAL, "n_heads must be a multiple of n_kv_heads");
+  ZO_CHECK(is_opt(*d) ? d->n_kv_heads == d->n_heads : true, ZO_E_INVAL, "OPT has n_kv_heads == n_heads");
+  ZO_CHECK(d->head_dim == 16 || d->head_dim == 32 || d->head_dim == 64 || d->head_dim == 128, ZO_E_INVAL,
+           "head_dim must be 16, 32, 64 or 128");
+  ZO_CHECK(d->dtype == ZO_DTYPE_F32 || d->head_dim >= 32, ZO_E_INVAL, "bf16 attention needs head_dim >= 32");
+  ZO_CHECK(d->d_model <= 6144, ZO_E_INVAL, "d_model above 6144 is not supported by the norm kernels");
+  ZO_CHECK(std::isfinite(d->norm_eps) && d->norm_eps > 0, ZO_E_INVAL, "norm_eps must be > 0");
+  ZO_CHECK(is_opt(*d) || (std::isfinite(d->rope_theta) && d->rope_theta > 1.0), ZO_E_INVAL,
+           "rope_theta must be > 1");
+  ZO_CHECK(is_opt(*d) || d->d_ffn % 16 == 0, ZO_E_INVAL, "Qwen3 d_ffn must be a multiple of 16");
+  return ZO_OK;
+}
+
+Layout make_layout(const zo_model_desc& d) {
+  Layout Lo;
+  size_t off = 0;
+  const int mdt = d.dtype;
+  auto esz = [](int dt) { return dt == ZO_DTYPE_BF16 ? (size_t)2 : (size_t)4; };
+  auto place = [&](TLoc& t, int64_t rows, int64_t cols, int dt, bool aligned, bool gain = false) {
+    if (aligned) off = align_up(off, 256);
+    t.present = true; t.off = off; t.rows = rows; t.cols = cols; t.dtype = dt; t.gain = gain;
+    off += (size_t)rows * cols * esz(dt);
+  };
+  const int64_t D = d.d_model, V = d.vocab, F = d.d_ffn;
+  const int64_t NQ = (int64_t)d.n_heads * d.head_dim, NKV = (int64_t)d.n_kv_heads * d.head_dim;
+  place(Lo.g[G_TOK], V, D, mdt, true);
+  if (is_opt(d)) place(Lo.g[G_POS], d.max_pos, D, mdt, true);
+  place(Lo.g[G_FNW], 1, D, ZO_DTYPE_F32, true, true);
+  if (is_opt(d)) place(Lo.g[G_FNB], 1, D, ZO_DTYPE_F32, true);
+  if (!is_opt(d)) place(Lo.g[G_HEAD], V, D, mdt, true);
+  Lo.L.resize(d.n_layers);
+  for (int l = 0; l < d.n_layers; ++l) {
+    auto& P = Lo.L[l];
+    if (is_opt(d)) {
+      place(P[P_LN1W], 1, D, ZO_DTYPE_F32, true, true);
+      place(P[P_LN1B], 1, D, ZO_DTYPE_F32, true);
+      place(P[P_WQ], NQ, D, mdt, true);
+      place(P[P_WK], NKV, D, mdt, false);
+      place(P[P_WV], NKV, D, mdt, false);
+      place(P[P_BQ], 1, NQ, ZO_DTYPE_F32, true);
+      place(P[P_BK], 1, NKV, ZO_DTYPE_F32, false);
+      place(P[P_BV], 1, NKV, ZO_DTYPE_F32, false);
+      place(P[P_WO], D, NQ, mdt, true);
+      place(P[P_BO], 1, D, ZO_DTYPE_F32, true);
+      place(P[P_LN2W], 1, D, ZO_DTYPE_F32, true, true);
+      place(P[P_LN2B], 1, D, ZO_DTYPE_F32, true);
+      place(P[P_W1], F, D, mdt, true);
+      place(P[P_B1], 1, F, ZO_DTYPE_F32, true);
+      place(P[P_W2], D, F, mdt, true);
+      place(P[P_B2], 1, D, ZO_DTYPE_F32, true);
+    } else {
+      place(P[P_LN1W], 1, D, ZO_DTYPE_F32, true, true);
+      place(P[P_WQ], NQ, D, mdt, true);
+      place(P[P_WK], NKV, D, mdt, false);
+      place(P[P_WV], NKV, D, mdt, false);
+      place(P[P_QNW], 1, d.head_dim, ZO_DTYPE_F32, true, true);
+      place(P[P_KNW], 1, d.head_dim, ZO_DTYPE_F32, true, true);
+      place(P[P_WO], D, NQ, mdt, true);
+      place(P[P_LN2W], 1, D, ZO_DTYPE_F32, true, true);
+      // gate/up: one packed [2F x D] matrix, 16-row interleave
+      place(P[P_W1], 2 * F, D, mdt, true);
+      P[P_W1].rows = F; P[P_W1].layout = 1;
+      P[P_W2] = P[P_W1]; P[P_W2].layout = 2;
+      place(P[P_WDOWN], D, F, mdt, true);
+    }
+  }
+  Lo.bytes = align_up(off, 256);
+  return Lo;
+}
+
+// ---- kinds ---------------------------------------------------------------------
+struct KindShape { int64_t n_out, n_in; };
+KindShape kind_shape(const zo_model_desc& d, int kind) {
+  const int64_t D = d.d_model, F = d.d_ffn;
+  const int64_t NQ = (int64_t)d.n_heads * d.head_dim, NKV = (int64_t)d.n_kv_heads * d.head_dim;
+  switch (kind) {
+    case ZO_KIND_Q: return {NQ, D};
+    case ZO_KIND_K: return {NKV, D};
+    case ZO_KIND_V: return {NKV, D};
+    case ZO_KIND_O: return {D, NQ};
+    case 4: return {F, D};                              // fc1 / gate
+    case 5: return is_opt(d) ? KindShape{D, F} : KindShape{F, D};   // fc2 / up
+    default: return {D, F};                             // down
+  }
+}
+
+inline uint32_t dir_tag(int layer, int kind, int factor) {
+  return ((uint32_t)layer << 8) | ((uint32_t)kind << 1) | (uint32_t)factor;
+}
+inline uint32_t weight_tag(int slot, int param) { return (1u << 30) | ((uint32_t)slot << 8) | (uint32_t)param; }
+
+}  // namespace
+
+// ---- opaque objects --------------------------------------------------------------
+struct zo_model {
+  zo_model_desc d;
+  Layout lo;
+  unsigned char* w = nullptr;
+  size_t w_bytes = 0;
+  float2* rope = nullptr;   // [rope_len x head_dim/2] (cos, sin), Qwen3
+  int rope_len = 0;
+  int device = 0;
+};
+
+struct zo_plan_s {
+  zo_model_desc md;
+  uint64_t t;
+  uint32_t nu;
+  int rank;
+  double eps, eps_tilde;
+  std::vector<uint64_t> seeds;
+  std::vector<int32_t> cdir, csign;
+  uint32_t mask, flags;
+  uint64_t window() const { return t / nu; }
+};
+
+struct zo_bank {
+  zo_model_desc md;
+  int n_slots, rank;
+  uint32_t mask;
+  float* u = nullptr;
+  size_t bytes = 0;
+  std::vector<uint64_t> seeds;
+  std::vector<int64_t> windows;
+  std::vector<int> kinds;            // target kinds, increasing
+  std::vector<int64_t> kind_off;     // floats within a layer
+  int64_t layer_stride = 0;          // floats per layer
+  int64_t slot_stride = 0;           // floats per slot
+};
+
+namespace {
+
+int bank_geometry(const zo_model_desc& d, int rank, uint32_t mask, std::vector<int>& kinds,
+                  std::vector<int64_t>& koff, int64_t& layer_stride) {
+  kinds.clear(); koff.clear();
+  int64_t o = 0;
+  for (int k = 0; k < n_kinds_of(d); ++k)
+    if (mask & (1u << k)) {
+      kinds.push_back(k);
+      koff.push_back(o);
+      o += kind_shape(d, k).n_out * rank;
+    }
+  layer_stride = o;
+  return ZO_OK;
+}
+
+// GEMM input groups of a layer: which kinds read the same activations.
+struct Group {
+  std::vector<int> kinds;   // kind of each column block of the side input
+  bool interleaved = false; // gate/up packed GEMM (both kinds in one tile)
+};
+
+std::vector<Group> layer_groups(const zo_model_desc& d) {
+  std::vector<Group> g(4);
+  g[0].kinds = {ZO_KIND_Q, ZO_KIND_K, ZO_KIND_V};
+  g[1].kinds = {ZO_KIND_O};
+  if (is_opt(d)) {
+    g[2].kinds = {4};
+    g[3].kinds = {5};
+  } else {
+    g[2].kinds = {4, 5};
+    g[2].interleaved = true;
+    g[3].kinds = {6};
+  }
+  return g;
+}
+
+// ---- workspace bump allocator ------------------------------------------------------
+struct Bump {
+  unsigned char* base;
+  size_t off = 0;
+  explicit Bump(void* b) : base((unsigned char*)b) {}
+  template <typename T>
+  T* take(size_t count) {
+    off = align_up(off, 256);
+    T* p = base ? (T*)(base + off) : nullptr;
+    off += count * sizeof(T);
+    return p;
+  }
+};
+
+// Everything zo_score needs to know about one batch under one plan and bank.
+struct Packing {
+  int n_phys = 0;
+  int64_t M = 0, n_scored = 0;
+  std::vector<int32_t> phys_seq, phys_cand, phys_cu, phys_first;
+  std::vector<int32_t> row_src, row_pos, row_cand;
+  std::vector<int32_t> sc_row, sc_lab_src;
+  std::vector<int32_t> work;
+  int max_len = 0;
+};
+
+int validate_batch(const zo_model_desc& d, const zo_batch* b) {
+  ZO_CHECK(b, ZO_E_INVAL, "null batch");
+  ZO_CHECK(b->n_seq >= 0, ZO_E_INVAL, "n_seq < 0");
+  if (b->n_seq == 0) return ZO_OK;
+  ZO_CHECK(b->cu_seqlens && b->role && b->score_mode, ZO_E_INVAL, "null batch array");
+  ZO_CHECK(b->cu_seqlens[0] == 0, ZO_E_SHAPE, "cu_seqlens[0] must be 0");
+  for (int i = 0; i < b->n_seq; ++i) {
+    const int len = b->cu_seqlens[i + 1] - b->cu_seqlens[i];
+    ZO_CHECK(len >= 1, ZO_E_SHAPE, "sequence %d has length %d", i, len);
+    ZO_CHECK(b->role[i] == ZO_ROLE_PROBE || b->role[i] == ZO_ROLE_FOREGROUND, ZO_E_INVAL, "bad role");
+    ZO_CHECK(b->score_mode[i] == ZO_SCORE_LAST_LABEL || b->score_mode[i] == ZO_SCORE_ALL_NEXT, ZO_E_INVAL,
+             "bad score mode");
+    ZO_CHECK(b->score_mode[i] != ZO_SCORE_LAST_LABEL || len >= 2, ZO_E_SHAPE,
+             "LAST_LABEL sequence %d needs length >= 2", i);
+    ZO_CHECK(len <= d.max_pos, ZO_E_SHAPE, "sequence %d longer than max_pos", i);
+    ZO_CHECK(len <= 4095 * 64, ZO_E_SHAPE, "sequence %d too long", i);
+  }
+  ZO_CHECK(b->tokens_dev || b->cu_seqlens[b->n_seq] == 0, ZO_E_INVAL, "null tokens");
+  return ZO_OK;
+}
+
+void build_packing(const zo_plan_s& p, const zo_batch& b, Packing& pk) {
+  pk = Packing();
+  auto add = [&](int li, int c) {
+    pk.phys_seq.push_back(li);
+    pk.phys_cand.push_back(c);
+  };
+  for (int i = 0; i < b.n_seq; ++i)
+    if (b.role[i] == ZO_ROLE_FOREGROUND) add(i, -1);
+  for (int c = 0; c < (int)p.cdir.size(); ++c)
+    for (int i = 0; i < b.n_seq; ++i)
+      if (b.role[i] == ZO_ROLE_PROBE) add(i, c);
+  pk.n_phys = (int)pk.phys_seq.size();
+  pk.phys_cu.assign(1, 0);
+  pk.phys_first.assign(1, 0);
+  for (int q = 0; q < pk.n_phys; ++q) {
+    const int li = pk.phys_seq[q], c = pk.phys_cand[q];
+    const int start = b.cu_seqlens[li], len = b.cu_seqlens[li + 1] - start;
+    const int prow0 = (int)pk.M;
+    for (int t = 0; t < len; ++t) {
+      pk.row_src.push_back(start + t);
+      pk.row_pos.push_back(t);
+      pk.row_cand.push_back(c);
+    }
+    if (b.score_mode[li] == ZO_SCORE_LAST_LABEL) {
+      pk.sc_row.push_back(prow0 + len - 2);
+      pk.sc_lab_src.push_back(start + len - 1);
+    } else {
+      for (int t = 0; t + 1 < len; ++t) {
+        pk.sc_row.push_back(prow0 + t);
+        pk.sc_lab_src.push_back(start + t + 1);
+      }
+    }
+    for (int qb = 0; qb * 64 < len; ++qb) pk.work.push_back((q << 12) | qb);
+    pk.M += len;
+    pk.max_len = std::max(pk.max_len, len);
+    pk.phys_cu.push_back((int32_t)pk.M);
+    pk.phys_first.push_back((int32_t)pk.sc_row.size());
+  }
+  pk.n_scored = (int64_t)pk.sc_row.size();
+}
+
+// Side-path geometry of a plan + bank (independent of the batch contents).
+struct SideGeom {
+  bool any = false;
+  int E = 0, q = 0, r = 0;
+  int used = 0, ks = 0;
+  std::vector<int> entry_slots;     // active bank slots in slot order
+  std::vector<Group> groups;
+  std::vector<bool> group_on;       // group has at least one target kind
+  std::vector<int64_t> vt_rows;     // rows of the group's V^T block (per layer)
+  std::vector<int64_t> bs_cols;     // ks_tile of the group's GEMM
+  std::vector<int64_t> bs_rows;     // physical output rows of the group's GEMM
+  std::vector<int64_t> n_in;
+};
+
+int side_geometry(const zo_model* m, const zo_plan_s& p, const zo_bank* bank, SideGeom& sg) {
+  const zo_model_desc& d = m->d;
+  sg = SideGeom();
+  sg.q = (int)p.seeds.size();
+  sg.r = p.rank;
+  if (bank) {
+    ZO_CHECK(bank->rank == p.rank, ZO_E_STATE, "bank rank %d != plan rank %d", bank->rank, p.rank);
+    ZO_CHECK(bank->mask == p.mask, ZO_E_STATE, "bank target mask differs from the plan's");
+    for (int s = 0; s < bank->n_slots; ++s)
+      if (bank->windows[s] >= 0) sg.entry_slots.push_back(s);
+  }
+  sg.E = (int)sg.entry_slots.size();
+  const int bk = gemm_bk(d.dtype == ZO_DTYPE_BF16);
+  sg.used = (sg.E + sg.q) * sg.r;
+  sg.ks = (int)round_up(sg.used, bk);
+  sg.groups = layer_groups(d);
+  const int64_t D = d.d_model, F = d.d_ffn;
+  const int64_t NQ = (int64_t)d.n_heads * d.head_dim, NKV = (int64_t)d.n_kv_heads * d.head_dim;
+  const int64_t nin[4] = {D, NQ, D, F};
+  const int64_t nrows[4] = {NQ + 2 * NKV, D, is_opt(d) ? F : 2 * F, D};
+  for (int g = 0; g < 4; ++g) {
+    bool on = false;
+    for (int k : sg.groups[g].kinds) on |= (p.mask >> k) & 1u;
+    sg.group_on.push_back(on);
+    sg.any |= on;
+    const int nb = (int)sg.groups[g].kinds.size();
+    sg.vt_rows.push_back(on ? (int64_t)nb * sg.ks : 0);
+    sg.bs_cols.push_back(on ? (sg.groups[g].interleaved ? (int64_t)nb * sg.ks : sg.ks) : 0);
+    sg.bs_rows.push_back(nrows[g]);
+    sg.n_in.push_back(nin[g]);
+  }
+  return ZO_OK;
+}
+
+struct WsPtrs {
+  int32_t *row_src, *row_pos, *row_cand, *phys_cu, *phys_first, *sc_row, *sc_lab_src, *work, *labels;
+  int32_t* cand_dir;
+  float* cand_scale;
+  SideJob* jobs;
+  float* h;
+  void *xa, *qkv, *attn, *hid, *as, *xs;
+  std::vector<void*> vt, bs;   // per layer*4 + group
+  unsigned char* side_begin = nullptr;
+  size_t side_bytes = 0;
+  float2* part;
+  float* lab_logit;
+  double *tok64, *seq_logp;
+  size_t bytes;
+};
+
+size_t act_size(const zo_model_desc& d) { return d.dtype == ZO_DTYPE_BF16 ? 2 : 4; }
+
+int n_side_jobs(const zo_model_desc& d, const zo_plan_s& p, const SideGeom& sg) {
+  if (!sg.any) return 0;
+  int per_kind = 0;
+  per_kind += sg.E + sg.q;   // V rows
+  per_kind += sg.E + sg.q;   // Bs columns (U entries, G directions)
+  int kinds = 0;
+  for (int k = 0; k < n_kinds_of(d); ++k) kinds += (p.mask >> k) & 1u;
+  return d.n_layers * kinds * per_kind;
+}
+
+void carve(const zo_model* m, const zo_plan_s& p, const Packing& pk, const SideGeom& sg, void* base, WsPtrs& w) {
+  const zo_model_desc& d = m->d;
+  const size_t as = act_size(d);
+  Bump b(base);
+  const int64_t M = std::max<int64_t>(pk.M, 1), S = std::max<int64_t>(pk.n_scored, 1);
+  const int nc = (int)p.cdir.size();
+  w.row_src = b.take<int32_t>(M);
+  w.row_pos = b.take<int32_t>(M);
+  w.row_cand = b.take<int32_t>(M);
+  w.phys_cu = b.take<int32_t>(pk.n_phys + 1);
+  w.phys_first = b.take<int32_t>(pk.n_phys + 1);
+  w.sc_row = b.take<int32_t>(S);
+  w.sc_lab_src = b.take<int32_t>(S);
+  w.work = b.take<int32_t>(std::max<size_t>(pk.work.size(), 1));
+  w.labels = b.take<int32_t>(S);
+  w.cand_dir = b.take<int32_t>(nc);
+  w.cand_scale = b.take<float>(nc);
+  w.jobs = b.take<SideJob>(std::max(n_side_jobs(d, p, sg), 1));
+  const int64_t D = d.d_model, F = d.d_ffn;
+  const int64_t NQ = (int64_t)d.n_heads * d.head_dim, NKV = (int64_t)d.n_kv_heads * d.head_dim;
+  w.h = b.take<float>(M * D);
+  w.xa = b.take<unsigned char>(M * D * as);
+  w.qkv = b.take<unsigned char>(M * (NQ + 2 * NKV) * as);
+  w.attn = b.take<unsigned char>(M * NQ * as);
+  w.hid = b.take<unsigned char>(M * F * as);
+  int64_t as_cols = 0;
+  for (int g = 0; g < 4; ++g) as_cols = std::max(as_cols, sg.vt_rows[g]);
+  w.as = b.take<unsigned char>(M * std::max<int64_t>(as_cols, 1) * as);
+  w.vt.assign((size_t)d.n_layers * 4, nullptr);
+  w.bs.assign((size_t)d.n_layers * 4, nullptr);
+  b.off = align_up(b.off, 256);
+  const size_t side0 = b.off;
+  for (int l = 0; l < d.n_layers; ++l)
+    for (int g = 0; g < 4; ++g)
+      if (sg.group_on[g]) {
+        w.vt[l * 4 + g] = b.take<unsigned char>(sg.vt_rows[g] * sg.n_in[g] * as);
+        w.bs[l * 4 + g] = b.take<unsigned char>(sg.bs_rows[g] * sg.bs_cols[g] * as);
+      }
+  w.side_begin = base ? (unsigned char*)base + side0 : nullptr;
+  w.side_bytes = b.off - side0;
+  w.xs = b.take<unsigned char>(S * D * as);
+  const int bn_head = gemm_cfg_bn(GEMM_CFG_HEAD, d.dtype == ZO_DTYPE_BF16);
+  const int64_t n_vt = (d.vocab + bn_head - 1) / bn_head;
+  w.part = b.take<float2>(S * n_vt);
+  w.lab_logit = b.take<float>(S);
+  w.tok64 = b.take<double>(S);
+  w.seq_logp = b.take<double>(std::max(pk.n_phys, 1));
+  w.bytes = align_up(b.off, 256);
+}
+
+int check_i32(int64_t elems, const char* what) {
+  ZO_CHECK(elems < ((int64_t)1 << 31), ZO_E_SHAPE, "%s has %lld elements; the GEMM uses 32-bit offsets", what,
+           (long long)elems);
+  return ZO_OK;
+}
+
+int run_gemm(const zo_model_desc& d, const GemmParams& gp, int cfg, hipStream_t s) {
+  if (d.dtype == ZO_DTYPE_BF16) {
+    const int bn = gemm_cfg_bn(cfg, true);
+    for (int i = 0; i < gp.n_bounds; ++i)
+      ZO_CHECK(gp.bounds[i] % bn == 0, ZO_E_SHAPE, "kind boundary %d not a multiple of the %d-column tile",
+               gp.bounds[i], bn);
+    ZO_CHECK(gp.K % gemm_bk(true) == 0 && gp.ks_tile % gemm_bk(true) == 0, ZO_E_SHAPE, "K not a multiple of 64");
+    int rc;
+    if ((rc = check_i32((int64_t)gp.M * gp.lda, "A")) != ZO_OK) return rc;
+    if ((rc = check_i32((int64_t)gp.N * gp.ldb, "B")) != ZO_OK) return rc;
+    if ((rc = check_i32((int64_t)gp.M * gp.ldas, "As")) != ZO_OK) return rc;
+    if ((rc = check_i32((int64_t)gp.N * gp.ldbs, "Bs")) != ZO_OK) return rc;
+    ZO_HIP(gemm_launch_bf16(gp, cfg, s));
+  } else {
+    const int bn = gemm_cfg_bn(cfg, false);
+    for (int i = 0; i < gp.n_bounds; ++i)
+      ZO_CHECK(gp.bounds[i] % bn == 0, ZO_E_SHAPE, "kind boundary not a multiple of the tile");
+    ZO_CHECK(gp.K % gemm_bk(false) == 0 && gp.ks_tile % gemm_bk(false) == 0, ZO_E_SHAPE,
+             "K not a multiple of 16");
+    ZO_HIP(gemm_launch_f32(gp, cfg, s));
+  }
+  return ZO_OK;
+}
+
+GemmParams gemm_base(const void* A, int64_t lda, const void* B, int64_t ldb, int M, int N, int K) {
+  GemmParams g;
+  memset(&g, 0, sizeof g);
+  g.A = A; g.lda = lda; g.B = B; g.ldb = ldb; g.M = M; g.N = N; g.K = K;
+  return g;
+}
+
+template <typename T>
+int forward(zo_model* m, const zo_plan_s& p, const Packing& pk, const SideGeom& sg, const WsPtrs& w,
+            const int32_t* tokens, hipStream_t s) {
+  const zo_model_desc& d = m->d;
+  const bool bf = d.dtype == ZO_DTYPE_BF16;
+  const Layout& Lo = m->lo;
+  auto W = [&](const TLoc& t) -> const void* { return t.present ? (const void*)(m->w + t.off) : nullptr; };
+  auto Wf = [&](const TLoc& t) -> const float* { return (const float*)W(t); };
+  const int M = (int)pk.M;
+  const int D = d.d_model, F = d.d_ffn;
+  const int NQ = d.n_heads * d.head_dim, NKV = d.n_kv_heads * d.head_dim;
+  const int NQKV = NQ + 2 * NKV;
+  const float eps = (float)d.norm_eps;
+  const bool rms = !is_opt(d);
+  const int big = GEMM_CFG_BIG, narrow = GEMM_CFG_NARROW;
+  int rc;
+
+  if (M > 0) {
+    if (bf)
+      ZO_HIP(launch_embed_t<bf16_t>((const bf16_t*)W(Lo.g[G_TOK]), (const bf16_t*)W(Lo.g[G_POS]), tokens,
+                                    w.row_src, w.row_pos, M, D, d.vocab, w.h, s));
+    else
+      ZO_HIP(launch_embed_t<float>((const float*)W(Lo.g[G_TOK]), (const float*)W(Lo.g[G_POS]), tokens, w.row_src,
+                                   w.row_pos, M, D, d.vocab, w.h, s));
+  }
+
+  auto tproj = [&](int l, int g, const void* X, int K) -> int {
+    if (!sg.group_on[g]) return ZO_OK;
+    GemmParams gp = gemm_base(X, K, w.vt[l * 4 + g], K, M, (int)sg.vt_rows[g], K);
+    gp.epi = EPI_TPROJ;
+    gp.C = w.as; gp.ldc = sg.vt_rows[g];
+    gp.row_cand = w.row_cand; gp.cand_dir = w.cand_dir; gp.cand_scale = w.cand_scale;
+    gp.tp_ks = sg.ks; gp.tp_rank = sg.r; gp.tp_entries = sg.E; gp.tp_used = sg.used;
+    return run_gemm(d, gp, narrow, s);
+  };
+  auto with_side = [&](GemmParams& gp, int l, int g) {
+    if (!sg.group_on[g]) return;
+    gp.As = w.as; gp.ldas = sg.vt_rows[g];
+    gp.Bs = w.bs[l * 4 + g]; gp.ldbs = sg.bs_cols[g];
+    gp.ks_tile = (int)sg.bs_cols[g];
+  };
+
+  for (int l = 0; l < d.n_layers && M > 0; ++l) {
+    const auto& P = Lo.L[l];
+    // attention block
+    ZO_HIP(launch_norm<T>(w.h, nullptr, M, D, Wf(P[P_LN1W]), Wf(P[P_LN1B]), eps, rms, (T*)w.xa, s));
+    if ((rc = tproj(l, 0, w.xa, D)) != ZO_OK) return rc;
+    {
+      GemmParams gp = gemm_base(w.xa, D, W(P[P_WQ]), D, M, NQKV, D);
+      with_side(gp, l, 0);
+      if (sg.group_on[0]) { gp.n_bounds = 2; gp.bounds[0] = NQ; gp.bounds[1] = NQ + NKV; }
+      gp.epi = EPI_STORE; gp.bias = Wf(P[P_BQ]); gp.C = w.qkv; gp.ldc = NQKV;
+      if ((rc = run_gemm(d, gp, big, s)) != ZO_OK) return rc;
+    }
+    if (!is_opt(d))
+      ZO_HIP(launch_qknorm_rope<T>((T*)w.qkv, M, NQKV, d.n_heads, d.n_kv_heads, d.head_dim, Wf(P[P_QNW]),
+                                   Wf(P[P_KNW]), eps, m->rope, w.row_pos, s));
+    ZO_HIP(launch_attention<T>((const T*)w.qkv, NQKV, (T*)w.attn, NQ, w.phys_cu, pk.n_phys, w.work,
+                               (int)pk.work.size(), d.n_heads, d.n_kv_heads, d.head_dim, s));
+    if ((rc = tproj(l, 1, w.attn, NQ)) != ZO_OK) return rc;
+    {
+      GemmParams gp = gemm_base(w.attn, NQ, W(P[P_WO]), NQ, M, D, NQ);
+      with_side(gp, l, 1);
+      gp.epi = EPI_RESID; gp.bias = Wf(P[P_BO]); gp.H = w.h; gp.ldh = D;
+      if ((rc = run_gemm(d, gp, big, s)) != ZO_OK) return rc;
+    }
+    // FFN block
+    ZO_HIP(launch_norm<T>(w.h, nullptr, M, D, Wf(P[P_LN2W]), Wf(P[P_LN2B]), eps, rms, (T*)w.xa, s));
+    if ((rc = tproj(l, 2, w.xa, D)) != ZO_OK) return rc;
+    {
+      const int N1 = is_opt(d) ? F : 2 * F;
+      GemmParams gp = gemm_base(w.xa, D, W(P[P_W1]), D, M, N1, D);
+      with_side(gp, l, 2);
+      gp.C = w.hid; gp.ldc = F;
+      if (is_opt(d)) { gp.epi = EPI_GELU; gp.bias = Wf(P[P_B1]); }
+      else gp.epi = EPI_SWIGLU;
+      if ((rc = run_gemm(d, gp, big, s)) != ZO_OK) return rc;
+    }
+    if ((rc = tproj(l, 3, w.hid, F)) != ZO_OK) return rc;
+    {
+      const TLoc& w2 = is_opt(d) ? P[P_W2] : P[P_WDOWN];
+      GemmParams gp = gemm_base(w.hid, F, W(w2), F, M, D, F);
+      with_side(gp, l, 3);
+      gp.epi = EPI_RESID; gp.bias = is_opt(d) ? Wf(P[P_B2]) : nullptr; gp.H = w.h; gp.ldh = D;
+      if ((rc = run_gemm(d, gp, big, s)) != ZO_OK) return rc;
+    }
+  }
+  const int S = (int)pk.n_scored;
+  if (S > 0) {
+    ZO_HIP(launch_norm<T>(w.h, w.sc_row, S, D, Wf(Lo.g[G_FNW]), Wf(Lo.g[G_FNB]), eps, rms, (T*)w.xs, s));
+    ZO_HIP(launch_gather_i32(tokens, w.sc_lab_src, S, w.labels, s));
+    const TLoc& head = is_opt(d) ? Lo.g[G_TOK] : Lo.g[G_HEAD];
+    GemmParams gp = gemm_base(w.xs, D, W(head), D, S, d.vocab, D);
+    const int bn = gemm_cfg_bn(GEMM_CFG_HEAD, bf);
+    gp.epi = EPI_LMHEAD; gp.labels = w.labels; gp.part = w.part; gp.lab_logit = w.lab_logit;
+    gp.n_ntiles = (d.vocab + bn - 1) / bn;
+    if ((rc = run_gemm(d, gp, GEMM_CFG_HEAD, s)) != ZO_OK) return rc;
+  }
+  return ZO_OK;
+}
+
+}  // namespace
+
+// =====================================================================================
+extern "C" {
+
+int zo_abi_version(void) { return ZO_ABI_VERSION; }
+const char* zo_last_error(void) { return g_err.c_str(); }
+
+int zo_weights_size(const zo_model_desc* desc, size_t* bytes) {
+  int rc = validate_desc(desc);
+  if (rc) return rc;
+  ZO_CHECK(bytes, ZO_E_INVAL, "null output");
+  *bytes = make_layout(*desc).bytes;
+  return ZO_OK;
+}
+
+int zo_weight_locate(const zo_model_desc* desc, int32_t slot, int32_t param, size_t* offset, int64_t* rows,
+                     int64_t* cols, int32_t* dtype, int32_t* layout) {
+  int rc = validate_desc(desc);
+  if (rc) return rc;
+  ZO_CHECK(offset && rows && cols && dtype && layout, ZO_E_INVAL, "null output");
+  Layout Lo = make_layout(*desc);
+  const TLoc* t = nullptr;
+  if (slot == 0) {
+    ZO_CHECK(param >= 0 && param < N_GLOBAL, ZO_E_INVAL, "bad global param %d", param);
+    t = &Lo.g[param];
+  } else {
+    ZO_CHECK(slot >= 1 && slot <= desc->n_layers, ZO_E_INVAL, "bad slot %d", slot);
+    ZO_CHECK(param >= 0 && param < N_LAYER_PARAMS, ZO_E_INVAL, "bad layer param %d", param);
+    t = &Lo.L[slot - 1][param];
+  }
+  ZO_CHECK(t->present, ZO_E_INVAL, "param %d absent for this architecture", param);
+  *offset = t->off; *rows = t->rows; *cols = t->cols; *dtype = t->dtype; *layout = t->layout;
+  return ZO_OK;
+}
+
+int zo_model_create(const zo_model_desc* desc, void* weights_dev, size_t bytes, zo_model** out) {
+  int rc = validate_desc(desc);
+  if (rc) return rc;
+  ZO_CHECK(weights_dev && out, ZO_E_INVAL, "null argument");
+  Layout Lo = make_layout(*desc);
+  ZO_CHECK(bytes >= Lo.bytes, ZO_E_SHAPE, "weight blob has %zu bytes, needs %zu", bytes, Lo.bytes);
+  zo_model* m = new (std::nothrow) zo_model();
+  ZO_CHECK(m, ZO_E_NOMEM, "out of host memory");
+  m->d = *desc;
+  m->lo = std::move(Lo);
+  m->w = (unsigned char*)weights_dev;
+  m->w_bytes = bytes;
+  if (hipGetDevice(&m->device) != hipSuccess) m->device = 0;
+  if (!is_opt(*desc)) {
+    // RoPE table: inv_freq_i = theta^(-2i/hd); angle = pos * inv_freq_i, in fp64, stored fp32
+    const int half = desc->head_dim / 2;
+    m->rope_len = desc->max_pos;
+    std::vector<float2> tab((size_t)m->rope_len * half);
+    std::vector<double> inv(half);
+    for (int i = 0; i < half; ++i) inv[i] = std::pow(desc->rope_theta, -(2.0 * i) / desc->head_dim);
+    for (int pos = 0; pos < m->rope_len; ++pos)
+      for (int i = 0; i < half; ++i) {
+        const double a = (double)pos * inv[i];
+        tab[(size_t)pos * half + i] = make_float2((float)std::cos(a), (float)std::sin(a));
+      }
+    hipError_t e = hipMalloc((void**)&m->rope, tab.size() * sizeof(float2));
+    if (e == hipSuccess) e = hipMemcpy(m->rope, tab.data(), tab.size() * sizeof(float2), hipMemcpyHostToDevice);
+    if (e != hipSuccess) {
+      if (m->rope) (void)hipFree(m->rope);
+      delete m;
+      return fail(ZO_E_DEVICE, "RoPE table: %s", hipGetErrorString(e));
+    }
+  }
+  *out = m;
+  return ZO_OK;
+}
+
+int zo_model_destroy(zo_model* m) {
+  if (!m) return ZO_OK;
+  if (m->rope) (void)hipFree(m->rope);
+  delete m;
+  return ZO_OK;
+}
+
+int zo_init_weights(zo_model* m, uint64_t seed, void* stream) {
+  ZO_CHECK(m, ZO_E_INVAL, "null model");
+  hipStream_t s = (hipStream_t)stream;
+  std::vector<NormalJob> jobs;
+  int64_t max_blocks = 0;
+  auto add = [&](const TLoc& t, int slot, int param) {
+    if (!t.present) return;
+    NormalJob j;
+    memset(&j, 0, sizeof j);
+    j.dst = m->w + t.off;
+    j.rows = t.rows; j.cols = t.cols; j.ld = t.cols;
+    j.seed = seed; j.tau = 0; j.tag = weight_tag(slot, param);
+    j.mode = t.gain ? 1 : 0;
+    j.dtype = t.dtype == ZO_DTYPE_BF16 ? 1 : 0;
+    j.aux = t.layout;
+    jobs.push_back(j);
+    max_blocks = std::max<int64_t>(max_blocks, (t.rows * t.cols + 3) / 4);
+  };
+  for (int p = 0; p < N_GLOBAL; ++p) add(m->lo.g[p], 0, p);
+  for (int l = 0; l < m->d.n_layers; ++l)
+    for (int p = 0; p < N_LAYER_PARAMS; ++p) add(m->lo.L[l][p], l + 1, p);
+  NormalJob* dj = nullptr;
+  ZO_HIP(hipMalloc((void**)&dj, jobs.size() * sizeof(NormalJob)));
+  hipError_t e = hipMemcpyAsync(dj, jobs.data(), jobs.size() * sizeof(NormalJob), hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = launch_normal_jobs(dj, (int)jobs.size(), max_blocks, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  (void)hipFree(dj);
+  if (e != hipSuccess) return fail(ZO_E_DEVICE, "weight init: %s", hipGetErrorString(e));
+  return ZO_OK;
+}
+
+int zo_plan(const zo_model* m, const zo_plan_desc* desc, zo_plan_t** out) {
+  ZO_CHECK(m && desc && out, ZO_E_INVAL, "null argument");
+  const zo_plan_desc& d = *desc;
+  ZO_CHECK(d.nu >= 1, ZO_E_INVAL, "nu must be >= 1");
+  ZO_CHECK(d.rank >= 1, ZO_E_INVAL, "rank must be >= 1");
+  ZO_CHECK((d.flags & ~(ZO_PLAN_SCALE_INV_SQRT_R | ZO_PLAN_ALLOW_ZERO_EPS)) == 0, ZO_E_INVAL, "unknown plan flag");
+  ZO_CHECK(std::isfinite(d.eps) && (d.eps > 0 || (d.eps == 0 && (d.flags & ZO_PLAN_ALLOW_ZERO_EPS))), ZO_E_INVAL,
+           "eps must be finite and > 0");
+  ZO_CHECK(d.n_dirs >= 1 && d.dir_seeds, ZO_E_INVAL, "need at least one direction");
+  ZO_CHECK(d.n_cand >= 1 && d.cand_dir && d.cand_sign, ZO_E_INVAL, "need at least one candidate");
+  for (int i = 0; i < d.n_dirs; ++i)
+    for (int j = 0; j < i; ++j)
+      ZO_CHECK(d.dir_seeds[i] != d.dir_seeds[j], ZO_E_INVAL, "direction seeds must be distinct");
+  for (int i = 0; i < d.n_cand; ++i) {
+    ZO_CHECK(d.cand_dir[i] >= 0 && d.cand_dir[i] < d.n_dirs, ZO_E_INVAL, "candidate %d: direction out of range",
+             i);
+    ZO_CHECK(d.cand_sign[i] == 1 || d.cand_sign[i] == -1, ZO_E_INVAL, "candidate %d: sign must be +1 or -1", i);
+  }
+  ZO_CHECK((d.target_mask >> n_kinds_of(m->d)) == 0, ZO_E_INVAL, "target mask names a kind this arch lacks");
+  zo_plan_s* p = new (std::nothrow) zo_plan_s();
+  ZO_CHECK(p, ZO_E_NOMEM, "out of host memory");
+  p->md = m->d;
+  p->t = d.step; p->nu = d.nu; p->rank = d.rank; p->eps = d.eps;
+  p->eps_tilde = (d.flags & ZO_PLAN_SCALE_INV_SQRT_R) ? d.eps / std::sqrt((double)d.rank) : d.eps;
+  p->seeds.assign(d.dir_seeds, d.dir_seeds + d.n_dirs);
+  p->cdir.assign(d.cand_dir, d.cand_dir + d.n_cand);
+  p->csign.assign(d.cand_sign, d.cand_sign + d.n_cand);
+  p->mask = d.target_mask;
+  p->flags = d.flags;
+  *out = p;
+  return ZO_OK;
+}
+
+int zo_plan_destroy(zo_plan_t* p) {
+  delete p;
+  return ZO_OK;
+}
+
+int zo_bank_size(const zo_model* m, int32_t n_slots, int32_t rank, uint32_t target_mask, size_t* bytes) {
+  ZO_CHECK(m && bytes, ZO_E_INVAL, "null argument");
+  ZO_CHECK(n_slots >= 1 && rank >= 1, ZO_E_INVAL, "n_slots and rank must be >= 1");
+  ZO_CHECK((target_mask >> n_kinds_of(m->d)) == 0, ZO_E_INVAL, "bad target mask");
+  std::vector<int> kinds;
+  std::vector<int64_t> koff;
+  int64_t ls;
+  bank_geometry(m->d, rank, target_mask, kinds, koff, ls);
+  *bytes = (size_t)n_slots * m->d.n_layers * ls * sizeof(float);
+  return ZO_OK;
+}
+
+int zo_bank_create(const zo_model* m, int32_t n_slots, int32_t rank, uint32_t target_mask, void* u_dev,
+                   size_t bytes, zo_bank** out) {
+  size_t need;
+  int rc = zo_bank_size(m, n_slots, rank, target_mask, &need);
+  if (rc) return rc;
+  ZO_CHECK(out && (u_dev || need == 0), ZO_E_INVAL, "null argument");
+  ZO_CHECK(bytes >= need, ZO_E_SHAPE, "bank memory has %zu bytes, needs %zu", bytes, need);
+  zo_bank* b = new (std::nothrow) zo_bank();
+  ZO_CHECK(b, ZO_E_NOMEM, "out of host memory");
+  b->md = m->d; b->n_slots = n_slots; b->rank = rank; b->mask = target_mask;
+  b->u = (float*)u_dev; b->bytes = bytes;
+  b->seeds.assign(n_slots, 0);
+  b->windows.assign(n_slots, -1);
+  bank_geometry(m->d, rank, target_mask, b->kinds, b->kind_off, b->layer_stride);
+  b->slot_stride = b->layer_stride * m->d.n_layers;
+  *out = b;
+  return ZO_OK;
+}
+
+int zo_bank_destroy(zo_bank* b) {
+  delete b;
+  return ZO_OK;
+}
+
+int zo_bank_keys(const zo_bank* b, uint64_t* seeds, int64_t* windows) {
+  ZO_CHECK(b && seeds && windows, ZO_E_INVAL, "null argument");
+  std::copy(b->seeds.begin(), b->seeds.end(), seeds);
+  std::copy(b->windows.begin(), b->windows.end(), windows);
+  return ZO_OK;
+}
+
+int zo_bank_set_keys(zo_bank* b, const uint64_t* seeds, const int64_t* windows) {
+  ZO_CHECK(b && seeds && windows, ZO_E_INVAL, "null argument");
+  for (int i = 0; i < b->n_slots; ++i) ZO_CHECK(windows[i] >= -1, ZO_E_INVAL, "bad window");
+  b->seeds.assign(seeds, seeds + b->n_slots);
+  b->windows.assign(windows, windows + b->n_slots);
+  return ZO_OK;
+}
+
+int zo_bank_entry_offset(const zo_bank* b, int32_t slot, int32_t layer, int32_t kind, size_t* offset) {
+  ZO_CHECK(b && offset, ZO_E_INVAL, "null argument");
+  ZO_CHECK(slot >= 0 && slot < b->n_slots && layer >= 0 && layer < b->md.n_layers, ZO_E_INVAL, "out of range");
+  for (size_t i = 0; i < b->kinds.size(); ++i)
+    if (b->kinds[i] == kind) {
+      *offset = ((size_t)slot * b->slot_stride + (size_t)layer * b->layer_stride + b->kind_off[i]) * sizeof(float);
+      return ZO_OK;
+    }
+  return fail(ZO_E_INVAL, "kind %d is not a target of this bank", kind);
+}
+
+int zo_batch_layout(const zo_model* m, const zo_plan_t* p, const zo_bank* bank, const zo_batch* b, int32_t* n_phys,
+                    int64_t* n_rows, int64_t* n_scored, size_t* ws_bytes) {
+  ZO_CHECK(m && p, ZO_E_INVAL, "null argument");
+  int rc = validate_batch(m->d, b);
+  if (rc) return rc;
+  Packing pk;
+  build_packing(*p, *b, pk);
+  SideGeom sg;
+  if ((rc = side_geometry(m, *p, bank, sg)) != ZO_OK) return rc;
+  WsPtrs w;
+  carve(m, *p, pk, sg, nullptr, w);
+  if (n_phys) *n_phys = pk.n_phys;
+  if (n_rows) *n_rows = pk.M;
+  if (n_scored) *n_scored = pk.n_scored;
+  if (ws_bytes) *ws_bytes = w.bytes;
+  return ZO_OK;
+}
+
+int zo_pack(const zo_plan_t* p, const zo_batch* b, int32_t* phys_seq, int32_t* phys_cand,
+            int32_t* phys_first_scored) {
+  ZO_CHECK(p && phys_seq && phys_cand && phys_first_scored, ZO_E_INVAL, "null argument");
+  int rc = validate_batch(p->md, b);
+  if (rc) return rc;
+  Packing pk;
+  build_packing(*p, *b, pk);
+  std::copy(pk.phys_seq.begin(), pk.phys_seq.end(), phys_seq);
+  std::copy(pk.phys_cand.begin(), pk.phys_cand.end(), phys_cand);
+  std::copy(pk.phys_first.begin(), pk.phys_first.end(), phys_first_scored);
+  return ZO_OK;
+}
+
+int zo_score(zo_model* m, const zo_plan_t* p, const zo_bank* bank, const zo_batch* b, void* ws_dev,
+             size_t ws_bytes, double* seq_logp_dev, float* tok_logp_dev, double* S_host, void* stream) {
+  ZO_CHECK(m && p && S_host, ZO_E_INVAL, "null argument");
+  int rc = validate_batch(m->d, b);
+  if (rc) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  const zo_model_desc& d = m->d;
+  const bool bf = d.dtype == ZO_DTYPE_BF16;
+  Packing pk;
+  build_packing(*p, *b, pk);
+  SideGeom sg;
+  if ((rc = side_geometry(m, *p, bank, sg)) != ZO_OK) return rc;
+  WsPtrs w;
+  carve(m, *p, pk, sg, nullptr, w);
+  ZO_CHECK(ws_dev && ws_bytes >= w.bytes, ZO_E_SHAPE, "workspace has %zu bytes, needs %zu", ws_bytes, w.bytes);
+  carve(m, *p, pk, sg, ws_dev, w);
+  const int nc = (int)p->cdir.size();
+
+  // ---- host tables -> device
+  std::vector<int32_t> cdir(p->cdir);
+  std::vector<float> cscale(nc);
+  for (int c = 0; c < nc; ++c) cscale[c] = (float)((double)p->csign[c] * p->eps_tilde);
+  auto h2d = [&](void* dst, const void* src, size_t n) -> hipError_t {
+    if (n == 0) return hipSuccess;
+    return hipMemcpyAsync(dst, src, n, hipMemcpyHostToDevice, s);
+  };
+  ZO_HIP(h2d(w.row_src, pk.row_src.data(), pk.row_src.size() * 4));
+  ZO_HIP(h2d(w.row_pos, pk.row_pos.data(), pk.row_pos.size() * 4));
+  ZO_HIP(h2d(w.row_cand, pk.row_cand.data(), pk.row_cand.size() * 4));
+  ZO_HIP(h2d(w.phys_cu, pk.phys_cu.data(), pk.phys_cu.size() * 4));
+  ZO_HIP(h2d(w.phys_first, pk.phys_first.data(), pk.phys_first.size() * 4));
+  ZO_HIP(h2d(w.sc_row, pk.sc_row.data(), pk.sc_row.size() * 4));
+  ZO_HIP(h2d(w.sc_lab_src, pk.sc_lab_src.data(), pk.sc_lab_src.size() * 4));
+  ZO_HIP(h2d(w.work, pk.work.data(), pk.work.size() * 4));
+  ZO_HIP(h2d(w.cand_dir, cdir.data(), cdir.size() * 4));
+  ZO_HIP(h2d(w.cand_scale, cscale.data(), cscale.size() * 4));
+
+  // ---- side factors: V^T rows for the input projections, [U | G] columns for the GEMMs
+  std::vector<SideJob> jobs;
+  int64_t max_items = 0;
+  if (sg.any && pk.M > 0) {
+    const uint64_t win = p->window();
+    const int dt = bf ? 1 : 0;
+    const int64_t NQ = (int64_t)d.n_heads * d.head_dim, NKV = (int64_t)d.n_kv_heads * d.head_dim;
+    ZO_HIP(hipMemsetAsync(w.side_begin, 0, w.side_bytes, s));   // padding rows/columns must be zero
+    for (int l = 0; l < d.n_layers; ++l)
+      for (int g = 0; g < 4; ++g) {
+        if (!sg.group_on[g]) continue;
+        const Group& G = sg.groups[g];
+        const size_t asz = act_size(d);
+        for (size_t kb = 0; kb < G.kinds.size(); ++kb) {
+          const int kind = G.kinds[kb];
+          if (!((p->mask >> kind) & 1u)) continue;
+          const KindShape ksh = kind_shape(d, kind);
+          // V^T rows: block kb of the group's V^T, slot j at rows kb*ks + j*r
+          unsigned char* vt = (unsigned char*)w.vt[l * 4 + g];
+          unsigned char* bs = (unsigned char*)w.bs[l * 4 + g];
+          int64_t row_base = 0;
+          int row_map = 0;
+          int64_t col_base = 0;
+          if (g == 0) row_base = kind == ZO_KIND_Q ? 0 : (kind == ZO_KIND_K ? NQ : NQ + NKV);
+          if (G.interleaved) { row_map = kind == 4 ? 1 : 2; col_base = (int64_t)kb * sg.ks; }
+          for (int j = 0; j < sg.E + sg.q; ++j) {
+            const bool entry = j < sg.E;
+            const uint64_t seed = entry ? bank->seeds[sg.entry_slots[j]] : p->seeds[j - sg.E];
+            const uint64_t vwin = entry ? (uint64_t)bank->windows[sg.entry_slots[j]] : win;
+            SideJob v;
+            memset(&v, 0, sizeof v);
+            v.dst = vt + ((int64_t)kb * sg.ks + (int64_t)j * sg.r) * sg.n_in[g] * asz;
+            v.ld = sg.n_in[g];
+            v.seed = seed; v.tau = vwin; v.tag = dir_tag(l, kind, 1);
+            v.src = 0; v.n = ksh.n_in; v.r = sg.r; v.dtype = dt;
+            jobs.push_back(v);
+            max_items = std::max<int64_t>(max_items, (ksh.n_in * sg.r + 3) / 4);
+            SideJob u;
+            memset(&u, 0, sizeof u);
+            u.dst = bs + row_base * sg.bs_cols[g] * asz;
+            u.ld = sg.bs_cols[g];
+            u.col0 = (int32_t)(col_base + (int64_t)j * sg.r);
+            u.row_map = row_map;
+            u.n = ksh.n_out; u.r = sg.r; u.dtype = dt;
+            if (entry) {
+              size_t off;
+              if ((rc = zo_bank_entry_offset(bank, sg.entry_slots[j], l, kind, &off)) != ZO_OK) return rc;
+              u.src = 2;
+              u.u_src = (const float*)((const unsigned char*)bank->u + off);
+              max_items = std::max<int64_t>(max_items, ksh.n_out * sg.r);
+            } else {
+              u.src = 1;
+              u.seed = seed; u.tau = p->t; u.tag = dir_tag(l, kind, 0);
+              max_items = std::max<int64_t>(max_items, (ksh.n_out * sg.r + 3) / 4);
+            }
+            jobs.push_back(u);
+          }
+        }
+      }
+    ZO_CHECK((int)jobs.size() <= std::max(n_side_jobs(d, *p, sg), 1), ZO_E_SHAPE, "side job table overflow");
+    ZO_HIP(h2d(w.jobs, jobs.data(), jobs.size() * sizeof(SideJob)));
+    ZO_HIP(launch_side_jobs(w.jobs, (int)jobs.size(), max_items, s));
+  }
+
+  // ---- forward, head, reduce
+  if (bf) rc = forward<bf16_t>(m, *p, pk, sg, w, b->tokens_dev, s);
+  else rc = forward<float>(m, *p, pk, sg, w, b->tokens_dev, s);
+  if (rc != ZO_OK) return rc;
+  double* seq_out = seq_logp_dev ? seq_logp_dev : w.seq_logp;
+  const int bn = gemm_cfg_bn(GEMM_CFG_HEAD, bf);
+  ZO_HIP(launch_logp_reduce(w.part, (d.vocab + bn - 1) / bn, w.lab_logit, (int)pk.n_scored, w.phys_first,
+                            pk.n_phys, w.tok64, tok_logp_dev, seq_out, s));
+  std::vector<double> seq(pk.n_phys);
+  if (pk.n_phys > 0)
+    ZO_HIP(hipMemcpyAsync(seq.data(), seq_out, pk.n_phys * sizeof(double), hipMemcpyDeviceToHost, s));
+  ZO_HIP(hipStreamSynchronize(s));
+  for (int c = 0; c < nc; ++c) S_host[c] = 0.0;
+  for (int q = 0; q < pk.n_phys; ++q)
+    if (pk.phys_cand[q] >= 0) S_host[pk.phys_cand[q]] += seq[q];
+  return ZO_OK;
+}
+
+int zo_estimate(const zo_plan_t* p, const double* S_host, const int64_t* n_scored, uint32_t flags,
+                double* c_out) {
+  ZO_CHECK(p && S_host && c_out, ZO_E_INVAL, "null argument");
+  ZO_CHECK((flags & ~(ZO_EST_INV_RANK | ZO_EST_MEAN)) == 0, ZO_E_INVAL, "unknown estimate flag");
+  ZO_CHECK(!(flags & ZO_EST_MEAN) || n_scored, ZO_E_INVAL, "ZO_EST_MEAN needs n_scored");
+  const int nc = (int)p->cdir.size(), q = (int)p->seeds.size();
+  for (int c = 0; c < nc; ++c)
+    ZO_CHECK(std::isfinite(S_host[c]), ZO_E_NONFINITE, "score of candidate %d is not finite", c);
+  std::vector<double> c(q);
+  const double two_eps = 2.0 * p->eps;
+  ZO_CHECK(two_eps > 0, ZO_E_STATE, "eps is zero: the estimate is undefined");
+  for (int dd = 0; dd < q; ++dd) {
+    int ip = -1, im = -1, np = 0, nm = 0;
+    for (int i = 0; i < nc; ++i)
+      if (p->cdir[i] == dd) {
+        if (p->csign[i] > 0) { ip = i; ++np; } else { im = i; ++nm; }
+      }
+    ZO_CHECK(np == 1 && nm == 1, ZO_E_STATE, "direction %d needs exactly one + and one - candidate", dd);
+    double Lp = -S_host[ip], Lm = -S_host[im];
+    if (flags & ZO_EST_MEAN) {
+      ZO_CHECK(n_scored[ip] > 0 && n_scored[im] > 0, ZO_E_INVAL, "n_scored must be > 0");
+      Lp = Lp / (double)n_scored[ip];
+      Lm = Lm / (double)n_scored[im];
+    }
+    double cd = (Lp - Lm) / two_eps;
+    if (flags & ZO_EST_INV_RANK) cd = cd / (double)p->rank;
+    c[dd] = cd;
+  }
+  std::copy(c.begin(), c.end(), c_out);
+  return ZO_OK;
+}
+
+int zo_update(zo_model* m, const zo_plan_t* p, zo_bank* bank, const double* c_host, double lr, void* stream) {
+  ZO_CHECK(m && p && bank && c_host, ZO_E_INVAL, "null argument");
+  ZO_CHECK(std::isfinite(lr), ZO_E_INVAL, "lr must be finite");
+  ZO_CHECK(bank->rank == p->rank && bank->mask == p->mask, ZO_E_STATE, "bank rank/targets differ from the plan's");
+  const int q = (int)p->seeds.size();
+  for (int dd = 0; dd < q; ++dd) ZO_CHECK(std::isfinite(c_host[dd]), ZO_E_NONFINITE, "c[%d] is not finite", dd);
+  hipStream_t s = (hipStream_t)stream;
+  const int64_t win = (int64_t)p->window();
+  // find or allocate each direction's entry (keys change only after every check passed)
+  std::vector<int> slot(q, -1);
+  std::vector<int> fresh(q, 0);
+  std::vector<bool> taken(bank->n_slots, false);
+  for (int dd = 0; dd < q; ++dd)
+    for (int sl = 0; sl < bank->n_slots; ++sl)
+      if (bank->windows[sl] == win && bank->seeds[sl] == p->seeds[dd]) { slot[dd] = sl; taken[sl] = true; }
+  for (int dd = 0; dd < q; ++dd) {
+    if (slot[dd] >= 0) continue;
+    for (int sl = 0; sl < bank->n_slots; ++sl)
+      if (bank->windows[sl] < 0 && !taken[sl]) { slot[dd] = sl; taken[sl] = true; fresh[dd] = 1; break; }
+    ZO_CHECK(slot[dd] >= 0, ZO_E_NOMEM, "bank has no free slot for direction %d window %lld", dd, (long long)win);
+  }
+  UpdateArgs a;
+  memset(&a, 0, sizeof a);
+  a.u_base = bank->u;
+  a.layer_stride = bank->layer_stride;
+  a.n_kinds = (int)bank->kinds.size();
+  int64_t max_n = 0;
+  for (int i = 0; i < a.n_kinds; ++i) {
+    a.kind_id[i] = bank->kinds[i];
+    a.kind_off[i] = bank->kind_off[i];
+    a.kind_n[i] = kind_shape(m->d, bank->kinds[i]).n_out * bank->rank;
+    max_n = std::max(max_n, a.kind_n[i]);
+  }
+  a.t = p->t;
+  for (int d0 = 0; d0 < q; d0 += ZO_MAX_UPDATE_DIRS) {
+    a.n_dirs = std::min(ZO_MAX_UPDATE_DIRS, q - d0);
+    for (int i = 0; i < a.n_dirs; ++i) {
+      const int dd = d0 + i;
+      a.seed[i] = p->seeds[dd];
+      a.slot_off[i] = (int64_t)slot[dd] * bank->slot_stride;
+      a.coef[i] = (lr / (double)q) * c_host[dd];
+      a.fresh[i] = fresh[dd];
+    }
+    ZO_HIP(launch_update(a, m->d.n_layers, max_n, s));
+  }
+  for (int dd = 0; dd < q; ++dd) {
+    bank->seeds[slot[dd]] = p->seeds[dd];
+    bank->windows[slot[dd]] = win;
+  }
+  return ZO_OK;
+}
+
+int zo_philox_words(uint64_t seed, uint32_t tag, uint64_t tau, int64_t first_block, int64_t n_blocks,
+                    uint32_t* out_dev, void* stream) {
+  ZO_CHECK(n_blocks >= 0 && first_block >= 0 && (out_dev || n_blocks == 0), ZO_E_INVAL, "bad argument");
+  ZO_CHECK(first_block + n_blocks <= ((int64_t)1 << 32), ZO_E_INVAL, "block index beyond 2^32");
+  ZO_HIP(launch_words_fill(seed, tag, tau, first_block, n_blocks, out_dev, (hipStream_t)stream));
+  return ZO_OK;
+}
+
+int zo_normal_fill(uint64_t seed, uint32_t tag, uint64_t tau, int64_t first, int64_t n, double* out_dev,
+                   void* stream) {
+  ZO_CHECK(n >= 0 && first >= 0 && (out_dev || n == 0), ZO_E_INVAL, "bad argument");
+  ZO_CHECK(first + n <= ((int64_t)1 << 34), ZO_E_INVAL, "element index beyond 2^34");
+  ZO_HIP(launch_normal_fill_f64(seed, tag, tau, first, n, out_dev, (hipStream_t)stream));
+  return ZO_OK;
+}
+
+int zo_direction(const zo_model* m, const zo_plan_t* p, int32_t dir, int32_t layer, int32_t kind, int32_t which,
+                 float* out_dev, void* stream) {
+  ZO_CHECK(m && p && out_dev, ZO_E_INVAL, "null argument");
+  ZO_CHECK(dir >= 0 && dir < (int)p->seeds.size(), ZO_E_INVAL, "direction out of range");
+  ZO_CHECK(layer >= 0 && layer < m->d.n_layers, ZO_E_INVAL, "layer out of range");
+  ZO_CHECK(kind >= 0 && kind < n_kinds_of(m->d), ZO_E_INVAL, "kind out of range");
+  ZO_CHECK(which == 0 || which == 1, ZO_E_INVAL, "which must be 0 (G) or 1 (V)");
+  const KindShape ks = kind_shape(m->d, kind);
+  SideJob j;
+  memset(&j, 0, sizeof j);
+  j.dst = out_dev;
+  j.seed = p->seeds[dir];
+  j.tau = which == 0 ? p->t : p->window();
+  j.tag = dir_tag(layer, kind, which);
+  j.n = which == 0 ? ks.n_out : ks.n_in;
+  j.r = p->rank;
+  ZO_HIP(launch_stream_rowmajor(j, (hipStream_t)stream));
+  return ZO_OK;
+}
+
+}  // extern "C"
