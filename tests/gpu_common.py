@@ -19,7 +19,8 @@ def flush(msg):
 
 
 SMALL_OPT_BF16 = ModelCfg("opt", 2, 256, 4, 4, 64, 512, 1000, 512, "bf16", 1e-5)
-SMALL_QWEN_BF16 = ModelCfg("qwen3", 2, 256, 4, 2, 64, 512, 1200, 1024, "bf16", 1e-6, 1e6)
+# kind boundaries of the packed QKV (q | k | v) fall on 256-column tiles, as in the real shapes
+SMALL_QWEN_BF16 = ModelCfg("qwen3", 2, 512, 4, 2, 128, 768, 1200, 1024, "bf16", 1e-6, 1e6)
 SMALL_QWEN_F32 = ModelCfg("qwen3", 2, 128, 4, 2, 32, 256, 300, 1024, "f32", 1e-6, 1e6)
 
 

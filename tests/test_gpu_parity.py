@@ -20,10 +20,14 @@ from .gpu_common import (SMALL_OPT_BF16, SMALL_QWEN_BF16, SMALL_QWEN_F32, GpuRun
 pytestmark = pytest.mark.gpu
 
 
-def _seq_close(gpu, ref, atol):
+def _seq_close(gpu, ref, atol, probes_only=True):
+    """Per physical sequence.  The bound applies to candidate (probe) sequences, whose
+    sums make up L+/-; foreground sequences are checked per token by the callers."""
     g = gpu["seq_logp"].cpu().numpy()
     r = ref["seq_logp"]
     err = np.abs(g - r)
+    if probes_only:
+        err = np.where(np.array([c >= 0 for _, c in ref["phys"]]), err, 0.0)
     assert np.all(err <= atol), "max |err| %.3g at %d (gpu %.6f oracle %.6f)" % (
         err.max(), err.argmax(), g[err.argmax()], r[err.argmax()])
     return err.max()
@@ -71,12 +75,16 @@ def test_small_models_with_bank_and_ragged_rows(cfg):
         o.update(t, c_fixed[0 if t == 0 else (1 if t == 3 else 2)], 5e-3)
     flush("score %s" % cfg.arch)
     gs, os_ = g.score(6, batch), o.score(6, batch)
-    tol = 1e-4 if cfg.dtype == "f32" else 2e-2
-    err = _seq_close(gs, os_, tol * (50 if cfg.dtype == "f32" else 1))
-    flush("max per-sequence |err| %.3g" % err)
+    if cfg.dtype == "f32":      # relative bound, every sequence
+        g_ = gs["seq_logp"].cpu().numpy()
+        err = np.max(np.abs(g_ - os_["seq_logp"]) / np.abs(os_["seq_logp"]))
+        assert err <= 1e-4, err
+    else:
+        err = _seq_close(gs, os_, 2e-2)
+    flush("max per-sequence err %.3g" % err)
     if cfg.dtype == "f32":
         assert np.all(np.abs(gs["S"] - os_["S"]) <= 1e-4 * np.abs(os_["S"]))
-    # per-token agreement on the foreground (ALL_NEXT) rows
+    # per-token agreement on every scored row (foreground rows score ALL_NEXT)
     tok = gs["tok_logp"].cpu().numpy()
     first = 0
     for p, (li, c) in enumerate(os_["phys"]):
@@ -117,13 +125,17 @@ def test_eps_zero_and_sign_swap_and_repeatability():
     b = g.score(1, batch)
     assert np.array_equal(a["S"], b["S"])
     assert np.array_equal(a["seq_logp"].cpu().numpy(), b["seq_logp"].cpu().numpy())
-    # the same candidates listed in the other order: c changes sign exactly
+    # the same candidates listed in the other order: every sequence lands elsewhere in the
+    # packed batch, yet each candidate's score is bitwise the same (row results do not
+    # depend on their position); exchanging the two scores negates c exactly
     import zeroth_order_fine_amd as zo
     p1 = g.plan(1)
     p2 = zo.Plan(g.model, 1, wl.nu, wl.rank, wl.eps, wl.dir_seeds, ((0, -1), (0, 1)), wl.targets)
     s1 = zo.score(g.model, p1, g.bank, zo.DeviceBatch(batch))["S"]
     s2 = zo.score(g.model, p2, g.bank, zo.DeviceBatch(batch))["S"]
-    assert np.array_equal(zo.estimate(p1, s1), -zo.estimate(p2, s2))
+    assert np.array_equal(s1, s2[::-1])
+    assert np.array_equal(zo.estimate(p1, s1), zo.estimate(p2, s2))
+    assert np.array_equal(zo.estimate(p1, s1[::-1]), -zo.estimate(p1, s1))
 
 
 def test_empty_and_foreground_only_batches():
@@ -133,7 +145,9 @@ def test_empty_and_foreground_only_batches():
     g, o = GpuRun(wl), OracleRun(wl)
     gs, os_ = g.score(0, batch), o.score(0, batch)
     assert np.all(gs["S"] == 0.0)
-    _seq_close(gs, os_, 2e-2)
+    tok = gs["tok_logp"].cpu().numpy()
+    ref = np.concatenate([os_["tok_logp"][p] for p in range(len(os_["phys"]))])
+    assert np.max(np.abs(tok - ref)) <= 2e-2
     empty = batch.subset([])
     ge = g.score(0, empty)
     assert ge["n_phys"] == 0 and np.all(ge["S"] == 0.0)
@@ -151,7 +165,7 @@ def test_high_rank_multi_direction():
     g.update(0, c, 2e-3)
     o.update(0, c, 2e-3)
     gs, os_ = g.score(1, batch), o.score(1, batch)
-    err = _seq_close(gs, os_, 2e-2 * 4)
+    err = _seq_close(gs, os_, 2e-2)
     flush("r=64 max per-sequence |err| %.3g over %d tokens" % (err, len(os_["tok_logp"][0])))
     tok = gs["tok_logp"].cpu().numpy()
     allref = np.concatenate([os_["tok_logp"][p] for p in range(len(os_["phys"]))])

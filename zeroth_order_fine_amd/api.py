@@ -135,10 +135,11 @@ class Plan:
         self.h = h
 
     @classmethod
-    def from_workload(cls, model, wl, t=0, **kw):
-        flags = PLAN_SCALE_INV_SQRT_R if wl.scale_inv_sqrt_r else 0
-        return cls(model, t, wl.nu, wl.rank, wl.eps, wl.dir_seeds, wl.candidates, wl.targets,
-                   kw.pop("flags", flags), **kw)
+    def from_workload(cls, model, wl, t=0, eps=None, flags=None, candidates=None):
+        if flags is None:
+            flags = PLAN_SCALE_INV_SQRT_R if wl.scale_inv_sqrt_r else 0
+        return cls(model, t, wl.nu, wl.rank, wl.eps if eps is None else eps, wl.dir_seeds,
+                   wl.candidates if candidates is None else candidates, wl.targets, flags)
 
     def close(self):
         if self.h:

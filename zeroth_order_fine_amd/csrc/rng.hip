@@ -44,7 +44,9 @@ __device__ __forceinline__ double ln_exact(double u) {
 #pragma clang fp contract(off)
   int e;
   double m = frexp(u, &e);
-  if (m < 0x1.6a09e667f3bcdp-1) { m = m * 2.0; e = e - 1; }
+  const int below = m < 0x1.6a09e667f3bcdp-1;
+  m = below ? m * 2.0 : m;
+  e = e - below;
   double s = (m - 1.0) / (m + 1.0);
   double s2 = s * s;
   double p = 1.0 / 23.0;
@@ -89,23 +91,32 @@ __device__ __forceinline__ double cos_q(double x) {
   return p;
 }
 
+__device__ __forceinline__ double flip_sign(double x, uint32_t neg) {
+  return __builtin_bit_cast(double, __builtin_bit_cast(uint64_t, x) ^ ((uint64_t)neg << 63));
+}
+
+// Branch-free selection: every case computes the same operations, then picks
+// bits, so the rotation by the quadrant is exact sign flips and swaps.
+__device__ __forceinline__ double pick(uint32_t cond, double a, double b) {   // cond ? a : b
+  const uint64_t m = 0ull - (uint64_t)(cond & 1u);
+  return __builtin_bit_cast(double, (__builtin_bit_cast(uint64_t, a) & m) | (__builtin_bit_cast(uint64_t, b) & ~m));
+}
+
 __device__ __forceinline__ void box_muller(uint32_t wa, uint32_t wb, double& za, double& zb) {
 #pragma clang fp contract(off)
   double u = ((double)wa + 0.5) * 0x1p-32;
   double l = ln_exact(u);
   double m2 = -2.0 * l;
   double R = __builtin_sqrt(m2);
-  uint32_t quad = wb >> 30;
-  uint32_t h = (wb >> 29) & 1u;
+  const uint32_t quad = wb >> 30;
+  const uint32_t h = (wb >> 29) & 1u;
   double f = ((double)(wb & 0x1FFFFFFFu) + 0.5) * 0x1p-29;
   double phi = f * 0x1.921fb54442d18p-1;
   double c = cos_q(phi), s = sin_q(phi);
-  double cp = h ? s : c, sp = h ? c : s;
-  double ct, st;
-  if (quad == 0) { ct = cp; st = sp; }
-  else if (quad == 1) { ct = -sp; st = cp; }
-  else if (quad == 2) { ct = -cp; st = -sp; }
-  else { ct = sp; st = -cp; }
+  const double cp = pick(h, s, c), sp = pick(h, c, s);          // psi = pi/2 - phi when h
+  const double x = pick(quad, sp, cp), y = pick(quad, cp, sp);  // odd quadrant: swap
+  const double ct = flip_sign(x, ((quad + 1) >> 1) & 1u);       // negative in quadrants 1, 2
+  const double st = flip_sign(y, quad >> 1);                    // negative in quadrants 2, 3
   za = R * ct;
   zb = R * st;
 }
