@@ -1,0 +1,199 @@
+#!/usr/bin/env python3
+"""Throughput of the inference-native ZO step on one MI355X.
+
+A step is the whole hot path on one batch: zo_plan (ProbePlan for step t),
+zo_score (one batched forward over every candidate state with the fused
+vocabulary log-softmax + label gather), zo_estimate and zo_update (lazy
+low-rank bank update), with t advancing.  Default workload: the OPT-13B-shaped
+batch-64 configuration (40 layers, d 5120, FFN 20480, vocab 50272, bf16
+random-init weights resident in HBM, 64 ragged prompts of U[16,128] tokens,
+LoZO rank 2 on every linear, 2 candidates, persistent bank).
+
+Prints one JSON line.  `value` = probe token rows scored per second over the
+whole step (sum of the lengths of every probe physical sequence / step time).
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "ZO probe scored tokens/sec + ZO steps/sec (OPT-13B shape, batch 64, 1 GPU)"
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_F32_TFLOPS = 157.3
+PEAK_HBM_GBS = 8000.0
+
+
+def base_gemm_flops(cfg, rows):
+    """Algorithmic FLOPs of the shared-weight projections for `rows` token rows."""
+    total = 0
+    for kind in cfg.kind_names:
+        n_out, n_in = cfg.linear_shape(kind)
+        total += 2 * rows * n_out * n_in
+    return total * cfg.n_layers
+
+
+def describe(wl):
+    m = wl.model
+    return ("%s: %s-shaped %d x d%d, heads %d/%d x %d, FFN %d, vocab %d, %s weights; %d prompts U[%d,%d]%s, "
+            "%d candidates (%d directions x +-), r=%d on %s, eps=%g" % (
+                wl.name, m.arch.upper(), m.n_layers, m.d_model, m.n_heads, m.n_kv_heads, m.head_dim, m.d_ffn,
+                m.vocab, m.dtype, wl.n_prompts, wl.len_lo, wl.len_hi,
+                (" + %d foreground" % wl.n_fg) if wl.n_fg else "", len(wl.candidates), wl.n_dirs, wl.rank,
+                ",".join(wl.targets), wl.eps))
+
+
+def cpu_baseline(wl, batch):
+    """Time the oracle (as it stands) on a bounded sample: the first probe prompt under
+    every candidate, through one decoder layer plus the vocabulary head; the per-token
+    rate for the whole model is extrapolated as n_layers x layer time + head time."""
+    import numpy as np
+
+    from oracle import model as om
+    from oracle import params
+    from oracle import zo as ozo
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    cfg = wl.model
+    t0 = time.perf_counter()
+    W = ozo.Weights(cfg, wl.model_seed, cache_layers=True)
+    G = W.get_global()
+    W0 = W.get_layer(0)
+    t_gen = time.perf_counter() - t0
+    plan = ozo.plan_from_workload(wl, 0)
+    phys = ozo.pack(batch, plan)
+    first_probe = [i for i in range(batch.n_seq) if batch.role[i] == 0][0]
+    sample = [(li, c) for li, c in phys if li == first_probe]
+    hs, sides, toks = [], [], []
+    for li, c in sample:
+        t = np.asarray(batch.tokens[li], np.int64)
+        toks.append(t)
+        hs.append(om.embed(cfg, G, t))
+        sides.append(ozo.side_terms(cfg, plan, None, c))
+    t1 = time.perf_counter()
+    outs = [om.layer_forward(cfg, W0, h, lambda kind, s=s: s(0, kind), False) for h, s in zip(hs, sides)]
+    t_layer = time.perf_counter() - t1
+    t2 = time.perf_counter()
+    for h, t, (li, c) in zip(outs, toks, sample):
+        pos, lab = ozo.scored_positions(t, int(batch.score_mode[li]))
+        om.final_logprobs(cfg, G, h, pos, lab)
+    t_head = time.perf_counter() - t2
+    rows = sum(len(t) for t in toks)
+    est = cfg.n_layers * t_layer + t_head
+    return {"value": rows / est, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": ("prompt %d (%d tokens) under all %d candidates through layer 0 of %d and the head; "
+                       "layer %.2f s, head %.2f s, extrapolated x%d layers; oracle weight generation for the "
+                       "sample %.1f s not counted" % (first_probe, len(toks[0]), len(sample), cfg.n_layers,
+                                                      t_layer, t_head, cfg.n_layers, t_gen))}
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--workload", default="opt13b")
+    ap.add_argument("--lr", type=float, default=1e-4)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py: this build runs on exactly one GPU (got --gpus %d); a multi-GPU run is not "
+              "provided" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import zeroth_order_fine_amd as zo
+    from synth import configs, inputs
+
+    wl = configs.CONFIGS[args.workload]
+    cfg = wl.model
+    torch.cuda.set_device(0)
+    model = zo.Model(cfg)
+    model.init_weights(wl.model_seed)
+    batch = inputs.make_batch(wl)
+    db = zo.DeviceBatch(batch)
+    bank = zo.Bank(model, 2 * wl.n_dirs, wl.rank, wl.targets)
+    torch.cuda.synchronize()
+
+    score_s = [0.0]
+
+    def step(t):
+        plan = zo.Plan.from_workload(model, wl, t=t)
+        a = time.perf_counter()
+        out = zo.score(model, plan, bank, db)
+        score_s[0] += time.perf_counter() - a
+        c = zo.estimate(plan, out["S"])
+        zo.update(model, plan, bank, c, args.lr)
+        return out
+
+    out = None
+    for t in range(args.warmup):
+        out = step(t)
+    torch.cuda.synchronize()
+    score_s[0] = 0.0
+    zo.api.profile_begin()
+    t0 = time.perf_counter()
+    for k in range(args.steps):
+        out = step(args.warmup + k)
+    torch.cuda.synchronize()
+    elapsed = time.perf_counter() - t0
+    prof = zo.api.profile_end()
+
+    phys = zo.pack(model, zo.Plan.from_workload(model, wl, t=0), db)
+    lengths = batch.lengths
+    probe_tokens = int(sum(lengths[li] for li, c in zip(phys[0], phys[1]) if c >= 0))
+    fg_tokens = int(sum(lengths[li] for li, c in zip(phys[0], phys[1]) if c < 0))
+    rows = probe_tokens + fg_tokens
+    ms_step = elapsed / args.steps * 1e3
+    value = probe_tokens / (ms_step / 1e3)
+
+    n_base, ms_base = prof["gemm_base"]
+    flops_step = base_gemm_flops(cfg, rows)
+    launches_per_step = n_base / args.steps
+    avg_launch_ms = ms_base / max(n_base, 1)
+    achieved = (flops_step / launches_per_step) / (avg_launch_ms / 1e3) / 1e12 if n_base else None
+    peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
+    line = {
+        "metric": METRIC,
+        "value": round(value, 1),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 3),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {"workload": describe(wl), "prompts": wl.n_prompts, "candidates": len(wl.candidates),
+                   "rank": wl.rank, "probe_tokens_per_step": probe_tokens, "foreground_tokens_per_step": fg_tokens,
+                   "scored_positions_per_step": int(out["n_scored"])},
+        "steps_per_s": round(args.steps / elapsed, 4),
+        "score_only_tokens_per_s": round(probe_tokens * args.steps / score_s[0], 1),
+        "score_share_of_step": round(score_s[0] / elapsed, 4),
+        "roofline": {"kernel": "gemm_base (shared-weight projections, bf16 MFMA)" if cfg.dtype == "bf16"
+                     else "gemm_base (fp32 VALU)",
+                     "bound": "mfma", "achieved": round(achieved, 1) if achieved else None, "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4) if achieved else None, "traffic": None,
+                     "launches_per_step": launches_per_step, "avg_launch_ms": round(avg_launch_ms, 4),
+                     "algorithmic_gflop_per_step": round(flops_step / 1e9, 1)},
+        "breakdown_ms_per_step": {k: round(v[1] / args.steps, 3) for k, v in prof.items()},
+        "launches_per_step": {k: v[0] / args.steps for k, v in prof.items()},
+    }
+    if not args.no_cpu_baseline:
+        line["cpu_baseline"] = cpu_baseline(wl, batch)
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -233,6 +233,24 @@ int zo_normal_fill(uint64_t seed, uint32_t tag, uint64_t tau, int64_t first, int
 int zo_direction(const zo_model* m, const zo_plan_t* p, int32_t dir, int32_t layer, int32_t kind, int32_t which,
                  float* out_dev, void* stream);
 
+/* ---- per-kernel-class timing (measurement) ---------------------------------------
+ * zo_profile_begin enables timing: every kernel launch of zo_score / zo_update is
+ * bracketed by HIP events on the launch stream, per class below.  zo_profile_end
+ * disables it, waits for the recorded events and writes, for each of the first
+ * n_classes classes, the number of launches and their summed duration (ms).
+ * Events come from a pool owned by the library (created on first use). */
+enum { ZO_PROF_GEMM_BASE = 0,   /* shared-weight projections (qkv, o, fc1/gate-up, fc2/down) */
+       ZO_PROF_GEMM_SIDE = 1,   /* side-input projections t = x [V...] */
+       ZO_PROF_GEMM_HEAD = 2,   /* vocabulary head + fused log-softmax partials */
+       ZO_PROF_ATTENTION = 3,
+       ZO_PROF_NORM = 4,        /* embedding, LayerNorm/RMSNorm, QK-norm + RoPE */
+       ZO_PROF_SIDE_PREP = 5,   /* regeneration of the G/V factors and bank packing */
+       ZO_PROF_REDUCE = 6,      /* log-prob combine and per-sequence sums */
+       ZO_PROF_UPDATE = 7,
+       ZO_PROF_N_CLASSES = 8 };
+int zo_profile_begin(void);
+int zo_profile_end(int32_t n_classes, int64_t* counts, double* total_ms);
+
 #ifdef __cplusplus
 }
 #endif

@@ -52,6 +52,8 @@ _SIGS = {
     "zo_philox_words": (c_i32, [c_u64, c_u32, c_u64, c_i64, c_i64, c_vp, c_vp]),
     "zo_normal_fill": (c_i32, [c_u64, c_u32, c_u64, c_i64, c_i64, c_vp, c_vp]),
     "zo_direction": (c_i32, [c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp]),
+    "zo_profile_begin": (c_i32, []),
+    "zo_profile_end": (c_i32, [c_i32, P(c_i64), P(c_dbl)]),
 }
 
 EXPORTED = tuple(_SIGS)

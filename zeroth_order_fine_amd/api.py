@@ -274,3 +274,19 @@ def direction(model, plan, dir_index, layer, kind_name, which):
     out = torch.empty(n * plan.rank, dtype=torch.float32, device=model.weights.device)
     _check(model.L.zo_direction(model.h, plan.h, dir_index, layer, kind, which, _ptr(out), _stream()))
     return out.view(n, plan.rank)
+
+
+PROFILE_CLASSES = ("gemm_base", "gemm_side", "gemm_head", "attention", "norm", "side_prep", "reduce", "update")
+
+
+def profile_begin():
+    _check(_lib.load().zo_profile_begin())
+
+
+def profile_end():
+    """{class: (launches, total ms)} for the launches since profile_begin."""
+    n = len(PROFILE_CLASSES)
+    counts = (ctypes.c_int64 * n)()
+    ms = (ctypes.c_double * n)()
+    _check(_lib.load().zo_profile_end(n, counts, ms))
+    return {k: (counts[i], ms[i]) for i, k in enumerate(PROFILE_CLASSES)}

@@ -45,6 +45,43 @@ int fail(int code, const char* fmt, ...) {
     if (!(cond)) return fail(code, __VA_ARGS__);  \
   } while (0)
 
+// ---- launch timing (zo_profile_begin / zo_profile_end) -------------------------
+struct Prof {
+  bool on = false;
+  std::vector<hipEvent_t> pool;
+  size_t used = 0;
+  struct Rec { int cls; size_t ev; };
+  std::vector<Rec> recs;
+};
+Prof g_prof;
+
+// Records the start event of a launch of class `cls`; returns the record index or -1.
+long prof_start(int cls, hipStream_t s) {
+  if (!g_prof.on) return -1;
+  if (g_prof.used + 2 > g_prof.pool.size()) {
+    for (int i = 0; i < 256; ++i) {
+      hipEvent_t e;
+      if (hipEventCreate(&e) != hipSuccess) return -1;
+      g_prof.pool.push_back(e);
+    }
+  }
+  const size_t ev = g_prof.used;
+  g_prof.used += 2;
+  if (hipEventRecord(g_prof.pool[ev], s) != hipSuccess) return -1;
+  g_prof.recs.push_back({cls, ev});
+  return (long)g_prof.recs.size() - 1;
+}
+void prof_stop(long rec, hipStream_t s) {
+  if (rec < 0) return;
+  (void)hipEventRecord(g_prof.pool[g_prof.recs[rec].ev + 1], s);
+}
+struct ProfScope {
+  long rec;
+  hipStream_t s;
+  ProfScope(int cls, hipStream_t st) : rec(prof_start(cls, st)), s(st) {}
+  ~ProfScope() { prof_stop(rec, s); }
+};
+
 inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
 inline int64_t round_up(int64_t v, int64_t a) { return (v + a - 1) / a * a; }
 
@@ -469,6 +506,8 @@ int check_i32(int64_t elems, const char* what) {
 }
 
 int run_gemm(const zo_model_desc& d, const GemmParams& gp, int cfg, hipStream_t s) {
+  ProfScope ps(cfg == GEMM_CFG_BIG ? ZO_PROF_GEMM_BASE : (cfg == GEMM_CFG_NARROW ? ZO_PROF_GEMM_SIDE : ZO_PROF_GEMM_HEAD),
+               s);
   if (d.dtype == ZO_DTYPE_BF16) {
     const int bn = gemm_cfg_bn(cfg, true);
     for (int i = 0; i < gp.n_bounds; ++i)
@@ -517,6 +556,7 @@ int forward(zo_model* m, const zo_plan_s& p, const Packing& pk, const SideGeom& 
   int rc;
 
   if (M > 0) {
+    ProfScope ps(ZO_PROF_NORM, s);
     if (bf)
       ZO_HIP(launch_embed_t<bf16_t>((const bf16_t*)W(Lo.g[G_TOK]), (const bf16_t*)W(Lo.g[G_POS]), tokens,
                                     w.row_src, w.row_pos, M, D, d.vocab, w.h, s));
@@ -544,7 +584,10 @@ int forward(zo_model* m, const zo_plan_s& p, const Packing& pk, const SideGeom& 
   for (int l = 0; l < d.n_layers && M > 0; ++l) {
     const auto& P = Lo.L[l];
     // attention block
-    ZO_HIP(launch_norm<T>(w.h, nullptr, M, D, Wf(P[P_LN1W]), Wf(P[P_LN1B]), eps, rms, (T*)w.xa, s));
+    {
+      ProfScope ps(ZO_PROF_NORM, s);
+      ZO_HIP(launch_norm<T>(w.h, nullptr, M, D, Wf(P[P_LN1W]), Wf(P[P_LN1B]), eps, rms, (T*)w.xa, s));
+    }
     if ((rc = tproj(l, 0, w.xa, D)) != ZO_OK) return rc;
     {
       GemmParams gp = gemm_base(w.xa, D, W(P[P_WQ]), D, M, NQKV, D);
@@ -553,11 +596,16 @@ int forward(zo_model* m, const zo_plan_s& p, const Packing& pk, const SideGeom& 
       gp.epi = EPI_STORE; gp.bias = Wf(P[P_BQ]); gp.C = w.qkv; gp.ldc = NQKV;
       if ((rc = run_gemm(d, gp, big, s)) != ZO_OK) return rc;
     }
-    if (!is_opt(d))
+    if (!is_opt(d)) {
+      ProfScope ps(ZO_PROF_NORM, s);
       ZO_HIP(launch_qknorm_rope<T>((T*)w.qkv, M, NQKV, d.n_heads, d.n_kv_heads, d.head_dim, Wf(P[P_QNW]),
                                    Wf(P[P_KNW]), eps, m->rope, w.row_pos, s));
-    ZO_HIP(launch_attention<T>((const T*)w.qkv, NQKV, (T*)w.attn, NQ, w.phys_cu, pk.n_phys, w.work,
-                               (int)pk.work.size(), d.n_heads, d.n_kv_heads, d.head_dim, s));
+    }
+    {
+      ProfScope ps(ZO_PROF_ATTENTION, s);
+      ZO_HIP(launch_attention<T>((const T*)w.qkv, NQKV, (T*)w.attn, NQ, w.phys_cu, pk.n_phys, w.work,
+                                 (int)pk.work.size(), d.n_heads, d.n_kv_heads, d.head_dim, s));
+    }
     if ((rc = tproj(l, 1, w.attn, NQ)) != ZO_OK) return rc;
     {
       GemmParams gp = gemm_base(w.attn, NQ, W(P[P_WO]), NQ, M, D, NQ);
@@ -566,7 +614,10 @@ int forward(zo_model* m, const zo_plan_s& p, const Packing& pk, const SideGeom& 
       if ((rc = run_gemm(d, gp, big, s)) != ZO_OK) return rc;
     }
     // FFN block
-    ZO_HIP(launch_norm<T>(w.h, nullptr, M, D, Wf(P[P_LN2W]), Wf(P[P_LN2B]), eps, rms, (T*)w.xa, s));
+    {
+      ProfScope ps(ZO_PROF_NORM, s);
+      ZO_HIP(launch_norm<T>(w.h, nullptr, M, D, Wf(P[P_LN2W]), Wf(P[P_LN2B]), eps, rms, (T*)w.xa, s));
+    }
     if ((rc = tproj(l, 2, w.xa, D)) != ZO_OK) return rc;
     {
       const int N1 = is_opt(d) ? F : 2 * F;
@@ -588,8 +639,11 @@ int forward(zo_model* m, const zo_plan_s& p, const Packing& pk, const SideGeom& 
   }
   const int S = (int)pk.n_scored;
   if (S > 0) {
-    ZO_HIP(launch_norm<T>(w.h, w.sc_row, S, D, Wf(Lo.g[G_FNW]), Wf(Lo.g[G_FNB]), eps, rms, (T*)w.xs, s));
-    ZO_HIP(launch_gather_i32(tokens, w.sc_lab_src, S, w.labels, s));
+    {
+      ProfScope ps(ZO_PROF_NORM, s);
+      ZO_HIP(launch_norm<T>(w.h, w.sc_row, S, D, Wf(Lo.g[G_FNW]), Wf(Lo.g[G_FNB]), eps, rms, (T*)w.xs, s));
+      ZO_HIP(launch_gather_i32(tokens, w.sc_lab_src, S, w.labels, s));
+    }
     const TLoc& head = is_opt(d) ? Lo.g[G_TOK] : Lo.g[G_HEAD];
     GemmParams gp = gemm_base(w.xs, D, W(head), D, S, d.vocab, D);
     const int bn = gemm_cfg_bn(GEMM_CFG_HEAD, bf);
@@ -940,6 +994,7 @@ int zo_score(zo_model* m, const zo_plan_t* p, const zo_bank* bank, const zo_batc
       }
     ZO_CHECK((int)jobs.size() <= std::max(n_side_jobs(d, *p, sg), 1), ZO_E_SHAPE, "side job table overflow");
     ZO_HIP(h2d(w.jobs, jobs.data(), jobs.size() * sizeof(SideJob)));
+    ProfScope ps(ZO_PROF_SIDE_PREP, s);
     ZO_HIP(launch_side_jobs(w.jobs, (int)jobs.size(), max_items, s));
   }
 
@@ -949,8 +1004,11 @@ int zo_score(zo_model* m, const zo_plan_t* p, const zo_bank* bank, const zo_batc
   if (rc != ZO_OK) return rc;
   double* seq_out = seq_logp_dev ? seq_logp_dev : w.seq_logp;
   const int bn = gemm_cfg_bn(GEMM_CFG_HEAD, bf);
+  ProfScope ps_red(ZO_PROF_REDUCE, s);
   ZO_HIP(launch_logp_reduce(w.part, (d.vocab + bn - 1) / bn, w.lab_logit, (int)pk.n_scored, w.phys_first,
                             pk.n_phys, w.tok64, tok_logp_dev, seq_out, s));
+  prof_stop(ps_red.rec, s);
+  ps_red.rec = -1;
   std::vector<double> seq(pk.n_phys);
   if (pk.n_phys > 0)
     ZO_HIP(hipMemcpyAsync(seq.data(), seq_out, pk.n_phys * sizeof(double), hipMemcpyDeviceToHost, s));
@@ -1036,12 +1094,36 @@ int zo_update(zo_model* m, const zo_plan_t* p, zo_bank* bank, const double* c_ho
       a.coef[i] = (lr / (double)q) * c_host[dd];
       a.fresh[i] = fresh[dd];
     }
+    ProfScope ps(ZO_PROF_UPDATE, s);
     ZO_HIP(launch_update(a, m->d.n_layers, max_n, s));
   }
   for (int dd = 0; dd < q; ++dd) {
     bank->seeds[slot[dd]] = p->seeds[dd];
     bank->windows[slot[dd]] = win;
   }
+  return ZO_OK;
+}
+
+int zo_profile_begin(void) {
+  g_prof.on = true;
+  g_prof.used = 0;
+  g_prof.recs.clear();
+  return ZO_OK;
+}
+
+int zo_profile_end(int32_t n_classes, int64_t* counts, double* total_ms) {
+  ZO_CHECK(n_classes >= 0 && n_classes <= ZO_PROF_N_CLASSES && (n_classes == 0 || (counts && total_ms)),
+           ZO_E_INVAL, "bad argument");
+  g_prof.on = false;
+  for (int c = 0; c < n_classes; ++c) { counts[c] = 0; total_ms[c] = 0.0; }
+  for (const auto& r : g_prof.recs) {
+    ZO_HIP(hipEventSynchronize(g_prof.pool[r.ev + 1]));
+    float ms = 0.f;
+    ZO_HIP(hipEventElapsedTime(&ms, g_prof.pool[r.ev], g_prof.pool[r.ev + 1]));
+    if (r.cls < n_classes) { counts[r.cls] += 1; total_ms[r.cls] += ms; }
+  }
+  g_prof.recs.clear();
+  g_prof.used = 0;
   return ZO_OK;
 }
 
