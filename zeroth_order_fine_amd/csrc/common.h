@@ -36,6 +36,7 @@ enum GemmEpi {
   EPI_RESID = 3,    // H (fp32) += acc + bias
   EPI_TPROJ = 4,    // side-input builder: columns of x.[V...] scattered by candidate
   EPI_LMHEAD = 5,   // per row and column tile: (max, sum exp) and the label logit
+  EPI_PARTIAL = 6,  // split-K: fp32 partial sums of one K-slice (blockIdx.z) to `partial`
 };
 
 struct GemmParams {
@@ -66,6 +67,9 @@ struct GemmParams {
   float2* part;               // [M x n_ntiles]
   float* lab_logit;           // [M]
   int n_ntiles;
+  // split-K (EPI_PARTIAL): K-slice z covers base K-steps [z*ksteps_per_split, ...)
+  int ksplit;
+  float* partial;             // [ksplit x M x N]
 };
 
 // Launch on `stream`; returns hipSuccess or the launch error.
@@ -75,6 +79,7 @@ enum GemmCfg { GEMM_CFG_BIG = 0, GEMM_CFG_NARROW = 1, GEMM_CFG_HEAD = 2 };
 int gemm_cfg_bn(int cfg, bool bf16);
 int gemm_cfg_bm(int cfg, bool bf16);
 int gemm_bk(bool bf16);
+int gemm_cfg_bk(int cfg, bool bf16);
 
 // ---- random streams ---------------------------------------------------------
 struct NormalJob {     // one generated tensor (or factor) written in a given layout
@@ -145,6 +150,7 @@ template <>
 hipError_t launch_attention<float>(const float* qkv, int ld_qkv, float* out, int ld_out, const int32_t* cu,
                                    int n_seq, const int32_t* work, int n_work, int hq, int hkv, int hd,
                                    hipStream_t s);
+hipError_t launch_tproj_reduce(const GemmParams& p, hipStream_t s);
 hipError_t launch_gather_i32(const int32_t* src, const int32_t* idx, int n, int32_t* dst, hipStream_t s);
 hipError_t launch_logp_reduce(const float2* part, int n_tiles, const float* lab_logit, int n_scored,
                               const int32_t* seq_first, int n_phys, double* tok_logp64, float* tok_logp32,

@@ -98,6 +98,22 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, floatx4_t (&acc)[T
       }
     return;
   }
+  if constexpr (epi == EPI_PARTIAL) {
+    float* out = p.partial + (int64_t)blockIdx.z * p.M * p.N;
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        const int r = rbase + i * 16 + q;
+        if (r >= p.M) continue;
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          const int c = cbase + j * 16;
+          if (c < p.N) out[(int64_t)r * p.N + c] = acc[i][j][q];
+        }
+      }
+    return;
+  }
   if constexpr (epi == EPI_SWIGLU) {
     // packed rows: 16 gate rows then 16 up rows; output column = gate index
 #pragma unroll
@@ -196,10 +212,16 @@ gemm_bf16_kernel(GemmParams p) {
   const int grp = (p.n_bounds > 0 && n0 >= p.bounds[0]) + (p.n_bounds > 1 && n0 >= p.bounds[1]) +
                   (p.n_bounds > 2 && n0 >= p.bounds[2]);
   const int a_side_off = grp * p.ks_tile;
-  const int nkb = p.K / BK, nk = nkb + p.ks_tile / BK;
-
+  int nkb = p.K / BK, nk = nkb + p.ks_tile / BK;
   const bf16_t* Ab = (const bf16_t*)p.A;
   const bf16_t* Bb = (const bf16_t*)p.B;
+  if constexpr (EPI == EPI_PARTIAL) {       // K-slice of this workgroup (no side path)
+    const int per = nkb / p.ksplit;
+    Ab += (int64_t)blockIdx.z * per * BK;
+    Bb += (int64_t)blockIdx.z * per * BK;
+    nkb = per;
+    nk = per;
+  }
   const bf16_t* Asb = (const bf16_t*)p.As;
   const bf16_t* Bsb = (const bf16_t*)p.Bs;
 
@@ -279,6 +301,125 @@ gemm_bf16_kernel(GemmParams p) {
   epilogue<EPI, TM, TN, BM, BN, WM, WN, bf16_t>(p, acc, m0, n0, nt, wm, wn, lane, (float*)smem_raw);
 #undef ZO_GLOAD
 #undef ZO_SSTORE
+}
+
+// ------------------------------------------------------------------------------
+// bf16 MFMA kernel for the shared-weight projections.
+//
+// 256 x 256 tile, eight waves (two per SIMD) of 128 x 64, K-steps of 32.  Tiles
+// are streamed global -> LDS with direct-to-LDS loads (no register staging) into
+// a ring of NSL stages, issued NSL - 1 stages ahead; the fragments of stage
+// kt + 1 are read from LDS while the MFMAs of stage kt run, interleaved one LDS
+// read per few MFMAs.  Within a 1 KB block (16 rows x 32 k) lane L of the load
+// writes row L/4, 16-byte chunk L%4, which holds logical chunk (L%4) ^ ((row/4)%4):
+// the fragment reads (16 rows, one chunk) are then free of bank conflicts.
+template <int BM, int BN, int WM, int WN, int NSL, int EPI>
+__global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
+gemm_bf16_pipe_kernel(GemmParams p) {
+  constexpr int BK = 32;
+  constexpr int NWM = BM / WM, NWN = BN / WN, NW = NWM * NWN;
+  constexpr int TM = WM / 16, TN = WN / 16;
+  constexpr int STAGE = (BM + BN) * BK;              // elements per stage
+  constexpr int ABLK = BM / 16, BBLK = BN / 16;      // 1 KB blocks per stage
+  constexpr int IA = ABLK / NW, IB = BBLK / NW;      // direct loads per wave per stage
+  static_assert(IA * NW == ABLK && IB * NW == BBLK, "blocks per wave");
+  static_assert(NSL >= 3, "the fragment pipeline needs three stages");
+  extern __shared__ __align__(16) unsigned char smem_raw[];
+  bf16_t* sm = (bf16_t*)smem_raw;
+
+  const int n_mt = (p.M + BM - 1) / BM, n_nt = (p.N + BN - 1) / BN;
+  int logical;
+  tile_swizzle(blockIdx.x, n_mt * n_nt, logical);
+  const int mt = logical % n_mt, nt = logical / n_mt;
+  const int m0 = mt * BM, n0 = nt * BN;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wm = wave / NWN, wn = wave % NWN;
+  const int grp = (p.n_bounds > 0 && n0 >= p.bounds[0]) + (p.n_bounds > 1 && n0 >= p.bounds[1]) +
+                  (p.n_bounds > 2 && n0 >= p.bounds[2]);
+  const int a_side_off = grp * p.ks_tile;
+  const int nkb = p.K / BK, nk = nkb + p.ks_tile / BK;
+  const bf16_t* Ab = (const bf16_t*)p.A;
+  const bf16_t* Bb = (const bf16_t*)p.B;
+  const bf16_t* Asb = (const bf16_t*)p.As;
+  const bf16_t* Bsb = (const bf16_t*)p.Bs;
+
+  const int lrow = lane >> 2;
+  const int lch = (lane & 3) ^ ((lrow >> 2) & 3);
+  int arow[IA], brow[IB];
+  static_for<0, IA>([&](auto i) { arow[i] = min(m0 + (wave * IA + i) * 16 + lrow, p.M - 1); });
+  static_for<0, IB>([&](auto i) { brow[i] = min(n0 + (wave * IB + i) * 16 + lrow, p.N - 1); });
+  const int lda = (int)p.lda, ldb = (int)p.ldb, ldas = (int)p.ldas, ldbs = (int)p.ldbs;
+
+  auto issue = [&](int s, int slot) {
+    bf16_t* sA = sm + slot * STAGE;
+    bf16_t* sB = sA + BM * BK;
+    const bool side = s >= nkb;
+    const bf16_t* ga = side ? Asb : Ab;
+    const bf16_t* gb = side ? Bsb : Bb;
+    const int la = side ? ldas : lda, lb = side ? ldbs : ldb;
+    const int kb = (side ? (s - nkb) : s) * BK + lch * 8;
+    const int ka = kb + (side ? a_side_off : 0);
+    static_for<0, IA>([&](auto i) {
+      __builtin_amdgcn_global_load_lds((const void*)(ga + (arow[i] * la + ka)),
+                                       (__attribute__((address_space(3))) void*)(sA + (wave * IA + i) * 16 * BK),
+                                       16, 0, 0);
+    });
+    static_for<0, IB>([&](auto i) {
+      __builtin_amdgcn_global_load_lds((const void*)(gb + (brow[i] * lb + kb)),
+                                       (__attribute__((address_space(3))) void*)(sB + (wave * IB + i) * 16 * BK),
+                                       16, 0, 0);
+    });
+  };
+  const int lr = lane & 15, lk = lane >> 4;
+  int aro[TM], bro[TN];
+  static_for<0, TM>([&](auto i) {
+    const int row = wm * WM + i * 16 + lr;
+    aro[i] = row * BK + ((lk ^ ((row >> 2) & 3)) << 3);
+  });
+  static_for<0, TN>([&](auto j) {
+    const int row = wn * WN + j * 16 + lr;
+    bro[j] = BM * BK + row * BK + ((lk ^ ((row >> 2) & 3)) << 3);
+  });
+  bf16x8_t fa[2][TM], fb[2][TN];
+  auto rd = [&](int slot, auto set) {
+    const bf16_t* base = sm + slot * STAGE;
+    static_for<0, TM>([&](auto i) { fa[set][i] = *(const bf16x8_t*)(base + aro[i]); });
+    static_for<0, TN>([&](auto j) { fb[set][j] = *(const bf16x8_t*)(base + bro[j]); });
+  };
+  floatx4_t acc[TM][TN];
+  static_for<0, TM>([&](auto i) {
+    static_for<0, TN>([&](auto j) { acc[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f}; });
+  });
+  auto mm = [&](auto set) {
+    static_for<0, TM>([&](auto i) {
+      static_for<0, TN>([&](auto j) {
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[set][i], fb[set][j], acc[i][j], 0, 0, 0);
+      });
+    });
+  };
+  // prologue: stages 0 .. NSL-2 in flight; wait for stage 0 in every wave
+  static_for<0, NSL - 1>([&](auto s) { issue(min((int)s, nk - 1), s); });
+  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"((NSL - 2) * (IA + IB)) : "memory");
+  rd(0, std::integral_constant<int, 0>{});
+  for (int kt0 = 0; kt0 < nk; kt0 += 2) {
+    static_for<0, 2>([&](auto j) {
+      const int kt = kt0 + j;
+      if (kt < nk) {
+        // stage kt+1 has landed in every wave's part (its loads are NSL-2 stages old);
+        // the barrier also retires every read of the slot refilled below
+        asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"((NSL - 3) * (IA + IB)) : "memory");
+        issue(min(kt + NSL - 1, nk - 1), (kt + NSL - 1) % NSL);
+        rd((kt + 1) % NSL, std::integral_constant<int, 1 - j>{});
+        mm(j);
+        static_for<0, TM + TN>([&](auto) {
+          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                        // one LDS read
+          __builtin_amdgcn_sched_group_barrier(0x008, (TM * TN) / (TM + TN), 0);   // then MFMAs
+        });
+      }
+    });
+  }
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no LDS write outlives the workgroup
+  epilogue<EPI, TM, TN, BM, BN, WM, WN, bf16_t>(p, acc, m0, n0, nt, wm, wn, lane, (float*)smem_raw);
 }
 
 // ------------------------------------------------------------------------------
@@ -362,7 +503,24 @@ hipError_t launch_bf16(const GemmParams& p, hipStream_t s) {
     attr_set = true;
   }
   const int tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, EPI>), dim3(tiles), dim3(NT), smem, s, p);
+  const int z = EPI == EPI_PARTIAL ? p.ksplit : 1;
+  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, EPI>), dim3(tiles, 1, z), dim3(NT), smem, s, p);
+  return hipGetLastError();
+}
+
+template <int BM, int BN, int WM, int WN, int NSL, int EPI>
+hipError_t launch_bf16_pipe(const GemmParams& p, hipStream_t s) {
+  constexpr int NT = (BM / WM) * (BN / WN) * 64;
+  const size_t smem = (size_t)NSL * (BM + BN) * 32 * sizeof(bf16_t);
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)gemm_bf16_pipe_kernel<BM, BN, WM, WN, NSL, EPI>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  const int tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
+  hipLaunchKernelGGL((gemm_bf16_pipe_kernel<BM, BN, WM, WN, NSL, EPI>), dim3(tiles), dim3(NT), smem, s, p);
   return hipGetLastError();
 }
 
@@ -374,35 +532,79 @@ hipError_t launch_f32(const GemmParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
+// Sum the K-slices in order and apply the side-input epilogue (see EPI_TPROJ).
+template <typename TAct>
+__global__ void tproj_reduce_kernel(GemmParams p) {
+  const int64_t n = (int64_t)p.M * p.N;
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n; e += (int64_t)gridDim.x * blockDim.x) {
+    const int r = (int)(e / p.N), c = (int)(e - (int64_t)r * p.N);
+    float v = 0.f;
+    for (int z = 0; z < p.ksplit; ++z) v += p.partial[(int64_t)z * n + e];
+    const int cand = p.row_cand[r];
+    const int w = c % p.tp_ks;
+    float o = 0.f;
+    if (cand >= 0 && w < p.tp_used) {
+      const int slot = w / p.tp_rank;
+      if (slot < p.tp_entries) o = v;
+      else if (slot - p.tp_entries == p.cand_dir[cand]) o = p.cand_scale[cand] * v;
+    }
+    ((TAct*)p.C)[(int64_t)r * p.ldc + c] = from_f32<TAct>(o);
+  }
+}
+
 }  // namespace
+
+hipError_t launch_tproj_reduce(const GemmParams& p, hipStream_t s) {
+  const int64_t n = (int64_t)p.M * p.N;
+  if (n <= 0) return hipSuccess;
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  hipLaunchKernelGGL(tproj_reduce_kernel<bf16_t>, dim3((unsigned)blocks), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
 
 // Tile shapes per call site.  BIG: the shared-weight projections; NARROW: the
 // side-input projection (N = a few kind blocks); HEAD: the vocabulary head
 // (few rows, many columns).
 int gemm_cfg_bm(int cfg, bool bf16) {
   if (!bf16) return 64;
-  return cfg == GEMM_CFG_HEAD ? 128 : 256;
+  return cfg == GEMM_CFG_BIG ? 256 : (cfg == GEMM_CFG_NARROW ? 64 : 128);
 }
 int gemm_cfg_bn(int cfg, bool bf16) {
   if (!bf16) return 64;
-  return cfg == GEMM_CFG_BIG ? 256 : (cfg == GEMM_CFG_NARROW ? 64 : 128);
+  return cfg == GEMM_CFG_BIG ? 256 : 128;
 }
-int gemm_bk(bool bf16) { return bf16 ? BK_BF16 : BK_F32; }
+// K granularity of each call site: the pipelined projection kernel steps K by 32,
+// the register-staged kernels by 64.
+int gemm_cfg_bk(int cfg, bool bf16) {
+  if (!bf16) return BK_F32;
+  return cfg == GEMM_CFG_BIG ? 32 : BK_BF16;
+}
+// side-input column granularity (a multiple of every consumer's K-step)
+int gemm_bk(bool bf16) { return bf16 ? 32 : BK_F32; }
 
 hipError_t gemm_launch_bf16(const GemmParams& p, int cfg, hipStream_t s) {
   if (p.M <= 0 || p.N <= 0) return hipSuccess;
   if (cfg == GEMM_CFG_BIG) {
     switch (p.epi) {
-      case EPI_STORE: return launch_bf16<256, 256, 128, 128, EPI_STORE>(p, s);
-      case EPI_GELU: return launch_bf16<256, 256, 128, 128, EPI_GELU>(p, s);
-      case EPI_SWIGLU: return launch_bf16<256, 256, 128, 128, EPI_SWIGLU>(p, s);
-      case EPI_RESID: return launch_bf16<256, 256, 128, 128, EPI_RESID>(p, s);
+      case EPI_STORE: return launch_bf16_pipe<256, 256, 128, 64, 4, EPI_STORE>(p, s);
+      case EPI_GELU: return launch_bf16_pipe<256, 256, 128, 64, 4, EPI_GELU>(p, s);
+      case EPI_SWIGLU: return launch_bf16_pipe<256, 256, 128, 64, 4, EPI_SWIGLU>(p, s);
+      case EPI_RESID: return launch_bf16_pipe<256, 256, 128, 64, 4, EPI_RESID>(p, s);
       default: return hipErrorInvalidValue;
     }
   }
   if (cfg == GEMM_CFG_NARROW) {
-    if (p.epi == EPI_TPROJ) return launch_bf16<256, 64, 64, 64, EPI_TPROJ>(p, s);
-    if (p.epi == EPI_STORE) return launch_bf16<256, 64, 64, 64, EPI_STORE>(p, s);
+    if (p.epi == EPI_TPROJ) {
+      if (p.ksplit <= 1) return launch_bf16<64, 128, 32, 64, EPI_TPROJ>(p, s);
+      // split-K partial sums, then a fixed-order reduction that applies the epilogue
+      GemmParams q = p;
+      q.epi = EPI_PARTIAL;
+      hipError_t e = launch_bf16<64, 128, 32, 64, EPI_PARTIAL>(q, s);
+      if (e != hipSuccess) return e;
+      return launch_tproj_reduce(p, s);
+    }
+    if (p.epi == EPI_STORE) return launch_bf16<64, 128, 32, 64, EPI_STORE>(p, s);
     return hipErrorInvalidValue;
   }
   if (p.epi == EPI_LMHEAD) return launch_bf16<128, 128, 64, 64, EPI_LMHEAD>(p, s);

@@ -431,11 +431,21 @@ struct WsPtrs {
   std::vector<void*> vt, bs;   // per layer*4 + group
   unsigned char* side_begin = nullptr;
   size_t side_bytes = 0;
+  float* tp_partial;
   float2* part;
   float* lab_logit;
   double *tok64, *seq_logp;
   size_t bytes;
 };
+
+// K-split of the side-input projection: only for the narrow case (one column tile),
+// chosen from N and K alone so that a row's result never depends on the batch.
+int tproj_split(const zo_model_desc& d, int64_t n_cols, int64_t k) {
+  if (d.dtype != ZO_DTYPE_BF16 || n_cols == 0 || n_cols > 128) return 1;
+  int s = 8;
+  while (s > 1 && (k % (64 * s) != 0 || k / (64 * s) < 8)) s >>= 1;
+  return s;
+}
 
 size_t act_size(const zo_model_desc& d) { return d.dtype == ZO_DTYPE_BF16 ? 2 : 4; }
 
@@ -490,6 +500,11 @@ void carve(const zo_model* m, const zo_plan_s& p, const Packing& pk, const SideG
   w.side_begin = base ? (unsigned char*)base + side0 : nullptr;
   w.side_bytes = b.off - side0;
   w.xs = b.take<unsigned char>(S * D * as);
+  {
+    int64_t np = 0;
+    for (int g = 0; g < 4; ++g) np = std::max(np, (int64_t)tproj_split(d, sg.vt_rows[g], sg.n_in[g]) * sg.vt_rows[g]);
+    w.tp_partial = b.take<float>(std::max<int64_t>(np * M, 1));
+  }
   const int bn_head = gemm_cfg_bn(GEMM_CFG_HEAD, d.dtype == ZO_DTYPE_BF16);
   const int64_t n_vt = (d.vocab + bn_head - 1) / bn_head;
   w.part = b.take<float2>(S * n_vt);
@@ -513,7 +528,9 @@ int run_gemm(const zo_model_desc& d, const GemmParams& gp, int cfg, hipStream_t 
     for (int i = 0; i < gp.n_bounds; ++i)
       ZO_CHECK(gp.bounds[i] % bn == 0, ZO_E_SHAPE, "kind boundary %d not a multiple of the %d-column tile",
                gp.bounds[i], bn);
-    ZO_CHECK(gp.K % gemm_bk(true) == 0 && gp.ks_tile % gemm_bk(true) == 0, ZO_E_SHAPE, "K not a multiple of 64");
+    const int bk = gemm_cfg_bk(cfg, true);
+    ZO_CHECK(gp.K % bk == 0 && gp.ks_tile % bk == 0, ZO_E_SHAPE, "K (%d) or side K (%d) not a multiple of %d", gp.K,
+             gp.ks_tile, bk);
     int rc;
     if ((rc = check_i32((int64_t)gp.M * gp.lda, "A")) != ZO_OK) return rc;
     if ((rc = check_i32((int64_t)gp.N * gp.ldb, "B")) != ZO_OK) return rc;
@@ -572,6 +589,8 @@ int forward(zo_model* m, const zo_plan_s& p, const Packing& pk, const SideGeom& 
     gp.C = w.as; gp.ldc = sg.vt_rows[g];
     gp.row_cand = w.row_cand; gp.cand_dir = w.cand_dir; gp.cand_scale = w.cand_scale;
     gp.tp_ks = sg.ks; gp.tp_rank = sg.r; gp.tp_entries = sg.E; gp.tp_used = sg.used;
+    gp.ksplit = tproj_split(d, sg.vt_rows[g], K);
+    gp.partial = w.tp_partial;
     return run_gemm(d, gp, narrow, s);
   };
   auto with_side = [&](GemmParams& gp, int l, int g) {
