@@ -330,7 +330,15 @@ gemm_bf16_pipe_kernel(GemmParams p) {
   const int n_mt = (p.M + BM - 1) / BM, n_nt = (p.N + BN - 1) / BN;
   int logical;
   tile_swizzle(blockIdx.x, n_mt * n_nt, logical);
-  const int mt = logical % n_mt, nt = logical / n_mt;
+  // groups of GM m-tiles, column-major inside a group: the ~32 tiles an XCD runs at
+  // once share a few A and B panels, so each K-step's chunks are fetched into its L2
+  // once and reused
+  constexpr int GM = 4;
+  const int per_group = GM * n_nt;
+  const int g = logical / per_group, gm0 = g * GM;
+  const int gsize = min(GM, n_mt - gm0);
+  const int in_g = logical - g * per_group;
+  const int mt = gm0 + in_g % gsize, nt = in_g / gsize;
   const int m0 = mt * BM, n0 = nt * BN;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wm = wave / NWN, wn = wave % NWN;
@@ -411,9 +419,10 @@ gemm_bf16_pipe_kernel(GemmParams p) {
         issue(min(kt + NSL - 1, nk - 1), (kt + NSL - 1) % NSL);
         rd((kt + 1) % NSL, std::integral_constant<int, 1 - j>{});
         mm(j);
+        __builtin_amdgcn_sched_group_barrier(0x020, IA + IB, 0);                   // the direct loads
         static_for<0, TM + TN>([&](auto) {
+          __builtin_amdgcn_sched_group_barrier(0x008, (TM * TN) / (TM + TN), 0);   // MFMAs on ready fragments
           __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                        // one LDS read
-          __builtin_amdgcn_sched_group_barrier(0x008, (TM * TN) / (TM + TN), 0);   // then MFMAs
         });
       }
     });
