@@ -28,6 +28,38 @@ PEAK_F32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 
 
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "opt13b_gemm_base_traffic.md")
+GEMM_SOURCE = os.path.join(ROOT, "zeroth_order_fine_amd", "csrc", "gemm.hip")
+
+
+def measured_traffic(workload):
+    """HBM bytes per projection launch from the committed rocprofv3 PMC summary, if it
+    was taken on the current GEMM source (else None)."""
+    import hashlib
+    import re
+    try:
+        text = open(TRAFFIC_FILE).read()
+        rec = json.loads(re.search(r"```json\n(.*?)\n```", text, re.S).group(1))
+        sha = hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest()
+    except Exception:
+        return None
+    if rec.get("gemm_source_sha256") != sha or rec.get("workload") != workload:
+        return None
+    return rec.get("traffic_bytes_per_launch")
+
+
+def copy_calibration():
+    """A plain device copy of known size, for scaling the FETCH_SIZE / WRITE_SIZE counters."""
+    import torch
+    n = 1 << 30
+    a = torch.empty(n, dtype=torch.uint8, device="cuda").fill_(1)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_bytes_read_per_launch": n, "copy_bytes_written_per_launch": n, "launches": 3}))
+
+
 def base_gemm_flops(cfg, rows):
     """Algorithmic FLOPs of the shared-weight projections for `rows` token rows."""
     total = 0
@@ -102,7 +134,12 @@ def main():
     ap.add_argument("--workload", default="opt13b")
     ap.add_argument("--lr", type=float, default=1e-4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a 1 GiB device copy (counter calibration for the traffic figure)")
     args = ap.parse_args()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1:
         print("bench.py: this build runs on exactly one GPU (got --gpus %d); a multi-GPU run is not "
               "provided" % args.gpus, file=sys.stderr)
@@ -184,7 +221,8 @@ def main():
         "roofline": {"kernel": "gemm_base (shared-weight projections, bf16 MFMA)" if cfg.dtype == "bf16"
                      else "gemm_base (fp32 VALU)",
                      "bound": "mfma", "achieved": round(achieved, 1) if achieved else None, "peak": peak,
-                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4) if achieved else None, "traffic": None,
+                     "unit": "TFLOP/s", "frac": round(achieved / peak, 4) if achieved else None,
+                     "traffic": measured_traffic(args.workload),
                      "launches_per_step": launches_per_step, "avg_launch_ms": round(avg_launch_ms, 4),
                      "algorithmic_gflop_per_step": round(flops_step / 1e9, 1)},
         "breakdown_ms_per_step": {k: round(v[1] / args.steps, 3) for k, v in prof.items()},

@@ -133,13 +133,15 @@ def _kind_id(cfg, kind):
 def side_terms(cfg, plan, bank, cand):
     """side(layer, kind) -> [(V, B)] for a physical sequence with candidate `cand`."""
     r, w = plan.rank, plan.window
-    cache = {}
+    cache = {}          # factors of the layer being processed only (layers run in order)
 
     def side(layer, kind):
         if cand < 0 or kind not in plan.targets:
             return []
         key = (layer, kind)
         if key not in cache:
+            for k in [k for k in cache if k[0] != layer]:
+                del cache[k]
             kid = _kind_id(cfg, kind)
             n_out, n_in = cfg.linear_shape(kind)
             terms = []
