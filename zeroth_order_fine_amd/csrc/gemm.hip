@@ -304,6 +304,62 @@ gemm_bf16_kernel(GemmParams p) {
 }
 
 // ------------------------------------------------------------------------------
+// Epilogue of the projection kernel, whose MFMAs take the weight fragment as the
+// first operand: acc[i][j][q] is C[m][n] with m = i*16 + (lane & 15) and
+// n = j*16 + 4*(lane >> 4) + q inside the wave tile, so every lane owns four
+// consecutive output columns and writes them with one 8-byte (bf16) or 16-byte
+// (fp32 residual) access.
+template <int EPI, int TM, int TN, int WM, int WN>
+__device__ __forceinline__ void epilogue_rows(const GemmParams& p, floatx4_t (&acc)[TM][TN], int m0, int n0, int wm,
+                                              int wn, int lane) {
+  const int rb = m0 + wm * WM + (lane & 15);
+  const int cb = n0 + wn * WN + 4 * (lane >> 4);
+  if constexpr (EPI == EPI_SWIGLU) {
+    // packed rows: blocks of 16 gate rows then 16 up rows; output column = gate index
+    const int ob = (n0 + wn * WN) / 2 + 4 * (lane >> 4);
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int r = rb + i * 16;
+      if (r >= p.M) continue;
+#pragma unroll
+      for (int jp = 0; jp < TN / 2; ++jp) {
+        const floatx4_t g = acc[i][2 * jp], u = acc[i][2 * jp + 1];
+        uint32_t w0 = (uint32_t)f32_to_bf16(silu(g[0]) * u[0]) | ((uint32_t)f32_to_bf16(silu(g[1]) * u[1]) << 16);
+        uint32_t w1 = (uint32_t)f32_to_bf16(silu(g[2]) * u[2]) | ((uint32_t)f32_to_bf16(silu(g[3]) * u[3]) << 16);
+        *(uint2*)((bf16_t*)p.C + (int64_t)r * p.ldc + ob + jp * 16) = make_uint2(w0, w1);
+      }
+    }
+    return;
+  } else {
+    floatx4_t bias[TN];
+#pragma unroll
+    for (int j = 0; j < TN; ++j)
+      bias[j] = p.bias ? *(const floatx4_t*)(p.bias + cb + j * 16) : floatx4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int r = rb + i * 16;
+      if (r >= p.M) continue;
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        floatx4_t v = acc[i][j] + bias[j];
+        if constexpr (EPI == EPI_RESID) {
+          floatx4_t* hp = (floatx4_t*)(p.H + (int64_t)r * p.ldh + cb + j * 16);
+          *hp = *hp + v;
+        } else {
+          if constexpr (EPI == EPI_GELU) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) v[q] = gelu_erf(v[q]);
+          }
+          uint32_t w0 = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+          uint32_t w1 = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+          *(uint2*)((bf16_t*)p.C + (int64_t)r * p.ldc + cb + j * 16) = make_uint2(w0, w1);
+        }
+      }
+    }
+  }
+}
+
+// ------------------------------------------------------------------------------
 // bf16 MFMA kernel for the shared-weight projections.
 //
 // 256 x 256 tile, eight waves (two per SIMD) of 128 x 64, K-steps of 32.  Tiles
@@ -401,7 +457,7 @@ gemm_bf16_pipe_kernel(GemmParams p) {
   auto mm = [&](auto set) {
     static_for<0, TM>([&](auto i) {
       static_for<0, TN>([&](auto j) {
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fa[set][i], fb[set][j], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[set][j], fa[set][i], acc[i][j], 0, 0, 0);
       });
     });
   };
@@ -428,7 +484,7 @@ gemm_bf16_pipe_kernel(GemmParams p) {
     });
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no LDS write outlives the workgroup
-  epilogue<EPI, TM, TN, BM, BN, WM, WN, bf16_t>(p, acc, m0, n0, nt, wm, wn, lane, (float*)smem_raw);
+  epilogue_rows<EPI, TM, TN, WM, WN>(p, acc, m0, n0, wm, wn, lane);
 }
 
 // ------------------------------------------------------------------------------

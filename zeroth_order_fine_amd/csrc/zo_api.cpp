@@ -529,6 +529,8 @@ int run_gemm(const zo_model_desc& d, const GemmParams& gp, int cfg, hipStream_t 
       ZO_CHECK(gp.bounds[i] % bn == 0, ZO_E_SHAPE, "kind boundary %d not a multiple of the %d-column tile",
                gp.bounds[i], bn);
     const int bk = gemm_cfg_bk(cfg, true);
+    ZO_CHECK(cfg != GEMM_CFG_BIG || (gp.N % 16 == 0 && gp.ldc % 4 == 0 && gp.ldh % 4 == 0), ZO_E_SHAPE,
+             "projection N must be a multiple of 16");
     ZO_CHECK(gp.K % bk == 0 && gp.ks_tile % bk == 0, ZO_E_SHAPE, "K (%d) or side K (%d) not a multiple of %d", gp.K,
              gp.ks_tile, bk);
     int rc;
