@@ -170,3 +170,51 @@ def test_high_rank_multi_direction():
     tok = gs["tok_logp"].cpu().numpy()
     allref = np.concatenate([os_["tok_logp"][p] for p in range(len(os_["phys"]))])
     assert np.max(np.abs(tok - allref)) <= 2e-2
+
+
+def test_multi_step_trajectory_with_window_rollover():
+    """Eight steps of score -> estimate -> update with nu = 4 (two windows: the
+    bank gains a second entry at t = 4 and the first stays as a frozen term).  The
+    oracle applies the GPU's c, so both states stay identical; S and c are checked at
+    every step and the bank keys and factors at the end."""
+    need_gpu()
+    wl = configs.CONFIGS["tiny"].with_(nu=4)
+    batch = inputs.make_batch(wl)
+    g, o = GpuRun(wl, n_slots=3), OracleRun(wl, n_slots=3)
+    for t in range(8):
+        gs, os_ = g.score(t, batch), o.score(t, batch)
+        assert np.all(np.abs(gs["S"] - os_["S"]) <= 1e-4 * np.abs(os_["S"])), (t, gs["S"], os_["S"])
+        cg = g.zo.estimate(g.plan(t), gs["S"])
+        co = ozo.estimate(ozo.plan_from_workload(wl, t), os_["S"])
+        assert np.all(np.abs(cg - co) <= 1e-2 * np.abs(co)), (t, cg, co)
+        g.update(t, cg, 1e-2)
+        o.update(t, cg, 1e-2)
+    seeds, windows = g.bank.keys()
+    assert sorted(w for w in windows if w >= 0) == [0, 1]
+    for slot, e in enumerate(o.bank.entries):
+        if e is None:
+            continue
+        gslot = [i for i in range(3) if windows[i] == e.window][0]
+        for (layer, kind), U in e.U.items():
+            assert np.array_equal(g.bank.entry(gslot, layer, kind).cpu().numpy(), U.astype(np.float32))
+
+
+def test_bank_checkpoint_restore_is_bitwise():
+    """The state is the bank memory plus its keys: restoring both into a fresh bank
+    gives bitwise the same scores."""
+    need_gpu()
+    import zeroth_order_fine_amd as zo
+    wl = workload(SMALL_OPT_BF16, dir_seeds=(2, 9), nu=2)
+    batch = inputs.make_batch(wl)
+    g = GpuRun(wl)
+    for t in range(3):
+        g.update(t, np.array([0.4 * (t + 1), -0.3]), 1e-2)
+    a = g.score(3, batch)
+    saved_mem = g.bank.mem.clone()
+    saved_keys = g.bank.keys()
+    fresh = zo.Bank(g.model, 4, wl.rank, wl.targets)
+    fresh.mem.copy_(saved_mem)
+    fresh.set_keys(*saved_keys)
+    b = zo.score(g.model, g.plan(3), fresh, zo.DeviceBatch(batch))
+    assert np.array_equal(a["S"], b["S"])
+    assert np.array_equal(a["seq_logp"].cpu().numpy(), b["seq_logp"].cpu().numpy())
