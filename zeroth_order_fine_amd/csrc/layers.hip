@@ -8,7 +8,7 @@
 namespace {
 
 constexpr int NORM_THREADS = 256;
-constexpr int NORM_MAXV = 24;      // d <= 256 * 24 = 6144
+constexpr int NORM_MAXV = 24;      // d <= 256 * 24 = 6144, in 16-byte groups
 
 __device__ __forceinline__ float block_sum(float v, float* sh) {
 #pragma unroll
@@ -40,50 +40,66 @@ __global__ void embed_kernel(const TW* __restrict__ E, const TW* __restrict__ P,
   }
 }
 
-// out[m] = norm(h[rows ? rows[m] : m]); LayerNorm (affine) or RMSNorm (gain only)
+// out[m] = norm(h[rows ? rows[m] : m]); LayerNorm (affine) or RMSNorm (gain only).
+// 16-byte loads (d is a multiple of 4); the row stays in registers between the
+// statistics and the write.
+template <typename T>
+__device__ __forceinline__ void store4(T* o, floatx4_t y);
+template <>
+__device__ __forceinline__ void store4<float>(float* o, floatx4_t y) { *(floatx4_t*)o = y; }
+template <>
+__device__ __forceinline__ void store4<bf16_t>(bf16_t* o, floatx4_t y) {
+  const uint32_t w0 = (uint32_t)f32_to_bf16(y[0]) | ((uint32_t)f32_to_bf16(y[1]) << 16);
+  const uint32_t w1 = (uint32_t)f32_to_bf16(y[2]) | ((uint32_t)f32_to_bf16(y[3]) << 16);
+  *(uint2*)o = make_uint2(w0, w1);
+}
+
 template <typename T>
 __global__ void __launch_bounds__(NORM_THREADS)
 norm_kernel(const float* __restrict__ h, const int32_t* __restrict__ rows, int d, const float* __restrict__ w,
             const float* __restrict__ b, float eps, int rms, T* __restrict__ out) {
+  constexpr int NV = NORM_MAXV / 4;
   __shared__ float sh[NORM_THREADS / 64];
   const int m = blockIdx.x;
   const int src = rows ? rows[m] : m;
   const float* x = h + (int64_t)src * d;
-  float v[NORM_MAXV];
+  floatx4_t v[NV];
   float s = 0.f;
 #pragma unroll
-  for (int k = 0; k < NORM_MAXV; ++k) {
-    const int i = threadIdx.x + k * NORM_THREADS;
-    v[k] = i < d ? x[i] : 0.f;
-    s += v[k];
+  for (int k = 0; k < NV; ++k) {
+    const int i = 4 * (threadIdx.x + k * NORM_THREADS);
+    v[k] = i < d ? *(const floatx4_t*)(x + i) : floatx4_t{0.f, 0.f, 0.f, 0.f};
+    s += (v[k][0] + v[k][1]) + (v[k][2] + v[k][3]);
   }
   float mean = 0.f, scale;
   if (!rms) {
     mean = block_sum(s, sh) / (float)d;
     float q = 0.f;
 #pragma unroll
-    for (int k = 0; k < NORM_MAXV; ++k) {
-      const int i = threadIdx.x + k * NORM_THREADS;
-      const float c = v[k] - mean;
-      q += i < d ? c * c : 0.f;
+    for (int k = 0; k < NV; ++k) {
+      const int i = 4 * (threadIdx.x + k * NORM_THREADS);
+      if (i < d) {
+        const floatx4_t c = v[k] - mean;
+        q += (c[0] * c[0] + c[1] * c[1]) + (c[2] * c[2] + c[3] * c[3]);
+      }
     }
     const float var = block_sum(q, sh) / (float)d;
     scale = 1.0f / sqrtf(var + eps);
   } else {
     float q = 0.f;
 #pragma unroll
-    for (int k = 0; k < NORM_MAXV; ++k) q += v[k] * v[k];
+    for (int k = 0; k < NV; ++k) q += (v[k][0] * v[k][0] + v[k][1] * v[k][1]) + (v[k][2] * v[k][2] + v[k][3] * v[k][3]);
     const float ms = block_sum(q, sh) / (float)d;
     scale = 1.0f / sqrtf(ms + eps);
   }
   T* o = out + (int64_t)m * d;
 #pragma unroll
-  for (int k = 0; k < NORM_MAXV; ++k) {
-    const int i = threadIdx.x + k * NORM_THREADS;
+  for (int k = 0; k < NV; ++k) {
+    const int i = 4 * (threadIdx.x + k * NORM_THREADS);
     if (i < d) {
-      float y = (v[k] - mean) * scale * w[i];
-      if (b) y += b[i];
-      o[i] = from_f32<T>(y);
+      floatx4_t y = (v[k] - mean) * scale * *(const floatx4_t*)(w + i);
+      if (b) y += *(const floatx4_t*)(b + i);
+      store4<T>(o + i, y);
     }
   }
 }
@@ -183,7 +199,7 @@ template <typename T>
 hipError_t launch_norm(const float* h, const int32_t* rows, int M, int d, const float* w, const float* b,
                        float eps, bool rms, T* out, hipStream_t s) {
   if (M <= 0) return hipSuccess;
-  if (d > NORM_THREADS * NORM_MAXV) return hipErrorInvalidValue;
+  if (d > NORM_THREADS * NORM_MAXV || d % 4 != 0) return hipErrorInvalidValue;
   hipLaunchKernelGGL(norm_kernel<T>, dim3(M), dim3(NORM_THREADS), 0, s, h, rows, d, w, b, eps, rms ? 1 : 0, out);
   return hipGetLastError();
 }

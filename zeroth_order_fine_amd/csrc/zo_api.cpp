@@ -124,7 +124,8 @@ int validate_desc(const zo_model_desc* d) {
   ZO_CHECK(d->head_dim == 16 || d->head_dim == 32 || d->head_dim == 64 || d->head_dim == 128, ZO_E_INVAL,
            "head_dim must be 16, 32, 64 or 128");
   ZO_CHECK(d->dtype == ZO_DTYPE_F32 || d->head_dim >= 32, ZO_E_INVAL, "bf16 attention needs head_dim >= 32");
-  ZO_CHECK(d->d_model <= 6144, ZO_E_INVAL, "d_model above 6144 is not supported by the norm kernels");
+  ZO_CHECK(d->d_model <= 6144 && d->d_model % 4 == 0, ZO_E_INVAL,
+           "d_model must be a multiple of 4 and at most 6144 (norm kernels)");
   ZO_CHECK(std::isfinite(d->norm_eps) && d->norm_eps > 0, ZO_E_INVAL, "norm_eps must be > 0");
   ZO_CHECK(is_opt(*d) || (std::isfinite(d->rope_theta) && d->rope_theta > 1.0), ZO_E_INVAL,
            "rope_theta must be > 1");
