@@ -67,10 +67,25 @@ attn_bf16_kernel(const bf16_t* __restrict__ qkv, int ld, bf16_t* __restrict__ ou
       const int krow = base + min(k0 + kr, len - 1);
       u32x4_t kv = *(const u32x4_t*)(qkv + (int64_t)krow * ld + kcol + ch * 8);
       *(u32x4_t*)(sK + kr * HD + ((ch ^ (kr & SWZ)) << 3)) = kv;
-      u32x4_t vv = *(const u32x4_t*)(qkv + (int64_t)krow * ld + vcol + ch * 8);
-      const bf16_t* ve = (const bf16_t*)&vv;
+    }
+    // V^T: a thread takes 4 consecutive keys of one 8-wide head-dim chunk, transposes
+    // them in registers and writes 8 rows of 4 keys (8 bytes each); the 16 lanes that
+    // share a chunk fill one 128-byte stretch of a V^T row
+    for (int c = tid; c < (KB / 4) * CH; c += 256) {
+      const int kg = c % (KB / 4), ch = c / (KB / 4);
+      u32x4_t vv[4];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) sVt[(ch * 8 + e) * VT_LD + kr] = ve[e];
+      for (int u = 0; u < 4; ++u) {
+        const int krow = base + min(k0 + kg * 4 + u, len - 1);
+        vv[u] = *(const u32x4_t*)(qkv + (int64_t)krow * ld + vcol + ch * 8);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int wi = e >> 1, sh = (e & 1) * 16;
+        const uint32_t lo = ((vv[0][wi] >> sh) & 0xFFFFu) | (((vv[1][wi] >> sh) & 0xFFFFu) << 16);
+        const uint32_t hi = ((vv[2][wi] >> sh) & 0xFFFFu) | (((vv[3][wi] >> sh) & 0xFFFFu) << 16);
+        *(uint2*)(sVt + (ch * 8 + e) * VT_LD + kg * 4) = make_uint2(lo, hi);
+      }
     }
     __syncthreads();
     // S^T[key][query] for 4 blocks of 16 keys
