@@ -72,6 +72,13 @@ enum { ZO_KIND_Q = 0, ZO_KIND_K = 1, ZO_KIND_V = 2, ZO_KIND_O = 3,
                                         unit-variance entries of G V^T (arXiv abstract: factorized
                                         perturbations approach dense Gaussian ZO as rank grows) */
 #define ZO_PLAN_ALLOW_ZERO_EPS 2u    /* permit eps == 0 (then S+ == S- exactly); testing only */
+#define ZO_PLAN_ACT_SPLIT 4u         /* bf16 models: feed every projection its activations as the two-term
+                                        bf16 expansion hi + lo (about 16 significant bits) against the exact
+                                        bf16 weights, the side path as three-term products of split t and
+                                        factors, and run attention in fp32.  Twice the MFMA work of the
+                                        projections; for summed long-sequence losses and deep stacks, where
+                                        bf16 activation rounding alone moves a sequence's sum by more than
+                                        2e-2.  ZO_E_INVAL on fp32 models. */
 
 /* zo_estimate flags */
 #define ZO_EST_INV_RANK 1u  /* divide c by r: the explicit 1/r of LoZO's estimator, which the

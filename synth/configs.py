@@ -64,6 +64,10 @@ class Workload:
     model_seed: int = 0
     data_seed: int = 0
     scale_inv_sqrt_r: bool = False
+    # score with two-term bf16 activations (hi + lo), fp32 attention and three-term side
+    # products: a precision choice of the GPU path for summed long-sequence losses and deep
+    # stacks; the oracle is exact either way
+    act_split: bool = False
 
     @property
     def n_dirs(self):
@@ -92,9 +96,9 @@ CONFIGS = {
     "opt1.3b": Workload("opt1.3b", OPT_1_3B, 16, 16, 64, "zipf", "last_label", 2, 1e-3, (0,), _ALL_OPT),
     "opt13b": Workload("opt13b", OPT_13B, 64, 16, 128, "zipf", "last_label", 2, 1e-3, (0,), _ALL_OPT),
     "opt6.7b-mezo": Workload("opt6.7b-mezo", OPT_6_7B, 32, 128, 128, "zipf", "all_next", 64, 1e-3,
-                             (0, 1, 2, 3), _ALL_OPT, scale_inv_sqrt_r=True),
+                             (0, 1, 2, 3), _ALL_OPT, scale_inv_sqrt_r=True, act_split=True),
     "qwen3-8b-mixed": Workload("qwen3-8b-mixed", QWEN3_8B, 16, 32, 512, "zipf", "last_label", 4, 1e-3,
-                               (0,), _ALL_QWEN, n_fg=32, fg_score_mode="all_next"),
+                               (0,), _ALL_QWEN, n_fg=32, fg_score_mode="all_next", act_split=True),
 }
 
 

@@ -59,14 +59,15 @@ def test_tiny_fp32_two_point_step():
                 assert np.array_equal(got, U.astype(np.float32)), (t, slot, layer, kind)
 
 
-@pytest.mark.parametrize("cfg", [SMALL_OPT_BF16, SMALL_QWEN_BF16, SMALL_QWEN_F32],
-                         ids=["opt-bf16", "qwen3-bf16", "qwen3-f32"])
-def test_small_models_with_bank_and_ragged_rows(cfg):
+@pytest.mark.parametrize("cfg,split", [(SMALL_OPT_BF16, False), (SMALL_QWEN_BF16, False), (SMALL_QWEN_F32, False),
+                                       (SMALL_OPT_BF16, True), (SMALL_QWEN_BF16, True)],
+                         ids=["opt-bf16", "qwen3-bf16", "qwen3-f32", "opt-bf16-split", "qwen3-bf16-split"])
+def test_small_models_with_bank_and_ragged_rows(cfg, split):
     """Lengths 5..150 (1-3 query blocks, ragged row count), foreground + probes, two
     directions, a bank with entries from two windows (nu = 4: a frozen entry and an
-    active one)."""
+    active one).  `split`: two-term bf16 activations (ZO_PLAN_ACT_SPLIT)."""
     need_gpu()
-    wl = workload(cfg, dir_seeds=(3, 8), n_fg=2, n_prompts=3)
+    wl = workload(cfg, dir_seeds=(3, 8), n_fg=2, n_prompts=3, act_split=split)
     batch = inputs.make_batch(wl)
     g, o = GpuRun(wl), OracleRun(wl)
     c_fixed = [np.array([0.9, -1.7]), np.array([-2.5, 0.4]), np.array([1.1, 0.8])]
@@ -80,7 +81,9 @@ def test_small_models_with_bank_and_ragged_rows(cfg):
         err = np.max(np.abs(g_ - os_["seq_logp"]) / np.abs(os_["seq_logp"]))
         assert err <= 1e-4, err
     else:
-        err = _seq_close(gs, os_, 2e-2)
+        # two-term activations carry ~16 significant bits: the bf16 bound shrinks by far more
+        # than 10x, so a dropped lo term (bf16-level error) fails here
+        err = _seq_close(gs, os_, 5e-4 if split else 2e-2)
     flush("max per-sequence err %.3g" % err)
     if cfg.dtype == "f32":
         assert np.all(np.abs(gs["S"] - os_["S"]) <= 1e-4 * np.abs(os_["S"]))
@@ -158,14 +161,14 @@ def test_high_rank_multi_direction():
     every next-token position, eps / sqrt(r) scaling; bank holding all four entries."""
     need_gpu()
     wl = workload(SMALL_OPT_BF16, rank=64, dir_seeds=(0, 1, 2, 3), n_prompts=2, len_lo=40, len_hi=70,
-                  score_mode="all_next", scale_inv_sqrt_r=True, nu=1024)
+                  score_mode="all_next", scale_inv_sqrt_r=True, nu=1024, act_split=True)
     batch = inputs.make_batch(wl)
     g, o = GpuRun(wl), OracleRun(wl)
     c = np.array([0.5, -0.25, 1.5, -2.0])
     g.update(0, c, 2e-3)
     o.update(0, c, 2e-3)
     gs, os_ = g.score(1, batch), o.score(1, batch)
-    err = _seq_close(gs, os_, 2e-2)
+    err = _seq_close(gs, os_, 5e-4)          # two-term activations (see the small-model test)
     flush("r=64 max per-sequence |err| %.3g over %d tokens" % (err, len(os_["tok_logp"][0])))
     tok = gs["tok_logp"].cpu().numpy()
     allref = np.concatenate([os_["tok_logp"][p] for p in range(len(os_["phys"]))])

@@ -14,7 +14,7 @@ from ._lib import BatchDesc, ModelDesc, PlanDesc
 ARCH = {"opt": 0, "qwen3": 1}
 DTYPE = {"f32": 0, "bf16": 1}
 KINDS = {"opt": ("q", "k", "v", "o", "fc1", "fc2"), "qwen3": ("q", "k", "v", "o", "gate", "up", "down")}
-PLAN_SCALE_INV_SQRT_R, PLAN_ALLOW_ZERO_EPS = 1, 2
+PLAN_SCALE_INV_SQRT_R, PLAN_ALLOW_ZERO_EPS, PLAN_ACT_SPLIT = 1, 2, 4
 EST_INV_RANK, EST_MEAN = 1, 2
 ROLE_PROBE, ROLE_FOREGROUND = 0, 1
 SCORE_LAST_LABEL, SCORE_ALL_NEXT = 0, 1
@@ -137,7 +137,7 @@ class Plan:
     @classmethod
     def from_workload(cls, model, wl, t=0, eps=None, flags=None, candidates=None):
         if flags is None:
-            flags = PLAN_SCALE_INV_SQRT_R if wl.scale_inv_sqrt_r else 0
+            flags = (PLAN_SCALE_INV_SQRT_R if wl.scale_inv_sqrt_r else 0) | (PLAN_ACT_SPLIT if wl.act_split else 0)
         return cls(model, t, wl.nu, wl.rank, wl.eps if eps is None else eps, wl.dir_seeds,
                    wl.candidates if candidates is None else candidates, wl.targets, flags)
 

@@ -162,11 +162,13 @@ attn_bf16_kernel(const bf16_t* __restrict__ qkv, int ld, bf16_t* __restrict__ ou
   }
 }
 
-// fp32 path: one thread per query row, online softmax in registers.
+// fp32 path: one thread per query row, online softmax in registers.  The output
+// is fp32, or (lo_off > 0) the two-term bf16 expansion hi | lo that feeds the
+// next bf16 projection.
 template <int HD>
-__global__ void attn_f32_kernel(const float* __restrict__ qkv, int ld, float* __restrict__ out, int ld_out,
-                                const int32_t* __restrict__ cu, const int32_t* __restrict__ work, int hq, int hkv,
-                                float scale) {
+__global__ void attn_f32_kernel(const float* __restrict__ qkv, int ld, void* __restrict__ out, int ld_out,
+                                int lo_off, const int32_t* __restrict__ cu, const int32_t* __restrict__ work, int hq,
+                                int hkv, float scale) {
   const int w = work[blockIdx.x];
   const int seq = w >> 12, qblk = w & 4095;
   const int h = blockIdx.y;
@@ -193,9 +195,31 @@ __global__ void attn_f32_kernel(const float* __restrict__ qkv, int ld, float* __
     for (int i = 0; i < HD; ++i) o[i] = o[i] * a + p * vr[i];
     m = mn;
   }
-  float* orow = out + (int64_t)(base + qi) * ld_out + h * HD;
+  const int64_t ob = (int64_t)(base + qi) * ld_out + h * HD;
+  if (lo_off) {
+    bf16_t* orow = (bf16_t*)out + ob;
 #pragma unroll
-  for (int i = 0; i < HD; ++i) orow[i] = o[i] / l;
+    for (int i = 0; i < HD; ++i) split_bf16(o[i] / l, orow[i], orow[i + lo_off]);
+  } else {
+    float* orow = (float*)out + ob;
+#pragma unroll
+    for (int i = 0; i < HD; ++i) orow[i] = o[i] / l;
+  }
+}
+
+hipError_t launch_attn_f32(const float* qkv, int ld_qkv, void* out, int ld_out, int lo_off, const int32_t* cu,
+                           const int32_t* work, int n_work, int hq, int hkv, int hd, hipStream_t s) {
+  if (n_work <= 0) return hipSuccess;
+  const float scale = (float)(1.0 / sqrt((double)hd));
+  dim3 grid(n_work, hq);
+  switch (hd) {
+    case 16: hipLaunchKernelGGL(attn_f32_kernel<16>, grid, dim3(QB), 0, s, qkv, ld_qkv, out, ld_out, lo_off, cu, work, hq, hkv, scale); break;
+    case 32: hipLaunchKernelGGL(attn_f32_kernel<32>, grid, dim3(QB), 0, s, qkv, ld_qkv, out, ld_out, lo_off, cu, work, hq, hkv, scale); break;
+    case 64: hipLaunchKernelGGL(attn_f32_kernel<64>, grid, dim3(QB), 0, s, qkv, ld_qkv, out, ld_out, lo_off, cu, work, hq, hkv, scale); break;
+    case 128: hipLaunchKernelGGL(attn_f32_kernel<128>, grid, dim3(QB), 0, s, qkv, ld_qkv, out, ld_out, lo_off, cu, work, hq, hkv, scale); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 }  // namespace
@@ -222,15 +246,12 @@ hipError_t launch_attention<float>(const float* qkv, int ld_qkv, float* out, int
                                    int n_seq, const int32_t* work, int n_work, int hq, int hkv, int hd,
                                    hipStream_t s) {
   (void)n_seq;
-  if (n_work <= 0) return hipSuccess;
-  const float scale = (float)(1.0 / sqrt((double)hd));
-  dim3 grid(n_work, hq);
-  switch (hd) {
-    case 16: hipLaunchKernelGGL(attn_f32_kernel<16>, grid, dim3(QB), 0, s, qkv, ld_qkv, out, ld_out, cu, work, hq, hkv, scale); break;
-    case 32: hipLaunchKernelGGL(attn_f32_kernel<32>, grid, dim3(QB), 0, s, qkv, ld_qkv, out, ld_out, cu, work, hq, hkv, scale); break;
-    case 64: hipLaunchKernelGGL(attn_f32_kernel<64>, grid, dim3(QB), 0, s, qkv, ld_qkv, out, ld_out, cu, work, hq, hkv, scale); break;
-    case 128: hipLaunchKernelGGL(attn_f32_kernel<128>, grid, dim3(QB), 0, s, qkv, ld_qkv, out, ld_out, cu, work, hq, hkv, scale); break;
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
+  return launch_attn_f32(qkv, ld_qkv, out, ld_out, 0, cu, work, n_work, hq, hkv, hd, s);
+}
+
+hipError_t launch_attention_split(const float* qkv, int ld_qkv, bf16_t* out, int ld_out, int lo_off,
+                                  const int32_t* cu, const int32_t* work, int n_work, int hq, int hkv, int hd,
+                                  hipStream_t s) {
+  if (lo_off <= 0) return hipErrorInvalidValue;
+  return launch_attn_f32(qkv, ld_qkv, out, ld_out, lo_off, cu, work, n_work, hq, hkv, hd, s);
 }

@@ -18,6 +18,13 @@ __host__ __device__ inline bf16_t f32_to_bf16(float f) {
 __host__ __device__ inline float bf16_to_f32(bf16_t b) {
   return __builtin_bit_cast(float, ((uint32_t)b) << 16);
 }
+// Two-term bf16 expansion of an fp32 value: hi = bf16(v), lo = bf16(v - hi).
+// v - hi is exact in fp32, so hi + lo carries 16 significant bits (relative
+// error <= 2^-17); a product with an exact bf16 weight then needs two MFMAs.
+__host__ __device__ inline void split_bf16(float v, bf16_t& hi, bf16_t& lo) {
+  hi = f32_to_bf16(v);
+  lo = f32_to_bf16(v - bf16_to_f32(hi));
+}
 
 // activation element type helpers: float (fp32 mode) or bf16_t (bf16 mode)
 template <typename T> __device__ inline float to_f32(T v);
@@ -43,16 +50,26 @@ struct GemmParams {
   const void* A; int64_t lda;
   const void* B; int64_t ldb;
   int M, N, K;
+  // Column wraps of the main segment (0: none): K-step k reads A column k mod kwa
+  // and B column k mod kwb (k < 2 * wrap).  With two-term bf16 activations
+  // A = [hi | lo], K = 2 kwb: hi.W^T + lo.W^T in one pass over the exact bf16 W;
+  // with B = [V_hi | V_hi | V_lo], K = 3 kwa: hi.V_hi + lo.V_hi + hi.V_lo.
+  int kwa, kwb;
   // extended-K side path (0 = none). Column tile starting at n0 uses the
   // As columns [g*ks_tile, (g+1)*ks_tile) where g = number of bounds <= n0.
   const void* As; int64_t ldas;
   const void* Bs; int64_t ldbs;
   int ks_tile;
   int n_bounds; int bounds[3];
+  int as_stride;              // As columns per group (0: ks_tile)
+  int kwas;                   // side-segment As column wrap (0: none), as kwa
+
   // epilogue
   int epi;
   const float* bias;          // [N] or null
   void* C; int64_t ldc;       // STORE/GELU/SWIGLU/TPROJ output
+  int c_lo;                   // bf16 outputs: 0, or write the two-term expansion with lo at column + c_lo
+  int c_f32;                  // STORE of the bf16 kernels: write fp32 instead of bf16
   float* H; int64_t ldh;      // RESID target
   // TPROJ
   const int32_t* row_cand;    // [M] candidate or -1
@@ -62,6 +79,8 @@ struct GemmParams {
   int tp_rank;                // r
   int tp_entries;             // E active bank entries (slots before the direction slots)
   int tp_used;                // (E + q) * r used columns per kind block
+  int tp_unit;                // 0, or write t as two-term bf16: column c of unit u = c / tp_unit goes to
+                              // u * 2 tp_unit + c % tp_unit (hi) and + tp_unit more (lo)
   // LMHEAD
   const int32_t* labels;      // [M]
   float2* part;               // [M x n_ntiles]
@@ -108,6 +127,7 @@ struct SideJob {       // one side-path factor block of one target linear
   int32_t col0;                   // first destination column (G/U: column offset in a Bs row)
   int32_t row_map;                // 0 plain, 1 = gate rows of a 16-interleaved pack, 2 = up rows
   int32_t dtype;                  // 0 f32, 1 bf16
+  int64_t split;                  // bf16 only: 0, or write hi | hi | lo copies `split` elements apart
 };
 hipError_t launch_side_jobs(const SideJob* jobs_dev, int n_jobs, int64_t max_items, hipStream_t s);
 
@@ -135,7 +155,7 @@ hipError_t launch_embed_t(const TW* E, const TW* P, const int32_t* tokens, const
                           const int32_t* row_pos, int M, int d, int vocab, float* h, hipStream_t s);
 template <typename T>
 hipError_t launch_norm(const float* h, const int32_t* rows, int M, int d, const float* w, const float* b,
-                       float eps, bool rms, T* out, hipStream_t s);
+                       float eps, bool rms, T* out, int64_t ld_out, int lo_off, hipStream_t s);
 template <typename T>
 hipError_t launch_qknorm_rope(T* qkv, int M, int ld, int hq, int hkv, int hd, const float* qw, const float* kw,
                               float eps, const float2* rope_cs, const int32_t* row_pos, hipStream_t s);
@@ -150,6 +170,10 @@ template <>
 hipError_t launch_attention<float>(const float* qkv, int ld_qkv, float* out, int ld_out, const int32_t* cu,
                                    int n_seq, const int32_t* work, int n_work, int hq, int hkv, int hd,
                                    hipStream_t s);
+// fp32 q|k|v -> attention output as the two-term bf16 expansion (hi at column c, lo at c + lo_off)
+hipError_t launch_attention_split(const float* qkv, int ld_qkv, bf16_t* out, int ld_out, int lo_off,
+                                  const int32_t* cu, const int32_t* work, int n_work, int hq, int hkv, int hd,
+                                  hipStream_t s);
 hipError_t launch_tproj_reduce(const GemmParams& p, hipStream_t s);
 hipError_t launch_gather_i32(const int32_t* src, const int32_t* idx, int n, int32_t* dst, hipStream_t s);
 hipError_t launch_logp_reduce(const float2* part, int n_tiles, const float* lab_logit, int n_scored,

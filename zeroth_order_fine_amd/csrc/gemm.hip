@@ -48,6 +48,44 @@ __device__ __forceinline__ int tile_swizzle(int bid, int total, int& logical) {
   return logical;
 }
 
+// one activation output at element offset o of C: fp32 models store fp32; bf16
+// models store bf16 (plus the lo term at + c_lo when set), or fp32 for a STORE
+// with c_f32
+template <typename TAct>
+__device__ __forceinline__ void store_act(const GemmParams& p, int64_t o, float v, bool store_epi) {
+  if constexpr (std::is_same<TAct, float>::value) {
+    ((float*)p.C)[o] = v;
+  } else {
+    if (store_epi && p.c_f32) {
+      ((float*)p.C)[o] = v;
+      return;
+    }
+    bf16_t hi, lo;
+    split_bf16(v, hi, lo);
+    ((bf16_t*)p.C)[o] = hi;
+    if (p.c_lo) ((bf16_t*)p.C)[o + p.c_lo] = lo;
+  }
+}
+
+// side input t of row r, column c (see tp_unit)
+template <typename TAct>
+__device__ __forceinline__ void store_tproj(const GemmParams& p, int r, int c, float v) {
+  if constexpr (std::is_same<TAct, float>::value) {
+    ((float*)p.C)[(int64_t)r * p.ldc + c] = v;
+  } else {
+    if (p.tp_unit == 0) {
+      ((bf16_t*)p.C)[(int64_t)r * p.ldc + c] = f32_to_bf16(v);
+      return;
+    }
+    const int u = c / p.tp_unit;
+    const int64_t o = (int64_t)r * p.ldc + c + u * p.tp_unit;   // u * 2 tp_unit + c % tp_unit
+    bf16_t hi, lo;
+    split_bf16(v, hi, lo);
+    ((bf16_t*)p.C)[o] = hi;
+    ((bf16_t*)p.C)[o + p.tp_unit] = lo;
+  }
+}
+
 // ------------------------------------------------------------------------------
 // epilogue, shared by both paths.  acc[i][j][q]: row r0 + i*16 + 4*(lane>>4) + q,
 // column c0 + j*16 + (lane&15).
@@ -83,7 +121,7 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, floatx4_t (&acc)[T
               if (slot < p.tp_entries) o = v;
               else if (slot - p.tp_entries == cdir) o = cscale * v;
             }
-            ((TAct*)p.C)[(int64_t)r * p.ldc + c] = from_f32<TAct>(o);
+            store_tproj<TAct>(p, r, c, o);
           } else {
             if (p.bias) v += p.bias[c];
             if constexpr (epi == EPI_RESID) {
@@ -91,7 +129,7 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, floatx4_t (&acc)[T
               *hp = *hp + v;
             } else {
               if constexpr (epi == EPI_GELU) v = gelu_erf(v);
-              ((TAct*)p.C)[(int64_t)r * p.ldc + c] = from_f32<TAct>(v);
+              store_act<TAct>(p, (int64_t)r * p.ldc + c, v, epi == EPI_STORE);
             }
           }
         }
@@ -128,7 +166,7 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, floatx4_t (&acc)[T
           if (cg >= p.N) continue;
           const int oc = (n0 + wn * WN) / 2 + jp * 16 + (lane & 15);
           float g = acc[i][2 * jp][q], u = acc[i][2 * jp + 1][q];
-          ((TAct*)p.C)[(int64_t)r * p.ldc + oc] = from_f32<TAct>(silu(g) * u);
+          store_act<TAct>(p, (int64_t)r * p.ldc + oc, silu(g) * u, false);
         }
       }
     return;
@@ -211,14 +249,16 @@ gemm_bf16_kernel(GemmParams p) {
 
   const int grp = (p.n_bounds > 0 && n0 >= p.bounds[0]) + (p.n_bounds > 1 && n0 >= p.bounds[1]) +
                   (p.n_bounds > 2 && n0 >= p.bounds[2]);
-  const int a_side_off = grp * p.ks_tile;
+  const int a_side_off = grp * (p.as_stride ? p.as_stride : p.ks_tile);
   int nkb = p.K / BK, nk = nkb + p.ks_tile / BK;
+  const int nkwa = p.kwa ? p.kwa / BK : (1 << 30), nkwb = p.kwb ? p.kwb / BK : (1 << 30);
+  const int nkwas = p.kwas ? p.kwas / BK : (1 << 30);
+  int kt_off = 0;                           // first base K-step of this workgroup
   const bf16_t* Ab = (const bf16_t*)p.A;
   const bf16_t* Bb = (const bf16_t*)p.B;
   if constexpr (EPI == EPI_PARTIAL) {       // K-slice of this workgroup (no side path)
     const int per = nkb / p.ksplit;
-    Ab += (int64_t)blockIdx.z * per * BK;
-    Bb += (int64_t)blockIdx.z * per * BK;
+    kt_off = blockIdx.z * per;
     nkb = per;
     nk = per;
   }
@@ -244,8 +284,10 @@ gemm_bf16_kernel(GemmParams p) {
     const bf16_t* ga__ = side__ ? Asb : Ab;                                       \
     const bf16_t* gb__ = side__ ? Bsb : Bb;                                       \
     const int la__ = side__ ? ldas : lda, lb__ = side__ ? ldbs : ldb;             \
-    const int kb__ = (side__ ? (kt__ - nkb) : kt__) * BK + ch * 8;                \
-    const int ka__ = kb__ + (side__ ? a_side_off : 0);                            \
+    const int kk__ = side__ ? (kt__ - nkb) : kt__ + kt_off;                       \
+    const int wa__ = side__ ? nkwas : nkwa, wb__ = side__ ? (1 << 30) : nkwb;     \
+    const int ka__ = (kk__ >= wa__ ? kk__ - wa__ : kk__) * BK + ch * 8 + (side__ ? a_side_off : 0); \
+    const int kb__ = (kk__ >= wb__ ? kk__ - wb__ : kk__) * BK + ch * 8;           \
     static_for<0, CA>([&](auto i) { ra[i] = *(const u32x4_t*)(ga__ + (arow[i] * la__ + ka__)); }); \
     static_for<0, CB>([&](auto i) { rb[i] = *(const u32x4_t*)(gb__ + (brow[i] * lb__ + kb__)); }); \
   } while (0)
@@ -309,6 +351,17 @@ gemm_bf16_kernel(GemmParams p) {
 // n = j*16 + 4*(lane >> 4) + q inside the wave tile, so every lane owns four
 // consecutive output columns and writes them with one 8-byte (bf16) or 16-byte
 // (fp32 residual) access.
+// four consecutive bf16 outputs (8 bytes), plus their lo terms at + c_lo when set
+__device__ __forceinline__ void store_bf16x4(const GemmParams& p, bf16_t* o, floatx4_t v) {
+  bf16_t hi[4], lo[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) split_bf16(v[q], hi[q], lo[q]);
+  *(uint2*)o = make_uint2((uint32_t)hi[0] | ((uint32_t)hi[1] << 16), (uint32_t)hi[2] | ((uint32_t)hi[3] << 16));
+  if (p.c_lo)
+    *(uint2*)(o + p.c_lo) =
+        make_uint2((uint32_t)lo[0] | ((uint32_t)lo[1] << 16), (uint32_t)lo[2] | ((uint32_t)lo[3] << 16));
+}
+
 template <int EPI, int TM, int TN, int WM, int WN>
 __device__ __forceinline__ void epilogue_rows(const GemmParams& p, floatx4_t (&acc)[TM][TN], int m0, int n0, int wm,
                                               int wn, int lane) {
@@ -324,9 +377,10 @@ __device__ __forceinline__ void epilogue_rows(const GemmParams& p, floatx4_t (&a
 #pragma unroll
       for (int jp = 0; jp < TN / 2; ++jp) {
         const floatx4_t g = acc[i][2 * jp], u = acc[i][2 * jp + 1];
-        uint32_t w0 = (uint32_t)f32_to_bf16(silu(g[0]) * u[0]) | ((uint32_t)f32_to_bf16(silu(g[1]) * u[1]) << 16);
-        uint32_t w1 = (uint32_t)f32_to_bf16(silu(g[2]) * u[2]) | ((uint32_t)f32_to_bf16(silu(g[3]) * u[3]) << 16);
-        *(uint2*)((bf16_t*)p.C + (int64_t)r * p.ldc + ob + jp * 16) = make_uint2(w0, w1);
+        floatx4_t v;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) v[q] = silu(g[q]) * u[q];
+        store_bf16x4(p, (bf16_t*)p.C + (int64_t)r * p.ldc + ob + jp * 16, v);
       }
     }
     return;
@@ -350,9 +404,10 @@ __device__ __forceinline__ void epilogue_rows(const GemmParams& p, floatx4_t (&a
 #pragma unroll
             for (int q = 0; q < 4; ++q) v[q] = gelu_erf(v[q]);
           }
-          uint32_t w0 = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
-          uint32_t w1 = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
-          *(uint2*)((bf16_t*)p.C + (int64_t)r * p.ldc + cb + j * 16) = make_uint2(w0, w1);
+          if (EPI == EPI_STORE && p.c_f32)
+            *(floatx4_t*)((float*)p.C + (int64_t)r * p.ldc + cb + j * 16) = v;
+          else
+            store_bf16x4(p, (bf16_t*)p.C + (int64_t)r * p.ldc + cb + j * 16, v);
         }
       }
     }
@@ -400,8 +455,10 @@ gemm_bf16_pipe_kernel(GemmParams p) {
   const int wm = wave / NWN, wn = wave % NWN;
   const int grp = (p.n_bounds > 0 && n0 >= p.bounds[0]) + (p.n_bounds > 1 && n0 >= p.bounds[1]) +
                   (p.n_bounds > 2 && n0 >= p.bounds[2]);
-  const int a_side_off = grp * p.ks_tile;
+  const int a_side_off = grp * (p.as_stride ? p.as_stride : p.ks_tile);
   const int nkb = p.K / BK, nk = nkb + p.ks_tile / BK;
+  const int nkwa = p.kwa ? p.kwa / BK : (1 << 30), nkwb = p.kwb ? p.kwb / BK : (1 << 30);
+  const int nkwas = p.kwas ? p.kwas / BK : (1 << 30);
   const bf16_t* Ab = (const bf16_t*)p.A;
   const bf16_t* Bb = (const bf16_t*)p.B;
   const bf16_t* Asb = (const bf16_t*)p.As;
@@ -421,8 +478,9 @@ gemm_bf16_pipe_kernel(GemmParams p) {
     const bf16_t* ga = side ? Asb : Ab;
     const bf16_t* gb = side ? Bsb : Bb;
     const int la = side ? ldas : lda, lb = side ? ldbs : ldb;
-    const int kb = (side ? (s - nkb) : s) * BK + lch * 8;
-    const int ka = kb + (side ? a_side_off : 0);
+    const int kk = side ? (s - nkb) : s, wa = side ? nkwas : nkwa, wb = side ? (1 << 30) : nkwb;
+    const int ka = (kk >= wa ? kk - wa : kk) * BK + lch * 8 + (side ? a_side_off : 0);
+    const int kb = (kk >= wb ? kk - wb : kk) * BK + lch * 8;
     static_for<0, IA>([&](auto i) {
       __builtin_amdgcn_global_load_lds((const void*)(ga + (arow[i] * la + ka)),
                                        (__attribute__((address_space(3))) void*)(sA + (wave * IA + i) * 16 * BK),
@@ -613,7 +671,7 @@ __global__ void tproj_reduce_kernel(GemmParams p) {
       if (slot < p.tp_entries) o = v;
       else if (slot - p.tp_entries == p.cand_dir[cand]) o = p.cand_scale[cand] * v;
     }
-    ((TAct*)p.C)[(int64_t)r * p.ldc + c] = from_f32<TAct>(o);
+    store_tproj<TAct>(p, r, c, o);
   }
 }
 

@@ -4,6 +4,7 @@
 // registers between the statistics and the write.
 #include "common.h"
 #include <math.h>
+#include <type_traits>
 
 namespace {
 
@@ -53,11 +54,20 @@ __device__ __forceinline__ void store4<bf16_t>(bf16_t* o, floatx4_t y) {
   const uint32_t w1 = (uint32_t)f32_to_bf16(y[2]) | ((uint32_t)f32_to_bf16(y[3]) << 16);
   *(uint2*)o = make_uint2(w0, w1);
 }
+// two-term bf16 expansion: hi at o, lo at o + lo_off
+__device__ __forceinline__ void store4_split(bf16_t* o, int lo_off, floatx4_t y) {
+  bf16_t hi[4], lo[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) split_bf16(y[q], hi[q], lo[q]);
+  *(uint2*)o = make_uint2((uint32_t)hi[0] | ((uint32_t)hi[1] << 16), (uint32_t)hi[2] | ((uint32_t)hi[3] << 16));
+  *(uint2*)(o + lo_off) =
+      make_uint2((uint32_t)lo[0] | ((uint32_t)lo[1] << 16), (uint32_t)lo[2] | ((uint32_t)lo[3] << 16));
+}
 
 template <typename T>
 __global__ void __launch_bounds__(NORM_THREADS)
 norm_kernel(const float* __restrict__ h, const int32_t* __restrict__ rows, int d, const float* __restrict__ w,
-            const float* __restrict__ b, float eps, int rms, T* __restrict__ out) {
+            const float* __restrict__ b, float eps, int rms, T* __restrict__ out, int64_t ld_out, int lo_off) {
   constexpr int NV = NORM_MAXV / 4;
   __shared__ float sh[NORM_THREADS / 64];
   const int m = blockIdx.x;
@@ -92,14 +102,19 @@ norm_kernel(const float* __restrict__ h, const int32_t* __restrict__ rows, int d
     const float ms = block_sum(q, sh) / (float)d;
     scale = 1.0f / sqrtf(ms + eps);
   }
-  T* o = out + (int64_t)m * d;
+  T* o = out + (int64_t)m * ld_out;
 #pragma unroll
   for (int k = 0; k < NV; ++k) {
     const int i = 4 * (threadIdx.x + k * NORM_THREADS);
     if (i < d) {
       floatx4_t y = (v[k] - mean) * scale * *(const floatx4_t*)(w + i);
       if (b) y += *(const floatx4_t*)(b + i);
-      store4<T>(o + i, y);
+      if constexpr (std::is_same<T, bf16_t>::value) {
+        if (lo_off) store4_split(o + i, lo_off, y);
+        else store4<T>(o + i, y);
+      } else {
+        store4<T>(o + i, y);
+      }
     }
   }
 }
@@ -197,16 +212,18 @@ template hipError_t launch_embed_t<bf16_t>(const bf16_t*, const bf16_t*, const i
 
 template <typename T>
 hipError_t launch_norm(const float* h, const int32_t* rows, int M, int d, const float* w, const float* b,
-                       float eps, bool rms, T* out, hipStream_t s) {
+                       float eps, bool rms, T* out, int64_t ld_out, int lo_off, hipStream_t s) {
   if (M <= 0) return hipSuccess;
-  if (d > NORM_THREADS * NORM_MAXV || d % 4 != 0) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(norm_kernel<T>, dim3(M), dim3(NORM_THREADS), 0, s, h, rows, d, w, b, eps, rms ? 1 : 0, out);
+  if (d > NORM_THREADS * NORM_MAXV || d % 4 != 0 || ld_out % 4 != 0 || lo_off % 4 != 0) return hipErrorInvalidValue;
+  if (lo_off && !std::is_same<T, bf16_t>::value) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(norm_kernel<T>, dim3(M), dim3(NORM_THREADS), 0, s, h, rows, d, w, b, eps, rms ? 1 : 0, out,
+                     ld_out, lo_off);
   return hipGetLastError();
 }
 template hipError_t launch_norm<float>(const float*, const int32_t*, int, int, const float*, const float*, float,
-                                       bool, float*, hipStream_t);
+                                       bool, float*, int64_t, int, hipStream_t);
 template hipError_t launch_norm<bf16_t>(const float*, const int32_t*, int, int, const float*, const float*, float,
-                                        bool, bf16_t*, hipStream_t);
+                                        bool, bf16_t*, int64_t, int, hipStream_t);
 
 template <typename T>
 hipError_t launch_qknorm_rope(T* qkv, int M, int ld, int hq, int hkv, int hd, const float* qw, const float* kw,

@@ -182,10 +182,22 @@ __global__ void words_fill_kernel(uint64_t seed, uint32_t tag, uint64_t tau, int
   }
 }
 
-template <typename T>
-__device__ __forceinline__ void store_as(void* dst, int64_t off, float v, int dtype) {
-  if (dtype == 1) ((bf16_t*)dst)[off] = f32_to_bf16(v);
-  else ((float*)dst)[off] = v;
+// fp32, bf16, or (split > 0, bf16) the copies hi | hi | lo at off, off + split, off + 2 split
+__device__ __forceinline__ void store_as(void* dst, int64_t off, float v, int dtype, int64_t split) {
+  if (dtype == 1) {
+    bf16_t* o = (bf16_t*)dst + off;
+    if (split > 0) {
+      bf16_t hi, lo;
+      split_bf16(v, hi, lo);
+      o[0] = hi;
+      o[split] = hi;
+      o[2 * split] = lo;
+    } else {
+      *o = f32_to_bf16(v);
+    }
+  } else {
+    ((float*)dst)[off] = v;
+  }
 }
 
 __global__ void side_jobs_kernel(const SideJob* __restrict__ jobs) {
@@ -209,7 +221,7 @@ __global__ void side_jobs_kernel(const SideJob* __restrict__ jobs) {
           int64_t prow = jb.row_map ? interleave16_row(i, jb.row_map) : i;
           off = prow * jb.ld + jb.col0 + k;
         }
-        store_as<float>(jb.dst, off, f, jb.dtype);
+        store_as(jb.dst, off, f, jb.dtype, jb.split);
       }
     }
   } else if (jb.src == 2) {                     // bank U -> Bs columns
@@ -217,7 +229,7 @@ __global__ void side_jobs_kernel(const SideJob* __restrict__ jobs) {
          e += (int64_t)gridDim.x * blockDim.x) {
       int64_t i = e / jb.r, k = e - i * jb.r;
       int64_t prow = jb.row_map ? interleave16_row(i, jb.row_map) : i;
-      store_as<float>(jb.dst, prow * jb.ld + jb.col0 + k, jb.u_src[e], jb.dtype);
+      store_as(jb.dst, prow * jb.ld + jb.col0 + k, jb.u_src[e], jb.dtype, jb.split);
     }
   }
 }

@@ -449,6 +449,7 @@ int tproj_split(const zo_model_desc& d, int64_t n_cols, int64_t k) {
 }
 
 size_t act_size(const zo_model_desc& d) { return d.dtype == ZO_DTYPE_BF16 ? 2 : 4; }
+bool split_act(const zo_plan_s& p) { return (p.flags & ZO_PLAN_ACT_SPLIT) != 0; }
 
 int n_side_jobs(const zo_model_desc& d, const zo_plan_s& p, const SideGeom& sg) {
   if (!sg.any) return 0;
@@ -480,14 +481,17 @@ void carve(const zo_model* m, const zo_plan_s& p, const Packing& pk, const SideG
   w.jobs = b.take<SideJob>(std::max(n_side_jobs(d, p, sg), 1));
   const int64_t D = d.d_model, F = d.d_ffn;
   const int64_t NQ = (int64_t)d.n_heads * d.head_dim, NKV = (int64_t)d.n_kv_heads * d.head_dim;
+  // two-term activations: [hi | lo] rows (x2), fp32 q|k|v, factor blocks hi | hi | lo (x3)
+  const bool sp = split_act(p);
+  const int64_t x2 = sp ? 2 : 1, x3 = sp ? 3 : 1;
   w.h = b.take<float>(M * D);
-  w.xa = b.take<unsigned char>(M * D * as);
-  w.qkv = b.take<unsigned char>(M * (NQ + 2 * NKV) * as);
-  w.attn = b.take<unsigned char>(M * NQ * as);
-  w.hid = b.take<unsigned char>(M * F * as);
+  w.xa = b.take<unsigned char>(M * D * as * x2);
+  w.qkv = b.take<unsigned char>(M * (NQ + 2 * NKV) * (sp ? sizeof(float) : as));
+  w.attn = b.take<unsigned char>(M * NQ * as * x2);
+  w.hid = b.take<unsigned char>(M * F * as * x2);
   int64_t as_cols = 0;
   for (int g = 0; g < 4; ++g) as_cols = std::max(as_cols, sg.vt_rows[g]);
-  w.as = b.take<unsigned char>(M * std::max<int64_t>(as_cols, 1) * as);
+  w.as = b.take<unsigned char>(M * std::max<int64_t>(as_cols, 1) * as * x2);
   w.vt.assign((size_t)d.n_layers * 4, nullptr);
   w.bs.assign((size_t)d.n_layers * 4, nullptr);
   b.off = align_up(b.off, 256);
@@ -495,15 +499,16 @@ void carve(const zo_model* m, const zo_plan_s& p, const Packing& pk, const SideG
   for (int l = 0; l < d.n_layers; ++l)
     for (int g = 0; g < 4; ++g)
       if (sg.group_on[g]) {
-        w.vt[l * 4 + g] = b.take<unsigned char>(sg.vt_rows[g] * sg.n_in[g] * as);
-        w.bs[l * 4 + g] = b.take<unsigned char>(sg.bs_rows[g] * sg.bs_cols[g] * as);
+        w.vt[l * 4 + g] = b.take<unsigned char>(sg.vt_rows[g] * sg.n_in[g] * as * x3);
+        w.bs[l * 4 + g] = b.take<unsigned char>(sg.bs_rows[g] * sg.bs_cols[g] * as * x3);
       }
   w.side_begin = base ? (unsigned char*)base + side0 : nullptr;
   w.side_bytes = b.off - side0;
-  w.xs = b.take<unsigned char>(S * D * as);
+  w.xs = b.take<unsigned char>(S * D * as * x2);
   {
     int64_t np = 0;
-    for (int g = 0; g < 4; ++g) np = std::max(np, (int64_t)tproj_split(d, sg.vt_rows[g], sg.n_in[g]) * sg.vt_rows[g]);
+    for (int g = 0; g < 4; ++g)
+      np = std::max(np, (int64_t)tproj_split(d, sg.vt_rows[g], sg.n_in[g] * x3) * sg.vt_rows[g]);
     w.tp_partial = b.take<float>(std::max<int64_t>(np * M, 1));
   }
   const int bn_head = gemm_cfg_bn(GEMM_CFG_HEAD, d.dtype == ZO_DTYPE_BF16);
@@ -534,6 +539,9 @@ int run_gemm(const zo_model_desc& d, const GemmParams& gp, int cfg, hipStream_t 
              "projection N must be a multiple of 16");
     ZO_CHECK(gp.K % bk == 0 && gp.ks_tile % bk == 0, ZO_E_SHAPE, "K (%d) or side K (%d) not a multiple of %d", gp.K,
              gp.ks_tile, bk);
+    ZO_CHECK(gp.kwa % bk == 0 && gp.kwb % bk == 0 && gp.kwas % bk == 0 && (!gp.kwa || gp.K <= 2 * gp.kwa) &&
+                 (!gp.kwb || gp.K <= 2 * gp.kwb) && (!gp.kwas || gp.ks_tile <= 2 * gp.kwas),
+             ZO_E_SHAPE, "operand wrap does not fit the K extent");
     int rc;
     if ((rc = check_i32((int64_t)gp.M * gp.lda, "A")) != ZO_OK) return rc;
     if ((rc = check_i32((int64_t)gp.N * gp.ldb, "B")) != ZO_OK) return rc;
@@ -573,6 +581,13 @@ int forward(zo_model* m, const zo_plan_s& p, const Packing& pk, const SideGeom& 
   const float eps = (float)d.norm_eps;
   const bool rms = !is_opt(d);
   const int big = GEMM_CFG_BIG, narrow = GEMM_CFG_NARROW;
+  // Two-term activations (bf16 only): every projection input is [hi | lo] of width
+  // 2K and the GEMM wraps B at K; q|k|v stay fp32 for the fp32 attention; the
+  // side-input projection reads A = [hi | lo] wrapped at 2K against
+  // V^T = [hi | hi | lo] (K' = 3K), and the side segment reads As = [t_hi | t_lo]
+  // per unit wrapped at 2 units against Bs = [U_hi | U_hi | U_lo].
+  const bool sp = split_act(p);
+  const int x2 = sp ? 2 : 1, x3 = sp ? 3 : 1;
   int rc;
 
   if (M > 0) {
@@ -587,20 +602,28 @@ int forward(zo_model* m, const zo_plan_s& p, const Packing& pk, const SideGeom& 
 
   auto tproj = [&](int l, int g, const void* X, int K) -> int {
     if (!sg.group_on[g]) return ZO_OK;
-    GemmParams gp = gemm_base(X, K, w.vt[l * 4 + g], K, M, (int)sg.vt_rows[g], K);
+    GemmParams gp = gemm_base(X, (int64_t)K * x2, w.vt[l * 4 + g], (int64_t)K * x3, M, (int)sg.vt_rows[g], K * x3);
+    if (sp) { gp.kwa = 2 * K; gp.tp_unit = (int)sg.bs_cols[g]; }
     gp.epi = EPI_TPROJ;
-    gp.C = w.as; gp.ldc = sg.vt_rows[g];
+    gp.C = w.as; gp.ldc = sg.vt_rows[g] * x2;
     gp.row_cand = w.row_cand; gp.cand_dir = w.cand_dir; gp.cand_scale = w.cand_scale;
     gp.tp_ks = sg.ks; gp.tp_rank = sg.r; gp.tp_entries = sg.E; gp.tp_used = sg.used;
-    gp.ksplit = tproj_split(d, sg.vt_rows[g], K);
+    gp.ksplit = tproj_split(d, sg.vt_rows[g], K * x3);
     gp.partial = w.tp_partial;
     return run_gemm(d, gp, narrow, s);
   };
+  // projection over activations X [M x K] (or [hi | lo]) with the exact weight B [N x K]
+  auto proj = [&](const void* X, const void* B, int N, int K) {
+    GemmParams gp = gemm_base(X, (int64_t)K * x2, B, K, M, N, K * x2);
+    if (sp) gp.kwb = K;
+    return gp;
+  };
   auto with_side = [&](GemmParams& gp, int l, int g) {
     if (!sg.group_on[g]) return;
-    gp.As = w.as; gp.ldas = sg.vt_rows[g];
-    gp.Bs = w.bs[l * 4 + g]; gp.ldbs = sg.bs_cols[g];
-    gp.ks_tile = (int)sg.bs_cols[g];
+    gp.As = w.as; gp.ldas = sg.vt_rows[g] * x2;
+    gp.Bs = w.bs[l * 4 + g]; gp.ldbs = sg.bs_cols[g] * x3;
+    gp.ks_tile = (int)sg.bs_cols[g] * x3;
+    if (sp) { gp.as_stride = 2 * (int)sg.bs_cols[g]; gp.kwas = 2 * (int)sg.bs_cols[g]; }
   };
 
   for (int l = 0; l < d.n_layers && M > 0; ++l) {
@@ -608,29 +631,38 @@ int forward(zo_model* m, const zo_plan_s& p, const Packing& pk, const SideGeom& 
     // attention block
     {
       ProfScope ps(ZO_PROF_NORM, s);
-      ZO_HIP(launch_norm<T>(w.h, nullptr, M, D, Wf(P[P_LN1W]), Wf(P[P_LN1B]), eps, rms, (T*)w.xa, s));
+      ZO_HIP(launch_norm<T>(w.h, nullptr, M, D, Wf(P[P_LN1W]), Wf(P[P_LN1B]), eps, rms, (T*)w.xa, (int64_t)D * x2,
+                            sp ? D : 0, s));
     }
     if ((rc = tproj(l, 0, w.xa, D)) != ZO_OK) return rc;
     {
-      GemmParams gp = gemm_base(w.xa, D, W(P[P_WQ]), D, M, NQKV, D);
+      GemmParams gp = proj(w.xa, W(P[P_WQ]), NQKV, D);
       with_side(gp, l, 0);
       if (sg.group_on[0]) { gp.n_bounds = 2; gp.bounds[0] = NQ; gp.bounds[1] = NQ + NKV; }
-      gp.epi = EPI_STORE; gp.bias = Wf(P[P_BQ]); gp.C = w.qkv; gp.ldc = NQKV;
+      gp.epi = EPI_STORE; gp.bias = Wf(P[P_BQ]); gp.C = w.qkv; gp.ldc = NQKV; gp.c_f32 = sp;
       if ((rc = run_gemm(d, gp, big, s)) != ZO_OK) return rc;
     }
     if (!is_opt(d)) {
       ProfScope ps(ZO_PROF_NORM, s);
-      ZO_HIP(launch_qknorm_rope<T>((T*)w.qkv, M, NQKV, d.n_heads, d.n_kv_heads, d.head_dim, Wf(P[P_QNW]),
-                                   Wf(P[P_KNW]), eps, m->rope, w.row_pos, s));
+      if (sp)
+        ZO_HIP(launch_qknorm_rope<float>((float*)w.qkv, M, NQKV, d.n_heads, d.n_kv_heads, d.head_dim, Wf(P[P_QNW]),
+                                         Wf(P[P_KNW]), eps, m->rope, w.row_pos, s));
+      else
+        ZO_HIP(launch_qknorm_rope<T>((T*)w.qkv, M, NQKV, d.n_heads, d.n_kv_heads, d.head_dim, Wf(P[P_QNW]),
+                                     Wf(P[P_KNW]), eps, m->rope, w.row_pos, s));
     }
     {
       ProfScope ps(ZO_PROF_ATTENTION, s);
-      ZO_HIP(launch_attention<T>((const T*)w.qkv, NQKV, (T*)w.attn, NQ, w.phys_cu, pk.n_phys, w.work,
-                                 (int)pk.work.size(), d.n_heads, d.n_kv_heads, d.head_dim, s));
+      if (sp)
+        ZO_HIP(launch_attention_split((const float*)w.qkv, NQKV, (bf16_t*)w.attn, 2 * NQ, NQ, w.phys_cu, w.work,
+                                      (int)pk.work.size(), d.n_heads, d.n_kv_heads, d.head_dim, s));
+      else
+        ZO_HIP(launch_attention<T>((const T*)w.qkv, NQKV, (T*)w.attn, NQ, w.phys_cu, pk.n_phys, w.work,
+                                   (int)pk.work.size(), d.n_heads, d.n_kv_heads, d.head_dim, s));
     }
     if ((rc = tproj(l, 1, w.attn, NQ)) != ZO_OK) return rc;
     {
-      GemmParams gp = gemm_base(w.attn, NQ, W(P[P_WO]), NQ, M, D, NQ);
+      GemmParams gp = proj(w.attn, W(P[P_WO]), D, NQ);
       with_side(gp, l, 1);
       gp.epi = EPI_RESID; gp.bias = Wf(P[P_BO]); gp.H = w.h; gp.ldh = D;
       if ((rc = run_gemm(d, gp, big, s)) != ZO_OK) return rc;
@@ -638,14 +670,15 @@ int forward(zo_model* m, const zo_plan_s& p, const Packing& pk, const SideGeom& 
     // FFN block
     {
       ProfScope ps(ZO_PROF_NORM, s);
-      ZO_HIP(launch_norm<T>(w.h, nullptr, M, D, Wf(P[P_LN2W]), Wf(P[P_LN2B]), eps, rms, (T*)w.xa, s));
+      ZO_HIP(launch_norm<T>(w.h, nullptr, M, D, Wf(P[P_LN2W]), Wf(P[P_LN2B]), eps, rms, (T*)w.xa, (int64_t)D * x2,
+                            sp ? D : 0, s));
     }
     if ((rc = tproj(l, 2, w.xa, D)) != ZO_OK) return rc;
     {
       const int N1 = is_opt(d) ? F : 2 * F;
-      GemmParams gp = gemm_base(w.xa, D, W(P[P_W1]), D, M, N1, D);
+      GemmParams gp = proj(w.xa, W(P[P_W1]), N1, D);
       with_side(gp, l, 2);
-      gp.C = w.hid; gp.ldc = F;
+      gp.C = w.hid; gp.ldc = (int64_t)F * x2; gp.c_lo = sp ? F : 0;
       if (is_opt(d)) { gp.epi = EPI_GELU; gp.bias = Wf(P[P_B1]); }
       else gp.epi = EPI_SWIGLU;
       if ((rc = run_gemm(d, gp, big, s)) != ZO_OK) return rc;
@@ -653,7 +686,7 @@ int forward(zo_model* m, const zo_plan_s& p, const Packing& pk, const SideGeom& 
     if ((rc = tproj(l, 3, w.hid, F)) != ZO_OK) return rc;
     {
       const TLoc& w2 = is_opt(d) ? P[P_W2] : P[P_WDOWN];
-      GemmParams gp = gemm_base(w.hid, F, W(w2), F, M, D, F);
+      GemmParams gp = proj(w.hid, W(w2), D, F);
       with_side(gp, l, 3);
       gp.epi = EPI_RESID; gp.bias = is_opt(d) ? Wf(P[P_B2]) : nullptr; gp.H = w.h; gp.ldh = D;
       if ((rc = run_gemm(d, gp, big, s)) != ZO_OK) return rc;
@@ -663,11 +696,13 @@ int forward(zo_model* m, const zo_plan_s& p, const Packing& pk, const SideGeom& 
   if (S > 0) {
     {
       ProfScope ps(ZO_PROF_NORM, s);
-      ZO_HIP(launch_norm<T>(w.h, w.sc_row, S, D, Wf(Lo.g[G_FNW]), Wf(Lo.g[G_FNB]), eps, rms, (T*)w.xs, s));
+      ZO_HIP(launch_norm<T>(w.h, w.sc_row, S, D, Wf(Lo.g[G_FNW]), Wf(Lo.g[G_FNB]), eps, rms, (T*)w.xs,
+                            (int64_t)D * x2, sp ? D : 0, s));
       ZO_HIP(launch_gather_i32(tokens, w.sc_lab_src, S, w.labels, s));
     }
     const TLoc& head = is_opt(d) ? Lo.g[G_TOK] : Lo.g[G_HEAD];
-    GemmParams gp = gemm_base(w.xs, D, W(head), D, S, d.vocab, D);
+    GemmParams gp = gemm_base(w.xs, (int64_t)D * x2, W(head), D, S, d.vocab, D * x2);
+    if (sp) gp.kwb = D;
     const int bn = gemm_cfg_bn(GEMM_CFG_HEAD, bf);
     gp.epi = EPI_LMHEAD; gp.labels = w.labels; gp.part = w.part; gp.lab_logit = w.lab_logit;
     gp.n_ntiles = (d.vocab + bn - 1) / bn;
@@ -792,7 +827,10 @@ int zo_plan(const zo_model* m, const zo_plan_desc* desc, zo_plan_t** out) {
   const zo_plan_desc& d = *desc;
   ZO_CHECK(d.nu >= 1, ZO_E_INVAL, "nu must be >= 1");
   ZO_CHECK(d.rank >= 1, ZO_E_INVAL, "rank must be >= 1");
-  ZO_CHECK((d.flags & ~(ZO_PLAN_SCALE_INV_SQRT_R | ZO_PLAN_ALLOW_ZERO_EPS)) == 0, ZO_E_INVAL, "unknown plan flag");
+  ZO_CHECK((d.flags & ~(ZO_PLAN_SCALE_INV_SQRT_R | ZO_PLAN_ALLOW_ZERO_EPS | ZO_PLAN_ACT_SPLIT)) == 0, ZO_E_INVAL,
+           "unknown plan flag");
+  ZO_CHECK(!(d.flags & ZO_PLAN_ACT_SPLIT) || m->d.dtype == ZO_DTYPE_BF16, ZO_E_INVAL,
+           "ZO_PLAN_ACT_SPLIT applies to bf16 models only");
   ZO_CHECK(std::isfinite(d.eps) && (d.eps > 0 || (d.eps == 0 && (d.flags & ZO_PLAN_ALLOW_ZERO_EPS))), ZO_E_INVAL,
            "eps must be finite and > 0");
   ZO_CHECK(d.n_dirs >= 1 && d.dir_seeds, ZO_E_INVAL, "need at least one direction");
@@ -961,6 +999,8 @@ int zo_score(zo_model* m, const zo_plan_t* p, const zo_bank* bank, const zo_batc
   if (sg.any && pk.M > 0) {
     const uint64_t win = p->window();
     const int dt = bf ? 1 : 0;
+    const bool sp = split_act(*p);
+    const int64_t x3 = sp ? 3 : 1;
     const int64_t NQ = (int64_t)d.n_heads * d.head_dim, NKV = (int64_t)d.n_kv_heads * d.head_dim;
     ZO_HIP(hipMemsetAsync(w.side_begin, 0, w.side_bytes, s));   // padding rows/columns must be zero
     for (int l = 0; l < d.n_layers; ++l)
@@ -986,16 +1026,18 @@ int zo_score(zo_model* m, const zo_plan_t* p, const zo_bank* bank, const zo_batc
             const uint64_t vwin = entry ? (uint64_t)bank->windows[sg.entry_slots[j]] : win;
             SideJob v;
             memset(&v, 0, sizeof v);
-            v.dst = vt + ((int64_t)kb * sg.ks + (int64_t)j * sg.r) * sg.n_in[g] * asz;
-            v.ld = sg.n_in[g];
+            v.dst = vt + ((int64_t)kb * sg.ks + (int64_t)j * sg.r) * sg.n_in[g] * x3 * asz;
+            v.ld = sg.n_in[g] * x3;
+            v.split = sp ? sg.n_in[g] : 0;
             v.seed = seed; v.tau = vwin; v.tag = dir_tag(l, kind, 1);
             v.src = 0; v.n = ksh.n_in; v.r = sg.r; v.dtype = dt;
             jobs.push_back(v);
             max_items = std::max<int64_t>(max_items, (ksh.n_in * sg.r + 3) / 4);
             SideJob u;
             memset(&u, 0, sizeof u);
-            u.dst = bs + row_base * sg.bs_cols[g] * asz;
-            u.ld = sg.bs_cols[g];
+            u.dst = bs + row_base * sg.bs_cols[g] * x3 * asz;
+            u.ld = sg.bs_cols[g] * x3;
+            u.split = sp ? sg.bs_cols[g] : 0;
             u.col0 = (int32_t)(col_base + (int64_t)j * sg.r);
             u.row_map = row_map;
             u.n = ksh.n_out; u.r = sg.r; u.dtype = dt;
