@@ -69,6 +69,50 @@ def base_gemm_flops(cfg, rows):
     return total * cfg.n_layers
 
 
+def group_kinds(cfg):
+    """Input groups of the side-input projection: linears that read the same activations."""
+    if cfg.arch == "opt":
+        return [("q", "k", "v"), ("o",), ("fc1",), ("fc2",)]
+    return [("q", "k", "v"), ("o",), ("gate", "up"), ("down",)]
+
+
+def hbm_bytes_per_step(cfg, wl, rows, scored, n_entries):
+    """Algorithmic HBM bytes per step of the bandwidth-bound kernel classes: every tensor
+    read or written once, no padding, no re-reads (the unit the HBM fractions use)."""
+    split = wl.act_split
+    a = 2 * (2 if split else 1)          # bytes per activation element fed to a bf16 GEMM
+    d, f, L = cfg.d_model, cfg.d_ffn, cfg.n_layers
+    nq, nkv = cfg.n_heads * cfg.head_dim, cfg.n_kv_heads * cfg.head_dim
+    w = 2 if cfg.dtype == "bf16" else 4
+    r, q = wl.rank, wl.n_dirs
+    used = (n_entries + q) * r
+    out = {}
+    # embedding (+ learned positions), two norms per layer, final norm, QK-norm + RoPE
+    nb = rows * d * (w * (2 if cfg.arch == "opt" else 1) + 4)
+    nb += 2 * L * rows * d * (4 + a) + scored * d * (4 + a)
+    if cfg.arch != "opt":
+        nb += L * rows * (nq + nkv) * 2 * (4 if split else w)
+    out["norm"] = nb
+    qkv_b = 4 if split else w
+    out["attention"] = L * rows * ((nq + 2 * nkv) * qkv_b + nq * a)
+    side = 0
+    prep = 0
+    for kinds in group_kinds(cfg):
+        tk = [k for k in kinds if k in wl.targets]
+        if not tk:
+            continue
+        n_in = cfg.linear_shape(tk[0])[1]
+        side += rows * n_in * a + len(tk) * used * n_in * 2 * (3 if split else 1) + rows * len(tk) * used * a
+        for k in tk:
+            n_out = cfg.linear_shape(k)[0]
+            prep += used * (n_in + n_out) * 2 * (3 if split else 1) + n_entries * r * n_out * 4
+    out["gemm_side"] = L * side
+    out["side_prep"] = L * prep
+    out["gemm_head"] = cfg.vocab * d * w + scored * d * a + scored * ((cfg.vocab + 127) // 128) * 8
+    out["update"] = q * L * sum(cfg.linear_shape(k)[0] * r * 8 for k in wl.targets)
+    return out
+
+
 def describe(wl):
     m = wl.model
     return ("%s: %s-shaped %d x d%d, heads %d/%d x %d, FFN %d, vocab %d, %s weights; %d prompts U[%d,%d]%s, "
@@ -129,7 +173,7 @@ def cpu_baseline(wl, batch):
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--workload", default="opt13b")
     ap.add_argument("--lr", type=float, default=1e-4)
@@ -228,6 +272,32 @@ def main():
         "breakdown_ms_per_step": {k: round(v[1] / args.steps, 3) for k, v in prof.items()},
         "launches_per_step": {k: v[0] / args.steps for k, v in prof.items()},
     }
+    # bandwidth-bound classes: algorithmic bytes per step / class time per step
+    n_entries = sum(1 for w in bank.keys()[1] if w >= 0)
+    hb = hbm_bytes_per_step(cfg, wl, rows, int(out["n_scored"]), n_entries)
+    hbm = {}
+    for k, b in hb.items():
+        ms = prof[k][1] / args.steps
+        if ms > 0:
+            gbs = b / (ms / 1e3) / 1e9
+            hbm[k] = {"achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                      "frac": round(gbs / PEAK_HBM_GBS, 4), "algorithmic_mb_per_step": round(b / 1e6, 2)}
+    line["hbm_kernels"] = hbm
+    # side-path cost: the projections' time with the side columns vs a plan with no targets
+    if wl.targets:
+        n_off = min(args.steps, 3)
+        wl0 = wl.with_(targets=())
+        zo.api.profile_begin()
+        for k in range(n_off):
+            zo.score(model, zo.Plan.from_workload(model, wl0, t=0), None, db)
+        torch.cuda.synchronize()
+        p0 = zo.api.profile_end()
+        base_on = prof["gemm_base"][1] / args.steps
+        base_off = p0["gemm_base"][1] / n_off
+        line["side_path"] = {
+            "gemm_base_ms_with_side": round(base_on, 3), "gemm_base_ms_without": round(base_off, 3),
+            "extended_k_overhead": round(base_on / base_off - 1.0, 4),
+            "total_ms_per_step": round(base_on - base_off + (prof["gemm_side"][1] + prof["side_prep"][1]) / args.steps, 3)}
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, batch)
     print(json.dumps(line), flush=True)

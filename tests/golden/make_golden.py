@@ -4,8 +4,9 @@ Calls only oracle/ (and the seeded input generators in synth/).  For each
 workload, the state is: one lazy update at step 0 with the fixed coefficients
 C_FIXED and learning rate LR, then scoring at step 1 (so the bank holds a
 non-zero entry, as in a running fine-tuning job).  The oracle scores a sample
-of the physical sequences of the full batch (all of them for opt1.3b) in
-fp64 on the bf16-rounded weights.
+of the physical sequences of the full batch (all of them for opt1.3b and
+opt13b, which also gives S and c per candidate) in fp64 on the bf16-rounded
+weights.
 
     python tests/golden/make_golden.py [workload ...]
 """
@@ -29,14 +30,12 @@ C_FIXED = [2.5, -1.75, 0.5, -3.0]
 
 def sample(wl, batch, phys):
     """Physical sequences checked at full size."""
-    if wl.name == "opt1.3b":
+    if wl.name in ("opt1.3b", "opt13b"):          # every sequence: S and c per candidate
         return list(range(len(phys)))
     lens = batch.lengths
     probes = [i for i in range(batch.n_seq) if batch.role[i] == 0]
     by_len = sorted(probes, key=lambda i: lens[i])
-    if wl.name == "opt13b":
-        pick = [by_len[0], by_len[len(by_len) // 2], by_len[-1]]
-    elif wl.name == "opt6.7b-mezo":
+    if wl.name == "opt6.7b-mezo":
         pick = [probes[0]]
     else:                                          # qwen3 mixed: two probes, two foreground
         pick = [by_len[0], by_len[-1]]

@@ -162,13 +162,195 @@ attn_bf16_kernel(const bf16_t* __restrict__ qkv, int ld, bf16_t* __restrict__ ou
   }
 }
 
-// fp32 path: one thread per query row, online softmax in registers.  The output
-// is fp32, or (lo_off > 0) the two-term bf16 expansion hi | lo that feeds the
-// next bf16 projection.
+// Two-term path (bf16 weights, ZO_PLAN_ACT_SPLIT): q|k|v arrive in fp32 and every
+// MFMA operand is split as x = hi + lo (bf16 each, 16 significant bits); each
+// product is formed as hi.hi + lo.hi + hi.lo (the lo.lo term is below 2^-17
+// relative), for S^T = K Q^T and for O^T += V^T P^T alike, with the same
+// layout as the bf16 kernel.  The output is written as hi | lo for the next
+// projection.
+__device__ __forceinline__ void split8(const float* v, bf16x8_t& hi, bf16x8_t& lo) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    bf16_t h, l;
+    split_bf16(v[e], h, l);
+    hi[e] = __builtin_bit_cast(__bf16, h);
+    lo[e] = __builtin_bit_cast(__bf16, l);
+  }
+}
+
+__device__ __forceinline__ floatx4_t mfma3(bf16x8_t ah, bf16x8_t al, bf16x8_t bh, bf16x8_t bl, floatx4_t c) {
+  c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bh, c, 0, 0, 0);
+  c = __builtin_amdgcn_mfma_f32_16x16x32_bf16(al, bh, c, 0, 0, 0);
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(ah, bl, c, 0, 0, 0);
+}
+
 template <int HD>
-__global__ void attn_f32_kernel(const float* __restrict__ qkv, int ld, void* __restrict__ out, int ld_out,
-                                int lo_off, const int32_t* __restrict__ cu, const int32_t* __restrict__ work, int hq,
-                                int hkv, float scale) {
+__global__ void __launch_bounds__(256)
+attn_split_kernel(const float* __restrict__ qkv, int ld, bf16_t* __restrict__ out, int ld_out, int lo_off,
+                  const int32_t* __restrict__ cu, const int32_t* __restrict__ work, int hq, int hkv,
+                  float scale_log2) {
+  constexpr int KS = HD / 32;
+  constexpr int HB = HD / 16;
+  constexpr int VT_LD = KB + 8;
+  __shared__ __align__(16) bf16_t sK[2][KB * HD];        // hi, lo: [key][hd], 16-byte chunks XOR-swizzled
+  __shared__ __align__(16) bf16_t sVt[2][HD * VT_LD];    // hi, lo: [hd][key] (+8 pad)
+
+  const int w = work[blockIdx.x];
+  const int seq = w >> 12, qblk = w & 4095;
+  const int h = blockIdx.y;
+  const int kvh = h / (hq / hkv);
+  const int base = cu[seq], len = cu[seq + 1] - base;
+  const int q0 = qblk * QB;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int lr = lane & 15, g = lane >> 4;
+  const int kcol = hq * HD + kvh * HD;
+  const int vcol = hq * HD + hkv * HD + kvh * HD;
+  constexpr int SWZ = (HD / 8 < 8 ? HD / 8 : 8) - 1;
+
+  const int qi = q0 + wave * 16 + lr;
+  const int qrow = base + min(qi, len - 1);
+  bf16x8_t qh[KS], ql[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const float* src = qkv + (int64_t)qrow * ld + h * HD + ks * 32 + g * 8;
+    float v[8];
+    *(floatx4_t*)v = *(const floatx4_t*)src;
+    *(floatx4_t*)(v + 4) = *(const floatx4_t*)(src + 4);
+    split8(v, qh[ks], ql[ks]);
+  }
+
+  floatx4_t acc[HB];
+#pragma unroll
+  for (int i = 0; i < HB; ++i) acc[i] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  const int q_last = min(q0 + QB, len) - 1;
+  const int n_kt = q_last / KB + 1;
+  for (int kt = 0; kt < n_kt; ++kt) {
+    const int k0 = kt * KB;
+    __syncthreads();
+    constexpr int CH = HD / 8;                      // 8-element chunks per row
+    for (int c = tid; c < KB * CH; c += 256) {
+      const int kr = c / CH, ch = c % CH;
+      const int krow = base + min(k0 + kr, len - 1);
+      const float* src = qkv + (int64_t)krow * ld + kcol + ch * 8;
+      float v[8];
+      *(floatx4_t*)v = *(const floatx4_t*)src;
+      *(floatx4_t*)(v + 4) = *(const floatx4_t*)(src + 4);
+      bf16x8_t hi, lo;
+      split8(v, hi, lo);
+      const int o = kr * HD + ((ch ^ (kr & SWZ)) << 3);
+      *(bf16x8_t*)(sK[0] + o) = hi;
+      *(bf16x8_t*)(sK[1] + o) = lo;
+    }
+    // V^T: 4 consecutive keys of one 8-wide head-dim chunk per thread, transposed in
+    // registers, 8-byte writes of 4 keys into 8 rows of each plane
+    for (int c = tid; c < (KB / 4) * CH; c += 256) {
+      const int kg = c % (KB / 4), ch = c / (KB / 4);
+      bf16_t vh[4][8], vl[4][8];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const int krow = base + min(k0 + kg * 4 + u, len - 1);
+        const float* src = qkv + (int64_t)krow * ld + vcol + ch * 8;
+        float v[8];
+        *(floatx4_t*)v = *(const floatx4_t*)src;
+        *(floatx4_t*)(v + 4) = *(const floatx4_t*)(src + 4);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) split_bf16(v[e], vh[u][e], vl[u][e]);
+      }
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int o = (ch * 8 + e) * VT_LD + kg * 4;
+        *(uint2*)(sVt[0] + o) = make_uint2((uint32_t)vh[0][e] | ((uint32_t)vh[1][e] << 16),
+                                          (uint32_t)vh[2][e] | ((uint32_t)vh[3][e] << 16));
+        *(uint2*)(sVt[1] + o) = make_uint2((uint32_t)vl[0][e] | ((uint32_t)vl[1][e] << 16),
+                                          (uint32_t)vl[2][e] | ((uint32_t)vl[3][e] << 16));
+      }
+    }
+    __syncthreads();
+    floatx4_t s[4];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb) {
+      s[kb] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+      const int kr = kb * 16 + lr;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const int o = kr * HD + (((ks * 4 + g) ^ (kr & SWZ)) << 3);
+        const bf16x8_t kh = *(const bf16x8_t*)(sK[0] + o), kl = *(const bf16x8_t*)(sK[1] + o);
+        s[kb] = mfma3(kh, kl, qh[ks], ql[ks], s[kb]);
+      }
+    }
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int key = k0 + kb * 16 + 4 * g + j;
+        float v = s[kb][j] * scale_log2;
+        if (key > qi || key >= len) v = -INFINITY;
+        s[kb][j] = v;
+        mx = fmaxf(mx, v);
+      }
+    mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
+    mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    const float m_new = fmaxf(m_run, mx);
+    const float alpha = (m_run == -INFINITY) ? 0.f : exp2f(m_run - m_new);
+    float psum = 0.f;
+    bf16x8_t ph[2], pl[2];
+#pragma unroll
+    for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float pv = (s[kb][j] == -INFINITY) ? 0.f : exp2f(s[kb][j] - m_new);
+        psum += pv;
+        bf16_t hb, lb;
+        split_bf16(pv, hb, lb);
+        ph[kb >> 1][(kb & 1) * 4 + j] = __builtin_bit_cast(__bf16, hb);
+        pl[kb >> 1][(kb & 1) * 4 + j] = __builtin_bit_cast(__bf16, lb);
+      }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+#pragma unroll
+    for (int i = 0; i < HB; ++i) acc[i] *= alpha;
+#pragma unroll
+    for (int t = 0; t < 2; ++t)
+#pragma unroll
+      for (int hb = 0; hb < HB; ++hb) {
+        bf16x8_t vf[2];
+#pragma unroll
+        for (int pl_ = 0; pl_ < 2; ++pl_) {
+          const bf16_t* vr = sVt[pl_] + (hb * 16 + lr) * VT_LD + t * 32 + 4 * g;
+          const uint2 a = *(const uint2*)(vr);
+          const uint2 b = *(const uint2*)(vr + 16);
+          vf[pl_] = __builtin_bit_cast(bf16x8_t, u32x4_t{a.x, a.y, b.x, b.y});
+        }
+        acc[hb] = mfma3(vf[0], vf[1], ph[t], pl[t], acc[hb]);
+      }
+  }
+  float lsum = l_run;
+  lsum += __shfl_xor(lsum, 16, 64);
+  lsum += __shfl_xor(lsum, 32, 64);
+  if (qi < len) {
+    const float inv = 1.0f / lsum;
+    bf16_t* orow = out + (int64_t)(base + qi) * ld_out + h * HD;
+#pragma unroll
+    for (int hb = 0; hb < HB; ++hb) {
+      bf16_t hi[4], lo[4];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) split_bf16(acc[hb][q] * inv, hi[q], lo[q]);
+      *(uint2*)(orow + hb * 16 + 4 * g) =
+          make_uint2((uint32_t)hi[0] | ((uint32_t)hi[1] << 16), (uint32_t)hi[2] | ((uint32_t)hi[3] << 16));
+      *(uint2*)(orow + lo_off + hb * 16 + 4 * g) =
+          make_uint2((uint32_t)lo[0] | ((uint32_t)lo[1] << 16), (uint32_t)lo[2] | ((uint32_t)lo[3] << 16));
+    }
+  }
+}
+
+// fp32 path: one thread per query row, online softmax in registers.
+template <int HD>
+__global__ void attn_f32_kernel(const float* __restrict__ qkv, int ld, float* __restrict__ out, int ld_out,
+                                const int32_t* __restrict__ cu, const int32_t* __restrict__ work, int hq, int hkv,
+                                float scale) {
   const int w = work[blockIdx.x];
   const int seq = w >> 12, qblk = w & 4095;
   const int h = blockIdx.y;
@@ -195,31 +377,9 @@ __global__ void attn_f32_kernel(const float* __restrict__ qkv, int ld, void* __r
     for (int i = 0; i < HD; ++i) o[i] = o[i] * a + p * vr[i];
     m = mn;
   }
-  const int64_t ob = (int64_t)(base + qi) * ld_out + h * HD;
-  if (lo_off) {
-    bf16_t* orow = (bf16_t*)out + ob;
+  float* orow = out + (int64_t)(base + qi) * ld_out + h * HD;
 #pragma unroll
-    for (int i = 0; i < HD; ++i) split_bf16(o[i] / l, orow[i], orow[i + lo_off]);
-  } else {
-    float* orow = (float*)out + ob;
-#pragma unroll
-    for (int i = 0; i < HD; ++i) orow[i] = o[i] / l;
-  }
-}
-
-hipError_t launch_attn_f32(const float* qkv, int ld_qkv, void* out, int ld_out, int lo_off, const int32_t* cu,
-                           const int32_t* work, int n_work, int hq, int hkv, int hd, hipStream_t s) {
-  if (n_work <= 0) return hipSuccess;
-  const float scale = (float)(1.0 / sqrt((double)hd));
-  dim3 grid(n_work, hq);
-  switch (hd) {
-    case 16: hipLaunchKernelGGL(attn_f32_kernel<16>, grid, dim3(QB), 0, s, qkv, ld_qkv, out, ld_out, lo_off, cu, work, hq, hkv, scale); break;
-    case 32: hipLaunchKernelGGL(attn_f32_kernel<32>, grid, dim3(QB), 0, s, qkv, ld_qkv, out, ld_out, lo_off, cu, work, hq, hkv, scale); break;
-    case 64: hipLaunchKernelGGL(attn_f32_kernel<64>, grid, dim3(QB), 0, s, qkv, ld_qkv, out, ld_out, lo_off, cu, work, hq, hkv, scale); break;
-    case 128: hipLaunchKernelGGL(attn_f32_kernel<128>, grid, dim3(QB), 0, s, qkv, ld_qkv, out, ld_out, lo_off, cu, work, hq, hkv, scale); break;
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
+  for (int i = 0; i < HD; ++i) orow[i] = o[i] / l;
 }
 
 }  // namespace
@@ -246,12 +406,31 @@ hipError_t launch_attention<float>(const float* qkv, int ld_qkv, float* out, int
                                    int n_seq, const int32_t* work, int n_work, int hq, int hkv, int hd,
                                    hipStream_t s) {
   (void)n_seq;
-  return launch_attn_f32(qkv, ld_qkv, out, ld_out, 0, cu, work, n_work, hq, hkv, hd, s);
+  if (n_work <= 0) return hipSuccess;
+  const float scale = (float)(1.0 / sqrt((double)hd));
+  dim3 grid(n_work, hq);
+  switch (hd) {
+    case 16: hipLaunchKernelGGL(attn_f32_kernel<16>, grid, dim3(QB), 0, s, qkv, ld_qkv, out, ld_out, cu, work, hq, hkv, scale); break;
+    case 32: hipLaunchKernelGGL(attn_f32_kernel<32>, grid, dim3(QB), 0, s, qkv, ld_qkv, out, ld_out, cu, work, hq, hkv, scale); break;
+    case 64: hipLaunchKernelGGL(attn_f32_kernel<64>, grid, dim3(QB), 0, s, qkv, ld_qkv, out, ld_out, cu, work, hq, hkv, scale); break;
+    case 128: hipLaunchKernelGGL(attn_f32_kernel<128>, grid, dim3(QB), 0, s, qkv, ld_qkv, out, ld_out, cu, work, hq, hkv, scale); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 hipError_t launch_attention_split(const float* qkv, int ld_qkv, bf16_t* out, int ld_out, int lo_off,
                                   const int32_t* cu, const int32_t* work, int n_work, int hq, int hkv, int hd,
                                   hipStream_t s) {
-  if (lo_off <= 0) return hipErrorInvalidValue;
-  return launch_attn_f32(qkv, ld_qkv, out, ld_out, lo_off, cu, work, n_work, hq, hkv, hd, s);
+  if (lo_off <= 0 || lo_off % 4 != 0 || ld_out % 4 != 0 || ld_qkv % 4 != 0) return hipErrorInvalidValue;
+  if (n_work <= 0) return hipSuccess;
+  const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)hd));
+  dim3 grid(n_work, hq);
+  switch (hd) {
+    case 32: hipLaunchKernelGGL(attn_split_kernel<32>, grid, dim3(256), 0, s, qkv, ld_qkv, out, ld_out, lo_off, cu, work, hq, hkv, scale_log2); break;
+    case 64: hipLaunchKernelGGL(attn_split_kernel<64>, grid, dim3(256), 0, s, qkv, ld_qkv, out, ld_out, lo_off, cu, work, hq, hkv, scale_log2); break;
+    case 128: hipLaunchKernelGGL(attn_split_kernel<128>, grid, dim3(256), 0, s, qkv, ld_qkv, out, ld_out, lo_off, cu, work, hq, hkv, scale_log2); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
