@@ -178,6 +178,8 @@ def main():
     ap.add_argument("--workload", default="opt13b")
     ap.add_argument("--lr", type=float, default=1e-4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-side-check", action="store_true",
+                    help="skip the extra scoring without side path that measures its cost (for profiler runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (counter calibration for the traffic figure)")
     args = ap.parse_args()
@@ -284,7 +286,7 @@ def main():
                       "frac": round(gbs / PEAK_HBM_GBS, 4), "algorithmic_mb_per_step": round(b / 1e6, 2)}
     line["hbm_kernels"] = hbm
     # side-path cost: the projections' time with the side columns vs a plan with no targets
-    if wl.targets:
+    if wl.targets and not args.no_side_check:
         n_off = min(args.steps, 3)
         wl0 = wl.with_(targets=())
         zo.api.profile_begin()

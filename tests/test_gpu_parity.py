@@ -14,8 +14,8 @@ import pytest
 from oracle import zo as ozo
 from synth import configs, inputs
 
-from .gpu_common import (SMALL_OPT_BF16, SMALL_QWEN_BF16, SMALL_QWEN_F32, GpuRun, OracleRun, flush, need_gpu,
-                         workload)
+from .gpu_common import (SMALL_OPT_BF16, SMALL_OPT_ODD, SMALL_QWEN_BF16, SMALL_QWEN_F32, GpuRun, OracleRun, flush,
+                         need_gpu, workload)
 
 pytestmark = pytest.mark.gpu
 
@@ -173,6 +173,40 @@ def test_high_rank_multi_direction():
     tok = gs["tok_logp"].cpu().numpy()
     allref = np.concatenate([os_["tok_logp"][p] for p in range(len(os_["phys"]))])
     assert np.max(np.abs(tok - allref)) <= 2e-2
+
+
+@pytest.mark.parametrize("split", [False, True], ids=["bf16", "split"])
+def test_projection_widths_not_multiple_of_tile(split):
+    """d = 320, FFN 1280: the o-proj and fc2 outputs (N = 320) end inside a 256-wide
+    column tile, and so does the QKV output (N = 960); side path on o, fc1, fc2 (the
+    q/k/v boundaries are not tile multiples, which the library rejects for targets)."""
+    need_gpu()
+    wl = workload(SMALL_OPT_ODD, targets=("o", "fc1", "fc2"), dir_seeds=(2, 5), n_fg=2, n_prompts=3,
+                  act_split=split)
+    batch = inputs.make_batch(wl)
+    g, o = GpuRun(wl), OracleRun(wl)
+    c = np.array([1.3, -0.6])
+    g.update(0, c, 5e-3)
+    o.update(0, c, 5e-3)
+    gs, os_ = g.score(1, batch), o.score(1, batch)
+    err = _seq_close(gs, os_, 5e-4 if split else 2e-2)
+    flush("odd widths (split %s): max per-sequence err %.3g" % (split, err))
+    tok = gs["tok_logp"].cpu().numpy()
+    allref = np.concatenate([os_["tok_logp"][p] for p in range(len(os_["phys"]))])
+    assert np.max(np.abs(tok - allref)) <= (5e-4 if split else 2e-2)
+
+
+def test_qkv_side_targets_off_tile_boundary_rejected():
+    """q/k/v targets on a model whose q|k|v boundaries are not column-tile multiples:
+    zo_score refuses with ZO_E_SHAPE instead of mixing kinds inside a tile."""
+    need_gpu()
+    import zeroth_order_fine_amd as zo
+    wl = workload(SMALL_OPT_ODD, targets=("q", "v"), n_prompts=2)
+    batch = inputs.make_batch(wl)
+    g = GpuRun(wl)
+    with pytest.raises(zo.ZoError) as ei:
+        g.score(0, batch)
+    assert ei.value.code == -2
 
 
 def test_multi_step_trajectory_with_window_rollover():

@@ -367,7 +367,35 @@ __device__ __forceinline__ void epilogue_rows(const GemmParams& p, floatx4_t (&a
                                               int wn, int lane) {
   const int rb = m0 + wm * WM + (lane & 15);
   const int cb = n0 + wn * WN + 4 * (lane >> 4);
-  if constexpr (EPI == EPI_SWIGLU) {
+  if constexpr (EPI == EPI_TPROJ) {
+    // side input t: columns of x.[V...] kept for the bank entries, scaled by s * eps~
+    // for the row's own direction, zero elsewhere (as in the register-staged epilogue)
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int r = rb + i * 16;
+      if (r >= p.M) continue;
+      const int cand = p.row_cand[r];
+      const int cdir = cand >= 0 ? p.cand_dir[cand] : -1;
+      const float cscale = cand >= 0 ? p.cand_scale[cand] : 0.f;
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        if (cb + j * 16 >= p.N) continue;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const int c = cb + j * 16 + q;
+          const int w = c % p.tp_ks;
+          float o = 0.f;
+          if (cand >= 0 && w < p.tp_used) {
+            const int slot = w / p.tp_rank;
+            if (slot < p.tp_entries) o = acc[i][j][q];
+            else if (slot - p.tp_entries == cdir) o = cscale * acc[i][j][q];
+          }
+          store_tproj<bf16_t>(p, r, c, o);
+        }
+      }
+    }
+    return;
+  } else if constexpr (EPI == EPI_SWIGLU) {
     // packed rows: blocks of 16 gate rows then 16 up rows; output column = gate index
     const int ob = (n0 + wn * WN) / 2 + 4 * (lane >> 4);
 #pragma unroll
@@ -376,6 +404,7 @@ __device__ __forceinline__ void epilogue_rows(const GemmParams& p, floatx4_t (&a
       if (r >= p.M) continue;
 #pragma unroll
       for (int jp = 0; jp < TN / 2; ++jp) {
+        if (cb + 2 * jp * 16 >= p.N) continue;                  // N is a multiple of 32 here
         const floatx4_t g = acc[i][2 * jp], u = acc[i][2 * jp + 1];
         floatx4_t v;
 #pragma unroll
@@ -385,16 +414,19 @@ __device__ __forceinline__ void epilogue_rows(const GemmParams& p, floatx4_t (&a
     }
     return;
   } else {
+    // a lane's four columns are all inside N or all outside (N is a multiple of 16)
     floatx4_t bias[TN];
 #pragma unroll
     for (int j = 0; j < TN; ++j)
-      bias[j] = p.bias ? *(const floatx4_t*)(p.bias + cb + j * 16) : floatx4_t{0.f, 0.f, 0.f, 0.f};
+      bias[j] = (p.bias && cb + j * 16 < p.N) ? *(const floatx4_t*)(p.bias + cb + j * 16)
+                                              : floatx4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       const int r = rb + i * 16;
       if (r >= p.M) continue;
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
+        if (cb + j * 16 >= p.N) continue;
         floatx4_t v = acc[i][j] + bias[j];
         if constexpr (EPI == EPI_RESID) {
           floatx4_t* hp = (floatx4_t*)(p.H + (int64_t)r * p.ldh + cb + j * 16);
@@ -718,12 +750,19 @@ hipError_t gemm_launch_bf16(const GemmParams& p, int cfg, hipStream_t s) {
     }
   }
   if (cfg == GEMM_CFG_NARROW) {
+    // many factor columns (high rank, several entries): the pipelined projection kernel
+    if (p.epi == EPI_TPROJ && p.N >= 512 && p.N % 16 == 0 && p.K % 32 == 0 && p.ksplit <= 1)
+      return launch_bf16_pipe<256, 256, 128, 64, 4, EPI_TPROJ>(p, s);
     if (p.epi == EPI_TPROJ) {
-      if (p.ksplit <= 1) return launch_bf16<64, 128, 32, 64, EPI_TPROJ>(p, s);
+      // N <= 32 (one kind block at rank <= 8 and few entries): a 128 x 32 tile, so the
+      // factor rows are not re-read for absent columns
+      const bool thin = p.N <= 32;
+      if (p.ksplit <= 1)
+        return thin ? launch_bf16<128, 32, 32, 32, EPI_TPROJ>(p, s) : launch_bf16<64, 128, 32, 64, EPI_TPROJ>(p, s);
       // split-K partial sums, then a fixed-order reduction that applies the epilogue
       GemmParams q = p;
       q.epi = EPI_PARTIAL;
-      hipError_t e = launch_bf16<64, 128, 32, 64, EPI_PARTIAL>(q, s);
+      hipError_t e = thin ? launch_bf16<128, 32, 32, 32, EPI_PARTIAL>(q, s) : launch_bf16<64, 128, 32, 64, EPI_PARTIAL>(q, s);
       if (e != hipSuccess) return e;
       return launch_tproj_reduce(p, s);
     }
