@@ -74,11 +74,13 @@ struct GemmParams {
   // TPROJ
   const int32_t* row_cand;    // [M] candidate or -1
   const int32_t* cand_dir;    // [n_cand]
+  const int32_t* cand_slot;   // [n_cand] computed t slot of the candidate's direction
   const float* cand_scale;    // [n_cand] sign * eps_tilde
-  int tp_ks;                  // columns per kind block
+  int tp_ks;                  // computed columns per kind block (nc * r, padded)
   int tp_rank;                // r
-  int tp_entries;             // E active bank entries (slots before the direction slots)
-  int tp_used;                // (E + q) * r used columns per kind block
+  int tp_entries;             // E active bank entries (computed slots and As blocks before the directions)
+  int tp_used;                // nc * r computed columns per kind block
+  int tp_as_ks;               // As columns per kind block ((E + q) * r, padded)
   int tp_unit;                // 0, or write t as two-term bf16: column c of unit u = c / tp_unit goes to
                               // u * 2 tp_unit + c % tp_unit (hi) and + tp_unit more (lo)
   // LMHEAD

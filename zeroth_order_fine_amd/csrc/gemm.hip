@@ -67,7 +67,27 @@ __device__ __forceinline__ void store_act(const GemmParams& p, int64_t o, float 
   }
 }
 
-// side input t of row r, column c (see tp_unit)
+template <typename TAct>
+__device__ __forceinline__ void store_tproj(const GemmParams& p, int r, int c, float v);
+
+// Side input of row r from computed column c = x.V (kind block c / tp_ks, computed
+// slot (c % tp_ks) / r): a bank entry's slot goes to the entry's As block; the slot
+// of the row's own direction also goes, times s * eps~, to that direction's As
+// block.  Nothing else is written (As is zero-filled once per call; foreground rows
+// and other directions keep zeros).
+template <typename TAct>
+__device__ __forceinline__ void tproj_out(const GemmParams& p, int r, int c, float v, int cand) {
+  if (cand < 0) return;
+  const int kb = c / p.tp_ks, w = c - kb * p.tp_ks;
+  if (w >= p.tp_used) return;
+  const int slot = w / p.tp_rank, k = w - slot * p.tp_rank;
+  const int base = kb * p.tp_as_ks + k;
+  if (slot < p.tp_entries) store_tproj<TAct>(p, r, base + slot * p.tp_rank, v);
+  if (slot == p.cand_slot[cand])
+    store_tproj<TAct>(p, r, base + (p.tp_entries + p.cand_dir[cand]) * p.tp_rank, p.cand_scale[cand] * v);
+}
+
+// side input t of row r, As column c (see tp_unit)
 template <typename TAct>
 __device__ __forceinline__ void store_tproj(const GemmParams& p, int r, int c, float v) {
   if constexpr (std::is_same<TAct, float>::value) {
@@ -102,26 +122,15 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, floatx4_t (&acc)[T
       for (int q = 0; q < 4; ++q) {
         const int r = rbase + i * 16 + q;
         if (r >= p.M) continue;
-        int cand = -1, cdir = -1;
-        float cscale = 0.f;
-        if constexpr (epi == EPI_TPROJ) {
-          cand = p.row_cand[r];
-          if (cand >= 0) { cdir = p.cand_dir[cand]; cscale = p.cand_scale[cand]; }
-        }
+        int cand = -1;
+        if constexpr (epi == EPI_TPROJ) cand = p.row_cand[r];
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
           const int c = cbase + j * 16;
           if (c >= p.N) continue;
           float v = acc[i][j][q];
           if constexpr (epi == EPI_TPROJ) {
-            int w = c % p.tp_ks;
-            float o = 0.f;
-            if (cand >= 0 && w < p.tp_used) {
-              int slot = w / p.tp_rank;
-              if (slot < p.tp_entries) o = v;
-              else if (slot - p.tp_entries == cdir) o = cscale * v;
-            }
-            store_tproj<TAct>(p, r, c, o);
+            tproj_out<TAct>(p, r, c, v, cand);
           } else {
             if (p.bias) v += p.bias[c];
             if constexpr (epi == EPI_RESID) {
@@ -375,23 +384,12 @@ __device__ __forceinline__ void epilogue_rows(const GemmParams& p, floatx4_t (&a
       const int r = rb + i * 16;
       if (r >= p.M) continue;
       const int cand = p.row_cand[r];
-      const int cdir = cand >= 0 ? p.cand_dir[cand] : -1;
-      const float cscale = cand >= 0 ? p.cand_scale[cand] : 0.f;
+      if (cand < 0) continue;
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
         if (cb + j * 16 >= p.N) continue;
 #pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int c = cb + j * 16 + q;
-          const int w = c % p.tp_ks;
-          float o = 0.f;
-          if (cand >= 0 && w < p.tp_used) {
-            const int slot = w / p.tp_rank;
-            if (slot < p.tp_entries) o = acc[i][j][q];
-            else if (slot - p.tp_entries == cdir) o = cscale * acc[i][j][q];
-          }
-          store_tproj<bf16_t>(p, r, c, o);
-        }
+        for (int q = 0; q < 4; ++q) tproj_out<bf16_t>(p, r, cb + j * 16 + q, acc[i][j][q], cand);
       }
     }
     return;
@@ -695,15 +693,7 @@ __global__ void tproj_reduce_kernel(GemmParams p) {
     const int r = (int)(e / p.N), c = (int)(e - (int64_t)r * p.N);
     float v = 0.f;
     for (int z = 0; z < p.ksplit; ++z) v += p.partial[(int64_t)z * n + e];
-    const int cand = p.row_cand[r];
-    const int w = c % p.tp_ks;
-    float o = 0.f;
-    if (cand >= 0 && w < p.tp_used) {
-      const int slot = w / p.tp_rank;
-      if (slot < p.tp_entries) o = v;
-      else if (slot - p.tp_entries == p.cand_dir[cand]) o = p.cand_scale[cand] * v;
-    }
-    store_tproj<TAct>(p, r, c, o);
+    tproj_out<TAct>(p, r, c, v, p.row_cand[r]);
   }
 }
 

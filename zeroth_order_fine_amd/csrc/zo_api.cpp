@@ -375,14 +375,23 @@ void build_packing(const zo_plan_s& p, const zo_batch& b, Packing& pk) {
 }
 
 // Side-path geometry of a plan + bank (independent of the batch contents).
+// Side-path geometry.  Per target kind, As holds (E + q) blocks of r columns (E bank
+// entries, then one block per direction; ks columns with padding) and Bs the matching
+// [U_j | G_d].  The side-input projection computes t only for the distinct V factors:
+// a direction whose (seed, window) is a bank entry's key has the entry's V, so its t is
+// the entry's and is not computed twice (nc = E + directions without an entry).
 struct SideGeom {
   bool any = false;
   int E = 0, q = 0, r = 0;
-  int used = 0, ks = 0;
+  int used = 0, ks = 0;             // As columns per kind: (E + q) r, padded to ks
+  int nc = 0, ks_c = 0;             // computed t slots and their columns per kind (padded)
   std::vector<int> entry_slots;     // active bank slots in slot order
+  std::vector<int> dslot;           // per direction: its computed t slot (< E: an entry's)
+  std::vector<int> cdirs;           // computed slots >= E: their direction
   std::vector<Group> groups;
   std::vector<bool> group_on;       // group has at least one target kind
-  std::vector<int64_t> vt_rows;     // rows of the group's V^T block (per layer)
+  std::vector<int64_t> vt_rows;     // rows of the group's V^T block = computed t columns (per layer)
+  std::vector<int64_t> as_cols;     // As columns of the group (kinds x ks)
   std::vector<int64_t> bs_cols;     // ks_tile of the group's GEMM
   std::vector<int64_t> bs_rows;     // physical output rows of the group's GEMM
   std::vector<int64_t> n_in;
@@ -403,6 +412,19 @@ int side_geometry(const zo_model* m, const zo_plan_s& p, const zo_bank* bank, Si
   const int bk = gemm_bk(d.dtype == ZO_DTYPE_BF16);
   sg.used = (sg.E + sg.q) * sg.r;
   sg.ks = (int)round_up(sg.used, bk);
+  sg.nc = sg.E;
+  for (int dd = 0; dd < sg.q; ++dd) {
+    int slot = -1;
+    for (int j = 0; j < sg.E && bank; ++j)
+      if (bank->seeds[sg.entry_slots[j]] == p.seeds[dd] && bank->windows[sg.entry_slots[j]] == (int64_t)p.window())
+        slot = j;
+    if (slot < 0) {
+      slot = sg.nc++;
+      sg.cdirs.push_back(dd);
+    }
+    sg.dslot.push_back(slot);
+  }
+  sg.ks_c = (int)round_up(sg.nc * sg.r, bk);
   sg.groups = layer_groups(d);
   const int64_t D = d.d_model, F = d.d_ffn;
   const int64_t NQ = (int64_t)d.n_heads * d.head_dim, NKV = (int64_t)d.n_kv_heads * d.head_dim;
@@ -414,7 +436,8 @@ int side_geometry(const zo_model* m, const zo_plan_s& p, const zo_bank* bank, Si
     sg.group_on.push_back(on);
     sg.any |= on;
     const int nb = (int)sg.groups[g].kinds.size();
-    sg.vt_rows.push_back(on ? (int64_t)nb * sg.ks : 0);
+    sg.vt_rows.push_back(on ? (int64_t)nb * sg.ks_c : 0);
+    sg.as_cols.push_back(on ? (int64_t)nb * sg.ks : 0);
     sg.bs_cols.push_back(on ? (sg.groups[g].interleaved ? (int64_t)nb * sg.ks : sg.ks) : 0);
     sg.bs_rows.push_back(nrows[g]);
     sg.n_in.push_back(nin[g]);
@@ -425,8 +448,10 @@ int side_geometry(const zo_model* m, const zo_plan_s& p, const zo_bank* bank, Si
 struct WsPtrs {
   int32_t *row_src, *row_pos, *row_cand, *phys_cu, *phys_first, *sc_row, *sc_lab_src, *work, *labels;
   int32_t* cand_dir;
+  int32_t* cand_slot;           // computed t slot of the candidate's direction
   float* cand_scale;
   SideJob* jobs;
+  int64_t as_ld;                // As row pitch (elements), the same for every group
   float* h;
   void *xa, *qkv, *attn, *hid, *as, *xs;
   std::vector<void*> vt, bs;   // per layer*4 + group
@@ -450,11 +475,19 @@ int tproj_split(const zo_model_desc& d, int64_t n_cols, int64_t k) {
 
 size_t act_size(const zo_model_desc& d) { return d.dtype == ZO_DTYPE_BF16 ? 2 : 4; }
 bool split_act(const zo_plan_s& p) { return (p.flags & ZO_PLAN_ACT_SPLIT) != 0; }
+// As columns per row: the widest group.  Every group writes, for a given row, the same
+// column offsets inside each ks-wide block, so one zero fill per call keeps the
+// columns that no group writes at zero.
+int64_t as_stride(const SideGeom& sg) {
+  int64_t c = 0;
+  for (int g = 0; g < 4; ++g) c = std::max(c, sg.as_cols[g]);
+  return c;
+}
 
 int n_side_jobs(const zo_model_desc& d, const zo_plan_s& p, const SideGeom& sg) {
   if (!sg.any) return 0;
   int per_kind = 0;
-  per_kind += sg.E + sg.q;   // V rows
+  per_kind += sg.nc;         // V rows of the computed t slots
   per_kind += sg.E + sg.q;   // Bs columns (U entries, G directions)
   int kinds = 0;
   for (int k = 0; k < n_kinds_of(d); ++k) kinds += (p.mask >> k) & 1u;
@@ -477,6 +510,7 @@ void carve(const zo_model* m, const zo_plan_s& p, const Packing& pk, const SideG
   w.work = b.take<int32_t>(std::max<size_t>(pk.work.size(), 1));
   w.labels = b.take<int32_t>(S);
   w.cand_dir = b.take<int32_t>(nc);
+  w.cand_slot = b.take<int32_t>(nc);
   w.cand_scale = b.take<float>(nc);
   w.jobs = b.take<SideJob>(std::max(n_side_jobs(d, p, sg), 1));
   const int64_t D = d.d_model, F = d.d_ffn;
@@ -489,9 +523,8 @@ void carve(const zo_model* m, const zo_plan_s& p, const Packing& pk, const SideG
   w.qkv = b.take<unsigned char>(M * (NQ + 2 * NKV) * (sp ? sizeof(float) : as));
   w.attn = b.take<unsigned char>(M * NQ * as * x2);
   w.hid = b.take<unsigned char>(M * F * as * x2);
-  int64_t as_cols = 0;
-  for (int g = 0; g < 4; ++g) as_cols = std::max(as_cols, sg.vt_rows[g]);
-  w.as = b.take<unsigned char>(M * std::max<int64_t>(as_cols, 1) * as * x2);
+  w.as_ld = std::max<int64_t>(as_stride(sg), 1) * x2;
+  w.as = b.take<unsigned char>(M * w.as_ld * as);
   w.vt.assign((size_t)d.n_layers * 4, nullptr);
   w.bs.assign((size_t)d.n_layers * 4, nullptr);
   b.off = align_up(b.off, 256);
@@ -605,9 +638,9 @@ int forward(zo_model* m, const zo_plan_s& p, const Packing& pk, const SideGeom& 
     GemmParams gp = gemm_base(X, (int64_t)K * x2, w.vt[l * 4 + g], (int64_t)K * x3, M, (int)sg.vt_rows[g], K * x3);
     if (sp) { gp.kwa = 2 * K; gp.tp_unit = (int)sg.bs_cols[g]; }
     gp.epi = EPI_TPROJ;
-    gp.C = w.as; gp.ldc = sg.vt_rows[g] * x2;
-    gp.row_cand = w.row_cand; gp.cand_dir = w.cand_dir; gp.cand_scale = w.cand_scale;
-    gp.tp_ks = sg.ks; gp.tp_rank = sg.r; gp.tp_entries = sg.E; gp.tp_used = sg.used;
+    gp.C = w.as; gp.ldc = w.as_ld;
+    gp.row_cand = w.row_cand; gp.cand_dir = w.cand_dir; gp.cand_slot = w.cand_slot; gp.cand_scale = w.cand_scale;
+    gp.tp_ks = sg.ks_c; gp.tp_rank = sg.r; gp.tp_entries = sg.E; gp.tp_used = sg.nc * sg.r; gp.tp_as_ks = sg.ks;
     gp.ksplit = tproj_split(d, sg.vt_rows[g], K * x3);
     gp.partial = w.tp_partial;
     return run_gemm(d, gp, narrow, s);
@@ -620,7 +653,7 @@ int forward(zo_model* m, const zo_plan_s& p, const Packing& pk, const SideGeom& 
   };
   auto with_side = [&](GemmParams& gp, int l, int g) {
     if (!sg.group_on[g]) return;
-    gp.As = w.as; gp.ldas = sg.vt_rows[g] * x2;
+    gp.As = w.as; gp.ldas = w.as_ld;
     gp.Bs = w.bs[l * 4 + g]; gp.ldbs = sg.bs_cols[g] * x3;
     gp.ks_tile = (int)sg.bs_cols[g] * x3;
     if (sp) { gp.as_stride = 2 * (int)sg.bs_cols[g]; gp.kwas = 2 * (int)sg.bs_cols[g]; }
@@ -990,7 +1023,10 @@ int zo_score(zo_model* m, const zo_plan_t* p, const zo_bank* bank, const zo_batc
   ZO_HIP(h2d(w.sc_row, pk.sc_row.data(), pk.sc_row.size() * 4));
   ZO_HIP(h2d(w.sc_lab_src, pk.sc_lab_src.data(), pk.sc_lab_src.size() * 4));
   ZO_HIP(h2d(w.work, pk.work.data(), pk.work.size() * 4));
+  std::vector<int32_t> cslot(nc, -1);
+  for (int c = 0; c < nc && !sg.dslot.empty(); ++c) cslot[c] = sg.dslot[cdir[c]];
   ZO_HIP(h2d(w.cand_dir, cdir.data(), cdir.size() * 4));
+  ZO_HIP(h2d(w.cand_slot, cslot.data(), cslot.size() * 4));
   ZO_HIP(h2d(w.cand_scale, cscale.data(), cscale.size() * 4));
 
   // ---- side factors: V^T rows for the input projections, [U | G] columns for the GEMMs
@@ -1003,6 +1039,7 @@ int zo_score(zo_model* m, const zo_plan_t* p, const zo_bank* bank, const zo_batc
     const int64_t x3 = sp ? 3 : 1;
     const int64_t NQ = (int64_t)d.n_heads * d.head_dim, NKV = (int64_t)d.n_kv_heads * d.head_dim;
     ZO_HIP(hipMemsetAsync(w.side_begin, 0, w.side_bytes, s));   // padding rows/columns must be zero
+    ZO_HIP(hipMemsetAsync(w.as, 0, (size_t)pk.M * w.as_ld * act_size(d), s));   // columns no row writes
     for (int l = 0; l < d.n_layers; ++l)
       for (int g = 0; g < 4; ++g) {
         if (!sg.group_on[g]) continue;
@@ -1012,7 +1049,7 @@ int zo_score(zo_model* m, const zo_plan_t* p, const zo_bank* bank, const zo_batc
           const int kind = G.kinds[kb];
           if (!((p->mask >> kind) & 1u)) continue;
           const KindShape ksh = kind_shape(d, kind);
-          // V^T rows: block kb of the group's V^T, slot j at rows kb*ks + j*r
+          // V^T: block kb of the group's V^T, computed slot j at rows kb*ks_c + j*r
           unsigned char* vt = (unsigned char*)w.vt[l * 4 + g];
           unsigned char* bs = (unsigned char*)w.bs[l * 4 + g];
           int64_t row_base = 0;
@@ -1020,19 +1057,25 @@ int zo_score(zo_model* m, const zo_plan_t* p, const zo_bank* bank, const zo_batc
           int64_t col_base = 0;
           if (g == 0) row_base = kind == ZO_KIND_Q ? 0 : (kind == ZO_KIND_K ? NQ : NQ + NKV);
           if (G.interleaved) { row_map = kind == 4 ? 1 : 2; col_base = (int64_t)kb * sg.ks; }
-          for (int j = 0; j < sg.E + sg.q; ++j) {
+          // V^T rows of the computed t slots: entries, then directions without an entry
+          for (int j = 0; j < sg.nc; ++j) {
             const bool entry = j < sg.E;
-            const uint64_t seed = entry ? bank->seeds[sg.entry_slots[j]] : p->seeds[j - sg.E];
+            const uint64_t seed = entry ? bank->seeds[sg.entry_slots[j]] : p->seeds[sg.cdirs[j - sg.E]];
             const uint64_t vwin = entry ? (uint64_t)bank->windows[sg.entry_slots[j]] : win;
             SideJob v;
             memset(&v, 0, sizeof v);
-            v.dst = vt + ((int64_t)kb * sg.ks + (int64_t)j * sg.r) * sg.n_in[g] * x3 * asz;
+            v.dst = vt + ((int64_t)kb * sg.ks_c + (int64_t)j * sg.r) * sg.n_in[g] * x3 * asz;
             v.ld = sg.n_in[g] * x3;
             v.split = sp ? sg.n_in[g] : 0;
             v.seed = seed; v.tau = vwin; v.tag = dir_tag(l, kind, 1);
             v.src = 0; v.n = ksh.n_in; v.r = sg.r; v.dtype = dt;
             jobs.push_back(v);
             max_items = std::max<int64_t>(max_items, (ksh.n_in * sg.r + 3) / 4);
+          }
+          // Bs columns: U of every entry, then G of every direction
+          for (int j = 0; j < sg.E + sg.q; ++j) {
+            const bool entry = j < sg.E;
+            const uint64_t seed = entry ? bank->seeds[sg.entry_slots[j]] : p->seeds[j - sg.E];
             SideJob u;
             memset(&u, 0, sizeof u);
             u.dst = bs + row_base * sg.bs_cols[g] * x3 * asz;
