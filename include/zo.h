@@ -171,6 +171,21 @@ int zo_bank_keys(const zo_bank* b, uint64_t* seeds, int64_t* windows);       /* 
 int zo_bank_set_keys(zo_bank* b, const uint64_t* seeds, const int64_t* windows);
 int zo_bank_entry_offset(const zo_bank* b, int32_t slot, int32_t layer, int32_t kind, size_t* offset);
 
+/* Fold a bank entry into the weights and free its slot: for every layer and target kind,
+ *   W <- round( W + sum_{k=0}^{r-1} U[:, k] V[:, k]^T )
+ * with V regenerated from the entry's (seed, window) key, the sum formed in fp64 in k
+ * order (products rounded, no fused multiply-add) starting from W, then rounded fp64 ->
+ * fp32 -> bf16 (round to nearest even; fp32 models stop at fp32).  This is the commit of a
+ * finished window's low-rank state into the dense weights (section "The System
+ * Reorganization": Delta W = U V^T of the lazy update), which keeps the bank from
+ * growing by one entry per window.  The only call that writes the weight blob; the
+ * entry's U memory is left as is (a later zo_update on the slot zero-initialises it).
+ * ws_dev: device workspace of at least zo_bank_fold_size bytes (the regenerated V
+ * factors, fp32).  Synchronises `stream` before returning; ZO_E_STATE if the slot is
+ * empty or the bank belongs to another model shape. */
+int zo_bank_fold_size(const zo_model* m, const zo_bank* b, size_t* bytes);
+int zo_bank_fold(zo_model* m, zo_bank* b, int32_t slot, void* ws_dev, size_t ws_bytes, void* stream);
+
 /* ---- batch and packing --------------------------------------------------------
  * Physical packing order (canonical): foreground sequences in input order, then for
  * each candidate in plan order, every probe sequence in input order.  Probe rows see

@@ -241,6 +241,40 @@ def estimate(plan, S, flags=0, n_scored=None):
     return c
 
 
+WEIGHT_NAME = {"q": "wq", "k": "wk", "v": "wv", "o": "wo", "fc1": "w_fc1", "fc2": "w_fc2",
+               "gate": "w_gate", "up": "w_up", "down": "w_down"}
+
+
+def fold(cfg, weights, bank, slot):
+    """Commit bank entry `slot` into the weights (the low-rank state of a finished window,
+    Delta W = U V^T of the lazy update) and free the slot:
+        W <- round(W + sum_k U[:, k] V[:, k]^T),
+    the sum in fp64 in k order (each product rounded, then added), rounded fp64 -> fp32,
+    then fp32 -> bf16 for bf16 models.  `weights` must cache its layers (the folded values
+    replace the generated ones)."""
+    if not weights.cache_layers:
+        raise ValueError("fold needs Weights(cache_layers=True)")
+    e = bank.entries[slot]
+    if e is None:
+        raise ValueError("slot %d is empty" % slot)
+    r = bank.rank
+    for l in range(cfg.n_layers):
+        W = weights.get_layer(l)
+        for kind in bank.targets:
+            n_out, n_in = cfg.linear_shape(kind)
+            V = params.factor(e.seed, l, _kind_id(cfg, kind), params.rng.FACTOR_V, e.window, n_in, r)
+            U = e.U[(l, kind)]
+            w = W[WEIGHT_NAME[kind]].copy()
+            for k in range(r):
+                w = w + np.outer(U[:, k], V[:, k])
+            w32 = w.astype(np.float32)
+            if cfg.dtype == "bf16":
+                w32 = params.bf16_round(w32)
+            W[WEIGHT_NAME[kind]] = w32.astype(np.float64)
+    bank.entries[slot] = None
+    return bank
+
+
 def update(cfg, plan, bank, c, lr):
     """U_{seed_d, window} <- fp32(U - ((lr / q) * c_d) * G_d), one entry per direction."""
     q = len(plan.dir_seeds)

@@ -209,6 +209,39 @@ def test_qkv_side_targets_off_tile_boundary_rejected():
     assert ei.value.code == -2
 
 
+@pytest.mark.parametrize("cfg", [SMALL_OPT_BF16, SMALL_QWEN_BF16], ids=["opt", "qwen3"])
+def test_fold_matches_oracle_bitwise_then_scores(cfg):
+    """zo_bank_fold commits a window-0 entry into the bf16 weights: every target weight
+    (packed q|k|v rows, the interleaved gate/up pack) equals the oracle's fold bit for
+    bit; the slot is freed; scoring at window 1 with the folded weights and the remaining
+    entry matches the oracle (two-term activations, 5e-4)."""
+    need_gpu()
+    from oracle import params
+    wl = workload(cfg, dir_seeds=(3, 8), n_fg=1, n_prompts=2, act_split=True)
+    batch = inputs.make_batch(wl)
+    g, o = GpuRun(wl), OracleRun(wl)
+    for t, c in enumerate([np.array([0.9, -1.7]), np.array([-2.5, 0.4])]):
+        g.update(t, c, 5e-3)
+        o.update(t, c, 5e-3)
+    seeds, wins = g.bank.keys()
+    gslot = [i for i in range(len(seeds)) if seeds[i] == 3 and wins[i] == 0][0]
+    oslot = [i for i, e in enumerate(o.bank.entries) if e is not None and e.seed == 3 and e.window == 0][0]
+    flush("fold %s slot %d" % (cfg.arch, gslot))
+    g.zo.fold(g.model, g.bank, gslot)
+    ozo.fold(cfg, o.W, o.bank, oslot)
+    assert g.bank.keys()[1][gslot] == -1
+    pid = {"q": params.WQ, "k": params.WK, "v": params.WV, "o": params.WO, "fc1": params.W_FC1,
+           "fc2": params.W_FC2, "gate": params.W_GATE, "up": params.W_UP, "down": params.W_DOWN}
+    for layer in range(cfg.n_layers):
+        for kind in wl.targets:
+            got = g.model.tensor(layer + 1, pid[kind]).float().cpu().numpy()
+            ref = o.W.get_layer(layer)[ozo.WEIGHT_NAME[kind]].astype(np.float32)
+            assert np.array_equal(got.view(np.uint32), ref.view(np.uint32)), (layer, kind)
+    gs, os_ = g.score(4, batch), o.score(4, batch)
+    err = _seq_close(gs, os_, 5e-4)
+    flush("after fold: max per-sequence err %.3g" % err)
+
+
 def test_multi_step_trajectory_with_window_rollover():
     """Eight steps of score -> estimate -> update with nu = 4 (two windows: the
     bank gains a second entry at t = 4 and the first stays as a frozen term).  The

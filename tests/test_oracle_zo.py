@@ -207,3 +207,53 @@ def test_all_next_scores_every_position():
     assert list(pos) == [3] and list(lab) == [23]
     with pytest.raises(ValueError):
         zo.scored_positions(np.array([3]), zo.MODE_LAST_LABEL)
+
+
+@pytest.mark.parametrize("cfg", [OPT_SMALL, QWEN_SMALL], ids=["opt", "qwen3"])
+def test_fold_commits_entry_into_weights(cfg):
+    """Folding a finished window's entry into W (Delta W = U V^T of the lazy update) leaves
+    every score unchanged up to the fp32 rounding of W, and the folded values are the
+    rounded W + U V^T."""
+    wl = _small_wl(cfg, cfg.kind_names, dirs=(0, 5))
+    bank = _bank_after_updates(cfg, wl, steps=2)            # window 0 entries for both seeds
+    batch = inputs.make_batch(wl)
+    plan = zo.plan_from_workload(wl, 4)                     # window 1: directions do not alias
+    W = Weights(cfg, wl.model_seed, cache_layers=True)
+    before = zo.score(cfg, W, plan, bank, batch)
+    plain = zo.score(cfg, W, plan, Bank(4, wl.rank, wl.targets), batch)
+    assert np.max(np.abs(before["seq_logp"] - plain["seq_logp"])) > 1e-2   # the entry matters
+    slot = [i for i, e in enumerate(bank.entries) if e is not None and e.seed == 0][0]
+    e = bank.entries[slot]
+    old = {(l, k): W.get_layer(l)[zo.WEIGHT_NAME[k]].copy() for l in range(cfg.n_layers) for k in wl.targets}
+    zo.fold(cfg, W, bank, slot)
+    assert bank.entries[slot] is None
+    for (l, k), w0 in old.items():
+        n_out, n_in = cfg.linear_shape(k)
+        V = params.factor(0, l, cfg.kind_names.index(k), params.rng.FACTOR_V, 0, n_in, wl.rank)
+        ref = (w0 + e.U[(l, k)] @ V.T).astype(np.float32)        # another summation order
+        got = W.get_layer(l)[zo.WEIGHT_NAME[k]].astype(np.float32)
+        ulp = np.spacing(np.abs(ref))
+        assert np.all(np.abs(got - ref) <= ulp), (l, k)
+        assert np.mean(got == ref) > 0.99
+    after = zo.score(cfg, W, plan, bank, batch)
+    assert np.allclose(after["seq_logp"], before["seq_logp"], rtol=1e-6, atol=0)
+    assert np.allclose(after["S"], before["S"], rtol=1e-6, atol=0)
+
+
+def test_fold_rounds_bf16_weights():
+    """bf16 weights: the fold rounds fp64 -> fp32 -> bf16 (each to nearest even)."""
+    cfg = configs.ModelCfg("opt", 1, 64, 4, 4, 16, 128, 97, 64, "bf16", 1e-5)
+    wl = _small_wl(cfg, ("q", "fc2"), dirs=(3,))
+    bank = _bank_after_updates(cfg, wl, steps=1)
+    W = Weights(cfg, wl.model_seed, cache_layers=True)
+    w0 = W.get_layer(0)["wq"].copy()
+    e = bank.entries[0]
+    zo.fold(cfg, W, bank, 0)
+    V = params.factor(3, 0, 0, params.rng.FACTOR_V, 0, cfg.d_model, wl.rank)
+    exact = w0 + e.U[(0, "q")] @ V.T
+    got = W.get_layer(0)["wq"]
+    assert np.all(params.bf16_round(got.astype(np.float32)) == got.astype(np.float32))   # bf16 values
+    # within half a bf16 step of the exact sum (plus the fp32 step of the first rounding)
+    step = np.spacing(np.abs(exact).astype(np.float32)).astype(np.float64) * 2.0 ** 16
+    assert np.all(np.abs(got - exact) <= 0.5 * step + np.spacing(np.abs(exact).astype(np.float32)))
+    assert not np.array_equal(got, w0)

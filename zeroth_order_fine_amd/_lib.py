@@ -44,6 +44,8 @@ _SIGS = {
     "zo_bank_keys": (c_i32, [c_vp, P(c_u64), P(c_i64)]),
     "zo_bank_set_keys": (c_i32, [c_vp, P(c_u64), P(c_i64)]),
     "zo_bank_entry_offset": (c_i32, [c_vp, c_i32, c_i32, c_i32, P(c_sz)]),
+    "zo_bank_fold_size": (c_i32, [c_vp, c_vp, P(c_sz)]),
+    "zo_bank_fold": (c_i32, [c_vp, c_vp, c_i32, c_vp, c_sz, c_vp]),
     "zo_batch_layout": (c_i32, [c_vp, c_vp, c_vp, P(BatchDesc), P(c_i32), P(c_i64), P(c_i64), P(c_sz)]),
     "zo_pack": (c_i32, [c_vp, P(BatchDesc), P(c_i32), P(c_i32), P(c_i32)]),
     "zo_score": (c_i32, [c_vp, c_vp, c_vp, P(BatchDesc), c_vp, c_sz, c_vp, c_vp, P(c_dbl), c_vp]),

@@ -253,6 +253,15 @@ def update(model, plan, bank, c, lr):
     _check(model.L.zo_update(model.h, plan.h, bank.h, _arr(ctypes.c_double, c), lr, _stream()))
 
 
+def fold(model, bank, slot):
+    """Fold bank entry `slot` into the model's weights (W <- round(W + U V^T) for every
+    target linear) and free the slot."""
+    n = ctypes.c_size_t()
+    _check(model.L.zo_bank_fold_size(model.h, bank.h, ctypes.byref(n)))
+    ws = torch.empty(n.value, dtype=torch.uint8, device="cuda")
+    _check(model.L.zo_bank_fold(model.h, bank.h, slot, _ptr(ws), n.value, _stream()))
+
+
 def philox_words(seed, tag, tau, first_block, n_blocks):
     L = _lib.load()
     out = torch.empty(max(4 * n_blocks, 1), dtype=torch.int32, device="cuda")

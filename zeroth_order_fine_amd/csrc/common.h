@@ -151,6 +151,18 @@ struct UpdateArgs {                // U <- fp32(U - coef_d * G_d) for every (lay
 hipError_t launch_update(const UpdateArgs& a, int n_layers, int64_t max_n, hipStream_t s);
 hipError_t launch_stream_rowmajor(const SideJob& jb, hipStream_t s);   // stream (seed, tag, tau) -> fp32 [n x r]
 
+struct FoldArgs {                  // W <- round(W + U V^T) of one target linear
+  void* w;                         // weight rows (physical layout)
+  int64_t ld;                      // physical row pitch (elements)
+  int64_t n_out, n_in;
+  int32_t layout;                  // 0 plain, 1 gate / 2 up of a 16-row interleave
+  int32_t bf16;                    // weight storage: 1 bf16, 0 fp32
+  int32_t r;
+  const float* u;                  // [n_out x r]
+  const float* v;                  // [n_in x r]
+};
+hipError_t launch_fold(const FoldArgs& a, hipStream_t s);
+
 // ---- transformer pieces ------------------------------------------------------
 template <typename TW>
 hipError_t launch_embed_t(const TW* E, const TW* P, const int32_t* tokens, const int32_t* row_src,

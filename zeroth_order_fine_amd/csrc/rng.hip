@@ -258,6 +258,23 @@ __global__ void update_kernel(UpdateArgs a) {
   }
 }
 
+// W <- round(W + sum_k U[:, k] V[:, k]^T) for one target linear: fp64 sum in k order
+// (no contraction), then fp64 -> fp32 -> (bf16) by round to nearest even.
+__global__ void fold_kernel(FoldArgs a) {
+#pragma clang fp contract(off)
+  const int64_t n = a.n_out * a.n_in;
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n; e += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t i = e / a.n_in, j = e - i * a.n_in;
+    const int64_t prow = a.layout ? interleave16_row(i, a.layout) : i;
+    const int64_t off = prow * a.ld + j;
+    double acc = a.bf16 ? (double)bf16_to_f32(((const bf16_t*)a.w)[off]) : (double)((const float*)a.w)[off];
+    for (int k = 0; k < a.r; ++k) acc = acc + (double)a.u[i * a.r + k] * (double)a.v[j * a.r + k];
+    const float f = (float)acc;
+    if (a.bf16) ((bf16_t*)a.w)[off] = f32_to_bf16(f);
+    else ((float*)a.w)[off] = f;
+  }
+}
+
 __global__ void side_job_single_kernel(SideJob jb) {
   const int64_t n_el = jb.n * jb.r;
   const int64_t nblk = (n_el + 3) / 4;
@@ -321,6 +338,13 @@ hipError_t launch_update(const UpdateArgs& a, int n_layers, int64_t max_n, hipSt
   if (a.n_dirs <= 0 || a.n_kinds <= 0 || n_layers <= 0) return hipSuccess;
   dim3 grid(grid_for((max_n + 3) / 4, 256, 256), n_layers * a.n_kinds, a.n_dirs);
   hipLaunchKernelGGL(update_kernel, grid, dim3(256), 0, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_fold(const FoldArgs& a, hipStream_t s) {
+  const int64_t n = a.n_out * a.n_in;
+  if (n <= 0) return hipSuccess;
+  hipLaunchKernelGGL(fold_kernel, dim3(grid_for(n, 256, 16384)), dim3(256), 0, s, a);
   return hipGetLastError();
 }
 

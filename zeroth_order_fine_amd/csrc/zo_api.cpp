@@ -1211,6 +1211,71 @@ int zo_update(zo_model* m, const zo_plan_t* p, zo_bank* bank, const double* c_ho
   return ZO_OK;
 }
 
+int zo_bank_fold_size(const zo_model* m, const zo_bank* bank, size_t* bytes) {
+  ZO_CHECK(m && bank && bytes, ZO_E_INVAL, "null argument");
+  size_t n = 0;
+  for (int kind : bank->kinds) n += (size_t)kind_shape(m->d, kind).n_in * bank->rank;
+  *bytes = std::max<size_t>(n * m->d.n_layers * sizeof(float), 256);
+  return ZO_OK;
+}
+
+int zo_bank_fold(zo_model* m, zo_bank* bank, int32_t slot, void* ws_dev, size_t ws_bytes, void* stream) {
+  ZO_CHECK(m && bank, ZO_E_INVAL, "null argument");
+  ZO_CHECK(slot >= 0 && slot < bank->n_slots, ZO_E_INVAL, "slot %d out of range", slot);
+  ZO_CHECK(bank->windows[slot] >= 0, ZO_E_STATE, "slot %d holds no entry", slot);
+  const zo_model_desc& bd = bank->md;
+  ZO_CHECK(bd.arch == m->d.arch && bd.dtype == m->d.dtype && bd.n_layers == m->d.n_layers &&
+               bd.d_model == m->d.d_model && bd.n_heads == m->d.n_heads && bd.n_kv_heads == m->d.n_kv_heads &&
+               bd.head_dim == m->d.head_dim && bd.d_ffn == m->d.d_ffn,
+           ZO_E_STATE, "bank was made for another model");
+  size_t need = 0;
+  int rc = zo_bank_fold_size(m, bank, &need);
+  if (rc) return rc;
+  ZO_CHECK(ws_dev && ws_bytes >= need, ZO_E_SHAPE, "workspace has %zu bytes, needs %zu", ws_bytes, need);
+  hipStream_t s = (hipStream_t)stream;
+  const zo_model_desc& d = m->d;
+  const int r = bank->rank;
+  float* v = (float*)ws_dev;
+  // V of every (layer, kind), regenerated from the entry's key
+  std::vector<float*> vptr;
+  for (int l = 0; l < d.n_layers; ++l)
+    for (int kind : bank->kinds) {
+      const KindShape ks = kind_shape(d, kind);
+      SideJob jb;
+      memset(&jb, 0, sizeof jb);
+      jb.dst = v; jb.seed = bank->seeds[slot]; jb.tau = (uint64_t)bank->windows[slot];
+      jb.tag = dir_tag(l, kind, 1); jb.n = ks.n_in; jb.r = r;
+      ZO_HIP(launch_stream_rowmajor(jb, s));
+      vptr.push_back(v);
+      v += ks.n_in * r;
+    }
+  const int pk[7] = {P_WQ, P_WK, P_WV, P_WO, P_W1, P_W2, P_WDOWN};
+  size_t vi = 0;
+  for (int l = 0; l < d.n_layers; ++l)
+    for (size_t kk = 0; kk < bank->kinds.size(); ++kk) {
+      const int kind = bank->kinds[kk];
+      const KindShape ks = kind_shape(d, kind);
+      const TLoc& t = m->lo.L[l][pk[kind]];
+      ZO_CHECK(t.present && t.rows == ks.n_out && t.cols == ks.n_in, ZO_E_STATE, "weight of kind %d not found",
+               kind);
+      FoldArgs a;
+      memset(&a, 0, sizeof a);
+      a.w = m->w + t.off;
+      a.ld = t.cols;
+      a.n_out = ks.n_out; a.n_in = ks.n_in;
+      a.layout = t.layout;
+      a.bf16 = t.dtype == ZO_DTYPE_BF16;
+      a.r = r;
+      a.u = bank->u + (size_t)slot * bank->slot_stride + (size_t)l * bank->layer_stride + bank->kind_off[kk];
+      a.v = vptr[vi++];
+      ZO_HIP(launch_fold(a, s));
+    }
+  ZO_HIP(hipStreamSynchronize(s));
+  bank->windows[slot] = -1;
+  bank->seeds[slot] = 0;
+  return ZO_OK;
+}
+
 int zo_profile_begin(void) {
   g_prof.on = true;
   g_prof.used = 0;
