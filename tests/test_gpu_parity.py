@@ -269,6 +269,36 @@ def test_multi_step_trajectory_with_window_rollover():
             assert np.array_equal(g.bank.entry(gslot, layer, kind).cpu().numpy(), U.astype(np.float32))
 
 
+def test_trajectory_with_fold_at_rollover():
+    """Twelve steps, nu = 4, a one-slot bank: at every window start the finished window's
+    entry is folded into W (zo_bank_fold) before the new window's first update, on the
+    GPU and in the oracle alike (the oracle applies the GPU's c).  S and c at every step,
+    the folded weights and the final entry are checked."""
+    need_gpu()
+    wl = configs.CONFIGS["tiny"].with_(nu=4)
+    batch = inputs.make_batch(wl)
+    g, o = GpuRun(wl, n_slots=1), OracleRun(wl, n_slots=1)
+    for t in range(12):
+        if t > 0 and t % wl.nu == 0:
+            g.zo.fold(g.model, g.bank, 0)
+            ozo.fold(wl.model, o.W, o.bank, 0)
+        gs, os_ = g.score(t, batch), o.score(t, batch)
+        assert np.all(np.abs(gs["S"] - os_["S"]) <= 1e-4 * np.abs(os_["S"])), (t, gs["S"], os_["S"])
+        cg = g.zo.estimate(g.plan(t), gs["S"])
+        co = ozo.estimate(ozo.plan_from_workload(wl, t), os_["S"])
+        assert np.all(np.abs(cg - co) <= 1e-2 * np.abs(co)), (t, cg, co)
+        g.update(t, cg, 1e-2)
+        o.update(t, cg, 1e-2)
+    assert g.bank.keys()[1] == [2]
+    from oracle import params
+    for layer in range(wl.model.n_layers):
+        for kind, pid in (("q", params.WQ), ("v", params.WV)):
+            got = g.model.tensor(layer + 1, pid).cpu().numpy()
+            assert np.array_equal(got, o.W.get_layer(layer)[ozo.WEIGHT_NAME[kind]].astype(np.float32))
+            assert np.array_equal(g.bank.entry(0, layer, kind).cpu().numpy(),
+                                  o.bank.entries[0].U[(layer, kind)].astype(np.float32))
+
+
 def test_bank_checkpoint_restore_is_bitwise():
     """The state is the bank memory plus its keys: restoring both into a fresh bank
     gives bitwise the same scores."""
