@@ -60,6 +60,33 @@ def copy_calibration():
     print(json.dumps({"copy_bytes_read_per_launch": n, "copy_bytes_written_per_launch": n, "launches": 3}))
 
 
+def measured_peaks():
+    """Ceilings measured on this GPU by the committed microbenchmarks (libzo_peaks.so): a
+    dense bf16 MFMA loop and a 1 GiB streaming copy; reported beside the published peaks."""
+    import ctypes
+    import torch
+    path = os.path.join(ROOT, "zeroth_order_fine_amd", "libzo_peaks.so")
+    if not os.path.exists(path):
+        return None
+    L = ctypes.CDLL(path)
+    for f in (L.zo_peak_mfma_bf16, L.zo_peak_copy, L.zo_peak_read):
+        f.restype = ctypes.c_double
+    L.zo_peak_mfma_bf16.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int]
+    L.zo_peak_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int]
+    L.zo_peak_read.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int]
+    blocks = 1024
+    out = torch.empty(blocks * 256 * 4, dtype=torch.float32, device="cuda")
+    n = 1 << 30
+    a = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+    b = torch.empty_like(a)
+    res = {"mfma_bf16_tflops": round(L.zo_peak_mfma_bf16(ctypes.c_void_p(out.data_ptr()), blocks, 2000), 1),
+           "copy_gbs": round(L.zo_peak_copy(ctypes.c_void_p(a.data_ptr()), ctypes.c_void_p(b.data_ptr()), n, 4096), 1),
+           "read_gbs": round(L.zo_peak_read(ctypes.c_void_p(a.data_ptr()), ctypes.c_void_p(out.data_ptr()), n, 4096), 1)}
+    del a, b, out
+    torch.cuda.empty_cache()
+    return res
+
+
 def base_gemm_flops(cfg, rows):
     """Algorithmic FLOPs of the shared-weight projections for `rows` token rows."""
     total = 0
@@ -178,6 +205,8 @@ def main():
     ap.add_argument("--workload", default="opt13b")
     ap.add_argument("--lr", type=float, default=1e-4)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-peaks", action="store_true",
+                    help="skip the MFMA-loop and copy microbenchmarks of the measured ceilings")
     ap.add_argument("--no-side-check", action="store_true",
                     help="skip the extra scoring without side path that measures its cost (for profiler runs)")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -285,6 +314,14 @@ def main():
             hbm[k] = {"achieved": round(gbs, 1), "peak": PEAK_HBM_GBS, "unit": "GB/s",
                       "frac": round(gbs / PEAK_HBM_GBS, 4), "algorithmic_mb_per_step": round(b / 1e6, 2)}
     line["hbm_kernels"] = hbm
+    if not args.no_peaks:
+        pk = measured_peaks()
+        if pk:
+            line["measured_peaks"] = pk
+            if achieved and cfg.dtype == "bf16":
+                line["roofline"]["frac_of_measured_mfma"] = round(achieved / pk["mfma_bf16_tflops"], 4)
+            for v in hbm.values():
+                v["frac_of_measured_copy"] = round(v["achieved"] / pk["copy_gbs"], 4)
     # side-path cost: the projections' time with the side columns vs a plan with no targets
     if wl.targets and not args.no_side_check:
         n_off = min(args.steps, 3)
@@ -300,6 +337,25 @@ def main():
             "gemm_base_ms_with_side": round(base_on, 3), "gemm_base_ms_without": round(base_off, 3),
             "extended_k_overhead": round(base_on / base_off - 1.0, 4),
             "total_ms_per_step": round(base_on - base_off + (prof["gemm_side"][1] + prof["side_prep"][1]) / args.steps, 3)}
+    # other states of the same workload, scored after the timed region (score only)
+    extra = {}
+
+    def score_ms(bank_, db_, n=3):
+        torch.cuda.synchronize()
+        a = time.perf_counter()
+        for k in range(n):
+            zo.score(model, zo.Plan.from_workload(model, wl, t=args.warmup + args.steps), bank_, db_)
+        torch.cuda.synchronize()
+        return (time.perf_counter() - a) / n * 1e3
+
+    if not args.no_side_check:
+        extra["score_ms_steady_bank"] = round(score_ms(bank, db), 3)
+        extra["score_ms_empty_bank"] = round(score_ms(None, db), 3)
+        if wl.n_fg:
+            fg = batch.subset([i for i in range(batch.n_seq) if batch.role[i] == inputs.ROLE_FOREGROUND])
+            extra["score_ms_foreground_only"] = round(score_ms(bank, zo.DeviceBatch(fg)), 3)
+            extra["foreground_only_tokens_per_s"] = round(fg_tokens / (extra["score_ms_foreground_only"] / 1e3), 1)
+        line["other_states"] = extra
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, batch)
     print(json.dumps(line), flush=True)

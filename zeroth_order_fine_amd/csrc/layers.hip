@@ -24,6 +24,31 @@ __device__ __forceinline__ float block_sum(float v, float* sh) {
   return t;
 }
 
+// merge (count, mean, M2) of two disjoint parts
+__device__ __forceinline__ void merge_moments(float& n, float& m, float& m2, float nb, float mb, float m2b) {
+  const float nn = n + nb;
+  if (nn > 0.f) {
+    const float delta = mb - m, f = nb / nn;
+    m = m + delta * f;
+    m2 = m2 + m2b + delta * delta * n * f;
+  }
+  n = nn;
+}
+
+// every thread ends with the (count, mean, M2) of the whole workgroup
+__device__ __forceinline__ void block_merge_moments(float& n, float& m, float& m2, float* sh) {
+#pragma unroll
+  for (int s = 32; s >= 1; s >>= 1)
+    merge_moments(n, m, m2, __shfl_xor(n, s, 64), __shfl_xor(m, s, 64), __shfl_xor(m2, s, 64));
+  const int w = threadIdx.x >> 6, l = threadIdx.x & 63;
+  const int nw = blockDim.x >> 6;
+  __syncthreads();
+  if (l == 0) { sh[3 * w] = n; sh[3 * w + 1] = m; sh[3 * w + 2] = m2; }
+  __syncthreads();
+  n = sh[0]; m = sh[1]; m2 = sh[2];
+  for (int i = 1; i < nw; ++i) merge_moments(n, m, m2, sh[3 * i], sh[3 * i + 1], sh[3 * i + 2]);
+}
+
 template <typename TW>
 __global__ void embed_kernel(const TW* __restrict__ E, const TW* __restrict__ P, const int32_t* __restrict__ tokens,
                              const int32_t* __restrict__ row_src, const int32_t* __restrict__ row_pos, int d,
@@ -69,7 +94,7 @@ __global__ void __launch_bounds__(NORM_THREADS)
 norm_kernel(const float* __restrict__ h, const int32_t* __restrict__ rows, int d, const float* __restrict__ w,
             const float* __restrict__ b, float eps, int rms, T* __restrict__ out, int64_t ld_out, int lo_off) {
   constexpr int NV = NORM_MAXV / 4;
-  __shared__ float sh[NORM_THREADS / 64];
+  __shared__ float sh[3 * (NORM_THREADS / 64)];
   const int m = blockIdx.x;
   const int src = rows ? rows[m] : m;
   const float* x = h + (int64_t)src * d;
@@ -83,18 +108,23 @@ norm_kernel(const float* __restrict__ h, const int32_t* __restrict__ rows, int d
   }
   float mean = 0.f, scale;
   if (!rms) {
-    mean = block_sum(s, sh) / (float)d;
-    float q = 0.f;
+    // one reduction: each thread's (count, mean, M2) over its own elements, merged
+    // pairwise (Chan et al.'s update for combining partial variances)
+    float n = 0.f;
+#pragma unroll
+    for (int k = 0; k < NV; ++k) n += (4 * (threadIdx.x + k * NORM_THREADS) < d) ? 4.f : 0.f;
+    float m = n > 0.f ? s / n : 0.f, m2 = 0.f;
 #pragma unroll
     for (int k = 0; k < NV; ++k) {
       const int i = 4 * (threadIdx.x + k * NORM_THREADS);
       if (i < d) {
-        const floatx4_t c = v[k] - mean;
-        q += (c[0] * c[0] + c[1] * c[1]) + (c[2] * c[2] + c[3] * c[3]);
+        const floatx4_t c = v[k] - m;
+        m2 += (c[0] * c[0] + c[1] * c[1]) + (c[2] * c[2] + c[3] * c[3]);
       }
     }
-    const float var = block_sum(q, sh) / (float)d;
-    scale = 1.0f / sqrtf(var + eps);
+    block_merge_moments(n, m, m2, sh);
+    mean = m;
+    scale = 1.0f / sqrtf(m2 / (float)d + eps);
   } else {
     float q = 0.f;
 #pragma unroll
