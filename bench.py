@@ -150,14 +150,14 @@ def describe(wl):
                 ",".join(wl.targets), wl.eps))
 
 
-def cpu_baseline(wl, batch):
-    """Time the oracle (as it stands) on a bounded sample: the first probe prompt under
-    every candidate, through one decoder layer plus the vocabulary head; the per-token
-    rate for the whole model is extrapolated as n_layers x layer time + head time."""
+def cpu_baseline(wl, batch, n_prompts=4, n_layers=3):
+    """Time the oracle (as it stands) on a bounded sample: the first `n_prompts` probe
+    prompts under every candidate, through the first `n_layers` decoder layers plus the
+    vocabulary head; the per-token rate for the whole model is extrapolated as
+    (n_layers_total / n_layers) x layer time + head time."""
     import numpy as np
 
     from oracle import model as om
-    from oracle import params
     from oracle import zo as ozo
     try:
         from threadpoolctl import threadpool_info
@@ -165,36 +165,38 @@ def cpu_baseline(wl, batch):
     except Exception:
         cores = os.cpu_count() or 1
     cfg = wl.model
+    nl = min(n_layers, cfg.n_layers)
     t0 = time.perf_counter()
-    W = ozo.Weights(cfg, wl.model_seed, cache_layers=True)
+    W = ozo.Weights(cfg, wl.model_seed, cache_layers=False)
     G = W.get_global()
-    W0 = W.get_layer(0)
     t_gen = time.perf_counter() - t0
     plan = ozo.plan_from_workload(wl, 0)
     phys = ozo.pack(batch, plan)
-    first_probe = [i for i in range(batch.n_seq) if batch.role[i] == 0][0]
-    sample = [(li, c) for li, c in phys if li == first_probe]
-    hs, sides, toks = [], [], []
-    for li, c in sample:
-        t = np.asarray(batch.tokens[li], np.int64)
-        toks.append(t)
-        hs.append(om.embed(cfg, G, t))
-        sides.append(ozo.side_terms(cfg, plan, None, c))
-    t1 = time.perf_counter()
-    outs = [om.layer_forward(cfg, W0, h, lambda kind, s=s: s(0, kind), False) for h, s in zip(hs, sides)]
-    t_layer = time.perf_counter() - t1
-    t2 = time.perf_counter()
-    for h, t, (li, c) in zip(outs, toks, sample):
+    probes = [i for i in range(batch.n_seq) if batch.role[i] == 0][:n_prompts]
+    sample = [(li, c) for li, c in phys if li in probes]
+    toks = [np.asarray(batch.tokens[li], np.int64) for li, c in sample]
+    hs = [om.embed(cfg, G, t) for t in toks]
+    sides = [ozo.side_terms(cfg, plan, None, c) for li, c in sample]
+    t_layer = 0.0
+    for l in range(nl):
+        a = time.perf_counter()
+        Wl = W.get_layer(l)
+        t_gen += time.perf_counter() - a
+        a = time.perf_counter()
+        hs = [om.layer_forward(cfg, Wl, h, lambda kind, s=s, l=l: s(l, kind), False) for h, s in zip(hs, sides)]
+        t_layer += time.perf_counter() - a
+    a = time.perf_counter()
+    for h, t, (li, c) in zip(hs, toks, sample):
         pos, lab = ozo.scored_positions(t, int(batch.score_mode[li]))
         om.final_logprobs(cfg, G, h, pos, lab)
-    t_head = time.perf_counter() - t2
+    t_head = time.perf_counter() - a
     rows = sum(len(t) for t in toks)
-    est = cfg.n_layers * t_layer + t_head
+    est = cfg.n_layers / nl * t_layer + t_head
     return {"value": rows / est, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": ("prompt %d (%d tokens) under all %d candidates through layer 0 of %d and the head; "
-                       "layer %.2f s, head %.2f s, extrapolated x%d layers; oracle weight generation for the "
-                       "sample %.1f s not counted" % (first_probe, len(toks[0]), len(sample), cfg.n_layers,
-                                                      t_layer, t_head, cfg.n_layers, t_gen))}
+            "sample": ("probe prompts %s (%d token rows) under all %d candidates through layers 0-%d of %d and "
+                       "the head; layers %.2f s, head %.2f s, extrapolated x%.1f; oracle weight generation "
+                       "%.1f s not counted" % (probes, rows, len(plan.candidates), nl - 1, cfg.n_layers, t_layer,
+                                               t_head, cfg.n_layers / nl, t_gen))}
 
 
 def main():
