@@ -96,10 +96,13 @@ def test_small_models_with_bank_and_ragged_rows(cfg, split):
         first += len(ref)
 
 
-def test_foreground_bitwise_invariance():
-    """Foreground rows are bitwise identical whether batched alone or alongside probes."""
+@pytest.mark.parametrize("n_prompts,len_lo", [(4, 5), (64, 100)], ids=["small-batch", "tile-switch"])
+def test_foreground_bitwise_invariance(n_prompts, len_lo):
+    """Foreground rows are bitwise identical whether batched alone or alongside probes.
+    "tile-switch": the mixed batch (about 16k rows) runs every projection in 256x256
+    tiles, the foreground batch alone (about 400 rows) in 128x128 tiles."""
     need_gpu()
-    wl = workload(SMALL_QWEN_BF16, n_fg=3, n_prompts=4, dir_seeds=(1,))
+    wl = workload(SMALL_QWEN_BF16, n_fg=3, n_prompts=n_prompts, len_lo=len_lo, dir_seeds=(1,))
     batch = inputs.make_batch(wl)
     g = GpuRun(wl)
     g.update(0, np.array([1.3]), 1e-2)
@@ -107,6 +110,7 @@ def test_foreground_bitwise_invariance():
     fg = batch.subset([i for i in range(batch.n_seq) if batch.role[i] == inputs.ROLE_FOREGROUND])
     alone = g.score(1, fg)
     n_fg = fg.n_seq
+    flush("rows: mixed %d, foreground alone %d" % (int(mixed["n_rows"]), int(alone["n_rows"])))
     a = mixed["seq_logp"].cpu().numpy()[:n_fg]
     b = alone["seq_logp"].cpu().numpy()[:n_fg]
     assert np.array_equal(a.view(np.uint64), b.view(np.uint64))

@@ -16,8 +16,10 @@
 // accumulator layout (lane l holds rows 4*(l/16)+j, column l%16 of every
 // 16x16 block), so both share the epilogues.
 //
-// The tile shape depends only on the call site (N and K), never on M: a row's
-// result does not depend on what else is in the batch.
+// A row's result never depends on what else is in the batch: the register-staged
+// tiles depend only on the call site (N and K), and the projection kernel's tile
+// choices (which may follow M) all form each output element by the same MFMA
+// sequence (same 128x64 wave tile, same K loop, no split-K).
 #include "common.h"
 #include <math.h>
 #include <type_traits>
@@ -728,15 +730,37 @@ int gemm_cfg_bk(int cfg, bool bf16) {
 // side-input column granularity (a multiple of every consumer's K-step)
 int gemm_bk(bool bf16) { return bf16 ? 32 : BK_F32; }
 
+template <int BM, int BN>
+hipError_t launch_pipe_epi(const GemmParams& p, hipStream_t s) {
+  switch (p.epi) {
+    case EPI_STORE: return launch_bf16_pipe<BM, BN, 128, 64, 4, EPI_STORE>(p, s);
+    case EPI_GELU: return launch_bf16_pipe<BM, BN, 128, 64, 4, EPI_GELU>(p, s);
+    case EPI_SWIGLU: return launch_bf16_pipe<BM, BN, 128, 64, 4, EPI_SWIGLU>(p, s);
+    case EPI_RESID: return launch_bf16_pipe<BM, BN, 128, 64, 4, EPI_RESID>(p, s);
+    default: return hipErrorInvalidValue;
+  }
+}
+
+// Workgroup tile of the projection kernel: 256x256 (8 waves), 128x256 (4) or 128x128
+// (2), all made of the same 128x64 wave tile with the same K loop, so every output
+// element is formed by the same MFMA sequence whichever tile holds it; the choice can
+// follow the batch without changing a row's result.  The 256x256 tile is the most
+// efficient per CU; measured on the projections of small batches, a smaller tile pays
+// off only when 256x256 tiles would occupy fewer than half of the 256 CUs.
+int pipe_tile(const GemmParams& p) {
+  auto tiles = [&](int bm, int bn) { return (int64_t)((p.M + bm - 1) / bm) * ((p.N + bn - 1) / bn); };
+  if (tiles(256, 256) >= 128) return 0;
+  if (tiles(128, 256) >= 128) return 1;
+  return 2;
+}
+
 hipError_t gemm_launch_bf16(const GemmParams& p, int cfg, hipStream_t s) {
   if (p.M <= 0 || p.N <= 0) return hipSuccess;
   if (cfg == GEMM_CFG_BIG) {
-    switch (p.epi) {
-      case EPI_STORE: return launch_bf16_pipe<256, 256, 128, 64, 4, EPI_STORE>(p, s);
-      case EPI_GELU: return launch_bf16_pipe<256, 256, 128, 64, 4, EPI_GELU>(p, s);
-      case EPI_SWIGLU: return launch_bf16_pipe<256, 256, 128, 64, 4, EPI_SWIGLU>(p, s);
-      case EPI_RESID: return launch_bf16_pipe<256, 256, 128, 64, 4, EPI_RESID>(p, s);
-      default: return hipErrorInvalidValue;
+    switch (pipe_tile(p)) {
+      case 0: return launch_pipe_epi<256, 256>(p, s);
+      case 1: return launch_pipe_epi<128, 256>(p, s);
+      default: return launch_pipe_epi<128, 128>(p, s);
     }
   }
   if (cfg == GEMM_CFG_NARROW) {
