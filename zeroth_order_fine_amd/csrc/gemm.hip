@@ -449,24 +449,27 @@ __device__ __forceinline__ void epilogue_rows(const GemmParams& p, floatx4_t (&a
 // ------------------------------------------------------------------------------
 // bf16 MFMA kernel for the shared-weight projections.
 //
-// 256 x 256 tile, eight waves (two per SIMD) of 128 x 64, K-steps of 32.  Tiles
-// are streamed global -> LDS with direct-to-LDS loads (no register staging) into
-// a ring of NSL stages, issued NSL - 1 stages ahead; the fragments of stage
-// kt + 1 are read from LDS while the MFMAs of stage kt run, interleaved one LDS
-// read per few MFMAs.  Within a 1 KB block (16 rows x 32 k) lane L of the load
-// writes row L/4, 16-byte chunk L%4, which holds logical chunk (L%4) ^ ((row/4)%4):
-// the fragment reads (16 rows, one chunk) are then free of bank conflicts.
-template <int BM, int BN, int WM, int WN, int NSL, int EPI>
+// Workgroup tiles of 128 x 64 wave tiles (256 x 256: eight waves, two per SIMD), K
+// steps of 64 held in two LDS stages of (BM + BN) x 64 bf16.  Tiles are streamed
+// global -> LDS with direct-to-LDS loads (no register staging): the loads of stage
+// k + 1 are issued right after the barrier that opens step k, so they run under the
+// step's 2 x TM x TN MFMAs; one barrier per 64-deep step.  Within a 1 KB block (8 rows
+// x 64 k, 128-byte rows) lane L of a load writes row L/8, 16-byte chunk L%8, which
+// holds logical chunk (L%8) ^ swz8(row): the fragment reads (16 rows, one logical
+// chunk) then fall on distinct banks.  Each output element is accumulated by the
+// same MFMA sequence (k ascending, 32 per instruction) for every tile shape.
+__device__ __forceinline__ int swz8(int r) { return (r ^ (r >> 3)) & 7; }
+
+template <int BM, int BN, int WM, int WN, int EPI>
 __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
 gemm_bf16_pipe_kernel(GemmParams p) {
-  constexpr int BK = 32;
+  constexpr int BK = 64;
   constexpr int NWM = BM / WM, NWN = BN / WN, NW = NWM * NWN;
   constexpr int TM = WM / 16, TN = WN / 16;
   constexpr int STAGE = (BM + BN) * BK;              // elements per stage
-  constexpr int ABLK = BM / 16, BBLK = BN / 16;      // 1 KB blocks per stage
+  constexpr int ABLK = BM / 8, BBLK = BN / 8;        // 1 KB blocks per stage
   constexpr int IA = ABLK / NW, IB = BBLK / NW;      // direct loads per wave per stage
   static_assert(IA * NW == ABLK && IB * NW == BBLK, "blocks per wave");
-  static_assert(NSL >= 3, "the fragment pipeline needs three stages");
   extern __shared__ __align__(16) unsigned char smem_raw[];
   bf16_t* sm = (bf16_t*)smem_raw;
 
@@ -496,11 +499,19 @@ gemm_bf16_pipe_kernel(GemmParams p) {
   const bf16_t* Asb = (const bf16_t*)p.As;
   const bf16_t* Bsb = (const bf16_t*)p.Bs;
 
-  const int lrow = lane >> 2;
-  const int lch = (lane & 3) ^ ((lrow >> 2) & 3);
-  int arow[IA], brow[IB];
-  static_for<0, IA>([&](auto i) { arow[i] = min(m0 + (wave * IA + i) * 16 + lrow, p.M - 1); });
-  static_for<0, IB>([&](auto i) { brow[i] = min(n0 + (wave * IB + i) * 16 + lrow, p.N - 1); });
+  // load i of this wave fills block wave * I + i: row blk * 8 + lane / 8 of the tile
+  const int lrow = lane >> 3;
+  int arow[IA], brow[IB], ach[IA], bch[IB];
+  static_for<0, IA>([&](auto i) {
+    const int blk = wave * IA + i;
+    arow[i] = min(m0 + blk * 8 + lrow, p.M - 1);
+    ach[i] = ((lane & 7) ^ ((lrow ^ blk) & 7)) << 3;     // logical chunk of swz8(blk * 8 + lrow)
+  });
+  static_for<0, IB>([&](auto i) {
+    const int blk = wave * IB + i;
+    brow[i] = min(n0 + blk * 8 + lrow, p.N - 1);
+    bch[i] = ((lane & 7) ^ ((lrow ^ blk) & 7)) << 3;
+  });
   const int lda = (int)p.lda, ldb = (int)p.ldb, ldas = (int)p.ldas, ldbs = (int)p.ldbs;
 
   auto issue = [&](int s, int slot) {
@@ -511,67 +522,67 @@ gemm_bf16_pipe_kernel(GemmParams p) {
     const bf16_t* gb = side ? Bsb : Bb;
     const int la = side ? ldas : lda, lb = side ? ldbs : ldb;
     const int kk = side ? (s - nkb) : s, wa = side ? nkwas : nkwa, wb = side ? (1 << 30) : nkwb;
-    const int ka = (kk >= wa ? kk - wa : kk) * BK + lch * 8 + (side ? a_side_off : 0);
-    const int kb = (kk >= wb ? kk - wb : kk) * BK + lch * 8;
+    const int ka = (kk >= wa ? kk - wa : kk) * BK + (side ? a_side_off : 0);
+    const int kb = (kk >= wb ? kk - wb : kk) * BK;
     static_for<0, IA>([&](auto i) {
-      __builtin_amdgcn_global_load_lds((const void*)(ga + (arow[i] * la + ka)),
-                                       (__attribute__((address_space(3))) void*)(sA + (wave * IA + i) * 16 * BK),
+      __builtin_amdgcn_global_load_lds((const void*)(ga + (arow[i] * la + ka + ach[i])),
+                                       (__attribute__((address_space(3))) void*)(sA + (wave * IA + i) * 8 * BK),
                                        16, 0, 0);
     });
     static_for<0, IB>([&](auto i) {
-      __builtin_amdgcn_global_load_lds((const void*)(gb + (brow[i] * lb + kb)),
-                                       (__attribute__((address_space(3))) void*)(sB + (wave * IB + i) * 16 * BK),
+      __builtin_amdgcn_global_load_lds((const void*)(gb + (brow[i] * lb + kb + bch[i])),
+                                       (__attribute__((address_space(3))) void*)(sB + (wave * IB + i) * 8 * BK),
                                        16, 0, 0);
     });
   };
+  // fragment offsets of the two 32-deep halves u of a stage
   const int lr = lane & 15, lk = lane >> 4;
-  int aro[TM], bro[TN];
-  static_for<0, TM>([&](auto i) {
-    const int row = wm * WM + i * 16 + lr;
-    aro[i] = row * BK + ((lk ^ ((row >> 2) & 3)) << 3);
-  });
-  static_for<0, TN>([&](auto j) {
-    const int row = wn * WN + j * 16 + lr;
-    bro[j] = BM * BK + row * BK + ((lk ^ ((row >> 2) & 3)) << 3);
+  int aro[2][TM], bro[2][TN];
+  static_for<0, 2>([&](auto u) {
+    static_for<0, TM>([&](auto i) {
+      const int row = wm * WM + i * 16 + lr;
+      aro[u][i] = row * BK + (((4 * u + lk) ^ swz8(row)) << 3);
+    });
+    static_for<0, TN>([&](auto j) {
+      const int row = wn * WN + j * 16 + lr;
+      bro[u][j] = BM * BK + row * BK + (((4 * u + lk) ^ swz8(row)) << 3);
+    });
   });
   bf16x8_t fa[2][TM], fb[2][TN];
-  auto rd = [&](int slot, auto set) {
-    const bf16_t* base = sm + slot * STAGE;
-    static_for<0, TM>([&](auto i) { fa[set][i] = *(const bf16x8_t*)(base + aro[i]); });
-    static_for<0, TN>([&](auto j) { fb[set][j] = *(const bf16x8_t*)(base + bro[j]); });
+  auto rd = [&](const bf16_t* base, auto u) {
+    static_for<0, TM>([&](auto i) { fa[u][i] = *(const bf16x8_t*)(base + aro[u][i]); });
+    static_for<0, TN>([&](auto j) { fb[u][j] = *(const bf16x8_t*)(base + bro[u][j]); });
   };
   floatx4_t acc[TM][TN];
   static_for<0, TM>([&](auto i) {
     static_for<0, TN>([&](auto j) { acc[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f}; });
   });
-  auto mm = [&](auto set) {
+  auto mm = [&](auto u) {
     static_for<0, TM>([&](auto i) {
       static_for<0, TN>([&](auto j) {
-        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[set][j], fa[set][i], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(fb[u][j], fa[u][i], acc[i][j], 0, 0, 0);
       });
     });
   };
-  // prologue: stages 0 .. NSL-2 in flight; wait for stage 0 in every wave
-  static_for<0, NSL - 1>([&](auto s) { issue(min((int)s, nk - 1), s); });
-  asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"((NSL - 2) * (IA + IB)) : "memory");
-  rd(0, std::integral_constant<int, 0>{});
-  for (int kt0 = 0; kt0 < nk; kt0 += 2) {
-    static_for<0, 2>([&](auto j) {
-      const int kt = kt0 + j;
-      if (kt < nk) {
-        // stage kt+1 has landed in every wave's part (its loads are NSL-2 stages old);
-        // the barrier also retires every read of the slot refilled below
-        asm volatile("s_waitcnt vmcnt(%0)\n\ts_barrier" ::"n"((NSL - 3) * (IA + IB)) : "memory");
-        issue(min(kt + NSL - 1, nk - 1), (kt + NSL - 1) % NSL);
-        rd((kt + 1) % NSL, std::integral_constant<int, 1 - j>{});
-        mm(j);
-        __builtin_amdgcn_sched_group_barrier(0x020, IA + IB, 0);                   // the direct loads
-        static_for<0, TM + TN>([&](auto) {
-          __builtin_amdgcn_sched_group_barrier(0x008, (TM * TN) / (TM + TN), 0);   // MFMAs on ready fragments
-          __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                        // one LDS read
-        });
-      }
+  constexpr int MPR = (TM * TN) / (TM + TN);           // MFMAs per interleaved LDS read
+  if (nk > 0) issue(0, 0);
+  for (int kt = 0; kt < nk; ++kt) {
+    // this wave's loads of stage kt have landed; after the barrier so have every
+    // wave's, and every read of the other slot (stage kt - 1) is retired
+    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+    if (kt + 1 < nk) issue(kt + 1, (kt + 1) & 1);
+    const bf16_t* base = sm + (kt & 1) * STAGE;
+    rd(base, std::integral_constant<int, 0>{});
+    rd(base, std::integral_constant<int, 1>{});
+    mm(std::integral_constant<int, 0>{});
+    mm(std::integral_constant<int, 1>{});
+    __builtin_amdgcn_sched_group_barrier(0x020, IA + IB, 0);                 // the direct loads
+    __builtin_amdgcn_sched_group_barrier(0x100, TM + TN, 0);                 // first half's fragments
+    static_for<0, TM + TN>([&](auto) {
+      __builtin_amdgcn_sched_group_barrier(0x008, MPR, 0);                   // MFMAs on ready fragments
+      __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                     // one read of the second half
     });
+    __builtin_amdgcn_sched_group_barrier(0x008, 2 * TM * TN - MPR * (TM + TN), 0);
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no LDS write outlives the workgroup
   epilogue_rows<EPI, TM, TN, WM, WN>(p, acc, m0, n0, wm, wn, lane);
@@ -663,19 +674,19 @@ hipError_t launch_bf16(const GemmParams& p, hipStream_t s) {
   return hipGetLastError();
 }
 
-template <int BM, int BN, int WM, int WN, int NSL, int EPI>
+template <int BM, int BN, int WM, int WN, int EPI>
 hipError_t launch_bf16_pipe(const GemmParams& p, hipStream_t s) {
   constexpr int NT = (BM / WM) * (BN / WN) * 64;
-  const size_t smem = (size_t)NSL * (BM + BN) * 32 * sizeof(bf16_t);
+  const size_t smem = (size_t)2 * (BM + BN) * 64 * sizeof(bf16_t);
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)gemm_bf16_pipe_kernel<BM, BN, WM, WN, NSL, EPI>,
+    hipError_t e = hipFuncSetAttribute((const void*)gemm_bf16_pipe_kernel<BM, BN, WM, WN, EPI>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   const int tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_bf16_pipe_kernel<BM, BN, WM, WN, NSL, EPI>), dim3(tiles), dim3(NT), smem, s, p);
+  hipLaunchKernelGGL((gemm_bf16_pipe_kernel<BM, BN, WM, WN, EPI>), dim3(tiles), dim3(NT), smem, s, p);
   return hipGetLastError();
 }
 
@@ -721,22 +732,21 @@ int gemm_cfg_bn(int cfg, bool bf16) {
   if (!bf16) return 64;
   return cfg == GEMM_CFG_BIG ? 256 : 128;
 }
-// K granularity of each call site: the pipelined projection kernel steps K by 32,
-// the register-staged kernels by 64.
+// K granularity of each call site: every bf16 kernel steps K by 64.
 int gemm_cfg_bk(int cfg, bool bf16) {
-  if (!bf16) return BK_F32;
-  return cfg == GEMM_CFG_BIG ? 32 : BK_BF16;
+  (void)cfg;
+  return bf16 ? BK_BF16 : BK_F32;
 }
 // side-input column granularity (a multiple of every consumer's K-step)
-int gemm_bk(bool bf16) { return bf16 ? 32 : BK_F32; }
+int gemm_bk(bool bf16) { return bf16 ? BK_BF16 : BK_F32; }
 
 template <int BM, int BN>
 hipError_t launch_pipe_epi(const GemmParams& p, hipStream_t s) {
   switch (p.epi) {
-    case EPI_STORE: return launch_bf16_pipe<BM, BN, 128, 64, 4, EPI_STORE>(p, s);
-    case EPI_GELU: return launch_bf16_pipe<BM, BN, 128, 64, 4, EPI_GELU>(p, s);
-    case EPI_SWIGLU: return launch_bf16_pipe<BM, BN, 128, 64, 4, EPI_SWIGLU>(p, s);
-    case EPI_RESID: return launch_bf16_pipe<BM, BN, 128, 64, 4, EPI_RESID>(p, s);
+    case EPI_STORE: return launch_bf16_pipe<BM, BN, 128, 64, EPI_STORE>(p, s);
+    case EPI_GELU: return launch_bf16_pipe<BM, BN, 128, 64, EPI_GELU>(p, s);
+    case EPI_SWIGLU: return launch_bf16_pipe<BM, BN, 128, 64, EPI_SWIGLU>(p, s);
+    case EPI_RESID: return launch_bf16_pipe<BM, BN, 128, 64, EPI_RESID>(p, s);
     default: return hipErrorInvalidValue;
   }
 }
@@ -765,8 +775,8 @@ hipError_t gemm_launch_bf16(const GemmParams& p, int cfg, hipStream_t s) {
   }
   if (cfg == GEMM_CFG_NARROW) {
     // many factor columns (high rank, several entries): the pipelined projection kernel
-    if (p.epi == EPI_TPROJ && p.N >= 512 && p.N % 16 == 0 && p.K % 32 == 0 && p.ksplit <= 1)
-      return launch_bf16_pipe<256, 256, 128, 64, 4, EPI_TPROJ>(p, s);
+    if (p.epi == EPI_TPROJ && p.N >= 512 && p.N % 16 == 0 && p.K % 64 == 0 && p.ksplit <= 1)
+      return launch_bf16_pipe<256, 256, 128, 64, EPI_TPROJ>(p, s);
     if (p.epi == EPI_TPROJ) {
       // N <= 32 (one kind block at rank <= 8 and few entries): a 128 x 32 tile, so the
       // factor rows are not re-read for absent columns

@@ -424,7 +424,9 @@ int side_geometry(const zo_model* m, const zo_plan_s& p, const zo_bank* bank, Si
     }
     sg.dslot.push_back(slot);
   }
-  sg.ks_c = (int)round_up(sg.nc * sg.r, bk);
+  // computed t columns per kind: an output width of the side-input projection (any
+  // multiple of 32 serves), not a K extent like ks
+  sg.ks_c = (int)round_up(sg.nc * sg.r, d.dtype == ZO_DTYPE_BF16 ? 32 : bk);
   sg.groups = layer_groups(d);
   const int64_t D = d.d_model, F = d.d_ffn;
   const int64_t NQ = (int64_t)d.n_heads * d.head_dim, NKV = (int64_t)d.n_kv_heads * d.head_dim;
