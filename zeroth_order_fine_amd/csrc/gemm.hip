@@ -373,12 +373,69 @@ __device__ __forceinline__ void store_bf16x4(const GemmParams& p, bf16_t* o, flo
         make_uint2((uint32_t)lo[0] | ((uint32_t)lo[1] << 16), (uint32_t)lo[2] | ((uint32_t)lo[3] << 16));
 }
 
-template <int EPI, int TM, int TN, int WM, int WN>
+template <int EPI, int TM, int TN, int BM, int BN, int WM, int WN>
 __device__ __forceinline__ void epilogue_rows(const GemmParams& p, floatx4_t (&acc)[TM][TN], int m0, int n0, int wm,
-                                              int wn, int lane) {
+                                              int wn, int lane, float* red) {
   const int rb = m0 + wm * WM + (lane & 15);
   const int cb = n0 + wn * WN + 4 * (lane >> 4);
-  if constexpr (EPI == EPI_TPROJ) {
+  if constexpr (EPI == EPI_LMHEAD) {
+    // per row and 256-column tile: max and sum of exp of the logits, and the label's
+    // logit; logits never leave registers.  A row's 64 columns of a wave sit in the
+    // four lanes l, l + 16, l + 32, l + 48; the NWN waves along N meet in LDS.
+    constexpr int NWN = BN / WN;
+    float* rmax = red;                 // [NWN][BM]
+    float* rsum = red + NWN * BM;      // [NWN][BM]
+    __syncthreads();                   // every wave is past its last LDS read of the stages
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      float m = -INFINITY;
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (cb + j * 16 + q < p.N) m = fmaxf(m, acc[i][j][q]);
+      m = fmaxf(m, __shfl_xor(m, 16, 64));
+      m = fmaxf(m, __shfl_xor(m, 32, 64));
+      if (lane < 16) rmax[wn * BM + wm * WM + i * 16 + lane] = m;
+    }
+    __syncthreads();
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int rl = wm * WM + i * 16 + (lane & 15);
+      float m = rmax[rl];
+#pragma unroll
+      for (int w = 1; w < NWN; ++w) m = fmaxf(m, rmax[w * BM + rl]);
+      float sum = 0.f;
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          if (cb + j * 16 + q < p.N) sum += expf(acc[i][j][q] - m);
+      sum += __shfl_xor(sum, 16, 64);
+      sum += __shfl_xor(sum, 32, 64);
+      if (lane < 16) rsum[wn * BM + rl] = sum;
+      const int r = m0 + rl;
+      if (r < p.M) {
+        const int lab = p.labels[r];
+#pragma unroll
+        for (int j = 0; j < TN; ++j)
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            if (cb + j * 16 + q == lab) p.lab_logit[r] = acc[i][j][q];
+      }
+    }
+    __syncthreads();
+    const int nt = n0 / BN;
+    for (int rl = threadIdx.x; rl < BM; rl += blockDim.x) {
+      const int r = m0 + rl;
+      if (r >= p.M) continue;
+      float m = rmax[rl], sum = 0.f;
+      for (int w = 1; w < NWN; ++w) m = fmaxf(m, rmax[w * BM + rl]);
+      for (int w = 0; w < NWN; ++w) sum += rsum[w * BM + rl];
+      p.part[(int64_t)r * p.n_ntiles + nt] = make_float2(m, sum);
+    }
+    return;
+  } else if constexpr (EPI == EPI_TPROJ) {
     // side input t: columns of x.[V...] kept for the bank entries, scaled by s * eps~
     // for the row's own direction, zero elsewhere (as in the register-staged epilogue)
 #pragma unroll
@@ -585,7 +642,7 @@ gemm_bf16_pipe_kernel(GemmParams p) {
     __builtin_amdgcn_sched_group_barrier(0x008, 2 * TM * TN - MPR * (TM + TN), 0);
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no LDS write outlives the workgroup
-  epilogue_rows<EPI, TM, TN, WM, WN>(p, acc, m0, n0, wm, wn, lane);
+  epilogue_rows<EPI, TM, TN, BM, BN, WM, WN>(p, acc, m0, n0, wm, wn, lane, (float*)smem_raw);
 }
 
 // ------------------------------------------------------------------------------
@@ -722,15 +779,15 @@ hipError_t launch_tproj_reduce(const GemmParams& p, hipStream_t s) {
 }
 
 // Tile shapes per call site.  BIG: the shared-weight projections; NARROW: the
-// side-input projection (N = a few kind blocks); HEAD: the vocabulary head
-// (few rows, many columns).
+// side-input projection (N = a few kind blocks); HEAD: the vocabulary head (the
+// projection kernel with 256-column tiles).
 int gemm_cfg_bm(int cfg, bool bf16) {
   if (!bf16) return 64;
-  return cfg == GEMM_CFG_BIG ? 256 : (cfg == GEMM_CFG_NARROW ? 64 : 128);
+  return cfg == GEMM_CFG_NARROW ? 64 : 256;
 }
 int gemm_cfg_bn(int cfg, bool bf16) {
   if (!bf16) return 64;
-  return cfg == GEMM_CFG_BIG ? 256 : 128;
+  return cfg == GEMM_CFG_NARROW ? 128 : 256;
 }
 // K granularity of each call site: every bf16 kernel steps K by 64.
 int gemm_cfg_bk(int cfg, bool bf16) {
@@ -793,7 +850,13 @@ hipError_t gemm_launch_bf16(const GemmParams& p, int cfg, hipStream_t s) {
     if (p.epi == EPI_STORE) return launch_bf16<64, 128, 32, 64, EPI_STORE>(p, s);
     return hipErrorInvalidValue;
   }
-  if (p.epi == EPI_LMHEAD) return launch_bf16<128, 128, 64, 64, EPI_LMHEAD>(p, s);
+  // the vocabulary head: always 256-column tiles (the log-sum-exp partials, and so each
+  // row's result, then do not depend on the batch); 128 or 256 rows per tile
+  if (p.epi == EPI_LMHEAD) {
+    auto tiles = [&](int bm) { return (int64_t)((p.M + bm - 1) / bm) * ((p.N + 255) / 256); };
+    if (tiles(256) >= 128) return launch_bf16_pipe<256, 256, 128, 64, EPI_LMHEAD>(p, s);
+    return launch_bf16_pipe<128, 256, 128, 64, EPI_LMHEAD>(p, s);
+  }
   return hipErrorInvalidValue;
 }
 

@@ -470,7 +470,8 @@ struct WsPtrs {
 // chosen from N and K alone so that a row's result never depends on the batch.
 int tproj_split(const zo_model_desc& d, int64_t n_cols, int64_t k) {
   if (d.dtype != ZO_DTYPE_BF16 || n_cols == 0 || n_cols > 128) return 1;
-  int s = 8;
+  // the 128 x 32 tile (n_cols <= 32) has half as many row tiles as the 64 x 128 one
+  int s = n_cols <= 32 ? 8 : 4;
   while (s > 1 && (k % (64 * s) != 0 || k / (64 * s) < 8)) s >>= 1;
   return s;
 }
