@@ -508,14 +508,23 @@ __device__ __forceinline__ void epilogue_rows(const GemmParams& p, floatx4_t (&a
 //
 // Workgroup tiles of 128 x 64 wave tiles (256 x 256: eight waves, two per SIMD), K
 // steps of 64 held in two LDS stages of (BM + BN) x 64 bf16.  Tiles are streamed
-// global -> LDS with direct-to-LDS loads (no register staging): the loads of stage
-// k + 1 are issued right after the barrier that opens step k, so they run under the
-// step's 2 x TM x TN MFMAs; one barrier per 64-deep step.  Within a 1 KB block (8 rows
-// x 64 k, 128-byte rows) lane L of a load writes row L/8, 16-byte chunk L%8, which
-// holds logical chunk (L%8) ^ swz8(row): the fragment reads (16 rows, one logical
-// chunk) then fall on distinct banks.  Each output element is accumulated by the
+// global -> LDS by buffer loads straight into LDS (no register staging; a fixed
+// per-lane byte offset in a VGPR, the K position in the scalar offset): the loads of
+// stage k + 1 are issued right after the barrier that opens step k, so they run under
+// the step's 2 x TM x TN MFMAs; one barrier per 64-deep step.  LDS holds
+// [A0 | A1 | B0 | B1], so the stage switch is an immediate offset of the LDS reads.
+// Within a 1 KB block (8 rows x 64 k, 128-byte rows) lane L of a load writes row L/8,
+// 16-byte chunk L%8, which holds logical chunk (L%8) ^ swz8(row): the fragment reads
+// (16 rows, one logical chunk) then fall on distinct banks.  Each output element is
+// accumulated by the
 // same MFMA sequence (k ascending, 32 per instruction) for every tile shape.
 __device__ __forceinline__ int swz8(int r) { return (r ^ (r >> 3)) & 7; }
+
+// buffer resource over `bytes` bytes at `base` (raw addressing: offsets past the end read 0)
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void* base, int64_t bytes) {
+  const uint32_t n = bytes > (int64_t)0xffffffff ? 0xffffffffu : (uint32_t)bytes;
+  return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)n, 0x00020000);
+}
 
 template <int BM, int BN, int WM, int WN, int EPI>
 __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
@@ -523,12 +532,12 @@ gemm_bf16_pipe_kernel(GemmParams p) {
   constexpr int BK = 64;
   constexpr int NWM = BM / WM, NWN = BN / WN, NW = NWM * NWN;
   constexpr int TM = WM / 16, TN = WN / 16;
-  constexpr int STAGE = (BM + BN) * BK;              // elements per stage
-  constexpr int ABLK = BM / 8, BBLK = BN / 8;        // 1 KB blocks per stage
-  constexpr int IA = ABLK / NW, IB = BBLK / NW;      // direct loads per wave per stage
+  constexpr int ASZ = BM * BK, BSZ = BN * BK;          // elements of one stage of A / of B
+  constexpr int ABLK = BM / 8, BBLK = BN / 8;          // 1 KB blocks per stage
+  constexpr int IA = ABLK / NW, IB = BBLK / NW;        // loads per wave per stage
   static_assert(IA * NW == ABLK && IB * NW == BBLK, "blocks per wave");
   extern __shared__ __align__(16) unsigned char smem_raw[];
-  bf16_t* sm = (bf16_t*)smem_raw;
+  bf16_t* sm = (bf16_t*)smem_raw;                      // [A stage 0 | A stage 1 | B stage 0 | B stage 1]
 
   const int n_mt = (p.M + BM - 1) / BM, n_nt = (p.N + BN - 1) / BN;
   int logical;
@@ -551,48 +560,59 @@ gemm_bf16_pipe_kernel(GemmParams p) {
   const int nkb = p.K / BK, nk = nkb + p.ks_tile / BK;
   const int nkwa = p.kwa ? p.kwa / BK : (1 << 30), nkwb = p.kwb ? p.kwb / BK : (1 << 30);
   const int nkwas = p.kwas ? p.kwas / BK : (1 << 30);
-  const bf16_t* Ab = (const bf16_t*)p.A;
-  const bf16_t* Bb = (const bf16_t*)p.B;
-  const bf16_t* Asb = (const bf16_t*)p.As;
-  const bf16_t* Bsb = (const bf16_t*)p.Bs;
+  const __amdgpu_buffer_rsrc_t rA = raw_rsrc(p.A, (int64_t)p.M * p.lda * 2);
+  const __amdgpu_buffer_rsrc_t rB = raw_rsrc(p.B, (int64_t)p.N * p.ldb * 2);
 
-  // load i of this wave fills block wave * I + i: row blk * 8 + lane / 8 of the tile
+  // load i of this wave fills 1 KB block wave * I + i: tile row blk * 8 + lane / 8, the
+  // lane's 16 bytes holding logical chunk (lane % 8) ^ swz8(row).  Byte offsets of the
+  // row and chunk stay in VGPRs; the K position goes in the scalar offset.
   const int lrow = lane >> 3;
-  int arow[IA], brow[IB], ach[IA], bch[IB];
-  static_for<0, IA>([&](auto i) {
+  // element offset (row * ld + chunk) of load i, recomputed where needed rather than kept
+  auto a_elem = [&](int i, int ld) {
     const int blk = wave * IA + i;
-    arow[i] = min(m0 + blk * 8 + lrow, p.M - 1);
-    ach[i] = ((lane & 7) ^ ((lrow ^ blk) & 7)) << 3;     // logical chunk of swz8(blk * 8 + lrow)
-  });
-  static_for<0, IB>([&](auto i) {
-    const int blk = wave * IB + i;
-    brow[i] = min(n0 + blk * 8 + lrow, p.N - 1);
-    bch[i] = ((lane & 7) ^ ((lrow ^ blk) & 7)) << 3;
-  });
-  const int lda = (int)p.lda, ldb = (int)p.ldb, ldas = (int)p.ldas, ldbs = (int)p.ldbs;
-
-  auto issue = [&](int s, int slot) {
-    bf16_t* sA = sm + slot * STAGE;
-    bf16_t* sB = sA + BM * BK;
-    const bool side = s >= nkb;
-    const bf16_t* ga = side ? Asb : Ab;
-    const bf16_t* gb = side ? Bsb : Bb;
-    const int la = side ? ldas : lda, lb = side ? ldbs : ldb;
-    const int kk = side ? (s - nkb) : s, wa = side ? nkwas : nkwa, wb = side ? (1 << 30) : nkwb;
-    const int ka = (kk >= wa ? kk - wa : kk) * BK + (side ? a_side_off : 0);
-    const int kb = (kk >= wb ? kk - wb : kk) * BK;
-    static_for<0, IA>([&](auto i) {
-      __builtin_amdgcn_global_load_lds((const void*)(ga + (arow[i] * la + ka + ach[i])),
-                                       (__attribute__((address_space(3))) void*)(sA + (wave * IA + i) * 8 * BK),
-                                       16, 0, 0);
-    });
-    static_for<0, IB>([&](auto i) {
-      __builtin_amdgcn_global_load_lds((const void*)(gb + (brow[i] * lb + kb + bch[i])),
-                                       (__attribute__((address_space(3))) void*)(sB + (wave * IB + i) * 8 * BK),
-                                       16, 0, 0);
-    });
+    return min(m0 + blk * 8 + lrow, p.M - 1) * ld + (((lane & 7) ^ ((lrow ^ blk) & 7)) << 3);
   };
-  // fragment offsets of the two 32-deep halves u of a stage
+  auto b_elem = [&](int i, int ld) {
+    const int blk = wave * IB + i;
+    return min(n0 + blk * 8 + lrow, p.N - 1) * ld + (((lane & 7) ^ ((lrow ^ blk) & 7)) << 3);
+  };
+  int aoff[IA], boff[IB];
+  static_for<0, IA>([&](auto i) { aoff[i] = a_elem(i, (int)p.lda) * 2; });
+  static_for<0, IB>([&](auto i) { boff[i] = b_elem(i, (int)p.ldb) * 2; });
+  auto issue = [&](int s, auto slot) {
+    bf16_t* sA = sm + slot * ASZ;
+    bf16_t* sB = sm + 2 * ASZ + slot * BSZ;
+    if (s < nkb) {
+      const int ka = (s >= nkwa ? s - nkwa : s) * BK * 2;
+      const int kb = (s >= nkwb ? s - nkwb : s) * BK * 2;
+      static_for<0, IA>([&](auto i) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rA, (__attribute__((address_space(3))) void*)(sA + (wave * IA + i) * 8 * BK), 16, aoff[i], ka, 0, 0);
+      });
+      static_for<0, IB>([&](auto i) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rB, (__attribute__((address_space(3))) void*)(sB + (wave * IB + i) * 8 * BK), 16, boff[i], kb, 0, 0);
+      });
+    } else {                                  // side segment (the last few steps)
+      const __amdgpu_buffer_rsrc_t rAs = raw_rsrc(p.As, (int64_t)p.M * p.ldas * 2);
+      const __amdgpu_buffer_rsrc_t rBs = raw_rsrc(p.Bs, (int64_t)p.N * p.ldbs * 2);
+      const int kk = s - nkb;
+      const int ka = ((kk >= nkwas ? kk - nkwas : kk) * BK + a_side_off) * 2;
+      const int kb = kk * BK * 2;
+      static_for<0, IA>([&](auto i) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rAs, (__attribute__((address_space(3))) void*)(sA + (wave * IA + i) * 8 * BK), 16,
+            a_elem(i, (int)p.ldas) * 2, ka, 0, 0);
+      });
+      static_for<0, IB>([&](auto i) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rBs, (__attribute__((address_space(3))) void*)(sB + (wave * IB + i) * 8 * BK), 16,
+            b_elem(i, (int)p.ldbs) * 2, kb, 0, 0);
+      });
+    }
+  };
+  // fragment offsets of the two 32-deep halves u of a stage (stage 0; stage 1 adds an
+  // immediate)
   const int lr = lane & 15, lk = lane >> 4;
   int aro[2][TM], bro[2][TN];
   static_for<0, 2>([&](auto u) {
@@ -602,13 +622,13 @@ gemm_bf16_pipe_kernel(GemmParams p) {
     });
     static_for<0, TN>([&](auto j) {
       const int row = wn * WN + j * 16 + lr;
-      bro[u][j] = BM * BK + row * BK + (((4 * u + lk) ^ swz8(row)) << 3);
+      bro[u][j] = 2 * ASZ + row * BK + (((4 * u + lk) ^ swz8(row)) << 3);
     });
   });
   bf16x8_t fa[2][TM], fb[2][TN];
-  auto rd = [&](const bf16_t* base, auto u) {
-    static_for<0, TM>([&](auto i) { fa[u][i] = *(const bf16x8_t*)(base + aro[u][i]); });
-    static_for<0, TN>([&](auto j) { fb[u][j] = *(const bf16x8_t*)(base + bro[u][j]); });
+  auto rd = [&](auto slot, auto u) {
+    static_for<0, TM>([&](auto i) { fa[u][i] = *(const bf16x8_t*)(sm + slot * ASZ + aro[u][i]); });
+    static_for<0, TN>([&](auto j) { fb[u][j] = *(const bf16x8_t*)(sm + slot * BSZ + bro[u][j]); });
   };
   floatx4_t acc[TM][TN];
   static_for<0, TM>([&](auto i) {
@@ -622,24 +642,27 @@ gemm_bf16_pipe_kernel(GemmParams p) {
     });
   };
   constexpr int MPR = (TM * TN) / (TM + TN);           // MFMAs per interleaved LDS read
-  if (nk > 0) issue(0, 0);
-  for (int kt = 0; kt < nk; ++kt) {
+  auto step = [&](int kt, auto slot) {
     // this wave's loads of stage kt have landed; after the barrier so have every
-    // wave's, and every read of the other slot (stage kt - 1) is retired
+    // wave's, and every read of the other stage (kt - 1) is retired
     asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
-    if (kt + 1 < nk) issue(kt + 1, (kt + 1) & 1);
-    const bf16_t* base = sm + (kt & 1) * STAGE;
-    rd(base, std::integral_constant<int, 0>{});
-    rd(base, std::integral_constant<int, 1>{});
+    if (kt + 1 < nk) issue(kt + 1, std::integral_constant<int, 1 - slot>{});
+    rd(slot, std::integral_constant<int, 0>{});
+    rd(slot, std::integral_constant<int, 1>{});
     mm(std::integral_constant<int, 0>{});
     mm(std::integral_constant<int, 1>{});
-    __builtin_amdgcn_sched_group_barrier(0x020, IA + IB, 0);                 // the direct loads
+    __builtin_amdgcn_sched_group_barrier(0x020, IA + IB, 0);                 // the loads
     __builtin_amdgcn_sched_group_barrier(0x100, TM + TN, 0);                 // first half's fragments
     static_for<0, TM + TN>([&](auto) {
       __builtin_amdgcn_sched_group_barrier(0x008, MPR, 0);                   // MFMAs on ready fragments
       __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);                     // one read of the second half
     });
     __builtin_amdgcn_sched_group_barrier(0x008, 2 * TM * TN - MPR * (TM + TN), 0);
+  };
+  if (nk > 0) issue(0, std::integral_constant<int, 0>{});
+  for (int kt = 0; kt < nk; kt += 2) {
+    step(kt, std::integral_constant<int, 0>{});
+    if (kt + 1 < nk) step(kt + 1, std::integral_constant<int, 1>{});
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no LDS write outlives the workgroup
   epilogue_rows<EPI, TM, TN, BM, BN, WM, WN>(p, acc, m0, n0, wm, wn, lane, (float*)smem_raw);
