@@ -272,6 +272,10 @@ enum { ZO_PROF_GEMM_BASE = 0,   /* shared-weight projections (qkv, o, fc1/gate-u
        ZO_PROF_N_CLASSES = 8 };
 int zo_profile_begin(void);
 int zo_profile_end(int32_t n_classes, int64_t* counts, double* total_ms);
+/* Restrict timing to the classes whose bit (1 << class) is set in class_mask (default:
+   all); fewer events on the stream, e.g. only the projections while a throughput
+   measurement runs. */
+int zo_profile_select(uint32_t class_mask);
 
 #ifdef __cplusplus
 }

@@ -56,6 +56,7 @@ _SIGS = {
     "zo_direction": (c_i32, [c_vp, c_vp, c_i32, c_i32, c_i32, c_i32, c_vp, c_vp]),
     "zo_profile_begin": (c_i32, []),
     "zo_profile_end": (c_i32, [c_i32, P(c_i64), P(c_dbl)]),
+    "zo_profile_select": (c_i32, [c_u32]),
 }
 
 EXPORTED = tuple(_SIGS)

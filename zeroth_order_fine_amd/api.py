@@ -288,8 +288,12 @@ def direction(model, plan, dir_index, layer, kind_name, which):
 PROFILE_CLASSES = ("gemm_base", "gemm_side", "gemm_head", "attention", "norm", "side_prep", "reduce", "update")
 
 
-def profile_begin():
-    _check(_lib.load().zo_profile_begin())
+def profile_begin(classes=None):
+    """Start timing every launch of the named classes (default: all)."""
+    L = _lib.load()
+    mask = 0xFFFFFFFF if classes is None else sum(1 << PROFILE_CLASSES.index(c) for c in classes)
+    _check(L.zo_profile_select(mask))
+    _check(L.zo_profile_begin())
 
 
 def profile_end():

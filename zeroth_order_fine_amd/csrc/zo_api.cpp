@@ -48,6 +48,7 @@ int fail(int code, const char* fmt, ...) {
 // ---- launch timing (zo_profile_begin / zo_profile_end) -------------------------
 struct Prof {
   bool on = false;
+  uint32_t mask = ~0u;        // classes recorded
   std::vector<hipEvent_t> pool;
   size_t used = 0;
   struct Rec { int cls; size_t ev; };
@@ -57,7 +58,7 @@ Prof g_prof;
 
 // Records the start event of a launch of class `cls`; returns the record index or -1.
 long prof_start(int cls, hipStream_t s) {
-  if (!g_prof.on) return -1;
+  if (!g_prof.on || !((g_prof.mask >> cls) & 1u)) return -1;
   if (g_prof.used + 2 > g_prof.pool.size()) {
     for (int i = 0; i < 256; ++i) {
       hipEvent_t e;
@@ -1276,6 +1277,11 @@ int zo_bank_fold(zo_model* m, zo_bank* bank, int32_t slot, void* ws_dev, size_t 
   ZO_HIP(hipStreamSynchronize(s));
   bank->windows[slot] = -1;
   bank->seeds[slot] = 0;
+  return ZO_OK;
+}
+
+int zo_profile_select(uint32_t class_mask) {
+  g_prof.mask = class_mask;
   return ZO_OK;
 }
 
