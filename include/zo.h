@@ -18,6 +18,8 @@
  *   zo_estimate  c_d = (L_{d,+} - L_{d,-}) / (2 eps), optional explicit 1/r
  *   zo_update    lazy low-rank accumulation into the persistent bank
  *
+ * plus zo_bank_fold, which commits a finished window's bank entry into the weights.
+ *
  * Conventions for every function:
  *   - returns ZO_OK (0) or a negative zo_status; no exception or abort crosses
  *     the ABI; zo_last_error() gives a message for the calling thread;
@@ -30,9 +32,16 @@
  *   - stream arguments are hipStream_t; work is enqueued on that stream.
  *
  * Random numbers: every random direction is a pure function of (seed, step,
- * layer, linear kind) through Philox4x32-10 and an exact-operation Box-Muller
- * transform (see the stream specification in the design notes shipped with
- * the library), so factors are regenerated on the GPU, never stored.
+ * layer, linear kind), so factors are regenerated on the GPU, never stored.
+ * Element e of the stream (seed, tag, tau) is word e % 4 of the Philox4x32-10
+ * block with counter (e / 4, tag, lo32 tau, hi32 tau) and key (lo32 seed,
+ * hi32 seed); a Gaussian pair comes from two words by Box-Muller evaluated with
+ * binary64 +, -, *, /, sqrt only (no fused multiply-add): u = (w + 1/2) 2^-32,
+ * R = sqrt(-2 ln u), ln by an exponent/mantissa split and the atanh series,
+ * the angle from the other word (2-bit quadrant, half-quadrant bit, 29-bit
+ * fraction times pi/4) with sin / cos by Taylor forms and an exact rotation;
+ * words (0, 1) and (2, 3) of a block form the two pairs; factors are rounded
+ * to fp32.
  */
 #ifndef ZO_H_
 #define ZO_H_

@@ -9,7 +9,7 @@ and the arXiv abstract of "Inference-Native Zeroth-Order Optimization"
 (query process, ProbePlan, candidate evaluation, factorized side states,
 persistent banked state).
 
-Readings where the pages are silent (all listed in the design notes):
+Readings where the pages are silent:
   * z = G V^T per target linear; G [n_out, r], V [n_in, r], entries N(0,1),
     and eps_tilde = eps (or eps/sqrt(r) with scale_inv_sqrt_r, the
     MeZO-factorized variant whose entries have unit variance).

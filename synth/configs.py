@@ -95,6 +95,8 @@ CONFIGS = {
     "tiny": Workload("tiny", TINY, 4, 32, 32, "uniform", "last_label", 2, 1e-3, (0,), ("q", "v")),
     "opt1.3b": Workload("opt1.3b", OPT_1_3B, 16, 16, 64, "zipf", "last_label", 2, 1e-3, (0,), _ALL_OPT),
     "opt13b": Workload("opt13b", OPT_13B, 64, 16, 128, "zipf", "last_label", 2, 1e-3, (0,), _ALL_OPT),
+    # one GPU's share of the batch-64 step split data-parallel over 8 GPUs (8 prompts)
+    "opt13b-share8": Workload("opt13b-share8", OPT_13B, 8, 16, 128, "zipf", "last_label", 2, 1e-3, (0,), _ALL_OPT),
     "opt6.7b-mezo": Workload("opt6.7b-mezo", OPT_6_7B, 32, 128, 128, "zipf", "all_next", 64, 1e-3,
                              (0, 1, 2, 3), _ALL_OPT, scale_inv_sqrt_r=True, act_split=True),
     "qwen3-8b-mixed": Workload("qwen3-8b-mixed", QWEN3_8B, 16, 32, 512, "zipf", "last_label", 4, 1e-3,
