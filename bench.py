@@ -367,6 +367,24 @@ def main():
             fg = batch.subset([i for i in range(batch.n_seq) if batch.role[i] == inputs.ROLE_FOREGROUND])
             extra["score_ms_foreground_only"] = round(score_ms(bank, zo.DeviceBatch(fg)), 3)
             extra["foreground_only_tokens_per_s"] = round(fg_tokens / (extra["score_ms_foreground_only"] / 1e3), 1)
+        if not wl.act_split and cfg.dtype == "bf16":
+            # the same step with two-term activations (what keeps c within 1e-2 at eps = 1e-3)
+            wl2 = wl.with_(act_split=True)
+            bank2 = zo.Bank(model, 2 * wl.n_dirs, wl.rank, wl.targets)
+            for t in range(2):
+                p2 = zo.Plan.from_workload(model, wl2, t=t)
+                zo.update(model, p2, bank2, zo.estimate(p2, zo.score(model, p2, bank2, db)["S"]), args.lr)
+            torch.cuda.synchronize()
+            a = time.perf_counter()
+            n2 = 3
+            for t in range(2, 2 + n2):
+                p2 = zo.Plan.from_workload(model, wl2, t=t)
+                zo.update(model, p2, bank2, zo.estimate(p2, zo.score(model, p2, bank2, db)["S"]), args.lr)
+            torch.cuda.synchronize()
+            ms2 = (time.perf_counter() - a) / n2 * 1e3
+            extra["two_term_ms_per_step"] = round(ms2, 3)
+            extra["two_term_tokens_per_s"] = round(probe_tokens / (ms2 / 1e3), 1)
+            del bank2
         line["other_states"] = extra
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, batch)

@@ -51,7 +51,7 @@ def _run(name, split=None):
     return gold, wl, batch, model, bank, db, out, list(zip(phys_seq, phys_cand)), first
 
 
-def _check(name, gold, wl, out, phys, first, seq_bound):
+def _check(name, gold, wl, out, phys, first, seq_bound, c_gpu=None):
     seq = out["seq_logp"].cpu().numpy()
     tok = out["tok_logp"].cpu().numpy()
     errs = []
@@ -73,6 +73,14 @@ def _check(name, gold, wl, out, phys, first, seq_bound):
         dS = np.abs(S - np.array(gold["S"]))
         flush("%s: per-candidate |dS| %s (budget %s)" % (name, np.round(dS, 4), 2e-2 * n_seq))
         assert np.all(dS <= 2e-2 * n_seq), (S, gold["S"])
+        if "c" in gold and c_gpu is not None:
+            c = np.asarray(c_gpu)
+            rel = np.abs(c - np.array(gold["c"])) / np.abs(np.array(gold["c"]))
+            flush("%s (split %s): c %s oracle %s, relative error %s" % (name, wl.act_split, c, gold["c"], rel))
+            if wl.act_split:
+                # the estimate divides the score difference by 2 eps: only two-term
+                # activations keep it within the fp32 contract's 1e-2 relative
+                assert np.all(rel <= 1e-2), (c, gold["c"])
     return seq, tok
 
 
@@ -80,8 +88,10 @@ def _check(name, gold, wl, out, phys, first, seq_bound):
 def test_full_size_against_oracle(name):
     need_gpu()
     import torch
+    import zeroth_order_fine_amd as zo
     gold, wl, batch, model, bank, db, out, phys, first = _run(name)
-    seq, tok = _check(name, gold, wl, out, phys, first, 2e-2 if wl.act_split else 5e-2)
+    c_gpu = zo.estimate(zo.Plan.from_workload(model, wl, t=1), out["S"])
+    seq, tok = _check(name, gold, wl, out, phys, first, 2e-2 if wl.act_split else 5e-2, c_gpu)
     if name == "qwen3-8b-mixed":
         # co-serving: the foreground rows are bitwise identical without the probes
         import zeroth_order_fine_amd as zo
@@ -99,11 +109,15 @@ def test_full_size_against_oracle(name):
 @pytest.mark.parametrize("name", ["opt1.3b", "opt13b"])
 def test_full_size_two_term_activations(name):
     """The plain-bf16 workloads scored with two-term activations: every sequence within
-    1e-3 of the oracle (measured about 3e-5)."""
+    1e-3 of the oracle (measured about 3e-5), and c = (L+ - L-)/2eps within 1e-2
+    relative (with plain bf16 activations c at eps = 1e-3 is off by about 20 % at the
+    OPT-13B shape: the score difference is divided by 2 eps)."""
     need_gpu()
     import torch
+    import zeroth_order_fine_amd as zo
     gold, wl, batch, model, bank, db, out, phys, first = _run(name, split=True)
-    _check(name, gold, wl, out, phys, first, 1e-3)
+    c_gpu = zo.estimate(zo.Plan.from_workload(model, wl, t=1), out["S"])
+    _check(name, gold, wl, out, phys, first, 1e-3, c_gpu)
     del model, bank, db, out
     gc.collect()
     torch.cuda.empty_cache()
