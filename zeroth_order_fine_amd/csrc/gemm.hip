@@ -398,7 +398,20 @@ __device__ __forceinline__ void epilogue_rows(const GemmParams& p, floatx4_t (&a
                                               int wn, int lane, float* red) {
   const int rb = m0 + wm * WM + (lane & 15);
   const int cb = n0 + wn * WN + 4 * (lane >> 4);
-  if constexpr (EPI == EPI_LMHEAD) {
+  if constexpr (EPI == EPI_PARTIAL) {
+    // fp32 sums of this workgroup's K-slice (blockIdx.z), [M x N] per slice; N is a
+    // multiple of 16, so each lane's four columns are one aligned 16-byte store
+    float* out = p.partial + (int64_t)blockIdx.z * p.M * p.N;
+#pragma unroll
+    for (int i = 0; i < TM; ++i) {
+      const int r = rb + i * 16;
+      if (r >= p.M) continue;
+#pragma unroll
+      for (int j = 0; j < TN; ++j)
+        if (cb + j * 16 < p.N) *(floatx4_t*)(out + (int64_t)r * p.N + cb + j * 16) = acc[i][j];
+    }
+    return;
+  } else if constexpr (EPI == EPI_LMHEAD) {
     // per row and 256-column tile: max and sum of exp of the logits, and the label's
     // logit; logits never leave registers.  A row's 64 columns of a wave sit in the
     // four lanes l, l + 16, l + 32, l + 48; the NWN waves along N meet in LDS.
@@ -577,7 +590,12 @@ gemm_bf16_pipe_kernel(GemmParams p) {
   const int grp = (p.n_bounds > 0 && n0 >= p.bounds[0]) + (p.n_bounds > 1 && n0 >= p.bounds[1]) +
                   (p.n_bounds > 2 && n0 >= p.bounds[2]);
   const int a_side_off = grp * (p.as_stride ? p.as_stride : p.ks_tile);
-  const int nkb = p.K / BK, nk = nkb + p.ks_tile / BK;
+  int nkb = p.K / BK, nk = nkb + p.ks_tile / BK;
+  int kt_off = 0;                      // first K-step of this workgroup's K-slice
+  if constexpr (EPI == EPI_PARTIAL) {  // split-K (no side segment)
+    nkb = nk = nkb / p.ksplit;
+    kt_off = blockIdx.z * nkb;
+  }
   const int nkwa = p.kwa ? p.kwa / BK : (1 << 30), nkwb = p.kwb ? p.kwb / BK : (1 << 30);
   const int nkwas = p.kwas ? p.kwas / BK : (1 << 30);
   const __amdgpu_buffer_rsrc_t rA = raw_rsrc(p.A, (int64_t)p.M * p.lda * 2);
@@ -603,8 +621,9 @@ gemm_bf16_pipe_kernel(GemmParams p) {
     bf16_t* sA = sm + slot * ASZ;
     bf16_t* sB = sm + 2 * ASZ + slot * BSZ;
     if (s < nkb) {
-      const int ka = (s >= nkwa ? s - nkwa : s) * BK * 2;
-      const int kb = (s >= nkwb ? s - nkwb : s) * BK * 2;
+      const int sk = s + kt_off;
+      const int ka = (sk >= nkwa ? sk - nkwa : sk) * BK * 2;
+      const int kb = (sk >= nkwb ? sk - nkwb : sk) * BK * 2;
       static_for<0, IA>([&](auto i) {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             rA, (__attribute__((address_space(3))) void*)(sA + (wave * IA + i) * 8 * BK), 16, aoff[i], ka, 0, 0);
@@ -786,7 +805,8 @@ hipError_t launch_bf16_pipe(const GemmParams& p, hipStream_t s) {
     attr_set = true;
   }
   const int tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
-  hipLaunchKernelGGL((gemm_bf16_pipe_kernel<BM, BN, WM, WN, EPI>), dim3(tiles), dim3(NT), smem, s, p);
+  const int z = EPI == EPI_PARTIAL ? p.ksplit : 1;
+  hipLaunchKernelGGL((gemm_bf16_pipe_kernel<BM, BN, WM, WN, EPI>), dim3(tiles, 1, z), dim3(NT), smem, s, p);
   return hipGetLastError();
 }
 
@@ -874,9 +894,18 @@ hipError_t gemm_launch_bf16(const GemmParams& p, int cfg, hipStream_t s) {
     }
   }
   if (cfg == GEMM_CFG_NARROW) {
-    // many factor columns (high rank, several entries): the pipelined projection kernel
-    if (p.epi == EPI_TPROJ && p.N >= 512 && p.N % 16 == 0 && p.K % 64 == 0 && p.ksplit <= 1)
-      return launch_bf16_pipe<256, 256, 128, 64, EPI_TPROJ>(p, s);
+    // more than one 128-column tile of factor columns (high rank, several entries): the
+    // pipelined projection kernel; with K-slices, fp32 partial sums and the fixed-order
+    // reduction that applies the epilogue
+    if (p.epi == EPI_TPROJ && p.N > 128 && p.N % 16 == 0 && p.K % 64 == 0) {
+      if (p.ksplit <= 1) return launch_bf16_pipe<256, 256, 128, 64, EPI_TPROJ>(p, s);
+      if ((p.K / 64) % p.ksplit != 0) return hipErrorInvalidValue;
+      GemmParams q = p;
+      q.epi = EPI_PARTIAL;
+      hipError_t e = launch_bf16_pipe<256, 256, 128, 64, EPI_PARTIAL>(q, s);
+      if (e != hipSuccess) return e;
+      return launch_tproj_reduce(p, s);
+    }
     if (p.epi == EPI_TPROJ) {
       // N <= 32 (one kind block at rank <= 8 and few entries): a 128 x 32 tile, so the
       // factor rows are not re-read for absent columns

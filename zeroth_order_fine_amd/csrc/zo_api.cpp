@@ -470,7 +470,10 @@ struct WsPtrs {
 // K-split of the side-input projection: only for the narrow case (one column tile),
 // chosen from N and K alone so that a row's result never depends on the batch.
 int tproj_split(const zo_model_desc& d, int64_t n_cols, int64_t k) {
-  if (d.dtype != ZO_DTYPE_BF16 || n_cols == 0 || n_cols > 128) return 1;
+  if (d.dtype != ZO_DTYPE_BF16 || n_cols == 0) return 1;
+  // wide outputs (the pipelined kernel, 256 x 256 tiles): two K-slices, so that a few
+  // column tiles over the batch's row tiles still fill the CUs
+  if (n_cols > 128) return (k % 128 == 0 && k / 128 >= 8) ? 2 : 1;
   // the 128 x 32 tile (n_cols <= 32) has half as many row tiles as the 64 x 128 one
   int s = n_cols <= 32 ? 8 : 4;
   while (s > 1 && (k % (64 * s) != 0 || k / (64 * s) < 8)) s >>= 1;
