@@ -100,7 +100,8 @@ def test_small_models_with_bank_and_ragged_rows(cfg, split):
 def test_foreground_bitwise_invariance(n_prompts, len_lo):
     """Foreground rows are bitwise identical whether batched alone or alongside probes.
     "tile-switch": the mixed batch (about 16k rows) runs every projection in 256x256
-    tiles, the foreground batch alone (about 400 rows) in 128x128 tiles."""
+    tiles of 128x64 wave tiles, the foreground batch alone (about 400 rows) in 128x128
+    tiles of 64x64 wave tiles."""
     need_gpu()
     wl = workload(SMALL_QWEN_BF16, n_fg=3, n_prompts=n_prompts, len_lo=len_lo, dir_seeds=(1,))
     batch = inputs.make_batch(wl)

@@ -860,38 +860,34 @@ int gemm_cfg_bk(int cfg, bool bf16) {
 // side-input column granularity (a multiple of every consumer's K-step)
 int gemm_bk(bool bf16) { return bf16 ? BK_BF16 : BK_F32; }
 
-template <int BM, int BN>
+template <int BM, int BN, int WM, int WN>
 hipError_t launch_pipe_epi(const GemmParams& p, hipStream_t s) {
   switch (p.epi) {
-    case EPI_STORE: return launch_bf16_pipe<BM, BN, 128, 64, EPI_STORE>(p, s);
-    case EPI_GELU: return launch_bf16_pipe<BM, BN, 128, 64, EPI_GELU>(p, s);
-    case EPI_SWIGLU: return launch_bf16_pipe<BM, BN, 128, 64, EPI_SWIGLU>(p, s);
-    case EPI_RESID: return launch_bf16_pipe<BM, BN, 128, 64, EPI_RESID>(p, s);
+    case EPI_STORE: return launch_bf16_pipe<BM, BN, WM, WN, EPI_STORE>(p, s);
+    case EPI_GELU: return launch_bf16_pipe<BM, BN, WM, WN, EPI_GELU>(p, s);
+    case EPI_SWIGLU: return launch_bf16_pipe<BM, BN, WM, WN, EPI_SWIGLU>(p, s);
+    case EPI_RESID: return launch_bf16_pipe<BM, BN, WM, WN, EPI_RESID>(p, s);
     default: return hipErrorInvalidValue;
   }
 }
 
-// Workgroup tile of the projection kernel: 256x256 (8 waves), 128x256 (4) or 128x128
-// (2), all made of the same 128x64 wave tile with the same K loop, so every output
+// Workgroup tile of the projection kernel: 256x256 (eight 128x64 wave tiles) or 128x128
+// (four 64x64 wave tiles).  Every wave tile is a grid of 16x16 MFMA blocks fed with the
+// same operands in the same K order (32 per instruction, ascending), so every output
 // element is formed by the same MFMA sequence whichever tile holds it; the choice can
-// follow the batch without changing a row's result.  The 256x256 tile is the most
-// efficient per CU; measured on the projections of small batches, a smaller tile pays
-// off only when 256x256 tiles would occupy fewer than half of the 256 CUs.
+// follow the batch without changing a row's result (checked bit for bit).  The 256x256
+// tile is the most efficient per CU; measured on the projections of small batches, the
+// 128x128 tile pays off when 256x256 tiles would occupy fewer than half of the 256 CUs.
 int pipe_tile(const GemmParams& p) {
-  auto tiles = [&](int bm, int bn) { return (int64_t)((p.M + bm - 1) / bm) * ((p.N + bn - 1) / bn); };
-  if (tiles(256, 256) >= 128) return 0;
-  if (tiles(128, 256) >= 128) return 1;
-  return 2;
+  const int64_t t256 = (int64_t)((p.M + 255) / 256) * ((p.N + 255) / 256);
+  return t256 >= 128 ? 0 : 1;
 }
 
 hipError_t gemm_launch_bf16(const GemmParams& p, int cfg, hipStream_t s) {
   if (p.M <= 0 || p.N <= 0) return hipSuccess;
   if (cfg == GEMM_CFG_BIG) {
-    switch (pipe_tile(p)) {
-      case 0: return launch_pipe_epi<256, 256>(p, s);
-      case 1: return launch_pipe_epi<128, 256>(p, s);
-      default: return launch_pipe_epi<128, 128>(p, s);
-    }
+    if (pipe_tile(p) == 0) return launch_pipe_epi<256, 256, 128, 64>(p, s);
+    return launch_pipe_epi<128, 128, 64, 64>(p, s);
   }
   if (cfg == GEMM_CFG_NARROW) {
     // more than one 128-column tile of factor columns (high rank, several entries): the
