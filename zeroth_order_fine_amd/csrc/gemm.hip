@@ -539,8 +539,9 @@ __device__ __forceinline__ void epilogue_rows(const GemmParams& p, floatx4_t (&a
 // ------------------------------------------------------------------------------
 // bf16 MFMA kernel for the shared-weight projections.
 //
-// Workgroup tiles of 128 x 64 wave tiles (256 x 256: eight waves, two per SIMD), K
-// steps of 64 held in two LDS stages of (BM + BN) x 64 bf16.  Tiles are streamed
+// Workgroup tiles of WM x WN wave tiles (256 x 256 of 128 x 64: eight waves, two per
+// SIMD; 128 x 128 of 64 x 64 for small batches), K steps of 64 held in two LDS stages
+// of (BM + BN) x 64 bf16; with EPI_PARTIAL, blockIdx.z selects one of ksplit K-slices.  Tiles are streamed
 // global -> LDS by buffer loads straight into LDS (no register staging; a fixed
 // per-lane byte offset in a VGPR, the K position in the scalar offset): the loads of
 // stage k + 1 are issued right after the barrier that opens step k, so they run under
@@ -549,8 +550,8 @@ __device__ __forceinline__ void epilogue_rows(const GemmParams& p, floatx4_t (&a
 // Within a 1 KB block (8 rows x 64 k, 128-byte rows) lane L of a load writes row L/8,
 // 16-byte chunk L%8, which holds logical chunk (L%8) ^ swz8(row): the fragment reads
 // (16 rows, one logical chunk) then fall on distinct banks.  Each output element is
-// accumulated by the
-// same MFMA sequence (k ascending, 32 per instruction) for every tile shape.
+// accumulated by the same MFMA sequence (k ascending, 32 per instruction) for every
+// workgroup and wave tile shape.
 __device__ __forceinline__ int swz8(int r) { return (r ^ (r >> 3)) & 7; }
 
 // buffer resource over `bytes` bytes at `base` (raw addressing: offsets past the end read 0)
