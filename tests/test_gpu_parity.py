@@ -96,10 +96,10 @@ def test_small_models_with_bank_and_ragged_rows(cfg, split):
         first += len(ref)
 
 
-@pytest.mark.parametrize("n_prompts,len_lo", [(4, 5), (64, 100)], ids=["small-batch", "tile-switch"])
+@pytest.mark.parametrize("n_prompts,len_lo", [(4, 5), (72, 100)], ids=["small-batch", "tile-switch"])
 def test_foreground_bitwise_invariance(n_prompts, len_lo):
     """Foreground rows are bitwise identical whether batched alone or alongside probes.
-    "tile-switch": the mixed batch (about 16k rows) runs every projection in 256x256
+    "tile-switch": the mixed batch (about 18k rows) runs every projection in 256x256
     tiles of 128x64 wave tiles, the foreground batch alone (about 400 rows) in 128x128
     tiles of 64x64 wave tiles."""
     need_gpu()
@@ -119,6 +119,28 @@ def test_foreground_bitwise_invariance(n_prompts, len_lo):
     ta = mixed["tok_logp"].cpu().numpy()[:nt]
     tb = alone["tok_logp"].cpu().numpy()[:nt]
     assert np.array_equal(ta.view(np.uint32), tb.view(np.uint32))
+
+
+def test_probe_rows_bitwise_across_tile_shapes():
+    """A probe sequence's log-prob, side path included, is bitwise the same whether its
+    batch is large (more than 16k rows: every projection in 256x256 tiles of 128x64 wave
+    tiles) or small (two prompts: 128x128 tiles of 64x64 wave tiles)."""
+    need_gpu()
+    wl = workload(SMALL_QWEN_BF16, n_prompts=72, len_lo=100, dir_seeds=(1,))
+    batch = inputs.make_batch(wl)
+    g = GpuRun(wl)
+    g.update(0, np.array([0.9]), 1e-2)
+    big = g.score(1, batch)
+    small = g.score(1, batch.subset([0, 1]))
+    flush("rows: large batch %d, small batch %d" % (int(big["n_rows"]), int(small["n_rows"])))
+    # o-proj output (N = d = 512) in 256x256 tiles needs more than 63 row tiles
+    assert int(big["n_rows"]) > 63 * 256 and int(small["n_rows"]) < 4 * 256
+    n = batch.n_seq
+    a = big["seq_logp"].cpu().numpy()
+    b = small["seq_logp"].cpu().numpy()
+    # packing: candidate-major, prompts in input order
+    for ia, ib in ((0, 0), (1, 1), (n, 2), (n + 1, 3)):
+        assert a[ia:ia + 1].view(np.uint64)[0] == b[ib:ib + 1].view(np.uint64)[0], (ia, ib)
 
 
 def test_eps_zero_and_sign_swap_and_repeatability():
