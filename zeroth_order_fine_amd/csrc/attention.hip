@@ -20,7 +20,7 @@ constexpr int QB = 64;     // queries per workgroup
 constexpr int KB = 64;     // keys per LDS tile
 
 template <int HD>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(256, 4)   // four waves per SIMD: the kernel waits on loads
 attn_bf16_kernel(const bf16_t* __restrict__ qkv, int ld, bf16_t* __restrict__ out, int ld_out,
                  const int32_t* __restrict__ cu, const int32_t* __restrict__ work, int hq, int hkv, float scale_log2) {
   constexpr int KS = HD / 32;        // MFMA k-steps over the head dimension
