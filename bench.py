@@ -218,7 +218,7 @@ def main():
         copy_calibration()
         return
     if args.gpus != 1:
-        print("bench.py: this build runs on exactly one GPU (got --gpus %d); a multi-GPU run is not "
+        print("bench.py: the library scores on one GPU (got --gpus %d); a multi-GPU run is not "
               "provided" % args.gpus, file=sys.stderr)
         sys.exit(2)
 
