@@ -1,7 +1,8 @@
 """Pins of the oracle's random streams (oracle/philox_normal.c).
 
-* Philox4x32-10 block function against an independent installed
-  implementation (PyTorch's header-only engine), compiled and run here.
+* Philox4x32-10 block function against two independent installed
+  implementations (PyTorch's header-only engine and rocRAND's device/host
+  engine), each compiled and run here.
 * ln, sin and cos of the exact-operation spec against mpmath at 4 ulp.
 * Box-Muller output against the textbook formula evaluated in mpmath.
 * the Gaussian stream's moments, a KS test and pair independence.
@@ -67,6 +68,52 @@ def test_philox_matches_installed_engine(torch_philox_exe):
     ref = np.array([[int(x, 16) for x in line.split()] for line in out.strip().splitlines()], np.uint32)
     got = rng.philox_blocks(ctr, key)
     assert np.array_equal(got, ref)
+
+
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+
+
+@pytest.fixture(scope="module")
+def rocrand_philox_exe():
+    hipcc = shutil.which("hipcc") or os.path.join(ROCM, "bin", "hipcc")
+    hdr = os.path.join(ROCM, "include", "rocrand", "rocrand_philox4x32_10.h")
+    if not (os.path.exists(hipcc) and os.path.exists(hdr)):
+        pytest.skip("hipcc or the rocRAND headers missing")
+    d = tempfile.mkdtemp()
+    src = os.path.join(d, "r.cpp")
+    with open(src, "w") as f:
+        f.write("""
+#include <rocrand/rocrand_philox4x32_10.h>
+#include <cstdio>
+// the engine's ten-round block function (a protected member), reached through a subclass
+struct Probe : rocrand_device::philox4x32_10_engine {
+  uint4 block(uint4 c, uint2 k) { return this->ten_rounds(c, k); }
+};
+// stdin: lines "c0 c1 c2 c3 k0 k1" (hex); stdout: the block, one line each.
+int main() { unsigned c[4], k[2]; Probe p;
+  while (scanf("%x %x %x %x %x %x", &c[0], &c[1], &c[2], &c[3], &k[0], &k[1]) == 6) {
+    uint4 r = p.block(make_uint4(c[0], c[1], c[2], c[3]), make_uint2(k[0], k[1]));
+    printf("%08x %08x %08x %08x\\n", r.x, r.y, r.z, r.w); } }
+""")
+    exe = os.path.join(d, "r")
+    subprocess.check_call([hipcc, "-O1", "-std=c++17", "-x", "hip", "--cuda-host-only", src, "-o", exe],
+                          stderr=subprocess.DEVNULL)
+    return exe
+
+
+def test_philox_matches_rocrand(rocrand_philox_exe):
+    """The same comparison against rocRAND's engine (counter = 4 words, key = 2 words)."""
+    rs = np.random.default_rng(2)
+    n = 20000
+    ctr = rs.integers(0, 2**32, size=(n, 4), dtype=np.uint64).astype(np.uint32)
+    key = rs.integers(0, 2**32, size=(n, 2), dtype=np.uint64).astype(np.uint32)
+    ctr[:3] = [[0, 0, 0, 0], [0xFFFFFFFF] * 4, [7, 0, 0xFFFFFFFF, 1]]
+    key[:3] = [[0, 0], [0xFFFFFFFF] * 2, [0xFFFFFFFF, 0]]
+    inp = "\n".join(" ".join("%x" % v for v in list(c) + list(k)) for c, k in zip(ctr, key))
+    out = subprocess.run([rocrand_philox_exe], input=inp, capture_output=True, text=True, check=True).stdout
+    ref = np.array([[int(x, 16) for x in line.split()] for line in out.strip().splitlines()], np.uint32)
+    assert ref.shape == (n, 4)
+    assert np.array_equal(rng.philox_blocks(ctr, key), ref)
 
 
 def test_words_layout():
