@@ -615,9 +615,10 @@ gemm_bf16_pipe_kernel(GemmParams p) {
     const int blk = wave * IB + i;
     return min(n0 + blk * 8 + lrow, p.N - 1) * ld + (((lane & 7) ^ ((lrow ^ blk) & 7)) << 3);
   };
-  int aoff[IA], boff[IB];
-  static_for<0, IA>([&](auto i) { aoff[i] = a_elem(i, (int)p.lda) * 2; });
-  static_for<0, IB>([&](auto i) { boff[i] = b_elem(i, (int)p.ldb) * 2; });
+  // byte offsets: the host keeps every operand under 2^31 elements, so they fit 32 unsigned bits
+  uint32_t aoff[IA], boff[IB];
+  static_for<0, IA>([&](auto i) { aoff[i] = (uint32_t)a_elem(i, (int)p.lda) * 2u; });
+  static_for<0, IB>([&](auto i) { boff[i] = (uint32_t)b_elem(i, (int)p.ldb) * 2u; });
   auto issue = [&](int s, auto slot) {
     bf16_t* sA = sm + slot * ASZ;
     bf16_t* sB = sm + 2 * ASZ + slot * BSZ;
@@ -642,12 +643,12 @@ gemm_bf16_pipe_kernel(GemmParams p) {
       static_for<0, IA>([&](auto i) {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             rAs, (__attribute__((address_space(3))) void*)(sA + (wave * IA + i) * 8 * BK), 16,
-            a_elem(i, (int)p.ldas) * 2, ka, 0, 0);
+            (uint32_t)a_elem(i, (int)p.ldas) * 2u, ka, 0, 0);
       });
       static_for<0, IB>([&](auto i) {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             rBs, (__attribute__((address_space(3))) void*)(sB + (wave * IB + i) * 8 * BK), 16,
-            b_elem(i, (int)p.ldbs) * 2, kb, 0, 0);
+            (uint32_t)b_elem(i, (int)p.ldbs) * 2u, kb, 0, 0);
       });
     }
   };
