@@ -223,6 +223,26 @@ def test_projection_widths_not_multiple_of_tile(split):
     assert np.max(np.abs(tok - allref)) <= (5e-4 if split else 2e-2)
 
 
+@pytest.mark.parametrize("split", [False, True], ids=["bf16", "split"])
+def test_wide_side_projection_in_k_slices(split):
+    """r = 64 with four directions on o, fc1, fc2 of the d = 320, FFN 1280 model: every
+    side-input projection has 256 factor columns per kind and runs on the pipelined kernel;
+    the fc2 input (K = 1280, or 3840 as two-term products) is split into two K-slices with
+    the ordered reduction, the others run whole."""
+    need_gpu()
+    wl = workload(SMALL_OPT_ODD, targets=("o", "fc1", "fc2"), rank=64, dir_seeds=(0, 1, 2, 3), n_prompts=2,
+                  len_lo=20, len_hi=60, score_mode="all_next" if split else "last_label", scale_inv_sqrt_r=True,
+                  nu=1024, act_split=split)
+    batch = inputs.make_batch(wl)
+    g, o = GpuRun(wl), OracleRun(wl)
+    c = np.array([0.5, -0.25, 1.5, -2.0])
+    g.update(0, c, 2e-3)
+    o.update(0, c, 2e-3)
+    gs, os_ = g.score(1, batch), o.score(1, batch)
+    err = _seq_close(gs, os_, 5e-4 if split else 2e-2)
+    flush("wide side projection (split %s): max per-sequence err %.3g" % (split, err))
+
+
 def test_qkv_side_targets_off_tile_boundary_rejected():
     """q/k/v targets on a model whose q|k|v boundaries are not column-tile multiples:
     zo_score refuses with ZO_E_SHAPE instead of mixing kinds inside a tile."""
