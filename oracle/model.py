@@ -15,6 +15,12 @@ which is what conventional implementations do (arXiv abstract of
 "Inference-Native Zeroth-Order Optimization": candidate states created by
 mutating model weights vs. factorized side states).
 
+fp8 models (OPT only) are the quantized model: the layer linears hold e4m3
+weights (see oracle.params) and every activation a layer linear reads - the
+two LayerNorm outputs, the attention output and the GELU output - is rounded to
+e4m3 (oracle.params.e4m3_round, no scale) before the product; q, k, v, the
+residual stream, the final norm and the head stay as in bf16 models.
+
 The architecture facts (pre-LN, learned positions, tied head for OPT;
 RMSNorm, QK-norm, rotate-half RoPE, GQA, SwiGLU, untied head for Qwen3) are
 the public definitions of those families; the pages only name the families.
@@ -23,6 +29,8 @@ import math
 
 import numpy as np
 from scipy.special import erf
+
+from .params import e4m3_round
 
 
 def layer_norm(x, w, b, eps):
@@ -111,14 +119,15 @@ def layer_forward(cfg, Wl, h, side, dense):
     n = h.shape[0]
     hq, hkv, hd = cfg.n_heads, cfg.n_kv_heads, cfg.head_dim
     if cfg.arch == "opt":
-        a = layer_norm(h, Wl["ln1_w"], Wl["ln1_b"], cfg.norm_eps)
+        qa = e4m3_round if cfg.dtype == "fp8" else (lambda x: x)   # linear inputs of fp8 models
+        a = qa(layer_norm(h, Wl["ln1_w"], Wl["ln1_b"], cfg.norm_eps))
         q = linear(a, Wl["wq"], Wl["bq"], side("q"), dense).reshape(n, hq, hd)
         k = linear(a, Wl["wk"], Wl["bk"], side("k"), dense).reshape(n, hkv, hd)
         v = linear(a, Wl["wv"], Wl["bv"], side("v"), dense).reshape(n, hkv, hd)
-        o = causal_attention(q, k, v).reshape(n, hq * hd)
+        o = qa(causal_attention(q, k, v).reshape(n, hq * hd))
         h = h + linear(o, Wl["wo"], Wl["bo"], side("o"), dense)
-        a = layer_norm(h, Wl["ln2_w"], Wl["ln2_b"], cfg.norm_eps)
-        f = gelu(linear(a, Wl["w_fc1"], Wl["b_fc1"], side("fc1"), dense))
+        a = qa(layer_norm(h, Wl["ln2_w"], Wl["ln2_b"], cfg.norm_eps))
+        f = qa(gelu(linear(a, Wl["w_fc1"], Wl["b_fc1"], side("fc1"), dense)))
         h = h + linear(f, Wl["w_fc2"], Wl["b_fc2"], side("fc2"), dense)
         return h
     a = rms_norm(h, Wl["ln1_w"], cfg.norm_eps)

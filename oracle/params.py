@@ -8,7 +8,12 @@ seed and the tensor's tag, element index = row-major index:
   norm gains          : 1 + 0.02 * z
 computed in fp64, rounded to fp32 (round to nearest even), and for bf16
 models the matrices are then rounded fp32 -> bf16 (round to nearest even).
-Vectors (biases, norm gains) stay fp32.
+Vectors (biases, norm gains) stay fp32.  fp8 models (OPT only) keep the
+embedding matrices in bf16 and store every layer linear as OCP e4m3 codes of
+w * 2^11 (round to nearest even, saturating at 448): |0.02 z| < 0.14 for every
+stream value (u >= 2^-33 bounds |z| below 6.8), so the fixed power-of-two
+scale keeps the whole range below 448 and the stored value is exactly
+e4m3(w * 2^11) * 2^-11.
 
 Direction factors (pages: "Zeroth-Order Fine-Tuning Was an Inference Workload
 All Along", section "Why ZO Fine-Tuning Is Really Scoring" - LoZO samples
@@ -30,6 +35,21 @@ LN2_W, LN2_B, W_FC1, B_FC1, W_FC2, B_FC2, W_DOWN, QNORM_W, KNORM_W = range(10, 1
 W_GATE, W_UP = W_FC1, W_FC2
 
 SCALE = 0.02
+FP8_WEIGHT_EXP = 11          # fp8 models: layer linears stored as e4m3(w * 2^11)
+E4M3_MAX = 448.0
+
+
+def e4m3_round(x):
+    """Nearest OCP e4m3 value (1 sign, 4 exponent bits with bias 7, 3 mantissa bits,
+    subnormals down to 2^-9, largest finite 448), ties to even, saturating at +-448.
+    The quantum of |x| in binade [2^E, 2^(E+1)) is 2^(max(E, -6) - 3); dividing by a
+    power of two and rounding to an integer is exact in binary64."""
+    x = np.asarray(x, np.float64)
+    a = np.abs(x)
+    _, e = np.frexp(a)                       # a = m 2^e, m in [0.5, 1)
+    q = np.ldexp(1.0, np.maximum(e - 1, -6) - 3)
+    y = np.minimum(np.round(a / q) * q, E4M3_MAX)   # np.round: half to even
+    return np.where(x < 0, -y, y)
 
 
 def bf16_round(x32):
@@ -92,7 +112,9 @@ def make_tensor(cfg, seed, slot, pid, shape, init, rows=None):
     else:
         v = SCALE * z
     v32 = v.astype(np.float32)
-    if init == "matrix" and cfg.dtype == "bf16":
+    if init == "matrix" and cfg.dtype == "fp8" and slot >= 1:
+        return (e4m3_round(v32.astype(np.float64) * 2.0 ** FP8_WEIGHT_EXP) * 2.0 ** -FP8_WEIGHT_EXP).reshape(out_shape)
+    if init == "matrix" and cfg.dtype in ("bf16", "fp8"):
         v32 = bf16_round(v32)
     return v32.astype(np.float64).reshape(out_shape)
 

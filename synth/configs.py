@@ -26,7 +26,7 @@ class ModelCfg:
     d_ffn: int
     vocab: int
     max_pos: int
-    dtype: str           # "f32" or "bf16": storage and GEMM operand type of the matrices
+    dtype: str           # "f32", "bf16" or "fp8" (OPT: e4m3 layer linears and linear inputs)
     norm_eps: float
     rope_theta: float = 0.0
 

@@ -1,0 +1,80 @@
+"""Pins of the oracle's fp8 (OCP e4m3) model (oracle/params.py e4m3_round,
+oracle/model.py quantization points).
+
+* e4m3_round against PyTorch's float8_e4m3fn conversion (an independent
+  implementation of the same format, round to nearest even) on random values,
+  on every representable value and on every midpoint between neighbours;
+* saturation at +-448 (the format's largest finite value) beyond the range;
+* the fp8 weights are e4m3 values times 2^-11 and stay inside the range;
+* the factorized side state equals dense mutation of the (quantized) weights.
+"""
+import dataclasses
+
+import numpy as np
+import torch
+
+from oracle import params, zo
+from oracle.zo import Weights
+from synth import configs, inputs
+
+from .test_oracle_model import OPT_SMALL
+from .test_oracle_zo import _bank_after_updates, _small_wl
+
+OPT_FP8 = dataclasses.replace(OPT_SMALL, dtype="fp8")
+
+
+def _torch_e4m3(x):
+    return torch.from_numpy(np.asarray(x, np.float64)).to(torch.float8_e4m3fn).double().numpy()
+
+
+def _all_finite_values():
+    v = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn).double().numpy()
+    return np.unique(v[np.isfinite(v)])
+
+
+def test_e4m3_matches_library_on_random_values():
+    rs = np.random.default_rng(3)
+    x = np.concatenate([rs.standard_normal(200000) * s for s in (1e-3, 0.05, 1.0, 30.0, 200.0)])
+    x = x[np.abs(x) < 448]
+    assert np.array_equal(params.e4m3_round(x), _torch_e4m3(x))
+
+
+def test_e4m3_fixed_points_and_ties_to_even():
+    v = _all_finite_values()                      # 253 values (+0 and -0 merge)
+    assert len(v) == 253 and v.max() == 448.0 and v[v > 0].min() == 2.0 ** -9
+    assert np.array_equal(params.e4m3_round(v), v)
+    mids = (v[:-1] + v[1:]) / 2                   # exactly representable in binary64
+    got, ref = params.e4m3_round(mids), _torch_e4m3(mids)
+    assert np.array_equal(got, ref)
+    # each midpoint goes to the neighbour with an even mantissa (code bit 0 clear)
+    codes = torch.from_numpy(got).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
+    assert np.all((codes & 1) == 0)
+
+
+def test_e4m3_saturates():
+    assert np.array_equal(params.e4m3_round(np.array([1e4, -1e4, 464.0, -500.0])), [448.0, -448.0, 448.0, -448.0])
+    assert params.e4m3_round(np.array([2.0 ** -11]))[0] == 0.0      # below half the smallest subnormal
+
+
+def test_fp8_weights_are_scaled_e4m3_values():
+    W = Weights(OPT_FP8, 2, cache_layers=False)
+    Wl = W.get_layer(0)
+    for name in ("wq", "wk", "wv", "wo", "w_fc1", "w_fc2"):
+        s = Wl[name] * 2.0 ** params.FP8_WEIGHT_EXP
+        assert np.array_equal(params.e4m3_round(s), s) and np.abs(s).max() < 448
+        assert len(np.unique(s)) > 100
+    G = W.get_global()                             # embeddings stay bf16
+    t = G["tok_embed"].astype(np.float32)
+    assert np.array_equal(params.bf16_round(t), t)
+
+
+def test_fp8_factorized_equals_dense_mutation():
+    wl = _small_wl(OPT_FP8, configs.KIND_NAMES_OPT, dirs=(0, 5), n_fg=1)
+    bank = _bank_after_updates(OPT_FP8, wl)
+    batch = inputs.make_batch(wl)
+    W = Weights(OPT_FP8, wl.model_seed, cache_layers=True)
+    plan = zo.plan_from_workload(wl, 2)
+    a = zo.score(OPT_FP8, W, plan, bank, batch)
+    b = zo.score(OPT_FP8, W, plan, bank, batch, dense=True)
+    assert np.allclose(a["seq_logp"], b["seq_logp"], rtol=1e-12, atol=0)
+    assert np.ptp(a["S"]) > 0
