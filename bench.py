@@ -24,6 +24,7 @@ if ROOT not in sys.path:
 
 METRIC = "ZO probe scored tokens/sec + ZO steps/sec (OPT-13B shape, batch 64, 1 GPU)"
 PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 MFMA
 PEAK_F32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 
@@ -110,18 +111,21 @@ def hbm_bytes_per_step(cfg, wl, rows, scored, n_entries):
     a = 2 * (2 if split else 1)          # bytes per activation element fed to a bf16 GEMM
     d, f, L = cfg.d_model, cfg.d_ffn, cfg.n_layers
     nq, nkv = cfg.n_heads * cfg.head_dim, cfg.n_kv_heads * cfg.head_dim
-    w = 2 if cfg.dtype == "bf16" else 4
+    w = 4 if cfg.dtype == "f32" else 2   # embeddings, head, q|k|v (bf16 in fp8 models too)
+    if cfg.dtype == "f32":
+        a = 4
+    ai = 1 if cfg.dtype == "fp8" else a  # layer-linear inputs (e4m3 in fp8 models)
     r, q = wl.rank, wl.n_dirs
     used = (n_entries + q) * r
     out = {}
     # embedding (+ learned positions), two norms per layer, final norm, QK-norm + RoPE
     nb = rows * d * (w * (2 if cfg.arch == "opt" else 1) + 4)
-    nb += 2 * L * rows * d * (4 + a) + scored * d * (4 + a)
+    nb += 2 * L * rows * d * (4 + ai) + scored * d * (4 + a)
     if cfg.arch != "opt":
         nb += L * rows * (nq + nkv) * 2 * (4 if split else w)
     out["norm"] = nb
     qkv_b = 4 if split else w
-    out["attention"] = L * rows * ((nq + 2 * nkv) * qkv_b + nq * a)
+    out["attention"] = L * rows * ((nq + 2 * nkv) * qkv_b + nq * ai)
     side = 0
     prep = 0
     for kinds in group_kinds(cfg):
@@ -129,7 +133,7 @@ def hbm_bytes_per_step(cfg, wl, rows, scored, n_entries):
         if not tk:
             continue
         n_in = cfg.linear_shape(tk[0])[1]
-        side += rows * n_in * a + len(tk) * used * n_in * 2 * (3 if split else 1) + rows * len(tk) * used * a
+        side += rows * n_in * ai + len(tk) * used * n_in * 2 * (3 if split else 1) + rows * len(tk) * used * a
         for k in tk:
             n_out = cfg.linear_shape(k)[0]
             prep += used * (n_in + n_out) * 2 * (3 if split else 1) + n_entries * r * n_out * 4
@@ -288,7 +292,7 @@ def main():
     launches_per_step = n_base / args.steps
     avg_launch_ms = ms_base / max(n_base, 1)
     achieved = (flops_step / launches_per_step) / (avg_launch_ms / 1e3) / 1e12 if n_base else None
-    peak = PEAK_BF16_TFLOPS if cfg.dtype == "bf16" else PEAK_F32_TFLOPS
+    peak = {"bf16": PEAK_BF16_TFLOPS, "fp8": PEAK_FP8_TFLOPS}.get(cfg.dtype, PEAK_F32_TFLOPS)
     line = {
         "metric": METRIC,
         "value": round(value, 1),
@@ -309,8 +313,9 @@ def main():
         "steps_per_s": round(args.steps / elapsed, 4),
         "score_only_tokens_per_s": round(probe_tokens * args.steps / score_timed, 1),
         "score_share_of_step": round(score_timed / elapsed, 4),
-        "roofline": {"kernel": "gemm_base (shared-weight projections, bf16 MFMA)" if cfg.dtype == "bf16"
-                     else "gemm_base (fp32 VALU)",
+        "roofline": {"kernel": {"bf16": "gemm_base (shared-weight projections, bf16 MFMA)",
+                                "fp8": "gemm_base (shared-weight projections, e4m3 x e4m3 MFMA)"}.get(
+                                    cfg.dtype, "gemm_base (fp32 VALU)"),
                      "bound": "mfma", "achieved": round(achieved, 1) if achieved else None, "peak": peak,
                      "unit": "TFLOP/s", "frac": round(achieved / peak, 4) if achieved else None,
                      "traffic": measured_traffic(args.workload),

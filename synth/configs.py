@@ -86,6 +86,8 @@ TINY = ModelCfg("opt", 2, 128, 4, 4, 32, 512, 512, 2048, "f32", 1e-5)
 OPT_1_3B = ModelCfg("opt", 24, 2048, 32, 32, 64, 8192, 50272, 2048, "bf16", 1e-5)
 OPT_13B = ModelCfg("opt", 40, 5120, 40, 40, 128, 20480, 50272, 2048, "bf16", 1e-5)
 OPT_6_7B = ModelCfg("opt", 32, 4096, 32, 32, 128, 16384, 50272, 2048, "bf16", 1e-5)
+# the fp8-quantized OPT-13B (e4m3 layer linears and linear inputs, bf16 embeddings)
+OPT_13B_FP8 = ModelCfg("opt", 40, 5120, 40, 40, 128, 20480, 50272, 2048, "fp8", 1e-5)
 QWEN3_8B = ModelCfg("qwen3", 36, 4096, 32, 8, 128, 12288, 151936, 40960, "bf16", 1e-6, 1e6)
 
 _ALL_OPT = ("q", "k", "v", "o", "fc1", "fc2")
@@ -97,6 +99,7 @@ CONFIGS = {
     "opt13b": Workload("opt13b", OPT_13B, 64, 16, 128, "zipf", "last_label", 2, 1e-3, (0,), _ALL_OPT),
     # one GPU's share of the batch-64 step split data-parallel over 8 GPUs (8 prompts)
     "opt13b-share8": Workload("opt13b-share8", OPT_13B, 8, 16, 128, "zipf", "last_label", 2, 1e-3, (0,), _ALL_OPT),
+    "opt13b-fp8": Workload("opt13b-fp8", OPT_13B_FP8, 64, 16, 128, "zipf", "last_label", 2, 1e-3, (0,), _ALL_OPT),
     "opt6.7b-mezo": Workload("opt6.7b-mezo", OPT_6_7B, 32, 128, 128, "zipf", "all_next", 64, 1e-3,
                              (0, 1, 2, 3), _ALL_OPT, scale_inv_sqrt_r=True, act_split=True),
     "qwen3-8b-mixed": Workload("qwen3-8b-mixed", QWEN3_8B, 16, 32, 512, "zipf", "last_label", 4, 1e-3,

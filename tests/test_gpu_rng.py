@@ -7,7 +7,7 @@ import pytest
 from oracle import params, rng
 from synth import configs
 
-from .gpu_common import SMALL_QWEN_BF16, flush, need_gpu
+from .gpu_common import SMALL_OPT_FP8, SMALL_QWEN_BF16, flush, need_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -67,21 +67,28 @@ def test_direction_factors_bit_exact():
     model.close()
 
 
-@pytest.mark.parametrize("name", ["tiny", "qwen_small"])
+@pytest.mark.parametrize("name", ["tiny", "qwen_small", "opt_fp8"])
 def test_weight_init_bit_exact(name):
+    """fp8: every layer linear's e4m3 code equals the oracle's e4m3(w * 2^11) (decoded by
+    PyTorch's float8_e4m3fn), the embeddings are bf16 as in bf16 models."""
     need_gpu()
     import torch
     import zeroth_order_fine_amd as zo
-    cfg = configs.CONFIGS["tiny"].model if name == "tiny" else SMALL_QWEN_BF16
+    cfg = {"tiny": configs.CONFIGS["tiny"].model, "qwen_small": SMALL_QWEN_BF16, "opt_fp8": SMALL_OPT_FP8}[name]
     model = zo.Model(cfg)
     model.init_weights(7)
     torch.cuda.synchronize()
+    n_fp8 = 0
     for slot, plist in [(0, params.global_params(cfg))] + [(l + 1, params.layer_params(cfg))
                                                            for l in range(cfg.n_layers)]:
         for pid, pname, shape, init in plist:
             got = model.tensor(slot, pid).float().cpu().numpy().reshape(shape)
+            if model.locate(slot, pid)[3] == 2:
+                got = got * np.float32(2.0 ** -params.FP8_WEIGHT_EXP)
+                n_fp8 += 1
             ref = params.make_tensor(cfg, 7, slot, pid, shape, init).astype(np.float32)
             assert np.array_equal(got, ref), (slot, pname)
+    assert n_fp8 == (6 * cfg.n_layers if cfg.dtype == "fp8" else 0)   # q, k, v, o, fc1, fc2
     model.close()
 
 

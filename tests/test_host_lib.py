@@ -63,9 +63,10 @@ def test_weight_layout_sizes(zlib):
         d = api.model_desc(cfg)
         n = ctypes.c_size_t()
         assert zlib.zo_weights_size(ctypes.byref(d), ctypes.byref(n)) == 0
-        es = 2 if cfg.dtype == "bf16" else 4
+        es = {"bf16": 2, "fp8": 1}.get(cfg.dtype, 4)     # layer linears
+        eg = 4 if cfg.dtype == "f32" else 2                # embeddings / head (bf16 in fp8 models)
         from oracle import params
-        logical = sum(np.prod(s) * (es if k == "matrix" else 4) for _, _, s, k in params.global_params(cfg))
+        logical = sum(np.prod(s) * (eg if k == "matrix" else 4) for _, _, s, k in params.global_params(cfg))
         logical += cfg.n_layers * sum(np.prod(s) * (es if k == "matrix" else 4)
                                       for _, _, s, k in params.layer_params(cfg))
         assert logical <= n.value < logical + 256 * 40 * (cfg.n_layers + 1)

@@ -12,7 +12,7 @@ from . import _lib
 from ._lib import BatchDesc, ModelDesc, PlanDesc
 
 ARCH = {"opt": 0, "qwen3": 1}
-DTYPE = {"f32": 0, "bf16": 1}
+DTYPE = {"f32": 0, "bf16": 1, "fp8": 2}
 KINDS = {"opt": ("q", "k", "v", "o", "fc1", "fc2"), "qwen3": ("q", "k", "v", "o", "gate", "up", "down")}
 PLAN_SCALE_INV_SQRT_R, PLAN_ALLOW_ZERO_EPS, PLAN_ACT_SPLIT = 1, 2, 4
 EST_INV_RANK, EST_MEAN = 1, 2
@@ -99,10 +99,10 @@ class Model:
 
     def tensor(self, slot, param):
         """Logical tensor as a torch tensor (a view for plain layouts, a gathered copy for
-        the interleaved gate/up pack)."""
+        the interleaved gate/up pack).  fp8 layer linears come back as stored: e4m3 codes
+        (torch.float8_e4m3fn) of w * 2^11."""
         off, rows, cols, dt, lay = self.locate(slot, param)
-        tdt = torch.bfloat16 if dt == 1 else torch.float32
-        es = 2 if dt == 1 else 4
+        tdt, es = {0: (torch.float32, 4), 1: (torch.bfloat16, 2), 2: (torch.float8_e4m3fn, 1)}[dt]
         if lay == 0:
             return self.weights[off:off + rows * cols * es].view(tdt).view(rows, cols)
         packed = self.weights[off:off + 2 * rows * cols * es].view(tdt).view(2 * rows, cols)

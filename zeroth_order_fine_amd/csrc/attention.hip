@@ -13,15 +13,17 @@
 // the rescale needs no cross-lane traffic.  K and V^T tiles are staged in LDS.
 #include "common.h"
 #include <math.h>
+#include <type_traits>
 
 namespace {
 
 constexpr int QB = 64;     // queries per workgroup
 constexpr int KB = 64;     // keys per LDS tile
 
-template <int HD>
+// TO: output element type, bf16_t, or e4m3_t for the e4m3 input of an fp8 model's o-projection
+template <int HD, typename TO>
 __global__ void __launch_bounds__(256, 4)   // four waves per SIMD: the kernel waits on loads
-attn_bf16_kernel(const bf16_t* __restrict__ qkv, int ld, bf16_t* __restrict__ out, int ld_out,
+attn_bf16_kernel(const bf16_t* __restrict__ qkv, int ld, TO* __restrict__ out, int ld_out,
                  const int32_t* __restrict__ cu, const int32_t* __restrict__ work, int hq, int hkv, float scale_log2) {
   constexpr int KS = HD / 32;        // MFMA k-steps over the head dimension
   constexpr int HB = HD / 16;        // 16-wide blocks of the head dimension
@@ -152,12 +154,17 @@ attn_bf16_kernel(const bf16_t* __restrict__ qkv, int ld, bf16_t* __restrict__ ou
   lsum += __shfl_xor(lsum, 32, 64);
   if (qi < len) {
     const float inv = 1.0f / lsum;
-    bf16_t* orow = out + (int64_t)(base + qi) * ld_out + h * HD;
+    TO* orow = out + (int64_t)(base + qi) * ld_out + h * HD;
 #pragma unroll
     for (int hb = 0; hb < HB; ++hb) {
-      uint32_t w0 = (uint32_t)f32_to_bf16(acc[hb][0] * inv) | ((uint32_t)f32_to_bf16(acc[hb][1] * inv) << 16);
-      uint32_t w1 = (uint32_t)f32_to_bf16(acc[hb][2] * inv) | ((uint32_t)f32_to_bf16(acc[hb][3] * inv) << 16);
-      *(uint2*)(orow + hb * 16 + 4 * g) = make_uint2(w0, w1);
+      if constexpr (std::is_same<TO, e4m3_t>::value) {
+        *(uint32_t*)(orow + hb * 16 + 4 * g) =
+            f32x4_to_e4m3(acc[hb][0] * inv, acc[hb][1] * inv, acc[hb][2] * inv, acc[hb][3] * inv);
+      } else {
+        uint32_t w0 = (uint32_t)f32_to_bf16(acc[hb][0] * inv) | ((uint32_t)f32_to_bf16(acc[hb][1] * inv) << 16);
+        uint32_t w1 = (uint32_t)f32_to_bf16(acc[hb][2] * inv) | ((uint32_t)f32_to_bf16(acc[hb][3] * inv) << 16);
+        *(uint2*)(orow + hb * 16 + 4 * g) = make_uint2(w0, w1);
+      }
     }
   }
 }
@@ -384,21 +391,32 @@ __global__ void attn_f32_kernel(const float* __restrict__ qkv, int ld, float* __
 
 }  // namespace
 
+template <typename TO>
+hipError_t launch_attention_bf16_to(const bf16_t* qkv, int ld_qkv, TO* out, int ld_out, const int32_t* cu,
+                                    const int32_t* work, int n_work, int hq, int hkv, int hd, hipStream_t s) {
+  if (n_work <= 0) return hipSuccess;
+  const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)hd));
+  dim3 grid(n_work, hq);
+  switch (hd) {
+    case 32: hipLaunchKernelGGL((attn_bf16_kernel<32, TO>), grid, dim3(256), 0, s, qkv, ld_qkv, out, ld_out, cu, work, hq, hkv, scale_log2); break;
+    case 64: hipLaunchKernelGGL((attn_bf16_kernel<64, TO>), grid, dim3(256), 0, s, qkv, ld_qkv, out, ld_out, cu, work, hq, hkv, scale_log2); break;
+    case 128: hipLaunchKernelGGL((attn_bf16_kernel<128, TO>), grid, dim3(256), 0, s, qkv, ld_qkv, out, ld_out, cu, work, hq, hkv, scale_log2); break;
+    default: return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
 template <>
 hipError_t launch_attention<bf16_t>(const bf16_t* qkv, int ld_qkv, bf16_t* out, int ld_out, const int32_t* cu,
                                     int n_seq, const int32_t* work, int n_work, int hq, int hkv, int hd,
                                     hipStream_t s) {
   (void)n_seq;
-  if (n_work <= 0) return hipSuccess;
-  const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)hd));
-  dim3 grid(n_work, hq);
-  switch (hd) {
-    case 32: hipLaunchKernelGGL(attn_bf16_kernel<32>, grid, dim3(256), 0, s, qkv, ld_qkv, out, ld_out, cu, work, hq, hkv, scale_log2); break;
-    case 64: hipLaunchKernelGGL(attn_bf16_kernel<64>, grid, dim3(256), 0, s, qkv, ld_qkv, out, ld_out, cu, work, hq, hkv, scale_log2); break;
-    case 128: hipLaunchKernelGGL(attn_bf16_kernel<128>, grid, dim3(256), 0, s, qkv, ld_qkv, out, ld_out, cu, work, hq, hkv, scale_log2); break;
-    default: return hipErrorInvalidValue;
-  }
-  return hipGetLastError();
+  return launch_attention_bf16_to<bf16_t>(qkv, ld_qkv, out, ld_out, cu, work, n_work, hq, hkv, hd, s);
+}
+
+hipError_t launch_attention_e4m3(const bf16_t* qkv, int ld_qkv, e4m3_t* out, int ld_out, const int32_t* cu,
+                                 const int32_t* work, int n_work, int hq, int hkv, int hd, hipStream_t s) {
+  return launch_attention_bf16_to<e4m3_t>(qkv, ld_qkv, out, ld_out, cu, work, n_work, hq, hkv, hd, s);
 }
 
 template <>

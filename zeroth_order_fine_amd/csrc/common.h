@@ -34,6 +34,33 @@ template <typename T> __device__ inline T from_f32(float v);
 template <> __device__ inline float from_f32<float>(float v) { return v; }
 template <> __device__ inline bf16_t from_f32<bf16_t>(float v) { return f32_to_bf16(v); }
 
+// ---- OCP e4m3 (fp8 models) ----------------------------------------------------
+// e4m3: 1 sign bit, 4 exponent bits (bias 7), 3 mantissa bits, no infinities, largest
+// finite magnitude 448.  fp8 models store their layer linears as e4m3 codes of w * 2^11
+// and feed those linears e4m3 activations.
+typedef uint8_t e4m3_t;
+constexpr int ZO_FP8_WEIGHT_EXP = 11;
+// four fp32 values -> four e4m3 codes, packed little-endian (value 0 in the low byte):
+// round to nearest even (the hardware conversion), magnitudes clamped to 448 first,
+// so an overflow saturates instead of producing NaN
+__device__ inline uint32_t f32x4_to_e4m3(float a, float b, float c, float d) {
+  auto cl = [](float x) { return fminf(fmaxf(x, -448.0f), 448.0f); };
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(cl(a), cl(b), 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(cl(c), cl(d), w, true);
+  return (uint32_t)w;
+}
+// eight e4m3 codes (little-endian in two words) -> eight bf16 (exact: every e4m3 value
+// is a bf16 value)
+__device__ inline u32x4_t e4m3x8_to_bf16(uint2 v) {
+  typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_v;
+  const bf16x2_v p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)v.x, 1.0f, false);
+  const bf16x2_v p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)v.x, 1.0f, true);
+  const bf16x2_v p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)v.y, 1.0f, false);
+  const bf16x2_v p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((int)v.y, 1.0f, true);
+  return u32x4_t{__builtin_bit_cast(uint32_t, p0), __builtin_bit_cast(uint32_t, p1),
+                 __builtin_bit_cast(uint32_t, p2), __builtin_bit_cast(uint32_t, p3)};
+}
+
 // ---- GEMM -------------------------------------------------------------------
 // C[M x N] = A[M x K] . B[N x K]^T  (+ side: As[M x Ks] . Bs[N x Ks]^T), fused epilogue.
 enum GemmEpi {
@@ -91,6 +118,11 @@ struct GemmParams {
   // split-K (EPI_PARTIAL): K-slice z covers base K-steps [z*ksteps_per_split, ...)
   int ksplit;
   float* partial;             // [ksplit x M x N]
+  // fp8 models: a_e4m3 = A holds e4m3 codes; b_e4m3 = B holds e4m3 codes of w * 2^11
+  // (the projection kernel then runs the main segment as e4m3 x e4m3 MFMAs, takes the
+  // side segment's Bs pre-scaled by 2^11, multiplies the sums by 2^-11 before the
+  // epilogue, and writes GELU outputs as e4m3)
+  int a_e4m3, b_e4m3;
 };
 
 // Launch on `stream`; returns hipSuccess or the launch error.
@@ -109,7 +141,7 @@ struct NormalJob {     // one generated tensor (or factor) written in a given la
   int64_t ld;          // physical row pitch (elements)
   uint64_t seed; uint64_t tau; uint32_t tag;
   int32_t mode;        // see rng.hip
-  int32_t dtype;       // 0 f32, 1 bf16
+  int32_t dtype;       // 0 f32, 1 bf16, 2 e4m3 code of v * 2^11
   int32_t pad_;
   int64_t aux;         // mode specific
 };
@@ -128,7 +160,7 @@ struct SideJob {       // one side-path factor block of one target linear
   int32_t r;                      // rank
   int32_t col0;                   // first destination column (G/U: column offset in a Bs row)
   int32_t row_map;                // 0 plain, 1 = gate rows of a 16-interleaved pack, 2 = up rows
-  int32_t dtype;                  // 0 f32, 1 bf16
+  int32_t dtype;                  // 0 f32, 1 bf16, 2 bf16 of v * 2^11 (factor columns of fp8 models)
   int64_t split;                  // bf16 only: 0, or write hi | hi | lo copies `split` elements apart
 };
 hipError_t launch_side_jobs(const SideJob* jobs_dev, int n_jobs, int64_t max_items, hipStream_t s);
@@ -185,6 +217,9 @@ hipError_t launch_attention<float>(const float* qkv, int ld_qkv, float* out, int
                                    int n_seq, const int32_t* work, int n_work, int hq, int hkv, int hd,
                                    hipStream_t s);
 // fp32 q|k|v -> attention output as the two-term bf16 expansion (hi at column c, lo at c + lo_off)
+// bf16 q|k|v, output as e4m3 codes (fp8 models)
+hipError_t launch_attention_e4m3(const bf16_t* qkv, int ld_qkv, e4m3_t* out, int ld_out, const int32_t* cu,
+                                 const int32_t* work, int n_work, int hq, int hkv, int hd, hipStream_t s);
 hipError_t launch_attention_split(const float* qkv, int ld_qkv, bf16_t* out, int ld_out, int lo_off,
                                   const int32_t* cu, const int32_t* work, int n_work, int hq, int hkv, int hd,
                                   hipStream_t s);

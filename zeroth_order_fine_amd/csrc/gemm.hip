@@ -257,8 +257,9 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, floatx4_t (&acc)[T
 }
 
 // ------------------------------------------------------------------------------
-// bf16 MFMA kernel
-template <int BM, int BN, int WM, int WN, int EPI>
+// bf16 MFMA kernel.  A8: the main segment's A holds e4m3 codes, widened to bf16 (exactly)
+// between the global load and the LDS store.
+template <int BM, int BN, int WM, int WN, int EPI, bool A8>
 __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
 gemm_bf16_kernel(GemmParams p) {
   constexpr int NWM = BM / WM, NWN = BN / WN, NT = NWM * NWN * 64;
@@ -319,7 +320,12 @@ gemm_bf16_kernel(GemmParams p) {
     const int wa__ = side__ ? nkwas : nkwa, wb__ = side__ ? (1 << 30) : nkwb;     \
     const int ka__ = (kk__ >= wa__ ? kk__ - wa__ : kk__) * BK + ch * 8 + (side__ ? a_side_off : 0); \
     const int kb__ = (kk__ >= wb__ ? kk__ - wb__ : kk__) * BK + ch * 8;           \
-    static_for<0, CA>([&](auto i) { ra[i] = *(const u32x4_t*)(ga__ + (arow[i] * la__ + ka__)); }); \
+    if (A8 && !side__)                                                            \
+      static_for<0, CA>([&](auto i) {                                             \
+        ra[i] = e4m3x8_to_bf16(*(const uint2*)((const e4m3_t*)p.A + (arow[i] * la__ + ka__))); \
+      });                                                                         \
+    else                                                                          \
+      static_for<0, CA>([&](auto i) { ra[i] = *(const u32x4_t*)(ga__ + (arow[i] * la__ + ka__)); }); \
     static_for<0, CB>([&](auto i) { rb[i] = *(const u32x4_t*)(gb__ + (brow[i] * lb__ + kb__)); }); \
   } while (0)
 #define ZO_SSTORE(buf_)                                                           \
@@ -393,7 +399,12 @@ __device__ __forceinline__ void store_bf16x4(const GemmParams& p, bf16_t* o, flo
         make_uint2((uint32_t)lo[0] | ((uint32_t)lo[1] << 16), (uint32_t)lo[2] | ((uint32_t)lo[3] << 16));
 }
 
-template <int EPI, int TM, int TN, int BM, int BN, int WM, int WN>
+// four consecutive outputs as e4m3 codes (4 bytes)
+__device__ __forceinline__ void store_e4m3x4(e4m3_t* o, floatx4_t v) {
+  *(uint32_t*)o = f32x4_to_e4m3(v[0], v[1], v[2], v[3]);
+}
+
+template <int EPI, int TM, int TN, int BM, int BN, int WM, int WN, bool F8>
 __device__ __forceinline__ void epilogue_rows(const GemmParams& p, floatx4_t (&acc)[TM][TN], int m0, int n0, int wm,
                                               int wn, int lane, float* red) {
   const int rb = m0 + wm * WM + (lane & 15);
@@ -517,7 +528,9 @@ __device__ __forceinline__ void epilogue_rows(const GemmParams& p, floatx4_t (&a
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
         if (cb + j * 16 >= p.N) continue;
-        floatx4_t v = acc[i][j] + bias[j];
+        // e4m3 main segments sum in units of 2^-11 of the result (the weights hold w * 2^11)
+        constexpr float unit = F8 ? 1.0f / (float)(1 << ZO_FP8_WEIGHT_EXP) : 1.0f;
+        floatx4_t v = F8 ? acc[i][j] * unit + bias[j] : acc[i][j] + bias[j];
         if constexpr (EPI == EPI_RESID) {
           floatx4_t* hp = (floatx4_t*)(p.H + (int64_t)r * p.ldh + cb + j * 16);
           *hp = *hp + v;
@@ -525,6 +538,10 @@ __device__ __forceinline__ void epilogue_rows(const GemmParams& p, floatx4_t (&a
           if constexpr (EPI == EPI_GELU) {
 #pragma unroll
             for (int q = 0; q < 4; ++q) v[q] = gelu_fast(v[q]);
+            if constexpr (F8) {        // the input of the next e4m3 projection
+              store_e4m3x4((e4m3_t*)p.C + (int64_t)r * p.ldc + cb + j * 16, v);
+              continue;
+            }
           }
           if (EPI == EPI_STORE && p.c_f32)
             *(floatx4_t*)((float*)p.C + (int64_t)r * p.ldc + cb + j * 16) = v;
@@ -560,10 +577,11 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void* base, int
   return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)n, 0x00020000);
 }
 
-template <int BM, int BN, int WM, int WN, int EPI>
+template <int BM, int BN, int WM, int WN, int EPI, bool F8>
 __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
 gemm_bf16_pipe_kernel(GemmParams p) {
-  constexpr int BK = 64;
+  constexpr int BK = 64;                               // bf16 elements of a K-step (128 bytes a row)
+  constexpr int BKM = F8 ? 128 : 64;                   // main-segment elements of a K-step (128 bytes a row)
   constexpr int NWM = BM / WM, NWN = BN / WN, NW = NWM * NWN;
   constexpr int TM = WM / 16, TN = WN / 16;
   constexpr int ASZ = BM * BK, BSZ = BN * BK;          // elements of one stage of A / of B
@@ -591,41 +609,51 @@ gemm_bf16_pipe_kernel(GemmParams p) {
   const int grp = (p.n_bounds > 0 && n0 >= p.bounds[0]) + (p.n_bounds > 1 && n0 >= p.bounds[1]) +
                   (p.n_bounds > 2 && n0 >= p.bounds[2]);
   const int a_side_off = grp * (p.as_stride ? p.as_stride : p.ks_tile);
-  int nkb = p.K / BK, nk = nkb + p.ks_tile / BK;
+  int nkb = p.K / BKM, nk = nkb + p.ks_tile / BK;
   int kt_off = 0;                      // first K-step of this workgroup's K-slice
   if constexpr (EPI == EPI_PARTIAL) {  // split-K (no side segment)
     nkb = nk = nkb / p.ksplit;
     kt_off = blockIdx.z * nkb;
   }
-  const int nkwa = p.kwa ? p.kwa / BK : (1 << 30), nkwb = p.kwb ? p.kwb / BK : (1 << 30);
+  const int nkwa = p.kwa ? p.kwa / BKM : (1 << 30), nkwb = p.kwb ? p.kwb / BKM : (1 << 30);
   const int nkwas = p.kwas ? p.kwas / BK : (1 << 30);
-  const __amdgpu_buffer_rsrc_t rA = raw_rsrc(p.A, (int64_t)p.M * p.lda * 2);
-  const __amdgpu_buffer_rsrc_t rB = raw_rsrc(p.B, (int64_t)p.N * p.ldb * 2);
+  constexpr int ESZ = F8 ? 1 : 2;                      // main-segment bytes per element
+  const __amdgpu_buffer_rsrc_t rA = raw_rsrc(p.A, (int64_t)p.M * p.lda * ESZ);
+  const __amdgpu_buffer_rsrc_t rB = raw_rsrc(p.B, (int64_t)p.N * p.ldb * ESZ);
 
   // load i of this wave fills 1 KB block wave * I + i: tile row blk * 8 + lane / 8, the
   // lane's 16 bytes holding logical chunk (lane % 8) ^ swz8(row).  Byte offsets of the
   // row and chunk stay in VGPRs; the K position goes in the scalar offset.
   const int lrow = lane >> 3;
-  // element offset (row * ld + chunk) of load i, recomputed where needed rather than kept
-  auto a_elem = [&](int i, int ld) {
-    const int blk = wave * IA + i;
-    return min(m0 + blk * 8 + lrow, p.M - 1) * ld + (((lane & 7) ^ ((lrow ^ blk) & 7)) << 3);
-  };
-  auto b_elem = [&](int i, int ld) {
-    const int blk = wave * IB + i;
-    return min(n0 + blk * 8 + lrow, p.N - 1) * ld + (((lane & 7) ^ ((lrow ^ blk) & 7)) << 3);
-  };
-  // byte offsets: the host keeps every operand under 2^31 elements, so they fit 32 unsigned bits
+  // tile row and physical 16-byte chunk of load i; its element offset (row * ld +
+  // 8 * chunk for bf16) is recomputed where needed rather than kept
+  auto a_row = [&](int i) { return min(m0 + (wave * IA + i) * 8 + lrow, p.M - 1); };
+  auto b_row = [&](int i) { return min(n0 + (wave * IB + i) * 8 + lrow, p.N - 1); };
+  auto a_chk = [&](int i) { return (lane & 7) ^ ((lrow ^ (wave * IA + i)) & 7); };
+  auto b_chk = [&](int i) { return (lane & 7) ^ ((lrow ^ (wave * IB + i)) & 7); };
+  auto a_elem = [&](int i, int ld) { return a_row(i) * ld + (a_chk(i) << 3); };
+  auto b_elem = [&](int i, int ld) { return b_row(i) * ld + (b_chk(i) << 3); };
+  // byte offsets: the host keeps every operand under 2^31 elements, so they fit 32 unsigned
+  // bits (e4m3 operands: one byte an element, 16 elements a chunk)
   uint32_t aoff[IA], boff[IB];
-  static_for<0, IA>([&](auto i) { aoff[i] = (uint32_t)a_elem(i, (int)p.lda) * 2u; });
-  static_for<0, IB>([&](auto i) { boff[i] = (uint32_t)b_elem(i, (int)p.ldb) * 2u; });
+  if constexpr (F8) {
+    static_for<0, IA>([&](auto i) { aoff[i] = (uint32_t)(a_row(i) * (int)p.lda) + (uint32_t)(a_chk(i) << 4); });
+    static_for<0, IB>([&](auto i) { boff[i] = (uint32_t)(b_row(i) * (int)p.ldb) + (uint32_t)(b_chk(i) << 4); });
+  } else {
+    static_for<0, IA>([&](auto i) { aoff[i] = (uint32_t)a_elem(i, (int)p.lda) * 2u; });
+    static_for<0, IB>([&](auto i) { boff[i] = (uint32_t)b_elem(i, (int)p.ldb) * 2u; });
+  }
+  // K-step order: bf16 kernels run the main segment, then the side segment; the e4m3
+  // kernel runs its (bf16) side segment first, so that the side operands' offsets are dead
+  // before the main loop, which needs every register it has
+  const int nks = nk - nkb;                            // side-segment steps
   auto issue = [&](int s, auto slot) {
     bf16_t* sA = sm + slot * ASZ;
     bf16_t* sB = sm + 2 * ASZ + slot * BSZ;
-    if (s < nkb) {
-      const int sk = s + kt_off;
-      const int ka = (sk >= nkwa ? sk - nkwa : sk) * BK * 2;
-      const int kb = (sk >= nkwb ? sk - nkwb : sk) * BK * 2;
+    if (F8 ? s >= nks : s < nkb) {
+      const int sk = (F8 ? s - nks : s) + kt_off;
+      const int ka = (sk >= nkwa ? sk - nkwa : sk) * BKM * ESZ;
+      const int kb = (sk >= nkwb ? sk - nkwb : sk) * BKM * ESZ;
       static_for<0, IA>([&](auto i) {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             rA, (__attribute__((address_space(3))) void*)(sA + (wave * IA + i) * 8 * BK), 16, aoff[i], ka, 0, 0);
@@ -634,10 +662,10 @@ gemm_bf16_pipe_kernel(GemmParams p) {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             rB, (__attribute__((address_space(3))) void*)(sB + (wave * IB + i) * 8 * BK), 16, boff[i], kb, 0, 0);
       });
-    } else {                                  // side segment (the last few steps)
+    } else {                                  // side segment
       const __amdgpu_buffer_rsrc_t rAs = raw_rsrc(p.As, (int64_t)p.M * p.ldas * 2);
       const __amdgpu_buffer_rsrc_t rBs = raw_rsrc(p.Bs, (int64_t)p.N * p.ldbs * 2);
-      const int kk = s - nkb;
+      const int kk = F8 ? s : s - nkb;
       const int ka = ((kk >= nkwas ? kk - nkwas : kk) * BK + a_side_off) * 2;
       const int kb = kk * BK * 2;
       static_for<0, IA>([&](auto i) {
@@ -683,10 +711,7 @@ gemm_bf16_pipe_kernel(GemmParams p) {
     });
   };
   constexpr int MPR = (TM * TN) / (TM + TN);           // MFMAs per interleaved LDS read
-  auto step = [&](int kt, auto slot) {
-    // this wave's loads of stage kt have landed; after the barrier so have every
-    // wave's, and every read of the other stage (kt - 1) is retired
-    asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory");
+  auto step_bf16 = [&](int kt, auto slot) {
     if (kt + 1 < nk) issue(kt + 1, std::integral_constant<int, 1 - slot>{});
     rd(slot, std::integral_constant<int, 0>{});
     rd(slot, std::integral_constant<int, 1>{});
@@ -700,13 +725,86 @@ gemm_bf16_pipe_kernel(GemmParams p) {
     });
     __builtin_amdgcn_sched_group_barrier(0x008, 2 * TM * TN - MPR * (TM + TN), 0);
   };
+  // Steps of the e4m3 kernel.  Every fragment is 32 bytes a lane: row lr, logical 16-byte
+  // chunks lk and lk + 4 of the 128-byte row.  Main steps (128 e4m3 k): one
+  // v_mfma_f32_16x16x128_f8f6f4 per 16x16 block; A and B bytes at the same lane group and
+  // position meet in one product and the four lane groups cover the row's 128 elements
+  // once, so the instruction sums all 128 products.  Side steps (64 bf16 k): the two
+  // 16-byte halves are the two 32-deep bf16 fragments of the bf16 kernel (k ascending).
+  // Both read the same LDS addresses into the same registers.
+  typedef __attribute__((ext_vector_type(8))) int i32x8_t;
+  typedef __attribute__((ext_vector_type(4))) int i32x4_t;
+  auto step8 = [&](int kt, auto slot, auto side) {
+    if (kt + 1 < nk) issue(kt + 1, std::integral_constant<int, 1 - slot>{});
+    // chunk lk + 4 = chunk lk ^ 4, so its offset is the first one's with bit 5 flipped (row
+    // starts are multiples of 64 elements); only the first offsets stay in registers
+    i32x8_t ga[TM], gb[TN];
+    static_for<0, TN>([&](auto j) {
+      const i32x4_t x0 = *(const i32x4_t*)(sm + slot * BSZ + bro[0][j]);
+      const i32x4_t x1 = *(const i32x4_t*)(sm + slot * BSZ + (bro[0][j] ^ 32));
+      gb[j] = __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
+    });
+    static_for<0, TM>([&](auto i) {
+      const i32x4_t x0 = *(const i32x4_t*)(sm + slot * ASZ + aro[0][i]);
+      const i32x4_t x1 = *(const i32x4_t*)(sm + slot * ASZ + (aro[0][i] ^ 32));
+      ga[i] = __builtin_shufflevector(x0, x1, 0, 1, 2, 3, 4, 5, 6, 7);
+    });
+    static_for<0, TM>([&](auto i) {
+      static_for<0, TN>([&](auto j) {
+        if constexpr (decltype(side)::value) {
+          const i32x4_t bl = __builtin_shufflevector(gb[j], gb[j], 0, 1, 2, 3);
+          const i32x4_t bh = __builtin_shufflevector(gb[j], gb[j], 4, 5, 6, 7);
+          const i32x4_t al = __builtin_shufflevector(ga[i], ga[i], 0, 1, 2, 3);
+          const i32x4_t ah = __builtin_shufflevector(ga[i], ga[i], 4, 5, 6, 7);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, bl),
+                                                              __builtin_bit_cast(bf16x8_t, al), acc[i][j], 0, 0, 0);
+          acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, bh),
+                                                              __builtin_bit_cast(bf16x8_t, ah), acc[i][j], 0, 0, 0);
+        } else {
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(gb[j], ga[i], acc[i][j], 0, 0, 0, 0, 0, 0);
+        }
+      });
+    });
+    constexpr int PER = decltype(side)::value ? 2 : 1;                       // MFMAs per block
+    __builtin_amdgcn_sched_group_barrier(0x020, IA + IB, 0);                 // the loads
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * TN + 2, 0);              // B fragments and A fragment 0
+    static_for<0, TM - 1>([&](auto) {
+      __builtin_amdgcn_sched_group_barrier(0x008, PER * TN, 0);              // one row of blocks
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);                     // the next A fragment
+    });
+    __builtin_amdgcn_sched_group_barrier(0x008, PER * TN, 0);
+  };
+  // this wave's loads of stage kt have landed; after the barrier so have every wave's,
+  // and every read of the other stage (kt - 1) is retired
+  auto wait_stage = [&]() { asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory"); };
   if (nk > 0) issue(0, std::integral_constant<int, 0>{});
-  for (int kt = 0; kt < nk; kt += 2) {
-    step(kt, std::integral_constant<int, 0>{});
-    if (kt + 1 < nk) step(kt + 1, std::integral_constant<int, 1>{});
+  if constexpr (F8) {
+    // the bf16 side segment, then the e4m3 main segment, in separate loops (stage kt in
+    // slot kt & 1)
+    int kt = 0;
+    using S0 = std::integral_constant<int, 0>;
+    using S1 = std::integral_constant<int, 1>;
+    using SIDE = std::true_type;
+    using MAIN = std::false_type;
+    for (; kt < nks; ++kt) {
+      wait_stage();
+      if (kt & 1) step8(kt, S1{}, SIDE{});
+      else step8(kt, S0{}, SIDE{});
+    }
+    if ((kt & 1) && kt < nk) { wait_stage(); step8(kt, S1{}, MAIN{}); ++kt; }
+    for (; kt + 1 < nk; kt += 2) {
+      wait_stage(); step8(kt, S0{}, MAIN{});
+      wait_stage(); step8(kt + 1, S1{}, MAIN{});
+    }
+    if (kt < nk) { wait_stage(); step8(kt, S0{}, MAIN{}); }
+  } else {
+    for (int kt = 0; kt < nk; kt += 2) {
+      wait_stage(); step_bf16(kt, std::integral_constant<int, 0>{});
+      if (kt + 1 < nk) { wait_stage(); step_bf16(kt + 1, std::integral_constant<int, 1>{}); }
+    }
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no LDS write outlives the workgroup
-  epilogue_rows<EPI, TM, TN, BM, BN, WM, WN>(p, acc, m0, n0, wm, wn, lane, (float*)smem_raw);
+  epilogue_rows<EPI, TM, TN, BM, BN, WM, WN, F8>(p, acc, m0, n0, wm, wn, lane, (float*)smem_raw);
 }
 
 // ------------------------------------------------------------------------------
@@ -775,7 +873,7 @@ gemm_f32_kernel(GemmParams p) {
   epilogue<EPI, TM, TN, BM, BN, WM, WN, float>(p, acc, m0, n0, nt, wm, wn, lane, red);
 }
 
-template <int BM, int BN, int WM, int WN, int EPI>
+template <int BM, int BN, int WM, int WN, int EPI, bool A8 = false>
 hipError_t launch_bf16(const GemmParams& p, hipStream_t s) {
   constexpr int NT = (BM / WM) * (BN / WN) * 64;
   const size_t stage = (size_t)(BM + BN) * BK_BF16 * sizeof(bf16_t);
@@ -784,31 +882,31 @@ hipError_t launch_bf16(const GemmParams& p, hipStream_t s) {
   if (smem < red) smem = red;
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)gemm_bf16_kernel<BM, BN, WM, WN, EPI>,
+    hipError_t e = hipFuncSetAttribute((const void*)gemm_bf16_kernel<BM, BN, WM, WN, EPI, A8>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   const int tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
   const int z = EPI == EPI_PARTIAL ? p.ksplit : 1;
-  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, EPI>), dim3(tiles, 1, z), dim3(NT), smem, s, p);
+  hipLaunchKernelGGL((gemm_bf16_kernel<BM, BN, WM, WN, EPI, A8>), dim3(tiles, 1, z), dim3(NT), smem, s, p);
   return hipGetLastError();
 }
 
-template <int BM, int BN, int WM, int WN, int EPI>
+template <int BM, int BN, int WM, int WN, int EPI, bool F8 = false>
 hipError_t launch_bf16_pipe(const GemmParams& p, hipStream_t s) {
   constexpr int NT = (BM / WM) * (BN / WN) * 64;
   const size_t smem = (size_t)2 * (BM + BN) * 64 * sizeof(bf16_t);
   static bool attr_set = false;
   if (!attr_set) {
-    hipError_t e = hipFuncSetAttribute((const void*)gemm_bf16_pipe_kernel<BM, BN, WM, WN, EPI>,
+    hipError_t e = hipFuncSetAttribute((const void*)gemm_bf16_pipe_kernel<BM, BN, WM, WN, EPI, F8>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
     if (e != hipSuccess) return e;
     attr_set = true;
   }
   const int tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
   const int z = EPI == EPI_PARTIAL ? p.ksplit : 1;
-  hipLaunchKernelGGL((gemm_bf16_pipe_kernel<BM, BN, WM, WN, EPI>), dim3(tiles, 1, z), dim3(NT), smem, s, p);
+  hipLaunchKernelGGL((gemm_bf16_pipe_kernel<BM, BN, WM, WN, EPI, F8>), dim3(tiles, 1, z), dim3(NT), smem, s, p);
   return hipGetLastError();
 }
 
@@ -864,6 +962,17 @@ int gemm_bk(bool bf16) { return bf16 ? BK_BF16 : BK_F32; }
 
 template <int BM, int BN, int WM, int WN>
 hipError_t launch_pipe_epi(const GemmParams& p, hipStream_t s) {
+  if (p.a_e4m3 || p.b_e4m3) {
+    // e4m3 x e4m3 main segment (fp8 OPT layers: no SwiGLU, no two-term operands)
+    if (!(p.a_e4m3 && p.b_e4m3) || p.kwa || p.kwb || p.kwas || p.c_lo || p.c_f32 || p.K % 128 != 0)
+      return hipErrorInvalidValue;
+    switch (p.epi) {
+      case EPI_STORE: return launch_bf16_pipe<BM, BN, WM, WN, EPI_STORE, true>(p, s);
+      case EPI_GELU: return launch_bf16_pipe<BM, BN, WM, WN, EPI_GELU, true>(p, s);
+      case EPI_RESID: return launch_bf16_pipe<BM, BN, WM, WN, EPI_RESID, true>(p, s);
+      default: return hipErrorInvalidValue;
+    }
+  }
   switch (p.epi) {
     case EPI_STORE: return launch_bf16_pipe<BM, BN, WM, WN, EPI_STORE>(p, s);
     case EPI_GELU: return launch_bf16_pipe<BM, BN, WM, WN, EPI_GELU>(p, s);
@@ -892,6 +1001,21 @@ hipError_t gemm_launch_bf16(const GemmParams& p, int cfg, hipStream_t s) {
     return launch_pipe_epi<128, 128, 64, 64>(p, s);
   }
   if (cfg == GEMM_CFG_NARROW) {
+    if (p.b_e4m3 || (p.a_e4m3 && (p.epi != EPI_TPROJ || p.N > 128 || p.kwa))) return hipErrorInvalidValue;
+    if (p.a_e4m3) {
+      // e4m3 activations against the bf16 factor rows: the register-staged tiles, which
+      // widen A to bf16 (exactly) on its way to LDS
+      const bool thin = p.N <= 32;
+      if (p.ksplit <= 1)
+        return thin ? launch_bf16<128, 32, 32, 32, EPI_TPROJ, true>(p, s)
+                    : launch_bf16<64, 128, 32, 64, EPI_TPROJ, true>(p, s);
+      GemmParams q = p;
+      q.epi = EPI_PARTIAL;
+      hipError_t e = thin ? launch_bf16<128, 32, 32, 32, EPI_PARTIAL, true>(q, s)
+                          : launch_bf16<64, 128, 32, 64, EPI_PARTIAL, true>(q, s);
+      if (e != hipSuccess) return e;
+      return launch_tproj_reduce(p, s);
+    }
     // more than one 128-column tile of factor columns (high rank, several entries): the
     // pipelined projection kernel; with K-slices, fp32 partial sums and the fixed-order
     // reduction that applies the epilogue
@@ -923,6 +1047,7 @@ hipError_t gemm_launch_bf16(const GemmParams& p, int cfg, hipStream_t s) {
   // the vocabulary head: always 256-column tiles (the log-sum-exp partials, and so each
   // row's result, then do not depend on the batch); 128 or 256 rows per tile
   if (p.epi == EPI_LMHEAD) {
+    if (p.a_e4m3 || p.b_e4m3) return hipErrorInvalidValue;
     auto tiles = [&](int bm) { return (int64_t)((p.M + bm - 1) / bm) * ((p.N + 255) / 256); };
     if (tiles(256) >= 128) return launch_bf16_pipe<256, 256, 128, 64, EPI_LMHEAD>(p, s);
     return launch_bf16_pipe<128, 256, 128, 64, EPI_LMHEAD>(p, s);

@@ -79,6 +79,10 @@ __device__ __forceinline__ void store4<bf16_t>(bf16_t* o, floatx4_t y) {
   const uint32_t w1 = (uint32_t)f32_to_bf16(y[2]) | ((uint32_t)f32_to_bf16(y[3]) << 16);
   *(uint2*)o = make_uint2(w0, w1);
 }
+template <>
+__device__ __forceinline__ void store4<e4m3_t>(e4m3_t* o, floatx4_t y) {
+  *(uint32_t*)o = f32x4_to_e4m3(y[0], y[1], y[2], y[3]);
+}
 // two-term bf16 expansion: hi at o, lo at o + lo_off
 __device__ __forceinline__ void store4_split(bf16_t* o, int lo_off, floatx4_t y) {
   bf16_t hi[4], lo[4];
@@ -254,6 +258,8 @@ template hipError_t launch_norm<float>(const float*, const int32_t*, int, int, c
                                        bool, float*, int64_t, int, hipStream_t);
 template hipError_t launch_norm<bf16_t>(const float*, const int32_t*, int, int, const float*, const float*, float,
                                         bool, bf16_t*, int64_t, int, hipStream_t);
+template hipError_t launch_norm<e4m3_t>(const float*, const int32_t*, int, int, const float*, const float*, float,
+                                        bool, e4m3_t*, int64_t, int, hipStream_t);
 
 template <typename T>
 hipError_t launch_qknorm_rope(T* qkv, int M, int ld, int hq, int hkv, int hd, const float* qw, const float* kw,

@@ -155,8 +155,14 @@ __global__ void normal_jobs_kernel(const NormalJob* __restrict__ jobs, int64_t m
       int64_t row = e / jb.cols, col = e - row * jb.cols;
       int64_t prow = layout ? interleave16_row(row, layout) : row;
       int64_t off = prow * jb.ld + col;
-      if (jb.dtype == 1) ((bf16_t*)jb.dst)[off] = f32_to_bf16(f);
-      else ((float*)jb.dst)[off] = f;
+      if (jb.dtype == 1) {
+        ((bf16_t*)jb.dst)[off] = f32_to_bf16(f);
+      } else if (jb.dtype == 2) {         // e4m3 code of f * 2^11 (exact scaling, then one rounding)
+        const float x = f * (float)(1 << ZO_FP8_WEIGHT_EXP);
+        ((e4m3_t*)jb.dst)[off] = (e4m3_t)(f32x4_to_e4m3(x, 0.f, 0.f, 0.f) & 0xffu);
+      } else {
+        ((float*)jb.dst)[off] = f;
+      }
     }
   }
 }
@@ -182,9 +188,12 @@ __global__ void words_fill_kernel(uint64_t seed, uint32_t tag, uint64_t tau, int
   }
 }
 
-// fp32, bf16, or (split > 0, bf16) the copies hi | hi | lo at off, off + split, off + 2 split
+// fp32, bf16, or (split > 0, bf16) the copies hi | hi | lo at off, off + split, off + 2 split;
+// dtype 2: bf16 of v * 2^11 (exact scaling), the side factors of fp8 models' projections
 __device__ __forceinline__ void store_as(void* dst, int64_t off, float v, int dtype, int64_t split) {
-  if (dtype == 1) {
+  if (dtype == 2) {
+    ((bf16_t*)dst)[off] = f32_to_bf16(v * (float)(1 << ZO_FP8_WEIGHT_EXP));
+  } else if (dtype == 1) {
     bf16_t* o = (bf16_t*)dst + off;
     if (split > 0) {
       bf16_t hi, lo;

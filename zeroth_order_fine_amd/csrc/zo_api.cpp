@@ -109,6 +109,10 @@ struct Layout {
 };
 
 bool is_opt(const zo_model_desc& d) { return d.arch == ZO_ARCH_OPT; }
+// bf16 and fp8 models share the bf16 kernels (activations, attention, side path, head);
+// fp8 models differ only in their layer linears and those linears' inputs
+bool bf16_like(const zo_model_desc& d) { return d.dtype == ZO_DTYPE_BF16 || d.dtype == ZO_DTYPE_FP8; }
+bool is_fp8(const zo_model_desc& d) { return d.dtype == ZO_DTYPE_FP8; }
 int n_kinds_of(const zo_model_desc& d) { return is_opt(d) ? 6 : 7; }
 
 int validate_desc(const zo_model_desc* d) {
@@ -116,7 +120,8 @@ int validate_desc(const zo_model_desc* d) {
   ZO_CHECK(d->abi_version == ZO_ABI_VERSION, ZO_E_ABI, "descriptor ABI %d, library ABI %d", d->abi_version,
            ZO_ABI_VERSION);
   ZO_CHECK(d->arch == ZO_ARCH_OPT || d->arch == ZO_ARCH_QWEN3, ZO_E_INVAL, "unknown arch %d", d->arch);
-  ZO_CHECK(d->dtype == ZO_DTYPE_F32 || d->dtype == ZO_DTYPE_BF16, ZO_E_INVAL, "unknown dtype %d", d->dtype);
+  ZO_CHECK(d->dtype == ZO_DTYPE_F32 || d->dtype == ZO_DTYPE_BF16 || d->dtype == ZO_DTYPE_FP8, ZO_E_INVAL,
+           "unknown dtype %d", d->dtype);
   ZO_CHECK(d->n_layers >= 1 && d->d_model >= 1 && d->n_heads >= 1 && d->n_kv_heads >= 1 && d->head_dim >= 1 &&
                d->d_ffn >= 1 && d->vocab >= 2 && d->max_pos >= 1,
            ZO_E_INVAL, "model sizes must be positive");
@@ -131,14 +136,17 @@ int validate_desc(const zo_model_desc* d) {
   ZO_CHECK(is_opt(*d) || (std::isfinite(d->rope_theta) && d->rope_theta > 1.0), ZO_E_INVAL,
            "rope_theta must be > 1");
   ZO_CHECK(is_opt(*d) || d->d_ffn % 16 == 0, ZO_E_INVAL, "Qwen3 d_ffn must be a multiple of 16");
+  ZO_CHECK(d->dtype != ZO_DTYPE_FP8 || (is_opt(*d) && d->d_model % 128 == 0 && d->d_ffn % 128 == 0), ZO_E_INVAL,
+           "fp8 models: OPT only, d_model and d_ffn multiples of 128 (the e4m3 K-step)");
   return ZO_OK;
 }
 
 Layout make_layout(const zo_model_desc& d) {
   Layout Lo;
   size_t off = 0;
-  const int mdt = d.dtype;
-  auto esz = [](int dt) { return dt == ZO_DTYPE_BF16 ? (size_t)2 : (size_t)4; };
+  const int mdt = d.dtype;                                   // layer linears
+  const int gdt = d.dtype == ZO_DTYPE_FP8 ? ZO_DTYPE_BF16 : mdt;   // embeddings and head
+  auto esz = [](int dt) { return dt == ZO_DTYPE_FP8 ? (size_t)1 : dt == ZO_DTYPE_BF16 ? (size_t)2 : (size_t)4; };
   auto place = [&](TLoc& t, int64_t rows, int64_t cols, int dt, bool aligned, bool gain = false) {
     if (aligned) off = align_up(off, 256);
     t.present = true; t.off = off; t.rows = rows; t.cols = cols; t.dtype = dt; t.gain = gain;
@@ -146,11 +154,11 @@ Layout make_layout(const zo_model_desc& d) {
   };
   const int64_t D = d.d_model, V = d.vocab, F = d.d_ffn;
   const int64_t NQ = (int64_t)d.n_heads * d.head_dim, NKV = (int64_t)d.n_kv_heads * d.head_dim;
-  place(Lo.g[G_TOK], V, D, mdt, true);
-  if (is_opt(d)) place(Lo.g[G_POS], d.max_pos, D, mdt, true);
+  place(Lo.g[G_TOK], V, D, gdt, true);
+  if (is_opt(d)) place(Lo.g[G_POS], d.max_pos, D, gdt, true);
   place(Lo.g[G_FNW], 1, D, ZO_DTYPE_F32, true, true);
   if (is_opt(d)) place(Lo.g[G_FNB], 1, D, ZO_DTYPE_F32, true);
-  if (!is_opt(d)) place(Lo.g[G_HEAD], V, D, mdt, true);
+  if (!is_opt(d)) place(Lo.g[G_HEAD], V, D, gdt, true);
   Lo.L.resize(d.n_layers);
   for (int l = 0; l < d.n_layers; ++l) {
     auto& P = Lo.L[l];
@@ -410,7 +418,7 @@ int side_geometry(const zo_model* m, const zo_plan_s& p, const zo_bank* bank, Si
       if (bank->windows[s] >= 0) sg.entry_slots.push_back(s);
   }
   sg.E = (int)sg.entry_slots.size();
-  const int bk = gemm_bk(d.dtype == ZO_DTYPE_BF16);
+  const int bk = gemm_bk(bf16_like(d));
   sg.used = (sg.E + sg.q) * sg.r;
   sg.ks = (int)round_up(sg.used, bk);
   sg.nc = sg.E;
@@ -427,7 +435,7 @@ int side_geometry(const zo_model* m, const zo_plan_s& p, const zo_bank* bank, Si
   }
   // computed t columns per kind: an output width of the side-input projection (any
   // multiple of 32 serves), not a K extent like ks
-  sg.ks_c = (int)round_up(sg.nc * sg.r, d.dtype == ZO_DTYPE_BF16 ? 32 : bk);
+  sg.ks_c = (int)round_up(sg.nc * sg.r, bf16_like(d) ? 32 : bk);
   sg.groups = layer_groups(d);
   const int64_t D = d.d_model, F = d.d_ffn;
   const int64_t NQ = (int64_t)d.n_heads * d.head_dim, NKV = (int64_t)d.n_kv_heads * d.head_dim;
@@ -444,6 +452,9 @@ int side_geometry(const zo_model* m, const zo_plan_s& p, const zo_bank* bank, Si
     sg.bs_cols.push_back(on ? (sg.groups[g].interleaved ? (int64_t)nb * sg.ks : sg.ks) : 0);
     sg.bs_rows.push_back(nrows[g]);
     sg.n_in.push_back(nin[g]);
+    ZO_CHECK(!is_fp8(d) || sg.vt_rows[g] <= 128, ZO_E_SHAPE,
+             "fp8 models: side-input projection of %lld columns (rank x computed slots per kind, at most 128)",
+             (long long)sg.vt_rows[g]);
   }
   return ZO_OK;
 }
@@ -470,7 +481,7 @@ struct WsPtrs {
 // K-split of the side-input projection: only for the narrow case (one column tile),
 // chosen from N and K alone so that a row's result never depends on the batch.
 int tproj_split(const zo_model_desc& d, int64_t n_cols, int64_t k) {
-  if (d.dtype != ZO_DTYPE_BF16 || n_cols == 0) return 1;
+  if (!bf16_like(d) || n_cols == 0) return 1;
   // wide outputs (the pipelined kernel, 256 x 256 tiles): two K-slices, so that a few
   // column tiles over the batch's row tiles still fill the CUs
   if (n_cols > 128) return (k % 128 == 0 && k / 128 >= 8) ? 2 : 1;
@@ -480,7 +491,9 @@ int tproj_split(const zo_model_desc& d, int64_t n_cols, int64_t k) {
   return s;
 }
 
-size_t act_size(const zo_model_desc& d) { return d.dtype == ZO_DTYPE_BF16 ? 2 : 4; }
+// bytes per activation element (fp8 models: bf16 except the e4m3 linear inputs, which
+// take the same buffers at one byte an element)
+size_t act_size(const zo_model_desc& d) { return bf16_like(d) ? 2 : 4; }
 bool split_act(const zo_plan_s& p) { return (p.flags & ZO_PLAN_ACT_SPLIT) != 0; }
 // As columns per row: the widest group.  Every group writes, for a given row, the same
 // column offsets inside each ks-wide block, so one zero fill per call keeps the
@@ -551,7 +564,7 @@ void carve(const zo_model* m, const zo_plan_s& p, const Packing& pk, const SideG
       np = std::max(np, (int64_t)tproj_split(d, sg.vt_rows[g], sg.n_in[g] * x3) * sg.vt_rows[g]);
     w.tp_partial = b.take<float>(std::max<int64_t>(np * M, 1));
   }
-  const int bn_head = gemm_cfg_bn(GEMM_CFG_HEAD, d.dtype == ZO_DTYPE_BF16);
+  const int bn_head = gemm_cfg_bn(GEMM_CFG_HEAD, bf16_like(d));
   const int64_t n_vt = (d.vocab + bn_head - 1) / bn_head;
   w.part = b.take<float2>(S * n_vt);
   w.lab_logit = b.take<float>(S);
@@ -569,16 +582,17 @@ int check_i32(int64_t elems, const char* what) {
 int run_gemm(const zo_model_desc& d, const GemmParams& gp, int cfg, hipStream_t s) {
   ProfScope ps(cfg == GEMM_CFG_BIG ? ZO_PROF_GEMM_BASE : (cfg == GEMM_CFG_NARROW ? ZO_PROF_GEMM_SIDE : ZO_PROF_GEMM_HEAD),
                s);
-  if (d.dtype == ZO_DTYPE_BF16) {
+  if (bf16_like(d)) {
     const int bn = gemm_cfg_bn(cfg, true);
     for (int i = 0; i < gp.n_bounds; ++i)
       ZO_CHECK(gp.bounds[i] % bn == 0, ZO_E_SHAPE, "kind boundary %d not a multiple of the %d-column tile",
                gp.bounds[i], bn);
-    const int bk = gemm_cfg_bk(cfg, true);
+    const int bk = (gp.a_e4m3 && gp.b_e4m3) ? 128 : gemm_cfg_bk(cfg, true);
+    ZO_CHECK(gp.ks_tile % gemm_cfg_bk(cfg, true) == 0, ZO_E_SHAPE, "side K (%d) not a multiple of %d", gp.ks_tile,
+             gemm_cfg_bk(cfg, true));
     ZO_CHECK(cfg != GEMM_CFG_BIG || (gp.N % 16 == 0 && gp.ldc % 4 == 0 && gp.ldh % 4 == 0), ZO_E_SHAPE,
              "projection N must be a multiple of 16");
-    ZO_CHECK(gp.K % bk == 0 && gp.ks_tile % bk == 0, ZO_E_SHAPE, "K (%d) or side K (%d) not a multiple of %d", gp.K,
-             gp.ks_tile, bk);
+    ZO_CHECK(gp.K % bk == 0, ZO_E_SHAPE, "K (%d) not a multiple of %d", gp.K, bk);
     ZO_CHECK(gp.kwa % bk == 0 && gp.kwb % bk == 0 && gp.kwas % bk == 0 && (!gp.kwa || gp.K <= 2 * gp.kwa) &&
                  (!gp.kwb || gp.K <= 2 * gp.kwb) && (!gp.kwas || gp.ks_tile <= 2 * gp.kwas),
              ZO_E_SHAPE, "operand wrap does not fit the K extent");
@@ -610,7 +624,8 @@ template <typename T>
 int forward(zo_model* m, const zo_plan_s& p, const Packing& pk, const SideGeom& sg, const WsPtrs& w,
             const int32_t* tokens, hipStream_t s) {
   const zo_model_desc& d = m->d;
-  const bool bf = d.dtype == ZO_DTYPE_BF16;
+  const bool bf = bf16_like(d);
+  const bool f8 = is_fp8(d);
   const Layout& Lo = m->lo;
   auto W = [&](const TLoc& t) -> const void* { return t.present ? (const void*)(m->w + t.off) : nullptr; };
   auto Wf = [&](const TLoc& t) -> const float* { return (const float*)W(t); };
@@ -650,13 +665,21 @@ int forward(zo_model* m, const zo_plan_s& p, const Packing& pk, const SideGeom& 
     gp.tp_ks = sg.ks_c; gp.tp_rank = sg.r; gp.tp_entries = sg.E; gp.tp_used = sg.nc * sg.r; gp.tp_as_ks = sg.ks;
     gp.ksplit = tproj_split(d, sg.vt_rows[g], K * x3);
     gp.partial = w.tp_partial;
+    gp.a_e4m3 = f8;                        // fp8 models: every layer-linear input is e4m3
     return run_gemm(d, gp, narrow, s);
   };
   // projection over activations X [M x K] (or [hi | lo]) with the exact weight B [N x K]
+  // (fp8 models: e4m3 X and e4m3 codes of B * 2^11)
   auto proj = [&](const void* X, const void* B, int N, int K) {
     GemmParams gp = gemm_base(X, (int64_t)K * x2, B, K, M, N, K * x2);
     if (sp) gp.kwb = K;
+    gp.a_e4m3 = gp.b_e4m3 = f8;
     return gp;
+  };
+  // LayerNorm / RMSNorm of the residual stream into the input of the next linears
+  auto norm_in = [&](const float* nw, const float* nb) -> hipError_t {
+    if (f8) return launch_norm<e4m3_t>(w.h, nullptr, M, D, nw, nb, eps, rms, (e4m3_t*)w.xa, D, 0, s);
+    return launch_norm<T>(w.h, nullptr, M, D, nw, nb, eps, rms, (T*)w.xa, (int64_t)D * x2, sp ? D : 0, s);
   };
   auto with_side = [&](GemmParams& gp, int l, int g) {
     if (!sg.group_on[g]) return;
@@ -671,8 +694,7 @@ int forward(zo_model* m, const zo_plan_s& p, const Packing& pk, const SideGeom& 
     // attention block
     {
       ProfScope ps(ZO_PROF_NORM, s);
-      ZO_HIP(launch_norm<T>(w.h, nullptr, M, D, Wf(P[P_LN1W]), Wf(P[P_LN1B]), eps, rms, (T*)w.xa, (int64_t)D * x2,
-                            sp ? D : 0, s));
+      ZO_HIP(norm_in(Wf(P[P_LN1W]), Wf(P[P_LN1B])));
     }
     if ((rc = tproj(l, 0, w.xa, D)) != ZO_OK) return rc;
     {
@@ -696,6 +718,9 @@ int forward(zo_model* m, const zo_plan_s& p, const Packing& pk, const SideGeom& 
       if (sp)
         ZO_HIP(launch_attention_split((const float*)w.qkv, NQKV, (bf16_t*)w.attn, 2 * NQ, NQ, w.phys_cu, w.work,
                                       (int)pk.work.size(), d.n_heads, d.n_kv_heads, d.head_dim, s));
+      else if (f8)
+        ZO_HIP(launch_attention_e4m3((const bf16_t*)w.qkv, NQKV, (e4m3_t*)w.attn, NQ, w.phys_cu, w.work,
+                                     (int)pk.work.size(), d.n_heads, d.n_kv_heads, d.head_dim, s));
       else
         ZO_HIP(launch_attention<T>((const T*)w.qkv, NQKV, (T*)w.attn, NQ, w.phys_cu, pk.n_phys, w.work,
                                    (int)pk.work.size(), d.n_heads, d.n_kv_heads, d.head_dim, s));
@@ -710,8 +735,7 @@ int forward(zo_model* m, const zo_plan_s& p, const Packing& pk, const SideGeom& 
     // FFN block
     {
       ProfScope ps(ZO_PROF_NORM, s);
-      ZO_HIP(launch_norm<T>(w.h, nullptr, M, D, Wf(P[P_LN2W]), Wf(P[P_LN2B]), eps, rms, (T*)w.xa, (int64_t)D * x2,
-                            sp ? D : 0, s));
+      ZO_HIP(norm_in(Wf(P[P_LN2W]), Wf(P[P_LN2B])));
     }
     if ((rc = tproj(l, 2, w.xa, D)) != ZO_OK) return rc;
     {
@@ -844,7 +868,7 @@ int zo_init_weights(zo_model* m, uint64_t seed, void* stream) {
     j.rows = t.rows; j.cols = t.cols; j.ld = t.cols;
     j.seed = seed; j.tau = 0; j.tag = weight_tag(slot, param);
     j.mode = t.gain ? 1 : 0;
-    j.dtype = t.dtype == ZO_DTYPE_BF16 ? 1 : 0;
+    j.dtype = t.dtype == ZO_DTYPE_FP8 ? 2 : t.dtype == ZO_DTYPE_BF16 ? 1 : 0;
     j.aux = t.layout;
     jobs.push_back(j);
     max_blocks = std::max<int64_t>(max_blocks, (t.rows * t.cols + 3) / 4);
@@ -1003,7 +1027,7 @@ int zo_score(zo_model* m, const zo_plan_t* p, const zo_bank* bank, const zo_batc
   if (rc) return rc;
   hipStream_t s = (hipStream_t)stream;
   const zo_model_desc& d = m->d;
-  const bool bf = d.dtype == ZO_DTYPE_BF16;
+  const bool bf = bf16_like(d);
   Packing pk;
   build_packing(*p, *b, pk);
   SideGeom sg;
@@ -1090,7 +1114,8 @@ int zo_score(zo_model* m, const zo_plan_t* p, const zo_bank* bank, const zo_batc
             u.split = sp ? sg.bs_cols[g] : 0;
             u.col0 = (int32_t)(col_base + (int64_t)j * sg.r);
             u.row_map = row_map;
-            u.n = ksh.n_out; u.r = sg.r; u.dtype = dt;
+            u.n = ksh.n_out; u.r = sg.r;
+            u.dtype = is_fp8(d) ? 2 : dt;     // fp8 models: in the 2^11 units of the e4m3 weights
             if (entry) {
               size_t off;
               if ((rc = zo_bank_entry_offset(bank, sg.entry_slots[j], l, kind, &off)) != ZO_OK) return rc;
@@ -1113,7 +1138,7 @@ int zo_score(zo_model* m, const zo_plan_t* p, const zo_bank* bank, const zo_batc
   }
 
   // ---- forward, head, reduce
-  if (bf) rc = forward<bf16_t>(m, *p, pk, sg, w, b->tokens_dev, s);
+  if (bf) rc = forward<bf16_t>(m, *p, pk, sg, w, b->tokens_dev, s);   // bf16 and fp8 models
   else rc = forward<float>(m, *p, pk, sg, w, b->tokens_dev, s);
   if (rc != ZO_OK) return rc;
   double* seq_out = seq_logp_dev ? seq_logp_dev : w.seq_logp;
@@ -1230,6 +1255,8 @@ int zo_bank_fold(zo_model* m, zo_bank* bank, int32_t slot, void* ws_dev, size_t 
   ZO_CHECK(m && bank, ZO_E_INVAL, "null argument");
   ZO_CHECK(slot >= 0 && slot < bank->n_slots, ZO_E_INVAL, "slot %d out of range", slot);
   ZO_CHECK(bank->windows[slot] >= 0, ZO_E_STATE, "slot %d holds no entry", slot);
+  ZO_CHECK(m->d.dtype != ZO_DTYPE_FP8, ZO_E_STATE,
+           "fp8 models keep their e4m3 weights frozen: entries stay in the bank (no fold)");
   const zo_model_desc& bd = bank->md;
   ZO_CHECK(bd.arch == m->d.arch && bd.dtype == m->d.dtype && bd.n_layers == m->d.n_layers &&
                bd.d_model == m->d.d_model && bd.n_heads == m->d.n_heads && bd.n_kv_heads == m->d.n_kv_heads &&
