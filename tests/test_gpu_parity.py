@@ -408,7 +408,7 @@ def test_fp8_model_with_bank_matches_oracle():
     flush("S gpu %s oracle %s" % (S_g, S_o))
 
 
-def test_fp8_probe_rows_bitwise_across_tile_shapes():
+def test_fp8_probe_rows_bitwise_across_batch_sizes():
     """As for bf16 models: a probe sequence's log-prob is bitwise the same in a large batch
     (256x256 tiles) and a two-prompt batch (128x128 tiles)."""
     need_gpu()

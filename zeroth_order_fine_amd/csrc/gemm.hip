@@ -765,14 +765,16 @@ gemm_bf16_pipe_kernel(GemmParams p) {
         }
       });
     });
+    // A fragments ping-pong: the read of fragment i + 2 follows row i's MFMAs (whose
+    // registers it reuses), so fragment i + 1 is in flight while row i runs
     constexpr int PER = decltype(side)::value ? 2 : 1;                       // MFMAs per block
     __builtin_amdgcn_sched_group_barrier(0x020, IA + IB, 0);                 // the loads
-    __builtin_amdgcn_sched_group_barrier(0x100, 2 * TN + 2, 0);              // B fragments and A fragment 0
-    static_for<0, TM - 1>([&](auto) {
+    __builtin_amdgcn_sched_group_barrier(0x100, 2 * TN + 4, 0);              // B fragments, A fragments 0 and 1
+    static_for<0, TM - 2>([&](auto) {
       __builtin_amdgcn_sched_group_barrier(0x008, PER * TN, 0);              // one row of blocks
-      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);                     // the next A fragment
+      __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);                     // A fragment two rows on
     });
-    __builtin_amdgcn_sched_group_barrier(0x008, PER * TN, 0);
+    __builtin_amdgcn_sched_group_barrier(0x008, 2 * PER * TN, 0);
   };
   // this wave's loads of stage kt have landed; after the barrier so have every wave's,
   // and every read of the other stage (kt - 1) is retired
@@ -964,14 +966,17 @@ template <int BM, int BN, int WM, int WN>
 hipError_t launch_pipe_epi(const GemmParams& p, hipStream_t s) {
   if (p.a_e4m3 || p.b_e4m3) {
     // e4m3 x e4m3 main segment (fp8 OPT layers: no SwiGLU, no two-term operands)
-    if (!(p.a_e4m3 && p.b_e4m3) || p.kwa || p.kwb || p.kwas || p.c_lo || p.c_f32 || p.K % 128 != 0)
-      return hipErrorInvalidValue;
-    switch (p.epi) {
-      case EPI_STORE: return launch_bf16_pipe<BM, BN, WM, WN, EPI_STORE, true>(p, s);
-      case EPI_GELU: return launch_bf16_pipe<BM, BN, WM, WN, EPI_GELU, true>(p, s);
-      case EPI_RESID: return launch_bf16_pipe<BM, BN, WM, WN, EPI_RESID, true>(p, s);
-      default: return hipErrorInvalidValue;
+    if constexpr (BM == 128 && BN == 128) {
+      if (!(p.a_e4m3 && p.b_e4m3) || p.kwa || p.kwb || p.kwas || p.c_lo || p.c_f32 || p.K % 128 != 0)
+        return hipErrorInvalidValue;
+      switch (p.epi) {
+        case EPI_STORE: return launch_bf16_pipe<BM, BN, WM, WN, EPI_STORE, true>(p, s);
+        case EPI_GELU: return launch_bf16_pipe<BM, BN, WM, WN, EPI_GELU, true>(p, s);
+        case EPI_RESID: return launch_bf16_pipe<BM, BN, WM, WN, EPI_RESID, true>(p, s);
+        default: break;
+      }
     }
+    return hipErrorInvalidValue;
   }
   switch (p.epi) {
     case EPI_STORE: return launch_bf16_pipe<BM, BN, WM, WN, EPI_STORE>(p, s);
@@ -997,6 +1002,11 @@ int pipe_tile(const GemmParams& p) {
 hipError_t gemm_launch_bf16(const GemmParams& p, int cfg, hipStream_t s) {
   if (p.M <= 0 || p.N <= 0) return hipSuccess;
   if (cfg == GEMM_CFG_BIG) {
+    // e4m3 projections: always 128x128 tiles of four 64x64 wave tiles.  The 128x64 wave
+    // tile needs 128 accumulator registers next to 32-byte fragments, more than the 256 a
+    // lane has at two waves a SIMD (spills); the 128x128 tile streams the same bytes per
+    // product from L2 as the bf16 256x256 tile (half-size elements)
+    if (p.a_e4m3 || p.b_e4m3) return launch_pipe_epi<128, 128, 64, 64>(p, s);
     if (pipe_tile(p) == 0) return launch_pipe_epi<256, 256, 128, 64>(p, s);
     return launch_pipe_epi<128, 128, 64, 64>(p, s);
   }
