@@ -410,7 +410,7 @@ def test_fp8_model_with_bank_matches_oracle():
 
 def test_fp8_probe_rows_bitwise_across_batch_sizes():
     """As for bf16 models: a probe sequence's log-prob is bitwise the same in a large batch
-    (256x256 tiles) and a two-prompt batch (128x128 tiles)."""
+    (about 45k rows) and in a two-prompt batch."""
     need_gpu()
     wl = workload(SMALL_OPT_FP8, n_prompts=72, len_lo=100, dir_seeds=(1,))
     batch = inputs.make_batch(wl)
