@@ -78,3 +78,21 @@ def test_fp8_factorized_equals_dense_mutation():
     b = zo.score(OPT_FP8, W, plan, bank, batch, dense=True)
     assert np.allclose(a["seq_logp"], b["seq_logp"], rtol=1e-12, atol=0)
     assert np.ptp(a["S"]) > 0
+
+
+def test_activation_rounding_is_visible_at_the_gpu_bound():
+    """Rounding the four linear inputs to e4m3 moves the per-sequence sums of the GPU
+    test's model (d = 256, FFN 512, 2 layers, same workload shape) by far more than the
+    6e-2 fp8 parity bound: a kernel that skipped it would fail that test."""
+    import dataclasses as dc
+    from tests.gpu_common import SMALL_OPT_FP8, workload
+    cfg_fp8 = SMALL_OPT_FP8
+    cfg_noq = dc.replace(cfg_fp8, dtype="bf16")          # same weights, unrounded inputs
+    wl = workload(cfg_fp8, dir_seeds=(3, 8), n_fg=2, n_prompts=3)
+    batch = inputs.make_batch(wl)
+    W = Weights(cfg_fp8, wl.model_seed, cache_layers=True)
+    plan = zo.plan_from_workload(wl, 0)
+    a = zo.score(cfg_fp8, W, plan, None, batch)
+    b = zo.score(cfg_noq, W, plan, None, batch)
+    gap = np.abs(np.asarray(a["seq_logp"]) - np.asarray(b["seq_logp"]))
+    assert gap.max() > 2 * 6e-2, gap.max()          # measured: max 0.20, median 0.012
