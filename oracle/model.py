@@ -165,6 +165,33 @@ def final_logprobs(cfg, G, h, positions, labels, row_chunk=64):
     return out
 
 
+def final_logsoftmax(cfg, G, h, position):
+    """Log-softmax over the whole vocabulary at one row of one sequence (final norm, head)."""
+    x = h[position:position + 1]
+    if cfg.arch == "opt":
+        x = layer_norm(x, G["final_norm_w"], G["final_norm_b"], cfg.norm_eps)
+        head = G["tok_embed"]
+    else:
+        x = rms_norm(x, G["final_norm_w"], cfg.norm_eps)
+        head = G["lm_head"]
+    z = (x @ head.T)[0]
+    m = z.max()
+    return z - (m + np.log(np.sum(np.exp(z - m))))
+
+
+def forward_last_logsoftmax(cfg, get_global, get_layer, seqs):
+    """Full-vocabulary log-softmax at the last position of each sequence (dicts with
+    tokens and side, as for forward_logprobs)."""
+    G = get_global()
+    hs = [embed(cfg, G, s["tokens"]) for s in seqs]
+    for l in range(cfg.n_layers):
+        Wl = get_layer(l)
+        for i, s in enumerate(seqs):
+            hs[i] = layer_forward(cfg, Wl, hs[i], lambda kind, s=s, l=l: s["side"](l, kind), False)
+        del Wl
+    return [final_logsoftmax(cfg, G, hs[i], len(s["tokens"]) - 1) for i, s in enumerate(seqs)]
+
+
 def forward_logprobs(cfg, get_global, get_layer, seqs, dense=False):
     """Run a list of sequences through the model, layer by layer (so that only
     one layer's weights are resident).  Each seq is a dict with

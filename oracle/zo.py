@@ -216,6 +216,44 @@ def score(cfg, weights, plan, bank, batch, dense=False, phys_subset=None):
     return out
 
 
+def generate(cfg, weights, plan, bank, batch, n_new, forced=None):
+    """Greedy generation of n_new tokens for every physical sequence (the packing of
+    score): at each step the whole sequence so far (prompt + tokens chosen so far) is run
+    through the model at its candidate state again - no cache, the plain definition - and
+    the next token is the first vocabulary id holding the largest log-probability at the
+    last position ("Inference-Native Zeroth-Order Optimization", arXiv abstract:
+    candidate-state queries cover autoregressive generation).  forced (optional,
+    [n_phys x n_new] ids): continue with these tokens instead of the argmax, so that the
+    log-probabilities can be compared along another implementation's choices.
+    Returns dict(phys, tokens (the continuation used), logp (its tokens' log-probs),
+    best_tok and best_logp (the argmax and its log-prob at every step), S [n_cand])."""
+    from .model import forward_last_logsoftmax
+    plan.validate()
+    phys = pack(batch, plan)
+    n = len(phys)
+    toks = [list(np.asarray(batch.tokens[li], np.int64)) for li, c in phys]
+    out_tok = np.zeros((n, n_new), np.int64)
+    logp = np.zeros((n, n_new))
+    best_tok = np.zeros((n, n_new), np.int64)
+    best_lp = np.zeros((n, n_new))
+    sides = [side_terms(cfg, plan, bank, c) for li, c in phys]
+    for j in range(n_new):
+        seqs = [dict(tokens=np.asarray(toks[p], np.int64), side=sides[p]) for p in range(n)]
+        lsm = forward_last_logsoftmax(cfg, weights.get_global, weights.get_layer, seqs)
+        for p in range(n):
+            b = int(np.argmax(lsm[p]))                 # first index of the maximum
+            t = b if forced is None else int(forced[p][j])
+            best_tok[p, j], best_lp[p, j] = b, lsm[p][b]
+            out_tok[p, j], logp[p, j] = t, lsm[p][t]
+            toks[p].append(t)
+    S = np.zeros(len(plan.candidates))
+    for p, (li, c) in enumerate(phys):
+        if c >= 0:
+            for v in logp[p]:
+                S[c] += v
+    return dict(phys=phys, tokens=out_tok, logp=logp, best_tok=best_tok, best_logp=best_lp, S=S)
+
+
 def estimate(plan, S, flags=0, n_scored=None):
     """c_d = (L_{d,+} - L_{d,-}) / (2 eps) with L = -S (optionally / n_scored);
     divided by r when EST_INV_RANK is set (the estimator's explicit 1/r, which
