@@ -249,6 +249,34 @@ int zo_pack(const zo_plan_t* p, const zo_batch* b, int32_t* phys_seq, int32_t* p
 int zo_score(zo_model* m, const zo_plan_t* p, const zo_bank* bank, const zo_batch* b, void* ws_dev,
              size_t ws_bytes, double* seq_logp_dev, float* tok_logp_dev, double* S_host, void* stream);
 
+
+/* ---- generation queries --------------------------------------------------
+ * "Inference-Native Zeroth-Order Optimization" (arXiv abstract): the candidate-state
+ * formulation covers autoregressive generation as well as token scoring.  zo_generate
+ * runs greedy generation of n_new tokens for every physical sequence of the packing
+ * (foreground prompts under W, every probe prompt under every candidate state of the
+ * plan, side path and bank as in zo_score): one prefill pass over the prompts, which also
+ * fills a per-layer K/V cache in the workspace, then n_new - 1 decode steps of one row
+ * per sequence attending over the cache.  Token j of a sequence is the first vocabulary
+ * id holding the maximum logit at position len + j - 1 (fp32 logits).
+ *   tokens_dev: device int32 [n_phys x n_new] out, the generated ids;
+ *   logp_dev:   device fp32 [n_phys x n_new] out, each token's log-probability (computed
+ *               in fp64 from the head's partial sums, stored fp32);
+ *   S_host:     host fp64 [n_cand] out, per candidate the sum over its sequences of the
+ *               generated tokens' log-probabilities (the generative objective, for
+ *               zo_estimate).
+ * Sequences are in zo_pack's order.  fp32 and bf16 models; not with ZO_PLAN_ACT_SPLIT;
+ * prompt length + n_new - 1 <= max_pos.  The batch's score modes are validated but not
+ * used.  zo_generate_layout gives n_phys and the workspace bytes (the cache takes
+ * 2 x n_layers x (sum of prompt lengths + n_phys (n_new - 1)) x n_kv_heads x head_dim
+ * activation elements).  Errors as zo_score; ZO_E_INVAL for an fp8 model, a two-term
+ * plan or n_new < 1, ZO_E_SHAPE beyond max_pos. */
+int zo_generate_layout(const zo_model* m, const zo_plan_t* p, const zo_bank* bank, const zo_batch* b,
+                       int32_t n_new, int32_t* n_phys, size_t* ws_bytes);
+int zo_generate(zo_model* m, const zo_plan_t* p, const zo_bank* bank, const zo_batch* b, int32_t n_new,
+                void* ws_dev, size_t ws_bytes, int32_t* tokens_dev, float* logp_dev, double* S_host,
+                void* stream);
+
 /* ---- zo_estimate (host only, launches nothing) ------------------------------------
  * For each direction d with candidates (d,+1) and (d,-1):
  *   c_d = (L_{d,+} - L_{d,-}) / (2 eps),  L = -S  (or -S / n_scored with ZO_EST_MEAN)

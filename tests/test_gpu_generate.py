@@ -1,0 +1,74 @@
+"""GPU parity of zo_generate (greedy generation with the K/V cache) against the oracle's
+full-recompute greedy generation.
+
+Several continuations can be correct where two logits are closer than the arithmetic's
+error, so the comparison follows the GPU's own choices: the oracle re-runs every step
+along the GPU's tokens (teacher forcing) and checks that
+  * each GPU token is a valid greedy choice: its oracle log-prob is within CHOICE_TOL of
+    the oracle's maximum at that step (exactly the argmax unless two logits nearly tie);
+  * each GPU log-prob equals the oracle's for that token (fp32 models 1e-4 absolute,
+    bf16 models 2e-2, the per-token bound of scoring);
+  * the per-candidate sums S agree to the per-token bound times the tokens summed.
+"""
+import numpy as np
+import pytest
+
+from oracle import zo as ozo
+from synth import configs, inputs
+
+from .gpu_common import SMALL_OPT_BF16, SMALL_OPT_FP8, SMALL_QWEN_BF16, GpuRun, OracleRun, flush, need_gpu, workload
+
+pytestmark = pytest.mark.gpu
+
+TINY_F32 = configs.CONFIGS["tiny"].model
+
+
+@pytest.mark.parametrize("cfg", [TINY_F32, SMALL_OPT_BF16, SMALL_QWEN_BF16], ids=["tiny-f32", "opt-bf16", "qwen3-bf16"])
+def test_generation_matches_oracle(cfg):
+    """Two directions, a bank entry, a foreground prompt; prompts of 5..70 tokens and 12
+    new tokens, so the cached keys of the longer ones span two 64-key chunks."""
+    need_gpu()
+    wl = workload(cfg, dir_seeds=(3, 8), n_fg=1, n_prompts=2, len_lo=5, len_hi=70)
+    batch = inputs.make_batch(wl)
+    g, o = GpuRun(wl), OracleRun(wl)
+    c0 = np.array([0.9, -1.7])
+    g.update(0, c0, 5e-3)
+    o.update(0, c0, 5e-3)
+    n_new = 12
+    flush("generate %s" % cfg.arch)
+    out = g.zo.generate(g.model, g.plan(1), g.bank, g.zo.DeviceBatch(batch), n_new)
+    tok = out["tokens"].cpu().numpy()
+    lp = out["logp"].cpu().numpy()
+    ref = ozo.generate(cfg, o.W, ozo.plan_from_workload(wl, 1), o.bank, batch, n_new, forced=tok)
+    f32 = cfg.dtype == "f32"
+    lp_tol, choice_tol = (1e-4, 1e-4) if f32 else (2e-2, 2e-2)
+    gap = ref["best_logp"] - ref["logp"]
+    flush("max choice gap %.3g, max |dlogp| %.3g, exact argmax %d of %d" % (
+        gap.max(), np.abs(lp - ref["logp"]).max(), int((tok == ref["best_tok"]).sum()), tok.size))
+    assert np.all(gap <= choice_tol)
+    assert np.max(np.abs(lp - ref["logp"])) <= lp_tol
+    per_cand = sum(1 for li, c in ref["phys"] if c == 0) * n_new
+    assert np.all(np.abs(out["S"] - ref["S"]) <= lp_tol * per_cand)
+    assert np.mean(tok == ref["best_tok"]) >= 0.9
+
+
+def test_generation_rejections():
+    """fp8 models and two-term plans are refused (ZO_E_INVAL), and so is a continuation
+    past max_pos (ZO_E_SHAPE)."""
+    need_gpu()
+    import zeroth_order_fine_amd as zo
+    wl = workload(SMALL_OPT_FP8, n_prompts=2)
+    g = GpuRun(wl)
+    db = zo.DeviceBatch(inputs.make_batch(wl))
+    with pytest.raises(zo.ZoError) as ei:
+        zo.generate(g.model, g.plan(0), None, db, 4)
+    assert ei.value.code == -1
+    wl2 = workload(SMALL_OPT_BF16, n_prompts=2, len_lo=500, len_hi=510)
+    g2 = GpuRun(wl2)
+    db2 = zo.DeviceBatch(inputs.make_batch(wl2))
+    with pytest.raises(zo.ZoError) as ei:
+        zo.generate(g2.model, g2.plan(0, flags=zo.api.PLAN_ACT_SPLIT), None, db2, 4)
+    assert ei.value.code == -1
+    with pytest.raises(zo.ZoError) as ei:
+        zo.generate(g2.model, g2.plan(0), None, db2, 16)     # 510 + 15 > max_pos 512
+    assert ei.value.code == -2

@@ -49,6 +49,8 @@ _SIGS = {
     "zo_batch_layout": (c_i32, [c_vp, c_vp, c_vp, P(BatchDesc), P(c_i32), P(c_i64), P(c_i64), P(c_sz)]),
     "zo_pack": (c_i32, [c_vp, P(BatchDesc), P(c_i32), P(c_i32), P(c_i32)]),
     "zo_score": (c_i32, [c_vp, c_vp, c_vp, P(BatchDesc), c_vp, c_sz, c_vp, c_vp, P(c_dbl), c_vp]),
+    "zo_generate_layout": (c_i32, [c_vp, c_vp, c_vp, P(BatchDesc), c_i32, P(c_i32), P(c_sz)]),
+    "zo_generate": (c_i32, [c_vp, c_vp, c_vp, P(BatchDesc), c_i32, c_vp, c_sz, c_vp, c_vp, P(c_dbl), c_vp]),
     "zo_estimate": (c_i32, [c_vp, P(c_dbl), P(c_i64), c_u32, P(c_dbl)]),
     "zo_update": (c_i32, [c_vp, c_vp, c_vp, P(c_dbl), c_dbl, c_vp]),
     "zo_philox_words": (c_i32, [c_u64, c_u32, c_u64, c_i64, c_i64, c_vp, c_vp]),

@@ -240,6 +240,24 @@ def score(model, plan, bank, db, want_tokens=False):
                 n_phys=n_phys, n_rows=n_rows, n_scored=n_sc)
 
 
+def generate(model, plan, bank, db, n_new):
+    """Greedy generation of n_new tokens for every physical sequence (zo_pack order).
+    Returns dict(tokens torch int32 [n_phys, n_new], logp torch fp32 [n_phys, n_new],
+    S numpy fp64 [n_cand] = per-candidate sums of the generated tokens' log-probs)."""
+    n_phys, ws_bytes = ctypes.c_int32(), ctypes.c_size_t()
+    _check(model.L.zo_generate_layout(model.h, plan.h, bank.h if bank else None, ctypes.byref(db.desc), n_new,
+                                      ctypes.byref(n_phys), ctypes.byref(ws_bytes)))
+    ws = model.workspace(ws_bytes.value)
+    dev = model.weights.device
+    n = n_phys.value
+    tok = torch.empty((max(n, 1), n_new), dtype=torch.int32, device=dev)
+    lp = torch.empty((max(n, 1), n_new), dtype=torch.float32, device=dev)
+    S = (ctypes.c_double * len(plan.candidates))()
+    _check(model.L.zo_generate(model.h, plan.h, bank.h if bank else None, ctypes.byref(db.desc), n_new, _ptr(ws),
+                               ws.numel(), _ptr(tok), _ptr(lp), S, _stream()))
+    return dict(tokens=tok[:n], logp=lp[:n], S=np.array(list(S)), n_phys=n)
+
+
 def estimate(plan, S, flags=0, n_scored=None):
     L = plan.L
     q = len(plan.dir_seeds)

@@ -16,7 +16,7 @@ ROOT = os.path.dirname(HERE)
 CSRC = os.path.join(HERE, "csrc")
 OUT = os.path.join(HERE, "libzo.so")
 BUILD_DIR = os.path.join(HERE, "_build")
-SOURCES = ["rng.hip", "gemm.hip", "layers.hip", "attention.hip", "zo_api.cpp"]
+SOURCES = ["rng.hip", "gemm.hip", "layers.hip", "attention.hip", "decode.hip", "zo_api.cpp"]
 # microbenchmarks for the measured ceilings bench.py reports (a library of their own)
 PEAKS_SOURCE = "peaks.hip"
 PEAKS_OUT = os.path.join(HERE, "libzo_peaks.so")

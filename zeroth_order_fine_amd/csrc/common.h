@@ -115,6 +115,7 @@ struct GemmParams {
   float2* part;               // [M x n_ntiles]
   float* lab_logit;           // [M]
   int n_ntiles;
+  int32_t* part_idx;          // null, or [M x n_ntiles]: first column holding the tile's row maximum (greedy decoding)
   // split-K (EPI_PARTIAL): K-slice z covers base K-steps [z*ksteps_per_split, ...)
   int ksplit;
   float* partial;             // [ksplit x M x N]
@@ -220,6 +221,17 @@ hipError_t launch_attention<float>(const float* qkv, int ld_qkv, float* out, int
 // bf16 q|k|v, output as e4m3 codes (fp8 models)
 hipError_t launch_attention_e4m3(const bf16_t* qkv, int ld_qkv, e4m3_t* out, int ld_out, const int32_t* cu,
                                  const int32_t* work, int n_work, int hq, int hkv, int hd, hipStream_t s);
+// ---- generation (decode.hip) --------------------------------------------------
+template <typename T>
+hipError_t launch_kv_append(const T* qkv, int ld, int M, const int32_t* row_cache, int nq, int nkv, T* kc, T* vc,
+                            hipStream_t s);
+template <typename T>
+hipError_t launch_decode_attention(const T* qkv, int ld, const T* kc, const T* vc, const int32_t* kv_first,
+                                   const int32_t* row_pos, int M, int hq, int hkv, int hd, T* out, int ld_out,
+                                   hipStream_t s);
+hipError_t launch_greedy_reduce(const float2* part, const int32_t* part_idx, int n_tiles, int n_rows,
+                                int32_t* next_tok, int32_t* tokens_out, float* logp_out, int n_new, int step,
+                                hipStream_t s);
 hipError_t launch_attention_split(const float* qkv, int ld_qkv, bf16_t* out, int ld_out, int lo_off,
                                   const int32_t* cu, const int32_t* work, int n_work, int hq, int hkv, int hd,
                                   hipStream_t s);

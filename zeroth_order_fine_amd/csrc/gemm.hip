@@ -207,6 +207,7 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, floatx4_t (&acc)[T
     // red: [2][NWN][BM] floats
     float* rmax = red;
     float* rsum = red + NWN * BM;
+    int* ridx = (int*)(red + 2 * NWN * BM);
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
@@ -235,6 +236,15 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, floatx4_t (&acc)[T
 #pragma unroll
         for (int sh = 1; sh < 16; sh <<= 1) s += __shfl_xor(s, sh, 64);
         if ((lane & 15) == 0) rsum[wn * BM + rl] = s;
+        if (p.part_idx) {              // first column holding the row maximum
+          int ix = 0x7fffffff;
+#pragma unroll
+          for (int j = TN - 1; j >= 0; --j)
+            if (cbase + j * 16 < p.N && acc[i][j][q] == m) ix = cbase + j * 16;
+#pragma unroll
+          for (int sh = 1; sh < 16; sh <<= 1) ix = min(ix, __shfl_xor(ix, sh, 64));
+          if ((lane & 15) == 0) ridx[wn * BM + rl] = ix;
+        }
         const int r = m0 + rl;
         if (r < p.M) {
           const int lab = p.labels[r];
@@ -252,6 +262,11 @@ __device__ __forceinline__ void epilogue(const GemmParams& p, floatx4_t (&acc)[T
       for (int w = 1; w < NWN; ++w) m = fmaxf(m, rmax[w * BM + rl]);
       for (int w = 0; w < NWN; ++w) s += rsum[w * BM + rl];
       p.part[(int64_t)r * p.n_ntiles + nt] = make_float2(m, s);
+      if (p.part_idx) {
+        int ix = ridx[rl];
+        for (int w = 1; w < NWN; ++w) ix = min(ix, ridx[w * BM + rl]);
+        p.part_idx[(int64_t)r * p.n_ntiles + nt] = ix;
+      }
     }
   }
 }
@@ -429,6 +444,7 @@ __device__ __forceinline__ void epilogue_rows(const GemmParams& p, floatx4_t (&a
     constexpr int NWN = BN / WN;
     float* rmax = red;                 // [NWN][BM]
     float* rsum = red + NWN * BM;      // [NWN][BM]
+    int* ridx = (int*)(red + 2 * NWN * BM);   // [NWN][BM] (greedy decoding)
     __syncthreads();                   // every wave is past its last LDS read of the stages
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
@@ -458,6 +474,17 @@ __device__ __forceinline__ void epilogue_rows(const GemmParams& p, floatx4_t (&a
       sum += __shfl_xor(sum, 16, 64);
       sum += __shfl_xor(sum, 32, 64);
       if (lane < 16) rsum[wn * BM + rl] = sum;
+      if (p.part_idx) {                // first column holding the row maximum
+        int ix = 0x7fffffff;
+#pragma unroll
+        for (int j = TN - 1; j >= 0; --j)
+#pragma unroll
+          for (int q = 3; q >= 0; --q)
+            if (cb + j * 16 + q < p.N && acc[i][j][q] == m) ix = cb + j * 16 + q;
+        ix = min(ix, __shfl_xor(ix, 16, 64));
+        ix = min(ix, __shfl_xor(ix, 32, 64));
+        if (lane < 16) ridx[wn * BM + rl] = ix;
+      }
       const int r = m0 + rl;
       if (r < p.M) {
         const int lab = p.labels[r];
@@ -477,6 +504,11 @@ __device__ __forceinline__ void epilogue_rows(const GemmParams& p, floatx4_t (&a
       for (int w = 1; w < NWN; ++w) m = fmaxf(m, rmax[w * BM + rl]);
       for (int w = 0; w < NWN; ++w) sum += rsum[w * BM + rl];
       p.part[(int64_t)r * p.n_ntiles + nt] = make_float2(m, sum);
+      if (p.part_idx) {
+        int ix = ridx[rl];
+        for (int w = 1; w < NWN; ++w) ix = min(ix, ridx[w * BM + rl]);
+        p.part_idx[(int64_t)r * p.n_ntiles + nt] = ix;
+      }
     }
     return;
   } else if constexpr (EPI == EPI_TPROJ) {
@@ -819,7 +851,7 @@ gemm_f32_kernel(GemmParams p) {
   constexpr int BK = BK_F32;
   __shared__ float sA[BM][BK + 1];
   __shared__ float sB[BN][BK + 1];
-  __shared__ float red[2 * NWN * BM];
+  __shared__ float red[3 * NWN * BM];
   const int n_mt = (p.M + BM - 1) / BM, n_nt = (p.N + BN - 1) / BN;
   int logical;
   tile_swizzle(blockIdx.x, n_mt * n_nt, logical);
@@ -880,7 +912,7 @@ hipError_t launch_bf16(const GemmParams& p, hipStream_t s) {
   constexpr int NT = (BM / WM) * (BN / WN) * 64;
   const size_t stage = (size_t)(BM + BN) * BK_BF16 * sizeof(bf16_t);
   size_t smem = 2 * stage;
-  const size_t red = (size_t)2 * (BN / WN) * BM * sizeof(float);
+  const size_t red = (size_t)3 * (BN / WN) * BM * sizeof(float);
   if (smem < red) smem = red;
   static bool attr_set = false;
   if (!attr_set) {

@@ -18,6 +18,7 @@
 #include <cstring>
 #include <new>
 #include <string>
+#include <deque>
 #include <vector>
 
 namespace {
@@ -475,6 +476,11 @@ struct WsPtrs {
   float2* part;
   float* lab_logit;
   double *tok64, *seq_logp;
+  // generation only: per-layer K and V caches, cache row of every packed row, first cache
+  // row of every physical sequence, current tokens, first column of each tile's maximum
+  void *kcache = nullptr, *vcache = nullptr;
+  int64_t kv_layer_elems = 0;
+  int32_t *kv_first = nullptr, *row_cache = nullptr, *gen_tok = nullptr, *part_idx = nullptr;
   size_t bytes;
 };
 
@@ -514,7 +520,9 @@ int n_side_jobs(const zo_model_desc& d, const zo_plan_s& p, const SideGeom& sg) 
   return d.n_layers * kinds * per_kind;
 }
 
-void carve(const zo_model* m, const zo_plan_s& p, const Packing& pk, const SideGeom& sg, void* base, WsPtrs& w) {
+// kv_rows > 0: a generation call whose caches hold kv_rows rows per layer
+void carve(const zo_model* m, const zo_plan_s& p, const Packing& pk, const SideGeom& sg, void* base, WsPtrs& w,
+           int64_t kv_rows = 0) {
   const zo_model_desc& d = m->d;
   const size_t as = act_size(d);
   Bump b(base);
@@ -570,6 +578,15 @@ void carve(const zo_model* m, const zo_plan_s& p, const Packing& pk, const SideG
   w.lab_logit = b.take<float>(S);
   w.tok64 = b.take<double>(S);
   w.seq_logp = b.take<double>(std::max(pk.n_phys, 1));
+  if (kv_rows > 0) {
+    w.kv_first = b.take<int32_t>(pk.n_phys + 1);
+    w.row_cache = b.take<int32_t>(M);
+    w.gen_tok = b.take<int32_t>(std::max(pk.n_phys, 1));
+    w.part_idx = b.take<int32_t>(S * n_vt);
+    w.kv_layer_elems = kv_rows * NKV;
+    w.kcache = b.take<unsigned char>(d.n_layers * w.kv_layer_elems * as);
+    w.vcache = b.take<unsigned char>(d.n_layers * w.kv_layer_elems * as);
+  }
   w.bytes = align_up(b.off, 256);
 }
 
@@ -620,9 +637,16 @@ GemmParams gemm_base(const void* A, int64_t lda, const void* B, int64_t ldb, int
   return g;
 }
 
+// Generation calls: every packed row's k and v also go to the cache (row w.row_cache[r]);
+// decode steps (one row per physical sequence) attend over the cache instead of the packed
+// rows, and the head also records each tile's first maximum column.
+struct GenCtx {
+  bool decode;
+};
+
 template <typename T>
 int forward(zo_model* m, const zo_plan_s& p, const Packing& pk, const SideGeom& sg, const WsPtrs& w,
-            const int32_t* tokens, hipStream_t s) {
+            const int32_t* tokens, hipStream_t s, const GenCtx* gen = nullptr) {
   const zo_model_desc& d = m->d;
   const bool bf = bf16_like(d);
   const bool f8 = is_fp8(d);
@@ -715,7 +739,13 @@ int forward(zo_model* m, const zo_plan_s& p, const Packing& pk, const SideGeom& 
     }
     {
       ProfScope ps(ZO_PROF_ATTENTION, s);
-      if (sp)
+      T* kc = gen ? (T*)w.kcache + (int64_t)l * w.kv_layer_elems : nullptr;
+      T* vc = gen ? (T*)w.vcache + (int64_t)l * w.kv_layer_elems : nullptr;
+      if (gen) ZO_HIP(launch_kv_append<T>((const T*)w.qkv, NQKV, M, w.row_cache, NQ, NKV, kc, vc, s));
+      if (gen && gen->decode)
+        ZO_HIP(launch_decode_attention<T>((const T*)w.qkv, NQKV, kc, vc, w.kv_first, w.row_pos, M, d.n_heads,
+                                          d.n_kv_heads, d.head_dim, (T*)w.attn, NQ, s));
+      else if (sp)
         ZO_HIP(launch_attention_split((const float*)w.qkv, NQKV, (bf16_t*)w.attn, 2 * NQ, NQ, w.phys_cu, w.work,
                                       (int)pk.work.size(), d.n_heads, d.n_kv_heads, d.head_dim, s));
       else if (f8)
@@ -769,6 +799,7 @@ int forward(zo_model* m, const zo_plan_s& p, const Packing& pk, const SideGeom& 
     if (sp) gp.kwb = D;
     const int bn = gemm_cfg_bn(GEMM_CFG_HEAD, bf);
     gp.epi = EPI_LMHEAD; gp.labels = w.labels; gp.part = w.part; gp.lab_logit = w.lab_logit;
+    gp.part_idx = gen ? w.part_idx : nullptr;
     gp.n_ntiles = (d.vocab + bn - 1) / bn;
     if ((rc = run_gemm(d, gp, GEMM_CFG_HEAD, s)) != ZO_OK) return rc;
   }
@@ -1020,27 +1051,56 @@ int zo_pack(const zo_plan_t* p, const zo_batch* b, int32_t* phys_seq, int32_t* p
   return ZO_OK;
 }
 
-int zo_score(zo_model* m, const zo_plan_t* p, const zo_bank* bank, const zo_batch* b, void* ws_dev,
-             size_t ws_bytes, double* seq_logp_dev, float* tok_logp_dev, double* S_host, void* stream) {
-  ZO_CHECK(m && p && S_host, ZO_E_INVAL, "null argument");
+// Set-up shared by scoring and generation calls: packing, side geometry, workspace
+// carve, host tables to the device and the side factors.  gen_new > 0: a generation call
+// (scored rows = the last row of every physical sequence, KV caches in the workspace).
+static int64_t gen_kv_rows(const Packing& pk, int gen_new) {
+  int64_t n = 0;
+  for (int q = 0; q < pk.n_phys; ++q) n += (pk.phys_cu[q + 1] - pk.phys_cu[q]) + gen_new - 1;
+  return n;
+}
+
+static void gen_scored_rows(Packing& pk) {
+  pk.sc_row.clear();
+  pk.sc_lab_src.clear();
+  pk.phys_first.assign(1, 0);
+  for (int q = 0; q < pk.n_phys; ++q) {
+    pk.sc_row.push_back(pk.phys_cu[q + 1] - 1);
+    pk.sc_lab_src.push_back(0);          // labels are not used; any valid index
+    pk.phys_first.push_back(q + 1);
+  }
+  pk.n_scored = pk.n_phys;
+}
+
+// host copies that queued transfers read (kept by the caller until its stream synchronisation)
+struct HostKeep {
+  std::vector<int32_t> cdir, cslot;
+  std::vector<float> cscale;
+  std::vector<SideJob> jobs;
+  std::deque<std::vector<int32_t>> steps;   // a deque: references stay valid as it grows
+};
+
+static int prepare_call(zo_model* m, const zo_plan_t* p, const zo_bank* bank, const zo_batch* b, void* ws_dev,
+                        size_t ws_bytes, hipStream_t s, int gen_new, Packing& pk, SideGeom& sg, WsPtrs& w,
+                        HostKeep& keep) {
   int rc = validate_batch(m->d, b);
   if (rc) return rc;
-  hipStream_t s = (hipStream_t)stream;
   const zo_model_desc& d = m->d;
   const bool bf = bf16_like(d);
-  Packing pk;
   build_packing(*p, *b, pk);
-  SideGeom sg;
+  if (gen_new > 0) gen_scored_rows(pk);
   if ((rc = side_geometry(m, *p, bank, sg)) != ZO_OK) return rc;
-  WsPtrs w;
-  carve(m, *p, pk, sg, nullptr, w);
+  const int64_t kv_rows = gen_new > 0 ? gen_kv_rows(pk, gen_new) : 0;
+  carve(m, *p, pk, sg, nullptr, w, kv_rows);
   ZO_CHECK(ws_dev && ws_bytes >= w.bytes, ZO_E_SHAPE, "workspace has %zu bytes, needs %zu", ws_bytes, w.bytes);
-  carve(m, *p, pk, sg, ws_dev, w);
+  carve(m, *p, pk, sg, ws_dev, w, kv_rows);
   const int nc = (int)p->cdir.size();
 
   // ---- host tables -> device
-  std::vector<int32_t> cdir(p->cdir);
-  std::vector<float> cscale(nc);
+  std::vector<int32_t>& cdir = keep.cdir;
+  cdir = p->cdir;
+  std::vector<float>& cscale = keep.cscale;
+  cscale.assign(nc, 0.f);
   for (int c = 0; c < nc; ++c) cscale[c] = (float)((double)p->csign[c] * p->eps_tilde);
   auto h2d = [&](void* dst, const void* src, size_t n) -> hipError_t {
     if (n == 0) return hipSuccess;
@@ -1054,14 +1114,15 @@ int zo_score(zo_model* m, const zo_plan_t* p, const zo_bank* bank, const zo_batc
   ZO_HIP(h2d(w.sc_row, pk.sc_row.data(), pk.sc_row.size() * 4));
   ZO_HIP(h2d(w.sc_lab_src, pk.sc_lab_src.data(), pk.sc_lab_src.size() * 4));
   ZO_HIP(h2d(w.work, pk.work.data(), pk.work.size() * 4));
-  std::vector<int32_t> cslot(nc, -1);
+  std::vector<int32_t>& cslot = keep.cslot;
+  cslot.assign(nc, -1);
   for (int c = 0; c < nc && !sg.dslot.empty(); ++c) cslot[c] = sg.dslot[cdir[c]];
   ZO_HIP(h2d(w.cand_dir, cdir.data(), cdir.size() * 4));
   ZO_HIP(h2d(w.cand_slot, cslot.data(), cslot.size() * 4));
   ZO_HIP(h2d(w.cand_scale, cscale.data(), cscale.size() * 4));
 
   // ---- side factors: V^T rows for the input projections, [U | G] columns for the GEMMs
-  std::vector<SideJob> jobs;
+  std::vector<SideJob>& jobs = keep.jobs;
   int64_t max_items = 0;
   if (sg.any && pk.M > 0) {
     const uint64_t win = p->window();
@@ -1137,6 +1198,23 @@ int zo_score(zo_model* m, const zo_plan_t* p, const zo_bank* bank, const zo_batc
     ZO_HIP(launch_side_jobs(w.jobs, (int)jobs.size(), max_items, s));
   }
 
+  return ZO_OK;
+}
+
+int zo_score(zo_model* m, const zo_plan_t* p, const zo_bank* bank, const zo_batch* b, void* ws_dev,
+             size_t ws_bytes, double* seq_logp_dev, float* tok_logp_dev, double* S_host, void* stream) {
+  ZO_CHECK(m && p && S_host, ZO_E_INVAL, "null argument");
+  hipStream_t s = (hipStream_t)stream;
+  const zo_model_desc& d = m->d;
+  const bool bf = bf16_like(d);
+  Packing pk;
+  SideGeom sg;
+  WsPtrs w;
+  HostKeep keep;
+  int rc = prepare_call(m, p, bank, b, ws_dev, ws_bytes, s, 0, pk, sg, w, keep);
+  if (rc != ZO_OK) return rc;
+  const int nc = (int)p->cdir.size();
+
   // ---- forward, head, reduce
   if (bf) rc = forward<bf16_t>(m, *p, pk, sg, w, b->tokens_dev, s);   // bf16 and fp8 models
   else rc = forward<float>(m, *p, pk, sg, w, b->tokens_dev, s);
@@ -1155,6 +1233,121 @@ int zo_score(zo_model* m, const zo_plan_t* p, const zo_bank* bank, const zo_batc
   for (int c = 0; c < nc; ++c) S_host[c] = 0.0;
   for (int q = 0; q < pk.n_phys; ++q)
     if (pk.phys_cand[q] >= 0) S_host[pk.phys_cand[q]] += seq[q];
+  return ZO_OK;
+}
+
+static int check_generate(const zo_model* m, const zo_plan_t* p, const zo_batch* b, int32_t n_new) {
+  const zo_model_desc& d = m->d;
+  ZO_CHECK(d.dtype == ZO_DTYPE_F32 || d.dtype == ZO_DTYPE_BF16, ZO_E_INVAL,
+           "generation: fp32 and bf16 models (fp8 models score only)");
+  ZO_CHECK(!split_act(*p), ZO_E_INVAL, "generation: not with ZO_PLAN_ACT_SPLIT");
+  ZO_CHECK(n_new >= 1, ZO_E_INVAL, "n_new must be >= 1");
+  int rc = validate_batch(d, b);
+  if (rc) return rc;
+  for (int i = 0; i < b->n_seq; ++i) {
+    const int len = b->cu_seqlens[i + 1] - b->cu_seqlens[i];
+    ZO_CHECK((int64_t)len + n_new - 1 <= d.max_pos, ZO_E_SHAPE,
+             "sequence %d: %d prompt + %d generated tokens exceed max_pos %d", i, len, n_new, d.max_pos);
+  }
+  return ZO_OK;
+}
+
+int zo_generate_layout(const zo_model* m, const zo_plan_t* p, const zo_bank* bank, const zo_batch* b,
+                       int32_t n_new, int32_t* n_phys, size_t* ws_bytes) {
+  ZO_CHECK(m && p, ZO_E_INVAL, "null argument");
+  int rc = check_generate(m, p, b, n_new);
+  if (rc) return rc;
+  Packing pk;
+  build_packing(*p, *b, pk);
+  gen_scored_rows(pk);
+  SideGeom sg;
+  if ((rc = side_geometry(m, *p, bank, sg)) != ZO_OK) return rc;
+  WsPtrs w;
+  carve(m, *p, pk, sg, nullptr, w, gen_kv_rows(pk, n_new));
+  if (n_phys) *n_phys = pk.n_phys;
+  if (ws_bytes) *ws_bytes = w.bytes;
+  return ZO_OK;
+}
+
+int zo_generate(zo_model* m, const zo_plan_t* p, const zo_bank* bank, const zo_batch* b, int32_t n_new,
+                void* ws_dev, size_t ws_bytes, int32_t* tokens_dev, float* logp_dev, double* S_host, void* stream) {
+  ZO_CHECK(m && p && tokens_dev && logp_dev && S_host, ZO_E_INVAL, "null argument");
+  int rc = check_generate(m, p, b, n_new);
+  if (rc) return rc;
+  hipStream_t s = (hipStream_t)stream;
+  const zo_model_desc& d = m->d;
+  const bool bf = d.dtype == ZO_DTYPE_BF16;
+  Packing pk;
+  SideGeom sg;
+  WsPtrs w;
+  HostKeep keep;
+  if ((rc = prepare_call(m, p, bank, b, ws_dev, ws_bytes, s, n_new, pk, sg, w, keep)) != ZO_OK) return rc;
+  const int nc = (int)p->cdir.size(), nq = pk.n_phys;
+  if (nq == 0) {
+    for (int c = 0; c < nc; ++c) S_host[c] = 0.0;
+    return ZO_OK;
+  }
+  auto h2d = [&](void* dst, const std::vector<int32_t>& v) -> hipError_t {
+    return v.empty() ? hipSuccess : hipMemcpyAsync(dst, v.data(), v.size() * 4, hipMemcpyHostToDevice, s);
+  };
+  // cache rows: sequence q owns len_q + n_new - 1 rows (the last generated token is never fed back)
+  keep.steps.emplace_back(nq + 1, 0);
+  std::vector<int32_t>& kv_first = keep.steps.back();
+  for (int q = 0; q < nq; ++q) kv_first[q + 1] = kv_first[q] + (pk.phys_cu[q + 1] - pk.phys_cu[q]) + n_new - 1;
+  keep.steps.emplace_back(pk.M, 0);
+  std::vector<int32_t>& row_cache = keep.steps.back();
+  for (int q = 0; q < nq; ++q)
+    for (int r = pk.phys_cu[q]; r < pk.phys_cu[q + 1]; ++r) row_cache[r] = kv_first[q] + (r - pk.phys_cu[q]);
+  ZO_HIP(h2d(w.kv_first, kv_first));
+  ZO_HIP(h2d(w.row_cache, row_cache));
+  const int bn = gemm_cfg_bn(GEMM_CFG_HEAD, bf);
+  const int n_tiles = (d.vocab + bn - 1) / bn;
+  // prefill: the prompts (the first token comes from each prompt's last row)
+  const GenCtx prefill{false}, decode{true};
+  rc = bf ? forward<bf16_t>(m, *p, pk, sg, w, b->tokens_dev, s, &prefill)
+          : forward<float>(m, *p, pk, sg, w, b->tokens_dev, s, &prefill);
+  if (rc != ZO_OK) return rc;
+  ZO_HIP(launch_greedy_reduce(w.part, w.part_idx, n_tiles, nq, w.gen_tok, tokens_dev, logp_dev, n_new, 0, s));
+  // decode steps: one row per physical sequence, token j - 1 at position len + j - 1
+  Packing pd;
+  pd.n_phys = nq;
+  pd.M = nq;
+  pd.n_scored = nq;
+  pd.phys_cand = pk.phys_cand;
+  pd.phys_seq = pk.phys_seq;
+  for (int j = 1; j < n_new; ++j) {
+    keep.steps.emplace_back(nq);
+    std::vector<int32_t>& ident = keep.steps.back();
+    keep.steps.emplace_back(nq);
+    std::vector<int32_t>& pos = keep.steps.back();
+    keep.steps.emplace_back(nq);
+    std::vector<int32_t>& cache = keep.steps.back();
+    keep.steps.emplace_back(nq, 0);
+    std::vector<int32_t>& zeros = keep.steps.back();
+    for (int q = 0; q < nq; ++q) {
+      ident[q] = q;
+      pos[q] = (pk.phys_cu[q + 1] - pk.phys_cu[q]) + j - 1;
+      cache[q] = kv_first[q] + pos[q];
+    }
+    ZO_HIP(h2d(w.row_src, ident));
+    ZO_HIP(h2d(w.row_pos, pos));
+    ZO_HIP(h2d(w.row_cand, pk.phys_cand));
+    ZO_HIP(h2d(w.sc_row, ident));
+    ZO_HIP(h2d(w.sc_lab_src, zeros));
+    ZO_HIP(h2d(w.row_cache, cache));
+    if (sg.any) ZO_HIP(hipMemsetAsync(w.as, 0, (size_t)nq * w.as_ld * act_size(d), s));   // rows change meaning
+    rc = bf ? forward<bf16_t>(m, *p, pd, sg, w, w.gen_tok, s, &decode)
+            : forward<float>(m, *p, pd, sg, w, w.gen_tok, s, &decode);
+    if (rc != ZO_OK) return rc;
+    ZO_HIP(launch_greedy_reduce(w.part, w.part_idx, n_tiles, nq, w.gen_tok, tokens_dev, logp_dev, n_new, j, s));
+  }
+  std::vector<float> lp((size_t)nq * n_new);
+  ZO_HIP(hipMemcpyAsync(lp.data(), logp_dev, lp.size() * sizeof(float), hipMemcpyDeviceToHost, s));
+  ZO_HIP(hipStreamSynchronize(s));
+  for (int c = 0; c < nc; ++c) S_host[c] = 0.0;
+  for (int q = 0; q < nq; ++q)
+    if (pk.phys_cand[q] >= 0)
+      for (int j = 0; j < n_new; ++j) S_host[pk.phys_cand[q]] += (double)lp[(size_t)q * n_new + j];
   return ZO_OK;
 }
 
