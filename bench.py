@@ -203,6 +203,62 @@ def cpu_baseline(wl, batch, n_prompts=8, n_layers=3):
                                                t_head, cfg.n_layers / nl, t_gen))}
 
 
+def generation_bench(args, wl, model, bank, batch, db):
+    """Greedy generation of args.generate tokens for every physical sequence of the
+    workload (every probe prompt under every candidate state, with a bank entry): one
+    zo_generate call = prefill + (N - 1) decode steps.  value = generated tokens/s; the
+    roofline is the decode attention's (HBM: every cached K and V row read once per
+    decode step and kv head)."""
+    import torch
+
+    import zeroth_order_fine_amd as zo
+    cfg = wl.model
+    n_new = args.generate
+    for t in range(2):                       # steady state: the bank holds an entry
+        plan = zo.Plan.from_workload(model, wl, t=t)
+        zo.update(model, plan, bank, zo.estimate(plan, zo.score(model, plan, bank, db)["S"]), args.lr)
+    plan = zo.Plan.from_workload(model, wl, t=2)
+    for _ in range(args.warmup):
+        zo.generate(model, plan, bank, db, n_new)
+    torch.cuda.synchronize()
+    a = time.perf_counter()
+    for _ in range(args.steps):
+        out = zo.generate(model, plan, bank, db, n_new)
+    torch.cuda.synchronize()
+    ms = (time.perf_counter() - a) / args.steps * 1e3
+    zo.api.profile_begin()
+    zo.generate(model, plan, bank, db, n_new)
+    torch.cuda.synchronize()
+    prof = zo.api.profile_end()
+    phys = zo.pack(model, plan, db)
+    lengths = [len(t) for t in batch.tokens]
+    n_phys = out["n_phys"]
+    esz = 4 if cfg.dtype == "f32" else 2
+    nq, nkv = cfg.n_heads * cfg.head_dim, cfg.n_kv_heads * cfg.head_dim
+    dec_bytes = 0
+    for li in phys[0]:
+        for j in range(1, n_new):
+            keys = lengths[li] + j
+            # cached K and V rows, q row in, output row out, appended k and v (read + write)
+            dec_bytes += cfg.n_layers * esz * (2 * keys * nkv + 2 * nq + 4 * nkv)
+    n_dec, ms_dec = prof["decode_attention"]
+    gbs = dec_bytes / (ms_dec / 1e3) / 1e9 if ms_dec > 0 else None
+    line = {
+        "metric": "ZO generation: generated tokens/s under candidate states (greedy, 1 GPU)",
+        "value": round(n_phys * n_new / (ms / 1e3), 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_call": round(ms, 3), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic",
+        "config": {"workload": describe(wl), "sequences": n_phys, "new_tokens": n_new,
+                   "prompt_tokens": int(sum(lengths[li] for li in phys[0]))},
+        "roofline": {"kernel": "decode attention (single-query attention over the K/V cache)", "bound": "hbm",
+                     "achieved": round(gbs, 1) if gbs else None, "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                     "frac": round(gbs / PEAK_HBM_GBS, 4) if gbs else None, "traffic": None,
+                     "launches_per_call": n_dec, "algorithmic_mb_per_call": round(dec_bytes / 1e6, 2)},
+        "breakdown_ms_per_call": {k: round(v[1], 3) for k, v in prof.items()},
+    }
+    print(json.dumps(line), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -217,6 +273,8 @@ def main():
                     help="skip the extra scoring without side path that measures its cost (for profiler runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (counter calibration for the traffic figure)")
+    ap.add_argument("--generate", type=int, default=0, metavar="N",
+                    help="time greedy generation of N tokens per sequence (zo_generate) instead of the ZO step")
     args = ap.parse_args()
     if args.copy_calibration:
         copy_calibration()
@@ -241,6 +299,9 @@ def main():
     db = zo.DeviceBatch(batch)
     bank = zo.Bank(model, 2 * wl.n_dirs, wl.rank, wl.targets)
     torch.cuda.synchronize()
+    if args.generate:
+        generation_bench(args, wl, model, bank, batch, db)
+        return
 
     score_s = [0.0]
 

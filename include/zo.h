@@ -320,7 +320,8 @@ enum { ZO_PROF_GEMM_BASE = 0,   /* shared-weight projections (qkv, o, fc1/gate-u
        ZO_PROF_SIDE_PREP = 5,   /* regeneration of the G/V factors and bank packing */
        ZO_PROF_REDUCE = 6,      /* log-prob combine and per-sequence sums */
        ZO_PROF_UPDATE = 7,
-       ZO_PROF_N_CLASSES = 8 };
+       ZO_PROF_DECODE_ATTN = 8, /* generation decode steps: K/V cache append + attention over the cache */
+       ZO_PROF_N_CLASSES = 9 };
 int zo_profile_begin(void);
 int zo_profile_end(int32_t n_classes, int64_t* counts, double* total_ms);
 /* Restrict timing to the classes whose bit (1 << class) is set in class_mask (default:

@@ -303,7 +303,8 @@ def direction(model, plan, dir_index, layer, kind_name, which):
     return out.view(n, plan.rank)
 
 
-PROFILE_CLASSES = ("gemm_base", "gemm_side", "gemm_head", "attention", "norm", "side_prep", "reduce", "update")
+PROFILE_CLASSES = ("gemm_base", "gemm_side", "gemm_head", "attention", "norm", "side_prep", "reduce", "update",
+                   "decode_attention")
 
 
 def profile_begin(classes=None):

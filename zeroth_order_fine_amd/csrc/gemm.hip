@@ -643,9 +643,11 @@ gemm_bf16_pipe_kernel(GemmParams p) {
   const int a_side_off = grp * (p.as_stride ? p.as_stride : p.ks_tile);
   int nkb = p.K / BKM, nk = nkb + p.ks_tile / BK;
   int kt_off = 0;                      // first K-step of this workgroup's K-slice
-  if constexpr (EPI == EPI_PARTIAL) {  // split-K (no side segment)
-    nkb = nk = nkb / p.ksplit;
+  if constexpr (EPI == EPI_PARTIAL) {  // split-K: the last K-slice also runs the side segment
+    const int nks_all = nk - nkb;
+    nkb = nkb / p.ksplit;
     kt_off = blockIdx.z * nkb;
+    nk = nkb + ((int)blockIdx.z == p.ksplit - 1 ? nks_all : 0);
   }
   const int nkwa = p.kwa ? p.kwa / BKM : (1 << 30), nkwb = p.kwb ? p.kwb / BKM : (1 << 30);
   const int nkwas = p.kwas ? p.kwas / BK : (1 << 30);
@@ -964,7 +966,42 @@ __global__ void tproj_reduce_kernel(GemmParams p) {
   }
 }
 
+// Sum the K-slices of a projection in order and apply its epilogue (bias, then the bf16
+// store, GELU, SwiGLU pairing or the fp32 residual update), the same forms as the
+// projection kernel's epilogue.
+__global__ void proj_reduce_kernel(GemmParams p) {
+  const int NO = p.epi == EPI_SWIGLU ? p.N / 2 : p.N;      // output columns
+  const int64_t n = (int64_t)p.M * NO, mn = (int64_t)p.M * p.N;
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n; e += (int64_t)gridDim.x * blockDim.x) {
+    const int r = (int)(e / NO), c = (int)(e - (int64_t)r * NO);
+    auto sum = [&](int col) {
+      float v = 0.f;
+      for (int z = 0; z < p.ksplit; ++z) v += p.partial[(int64_t)z * mn + (int64_t)r * p.N + col];
+      return v + (p.bias ? p.bias[col] : 0.f);
+    };
+    if (p.epi == EPI_SWIGLU) {       // packed rows: 16 gate rows, then the 16 matching up rows
+      const int g = (c / 16) * 32 + c % 16;
+      ((bf16_t*)p.C)[(int64_t)r * p.ldc + c] = f32_to_bf16(silu_fast(sum(g)) * sum(g + 16));
+    } else if (p.epi == EPI_RESID) {
+      p.H[(int64_t)r * p.ldh + c] += sum(c);
+    } else if (p.epi == EPI_GELU) {
+      ((bf16_t*)p.C)[(int64_t)r * p.ldc + c] = f32_to_bf16(gelu_fast(sum(c)));
+    } else {
+      ((bf16_t*)p.C)[(int64_t)r * p.ldc + c] = f32_to_bf16(sum(c));
+    }
+  }
+}
+
 }  // namespace
+
+hipError_t launch_proj_reduce(const GemmParams& p, hipStream_t s) {
+  const int64_t n = (int64_t)p.M * (p.epi == EPI_SWIGLU ? p.N / 2 : p.N);
+  if (n <= 0) return hipSuccess;
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  hipLaunchKernelGGL(proj_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
 
 hipError_t launch_tproj_reduce(const GemmParams& p, hipStream_t s) {
   const int64_t n = (int64_t)p.M * p.N;
@@ -1034,6 +1071,19 @@ int pipe_tile(const GemmParams& p) {
 hipError_t gemm_launch_bf16(const GemmParams& p, int cfg, hipStream_t s) {
   if (p.M <= 0 || p.N <= 0) return hipSuccess;
   if (cfg == GEMM_CFG_BIG) {
+    // K-slices (decode steps of generation: a few rows, so the weights are streamed by
+    // ksplit x more workgroups): fp32 partial sums of the 128x128-tile kernel, the side
+    // segment in the last slice, then an ordered reduction that applies the epilogue
+    if (p.ksplit > 1) {
+      if (p.a_e4m3 || p.b_e4m3 || p.kwa || p.kwb || p.kwas || p.c_lo || p.c_f32 || !p.partial ||
+          (p.K / 64) % p.ksplit != 0)
+        return hipErrorInvalidValue;
+      GemmParams q = p;
+      q.epi = EPI_PARTIAL;
+      hipError_t e = launch_bf16_pipe<128, 128, 64, 64, EPI_PARTIAL>(q, s);
+      if (e != hipSuccess) return e;
+      return launch_proj_reduce(p, s);
+    }
     // e4m3 projections: always 128x128 tiles of four 64x64 wave tiles.  The 128x64 wave
     // tile needs 128 accumulator registers next to 32-byte fragments, more than the 256 a
     // lane has at two waves a SIMD (spills); the 128x128 tile streams the same bytes per

@@ -460,6 +460,8 @@ int side_geometry(const zo_model* m, const zo_plan_s& p, const zo_bank* bank, Si
   return ZO_OK;
 }
 
+constexpr int kMaxDecodeSplit = 8;   // K-slices of a decode-step projection, at most
+
 struct WsPtrs {
   int32_t *row_src, *row_pos, *row_cand, *phys_cu, *phys_first, *sc_row, *sc_lab_src, *work, *labels;
   int32_t* cand_dir;
@@ -481,6 +483,7 @@ struct WsPtrs {
   void *kcache = nullptr, *vcache = nullptr;
   int64_t kv_layer_elems = 0;
   int32_t *kv_first = nullptr, *row_cache = nullptr, *gen_tok = nullptr, *part_idx = nullptr;
+  float* proj_partial = nullptr;   // K-slice partial sums of decode-step projections
   size_t bytes;
 };
 
@@ -586,6 +589,8 @@ void carve(const zo_model* m, const zo_plan_s& p, const Packing& pk, const SideG
     w.kv_layer_elems = kv_rows * NKV;
     w.kcache = b.take<unsigned char>(d.n_layers * w.kv_layer_elems * as);
     w.vcache = b.take<unsigned char>(d.n_layers * w.kv_layer_elems * as);
+    const int64_t max_n = std::max<int64_t>(NQ + 2 * NKV, std::max<int64_t>(D, is_opt(d) ? F : 2 * F));
+    w.proj_partial = b.take<float>((int64_t)kMaxDecodeSplit * std::max(pk.n_phys, 1) * max_n);
   }
   w.bytes = align_up(b.off, 256);
 }
@@ -698,6 +703,14 @@ int forward(zo_model* m, const zo_plan_s& p, const Packing& pk, const SideGeom& 
     GemmParams gp = gemm_base(X, (int64_t)K * x2, B, K, M, N, K * x2);
     if (sp) gp.kwb = K;
     gp.a_e4m3 = gp.b_e4m3 = f8;
+    if (gen && gen->decode && !f8 && !sp && bf) {
+      // decode steps (one row per sequence): K-slices until the 128x128 tiles fill the
+      // CUs, at least four 64-deep steps a slice
+      const int64_t tiles = (int64_t)((M + 127) / 128) * ((N + 127) / 128);
+      int ks = 1;
+      while (ks < kMaxDecodeSplit && tiles * ks < 256 && (K / 64) % (2 * ks) == 0 && K / 64 / (2 * ks) >= 4) ks *= 2;
+      if (ks > 1) { gp.ksplit = ks; gp.partial = w.proj_partial; }
+    }
     return gp;
   };
   // LayerNorm / RMSNorm of the residual stream into the input of the next linears
@@ -738,7 +751,7 @@ int forward(zo_model* m, const zo_plan_s& p, const Packing& pk, const SideGeom& 
                                      Wf(P[P_KNW]), eps, m->rope, w.row_pos, s));
     }
     {
-      ProfScope ps(ZO_PROF_ATTENTION, s);
+      ProfScope ps(gen && gen->decode ? ZO_PROF_DECODE_ATTN : ZO_PROF_ATTENTION, s);
       T* kc = gen ? (T*)w.kcache + (int64_t)l * w.kv_layer_elems : nullptr;
       T* vc = gen ? (T*)w.vcache + (int64_t)l * w.kv_layer_elems : nullptr;
       if (gen) ZO_HIP(launch_kv_append<T>((const T*)w.qkv, NQKV, M, w.row_cache, NQ, NKV, kc, vc, s));
