@@ -228,7 +228,7 @@ hipError_t launch_kv_append(const T* qkv, int ld, int M, const int32_t* row_cach
 template <typename T>
 hipError_t launch_decode_attention(const T* qkv, int ld, const T* kc, const T* vc, const int32_t* kv_first,
                                    const int32_t* row_pos, int M, int hq, int hkv, int hd, T* out, int ld_out,
-                                   hipStream_t s);
+                                   int max_keys, hipStream_t s);
 hipError_t launch_greedy_reduce(const float2* part, const int32_t* part_idx, int n_tiles, int n_rows,
                                 int32_t* next_tok, int32_t* tokens_out, float* logp_out, int n_new, int step,
                                 hipStream_t s);

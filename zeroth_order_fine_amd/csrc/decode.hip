@@ -17,9 +17,6 @@
 
 namespace {
 
-template <typename T>
-__device__ __forceinline__ float ld_act(const T* p) { return to_f32<T>(*p); }
-
 // Append the k and v parts of each row of the packed q|k|v activations to the cache row
 // row_cache[r].  One workgroup per row, 16-byte copies (NKV * head_dim elements each).
 template <typename T>
@@ -36,74 +33,113 @@ __global__ void kv_append_kernel(const T* __restrict__ qkv, int ld, const int32_
 }
 
 // One query row per (sequence, head): attention of the row at position row_pos[s] over
-// the cached keys 0 .. row_pos[s] of sequence s (its own key included: causal).  One wave
-// per (sequence, head); keys in chunks of 64, one key a lane for the scores, an online
-// softmax across chunks (running max and sum, fp32), and for the weighted sum of values
-// every lane owns HD / 64 of the head dimensions and walks the chunk's 64 keys.
-template <typename T, int HD>
-__global__ void __launch_bounds__(64)
+// the cached keys 0 .. row_pos[s] of sequence s (its own key included: causal).  NW
+// waves per (sequence, head), wave w taking the 64-key chunks w, w + NW, ... (one wave
+// for short contexts, four beyond 512 keys); inside a
+// wave LPK = head_dim / E lanes share a key (E elements = 16 bytes a lane), so every
+// cached row is read as whole 16-byte pieces by neighbouring lanes.  Scores: partial dot
+// products of the lane's q piece, summed over the key's lanes by shuffles; an online
+// softmax across the wave's chunks in fp32; values: the same lane split, then a shuffle
+// sum over the keys a lane group covered.  The waves' (max, sum, output) meet in LDS.
+template <typename T, int HD, int NW>
+__global__ void __launch_bounds__(64 * NW)
 decode_attn_kernel(const T* __restrict__ qkv, int ld, const T* __restrict__ kc, const T* __restrict__ vc,
                    const int32_t* __restrict__ kv_first, const int32_t* __restrict__ row_pos, int hq, int hkv,
                    float scale, T* __restrict__ out, int ld_out) {
-  constexpr int DPL = HD / 64 > 0 ? HD / 64 : 1;    // head dimensions per lane in the value sum
-  __shared__ float q_s[HD];
-  __shared__ float p_s[64];
-  const int s = blockIdx.x, h = blockIdx.y, lane = threadIdx.x;
+  constexpr int E = 16 / sizeof(T);                  // elements in a lane's 16-byte piece
+  constexpr int LPK = HD / E;                        // lanes per key row
+  constexpr int KPI = 64 / LPK;                      // keys per wave-wide step
+  static_assert(LPK >= 1 && LPK <= 64 && 64 % LPK == 0, "head_dim");
+  __shared__ float sc[NW][64];
+  __shared__ float wm[NW], wl[NW];
+  __shared__ float wo[NW][HD];
+  const int s = blockIdx.x, h = blockIdx.y;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int c = lane % LPK, g = lane / LPK;          // piece of the row, key within the step
   const int kvh = h / (hq / hkv);
   const int nkv = hkv * HD;
-  for (int d = lane; d < HD; d += 64) q_s[d] = ld_act<T>(qkv + (int64_t)s * ld + h * HD + d) * scale;
-  __syncthreads();
-  const int n_keys = row_pos[s] + 1;
-  const int64_t base = (int64_t)kv_first[s] * nkv + kvh * HD;
-  float run_max = -INFINITY, run_sum = 0.f;
-  float acc[DPL];
+  float q[E];
+  {
+    const u32x4_t w = *(const u32x4_t*)(qkv + (int64_t)s * ld + h * HD + c * E);
+    const T* e = (const T*)&w;
 #pragma unroll
-  for (int e = 0; e < DPL; ++e) acc[e] = 0.f;
-  for (int k0 = 0; k0 < n_keys; k0 += 64) {
-    const int k = k0 + lane;
-    float sc = -INFINITY;
-    if (k < n_keys) {                             // the lane's key row in 16-byte pieces
-      const T* kr = kc + base + (int64_t)k * nkv;
-      constexpr int V = 16 / sizeof(T);
-      float dot = 0.f;
+    for (int u = 0; u < E; ++u) q[u] = to_f32<T>(e[u]) * scale;
+  }
+  const int n_keys = row_pos[s] + 1;
+  const int64_t base = (int64_t)kv_first[s] * nkv + kvh * HD + c * E;
+  float run_max = -INFINITY, run_sum = 0.f;
+  float acc[E];
+#pragma unroll
+  for (int u = 0; u < E; ++u) acc[u] = 0.f;
+  for (int k0 = wave * 64; k0 < n_keys; k0 += 64 * NW) {
+    // scores of the chunk's 64 keys
 #pragma unroll 4
-      for (int d0 = 0; d0 < HD; d0 += V) {
-        const u32x4_t w = *(const u32x4_t*)(kr + d0);
+    for (int it = 0; it < 64 / KPI; ++it) {
+      const int j = it * KPI + g, k = k0 + j;
+      float part = 0.f;
+      if (k < n_keys) {
+        const u32x4_t w = *(const u32x4_t*)(kc + base + (int64_t)k * nkv);
         const T* e = (const T*)&w;
 #pragma unroll
-        for (int u = 0; u < V; ++u) dot += q_s[d0 + u] * to_f32<T>(e[u]);
+        for (int u = 0; u < E; ++u) part += q[u] * to_f32<T>(e[u]);
       }
-      sc = dot;
+#pragma unroll
+      for (int sh = 1; sh < LPK; sh <<= 1) part += __shfl_xor(part, sh, 64);
+      if (c == 0) sc[wave][j] = k < n_keys ? part : -INFINITY;
     }
-    float cm = sc;
+    __builtin_amdgcn_wave_barrier();
+    const float sj = sc[wave][lane];
+    float cm = sj;
 #pragma unroll
     for (int sh = 32; sh >= 1; sh >>= 1) cm = fmaxf(cm, __shfl_xor(cm, sh, 64));
     const float new_max = fmaxf(run_max, cm);
-    const float corr = expf(run_max - new_max);   // 0 on the first chunk (run_max = -inf)
-    const float pk = k < n_keys ? expf(sc - new_max) : 0.f;
-    float ps = pk;
+    const float corr = expf(run_max - new_max);      // 0 on the wave's first chunk
+    const float pj = sj == -INFINITY ? 0.f : expf(sj - new_max);
+    float ps = pj;
 #pragma unroll
     for (int sh = 32; sh >= 1; sh >>= 1) ps += __shfl_xor(ps, sh, 64);
     run_sum = run_sum * corr + ps;
     run_max = new_max;
-    p_s[lane] = pk;
-    __syncthreads();
+    __builtin_amdgcn_wave_barrier();
+    sc[wave][lane] = pj;                               // the chunk's probabilities
+    __builtin_amdgcn_wave_barrier();
 #pragma unroll
-    for (int e = 0; e < DPL; ++e) acc[e] *= corr;
-    const int kn = min(64, n_keys - k0);
-    for (int j = 0; j < kn; ++j) {
-      const T* vr = vc + base + (int64_t)(k0 + j) * nkv;
-      const float pj = p_s[j];
+    for (int u = 0; u < E; ++u) acc[u] *= corr;
+#pragma unroll 4
+    for (int it = 0; it < 64 / KPI; ++it) {
+      const int j = it * KPI + g, k = k0 + j;
+      if (k < n_keys) {
+        const float p = sc[wave][j];
+        const u32x4_t w = *(const u32x4_t*)(vc + base + (int64_t)k * nkv);
+        const T* e = (const T*)&w;
 #pragma unroll
-      for (int e = 0; e < DPL; ++e)
-        if (lane + 64 * e < HD) acc[e] += pj * ld_act<T>(vr + lane + 64 * e);
+        for (int u = 0; u < E; ++u) acc[u] += p * to_f32<T>(e[u]);
+      }
     }
-    __syncthreads();
+    __builtin_amdgcn_wave_barrier();
   }
-  const float inv = 1.0f / run_sum;
+  // sum over the key groups of the wave (lanes with the same piece c)
 #pragma unroll
-  for (int e = 0; e < DPL; ++e)
-    if (lane + 64 * e < HD) out[(int64_t)s * ld_out + h * HD + lane + 64 * e] = from_f32<T>(acc[e] * inv);
+  for (int u = 0; u < E; ++u)
+#pragma unroll
+    for (int sh = LPK; sh < 64; sh <<= 1) acc[u] += __shfl_xor(acc[u], sh, 64);
+  if (lane == 0) { wm[wave] = run_max; wl[wave] = run_sum; }
+  if (g == 0)
+#pragma unroll
+    for (int u = 0; u < E; ++u) wo[wave][c * E + u] = acc[u];
+  __syncthreads();
+  for (int d = threadIdx.x; d < HD; d += 64 * NW) {
+    float m = -INFINITY;
+    for (int w = 0; w < NW; ++w) m = fmaxf(m, wm[w]);
+    float l = 0.f, o = 0.f;
+    for (int w = 0; w < NW; ++w) {
+      if (wm[w] == -INFINITY) continue;               // a wave without keys
+      const float f = expf(wm[w] - m);
+      l += wl[w] * f;
+      o += wo[w][d] * f;
+    }
+    out[(int64_t)s * ld_out + h * HD + d] = from_f32<T>(o / l);
+  }
 }
 
 // Greedy choice per row from the head's vocabulary-tile partials (max, sum of exp, first
@@ -148,24 +184,33 @@ template hipError_t launch_kv_append<bf16_t>(const bf16_t*, int, int, const int3
 template <typename T>
 hipError_t launch_decode_attention(const T* qkv, int ld, const T* kc, const T* vc, const int32_t* kv_first,
                                    const int32_t* row_pos, int M, int hq, int hkv, int hd, T* out, int ld_out,
-                                   hipStream_t s) {
+                                   int max_keys, hipStream_t s) {
   if (M <= 0) return hipSuccess;
   const float scale = (float)(1.0 / sqrt((double)hd));
-  dim3 grid(M, hq);
+  const dim3 grid(M, hq);
+  const bool wide = max_keys > 512;
+#define ZO_DEC(HD)                                                                                       \
+  if (wide)                                                                                              \
+    hipLaunchKernelGGL((decode_attn_kernel<T, HD, 4>), grid, dim3(256), 0, s, qkv, ld, kc, vc, kv_first, \
+                       row_pos, hq, hkv, scale, out, ld_out);                                            \
+  else                                                                                                   \
+    hipLaunchKernelGGL((decode_attn_kernel<T, HD, 1>), grid, dim3(64), 0, s, qkv, ld, kc, vc, kv_first,  \
+                       row_pos, hq, hkv, scale, out, ld_out);
   switch (hd) {
-    case 16: hipLaunchKernelGGL((decode_attn_kernel<T, 16>), grid, dim3(64), 0, s, qkv, ld, kc, vc, kv_first, row_pos, hq, hkv, scale, out, ld_out); break;
-    case 32: hipLaunchKernelGGL((decode_attn_kernel<T, 32>), grid, dim3(64), 0, s, qkv, ld, kc, vc, kv_first, row_pos, hq, hkv, scale, out, ld_out); break;
-    case 64: hipLaunchKernelGGL((decode_attn_kernel<T, 64>), grid, dim3(64), 0, s, qkv, ld, kc, vc, kv_first, row_pos, hq, hkv, scale, out, ld_out); break;
-    case 128: hipLaunchKernelGGL((decode_attn_kernel<T, 128>), grid, dim3(64), 0, s, qkv, ld, kc, vc, kv_first, row_pos, hq, hkv, scale, out, ld_out); break;
+    case 16: ZO_DEC(16) break;
+    case 32: ZO_DEC(32) break;
+    case 64: ZO_DEC(64) break;
+    case 128: ZO_DEC(128) break;
     default: return hipErrorInvalidValue;
   }
+#undef ZO_DEC
   return hipGetLastError();
 }
 template hipError_t launch_decode_attention<float>(const float*, int, const float*, const float*, const int32_t*,
-                                                   const int32_t*, int, int, int, int, float*, int, hipStream_t);
+                                                   const int32_t*, int, int, int, int, float*, int, int, hipStream_t);
 template hipError_t launch_decode_attention<bf16_t>(const bf16_t*, int, const bf16_t*, const bf16_t*,
                                                     const int32_t*, const int32_t*, int, int, int, int, bf16_t*, int,
-                                                    hipStream_t);
+                                                    int, hipStream_t);
 
 hipError_t launch_greedy_reduce(const float2* part, const int32_t* part_idx, int n_tiles, int n_rows,
                                 int32_t* next_tok, int32_t* tokens_out, float* logp_out, int n_new, int step,

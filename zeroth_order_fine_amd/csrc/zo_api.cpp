@@ -647,6 +647,7 @@ GemmParams gemm_base(const void* A, int64_t lda, const void* B, int64_t ldb, int
 // rows, and the head also records each tile's first maximum column.
 struct GenCtx {
   bool decode;
+  int max_keys;       // decode: the longest sequence's key count this step
 };
 
 template <typename T>
@@ -757,7 +758,7 @@ int forward(zo_model* m, const zo_plan_s& p, const Packing& pk, const SideGeom& 
       if (gen) ZO_HIP(launch_kv_append<T>((const T*)w.qkv, NQKV, M, w.row_cache, NQ, NKV, kc, vc, s));
       if (gen && gen->decode)
         ZO_HIP(launch_decode_attention<T>((const T*)w.qkv, NQKV, kc, vc, w.kv_first, w.row_pos, M, d.n_heads,
-                                          d.n_kv_heads, d.head_dim, (T*)w.attn, NQ, s));
+                                          d.n_kv_heads, d.head_dim, (T*)w.attn, NQ, gen->max_keys, s));
       else if (sp)
         ZO_HIP(launch_attention_split((const float*)w.qkv, NQKV, (bf16_t*)w.attn, 2 * NQ, NQ, w.phys_cu, w.work,
                                       (int)pk.work.size(), d.n_heads, d.n_kv_heads, d.head_dim, s));
@@ -1316,7 +1317,8 @@ int zo_generate(zo_model* m, const zo_plan_t* p, const zo_bank* bank, const zo_b
   const int bn = gemm_cfg_bn(GEMM_CFG_HEAD, bf);
   const int n_tiles = (d.vocab + bn - 1) / bn;
   // prefill: the prompts (the first token comes from each prompt's last row)
-  const GenCtx prefill{false}, decode{true};
+  const GenCtx prefill{false, 0};
+  GenCtx decode{true, 0};
   rc = bf ? forward<bf16_t>(m, *p, pk, sg, w, b->tokens_dev, s, &prefill)
           : forward<float>(m, *p, pk, sg, w, b->tokens_dev, s, &prefill);
   if (rc != ZO_OK) return rc;
@@ -1337,10 +1339,12 @@ int zo_generate(zo_model* m, const zo_plan_t* p, const zo_bank* bank, const zo_b
     std::vector<int32_t>& cache = keep.steps.back();
     keep.steps.emplace_back(nq, 0);
     std::vector<int32_t>& zeros = keep.steps.back();
+    decode.max_keys = 0;
     for (int q = 0; q < nq; ++q) {
       ident[q] = q;
       pos[q] = (pk.phys_cu[q + 1] - pk.phys_cu[q]) + j - 1;
       cache[q] = kv_first[q] + pos[q];
+      decode.max_keys = std::max(decode.max_keys, pos[q] + 1);
     }
     ZO_HIP(h2d(w.row_src, ident));
     ZO_HIP(h2d(w.row_pos, pos));
