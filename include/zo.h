@@ -265,12 +265,12 @@ int zo_score(zo_model* m, const zo_plan_t* p, const zo_bank* bank, const zo_batc
  *   S_host:     host fp64 [n_cand] out, per candidate the sum over its sequences of the
  *               generated tokens' log-probabilities (the generative objective, for
  *               zo_estimate).
- * Sequences are in zo_pack's order.  fp32 and bf16 models; not with ZO_PLAN_ACT_SPLIT;
+ * Sequences are in zo_pack's order.  fp32, bf16 and fp8 models; not with ZO_PLAN_ACT_SPLIT;
  * prompt length + n_new - 1 <= max_pos.  The batch's score modes are validated but not
  * used.  zo_generate_layout gives n_phys and the workspace bytes (the cache takes
  * 2 x n_layers x (sum of prompt lengths + n_phys (n_new - 1)) x n_kv_heads x head_dim
- * activation elements).  Errors as zo_score; ZO_E_INVAL for an fp8 model, a two-term
- * plan or n_new < 1, ZO_E_SHAPE beyond max_pos. */
+ * activation elements).  Errors as zo_score; ZO_E_INVAL for a two-term plan or
+ * n_new < 1, ZO_E_SHAPE beyond max_pos. */
 int zo_generate_layout(const zo_model* m, const zo_plan_t* p, const zo_bank* bank, const zo_batch* b,
                        int32_t n_new, int32_t* n_phys, size_t* ws_bytes);
 int zo_generate(zo_model* m, const zo_plan_t* p, const zo_bank* bank, const zo_batch* b, int32_t n_new,

@@ -1,6 +1,8 @@
 """GPU parity of zo_generate (greedy generation with the K/V cache) against the oracle's
 full-recompute greedy generation.
 
+fp8 models follow the same checks with the fp8 scoring bound (6e-2).
+
 Several continuations can be correct where two logits are closer than the arithmetic's
 error, so the comparison follows the GPU's own choices: the oracle re-runs every step
 along the GPU's tokens (teacher forcing) and checks that
@@ -25,8 +27,8 @@ TINY_F32 = configs.CONFIGS["tiny"].model
 
 @pytest.mark.parametrize("cfg,n_prompts,len_lo,len_hi,n_new",
                          [(TINY_F32, 2, 5, 70, 12), (SMALL_OPT_BF16, 2, 5, 70, 12), (SMALL_QWEN_BF16, 2, 5, 70, 12),
-                          (SMALL_QWEN_BF16, 1, 600, 700, 3)],
-                         ids=["tiny-f32", "opt-bf16", "qwen3-bf16", "qwen3-bf16-long"])
+                          (SMALL_QWEN_BF16, 1, 600, 700, 3), (SMALL_OPT_FP8, 2, 5, 70, 12)],
+                         ids=["tiny-f32", "opt-bf16", "qwen3-bf16", "qwen3-bf16-long", "opt-fp8"])
 def test_generation_matches_oracle(cfg, n_prompts, len_lo, len_hi, n_new):
     """Two directions, a bank entry, a foreground prompt; prompts of 5..70 tokens and 12
     new tokens, so the cached keys of the longer ones span two 64-key chunks; "long":
@@ -43,8 +45,8 @@ def test_generation_matches_oracle(cfg, n_prompts, len_lo, len_hi, n_new):
     tok = out["tokens"].cpu().numpy()
     lp = out["logp"].cpu().numpy()
     ref = ozo.generate(cfg, o.W, ozo.plan_from_workload(wl, 1), o.bank, batch, n_new, forced=tok)
-    f32 = cfg.dtype == "f32"
-    lp_tol, choice_tol = (1e-4, 1e-4) if f32 else (2e-2, 2e-2)
+    # fp8 models: the fp8 scoring bound (tests/test_gpu_parity.py FP8_SEQ_ATOL) per token
+    lp_tol, choice_tol = {"f32": (1e-4, 1e-4), "bf16": (2e-2, 2e-2), "fp8": (6e-2, 6e-2)}[cfg.dtype]
     gap = ref["best_logp"] - ref["logp"]
     flush("max choice gap %.3g, max |dlogp| %.3g, exact argmax %d of %d" % (
         gap.max(), np.abs(lp - ref["logp"]).max(), int((tok == ref["best_tok"]).sum()), tok.size))
@@ -56,16 +58,10 @@ def test_generation_matches_oracle(cfg, n_prompts, len_lo, len_hi, n_new):
 
 
 def test_generation_rejections():
-    """fp8 models and two-term plans are refused (ZO_E_INVAL), and so is a continuation
-    past max_pos (ZO_E_SHAPE)."""
+    """Two-term plans are refused (ZO_E_INVAL), and so is a continuation past max_pos
+    (ZO_E_SHAPE)."""
     need_gpu()
     import zeroth_order_fine_amd as zo
-    wl = workload(SMALL_OPT_FP8, n_prompts=2)
-    g = GpuRun(wl)
-    db = zo.DeviceBatch(inputs.make_batch(wl))
-    with pytest.raises(zo.ZoError) as ei:
-        zo.generate(g.model, g.plan(0), None, db, 4)
-    assert ei.value.code == -1
     wl2 = workload(SMALL_OPT_BF16, n_prompts=2, len_lo=500, len_hi=510)
     g2 = GpuRun(wl2)
     db2 = zo.DeviceBatch(inputs.make_batch(wl2))

@@ -225,9 +225,9 @@ hipError_t launch_attention_e4m3(const bf16_t* qkv, int ld_qkv, e4m3_t* out, int
 template <typename T>
 hipError_t launch_kv_append(const T* qkv, int ld, int M, const int32_t* row_cache, int nq, int nkv, T* kc, T* vc,
                             hipStream_t s);
-template <typename T>
+template <typename T, typename TO>
 hipError_t launch_decode_attention(const T* qkv, int ld, const T* kc, const T* vc, const int32_t* kv_first,
-                                   const int32_t* row_pos, int M, int hq, int hkv, int hd, T* out, int ld_out,
+                                   const int32_t* row_pos, int M, int hq, int hkv, int hd, TO* out, int ld_out,
                                    int max_keys, hipStream_t s);
 hipError_t launch_greedy_reduce(const float2* part, const int32_t* part_idx, int n_tiles, int n_rows,
                                 int32_t* next_tok, int32_t* tokens_out, float* logp_out, int n_new, int step,

@@ -41,11 +41,11 @@ __global__ void kv_append_kernel(const T* __restrict__ qkv, int ld, const int32_
 // products of the lane's q piece, summed over the key's lanes by shuffles; an online
 // softmax across the wave's chunks in fp32; values: the same lane split, then a shuffle
 // sum over the keys a lane group covered.  The waves' (max, sum, output) meet in LDS.
-template <typename T, int HD, int NW>
+template <typename T, int HD, int NW, typename TO>
 __global__ void __launch_bounds__(64 * NW)
 decode_attn_kernel(const T* __restrict__ qkv, int ld, const T* __restrict__ kc, const T* __restrict__ vc,
                    const int32_t* __restrict__ kv_first, const int32_t* __restrict__ row_pos, int hq, int hkv,
-                   float scale, T* __restrict__ out, int ld_out) {
+                   float scale, TO* __restrict__ out, int ld_out) {
   constexpr int E = 16 / sizeof(T);                  // elements in a lane's 16-byte piece
   constexpr int LPK = HD / E;                        // lanes per key row
   constexpr int KPI = 64 / LPK;                      // keys per wave-wide step
@@ -138,7 +138,10 @@ decode_attn_kernel(const T* __restrict__ qkv, int ld, const T* __restrict__ kc, 
       l += wl[w] * f;
       o += wo[w][d] * f;
     }
-    out[(int64_t)s * ld_out + h * HD + d] = from_f32<T>(o / l);
+    if constexpr (std::is_same<TO, e4m3_t>::value)   // the e4m3 input of an fp8 model's o-projection
+      out[(int64_t)s * ld_out + h * HD + d] = (e4m3_t)(f32x4_to_e4m3(o / l, 0.f, 0.f, 0.f) & 0xffu);
+    else
+      out[(int64_t)s * ld_out + h * HD + d] = from_f32<T>(o / l);
   }
 }
 
@@ -181,20 +184,20 @@ template hipError_t launch_kv_append<float>(const float*, int, int, const int32_
 template hipError_t launch_kv_append<bf16_t>(const bf16_t*, int, int, const int32_t*, int, int, bf16_t*, bf16_t*,
                                              hipStream_t);
 
-template <typename T>
+template <typename T, typename TO>
 hipError_t launch_decode_attention(const T* qkv, int ld, const T* kc, const T* vc, const int32_t* kv_first,
-                                   const int32_t* row_pos, int M, int hq, int hkv, int hd, T* out, int ld_out,
+                                   const int32_t* row_pos, int M, int hq, int hkv, int hd, TO* out, int ld_out,
                                    int max_keys, hipStream_t s) {
   if (M <= 0) return hipSuccess;
   const float scale = (float)(1.0 / sqrt((double)hd));
   const dim3 grid(M, hq);
   const bool wide = max_keys > 512;
-#define ZO_DEC(HD)                                                                                       \
-  if (wide)                                                                                              \
-    hipLaunchKernelGGL((decode_attn_kernel<T, HD, 4>), grid, dim3(256), 0, s, qkv, ld, kc, vc, kv_first, \
-                       row_pos, hq, hkv, scale, out, ld_out);                                            \
-  else                                                                                                   \
-    hipLaunchKernelGGL((decode_attn_kernel<T, HD, 1>), grid, dim3(64), 0, s, qkv, ld, kc, vc, kv_first,  \
+#define ZO_DEC(HD)                                                                                          \
+  if (wide)                                                                                                 \
+    hipLaunchKernelGGL((decode_attn_kernel<T, HD, 4, TO>), grid, dim3(256), 0, s, qkv, ld, kc, vc, kv_first, \
+                       row_pos, hq, hkv, scale, out, ld_out);                                               \
+  else                                                                                                      \
+    hipLaunchKernelGGL((decode_attn_kernel<T, HD, 1, TO>), grid, dim3(64), 0, s, qkv, ld, kc, vc, kv_first,  \
                        row_pos, hq, hkv, scale, out, ld_out);
   switch (hd) {
     case 16: ZO_DEC(16) break;
@@ -206,11 +209,15 @@ hipError_t launch_decode_attention(const T* qkv, int ld, const T* kc, const T* v
 #undef ZO_DEC
   return hipGetLastError();
 }
-template hipError_t launch_decode_attention<float>(const float*, int, const float*, const float*, const int32_t*,
-                                                   const int32_t*, int, int, int, int, float*, int, int, hipStream_t);
-template hipError_t launch_decode_attention<bf16_t>(const bf16_t*, int, const bf16_t*, const bf16_t*,
-                                                    const int32_t*, const int32_t*, int, int, int, int, bf16_t*, int,
-                                                    int, hipStream_t);
+template hipError_t launch_decode_attention<float, float>(const float*, int, const float*, const float*,
+                                                          const int32_t*, const int32_t*, int, int, int, int, float*,
+                                                          int, int, hipStream_t);
+template hipError_t launch_decode_attention<bf16_t, bf16_t>(const bf16_t*, int, const bf16_t*, const bf16_t*,
+                                                            const int32_t*, const int32_t*, int, int, int, int,
+                                                            bf16_t*, int, int, hipStream_t);
+template hipError_t launch_decode_attention<bf16_t, e4m3_t>(const bf16_t*, int, const bf16_t*, const bf16_t*,
+                                                            const int32_t*, const int32_t*, int, int, int, int,
+                                                            e4m3_t*, int, int, hipStream_t);
 
 hipError_t launch_greedy_reduce(const float2* part, const int32_t* part_idx, int n_tiles, int n_rows,
                                 int32_t* next_tok, int32_t* tokens_out, float* logp_out, int n_new, int step,

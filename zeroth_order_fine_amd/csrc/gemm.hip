@@ -974,10 +974,12 @@ __global__ void proj_reduce_kernel(GemmParams p) {
   const int64_t n = (int64_t)p.M * NO, mn = (int64_t)p.M * p.N;
   for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n; e += (int64_t)gridDim.x * blockDim.x) {
     const int r = (int)(e / NO), c = (int)(e - (int64_t)r * NO);
+    // e4m3 main segments sum in units of 2^-11 of the result (the weights hold w * 2^11)
+    const float unit = p.b_e4m3 ? 1.0f / (float)(1 << ZO_FP8_WEIGHT_EXP) : 1.0f;
     auto sum = [&](int col) {
       float v = 0.f;
       for (int z = 0; z < p.ksplit; ++z) v += p.partial[(int64_t)z * mn + (int64_t)r * p.N + col];
-      return v + (p.bias ? p.bias[col] : 0.f);
+      return v * unit + (p.bias ? p.bias[col] : 0.f);
     };
     if (p.epi == EPI_SWIGLU) {       // packed rows: 16 gate rows, then the 16 matching up rows
       const int g = (c / 16) * 32 + c % 16;
@@ -985,7 +987,11 @@ __global__ void proj_reduce_kernel(GemmParams p) {
     } else if (p.epi == EPI_RESID) {
       p.H[(int64_t)r * p.ldh + c] += sum(c);
     } else if (p.epi == EPI_GELU) {
-      ((bf16_t*)p.C)[(int64_t)r * p.ldc + c] = f32_to_bf16(gelu_fast(sum(c)));
+      const float v = gelu_fast(sum(c));
+      if (p.a_e4m3)                  // the e4m3 input of the next projection
+        ((e4m3_t*)p.C)[(int64_t)r * p.ldc + c] = (e4m3_t)(f32x4_to_e4m3(v, 0.f, 0.f, 0.f) & 0xffu);
+      else
+        ((bf16_t*)p.C)[(int64_t)r * p.ldc + c] = f32_to_bf16(v);
     } else {
       ((bf16_t*)p.C)[(int64_t)r * p.ldc + c] = f32_to_bf16(sum(c));
     }
@@ -1075,12 +1081,14 @@ hipError_t gemm_launch_bf16(const GemmParams& p, int cfg, hipStream_t s) {
     // ksplit x more workgroups): fp32 partial sums of the 128x128-tile kernel, the side
     // segment in the last slice, then an ordered reduction that applies the epilogue
     if (p.ksplit > 1) {
-      if (p.a_e4m3 || p.b_e4m3 || p.kwa || p.kwb || p.kwas || p.c_lo || p.c_f32 || !p.partial ||
-          (p.K / 64) % p.ksplit != 0)
+      const bool f8 = p.a_e4m3 && p.b_e4m3;
+      if (p.a_e4m3 != p.b_e4m3 || p.kwa || p.kwb || p.kwas || p.c_lo || p.c_f32 || !p.partial ||
+          (p.K / (f8 ? 128 : 64)) % p.ksplit != 0 || (f8 && p.epi == EPI_SWIGLU))
         return hipErrorInvalidValue;
       GemmParams q = p;
       q.epi = EPI_PARTIAL;
-      hipError_t e = launch_bf16_pipe<128, 128, 64, 64, EPI_PARTIAL>(q, s);
+      hipError_t e = f8 ? launch_bf16_pipe<128, 128, 64, 64, EPI_PARTIAL, true>(q, s)
+                        : launch_bf16_pipe<128, 128, 64, 64, EPI_PARTIAL>(q, s);
       if (e != hipSuccess) return e;
       return launch_proj_reduce(p, s);
     }

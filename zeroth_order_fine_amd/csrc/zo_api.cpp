@@ -704,12 +704,13 @@ int forward(zo_model* m, const zo_plan_s& p, const Packing& pk, const SideGeom& 
     GemmParams gp = gemm_base(X, (int64_t)K * x2, B, K, M, N, K * x2);
     if (sp) gp.kwb = K;
     gp.a_e4m3 = gp.b_e4m3 = f8;
-    if (gen && gen->decode && !f8 && !sp && bf) {
+    if (gen && gen->decode && !sp && bf) {
       // decode steps (one row per sequence): K-slices until the 128x128 tiles fill the
-      // CUs, at least four 64-deep steps a slice
+      // CUs, at least four K-steps (64 bf16 or 128 e4m3 deep) a slice
       const int64_t tiles = (int64_t)((M + 127) / 128) * ((N + 127) / 128);
+      const int nks = K / (f8 ? 128 : 64);
       int ks = 1;
-      while (ks < kMaxDecodeSplit && tiles * ks < 256 && (K / 64) % (2 * ks) == 0 && K / 64 / (2 * ks) >= 4) ks *= 2;
+      while (ks < kMaxDecodeSplit && tiles * ks < 256 && nks % (2 * ks) == 0 && nks / (2 * ks) >= 4) ks *= 2;
       if (ks > 1) { gp.ksplit = ks; gp.partial = w.proj_partial; }
     }
     return gp;
@@ -756,9 +757,22 @@ int forward(zo_model* m, const zo_plan_s& p, const Packing& pk, const SideGeom& 
       T* kc = gen ? (T*)w.kcache + (int64_t)l * w.kv_layer_elems : nullptr;
       T* vc = gen ? (T*)w.vcache + (int64_t)l * w.kv_layer_elems : nullptr;
       if (gen) ZO_HIP(launch_kv_append<T>((const T*)w.qkv, NQKV, M, w.row_cache, NQ, NKV, kc, vc, s));
-      if (gen && gen->decode)
-        ZO_HIP(launch_decode_attention<T>((const T*)w.qkv, NQKV, kc, vc, w.kv_first, w.row_pos, M, d.n_heads,
-                                          d.n_kv_heads, d.head_dim, (T*)w.attn, NQ, gen->max_keys, s));
+      if (gen && gen->decode) {
+        hipError_t e;
+        if constexpr (std::is_same<T, bf16_t>::value) {
+          if (f8)
+            e = launch_decode_attention<T, e4m3_t>((const T*)w.qkv, NQKV, kc, vc, w.kv_first, w.row_pos, M,
+                                                   d.n_heads, d.n_kv_heads, d.head_dim, (e4m3_t*)w.attn, NQ,
+                                                   gen->max_keys, s);
+          else
+            e = launch_decode_attention<T, T>((const T*)w.qkv, NQKV, kc, vc, w.kv_first, w.row_pos, M, d.n_heads,
+                                              d.n_kv_heads, d.head_dim, (T*)w.attn, NQ, gen->max_keys, s);
+        } else {
+          e = launch_decode_attention<T, T>((const T*)w.qkv, NQKV, kc, vc, w.kv_first, w.row_pos, M, d.n_heads,
+                                            d.n_kv_heads, d.head_dim, (T*)w.attn, NQ, gen->max_keys, s);
+        }
+        ZO_HIP(e);
+      }
       else if (sp)
         ZO_HIP(launch_attention_split((const float*)w.qkv, NQKV, (bf16_t*)w.attn, 2 * NQ, NQ, w.phys_cu, w.work,
                                       (int)pk.work.size(), d.n_heads, d.n_kv_heads, d.head_dim, s));
@@ -1252,8 +1266,6 @@ int zo_score(zo_model* m, const zo_plan_t* p, const zo_bank* bank, const zo_batc
 
 static int check_generate(const zo_model* m, const zo_plan_t* p, const zo_batch* b, int32_t n_new) {
   const zo_model_desc& d = m->d;
-  ZO_CHECK(d.dtype == ZO_DTYPE_F32 || d.dtype == ZO_DTYPE_BF16, ZO_E_INVAL,
-           "generation: fp32 and bf16 models (fp8 models score only)");
   ZO_CHECK(!split_act(*p), ZO_E_INVAL, "generation: not with ZO_PLAN_ACT_SPLIT");
   ZO_CHECK(n_new >= 1, ZO_E_INVAL, "n_new must be >= 1");
   int rc = validate_batch(d, b);
@@ -1290,7 +1302,7 @@ int zo_generate(zo_model* m, const zo_plan_t* p, const zo_bank* bank, const zo_b
   if (rc) return rc;
   hipStream_t s = (hipStream_t)stream;
   const zo_model_desc& d = m->d;
-  const bool bf = d.dtype == ZO_DTYPE_BF16;
+  const bool bf = bf16_like(d);
   Packing pk;
   SideGeom sg;
   WsPtrs w;
