@@ -71,3 +71,30 @@ def test_generation_rejections():
     with pytest.raises(zo.ZoError) as ei:
         zo.generate(g2.model, g2.plan(0), None, db2, 16)     # 510 + 15 > max_pos 512
     assert ei.value.code == -2
+
+
+def test_generative_zo_step_matches_oracle():
+    """A whole ZO step on a generative objective (fp32 tiny model): S from zo_generate, c
+    from zo_estimate, the factor update; the oracle follows the GPU's continuations, its
+    c agrees within 1e-2 relative and, given the same c, the updated factors are equal."""
+    need_gpu()
+    wl = workload(TINY_F32, dir_seeds=(3, 8), n_fg=1, n_prompts=2, len_lo=5, len_hi=40)
+    batch = inputs.make_batch(wl)
+    g, o = GpuRun(wl), OracleRun(wl)
+    n_new = 8
+    for t in range(2):
+        out = g.zo.generate(g.model, g.plan(t), g.bank, g.zo.DeviceBatch(batch), n_new)
+        plan_o = ozo.plan_from_workload(wl, t)
+        ref = ozo.generate(TINY_F32, o.W, plan_o, o.bank, batch, n_new, forced=out["tokens"].cpu().numpy())
+        assert np.array_equal(out["tokens"].cpu().numpy(), ref["best_tok"])
+        cg = g.zo.estimate(g.plan(t), out["S"])
+        co = ozo.estimate(plan_o, ref["S"])
+        flush("step %d: c gpu %s oracle %s" % (t, cg, co))
+        assert np.all(np.abs(cg - co) <= 1e-2 * np.abs(co))
+        g.update(t, cg, 1e-2)
+        o.update(t, cg, 1e-2)
+        for slot, e in enumerate(o.bank.entries):
+            if e is None:
+                continue
+            for (layer, kind), U in e.U.items():
+                assert np.array_equal(g.bank.entry(slot, layer, kind).cpu().numpy(), U.astype(np.float32))
