@@ -502,6 +502,16 @@ int tproj_split(const zo_model_desc& d, int64_t n_cols, int64_t k) {
 
 // bytes per activation element (fp8 models: bf16 except the e4m3 linear inputs, which
 // take the same buffers at one byte an element)
+// Decode steps of generation (one row per sequence, no batch invariance to keep): narrow
+// side-input projections in K-slices of two to four 64-deep steps, up to 32 slices; the
+// K loop of the register-staged kernel is latency-bound at these few rows.
+int tproj_split_decode(const zo_model_desc& d, int64_t n_cols, int64_t k) {
+  if (!bf16_like(d) || n_cols == 0 || n_cols > 128) return tproj_split(d, n_cols, k);
+  int s = 32;
+  while (s > 1 && (k % (64 * s) != 0 || k / (64 * s) < 2)) s >>= 1;
+  return s;
+}
+
 size_t act_size(const zo_model_desc& d) { return bf16_like(d) ? 2 : 4; }
 bool split_act(const zo_plan_s& p) { return (p.flags & ZO_PLAN_ACT_SPLIT) != 0; }
 // As columns per row: the widest group.  Every group writes, for a given row, the same
@@ -570,10 +580,13 @@ void carve(const zo_model* m, const zo_plan_s& p, const Packing& pk, const SideG
   w.side_bytes = b.off - side0;
   w.xs = b.take<unsigned char>(S * D * as * x2);
   {
-    int64_t np = 0;
-    for (int g = 0; g < 4; ++g)
+    int64_t np = 0, npd = 0;
+    for (int g = 0; g < 4; ++g) {
       np = std::max(np, (int64_t)tproj_split(d, sg.vt_rows[g], sg.n_in[g] * x3) * sg.vt_rows[g]);
-    w.tp_partial = b.take<float>(std::max<int64_t>(np * M, 1));
+      npd = std::max(npd, (int64_t)tproj_split_decode(d, sg.vt_rows[g], sg.n_in[g]) * sg.vt_rows[g]);
+    }
+    const int64_t n = std::max<int64_t>(np * M, kv_rows > 0 ? npd * std::max(pk.n_phys, 1) : 0);
+    w.tp_partial = b.take<float>(std::max<int64_t>(n, 1));
   }
   const int bn_head = gemm_cfg_bn(GEMM_CFG_HEAD, bf16_like(d));
   const int64_t n_vt = (d.vocab + bn_head - 1) / bn_head;
@@ -693,7 +706,8 @@ int forward(zo_model* m, const zo_plan_s& p, const Packing& pk, const SideGeom& 
     gp.C = w.as; gp.ldc = w.as_ld;
     gp.row_cand = w.row_cand; gp.cand_dir = w.cand_dir; gp.cand_slot = w.cand_slot; gp.cand_scale = w.cand_scale;
     gp.tp_ks = sg.ks_c; gp.tp_rank = sg.r; gp.tp_entries = sg.E; gp.tp_used = sg.nc * sg.r; gp.tp_as_ks = sg.ks;
-    gp.ksplit = tproj_split(d, sg.vt_rows[g], K * x3);
+    gp.ksplit = (gen && gen->decode && !sp) ? tproj_split_decode(d, sg.vt_rows[g], K)
+                                            : tproj_split(d, sg.vt_rows[g], K * x3);
     gp.partial = w.tp_partial;
     gp.a_e4m3 = f8;                        // fp8 models: every layer-linear input is e4m3
     return run_gemm(d, gp, narrow, s);
