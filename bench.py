@@ -29,7 +29,7 @@ PEAK_F32_TFLOPS = 157.3
 PEAK_HBM_GBS = 8000.0
 
 
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "opt13b_gemm_base_traffic.md")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "%s_gemm_base_traffic.md")   # per workload
 GEMM_SOURCE = os.path.join(ROOT, "zeroth_order_fine_amd", "csrc", "gemm.hip")
 
 
@@ -39,7 +39,7 @@ def measured_traffic(workload):
     import hashlib
     import re
     try:
-        text = open(TRAFFIC_FILE).read()
+        text = open(TRAFFIC_FILE % workload).read()
         rec = json.loads(re.search(r"```json\n(.*?)\n```", text, re.S).group(1))
         sha = hashlib.sha256(open(GEMM_SOURCE, "rb").read()).hexdigest()
     except Exception:
