@@ -98,3 +98,21 @@ def test_generative_zo_step_matches_oracle():
                 continue
             for (layer, kind), U in e.U.items():
                 assert np.array_equal(g.bank.entry(slot, layer, kind).cpu().numpy(), U.astype(np.float32))
+
+
+def test_generation_edge_cases():
+    """Foreground-only batch (no candidate: S is zero, tokens as the oracle's under W), one
+    new token (prefill only), and an empty batch."""
+    need_gpu()
+    wl = workload(SMALL_OPT_BF16, n_fg=2, n_prompts=0, len_lo=5, len_hi=40)
+    batch = inputs.make_batch(wl)
+    g, o = GpuRun(wl), OracleRun(wl)
+    for n_new in (1, 5):
+        out = g.zo.generate(g.model, g.plan(0), None, g.zo.DeviceBatch(batch), n_new)
+        tok = out["tokens"].cpu().numpy()
+        ref = ozo.generate(SMALL_OPT_BF16, o.W, ozo.plan_from_workload(wl, 0), None, batch, n_new, forced=tok)
+        assert np.all(out["S"] == 0.0) and tok.shape == (2, n_new)
+        assert np.all(ref["best_logp"] - ref["logp"] <= 2e-2)
+        assert np.max(np.abs(out["logp"].cpu().numpy() - ref["logp"])) <= 2e-2
+    empty = g.zo.generate(g.model, g.plan(0), None, g.zo.DeviceBatch(batch.subset([])), 3)
+    assert empty["n_phys"] == 0 and np.all(empty["S"] == 0.0)
