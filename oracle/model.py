@@ -15,11 +15,12 @@ which is what conventional implementations do (arXiv abstract of
 "Inference-Native Zeroth-Order Optimization": candidate states created by
 mutating model weights vs. factorized side states).
 
-fp8 models (OPT only) are the quantized model: the layer linears hold e4m3
-weights (see oracle.params) and every activation a layer linear reads - the
-two LayerNorm outputs, the attention output and the GELU output - is rounded to
-e4m3 (oracle.params.e4m3_round, no scale) before the product; q, k, v, the
-residual stream, the final norm and the head stay as in bf16 models.
+fp8 models are the quantized model: the layer linears hold e4m3 weights (see
+oracle.params) and every activation a layer linear reads - the two norm outputs,
+the attention output and the GELU (OPT) or SwiGLU (Qwen3) output - is rounded to
+e4m3 (oracle.params.e4m3_round, no scale) before the product; q, k, v (with
+Qwen3's QK-norm and RoPE), the residual stream, the final norm and the head stay
+as in bf16 models.
 
 The architecture facts (pre-LN, learned positions, tied head for OPT;
 RMSNorm, QK-norm, rotate-half RoPE, GQA, SwiGLU, untied head for Qwen3) are
@@ -118,8 +119,8 @@ def layer_forward(cfg, Wl, h, side, dense):
     """One decoder layer on one sequence.  side(kind) -> [(V, B)]."""
     n = h.shape[0]
     hq, hkv, hd = cfg.n_heads, cfg.n_kv_heads, cfg.head_dim
+    qa = e4m3_round if cfg.dtype == "fp8" else (lambda x: x)   # linear inputs of fp8 models
     if cfg.arch == "opt":
-        qa = e4m3_round if cfg.dtype == "fp8" else (lambda x: x)   # linear inputs of fp8 models
         a = qa(layer_norm(h, Wl["ln1_w"], Wl["ln1_b"], cfg.norm_eps))
         q = linear(a, Wl["wq"], Wl["bq"], side("q"), dense).reshape(n, hq, hd)
         k = linear(a, Wl["wk"], Wl["bk"], side("k"), dense).reshape(n, hkv, hd)
@@ -130,7 +131,7 @@ def layer_forward(cfg, Wl, h, side, dense):
         f = qa(gelu(linear(a, Wl["w_fc1"], Wl["b_fc1"], side("fc1"), dense)))
         h = h + linear(f, Wl["w_fc2"], Wl["b_fc2"], side("fc2"), dense)
         return h
-    a = rms_norm(h, Wl["ln1_w"], cfg.norm_eps)
+    a = qa(rms_norm(h, Wl["ln1_w"], cfg.norm_eps))
     q = linear(a, Wl["wq"], None, side("q"), dense).reshape(n, hq, hd)
     k = linear(a, Wl["wk"], None, side("k"), dense).reshape(n, hkv, hd)
     v = linear(a, Wl["wv"], None, side("v"), dense).reshape(n, hkv, hd)
@@ -138,12 +139,12 @@ def layer_forward(cfg, Wl, h, side, dense):
     k = rms_norm(k, Wl["k_norm_w"], cfg.norm_eps)
     pos = np.arange(n)
     q, k = rope(q, pos, cfg.rope_theta), rope(k, pos, cfg.rope_theta)
-    o = causal_attention(q, k, v).reshape(n, hq * hd)
+    o = qa(causal_attention(q, k, v).reshape(n, hq * hd))
     h = h + linear(o, Wl["wo"], None, side("o"), dense)
-    a = rms_norm(h, Wl["ln2_w"], cfg.norm_eps)
+    a = qa(rms_norm(h, Wl["ln2_w"], cfg.norm_eps))
     g = linear(a, Wl["w_gate"], None, side("gate"), dense)
     u = linear(a, Wl["w_up"], None, side("up"), dense)
-    h = h + linear(silu(g) * u, Wl["w_down"], None, side("down"), dense)
+    h = h + linear(qa(silu(g) * u), Wl["w_down"], None, side("down"), dense)
     return h
 
 

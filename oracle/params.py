@@ -8,7 +8,7 @@ seed and the tensor's tag, element index = row-major index:
   norm gains          : 1 + 0.02 * z
 computed in fp64, rounded to fp32 (round to nearest even), and for bf16
 models the matrices are then rounded fp32 -> bf16 (round to nearest even).
-Vectors (biases, norm gains) stay fp32.  fp8 models (OPT only) keep the
+Vectors (biases, norm gains) stay fp32.  fp8 models keep the
 embedding matrices in bf16 and store every layer linear as OCP e4m3 codes of
 w * 2^11 (round to nearest even, saturating at 448): |0.02 z| < 0.14 for every
 stream value (u >= 2^-33 bounds |z| below 6.8), so the fixed power-of-two

@@ -25,6 +25,7 @@ SMALL_QWEN_BF16 = ModelCfg("qwen3", 2, 512, 4, 2, 128, 768, 1200, 1024, "bf16", 
 SMALL_OPT_ODD = ModelCfg("opt", 2, 320, 5, 5, 64, 1280, 1000, 512, "bf16", 1e-5)
 # the fp8-quantized OPT (e4m3 layer linears and linear inputs; d and FFN multiples of 128)
 SMALL_OPT_FP8 = ModelCfg("opt", 2, 256, 4, 4, 64, 512, 1000, 512, "fp8", 1e-5)
+SMALL_QWEN_FP8 = ModelCfg("qwen3", 2, 512, 4, 2, 128, 768, 1200, 1024, "fp8", 1e-6, 1e6)
 SMALL_QWEN_F32 = ModelCfg("qwen3", 2, 128, 4, 2, 32, 256, 300, 1024, "f32", 1e-6, 1e6)
 
 

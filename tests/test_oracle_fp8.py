@@ -11,16 +11,18 @@ oracle/model.py quantization points).
 import dataclasses
 
 import numpy as np
+import pytest
 import torch
 
 from oracle import params, zo
 from oracle.zo import Weights
 from synth import configs, inputs
 
-from .test_oracle_model import OPT_SMALL
+from .test_oracle_model import OPT_SMALL, QWEN_SMALL
 from .test_oracle_zo import _bank_after_updates, _small_wl
 
 OPT_FP8 = dataclasses.replace(OPT_SMALL, dtype="fp8")
+QWEN_FP8 = dataclasses.replace(QWEN_SMALL, dtype="fp8")
 
 
 def _torch_e4m3(x):
@@ -68,25 +70,28 @@ def test_fp8_weights_are_scaled_e4m3_values():
     assert np.array_equal(params.bf16_round(t), t)
 
 
-def test_fp8_factorized_equals_dense_mutation():
-    wl = _small_wl(OPT_FP8, configs.KIND_NAMES_OPT, dirs=(0, 5), n_fg=1)
-    bank = _bank_after_updates(OPT_FP8, wl)
+@pytest.mark.parametrize("cfg", [OPT_FP8, QWEN_FP8], ids=["opt", "qwen3"])
+def test_fp8_factorized_equals_dense_mutation(cfg):
+    kinds = configs.KIND_NAMES_OPT if cfg.arch == "opt" else configs.KIND_NAMES_QWEN3
+    wl = _small_wl(cfg, kinds, dirs=(0, 5), n_fg=1)
+    bank = _bank_after_updates(cfg, wl)
     batch = inputs.make_batch(wl)
-    W = Weights(OPT_FP8, wl.model_seed, cache_layers=True)
+    W = Weights(cfg, wl.model_seed, cache_layers=True)
     plan = zo.plan_from_workload(wl, 2)
-    a = zo.score(OPT_FP8, W, plan, bank, batch)
-    b = zo.score(OPT_FP8, W, plan, bank, batch, dense=True)
+    a = zo.score(cfg, W, plan, bank, batch)
+    b = zo.score(cfg, W, plan, bank, batch, dense=True)
     assert np.allclose(a["seq_logp"], b["seq_logp"], rtol=1e-12, atol=0)
     assert np.ptp(a["S"]) > 0
 
 
-def test_activation_rounding_is_visible_at_the_gpu_bound():
+@pytest.mark.parametrize("which", ["opt", "qwen3"])
+def test_activation_rounding_is_visible_at_the_gpu_bound(which):
     """Rounding the four linear inputs to e4m3 moves the per-sequence sums of the GPU
-    test's model (d = 256, FFN 512, 2 layers, same workload shape) by far more than the
-    6e-2 fp8 parity bound: a kernel that skipped it would fail that test."""
+    tests' models (same workload shape) by far more than the 6e-2 fp8 parity bound: a
+    kernel that skipped it would fail those tests."""
     import dataclasses as dc
-    from tests.gpu_common import SMALL_OPT_FP8, workload
-    cfg_fp8 = SMALL_OPT_FP8
+    from tests.gpu_common import SMALL_OPT_FP8, SMALL_QWEN_FP8, workload
+    cfg_fp8 = SMALL_OPT_FP8 if which == "opt" else SMALL_QWEN_FP8
     cfg_noq = dc.replace(cfg_fp8, dtype="bf16")          # same weights, unrounded inputs
     wl = workload(cfg_fp8, dir_seeds=(3, 8), n_fg=2, n_prompts=3)
     batch = inputs.make_batch(wl)
