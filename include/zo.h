@@ -67,18 +67,19 @@ typedef enum {
 } zo_status;
 
 enum { ZO_ARCH_OPT = 0, ZO_ARCH_QWEN3 = 1 };
-/* ZO_DTYPE_FP8 (OPT only): the fp8-quantized model.  The layer linears (q|k|v, o, fc1,
-   fc2) are stored as OCP e4m3 codes (1 sign, 4 exponent bits with bias 7, 3 mantissa
+/* ZO_DTYPE_FP8: the fp8-quantized model.  The layer linears (q|k|v, o, fc1 | gate|up,
+   fc2 | down) are stored as OCP e4m3 codes (1 sign, 4 exponent bits with bias 7, 3 mantissa
    bits, largest magnitude 448) of w * 2^11, one byte an element; the embeddings are bf16
-   and the vectors fp32.  Every input of a layer linear (both LayerNorm outputs, the
-   attention output, the GELU output) is rounded to e4m3 (nearest even, saturating) and
+   and the vectors fp32.  Every input of a layer linear (both norm outputs, the attention
+   output, the GELU or SwiGLU output) is rounded to e4m3 (nearest even, saturating) and
    the base projections run e4m3 x e4m3 on the matrix cores; q, k, v, the residual
    stream, the final norm and the head are as in bf16 models; the side path keeps bf16
    factors.  A quantized frozen base under unquantized factorized side states is what
    "Inference-Native Zeroth-Order Optimization" has the method inherit from the runtime
    (arXiv abstract: frozen base weights; quantization among what the runtime supplies);
    the e4m3 encoding is the one of "FP8 Formats for Deep Learning", which that page's
-   list of prior work names.  Requires d_model and d_ffn multiples of 128; not with
+   list of prior work names.  Requires d_model, d_ffn and n_heads * head_dim multiples
+   of 128; not with
    ZO_PLAN_ACT_SPLIT; side-input projections of at most 128 columns; zo_bank_fold
    returns ZO_E_STATE (the e4m3 weights stay frozen). */
 enum { ZO_DTYPE_F32 = 0, ZO_DTYPE_BF16 = 1, ZO_DTYPE_FP8 = 2 };

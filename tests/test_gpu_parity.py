@@ -16,8 +16,8 @@ import pytest
 from oracle import zo as ozo
 from synth import configs, inputs
 
-from .gpu_common import (SMALL_OPT_BF16, SMALL_OPT_FP8, SMALL_OPT_ODD, SMALL_QWEN_BF16, SMALL_QWEN_F32, GpuRun,
-                         OracleRun, flush, need_gpu, workload)
+from .gpu_common import (SMALL_OPT_BF16, SMALL_OPT_FP8, SMALL_OPT_ODD, SMALL_QWEN_BF16, SMALL_QWEN_F32, SMALL_QWEN_FP8,
+                         GpuRun, OracleRun, flush, need_gpu, workload)
 
 pytestmark = pytest.mark.gpu
 
@@ -376,16 +376,20 @@ def test_bank_checkpoint_restore_is_bitwise():
 # attention output about 2^-9 / 2^-4, i.e. a few percent, of its elements do, which
 # makes the fp8 difference larger than the bf16 one, and random in sign.  The bound is
 # 3x the bf16 one; leaving the activations unrounded on one side moves the sums by far
-# more (checked on the oracle alone in the CPU tests).
+# more (checked on the oracle alone in the CPU tests).  Qwen3's stack amplifies activation
+# rounding more than OPT's (small bf16 models: about 1e-2 against 2e-3 per sequence; fp8
+# per-token maxima measured 0.062 against 0.032), so its bound is twice OPT's.
 FP8_SEQ_ATOL = 6e-2
+FP8_SEQ_ATOL_QWEN3 = 1.2e-1
 
 
-def test_fp8_model_with_bank_matches_oracle():
-    """fp8 OPT: e4m3 x e4m3 projections with the bf16 side path (two directions, a bank
-    with entries of two windows), ragged rows (128x128 tiles; the 256x256 tiles of large
-    batches give these rows bit for bit, checked below)."""
+@pytest.mark.parametrize("cfg", [SMALL_OPT_FP8, SMALL_QWEN_FP8], ids=["opt", "qwen3"])
+def test_fp8_model_with_bank_matches_oracle(cfg):
+    """fp8 models: e4m3 x e4m3 projections with the bf16 side path (two directions, a bank
+    with entries of two windows), ragged rows; Qwen3: GQA, QK-norm + RoPE on bf16 q|k|v,
+    SwiGLU written as e4m3 from the interleaved gate/up tile."""
     need_gpu()
-    wl = workload(SMALL_OPT_FP8, dir_seeds=(3, 8), n_fg=2, n_prompts=3)
+    wl = workload(cfg, dir_seeds=(3, 8), n_fg=2, n_prompts=3)
     batch = inputs.make_batch(wl)
     g, o = GpuRun(wl), OracleRun(wl)
     c_fixed = [np.array([0.9, -1.7]), np.array([-2.5, 0.4]), np.array([1.1, 0.8])]
@@ -395,14 +399,18 @@ def test_fp8_model_with_bank_matches_oracle():
     flush("fp8 score")
     gs, os_ = g.score(6, batch), o.score(6, batch)
     flush("rows %d" % int(gs["n_rows"]))
-    err = _seq_close(gs, os_, FP8_SEQ_ATOL)
+    bound = FP8_SEQ_ATOL if cfg.arch == "opt" else FP8_SEQ_ATOL_QWEN3
+    err = _seq_close(gs, os_, bound)
     flush("fp8: max per-sequence err %.3g" % err)
     tok = gs["tok_logp"].cpu().numpy()
     first = 0
+    tok_err = []
     for p, (li, c) in enumerate(os_["phys"]):
         ref = os_["tok_logp"][p]
-        assert np.all(np.abs(tok[first:first + len(ref)] - ref) <= FP8_SEQ_ATOL), p
+        tok_err.append(np.max(np.abs(tok[first:first + len(ref)] - ref)))
         first += len(ref)
+    flush("fp8 %s: max per-token err %.3g (per sequence %s)" % (cfg.arch, max(tok_err), np.round(tok_err, 3)))
+    assert max(tok_err) <= bound
     # the probes' differences (what c is made of) agree too
     S_g, S_o = np.asarray(gs["S"]), np.asarray(os_["S"])
     flush("S gpu %s oracle %s" % (S_g, S_o))

@@ -7,7 +7,7 @@ import pytest
 from oracle import params, rng
 from synth import configs
 
-from .gpu_common import SMALL_OPT_FP8, SMALL_QWEN_BF16, flush, need_gpu
+from .gpu_common import SMALL_OPT_FP8, SMALL_QWEN_BF16, SMALL_QWEN_FP8, flush, need_gpu
 
 pytestmark = pytest.mark.gpu
 
@@ -67,14 +67,15 @@ def test_direction_factors_bit_exact():
     model.close()
 
 
-@pytest.mark.parametrize("name", ["tiny", "qwen_small", "opt_fp8"])
+@pytest.mark.parametrize("name", ["tiny", "qwen_small", "opt_fp8", "qwen_fp8"])
 def test_weight_init_bit_exact(name):
     """fp8: every layer linear's e4m3 code equals the oracle's e4m3(w * 2^11) (decoded by
     PyTorch's float8_e4m3fn), the embeddings are bf16 as in bf16 models."""
     need_gpu()
     import torch
     import zeroth_order_fine_amd as zo
-    cfg = {"tiny": configs.CONFIGS["tiny"].model, "qwen_small": SMALL_QWEN_BF16, "opt_fp8": SMALL_OPT_FP8}[name]
+    cfg = {"tiny": configs.CONFIGS["tiny"].model, "qwen_small": SMALL_QWEN_BF16, "opt_fp8": SMALL_OPT_FP8,
+           "qwen_fp8": SMALL_QWEN_FP8}[name]
     model = zo.Model(cfg)
     model.init_weights(7)
     torch.cuda.synchronize()
@@ -88,7 +89,8 @@ def test_weight_init_bit_exact(name):
                 n_fp8 += 1
             ref = params.make_tensor(cfg, 7, slot, pid, shape, init).astype(np.float32)
             assert np.array_equal(got, ref), (slot, pname)
-    assert n_fp8 == (6 * cfg.n_layers if cfg.dtype == "fp8" else 0)   # q, k, v, o, fc1, fc2
+    # q, k, v, o, fc1, fc2 (OPT) or q, k, v, o, gate, up, down (Qwen3)
+    assert n_fp8 == ((6 if cfg.arch == "opt" else 7) * cfg.n_layers if cfg.dtype == "fp8" else 0)
     model.close()
 
 

@@ -100,4 +100,5 @@ def test_activation_rounding_is_visible_at_the_gpu_bound(which):
     a = zo.score(cfg_fp8, W, plan, None, batch)
     b = zo.score(cfg_noq, W, plan, None, batch)
     gap = np.abs(np.asarray(a["seq_logp"]) - np.asarray(b["seq_logp"]))
-    assert gap.max() > 2 * 6e-2, gap.max()          # measured: max 0.20, median 0.012
+    # twice the family's GPU bound (6e-2 OPT, 1.2e-1 Qwen3); measured max 0.20 / 0.66
+    assert gap.max() > 2 * (6e-2 if which == "opt" else 1.2e-1), gap.max()

@@ -538,11 +538,16 @@ __device__ __forceinline__ void epilogue_rows(const GemmParams& p, floatx4_t (&a
 #pragma unroll
       for (int jp = 0; jp < TN / 2; ++jp) {
         if (cb + 2 * jp * 16 >= p.N) continue;                  // N is a multiple of 32 here
-        const floatx4_t g = acc[i][2 * jp], u = acc[i][2 * jp + 1];
+        // (e4m3 main segments sum in units of 2^-11 of the result)
+        constexpr float unit = F8 ? 1.0f / (float)(1 << ZO_FP8_WEIGHT_EXP) : 1.0f;
+        const floatx4_t g = acc[i][2 * jp] * unit, u = acc[i][2 * jp + 1] * unit;
         floatx4_t v;
 #pragma unroll
         for (int q = 0; q < 4; ++q) v[q] = silu_fast(g[q]) * u[q];
-        store_bf16x4(p, (bf16_t*)p.C + (int64_t)r * p.ldc + ob + jp * 16, v);
+        if constexpr (F8)              // the e4m3 input of the down projection
+          store_e4m3x4((e4m3_t*)p.C + (int64_t)r * p.ldc + ob + jp * 16, v);
+        else
+          store_bf16x4(p, (bf16_t*)p.C + (int64_t)r * p.ldc + ob + jp * 16, v);
       }
     }
     return;
@@ -983,7 +988,11 @@ __global__ void proj_reduce_kernel(GemmParams p) {
     };
     if (p.epi == EPI_SWIGLU) {       // packed rows: 16 gate rows, then the 16 matching up rows
       const int g = (c / 16) * 32 + c % 16;
-      ((bf16_t*)p.C)[(int64_t)r * p.ldc + c] = f32_to_bf16(silu_fast(sum(g)) * sum(g + 16));
+      const float v = silu_fast(sum(g)) * sum(g + 16);
+      if (p.a_e4m3)                  // the e4m3 input of the down projection
+        ((e4m3_t*)p.C)[(int64_t)r * p.ldc + c] = (e4m3_t)(f32x4_to_e4m3(v, 0.f, 0.f, 0.f) & 0xffu);
+      else
+        ((bf16_t*)p.C)[(int64_t)r * p.ldc + c] = f32_to_bf16(v);
     } else if (p.epi == EPI_RESID) {
       p.H[(int64_t)r * p.ldh + c] += sum(c);
     } else if (p.epi == EPI_GELU) {
@@ -1040,13 +1049,14 @@ int gemm_bk(bool bf16) { return bf16 ? BK_BF16 : BK_F32; }
 template <int BM, int BN, int WM, int WN>
 hipError_t launch_pipe_epi(const GemmParams& p, hipStream_t s) {
   if (p.a_e4m3 || p.b_e4m3) {
-    // e4m3 x e4m3 main segment (fp8 OPT layers: no SwiGLU, no two-term operands)
+    // e4m3 x e4m3 main segment (fp8 models: no two-term operands)
     if constexpr (BM == 128 && BN == 128) {
       if (!(p.a_e4m3 && p.b_e4m3) || p.kwa || p.kwb || p.kwas || p.c_lo || p.c_f32 || p.K % 128 != 0)
         return hipErrorInvalidValue;
       switch (p.epi) {
         case EPI_STORE: return launch_bf16_pipe<BM, BN, WM, WN, EPI_STORE, true>(p, s);
         case EPI_GELU: return launch_bf16_pipe<BM, BN, WM, WN, EPI_GELU, true>(p, s);
+        case EPI_SWIGLU: return launch_bf16_pipe<BM, BN, WM, WN, EPI_SWIGLU, true>(p, s);
         case EPI_RESID: return launch_bf16_pipe<BM, BN, WM, WN, EPI_RESID, true>(p, s);
         default: break;
       }
@@ -1083,7 +1093,7 @@ hipError_t gemm_launch_bf16(const GemmParams& p, int cfg, hipStream_t s) {
     if (p.ksplit > 1) {
       const bool f8 = p.a_e4m3 && p.b_e4m3;
       if (p.a_e4m3 != p.b_e4m3 || p.kwa || p.kwb || p.kwas || p.c_lo || p.c_f32 || !p.partial ||
-          (p.K / (f8 ? 128 : 64)) % p.ksplit != 0 || (f8 && p.epi == EPI_SWIGLU))
+          (p.K / (f8 ? 128 : 64)) % p.ksplit != 0)
         return hipErrorInvalidValue;
       GemmParams q = p;
       q.epi = EPI_PARTIAL;

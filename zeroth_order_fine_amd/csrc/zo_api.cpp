@@ -137,8 +137,9 @@ int validate_desc(const zo_model_desc* d) {
   ZO_CHECK(is_opt(*d) || (std::isfinite(d->rope_theta) && d->rope_theta > 1.0), ZO_E_INVAL,
            "rope_theta must be > 1");
   ZO_CHECK(is_opt(*d) || d->d_ffn % 16 == 0, ZO_E_INVAL, "Qwen3 d_ffn must be a multiple of 16");
-  ZO_CHECK(d->dtype != ZO_DTYPE_FP8 || (is_opt(*d) && d->d_model % 128 == 0 && d->d_ffn % 128 == 0), ZO_E_INVAL,
-           "fp8 models: OPT only, d_model and d_ffn multiples of 128 (the e4m3 K-step)");
+  ZO_CHECK(d->dtype != ZO_DTYPE_FP8 || (d->d_model % 128 == 0 && d->d_ffn % 128 == 0 &&
+                                        (d->n_heads * d->head_dim) % 128 == 0),
+           ZO_E_INVAL, "fp8 models: d_model, d_ffn and n_heads * head_dim multiples of 128 (the e4m3 K-step)");
   return ZO_OK;
 }
 
