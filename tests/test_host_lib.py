@@ -238,3 +238,28 @@ def test_bank_geometry(zlib):
     assert zlib.zo_bank_entry_offset(h, 0, 1, 0, ctypes.byref(off)) == 0
     assert off.value == (3 * 5120 + 5120 + 20480 + 5120) * 2 * 4
     assert zlib.zo_bank_create(m.h, 1, 2, mask, ctypes.c_void_p(0x3000), n.value - 4, ctypes.byref(h)) == -2
+
+
+def test_fp8_layout_and_validation(zlib):
+    """fp8 models: layer linears one byte an element and reported as ZO_DTYPE_FP8, the
+    embeddings (and Qwen3's head) bf16, vectors fp32; shapes whose e4m3 K-steps would not
+    divide are refused (ZO_E_INVAL)."""
+    import dataclasses
+    from zeroth_order_fine_amd import api
+    from tests.gpu_common import SMALL_OPT_FP8, SMALL_QWEN_FP8
+    off, rows, cols, dt, lay = (ctypes.c_size_t(), ctypes.c_int64(), ctypes.c_int64(), ctypes.c_int32(),
+                                ctypes.c_int32())
+    args = [ctypes.byref(x) for x in (off, rows, cols, dt, lay)]
+    for cfg, w1 in ((SMALL_OPT_FP8, 12), (SMALL_QWEN_FP8, 12)):
+        d = api.model_desc(cfg)
+        assert zlib.zo_weight_locate(ctypes.byref(d), 1, 2, *args) == 0 and dt.value == 2   # wq
+        q_off = off.value
+        assert zlib.zo_weight_locate(ctypes.byref(d), 1, 4, *args) == 0
+        assert off.value == q_off + cfg.n_heads * cfg.head_dim * cfg.d_model     # k follows q, 1 B each
+        assert zlib.zo_weight_locate(ctypes.byref(d), 1, w1, *args) == 0 and dt.value == 2
+        assert zlib.zo_weight_locate(ctypes.byref(d), 0, 0, *args) == 0 and dt.value == 1   # embeddings bf16
+        assert zlib.zo_weight_locate(ctypes.byref(d), 1, 0, *args) == 0 and dt.value == 0   # norm gain fp32
+    n = ctypes.c_size_t()
+    for bad in (dataclasses.replace(SMALL_OPT_FP8, d_ffn=576), dataclasses.replace(SMALL_QWEN_FP8, d_model=320)):
+        d = api.model_desc(bad)
+        assert zlib.zo_weights_size(ctypes.byref(d), ctypes.byref(n)) == -1
