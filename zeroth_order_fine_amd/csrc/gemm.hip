@@ -966,7 +966,8 @@ __global__ void tproj_reduce_kernel(GemmParams p) {
   for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n; e += (int64_t)gridDim.x * blockDim.x) {
     const int r = (int)(e / p.N), c = (int)(e - (int64_t)r * p.N);
     float v = 0.f;
-    for (int z = 0; z < p.ksplit; ++z) v += p.partial[(int64_t)z * n + e];
+#pragma unroll 8
+    for (int z = 0; z < p.ksplit; ++z) v += p.partial[(int64_t)z * n + e];   // loads in flight together, sums in order
     tproj_out<TAct>(p, r, c, v, p.row_cand[r]);
   }
 }
@@ -983,6 +984,7 @@ __global__ void proj_reduce_kernel(GemmParams p) {
     const float unit = p.b_e4m3 ? 1.0f / (float)(1 << ZO_FP8_WEIGHT_EXP) : 1.0f;
     auto sum = [&](int col) {
       float v = 0.f;
+#pragma unroll 8
       for (int z = 0; z < p.ksplit; ++z) v += p.partial[(int64_t)z * mn + (int64_t)r * p.N + col];
       return v * unit + (p.bias ? p.bias[col] : 0.f);
     };
