@@ -89,6 +89,7 @@ OPT_6_7B = ModelCfg("opt", 32, 4096, 32, 32, 128, 16384, 50272, 2048, "bf16", 1e
 # the fp8-quantized OPT-13B (e4m3 layer linears and linear inputs, bf16 embeddings)
 OPT_13B_FP8 = ModelCfg("opt", 40, 5120, 40, 40, 128, 20480, 50272, 2048, "fp8", 1e-5)
 QWEN3_8B = ModelCfg("qwen3", 36, 4096, 32, 8, 128, 12288, 151936, 40960, "bf16", 1e-6, 1e6)
+QWEN3_8B_FP8 = ModelCfg("qwen3", 36, 4096, 32, 8, 128, 12288, 151936, 40960, "fp8", 1e-6, 1e6)
 
 _ALL_OPT = ("q", "k", "v", "o", "fc1", "fc2")
 _ALL_QWEN = ("q", "k", "v", "o", "gate", "up", "down")
@@ -104,6 +105,9 @@ CONFIGS = {
                              (0, 1, 2, 3), _ALL_OPT, scale_inv_sqrt_r=True, act_split=True),
     "qwen3-8b-mixed": Workload("qwen3-8b-mixed", QWEN3_8B, 16, 32, 512, "zipf", "last_label", 4, 1e-3,
                                (0,), _ALL_QWEN, n_fg=32, fg_score_mode="all_next", act_split=True),
+    # the same mixed batch on the fp8-quantized model (e4m3 layer linears and linear inputs)
+    "qwen3-8b-fp8": Workload("qwen3-8b-fp8", QWEN3_8B_FP8, 16, 32, 512, "zipf", "last_label", 4, 1e-3,
+                             (0,), _ALL_QWEN, n_fg=32, fg_score_mode="all_next"),
 }
 
 
