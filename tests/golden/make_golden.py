@@ -6,7 +6,7 @@ C_FIXED and learning rate LR, then scoring at step 1 (so the bank holds a
 non-zero entry, as in a running fine-tuning job).  The oracle scores a sample
 of the physical sequences of the full batch (all of them for opt1.3b and
 opt13b, which also gives S and c per candidate) in fp64 on the bf16-rounded
-weights (the e4m3 weights and e4m3-rounded linear inputs for opt13b-fp8).
+weights (the e4m3 weights and e4m3-rounded linear inputs for the fp8 workloads).
 
     python tests/golden/make_golden.py [workload ...]
 """
@@ -37,10 +37,10 @@ def sample(wl, batch, phys):
     by_len = sorted(probes, key=lambda i: lens[i])
     if wl.name == "opt6.7b-mezo":
         pick = [probes[0]]
-    else:                                          # qwen3 mixed, opt13b fp8: the shortest and longest probe
+    else:                                          # qwen3 mixed (bf16, fp8), opt13b fp8: shortest and longest probe
         pick = [by_len[0], by_len[-1]]
     out = [p for p, (li, c) in enumerate(phys) if li in pick]
-    if wl.name == "qwen3-8b-mixed":
+    if wl.name in ("qwen3-8b-mixed", "qwen3-8b-fp8"):
         fg = [i for i in range(batch.n_seq) if batch.role[i] == 1]
         fg_short = sorted(fg, key=lambda i: lens[i])[:2]
         out += [p for p, (li, c) in enumerate(phys) if li in fg_short]

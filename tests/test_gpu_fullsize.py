@@ -51,10 +51,10 @@ def _run(name, split=None):
     return gold, wl, batch, model, bank, db, out, list(zip(phys_seq, phys_cand)), first
 
 
-def _check(name, gold, wl, out, phys, first, seq_bound, c_gpu=None):
+def _check(name, gold, wl, out, phys, first, seq_bound, c_gpu=None, fg_tok_bound=2e-2, fg_median_bound=None):
     seq = out["seq_logp"].cpu().numpy()
     tok = out["tok_logp"].cpu().numpy()
-    errs = []
+    errs, fg_errs = [], []
     for p, (ls, c), g, gt in zip(gold["phys_index"], gold["phys"], gold["seq_logp"], gold["tok_logp"]):
         assert tuple(phys[p]) == (ls, c)                        # packing agrees with the oracle's
         t = tok[first[p]:first[p + 1]]
@@ -62,7 +62,13 @@ def _check(name, gold, wl, out, phys, first, seq_bound, c_gpu=None):
         if c >= 0:
             errs.append(abs(seq[p] - g))
         else:
-            assert np.max(np.abs(t - np.array(gt))) <= 2e-2, (name, p)
+            d = np.abs(t - np.array(gt))
+            fg_errs.append((p, len(d), float(d.max()), float(np.median(d))))
+    if fg_errs:
+        flush("%s: foreground sequences (index, tokens, max, median |err|): %s" % (name, fg_errs))
+        assert max(e[2] for e in fg_errs) <= fg_tok_bound, (name, fg_errs)
+        if fg_median_bound is not None:
+            assert max(e[3] for e in fg_errs) <= fg_median_bound, (name, fg_errs)
     errs = np.array(errs)
     flush("%s (split %s): %d probe sequences, max per-sequence |err| %.4f, %d above 2e-2" % (
         name, wl.act_split, len(errs), errs.max(), int((errs > 2e-2).sum())))
@@ -133,14 +139,31 @@ def test_full_size_two_term_activations(name):
 FP8_FULL_SEQ_BOUND = 3e-1
 
 
-def test_full_size_fp8_against_oracle():
-    """opt13b-fp8 in the launch configuration bench.py times (e4m3 projections on 128x128
-    tiles, 8680 probe rows): the shortest and the longest probe prompt under both
-    candidates against the oracle's e4m3 model."""
+# Qwen3-8B fp8: at the Qwen3-8B width the fp8 model's GPU-oracle difference is about 10x
+# the bf16 model's at the same depth (measured on 2- and 8-layer cuts: foreground tokens
+# max 0.20 / 0.42, median 0.076 / 0.12 against bf16 0.025 / 0.041 and 0.0075 / 0.015:
+# 4096-wide rows hold more elements near an e4m3 boundary), and both grow with depth.
+# Full depth measured: foreground tokens max 1.08 / 1.29, median 0.26 / 0.27.  Bounds: 2.0
+# per probe sequence and foreground token, 0.5 on a foreground sequence's median token; an
+# indexing fault at these shapes moves log-probs by many nats.
+FP8_FULL_SEQ_BOUND_QWEN3 = 2.0
+FP8_FULL_MEDIAN_BOUND_QWEN3 = 0.5
+
+
+@pytest.mark.parametrize("name", ["opt13b-fp8", "qwen3-8b-fp8"])
+def test_full_size_fp8_against_oracle(name):
+    """The fp8 workloads in the launch configuration bench.py times (e4m3 projections on
+    128x128 tiles): the shortest and the longest probe prompt under every candidate (and,
+    for the Qwen3 mixed batch, the two shortest foreground sequences, every token) against
+    the oracle's e4m3 model."""
     need_gpu()
     import torch
-    gold, wl, batch, model, bank, db, out, phys, first = _run("opt13b-fp8")
-    _check("opt13b-fp8", gold, wl, out, phys, first, FP8_FULL_SEQ_BOUND)
+    gold, wl, batch, model, bank, db, out, phys, first = _run(name)
+    if name == "opt13b-fp8":
+        _check(name, gold, wl, out, phys, first, FP8_FULL_SEQ_BOUND)
+    else:
+        _check(name, gold, wl, out, phys, first, FP8_FULL_SEQ_BOUND_QWEN3, fg_tok_bound=FP8_FULL_SEQ_BOUND_QWEN3,
+               fg_median_bound=FP8_FULL_MEDIAN_BOUND_QWEN3)
     del model, bank, db, out
     gc.collect()
     torch.cuda.empty_cache()
