@@ -23,7 +23,12 @@
  * Conventions for every function:
  *   - returns ZO_OK (0) or a negative zo_status; no exception or abort crosses
  *     the ABI; zo_last_error() gives a message for the calling thread;
- *   - all argument checks run on the host before anything is launched;
+ *   - all argument checks run on the host before anything is launched, except the
+ *     token ids of a batch, which live in device memory: the kernels that read them
+ *     flag an id outside [0, vocab) (and clamp it, so every access stays in bounds), and
+ *     zo_score / zo_generate then return ZO_E_INVAL with their outputs undefined;
+ *   - a plan or bank used with a model must have been made for a model of the same
+ *     architecture, dtype and shapes (ZO_E_STATE otherwise, before any launch);
  *   - "device" pointers are HIP device memory of the model's device; "host"
  *     pointers are ordinary host memory;
  *   - the caller owns every buffer it passes (weights, workspace, bank memory,
@@ -92,9 +97,10 @@ enum { ZO_KIND_Q = 0, ZO_KIND_K = 1, ZO_KIND_V = 2, ZO_KIND_O = 3,
        ZO_KIND_FC1 = 4, ZO_KIND_FC2 = 5, ZO_KIND_GATE = 4, ZO_KIND_UP = 5, ZO_KIND_DOWN = 6 };
 
 /* zo_plan flags */
-#define ZO_PLAN_SCALE_INV_SQRT_R 1u  /* eps_tilde = eps / sqrt(r): MeZO-style factorized probes with
-                                        unit-variance entries of G V^T (arXiv abstract: factorized
-                                        perturbations approach dense Gaussian ZO as rank grows) */
+#define ZO_PLAN_SCALE_INV_SQRT_R 1u  /* z = G V^T / sqrt(r) (eps_tilde = eps / sqrt(r)): MeZO-style
+                                        factorized probes whose z has unit-variance entries (arXiv
+                                        abstract: factorized perturbations approach dense Gaussian ZO as
+                                        rank grows); zo_update then steps along the same z */
 #define ZO_PLAN_ALLOW_ZERO_EPS 2u    /* permit eps == 0 (then S+ == S- exactly); testing only */
 #define ZO_PLAN_ACT_SPLIT 4u         /* bf16 models: feed every projection its activations as the two-term
                                         bf16 expansion hi + lo (about 16 significant bits) against the exact
@@ -221,7 +227,8 @@ int zo_bank_fold(zo_model* m, zo_bank* b, int32_t slot, void* ws_dev, size_t ws_
 typedef struct {
   int32_t n_seq;               /* logical sequences, >= 0 */
   const int32_t* cu_seqlens;   /* host [n_seq + 1], cu[0] = 0, non-decreasing, lengths >= 1 */
-  const int32_t* tokens_dev;   /* device int32 [cu_seqlens[n_seq]], ids in [0, vocab) */
+  const int32_t* tokens_dev;   /* device int32 [cu_seqlens[n_seq]], ids in [0, vocab) (checked on the
+                                  device: ZO_E_INVAL from zo_score / zo_generate otherwise) */
   const int32_t* role;         /* host [n_seq] ZO_ROLE_* */
   const int32_t* score_mode;   /* host [n_seq] ZO_SCORE_* */
 } zo_batch;
@@ -289,7 +296,11 @@ int zo_estimate(const zo_plan_t* p, const double* S_host, const int64_t* n_score
 
 /* ---- zo_update ------------------------------------------------------------------
  * Lazy low-rank update, one launch for every target linear of every layer:
- *   U_{seed_d, floor(t/nu)} <- fp32( U - ((lr / q) * c_d) * G_d(t) )   for each direction d,
+ *   U_{seed_d, floor(t/nu)} <- fp32( U - (((lr / q) * c_d) * sigma) * G_d(t) )   for each direction d,
+ * sigma = 1, or 1/sqrt(r) with ZO_PLAN_SCALE_INV_SQRT_R: the step theta <- theta - (lr/q) sum_d c_d z_d
+ * along the directions z_d = sigma G_d V_d^T that the candidates theta +- eps z_d probed
+ * ("Zeroth-Order Fine-Tuning Was an Inference Workload All Along", section "Why ZO
+ * Fine-Tuning Is Really Scoring": theta <- theta - eta c z);
  * allocating (and zero-initialising) the bank entry of (seed_d, window) if absent;
  * ZO_E_NOMEM if the bank has no free slot.  W is never written. */
 int zo_update(zo_model* m, const zo_plan_t* p, zo_bank* bank, const double* c_host, double lr, void* stream);

@@ -17,7 +17,8 @@ Readings where the pages are silent:
   * candidate (d, s) sees W + sum_j U_j V_j^T + s*eps_tilde*G_d V_d^T, where j
     runs over the bank's entries; a foreground sequence sees W only.
   * the update accumulates into the bank entry keyed (seed_d, floor(t/nu)),
-    U <- U - (eta/q) c_d G_d, with q the number of directions.
+    U <- U - (eta/q) c_d sigma G_d, with q the number of directions and sigma =
+    eps_tilde/eps, so that the step follows the probed direction z_d = sigma G_d V_d^T.
 """
 from dataclasses import dataclass, field
 from typing import Dict, List, Optional, Sequence, Tuple
@@ -314,13 +315,20 @@ def fold(cfg, weights, bank, slot):
 
 
 def update(cfg, plan, bank, c, lr):
-    """U_{seed_d, window} <- fp32(U - ((lr / q) * c_d) * G_d), one entry per direction."""
+    """U_{seed_d, window} <- fp32(U - (((lr / q) * c_d) * sigma) * G_d), one entry per direction.
+
+    The step is theta <- theta - (eta / q) sum_d c_d z_d along the directions the probes
+    used ("Zeroth-Order Fine-Tuning Was an Inference Workload All Along", section "Why ZO
+    Fine-Tuning Is Really Scoring": theta <- theta - eta c z, with c measured along z).  A
+    candidate sits at theta + s eps z_d with z_d = sigma G_d V_d^T (sigma = eps_tilde / eps:
+    1, or 1/sqrt(r) with scale_inv_sqrt_r), so the accumulated factor takes sigma too."""
     q = len(plan.dir_seeds)
     r = plan.rank
+    sigma = 1.0 / np.sqrt(float(r)) if plan.scale_inv_sqrt_r else 1.0
     for d in range(q):
         seed = plan.dir_seeds[d]
         e = bank.find_or_alloc(cfg, seed, plan.window)
-        coef = (lr / float(q)) * float(c[d])
+        coef = ((lr / float(q)) * float(c[d])) * sigma
         for l in range(cfg.n_layers):
             for kind in plan.targets:
                 n_out, _ = cfg.linear_shape(kind)

@@ -185,6 +185,54 @@ def test_empty_and_foreground_only_batches():
     assert ge["n_phys"] == 0 and np.all(ge["S"] == 0.0)
 
 
+def test_token_ids_outside_vocab_rejected():
+    """Token ids are device data, checked by the kernels that read them: a label (the
+    last token of a probe prompt) or a prompt token outside [0, vocab) makes zo_score
+    return ZO_E_INVAL instead of a wrong S; the next call with valid ids is unaffected."""
+    need_gpu()
+    import zeroth_order_fine_amd as zo
+    wl = workload(SMALL_OPT_BF16, n_prompts=3, n_fg=1, fg_score_mode="all_next")
+    batch = inputs.make_batch(wl)
+    g = GpuRun(wl)
+    good = g.score(0, batch)
+    vocab = wl.model.vocab
+    for where, value in (("label", vocab), ("label", -3), ("prompt", vocab + 7), ("foreground", -1)):
+        bad = inputs.Batch([t.copy() for t in batch.tokens], batch.role.copy(), batch.score_mode.copy())
+        if where == "label":
+            bad.tokens[2][-1] = value
+        elif where == "prompt":
+            bad.tokens[3][1] = value
+        else:
+            bad.tokens[0][4] = value
+        flush("bad id %d at %s" % (value, where))
+        with pytest.raises(zo.ZoError) as ei:
+            g.score(0, bad)
+        assert ei.value.code == -1 and "vocab" in str(ei.value)
+    again = g.score(0, batch)
+    assert np.array_equal(again["S"], good["S"])
+
+
+def test_length_one_all_next_foreground_sequence():
+    """A foreground sequence of one token scores no position (ALL_NEXT scores tokens
+    1..n-1): its sum is 0 and it changes no other sequence's result (bitwise)."""
+    need_gpu()
+    wl = workload(SMALL_OPT_BF16, n_prompts=3, n_fg=2, fg_score_mode="all_next", dir_seeds=(4,))
+    batch = inputs.make_batch(wl)
+    g = GpuRun(wl)
+    g.update(0, np.array([0.6]), 1e-2)
+    base = g.score(1, batch)
+    one = inputs.Batch([np.array([17], np.int32)] + list(batch.tokens),
+                       np.concatenate([[inputs.ROLE_FOREGROUND], batch.role]).astype(np.int32),
+                       np.concatenate([[inputs.MODE_ALL_NEXT], batch.score_mode]).astype(np.int32))
+    got = g.score(1, one)
+    assert got["n_phys"] == base["n_phys"] + 1 and got["n_scored"] == base["n_scored"]
+    a = got["seq_logp"].cpu().numpy()
+    b = base["seq_logp"].cpu().numpy()
+    assert a[0] == 0.0
+    assert np.array_equal(a[1:].view(np.uint64), b.view(np.uint64))
+    assert np.array_equal(got["S"], base["S"])
+
+
 def test_high_rank_multi_direction():
     """r = 64, four directions, eight candidates sharing one base pass, loss summed over
     every next-token position, eps / sqrt(r) scaling; bank holding all four entries."""

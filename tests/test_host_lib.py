@@ -263,3 +263,43 @@ def test_fp8_layout_and_validation(zlib):
     for bad in (dataclasses.replace(SMALL_OPT_FP8, d_ffn=576), dataclasses.replace(SMALL_QWEN_FP8, d_model=320)):
         d = api.model_desc(bad)
         assert zlib.zo_weights_size(ctypes.byref(d), ctypes.byref(n)) == -1
+
+
+def test_plan_and_bank_of_another_model_rejected(zlib):
+    """A plan or bank made for one model shape is refused (ZO_E_STATE) by every call that
+    would index the other model's launches with it; the calls return before any launch, so
+    this runs without a GPU (the device pointers are never touched)."""
+    from zeroth_order_fine_amd import api
+    small, big = configs.CONFIGS["opt1.3b"], configs.CONFIGS["opt13b"]
+    ma, mb = _M(zlib, small.model), _M(zlib, big.model)
+    rc, pa = _plan(zlib, ma, small)
+    assert rc == 0
+    rc, pb = _plan(zlib, mb, big)
+    assert rc == 0
+    mask = api.kind_mask(small.model, small.targets)
+    assert mask == api.kind_mask(big.model, big.targets) and small.rank == big.rank
+    n = ctypes.c_size_t()
+    assert zlib.zo_bank_size(ma.h, 2, small.rank, mask, ctypes.byref(n)) == 0
+    bank_a = ctypes.c_void_p()
+    assert zlib.zo_bank_create(ma.h, 2, small.rank, mask, ctypes.c_void_p(0x3000), n.value,
+                               ctypes.byref(bank_a)) == 0
+    batch = inputs.make_batch(small)
+    desc, keep = _batch_desc(batch)
+    x, y, z_, w = ctypes.c_int32(), ctypes.c_int64(), ctypes.c_int64(), ctypes.c_size_t()
+    lay = lambda m, p, b: zlib.zo_batch_layout(m.h, p, b, ctypes.byref(desc), ctypes.byref(x), ctypes.byref(y),
+                                                ctypes.byref(z_), ctypes.byref(w))
+    assert lay(ma, pa, bank_a) == 0
+    assert lay(mb, pa, None) == -6                    # plan of the small model
+    assert lay(mb, pb, bank_a) == -6                  # bank of the small model
+    c = (ctypes.c_double * 1)(0.5)
+    assert zlib.zo_update(mb.h, pb, bank_a, c, 1e-3, None) == -6
+    assert zlib.zo_update(mb.h, pa, bank_a, c, 1e-3, None) == -6
+    S = (ctypes.c_double * 2)()
+    assert zlib.zo_score(mb.h, pb, bank_a, ctypes.byref(desc), ctypes.c_void_p(0x4000), 1 << 40, None, None, S,
+                         None) == -6
+    g = ctypes.c_int32()
+    assert zlib.zo_generate_layout(mb.h, pa, None, ctypes.byref(desc), 4, ctypes.byref(g), ctypes.byref(w)) == -6
+    assert zlib.zo_bank_fold(mb.h, bank_a, 0, ctypes.c_void_p(0x5000), 1 << 40, None) == -6
+    out = ctypes.c_void_p(0x6000)
+    assert zlib.zo_direction(mb.h, pa, 0, 0, 0, 0, out, None) == -6
+    assert b"another model" in zlib.zo_last_error()

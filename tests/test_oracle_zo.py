@@ -257,3 +257,36 @@ def test_fold_rounds_bf16_weights():
     step = np.spacing(np.abs(exact).astype(np.float32)).astype(np.float64) * 2.0 ** 16
     assert np.all(np.abs(got - exact) <= 0.5 * step + np.spacing(np.abs(exact).astype(np.float32)))
     assert not np.array_equal(got, w0)
+
+
+@pytest.mark.parametrize("scaled", [False, True])
+def test_update_follows_the_probed_direction(scaled):
+    """theta <- theta - (eta/q) sum_d c_d z_d with z_d the direction the candidates probed:
+    the + candidate's dense weight is W + eps z_d, so after one update from an empty bank
+    the applied Delta W = U V^T must equal -(eta/q) c_d (W_plus - W) / eps, with or without
+    the 1/sqrt(r) scaling of the MeZO-style factorized probes."""
+    cfg = OPT_SMALL
+    wl = _small_wl(cfg, ("q", "fc1"), rank=4, dirs=(2, 7))
+    plan = zo.plan_from_workload(wl, 0)
+    plan.scale_inv_sqrt_r = scaled
+    c, lr, q = np.array([0.9, -0.4]), 0.3, 2
+    bank = Bank(2, wl.rank, wl.targets)
+    zo.update(cfg, plan, bank, c, lr)
+    for d in range(q):
+        e = [x for x in bank.active() if x.seed == wl.dir_seeds[d]][0]
+        for l in range(cfg.n_layers):
+            for kind in wl.targets:
+                n_out, n_in = cfg.linear_shape(kind)
+                kid = cfg.kind_names.index(kind)
+                V = params.factor(wl.dir_seeds[d], l, kid, 1, 0, n_in, wl.rank)
+                # the probed direction, read off the + candidate's side term (V, s eps~ G)
+                probe = Plan(plan.t, plan.nu, plan.rank, plan.eps, plan.dir_seeds, ((d, 1), (d, -1)),
+                             plan.targets, scaled)
+                (Vp, B), = zo.side_terms(cfg, probe, None, 0)(l, kind)
+                z = (B @ Vp.T) / plan.eps
+                applied = e.U[(l, kind)] @ V.T
+                ref = -(lr / q) * c[d] * z
+                assert np.allclose(applied, ref, rtol=0, atol=1e-6 * np.abs(ref).max())
+                # and z has unit-variance entries exactly when scaled (within sampling error)
+                var = float(np.mean(z * z))
+                assert (abs(var - 1.0) < 0.35) if scaled else (abs(var - wl.rank) < 0.35 * wl.rank)

@@ -197,9 +197,10 @@ struct FoldArgs {                  // W <- round(W + U V^T) of one target linear
 hipError_t launch_fold(const FoldArgs& a, hipStream_t s);
 
 // ---- transformer pieces ------------------------------------------------------
+// token ids outside [0, vocab) are clamped and set *bad (when bad is not null)
 template <typename TW>
 hipError_t launch_embed_t(const TW* E, const TW* P, const int32_t* tokens, const int32_t* row_src,
-                          const int32_t* row_pos, int M, int d, int vocab, float* h, hipStream_t s);
+                          const int32_t* row_pos, int M, int d, int vocab, float* h, int32_t* bad, hipStream_t s);
 template <typename T>
 hipError_t launch_norm(const float* h, const int32_t* rows, int M, int d, const float* w, const float* b,
                        float eps, bool rms, T* out, int64_t ld_out, int lo_off, hipStream_t s);
@@ -236,7 +237,8 @@ hipError_t launch_attention_split(const float* qkv, int ld_qkv, bf16_t* out, int
                                   const int32_t* cu, const int32_t* work, int n_work, int hq, int hkv, int hd,
                                   hipStream_t s);
 hipError_t launch_tproj_reduce(const GemmParams& p, hipStream_t s);
-hipError_t launch_gather_i32(const int32_t* src, const int32_t* idx, int n, int32_t* dst, hipStream_t s);
+hipError_t launch_gather_labels(const int32_t* src, const int32_t* idx, int n, int vocab, int32_t* dst,
+                                int32_t* bad, hipStream_t s);
 hipError_t launch_logp_reduce(const float2* part, int n_tiles, const float* lab_logit, int n_scored,
                               const int32_t* seq_first, int n_phys, double* tok_logp64, float* tok_logp32,
                               double* seq_logp, hipStream_t s);

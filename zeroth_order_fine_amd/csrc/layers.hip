@@ -49,12 +49,17 @@ __device__ __forceinline__ void block_merge_moments(float& n, float& m, float& m
   for (int i = 1; i < nw; ++i) merge_moments(n, m, m2, sh[3 * i], sh[3 * i + 1], sh[3 * i + 2]);
 }
 
+// Token ids live in device memory, so the kernels that read them validate them: an id
+// outside [0, vocab) sets *bad (read back by the host, which then fails the call) and is
+// clamped so that every access stays in bounds.
 template <typename TW>
 __global__ void embed_kernel(const TW* __restrict__ E, const TW* __restrict__ P, const int32_t* __restrict__ tokens,
                              const int32_t* __restrict__ row_src, const int32_t* __restrict__ row_pos, int d,
-                             int vocab, float* __restrict__ h) {
+                             int vocab, float* __restrict__ h, int32_t* __restrict__ bad) {
   const int m = blockIdx.x;
-  const int tok = min(max(tokens[row_src[m]], 0), vocab - 1);   // ids outside the vocabulary are clamped
+  const int raw = tokens[row_src[m]];
+  if ((raw < 0 || raw >= vocab) && threadIdx.x == 0 && bad) *bad = 1;
+  const int tok = min(max(raw, 0), vocab - 1);
   const int pos = row_pos[m];
   const TW* e = E + (int64_t)tok * d;
   const TW* pp = P ? P + (int64_t)pos * d : nullptr;
@@ -218,31 +223,36 @@ __global__ void logp_reduce_kernel(const float2* __restrict__ part, int n_tiles,
   }
 }
 
-__global__ void gather_i32_kernel(const int32_t* __restrict__ src, const int32_t* __restrict__ idx, int n,
-                                  int32_t* __restrict__ dst) {
+// labels of the scored rows: dst[i] = src[idx[i]], validated like the embedding's ids
+__global__ void gather_label_kernel(const int32_t* __restrict__ src, const int32_t* __restrict__ idx, int n,
+                                    int vocab, int32_t* __restrict__ dst, int32_t* __restrict__ bad) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i < n) dst[i] = src[idx[i]];
+  if (i >= n) return;
+  const int v = src[idx[i]];
+  if ((v < 0 || v >= vocab) && bad) *bad = 1;
+  dst[i] = min(max(v, 0), vocab - 1);
 }
 
 }  // namespace
 
-hipError_t launch_gather_i32(const int32_t* src, const int32_t* idx, int n, int32_t* dst, hipStream_t s) {
+hipError_t launch_gather_labels(const int32_t* src, const int32_t* idx, int n, int vocab, int32_t* dst,
+                                int32_t* bad, hipStream_t s) {
   if (n <= 0) return hipSuccess;
-  hipLaunchKernelGGL(gather_i32_kernel, dim3((n + 255) / 256), dim3(256), 0, s, src, idx, n, dst);
+  hipLaunchKernelGGL(gather_label_kernel, dim3((n + 255) / 256), dim3(256), 0, s, src, idx, n, vocab, dst, bad);
   return hipGetLastError();
 }
 
 template <typename TW>
 hipError_t launch_embed_t(const TW* E, const TW* P, const int32_t* tokens, const int32_t* row_src,
-                          const int32_t* row_pos, int M, int d, int vocab, float* h, hipStream_t s) {
+                          const int32_t* row_pos, int M, int d, int vocab, float* h, int32_t* bad, hipStream_t s) {
   if (M <= 0) return hipSuccess;
-  hipLaunchKernelGGL(embed_kernel<TW>, dim3(M), dim3(256), 0, s, E, P, tokens, row_src, row_pos, d, vocab, h);
+  hipLaunchKernelGGL(embed_kernel<TW>, dim3(M), dim3(256), 0, s, E, P, tokens, row_src, row_pos, d, vocab, h, bad);
   return hipGetLastError();
 }
 template hipError_t launch_embed_t<float>(const float*, const float*, const int32_t*, const int32_t*,
-                                          const int32_t*, int, int, int, float*, hipStream_t);
+                                          const int32_t*, int, int, int, float*, int32_t*, hipStream_t);
 template hipError_t launch_embed_t<bf16_t>(const bf16_t*, const bf16_t*, const int32_t*, const int32_t*,
-                                           const int32_t*, int, int, int, float*, hipStream_t);
+                                           const int32_t*, int, int, int, float*, int32_t*, hipStream_t);
 
 template <typename T>
 hipError_t launch_norm(const float* h, const int32_t* rows, int M, int d, const float* w, const float* b,

@@ -277,6 +277,20 @@ int bank_geometry(const zo_model_desc& d, int rank, uint32_t mask, std::vector<i
   return ZO_OK;
 }
 
+// A plan or a bank made for one model describes shapes (kinds, n_out, n_in, layers) that
+// the launches of another model would index with; every call that takes a plan or bank
+// together with a model checks that they were made for the same shapes.
+bool same_shape(const zo_model_desc& a, const zo_model_desc& b) {
+  return a.arch == b.arch && a.dtype == b.dtype && a.n_layers == b.n_layers && a.d_model == b.d_model &&
+         a.n_heads == b.n_heads && a.n_kv_heads == b.n_kv_heads && a.head_dim == b.head_dim && a.d_ffn == b.d_ffn;
+}
+
+int check_objects(const zo_model* m, const zo_plan_s* p, const zo_bank* bank) {
+  ZO_CHECK(!p || same_shape(p->md, m->d), ZO_E_STATE, "plan was made for another model");
+  ZO_CHECK(!bank || same_shape(bank->md, m->d), ZO_E_STATE, "bank was made for another model");
+  return ZO_OK;
+}
+
 // GEMM input groups of a layer: which kinds read the same activations.
 struct Group {
   std::vector<int> kinds;   // kind of each column block of the side input
@@ -411,6 +425,7 @@ struct SideGeom {
 int side_geometry(const zo_model* m, const zo_plan_s& p, const zo_bank* bank, SideGeom& sg) {
   const zo_model_desc& d = m->d;
   sg = SideGeom();
+  if (int rc = check_objects(m, &p, bank)) return rc;
   sg.q = (int)p.seeds.size();
   sg.r = p.rank;
   if (bank) {
@@ -467,6 +482,7 @@ struct WsPtrs {
   int32_t *row_src, *row_pos, *row_cand, *phys_cu, *phys_first, *sc_row, *sc_lab_src, *work, *labels;
   int32_t* cand_dir;
   int32_t* cand_slot;           // computed t slot of the candidate's direction
+  int32_t* bad_ids;             // set by the kernels when a token id lies outside [0, vocab)
   float* cand_scale;
   SideJob* jobs;
   int64_t as_ld;                // As row pitch (elements), the same for every group
@@ -553,6 +569,7 @@ void carve(const zo_model* m, const zo_plan_s& p, const Packing& pk, const SideG
   w.labels = b.take<int32_t>(S);
   w.cand_dir = b.take<int32_t>(nc);
   w.cand_slot = b.take<int32_t>(nc);
+  w.bad_ids = b.take<int32_t>(1);
   w.cand_scale = b.take<float>(nc);
   w.jobs = b.take<SideJob>(std::max(n_side_jobs(d, p, sg), 1));
   const int64_t D = d.d_model, F = d.d_ffn;
@@ -693,10 +710,10 @@ int forward(zo_model* m, const zo_plan_s& p, const Packing& pk, const SideGeom& 
     ProfScope ps(ZO_PROF_NORM, s);
     if (bf)
       ZO_HIP(launch_embed_t<bf16_t>((const bf16_t*)W(Lo.g[G_TOK]), (const bf16_t*)W(Lo.g[G_POS]), tokens,
-                                    w.row_src, w.row_pos, M, D, d.vocab, w.h, s));
+                                    w.row_src, w.row_pos, M, D, d.vocab, w.h, w.bad_ids, s));
     else
       ZO_HIP(launch_embed_t<float>((const float*)W(Lo.g[G_TOK]), (const float*)W(Lo.g[G_POS]), tokens, w.row_src,
-                                   w.row_pos, M, D, d.vocab, w.h, s));
+                                   w.row_pos, M, D, d.vocab, w.h, w.bad_ids, s));
   }
 
   auto tproj = [&](int l, int g, const void* X, int K) -> int {
@@ -835,7 +852,7 @@ int forward(zo_model* m, const zo_plan_s& p, const Packing& pk, const SideGeom& 
       ProfScope ps(ZO_PROF_NORM, s);
       ZO_HIP(launch_norm<T>(w.h, w.sc_row, S, D, Wf(Lo.g[G_FNW]), Wf(Lo.g[G_FNB]), eps, rms, (T*)w.xs,
                             (int64_t)D * x2, sp ? D : 0, s));
-      ZO_HIP(launch_gather_i32(tokens, w.sc_lab_src, S, w.labels, s));
+      ZO_HIP(launch_gather_labels(tokens, w.sc_lab_src, S, d.vocab, w.labels, w.bad_ids, s));
     }
     const TLoc& head = is_opt(d) ? Lo.g[G_TOK] : Lo.g[G_HEAD];
     GemmParams gp = gemm_base(w.xs, (int64_t)D * x2, W(head), D, S, d.vocab, D * x2);
@@ -1157,6 +1174,7 @@ static int prepare_call(zo_model* m, const zo_plan_t* p, const zo_bank* bank, co
   ZO_HIP(h2d(w.sc_row, pk.sc_row.data(), pk.sc_row.size() * 4));
   ZO_HIP(h2d(w.sc_lab_src, pk.sc_lab_src.data(), pk.sc_lab_src.size() * 4));
   ZO_HIP(h2d(w.work, pk.work.data(), pk.work.size() * 4));
+  ZO_HIP(hipMemsetAsync(w.bad_ids, 0, sizeof(int32_t), s));
   std::vector<int32_t>& cslot = keep.cslot;
   cslot.assign(nc, -1);
   for (int c = 0; c < nc && !sg.dslot.empty(); ++c) cslot[c] = sg.dslot[cdir[c]];
@@ -1270,9 +1288,12 @@ int zo_score(zo_model* m, const zo_plan_t* p, const zo_bank* bank, const zo_batc
   prof_stop(ps_red.rec, s);
   ps_red.rec = -1;
   std::vector<double> seq(pk.n_phys);
+  int32_t bad = 0;
   if (pk.n_phys > 0)
     ZO_HIP(hipMemcpyAsync(seq.data(), seq_out, pk.n_phys * sizeof(double), hipMemcpyDeviceToHost, s));
+  ZO_HIP(hipMemcpyAsync(&bad, w.bad_ids, sizeof bad, hipMemcpyDeviceToHost, s));
   ZO_HIP(hipStreamSynchronize(s));
+  ZO_CHECK(!bad, ZO_E_INVAL, "a token id of the batch lies outside [0, vocab)");
   for (int c = 0; c < nc; ++c) S_host[c] = 0.0;
   for (int q = 0; q < pk.n_phys; ++q)
     if (pk.phys_cand[q] >= 0) S_host[pk.phys_cand[q]] += seq[q];
@@ -1386,8 +1407,11 @@ int zo_generate(zo_model* m, const zo_plan_t* p, const zo_bank* bank, const zo_b
     ZO_HIP(launch_greedy_reduce(w.part, w.part_idx, n_tiles, nq, w.gen_tok, tokens_dev, logp_dev, n_new, j, s));
   }
   std::vector<float> lp((size_t)nq * n_new);
+  int32_t bad = 0;
   ZO_HIP(hipMemcpyAsync(lp.data(), logp_dev, lp.size() * sizeof(float), hipMemcpyDeviceToHost, s));
+  ZO_HIP(hipMemcpyAsync(&bad, w.bad_ids, sizeof bad, hipMemcpyDeviceToHost, s));
   ZO_HIP(hipStreamSynchronize(s));
+  ZO_CHECK(!bad, ZO_E_INVAL, "a token id of the batch lies outside [0, vocab)");
   for (int c = 0; c < nc; ++c) S_host[c] = 0.0;
   for (int q = 0; q < nq; ++q)
     if (pk.phys_cand[q] >= 0)
@@ -1430,6 +1454,7 @@ int zo_estimate(const zo_plan_t* p, const double* S_host, const int64_t* n_score
 int zo_update(zo_model* m, const zo_plan_t* p, zo_bank* bank, const double* c_host, double lr, void* stream) {
   ZO_CHECK(m && p && bank && c_host, ZO_E_INVAL, "null argument");
   ZO_CHECK(std::isfinite(lr), ZO_E_INVAL, "lr must be finite");
+  if (int rc = check_objects(m, p, bank)) return rc;
   ZO_CHECK(bank->rank == p->rank && bank->mask == p->mask, ZO_E_STATE, "bank rank/targets differ from the plan's");
   const int q = (int)p->seeds.size();
   for (int dd = 0; dd < q; ++dd) ZO_CHECK(std::isfinite(c_host[dd]), ZO_E_NONFINITE, "c[%d] is not finite", dd);
@@ -1461,13 +1486,16 @@ int zo_update(zo_model* m, const zo_plan_t* p, zo_bank* bank, const double* c_ho
     max_n = std::max(max_n, a.kind_n[i]);
   }
   a.t = p->t;
+  // the step follows the probed direction z_d = sigma G_d V_d^T (sigma = 1, or 1/sqrt(r) with
+  // ZO_PLAN_SCALE_INV_SQRT_R): theta <- theta - (lr / q) sum_d c_d z_d
+  const double sigma = (p->flags & ZO_PLAN_SCALE_INV_SQRT_R) ? 1.0 / std::sqrt((double)p->rank) : 1.0;
   for (int d0 = 0; d0 < q; d0 += ZO_MAX_UPDATE_DIRS) {
     a.n_dirs = std::min(ZO_MAX_UPDATE_DIRS, q - d0);
     for (int i = 0; i < a.n_dirs; ++i) {
       const int dd = d0 + i;
       a.seed[i] = p->seeds[dd];
       a.slot_off[i] = (int64_t)slot[dd] * bank->slot_stride;
-      a.coef[i] = (lr / (double)q) * c_host[dd];
+      a.coef[i] = ((lr / (double)q) * c_host[dd]) * sigma;
       a.fresh[i] = fresh[dd];
     }
     ProfScope ps(ZO_PROF_UPDATE, s);
@@ -1494,11 +1522,7 @@ int zo_bank_fold(zo_model* m, zo_bank* bank, int32_t slot, void* ws_dev, size_t 
   ZO_CHECK(bank->windows[slot] >= 0, ZO_E_STATE, "slot %d holds no entry", slot);
   ZO_CHECK(m->d.dtype != ZO_DTYPE_FP8, ZO_E_STATE,
            "fp8 models keep their e4m3 weights frozen: entries stay in the bank (no fold)");
-  const zo_model_desc& bd = bank->md;
-  ZO_CHECK(bd.arch == m->d.arch && bd.dtype == m->d.dtype && bd.n_layers == m->d.n_layers &&
-               bd.d_model == m->d.d_model && bd.n_heads == m->d.n_heads && bd.n_kv_heads == m->d.n_kv_heads &&
-               bd.head_dim == m->d.head_dim && bd.d_ffn == m->d.d_ffn,
-           ZO_E_STATE, "bank was made for another model");
+  if (int rc = check_objects(m, nullptr, bank)) return rc;
   size_t need = 0;
   int rc = zo_bank_fold_size(m, bank, &need);
   if (rc) return rc;
@@ -1594,6 +1618,7 @@ int zo_normal_fill(uint64_t seed, uint32_t tag, uint64_t tau, int64_t first, int
 int zo_direction(const zo_model* m, const zo_plan_t* p, int32_t dir, int32_t layer, int32_t kind, int32_t which,
                  float* out_dev, void* stream) {
   ZO_CHECK(m && p && out_dev, ZO_E_INVAL, "null argument");
+  if (int rc = check_objects(m, p, nullptr)) return rc;
   ZO_CHECK(dir >= 0 && dir < (int)p->seeds.size(), ZO_E_INVAL, "direction out of range");
   ZO_CHECK(layer >= 0 && layer < m->d.n_layers, ZO_E_INVAL, "layer out of range");
   ZO_CHECK(kind >= 0 && kind < n_kinds_of(m->d), ZO_E_INVAL, "kind out of range");
