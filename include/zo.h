@@ -257,6 +257,19 @@ int zo_pack(const zo_plan_t* p, const zo_batch* b, int32_t* phys_seq, int32_t* p
 int zo_score(zo_model* m, const zo_plan_t* p, const zo_bank* bank, const zo_batch* b, void* ws_dev,
              size_t ws_bytes, double* seq_logp_dev, float* tok_logp_dev, double* S_host, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid allocation): zo_score with the workspace taken from
+ * a scratch array of ZO_NOALLOC_SCRATCH_BYTES that the library holds on each device it
+ * runs on (in the code object, for the life of the process) instead of a caller buffer;
+ * the caller still passes the outputs.  Allocates no device memory.  ZO_E_SHAPE if the
+ * batch's workspace (zo_batch_layout) exceeds the scratch; ZO_E_DEVICE if the scratch
+ * address of the model's device could not be found when the model was created.  Every
+ * call on one device shares that device's scratch: calls that overlap on one device
+ * (other streams or threads) race and must be serialised by the caller.  Returns after
+ * synchronising `stream`, as zo_score. */
+#define ZO_NOALLOC_SCRATCH_BYTES (256u << 20)
+int zo_score_noalloc(zo_model* m, const zo_plan_t* p, const zo_bank* bank, const zo_batch* b, double* seq_logp_dev,
+                     float* tok_logp_dev, double* S_host, void* stream);
 
 /* ---- generation queries --------------------------------------------------
  * "Inference-Native Zeroth-Order Optimization" (arXiv abstract): the candidate-state

@@ -16,6 +16,7 @@ DTYPE = {"f32": 0, "bf16": 1, "fp8": 2}
 KINDS = {"opt": ("q", "k", "v", "o", "fc1", "fc2"), "qwen3": ("q", "k", "v", "o", "gate", "up", "down")}
 PLAN_SCALE_INV_SQRT_R, PLAN_ALLOW_ZERO_EPS, PLAN_ACT_SPLIT = 1, 2, 4
 EST_INV_RANK, EST_MEAN = 1, 2
+NOALLOC_SCRATCH_BYTES = 256 << 20    # ZO_NOALLOC_SCRATCH_BYTES
 ROLE_PROBE, ROLE_FOREGROUND = 0, 1
 SCORE_LAST_LABEL, SCORE_ALL_NEXT = 0, 1
 
@@ -238,6 +239,16 @@ def score(model, plan, bank, db, want_tokens=False):
                             _ptr(seq), _ptr(tok), S, _stream()))
     return dict(S=np.array(list(S)), seq_logp=seq[:n_phys], tok_logp=tok[:n_sc] if tok is not None else None,
                 n_phys=n_phys, n_rows=n_rows, n_scored=n_sc)
+
+
+def score_noalloc(model, plan, bank, db, seq_out, tok_out=None):
+    """zo_score_noalloc: the workspace is the library's own device scratch; the outputs
+    (seq_out fp64 [n_phys], tok_out fp32 [n_scored] or None) are the caller's tensors.
+    Returns the per-candidate sums S (numpy fp64)."""
+    S = (ctypes.c_double * len(plan.candidates))()
+    _check(model.L.zo_score_noalloc(model.h, plan.h, bank.h if bank else None, ctypes.byref(db.desc),
+                                    _ptr(seq_out), _ptr(tok_out), S, _stream()))
+    return np.array(list(S))
 
 
 def generate(model, plan, bank, db, n_new):

@@ -16,14 +16,40 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstring>
+#include <mutex>
 #include <new>
 #include <string>
 #include <deque>
 #include <vector>
 
+// Device scratch of zo_score_noalloc: the workspace of a score call, held in the code
+// object so that the call allocates nothing.  Each device that loads the library holds its
+// own copy for the life of the process.  In host code `scratch` names a host-side stand-in:
+// its device address comes from hipGetSymbolAddress, once per device (scratch_init).
+static __device__ __align__(256) unsigned char scratch[ZO_NOALLOC_SCRATCH_BYTES];
+
 namespace {
 
 thread_local std::string g_err;
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+bool g_scratch_tried[kMaxDevices] = {};
+
+// Looks up the scratch array's address on `device`, which must be the current device;
+// once per device (later calls return the recorded result).
+void* scratch_init(int device) {
+  if (device < 0 || device >= kMaxDevices) return nullptr;
+  std::lock_guard<std::mutex> lk(g_scratch_mu);
+  if (!g_scratch_tried[device]) {
+    g_scratch_tried[device] = true;
+    void* ptr = nullptr;
+    if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) == hipSuccess) g_scratch_ptr[device] = ptr;
+    else (void)hipGetLastError();        // no device here (host-only use): the entry point refuses
+  }
+  return g_scratch_ptr[device];
+}
 
 int fail(int code, const char* fmt, ...) {
   char buf[512];
@@ -915,6 +941,7 @@ int zo_model_create(const zo_model_desc* desc, void* weights_dev, size_t bytes, 
   m->w = (unsigned char*)weights_dev;
   m->w_bytes = bytes;
   if (hipGetDevice(&m->device) != hipSuccess) m->device = 0;
+  (void)scratch_init(m->device);        // the device is current: record its scratch address
   if (!is_opt(*desc)) {
     // RoPE table: inv_freq_i = theta^(-2i/hd); angle = pos * inv_freq_i, in fp64, stored fp32
     const int half = desc->head_dim / 2;
@@ -1298,6 +1325,25 @@ int zo_score(zo_model* m, const zo_plan_t* p, const zo_bank* bank, const zo_batc
   for (int q = 0; q < pk.n_phys; ++q)
     if (pk.phys_cand[q] >= 0) S_host[pk.phys_cand[q]] += seq[q];
   return ZO_OK;
+}
+
+int zo_score_noalloc(zo_model* m, const zo_plan_t* p, const zo_bank* bank, const zo_batch* b,
+                     double* seq_logp_dev, float* tok_logp_dev, double* S_host, void* stream) {
+  ZO_CHECK(m && p && S_host, ZO_E_INVAL, "null argument");
+  size_t need = 0;
+  int rc = zo_batch_layout(m, p, bank, b, nullptr, nullptr, nullptr, &need);
+  if (rc != ZO_OK) return rc;
+  ZO_CHECK(need <= (size_t)ZO_NOALLOC_SCRATCH_BYTES, ZO_E_SHAPE,
+           "batch needs %zu bytes of workspace; the no-allocation scratch holds %zu", need,
+           (size_t)ZO_NOALLOC_SCRATCH_BYTES);
+  void* ws = nullptr;
+  {
+    std::lock_guard<std::mutex> lk(g_scratch_mu);
+    if (m->device >= 0 && m->device < kMaxDevices) ws = g_scratch_ptr[m->device];
+  }
+  ZO_CHECK(ws, ZO_E_DEVICE, "no scratch address for device %d (hipGetSymbolAddress failed at model creation)",
+           m->device);
+  return zo_score(m, p, bank, b, ws, (size_t)ZO_NOALLOC_SCRATCH_BYTES, seq_logp_dev, tok_logp_dev, S_host, stream);
 }
 
 static int check_generate(const zo_model* m, const zo_plan_t* p, const zo_batch* b, int32_t n_new) {
