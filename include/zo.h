@@ -86,7 +86,7 @@ enum { ZO_ARCH_OPT = 0, ZO_ARCH_QWEN3 = 1 };
    list of prior work names.  Requires d_model, d_ffn and n_heads * head_dim multiples
    of 128; not with
    ZO_PLAN_ACT_SPLIT; side-input projections of at most 128 columns; zo_bank_fold
-   returns ZO_E_STATE (the e4m3 weights stay frozen). */
+   requantizes the folded weights to e4m3. */
 enum { ZO_DTYPE_F32 = 0, ZO_DTYPE_BF16 = 1, ZO_DTYPE_FP8 = 2 };
 enum { ZO_ROLE_PROBE = 0, ZO_ROLE_FOREGROUND = 1 };
 enum { ZO_SCORE_LAST_LABEL = 0, ZO_SCORE_ALL_NEXT = 1 };
@@ -205,7 +205,9 @@ int zo_bank_entry_offset(const zo_bank* b, int32_t slot, int32_t layer, int32_t 
  *   W <- round( W + sum_{k=0}^{r-1} U[:, k] V[:, k]^T )
  * with V regenerated from the entry's (seed, window) key, the sum formed in fp64 in k
  * order (products rounded, no fused multiply-add) starting from W, then rounded fp64 ->
- * fp32 -> bf16 (round to nearest even; fp32 models stop at fp32).  This is the commit of a
+ * fp32 -> bf16 (round to nearest even; fp32 models stop at fp32; fp8 models requantize: the
+ * e4m3 code of the fp32 value times 2^11, nearest even, saturating, so that a change
+ * smaller than half an e4m3 step of that weight is lost).  This is the commit of a
  * finished window's low-rank state into the dense weights (section "The System
  * Reorganization": Delta W = U V^T of the lazy update), which keeps the bank from
  * growing by one entry per window.  The only call that writes the weight blob; the
@@ -215,6 +217,16 @@ int zo_bank_entry_offset(const zo_bank* b, int32_t slot, int32_t layer, int32_t 
  * empty or the bank belongs to another model shape. */
 int zo_bank_fold_size(const zo_model* m, const zo_bank* b, size_t* bytes);
 int zo_bank_fold(zo_model* m, zo_bank* b, int32_t slot, void* ws_dev, size_t ws_bytes, void* stream);
+
+/* Bank cap: every entry of a window other than the plan's is frozen (its window is over,
+ * so every probe row still carries it as a rank-r side term, and the side segment of every
+ * projection grows with their count).  zo_bank_cap folds the oldest frozen entries (lowest
+ * window first, then lowest slot) into the weights with zo_bank_fold until at most
+ * max_frozen remain; entries of the plan's window are never folded.  *n_folded (may be
+ * NULL) receives the number folded.  ws_dev: as zo_bank_fold (needed only when something
+ * is folded).  Synchronises `stream` when it folds. */
+int zo_bank_cap(zo_model* m, zo_bank* b, const zo_plan_t* p, int32_t max_frozen, void* ws_dev, size_t ws_bytes,
+                void* stream, int32_t* n_folded);
 
 /* ---- batch and packing --------------------------------------------------------
  * Physical packing order (canonical): foreground sequences in input order, then for

@@ -22,6 +22,14 @@ e4m3 (oracle.params.e4m3_round, no scale) before the product; q, k, v (with
 Qwen3's QK-norm and RoPE), the residual stream, the final norm and the head stay
 as in bf16 models.
 
+Error model for fp8 tolerances (not part of the definition): with
+jitter = (delta, numpy Generator), every value about to be rounded to e4m3 is first
+multiplied by (1 + delta u), u uniform on [-1, 1] per element.  e4m3 rounding is a
+step function, so an implementation whose values before a rounding differ from the
+definition's by a relative delta lands one e4m3 step away wherever the two straddle a
+rounding boundary; running the definition with and without the jitter measures how far
+the log-probs move when that happens (the floor that any such implementation meets).
+
 The architecture facts (pre-LN, learned positions, tied head for OPT;
 RMSNorm, QK-norm, rotate-half RoPE, GQA, SwiGLU, untied head for Qwen3) are
 the public definitions of those families; the pages only name the families.
@@ -115,11 +123,23 @@ def embed(cfg, G, tokens):
     return h.astype(np.float64)
 
 
-def layer_forward(cfg, Wl, h, side, dense):
+def _e4m3_input(jitter):
+    """The rounding of an fp8 model's linear inputs, optionally under the error model."""
+    if jitter is None:
+        return e4m3_round
+    delta, rs = jitter
+
+    def qa(x):
+        x = np.asarray(x, np.float64)
+        return e4m3_round(x * (1.0 + delta * rs.uniform(-1.0, 1.0, size=x.shape)))
+    return qa
+
+
+def layer_forward(cfg, Wl, h, side, dense, jitter=None):
     """One decoder layer on one sequence.  side(kind) -> [(V, B)]."""
     n = h.shape[0]
     hq, hkv, hd = cfg.n_heads, cfg.n_kv_heads, cfg.head_dim
-    qa = e4m3_round if cfg.dtype == "fp8" else (lambda x: x)   # linear inputs of fp8 models
+    qa = _e4m3_input(jitter) if cfg.dtype == "fp8" else (lambda x: x)   # linear inputs of fp8 models
     if cfg.arch == "opt":
         a = qa(layer_norm(h, Wl["ln1_w"], Wl["ln1_b"], cfg.norm_eps))
         q = linear(a, Wl["wq"], Wl["bq"], side("q"), dense).reshape(n, hq, hd)
@@ -193,7 +213,7 @@ def forward_last_logsoftmax(cfg, get_global, get_layer, seqs):
     return [final_logsoftmax(cfg, G, hs[i], len(s["tokens"]) - 1) for i, s in enumerate(seqs)]
 
 
-def forward_logprobs(cfg, get_global, get_layer, seqs, dense=False):
+def forward_logprobs(cfg, get_global, get_layer, seqs, dense=False, jitter=None):
     """Run a list of sequences through the model, layer by layer (so that only
     one layer's weights are resident).  Each seq is a dict with
       tokens    int array
@@ -206,7 +226,7 @@ def forward_logprobs(cfg, get_global, get_layer, seqs, dense=False):
     for l in range(cfg.n_layers):
         Wl = get_layer(l)
         for i, s in enumerate(seqs):
-            hs[i] = layer_forward(cfg, Wl, hs[i], lambda kind, s=s, l=l: s["side"](l, kind), dense)
+            hs[i] = layer_forward(cfg, Wl, hs[i], lambda kind, s=s, l=l: s["side"](l, kind), dense, jitter)
         del Wl
     return [final_logprobs(cfg, G, hs[i], np.asarray(s["positions"], np.int64),
                            np.asarray(s["labels"], np.int64)) for i, s in enumerate(seqs)]

@@ -182,8 +182,10 @@ class Weights:
         return W
 
 
-def score(cfg, weights, plan, bank, batch, dense=False, phys_subset=None):
+def score(cfg, weights, plan, bank, batch, dense=False, phys_subset=None, e4m3_jitter=None):
     """Score every physical sequence (or the given subset of physical indices).
+    e4m3_jitter = (delta, seed): fp8 models only, the error model of oracle.model (values
+    perturbed by a relative delta before their e4m3 rounding), for sizing tolerances.
     Returns dict(phys, seq_logp [n_phys] (nan where not computed),
                  tok_logp {phys index: fp64 array}, S [n_cand] (only when all computed))."""
     plan.validate()
@@ -196,7 +198,11 @@ def score(cfg, weights, plan, bank, batch, dense=False, phys_subset=None):
         pos, lab = scored_positions(toks, int(batch.score_mode[li]))
         seqs.append(dict(tokens=np.asarray(toks, np.int64), side=side_terms(cfg, plan, bank, c),
                          positions=pos, labels=lab))
-    lps = forward_logprobs(cfg, weights.get_global, weights.get_layer, seqs, dense=dense) if seqs else []
+    jitter = None
+    if e4m3_jitter is not None:
+        jitter = (float(e4m3_jitter[0]), np.random.default_rng(int(e4m3_jitter[1])))
+    lps = forward_logprobs(cfg, weights.get_global, weights.get_layer, seqs, dense=dense,
+                           jitter=jitter) if seqs else []
     seq_logp = np.full(len(phys), np.nan)
     tok = {}
     for p, lp in zip(idx, lps):
@@ -289,8 +295,9 @@ def fold(cfg, weights, bank, slot):
     Delta W = U V^T of the lazy update) and free the slot:
         W <- round(W + sum_k U[:, k] V[:, k]^T),
     the sum in fp64 in k order (each product rounded, then added), rounded fp64 -> fp32,
-    then fp32 -> bf16 for bf16 models.  `weights` must cache its layers (the folded values
-    replace the generated ones)."""
+    then fp32 -> bf16 for bf16 models, or for fp8 models fp32 -> the e4m3 value of w * 2^11
+    (nearest even, saturating) times 2^-11, the quantized base requantized.  `weights` must
+    cache its layers (the folded values replace the generated ones)."""
     if not weights.cache_layers:
         raise ValueError("fold needs Weights(cache_layers=True)")
     e = bank.entries[slot]
@@ -309,9 +316,28 @@ def fold(cfg, weights, bank, slot):
             w32 = w.astype(np.float32)
             if cfg.dtype == "bf16":
                 w32 = params.bf16_round(w32)
-            W[WEIGHT_NAME[kind]] = w32.astype(np.float64)
+            if cfg.dtype == "fp8":       # requantized: the e4m3 value of w * 2^11, times 2^-11
+                scale = 2.0 ** params.FP8_WEIGHT_EXP
+                W[WEIGHT_NAME[kind]] = params.e4m3_round(w32.astype(np.float64) * scale) / scale
+            else:
+                W[WEIGHT_NAME[kind]] = w32.astype(np.float64)
     bank.entries[slot] = None
     return bank
+
+
+def cap(cfg, weights, bank, plan, max_frozen):
+    """Keep at most max_frozen frozen entries (entries of windows other than the plan's):
+    fold the oldest ones into the weights, lowest window first, then lowest slot.  The pages
+    commit a finished window's low-rank state as Delta W = U V^T ("Zeroth-Order Fine-Tuning
+    Was an Inference Workload All Along", section "The System Reorganization"); they do not
+    say when, so this bounds how many finished windows stay as side terms.  Returns the
+    number folded."""
+    frozen = sorted((e.window, i) for i, e in enumerate(bank.entries)
+                    if e is not None and e.window != plan.window)
+    n = max(0, len(frozen) - max_frozen)
+    for _, slot in frozen[:n]:
+        fold(cfg, weights, bank, slot)
+    return n
 
 
 def update(cfg, plan, bank, c, lr):

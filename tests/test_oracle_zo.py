@@ -290,3 +290,60 @@ def test_update_follows_the_probed_direction(scaled):
                 # and z has unit-variance entries exactly when scaled (within sampling error)
                 var = float(np.mean(z * z))
                 assert (abs(var - 1.0) < 0.35) if scaled else (abs(var - wl.rank) < 0.35 * wl.rank)
+
+
+def test_fold_requantizes_fp8_weights():
+    """fp8 models: the fold adds U V^T to the dequantized weights and requantizes, i.e. each
+    folded weight is the e4m3 value nearest to (w + sum_k U V^T) * 2^11, times 2^-11; checked
+    against PyTorch's float8_e4m3fn conversion of the fp32 sum."""
+    import dataclasses
+    cfg = dataclasses.replace(OPT_SMALL, dtype="fp8", d_model=128, d_ffn=256, n_heads=4, head_dim=32)
+    wl = _small_wl(cfg, ("q", "fc2"), dirs=(3,))
+    bank = Bank(4, wl.rank, wl.targets)
+    for t in range(2):
+        zo.update(cfg, zo.plan_from_workload(wl, t), bank, np.array([0.02 * (t + 1)]), 0.5)
+    W = Weights(cfg, wl.model_seed, cache_layers=True)
+    w0 = {k: W.get_layer(0)[k].copy() for k in ("wq", "w_fc2")}
+    e = bank.entries[0]
+    zo.fold(cfg, W, bank, 0)
+    for kind, name in (("q", "wq"), ("fc2", "w_fc2")):
+        n_out, n_in = cfg.linear_shape(kind)
+        V = params.factor(3, 0, cfg.kind_names.index(kind), params.rng.FACTOR_V, 0, n_in, wl.rank)
+        exact32 = (w0[name] + e.U[(0, kind)] @ V.T).astype(np.float32)      # another summation order
+        scaled = exact32.astype(np.float64) * 2048.0
+        inside = np.abs(scaled) < 448.0                   # PyTorch's conversion gives NaN beyond the range
+        ref = torch.from_numpy(np.where(inside, scaled, 0.0)).to(torch.float8_e4m3fn).double().numpy() / 2048.0
+        got = W.get_layer(0)[name]
+        # identical except where the two fp32 sums round differently next to an e4m3 midpoint
+        assert np.mean(got[inside] == ref[inside]) > 0.999
+        assert np.all(np.abs(got - ref)[inside] <= np.abs(ref[inside]) / 8 + 2.0 ** -20)
+        assert np.all(got[~inside] == np.sign(scaled[~inside]) * 448.0 / 2048.0)   # saturated
+        assert np.mean(got != w0[name]) > 0.01                                # the update is visible
+
+
+def test_cap_trajectory_crosses_the_cap():
+    """Eight steps with nu = 2 (four windows) and at most one frozen entry: after each update
+    the oldest frozen entries are folded into W.  The frozen count never exceeds the cap, the
+    active window's entry is never folded, and the capped state scores like the uncapped one
+    (every window's entry kept as a side term) up to the fp32 rounding of the folds."""
+    cfg = configs.CONFIGS["tiny"].model
+    wl = configs.CONFIGS["tiny"].with_(nu=2)
+    batch = inputs.make_batch(wl)
+    Wc = Weights(cfg, wl.model_seed, cache_layers=True)
+    Wf = Weights(cfg, wl.model_seed, cache_layers=True)
+    capped, full = Bank(3, wl.rank, wl.targets), Bank(5, wl.rank, wl.targets)
+    folds = []
+    for t in range(8):
+        plan = zo.plan_from_workload(wl, t)
+        c = np.array([1.5 * (-1) ** t + 0.25 * t])
+        zo.update(cfg, plan, capped, c, 1e-2)
+        zo.update(cfg, plan, full, c, 1e-2)
+        folds.append(zo.cap(cfg, Wc, capped, plan, 1))
+        frozen = [e for e in capped.active() if e.window != plan.window]
+        assert len(frozen) <= 1 and any(e.window == plan.window for e in capped.active())
+    assert folds == [0, 0, 0, 0, 1, 0, 1, 0]               # windows 0 and 1 folded at t = 4 and 6
+    plan = zo.plan_from_workload(wl, 7)
+    a = zo.score(cfg, Wc, plan, capped, batch)
+    b = zo.score(cfg, Wf, plan, full, batch)
+    assert np.allclose(a["seq_logp"], b["seq_logp"], rtol=1e-6, atol=0)
+    assert not np.array_equal(Wc.get_layer(0)["wq"], Wf.get_layer(0)["wq"])

@@ -291,6 +291,17 @@ def fold(model, bank, slot):
     _check(model.L.zo_bank_fold(model.h, bank.h, slot, _ptr(ws), n.value, _stream()))
 
 
+def bank_cap(model, bank, plan, max_frozen):
+    """Fold the oldest frozen entries (windows other than the plan's) into the weights until
+    at most max_frozen remain; returns the number folded."""
+    n = ctypes.c_size_t()
+    _check(model.L.zo_bank_fold_size(model.h, bank.h, ctypes.byref(n)))
+    ws = torch.empty(n.value, dtype=torch.uint8, device="cuda")
+    k = ctypes.c_int32()
+    _check(model.L.zo_bank_cap(model.h, bank.h, plan.h, max_frozen, _ptr(ws), n.value, _stream(), ctypes.byref(k)))
+    return k.value
+
+
 def philox_words(seed, tag, tau, first_block, n_blocks):
     L = _lib.load()
     out = torch.empty(max(4 * n_blocks, 1), dtype=torch.int32, device="cuda")

@@ -189,7 +189,7 @@ struct FoldArgs {                  // W <- round(W + U V^T) of one target linear
   int64_t ld;                      // physical row pitch (elements)
   int64_t n_out, n_in;
   int32_t layout;                  // 0 plain, 1 gate / 2 up of a 16-row interleave
-  int32_t bf16;                    // weight storage: 1 bf16, 0 fp32
+  int32_t dtype;                   // weight storage: 0 fp32, 1 bf16, 2 e4m3 codes of w * 2^11
   int32_t r;
   const float* u;                  // [n_out x r]
   const float* v;                  // [n_in x r]

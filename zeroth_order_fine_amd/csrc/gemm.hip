@@ -1009,7 +1009,130 @@ __global__ void proj_reduce_kernel(GemmParams p) {
   }
 }
 
+// ------------------------------------------------------------------------------
+// Side-input projection for few factor columns (rank <= 8, a few t slots): a streaming
+// kernel on the vector units instead of an MFMA tile that is mostly padding.  A workgroup
+// takes R rows; its 256 lanes split each row into 8-element chunks (lane l of wave w takes
+// chunks l + 64 w + 256 i), multiply them with the same chunks of NC used V^T rows
+// (bf16, read through the caches, shared by every row) and sum in fp32; the partial sums
+// are reduced across a wave's lanes (butterfly) and then across the four waves in wave
+// order, so each (row, column) value is formed by the same operations whatever the batch.
+// Column c_j = (j / tp_used) * tp_ks + j % tp_used (kind block, used column of the block);
+// the result goes through tproj_out like the tiled kernel's.  A8: e4m3 activations.
+template <int R, int NC, bool A8>
+__global__ void __launch_bounds__(256)
+side_dot_kernel(GemmParams p, int j0, int n_used) {
+  __shared__ float red[4][R][NC];
+  const int m0 = blockIdx.x * R;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int ncols = min(NC, n_used - j0);            // used columns of this pass
+  const int nch = p.K / 8;
+  int rows[R];
+  bool live = false;
+#pragma unroll
+  for (int i = 0; i < R; ++i) {
+    rows[i] = min(m0 + i, p.M - 1);
+    live |= (m0 + i < p.M) && p.row_cand[rows[i]] >= 0;
+  }
+  if (!live) return;                                   // foreground rows only: nothing to write
+  const bf16_t* vrow[NC];
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    const int j = j0 + min(c, ncols - 1);
+    const int col = (j / p.tp_used) * p.tp_ks + j % p.tp_used;
+    vrow[c] = (const bf16_t*)p.B + (int64_t)col * p.ldb;
+  }
+  float acc[R][NC];
+#pragma unroll
+  for (int i = 0; i < R; ++i)
+#pragma unroll
+    for (int c = 0; c < NC; ++c) acc[i][c] = 0.f;
+  for (int ch = tid; ch < nch; ch += 256) {
+    float v[NC][8];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      const u32x4_t w = *(const u32x4_t*)(vrow[c] + ch * 8);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        v[c][2 * e] = bf16_to_f32((bf16_t)(w[e] & 0xFFFFu));
+        v[c][2 * e + 1] = bf16_to_f32((bf16_t)(w[e] >> 16));
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < R; ++i) {
+      float x[8];
+      if constexpr (A8) {
+        const uint2 b = *(const uint2*)((const e4m3_t*)p.A + (int64_t)rows[i] * p.lda + ch * 8);
+        const u32x4_t w = e4m3x8_to_bf16(b);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          x[2 * e] = bf16_to_f32((bf16_t)(w[e] & 0xFFFFu));
+          x[2 * e + 1] = bf16_to_f32((bf16_t)(w[e] >> 16));
+        }
+      } else {
+        const u32x4_t w = *(const u32x4_t*)((const bf16_t*)p.A + (int64_t)rows[i] * p.lda + ch * 8);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          x[2 * e] = bf16_to_f32((bf16_t)(w[e] & 0xFFFFu));
+          x[2 * e + 1] = bf16_to_f32((bf16_t)(w[e] >> 16));
+        }
+      }
+#pragma unroll
+      for (int c = 0; c < NC; ++c)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) acc[i][c] = fmaf(x[e], v[c][e], acc[i][c]);
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < R; ++i)
+#pragma unroll
+    for (int c = 0; c < NC; ++c) {
+      float a = acc[i][c];
+#pragma unroll
+      for (int sh = 32; sh >= 1; sh >>= 1) a += __shfl_xor(a, sh, 64);
+      if (lane == 0) red[wave][i][c] = a;
+    }
+  __syncthreads();
+  if (tid < R * NC) {
+    const int i = tid / NC, c = tid % NC;
+    const int r = m0 + i;
+    if (r < p.M && c < ncols) {
+      const float t = ((red[0][i][c] + red[1][i][c]) + red[2][i][c]) + red[3][i][c];
+      const int j = j0 + c;
+      tproj_out<bf16_t>(p, r, (j / p.tp_used) * p.tp_ks + j % p.tp_used, t, p.row_cand[r]);
+    }
+  }
+}
+
 }  // namespace
+
+// Used factor columns of a side-input projection (the kind blocks times the used columns
+// of each block) when the streaming kernel serves it, else 0.
+static int side_dot_columns(const GemmParams& p) {
+  if (p.epi != EPI_TPROJ || p.kwa || p.tp_unit || p.b_e4m3 || p.tp_used <= 0 || p.tp_ks <= 0) return 0;
+  if (p.K % 8 != 0 || p.lda % 8 != 0 || p.ldb % 8 != 0 || p.N % p.tp_ks != 0) return 0;
+  // measured at OPT-13B batch 64: two columns (one kind block at r = 2) stream at about the
+  // rate of the tiled kernel without its K-slice reduction; six columns (q|k|v) ran at a
+  // third of it (the per-row reduction of 64 partial sums dominates), so wider sets keep
+  // the tiled kernel
+  const int n = (p.N / p.tp_ks) * p.tp_used;
+  return n <= 2 ? n : 0;
+}
+
+template <int NC>
+static hipError_t launch_side_dot_nc(const GemmParams& p, int j0, int ncols, hipStream_t s) {
+  constexpr int R = 8;
+  const int blocks = (p.M + R - 1) / R;
+  if (p.a_e4m3)
+    hipLaunchKernelGGL((side_dot_kernel<R, NC, true>), dim3(blocks), dim3(256), 0, s, p, j0, ncols);
+  else
+    hipLaunchKernelGGL((side_dot_kernel<R, NC, false>), dim3(blocks), dim3(256), 0, s, p, j0, ncols);
+  return hipGetLastError();
+}
+
+static hipError_t launch_side_dot(const GemmParams& p, int ncols, hipStream_t s) {
+  return launch_side_dot_nc<2>(p, 0, ncols, s);
+}
 
 hipError_t launch_proj_reduce(const GemmParams& p, hipStream_t s) {
   const int64_t n = (int64_t)p.M * (p.epi == EPI_SWIGLU ? p.N / 2 : p.N);
@@ -1114,6 +1237,8 @@ hipError_t gemm_launch_bf16(const GemmParams& p, int cfg, hipStream_t s) {
   }
   if (cfg == GEMM_CFG_NARROW) {
     if (p.b_e4m3 || (p.a_e4m3 && (p.epi != EPI_TPROJ || p.N > 128 || p.kwa))) return hipErrorInvalidValue;
+    // rank <= 8 with a few t slots: the streaming kernel over the used columns only
+    if (const int nc = side_dot_columns(p)) return launch_side_dot(p, nc, s);
     if (p.a_e4m3) {
       // e4m3 activations against the bf16 factor rows: the register-staged tiles, which
       // widen A to bf16 (exactly) on its way to LDS

@@ -269,17 +269,29 @@ __global__ void update_kernel(UpdateArgs a) {
 
 // W <- round(W + sum_k U[:, k] V[:, k]^T) for one target linear: fp64 sum in k order
 // (no contraction), then fp64 -> fp32 -> (bf16) by round to nearest even.
+// value of an OCP e4m3 code (exact: subnormals mant * 2^-9, normals (8 + mant) * 2^(exp - 10))
+__device__ __forceinline__ float e4m3_value(uint32_t c) {
+  const uint32_t e = (c >> 3) & 15u, mant = c & 7u;
+  const float mag = e == 0 ? (float)mant * 0x1p-9f : ldexpf((float)(8u + mant), (int)e - 10);
+  return (c & 0x80u) ? -mag : mag;
+}
+
 __global__ void fold_kernel(FoldArgs a) {
 #pragma clang fp contract(off)
   const int64_t n = a.n_out * a.n_in;
+  constexpr float kUnit = 1.0f / (float)(1 << ZO_FP8_WEIGHT_EXP);
   for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n; e += (int64_t)gridDim.x * blockDim.x) {
     const int64_t i = e / a.n_in, j = e - i * a.n_in;
     const int64_t prow = a.layout ? interleave16_row(i, a.layout) : i;
     const int64_t off = prow * a.ld + j;
-    double acc = a.bf16 ? (double)bf16_to_f32(((const bf16_t*)a.w)[off]) : (double)((const float*)a.w)[off];
+    double acc = a.dtype == 1   ? (double)bf16_to_f32(((const bf16_t*)a.w)[off])
+                 : a.dtype == 2 ? (double)(e4m3_value(((const e4m3_t*)a.w)[off]) * kUnit)
+                                : (double)((const float*)a.w)[off];
     for (int k = 0; k < a.r; ++k) acc = acc + (double)a.u[i * a.r + k] * (double)a.v[j * a.r + k];
     const float f = (float)acc;
-    if (a.bf16) ((bf16_t*)a.w)[off] = f32_to_bf16(f);
+    if (a.dtype == 1) ((bf16_t*)a.w)[off] = f32_to_bf16(f);
+    else if (a.dtype == 2)   // requantize: the e4m3 code of f * 2^11 (nearest even, saturating)
+      ((e4m3_t*)a.w)[off] = (e4m3_t)(f32x4_to_e4m3(f * (float)(1 << ZO_FP8_WEIGHT_EXP), 0.f, 0.f, 0.f) & 0xFFu);
     else ((float*)a.w)[off] = f;
   }
 }

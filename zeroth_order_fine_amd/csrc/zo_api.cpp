@@ -1566,8 +1566,6 @@ int zo_bank_fold(zo_model* m, zo_bank* bank, int32_t slot, void* ws_dev, size_t 
   ZO_CHECK(m && bank, ZO_E_INVAL, "null argument");
   ZO_CHECK(slot >= 0 && slot < bank->n_slots, ZO_E_INVAL, "slot %d out of range", slot);
   ZO_CHECK(bank->windows[slot] >= 0, ZO_E_STATE, "slot %d holds no entry", slot);
-  ZO_CHECK(m->d.dtype != ZO_DTYPE_FP8, ZO_E_STATE,
-           "fp8 models keep their e4m3 weights frozen: entries stay in the bank (no fold)");
   if (int rc = check_objects(m, nullptr, bank)) return rc;
   size_t need = 0;
   int rc = zo_bank_fold_size(m, bank, &need);
@@ -1605,7 +1603,7 @@ int zo_bank_fold(zo_model* m, zo_bank* bank, int32_t slot, void* ws_dev, size_t 
       a.ld = t.cols;
       a.n_out = ks.n_out; a.n_in = ks.n_in;
       a.layout = t.layout;
-      a.bf16 = t.dtype == ZO_DTYPE_BF16;
+      a.dtype = t.dtype == ZO_DTYPE_BF16 ? 1 : t.dtype == ZO_DTYPE_FP8 ? 2 : 0;
       a.r = r;
       a.u = bank->u + (size_t)slot * bank->slot_stride + (size_t)l * bank->layer_stride + bank->kind_off[kk];
       a.v = vptr[vi++];
@@ -1614,6 +1612,32 @@ int zo_bank_fold(zo_model* m, zo_bank* bank, int32_t slot, void* ws_dev, size_t 
   ZO_HIP(hipStreamSynchronize(s));
   bank->windows[slot] = -1;
   bank->seeds[slot] = 0;
+  return ZO_OK;
+}
+
+int zo_bank_cap(zo_model* m, zo_bank* bank, const zo_plan_t* p, int32_t max_frozen, void* ws_dev, size_t ws_bytes,
+                void* stream, int32_t* n_folded) {
+  ZO_CHECK(m && bank && p, ZO_E_INVAL, "null argument");
+  ZO_CHECK(max_frozen >= 0, ZO_E_INVAL, "max_frozen must be >= 0");
+  if (int rc = check_objects(m, p, bank)) return rc;
+  const int64_t win = (int64_t)p->window();
+  // frozen entries (windows other than the plan's), oldest window first, then slot order
+  std::vector<std::pair<int64_t, int>> frozen;
+  for (int s = 0; s < bank->n_slots; ++s)
+    if (bank->windows[s] >= 0 && bank->windows[s] != win) frozen.push_back({bank->windows[s], s});
+  std::sort(frozen.begin(), frozen.end());
+  int folded = 0;
+  if ((int)frozen.size() > max_frozen) {
+    size_t need = 0;
+    int rc = zo_bank_fold_size(m, bank, &need);
+    if (rc) return rc;
+    ZO_CHECK(ws_dev && ws_bytes >= need, ZO_E_SHAPE, "workspace has %zu bytes, needs %zu", ws_bytes, need);
+    for (size_t i = 0; i + max_frozen < frozen.size(); ++i) {
+      if ((rc = zo_bank_fold(m, bank, frozen[i].second, ws_dev, ws_bytes, stream)) != ZO_OK) return rc;
+      ++folded;
+    }
+  }
+  if (n_folded) *n_folded = folded;
   return ZO_OK;
 }
 
