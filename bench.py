@@ -128,11 +128,16 @@ def hbm_bytes_per_step(cfg, wl, rows, scored, n_entries):
     out["attention"] = L * rows * ((nq + 2 * nkv) * qkv_b + nq * ai)
     side = 0
     prep = 0
-    for kinds in group_kinds(cfg):
+    for g, kinds in enumerate(group_kinds(cfg)):
         tk = [k for k in kinds if k in wl.targets]
         if not tk:
             continue
         n_in = cfg.linear_shape(tk[0])[1]
+        # groups 0 and 2 read a norm's output: with one-term activations and at most 16 used
+        # factor columns the norm kernel forms t from the row it holds (no re-read)
+        if g in (0, 2) and cfg.dtype != "f32" and not split and len(kinds) * used <= 16:
+            out["norm"] += len(tk) * used * n_in * 2 + rows * len(tk) * used * a
+            continue
         side += rows * n_in * ai + len(tk) * used * n_in * 2 * (3 if split else 1) + rows * len(tk) * used * a
         for k in tk:
             n_out = cfg.linear_shape(k)[0]
@@ -142,6 +147,36 @@ def hbm_bytes_per_step(cfg, wl, rows, scored, n_entries):
     out["gemm_head"] = cfg.vocab * d * w + scored * d * a + scored * ((cfg.vocab + 127) // 128) * 8
     out["update"] = q * L * sum(cfg.linear_shape(k)[0] * r * 8 for k in wl.targets)
     return out
+
+
+def accuracy_vs_golden(name, wl, model, db):
+    """The timed precision mode against the expected values the oracle wrote for this
+    workload (tests/golden/<workload>_step1.json: one update at step 0 with fixed
+    coefficients, scoring at step 1): per probe sequence |error|, how many exceed the bf16
+    bound 2e-2, and the relative error of c = (L+ - L-)/2eps where the file has S."""
+    import numpy as np
+
+    import zeroth_order_fine_amd as zo
+    path = os.path.join(ROOT, "tests", "golden", "%s_step1.json" % name)
+    if not os.path.exists(path):
+        return None
+    gold = json.load(open(path))
+    bank = zo.Bank(model, 2 * wl.n_dirs, wl.rank, wl.targets)
+    zo.update(model, zo.Plan.from_workload(model, wl, t=0), bank, gold["state"]["c"], gold["state"]["lr"])
+    plan = zo.Plan.from_workload(model, wl, t=1)
+    out = zo.score(model, plan, bank, db)
+    seq = out["seq_logp"].cpu().numpy()
+    err = np.array([abs(seq[p] - g) for p, (li, c), g in zip(gold["phys_index"], gold["phys"], gold["seq_logp"])
+                    if c >= 0])
+    res = {"probe_sequences": int(err.size), "max_seq_err": round(float(err.max()), 5),
+           "mean_seq_err": round(float(err.mean()), 5), "seq_above_2e-2": int((err > 2e-2).sum())}
+    if "c" in gold:
+        c = zo.estimate(plan, out["S"])
+        res["c"] = [round(float(x), 4) for x in c]
+        res["c_oracle"] = [round(float(x), 4) for x in gold["c"]]
+        res["c_rel_err"] = round(float(np.max(np.abs(c - np.array(gold["c"])) / np.abs(np.array(gold["c"])))), 4)
+    del bank
+    return res
 
 
 def describe(wl):
@@ -406,19 +441,27 @@ def main():
                 v["frac_of_measured_copy"] = round(v["achieved"] / pk["copy_gbs"], 4)
     # side-path cost: the projections' time with the side columns vs a plan with no targets
     if wl.targets and not args.no_side_check:
-        n_off = min(args.steps, 3)
+        # scores with and without the side path, alternated so that clock drift between
+        # the two phases does not masquerade as side-path cost
+        n_off = 4
         wl0 = wl.with_(targets=())
-        zo.api.profile_begin()
+        on, off = {}, {}
         for k in range(n_off):
-            zo.score(model, zo.Plan.from_workload(model, wl0, t=0), None, db)
-        torch.cuda.synchronize()
-        p0 = zo.api.profile_end()
-        base_on = prof["gemm_base"][1] / n_bd
-        base_off = p0["gemm_base"][1] / n_off
+            for tgt, plan_ in ((on, zo.Plan.from_workload(model, wl, t=t_next)),
+                               (off, zo.Plan.from_workload(model, wl0, t=0))):
+                zo.api.profile_begin()
+                zo.score(model, plan_, bank if tgt is on else None, db)
+                torch.cuda.synchronize()
+                for cls, (n_, ms_) in zo.api.profile_end().items():
+                    tgt[cls] = tgt.get(cls, 0.0) + ms_ / n_off
+        base_on, base_off = on["gemm_base"], off["gemm_base"]
+        norm_on, norm_off = on["norm"], off["norm"]
+        total = base_on - base_off + norm_on - norm_off + on["gemm_side"] + on["side_prep"]
         line["side_path"] = {
             "gemm_base_ms_with_side": round(base_on, 3), "gemm_base_ms_without": round(base_off, 3),
             "extended_k_overhead": round(base_on / base_off - 1.0, 4),
-            "total_ms_per_step": round(base_on - base_off + (prof["gemm_side"][1] + prof["side_prep"][1]) / n_bd, 3)}
+            "norm_ms_with_side": round(norm_on, 3), "norm_ms_without": round(norm_off, 3),
+            "total_ms_per_step": round(total, 3), "share_of_step": round(total / ms_step, 4)}
     # other states of the same workload, scored after the timed region (score only)
     extra = {}
 
@@ -431,6 +474,23 @@ def main():
         return (time.perf_counter() - a) / n * 1e3
 
     if not args.no_side_check:
+        # bank growth: score time with E frozen entries (windows 0 .. E-1, each a rank-r side
+        # term of every probe row) besides the plan's direction
+        growth = {}
+        for E in (0, 1, 4, 16):
+            bE = zo.Bank(model, E + 2 * wl.n_dirs, wl.rank, wl.targets)
+            for win in range(E):
+                zo.update(model, zo.Plan.from_workload(model, wl, t=win * wl.nu), bE, [0.5] * wl.n_dirs, args.lr)
+            pE = zo.Plan.from_workload(model, wl, t=E * wl.nu)
+            zo.score(model, pE, bE, db)
+            torch.cuda.synchronize()
+            a = time.perf_counter()
+            for k in range(3):
+                zo.score(model, pE, bE, db)
+            torch.cuda.synchronize()
+            growth[str(E)] = round((time.perf_counter() - a) / 3 * 1e3, 3)
+            del bE
+        extra["score_ms_by_frozen_entries"] = growth
         extra["score_ms_steady_bank"] = round(score_ms(bank, db), 3)
         extra["score_ms_empty_bank"] = round(score_ms(None, db), 3)
         if wl.n_fg:
@@ -456,6 +516,10 @@ def main():
             extra["two_term_tokens_per_s"] = round(probe_tokens / (ms2 / 1e3), 1)
             del bank2
         line["other_states"] = extra
+    if not args.no_side_check:
+        acc = accuracy_vs_golden(args.workload, wl, model, db)
+        if acc:
+            line["accuracy_vs_oracle"] = acc
     if not args.no_cpu_baseline:
         line["cpu_baseline"] = cpu_baseline(wl, batch)
     print(json.dumps(line), flush=True)

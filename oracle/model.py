@@ -23,12 +23,14 @@ Qwen3's QK-norm and RoPE), the residual stream, the final norm and the head stay
 as in bf16 models.
 
 Error model for fp8 tolerances (not part of the definition): with
-jitter = (delta, numpy Generator), every value about to be rounded to e4m3 is first
-multiplied by (1 + delta u), u uniform on [-1, 1] per element.  e4m3 rounding is a
-step function, so an implementation whose values before a rounding differ from the
-definition's by a relative delta lands one e4m3 step away wherever the two straddle a
-rounding boundary; running the definition with and without the jitter measures how far
-the log-probs move when that happens (the floor that any such implementation meets).
+jitter = ({site: delta}, numpy Generator), every value about to be rounded to e4m3 at a
+site ("norm": the two norm outputs, "attn": the attention output, "ffn": the GELU or
+SwiGLU output) is first multiplied by (1 + delta u), u uniform on [-1, 1] per element.
+e4m3 rounding is a step function, so an implementation whose values before a rounding
+differ from the definition's by a relative delta lands one e4m3 step away wherever the
+two straddle a rounding boundary, and every later layer sees the difference; running the
+definition with and without the jitter measures how far the log-probs move when that
+happens (the floor that an implementation of that precision meets).
 
 The architecture facts (pre-LN, learned positions, tied head for OPT;
 RMSNorm, QK-norm, rotate-half RoPE, GQA, SwiGLU, untied head for Qwen3) are
@@ -124,14 +126,15 @@ def embed(cfg, G, tokens):
 
 
 def _e4m3_input(jitter):
-    """The rounding of an fp8 model's linear inputs, optionally under the error model."""
+    """The rounding of an fp8 model's linear inputs (qa(x, site)), optionally under the
+    error model."""
     if jitter is None:
-        return e4m3_round
-    delta, rs = jitter
+        return lambda x, site: e4m3_round(x)
+    deltas, rs = jitter
 
-    def qa(x):
+    def qa(x, site):
         x = np.asarray(x, np.float64)
-        return e4m3_round(x * (1.0 + delta * rs.uniform(-1.0, 1.0, size=x.shape)))
+        return e4m3_round(x * (1.0 + deltas[site] * rs.uniform(-1.0, 1.0, size=x.shape)))
     return qa
 
 
@@ -139,19 +142,19 @@ def layer_forward(cfg, Wl, h, side, dense, jitter=None):
     """One decoder layer on one sequence.  side(kind) -> [(V, B)]."""
     n = h.shape[0]
     hq, hkv, hd = cfg.n_heads, cfg.n_kv_heads, cfg.head_dim
-    qa = _e4m3_input(jitter) if cfg.dtype == "fp8" else (lambda x: x)   # linear inputs of fp8 models
+    qa = _e4m3_input(jitter) if cfg.dtype == "fp8" else (lambda x, site: x)   # linear inputs of fp8 models
     if cfg.arch == "opt":
-        a = qa(layer_norm(h, Wl["ln1_w"], Wl["ln1_b"], cfg.norm_eps))
+        a = qa(layer_norm(h, Wl["ln1_w"], Wl["ln1_b"], cfg.norm_eps), "norm")
         q = linear(a, Wl["wq"], Wl["bq"], side("q"), dense).reshape(n, hq, hd)
         k = linear(a, Wl["wk"], Wl["bk"], side("k"), dense).reshape(n, hkv, hd)
         v = linear(a, Wl["wv"], Wl["bv"], side("v"), dense).reshape(n, hkv, hd)
-        o = qa(causal_attention(q, k, v).reshape(n, hq * hd))
+        o = qa(causal_attention(q, k, v).reshape(n, hq * hd), "attn")
         h = h + linear(o, Wl["wo"], Wl["bo"], side("o"), dense)
-        a = qa(layer_norm(h, Wl["ln2_w"], Wl["ln2_b"], cfg.norm_eps))
-        f = qa(gelu(linear(a, Wl["w_fc1"], Wl["b_fc1"], side("fc1"), dense)))
+        a = qa(layer_norm(h, Wl["ln2_w"], Wl["ln2_b"], cfg.norm_eps), "norm")
+        f = qa(gelu(linear(a, Wl["w_fc1"], Wl["b_fc1"], side("fc1"), dense)), "ffn")
         h = h + linear(f, Wl["w_fc2"], Wl["b_fc2"], side("fc2"), dense)
         return h
-    a = qa(rms_norm(h, Wl["ln1_w"], cfg.norm_eps))
+    a = qa(rms_norm(h, Wl["ln1_w"], cfg.norm_eps), "norm")
     q = linear(a, Wl["wq"], None, side("q"), dense).reshape(n, hq, hd)
     k = linear(a, Wl["wk"], None, side("k"), dense).reshape(n, hkv, hd)
     v = linear(a, Wl["wv"], None, side("v"), dense).reshape(n, hkv, hd)
@@ -159,12 +162,12 @@ def layer_forward(cfg, Wl, h, side, dense, jitter=None):
     k = rms_norm(k, Wl["k_norm_w"], cfg.norm_eps)
     pos = np.arange(n)
     q, k = rope(q, pos, cfg.rope_theta), rope(k, pos, cfg.rope_theta)
-    o = qa(causal_attention(q, k, v).reshape(n, hq * hd))
+    o = qa(causal_attention(q, k, v).reshape(n, hq * hd), "attn")
     h = h + linear(o, Wl["wo"], None, side("o"), dense)
-    a = qa(rms_norm(h, Wl["ln2_w"], cfg.norm_eps))
+    a = qa(rms_norm(h, Wl["ln2_w"], cfg.norm_eps), "norm")
     g = linear(a, Wl["w_gate"], None, side("gate"), dense)
     u = linear(a, Wl["w_up"], None, side("up"), dense)
-    h = h + linear(qa(silu(g) * u), Wl["w_down"], None, side("down"), dense)
+    h = h + linear(qa(silu(g) * u, "ffn"), Wl["w_down"], None, side("down"), dense)
     return h
 
 

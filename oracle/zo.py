@@ -184,8 +184,8 @@ class Weights:
 
 def score(cfg, weights, plan, bank, batch, dense=False, phys_subset=None, e4m3_jitter=None):
     """Score every physical sequence (or the given subset of physical indices).
-    e4m3_jitter = (delta, seed): fp8 models only, the error model of oracle.model (values
-    perturbed by a relative delta before their e4m3 rounding), for sizing tolerances.
+    e4m3_jitter = ({site: delta}, seed): fp8 models only, the error model of oracle.model
+    (values perturbed by a relative delta before their e4m3 rounding), for sizing tolerances.
     Returns dict(phys, seq_logp [n_phys] (nan where not computed),
                  tok_logp {phys index: fp64 array}, S [n_cand] (only when all computed))."""
     plan.validate()
@@ -200,7 +200,7 @@ def score(cfg, weights, plan, bank, batch, dense=False, phys_subset=None, e4m3_j
                          positions=pos, labels=lab))
     jitter = None
     if e4m3_jitter is not None:
-        jitter = (float(e4m3_jitter[0]), np.random.default_rng(int(e4m3_jitter[1])))
+        jitter = ({k: float(v) for k, v in e4m3_jitter[0].items()}, np.random.default_rng(int(e4m3_jitter[1])))
     lps = forward_logprobs(cfg, weights.get_global, weights.get_layer, seqs, dense=dense,
                            jitter=jitter) if seqs else []
     seq_logp = np.full(len(phys), np.nan)

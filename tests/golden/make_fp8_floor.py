@@ -1,17 +1,20 @@
 """Tolerances of the fp8 parity tests, derived from the oracle alone, and the expected
 values of the full-width layer cuts.
 
-fp8 models round every linear input to e4m3, a step function.  The kernels compute the
-values being rounded in fp32 from bf16 q, k, v and bf16 attention probabilities, so
-those values differ from the fp64 definition by up to a relative 2^-9 (the bf16 step),
-and wherever the two straddle an e4m3 rounding boundary the rounded values are one e4m3
-step (1/16 to 1/8 relative) apart.  How far that moves a log-prob depends on the model
-and the sequence, not on the kernels, so it is measured on the oracle: the same forward
-with every pre-rounding value multiplied by (1 + delta u), u uniform on [-1, 1]
-(oracle.model's error model), delta = 2^-9, for SEEDS seeds.  The floor of a case is the
-largest change of a probe sequence's sum (and of a foreground token's log-prob) over the
-seeds; the bound a test applies is FACTOR times the floor, and never below the bf16 bound
-2e-2 (the head and the side path run in bf16 as in bf16 models).
+fp8 models round every linear input to e4m3, a step function.  Wherever the kernels'
+value before a rounding and the fp64 definition's straddle an e4m3 rounding boundary,
+the rounded values are one e4m3 step (1/16 to 1/8 relative) apart, and every later layer
+sees the difference.  How far that moves a log-prob depends on the model and the
+sequence, not on the kernels, so it is measured on the oracle: the same forward with every
+pre-rounding value multiplied by (1 + delta u), u uniform on [-1, 1] (oracle.model's error
+model), with delta the precision the kernels form that value in:
+  attention output   2^-8   (bf16 q, k, v and probabilities: a few bf16 roundings, 2^-9 each)
+  norm outputs, GELU / SwiGLU outputs   2^-20   (fp32 arithmetic on an fp32 residual or on
+                     fp32 sums of exact e4m3 products)
+for SEEDS seeds.  The floor of a case is the largest change of a probe sequence's sum (and
+of a foreground token's log-prob) over the seeds; the bound a test applies is FACTOR times
+the floor, and never below the bf16 bound 2e-2 (the head and the side path run in bf16 as
+in bf16 models).
 
 Cases (each written to fp8floor_<case>.json):
   opt-small-fp8, qwen3-small-fp8  the small fp8 models of tests/test_gpu_parity.py
@@ -38,8 +41,9 @@ sys.path.insert(0, ROOT)
 from oracle import zo as ozo          # noqa: E402
 from synth import configs, inputs     # noqa: E402
 
-DELTA = 2.0 ** -9
+DELTAS = {"attn": 2.0 ** -8, "norm": 2.0 ** -20, "ffn": 2.0 ** -20}
 SEEDS = (1, 2, 3)
+SEEDS_FULL = (1, 2)         # the full-depth workloads (each seed is a whole oracle run)
 FACTOR = 2.0
 BF16_BOUND = 2e-2
 LR = 1e-3
@@ -122,8 +126,9 @@ def make(case):
     if cfg.dtype == "fp8":
         floor_seq = np.zeros(len(idx))
         floor_tok = np.zeros(len(idx))
-        for seed in SEEDS:
-            j = ozo.score(cfg, W, plan, bank, batch, phys_subset=idx, e4m3_jitter=(DELTA, seed))
+        seeds = SEEDS_FULL if sample == "golden" else SEEDS
+        for seed in seeds:
+            j = ozo.score(cfg, W, plan, bank, batch, phys_subset=idx, e4m3_jitter=(DELTAS, seed))
             for i, p in enumerate(idx):
                 floor_seq[i] = max(floor_seq[i], abs(j["seq_logp"][p] - plain_seq[p]))
                 floor_tok[i] = max(floor_tok[i], float(np.max(np.abs(j["tok_logp"][p] - plain_tok[p]))))
@@ -131,7 +136,7 @@ def make(case):
         probe = np.array([phys[p][1] >= 0 for p in idx])
         fs = float(floor_seq[probe].max())
         ft = float(floor_tok[~probe].max()) if (~probe).any() else 0.0
-        rec.update({"delta": DELTA, "seeds": list(SEEDS), "factor": FACTOR,
+        rec.update({"deltas": DELTAS, "seeds": list(seeds), "factor": FACTOR,
                     "floor_seq": floor_seq.tolist(), "floor_tok": floor_tok.tolist(),
                     "floor_seq_max": fs, "floor_tok_max": ft,
                     "bound_seq": max(BF16_BOUND, FACTOR * fs), "bound_tok": max(BF16_BOUND, FACTOR * ft)})

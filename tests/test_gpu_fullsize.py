@@ -129,25 +129,13 @@ def test_full_size_two_term_activations(name):
     torch.cuda.empty_cache()
 
 
-# fp8 OPT-13B: see the fp8 bound of tests/test_gpu_parity.py.  Over 40 layers the kernels'
-# residual stream drifts from the oracle's (fp32 and bf16 against fp64), so more and more
-# linear inputs land on the other side of an e4m3 rounding boundary (one e4m3 step, 1/16
-# to 1/8 relative, each).  Bound: the small fp8 model's measured 0.023 grown by the factor
-# the bf16 difference grows from the small model to OPT-13B (about 0.002 to 0.026, 13x):
-# 0.3.  Measured 0.033 / 0.050 / 0.036 / 0.159.  An indexing or tiling fault at these
-# shapes moves a log-prob by units, not tenths.
-FP8_FULL_SEQ_BOUND = 3e-1
-
-
-# Qwen3-8B fp8: at the Qwen3-8B width the fp8 model's GPU-oracle difference is about 10x
-# the bf16 model's at the same depth (measured on 2- and 8-layer cuts: foreground tokens
-# max 0.20 / 0.42, median 0.076 / 0.12 against bf16 0.025 / 0.041 and 0.0075 / 0.015:
-# 4096-wide rows hold more elements near an e4m3 boundary), and both grow with depth.
-# Full depth measured: foreground tokens max 1.08 / 1.29, median 0.26 / 0.27.  Bounds: 2.0
-# per probe sequence and foreground token, 0.5 on a foreground sequence's median token; an
-# indexing fault at these shapes moves log-probs by many nats.
-FP8_FULL_SEQ_BOUND_QWEN3 = 2.0
-FP8_FULL_MEDIAN_BOUND_QWEN3 = 0.5
+# fp8 workloads: the bounds are written by tests/golden/make_fp8_floor.py from the oracle
+# alone (fp8floor_<workload>.json: the oracle's own log-probs perturbed by a relative 2^-9
+# before every e4m3 rounding, three seeds, times two, never below 2e-2) - see
+# tests/test_gpu_parity.py fp8_bounds.
+def _floor(case):
+    with open(os.path.join(GOLDEN, "fp8floor_%s.json" % case)) as f:
+        return json.load(f)
 
 
 @pytest.mark.parametrize("name", ["opt13b-fp8", "qwen3-8b-fp8"])
@@ -158,12 +146,68 @@ def test_full_size_fp8_against_oracle(name):
     the oracle's e4m3 model."""
     need_gpu()
     import torch
+    rec = _floor(name)
     gold, wl, batch, model, bank, db, out, phys, first = _run(name)
-    if name == "opt13b-fp8":
-        _check(name, gold, wl, out, phys, first, FP8_FULL_SEQ_BOUND)
-    else:
-        _check(name, gold, wl, out, phys, first, FP8_FULL_SEQ_BOUND_QWEN3, fg_tok_bound=FP8_FULL_SEQ_BOUND_QWEN3,
-               fg_median_bound=FP8_FULL_MEDIAN_BOUND_QWEN3)
+    assert rec["phys_index"] == gold["phys_index"] and np.allclose(rec["seq_logp"], gold["seq_logp"])
+    flush("%s: bounds per sequence %.3g, per foreground token %.3g (oracle floors %.3g / %.3g)" % (
+        name, rec["bound_seq"], rec["bound_tok"], rec["floor_seq_max"], rec["floor_tok_max"]))
+    _check(name, gold, wl, out, phys, first, rec["bound_seq"], fg_tok_bound=rec["bound_tok"])
+    del model, bank, db, out
+    gc.collect()
+    torch.cuda.empty_cache()
+
+
+CUT_BASE = {"opt13b-fp8": "opt13b-fp8", "qwen3-8b-fp8": "qwen3-8b-fp8", "opt13b": "opt13b",
+            "qwen3-8b": "qwen3-8b-mixed"}
+
+
+@pytest.mark.parametrize("case,split", [("opt13b-fp8-L1", False), ("opt13b-fp8-L2", False),
+                                        ("qwen3-8b-fp8-L1", False), ("qwen3-8b-fp8-L2", False),
+                                        ("opt13b-L2", False), ("opt13b-L2", True),
+                                        ("qwen3-8b-L2", False), ("qwen3-8b-L2", True)])
+def test_full_width_layer_cuts(case, split):
+    """The first one or two layers of the OPT-13B and Qwen3-8B shapes at full width (same
+    embeddings, head and batch as the full workloads, whole batch in one zo_score call)
+    against tests/golden/fp8floor_<case>.json (oracle only): the first eight probe prompts
+    under both candidates and the two shortest foreground sequences.  bf16: every probe
+    sequence within 2e-2 (two-term activations: foreground tokens too); fp8: the bounds
+    derived from the oracle's floor for the same cut."""
+    need_gpu()
+    import dataclasses
+    import torch
+    import zeroth_order_fine_amd as zo
+    rec = _floor(case)
+    base, layers = case.rsplit("-L", 1)
+    wl0 = configs.CONFIGS[CUT_BASE[base]]
+    wl = wl0.with_(model=dataclasses.replace(wl0.model, n_layers=int(layers)), act_split=split)
+    batch = inputs.make_batch(wl)
+    flush("cut %s (split %s): init" % (case, split))
+    model = zo.Model(wl.model)
+    model.init_weights(wl.model_seed)
+    bank = zo.Bank(model, 2 * wl.n_dirs, wl.rank, wl.targets)
+    db = zo.DeviceBatch(batch)
+    zo.update(model, zo.Plan.from_workload(model, wl, t=0), bank, [2.5, -1.75, 0.5, -3.0][:wl.n_dirs], 1e-3)
+    out = zo.score(model, zo.Plan.from_workload(model, wl, t=1), bank, db, want_tokens=True)
+    phys_seq, phys_cand, first = zo.pack(model, zo.Plan.from_workload(model, wl, t=1), db)
+    phys = list(zip(phys_seq, phys_cand))
+    fp8 = wl.model.dtype == "fp8"
+    bseq = rec["bound_seq"] if fp8 else 2e-2
+    btok = rec["bound_tok"] if fp8 else (2e-2 if split else None)
+    seq = out["seq_logp"].cpu().numpy()
+    tok = out["tok_logp"].cpu().numpy()
+    perr, ferr = [], []
+    for p, (ls, c), g, gt in zip(rec["phys_index"], rec["phys"], rec["seq_logp"], rec["tok_logp"]):
+        assert tuple(phys[p]) == (ls, c)
+        if c >= 0:
+            perr.append(abs(seq[p] - g))
+        else:
+            ferr.append(float(np.max(np.abs(tok[first[p]:first[p + 1]] - np.array(gt)))))
+    flush("cut %s (split %s): probe sequences max |err| %.4f (bound %.3g), foreground tokens max %s (bound %s)%s" % (
+        case, split, max(perr), bseq, ["%.4f" % e for e in ferr], btok,
+        " oracle floors %.3g / %.3g" % (rec["floor_seq_max"], rec["floor_tok_max"]) if fp8 else ""))
+    assert max(perr) <= bseq
+    if btok is not None and ferr:
+        assert max(ferr) <= btok
     del model, bank, db, out
     gc.collect()
     torch.cuda.empty_cache()

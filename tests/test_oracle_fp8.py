@@ -106,3 +106,19 @@ def test_activation_rounding_is_visible_at_the_gpu_bound(which):
         bound = json.load(f)["bound_seq"]
     # twice the derived bound (0.059 OPT, 0.119 Qwen3); measured max 0.20 / 0.66
     assert gap.max() > 2 * bound, (gap.max(), bound)
+
+
+def test_error_model_is_off_by_default_and_exact_at_zero():
+    """The tolerance error model (oracle.model jitter) changes nothing at delta = 0 and
+    moves the sums once deltas reach e4m3-boundary distances (pinned: it is the knob the
+    fp8 bounds are measured with)."""
+    from tests.gpu_common import SMALL_OPT_FP8, workload
+    wl = workload(SMALL_OPT_FP8, dir_seeds=(3,), n_prompts=2)
+    batch = inputs.make_batch(wl)
+    W = Weights(SMALL_OPT_FP8, wl.model_seed, cache_layers=True)
+    plan = zo.plan_from_workload(wl, 0)
+    a = zo.score(SMALL_OPT_FP8, W, plan, None, batch)
+    z = zo.score(SMALL_OPT_FP8, W, plan, None, batch, e4m3_jitter=({"attn": 0.0, "norm": 0.0, "ffn": 0.0}, 1))
+    assert np.array_equal(a["seq_logp"], z["seq_logp"])
+    j = zo.score(SMALL_OPT_FP8, W, plan, None, batch, e4m3_jitter=({"attn": 2.0 ** -8, "norm": 0.0, "ffn": 0.0}, 1))
+    assert not np.array_equal(a["seq_logp"], j["seq_logp"])

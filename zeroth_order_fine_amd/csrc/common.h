@@ -135,6 +135,49 @@ int gemm_cfg_bm(int cfg, bool bf16);
 int gemm_bk(bool bf16);
 int gemm_cfg_bk(int cfg, bool bf16);
 
+// ---- side input t: the As columns a row's candidate state needs -----------------
+// Shared by the side-input projections (gemm.hip) and the norm kernel that forms t for the
+// projections reading its output (layers.hip).
+template <typename TAct>
+__device__ __forceinline__ void store_tproj(const GemmParams& p, int r, int c, float v);
+
+// Side input of row r from computed column c = x.V (kind block c / tp_ks, computed
+// slot (c % tp_ks) / r): a bank entry's slot goes to the entry's As block; the slot
+// of the row's own direction also goes, times s * eps~, to that direction's As
+// block.  Nothing else is written (As is zero-filled once per call; foreground rows
+// and other directions keep zeros).
+template <typename TAct>
+__device__ __forceinline__ void tproj_out(const GemmParams& p, int r, int c, float v, int cand) {
+  if (cand < 0) return;
+  const int kb = c / p.tp_ks, w = c - kb * p.tp_ks;
+  if (w >= p.tp_used) return;
+  const int slot = w / p.tp_rank, k = w - slot * p.tp_rank;
+  const int base = kb * p.tp_as_ks + k;
+  if (slot < p.tp_entries) store_tproj<TAct>(p, r, base + slot * p.tp_rank, v);
+  if (slot == p.cand_slot[cand])
+    store_tproj<TAct>(p, r, base + (p.tp_entries + p.cand_dir[cand]) * p.tp_rank, p.cand_scale[cand] * v);
+}
+
+// side input t of row r, As column c (see tp_unit)
+template <typename TAct>
+__device__ __forceinline__ void store_tproj(const GemmParams& p, int r, int c, float v) {
+  if constexpr (std::is_same<TAct, float>::value) {
+    ((float*)p.C)[(int64_t)r * p.ldc + c] = v;
+  } else {
+    if (p.tp_unit == 0) {
+      ((bf16_t*)p.C)[(int64_t)r * p.ldc + c] = f32_to_bf16(v);
+      return;
+    }
+    const int u = c / p.tp_unit;
+    const int64_t o = (int64_t)r * p.ldc + c + u * p.tp_unit;   // u * 2 tp_unit + c % tp_unit
+    bf16_t hi, lo;
+    split_bf16(v, hi, lo);
+    ((bf16_t*)p.C)[o] = hi;
+    ((bf16_t*)p.C)[o + p.tp_unit] = lo;
+  }
+}
+
+
 // ---- random streams ---------------------------------------------------------
 struct NormalJob {     // one generated tensor (or factor) written in a given layout
   void* dst;           // output base
@@ -204,6 +247,12 @@ hipError_t launch_embed_t(const TW* E, const TW* P, const int32_t* tokens, const
 template <typename T>
 hipError_t launch_norm(const float* h, const int32_t* rows, int M, int d, const float* w, const float* b,
                        float eps, bool rms, T* out, int64_t ld_out, int lo_off, hipStream_t s);
+// norm (as launch_norm, no row list, no two-term output) fused with the side input t of the
+// projections reading its output: p carries the V^T rows (B, ldb) and the tproj_out fields;
+// n_used (1..16) used columns of tp_used per block of tp_ks
+template <typename T>
+hipError_t launch_norm_side(const float* h, int M, int d, const float* w, const float* b, float eps, bool rms, T* out,
+                            int64_t ld_out, const GemmParams& p, int n_used, hipStream_t s);
 template <typename T>
 hipError_t launch_qknorm_rope(T* qkv, int M, int ld, int hq, int hkv, int hd, const float* qw, const float* kw,
                               float eps, const float2* rope_cs, const int32_t* row_pos, hipStream_t s);

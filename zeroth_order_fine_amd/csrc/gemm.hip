@@ -89,45 +89,6 @@ __device__ __forceinline__ void store_act(const GemmParams& p, int64_t o, float 
   }
 }
 
-template <typename TAct>
-__device__ __forceinline__ void store_tproj(const GemmParams& p, int r, int c, float v);
-
-// Side input of row r from computed column c = x.V (kind block c / tp_ks, computed
-// slot (c % tp_ks) / r): a bank entry's slot goes to the entry's As block; the slot
-// of the row's own direction also goes, times s * eps~, to that direction's As
-// block.  Nothing else is written (As is zero-filled once per call; foreground rows
-// and other directions keep zeros).
-template <typename TAct>
-__device__ __forceinline__ void tproj_out(const GemmParams& p, int r, int c, float v, int cand) {
-  if (cand < 0) return;
-  const int kb = c / p.tp_ks, w = c - kb * p.tp_ks;
-  if (w >= p.tp_used) return;
-  const int slot = w / p.tp_rank, k = w - slot * p.tp_rank;
-  const int base = kb * p.tp_as_ks + k;
-  if (slot < p.tp_entries) store_tproj<TAct>(p, r, base + slot * p.tp_rank, v);
-  if (slot == p.cand_slot[cand])
-    store_tproj<TAct>(p, r, base + (p.tp_entries + p.cand_dir[cand]) * p.tp_rank, p.cand_scale[cand] * v);
-}
-
-// side input t of row r, As column c (see tp_unit)
-template <typename TAct>
-__device__ __forceinline__ void store_tproj(const GemmParams& p, int r, int c, float v) {
-  if constexpr (std::is_same<TAct, float>::value) {
-    ((float*)p.C)[(int64_t)r * p.ldc + c] = v;
-  } else {
-    if (p.tp_unit == 0) {
-      ((bf16_t*)p.C)[(int64_t)r * p.ldc + c] = f32_to_bf16(v);
-      return;
-    }
-    const int u = c / p.tp_unit;
-    const int64_t o = (int64_t)r * p.ldc + c + u * p.tp_unit;   // u * 2 tp_unit + c % tp_unit
-    bf16_t hi, lo;
-    split_bf16(v, hi, lo);
-    ((bf16_t*)p.C)[o] = hi;
-    ((bf16_t*)p.C)[o + p.tp_unit] = lo;
-  }
-}
-
 // ------------------------------------------------------------------------------
 // epilogue, shared by both paths.  acc[i][j][q]: row r0 + i*16 + 4*(lane>>4) + q,
 // column c0 + j*16 + (lane&15).

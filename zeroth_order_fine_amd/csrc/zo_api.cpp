@@ -742,6 +742,19 @@ int forward(zo_model* m, const zo_plan_s& p, const Packing& pk, const SideGeom& 
                                    w.row_pos, M, D, d.vocab, w.h, w.bad_ids, s));
   }
 
+  // the side input of a group formed inside the norm kernel that produces its activations
+  // (bf16 and fp8 models, one-term activations, at most 16 used factor columns)
+  auto side_in_norm = [&](int g) {
+    return bf && !sp && sg.group_on[g] && (sg.vt_rows[g] / sg.ks_c) * (int64_t)(sg.nc * sg.r) <= 16;
+  };
+  auto tproj_params = [&](int l, int g, const void* X, int K) {
+    GemmParams gp = gemm_base(X, (int64_t)K * x2, w.vt[l * 4 + g], (int64_t)K * x3, M, (int)sg.vt_rows[g], K * x3);
+    gp.epi = EPI_TPROJ;
+    gp.C = w.as; gp.ldc = w.as_ld;
+    gp.row_cand = w.row_cand; gp.cand_dir = w.cand_dir; gp.cand_slot = w.cand_slot; gp.cand_scale = w.cand_scale;
+    gp.tp_ks = sg.ks_c; gp.tp_rank = sg.r; gp.tp_entries = sg.E; gp.tp_used = sg.nc * sg.r; gp.tp_as_ks = sg.ks;
+    return gp;
+  };
   auto tproj = [&](int l, int g, const void* X, int K) -> int {
     if (!sg.group_on[g]) return ZO_OK;
     GemmParams gp = gemm_base(X, (int64_t)K * x2, w.vt[l * 4 + g], (int64_t)K * x3, M, (int)sg.vt_rows[g], K * x3);
@@ -773,8 +786,16 @@ int forward(zo_model* m, const zo_plan_s& p, const Packing& pk, const SideGeom& 
     }
     return gp;
   };
-  // LayerNorm / RMSNorm of the residual stream into the input of the next linears
-  auto norm_in = [&](const float* nw, const float* nb) -> hipError_t {
+  // LayerNorm / RMSNorm of the residual stream into the input of the next linears (group g),
+  // with the group's side input t when side_in_norm(g)
+  auto norm_in = [&](const float* nw, const float* nb, int l, int g) -> hipError_t {
+    if (side_in_norm(g)) {
+      const GemmParams gp = tproj_params(l, g, w.xa, D);
+      const int n_used = (int)(sg.vt_rows[g] / sg.ks_c) * sg.nc * sg.r;
+      if (f8) return launch_norm_side<e4m3_t>(w.h, M, D, nw, nb, eps, rms, (e4m3_t*)w.xa, D, gp, n_used, s);
+      if constexpr (std::is_same<T, bf16_t>::value)
+        return launch_norm_side<bf16_t>(w.h, M, D, nw, nb, eps, rms, (bf16_t*)w.xa, D, gp, n_used, s);
+    }
     if (f8) return launch_norm<e4m3_t>(w.h, nullptr, M, D, nw, nb, eps, rms, (e4m3_t*)w.xa, D, 0, s);
     return launch_norm<T>(w.h, nullptr, M, D, nw, nb, eps, rms, (T*)w.xa, (int64_t)D * x2, sp ? D : 0, s);
   };
@@ -791,9 +812,9 @@ int forward(zo_model* m, const zo_plan_s& p, const Packing& pk, const SideGeom& 
     // attention block
     {
       ProfScope ps(ZO_PROF_NORM, s);
-      ZO_HIP(norm_in(Wf(P[P_LN1W]), Wf(P[P_LN1B])));
+      ZO_HIP(norm_in(Wf(P[P_LN1W]), Wf(P[P_LN1B]), l, 0));
     }
-    if ((rc = tproj(l, 0, w.xa, D)) != ZO_OK) return rc;
+    if (!side_in_norm(0) && (rc = tproj(l, 0, w.xa, D)) != ZO_OK) return rc;
     {
       GemmParams gp = proj(w.xa, W(P[P_WQ]), NQKV, D);
       with_side(gp, l, 0);
@@ -851,9 +872,9 @@ int forward(zo_model* m, const zo_plan_s& p, const Packing& pk, const SideGeom& 
     // FFN block
     {
       ProfScope ps(ZO_PROF_NORM, s);
-      ZO_HIP(norm_in(Wf(P[P_LN2W]), Wf(P[P_LN2B])));
+      ZO_HIP(norm_in(Wf(P[P_LN2W]), Wf(P[P_LN2B]), l, 2));
     }
-    if ((rc = tproj(l, 2, w.xa, D)) != ZO_OK) return rc;
+    if (!side_in_norm(2) && (rc = tproj(l, 2, w.xa, D)) != ZO_OK) return rc;
     {
       const int N1 = is_opt(d) ? F : 2 * F;
       GemmParams gp = proj(w.xa, W(P[P_W1]), N1, D);
