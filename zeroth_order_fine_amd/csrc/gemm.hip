@@ -1080,15 +1080,20 @@ static int side_dot_columns(const GemmParams& p) {
   return n <= 2 ? n : 0;
 }
 
-template <int NC>
-static hipError_t launch_side_dot_nc(const GemmParams& p, int j0, int ncols, hipStream_t s) {
-  constexpr int R = 8;
+// R rows per workgroup: 8 for large batches, 2 for small ones (more workgroups in flight).
+// A lane's chunks and the reduction order do not depend on R, so neither does any result.
+template <int R, int NC>
+static hipError_t launch_side_dot_rnc(const GemmParams& p, int j0, int ncols, hipStream_t s) {
   const int blocks = (p.M + R - 1) / R;
   if (p.a_e4m3)
     hipLaunchKernelGGL((side_dot_kernel<R, NC, true>), dim3(blocks), dim3(256), 0, s, p, j0, ncols);
   else
     hipLaunchKernelGGL((side_dot_kernel<R, NC, false>), dim3(blocks), dim3(256), 0, s, p, j0, ncols);
   return hipGetLastError();
+}
+template <int NC>
+static hipError_t launch_side_dot_nc(const GemmParams& p, int j0, int ncols, hipStream_t s) {
+  return p.M >= 4096 ? launch_side_dot_rnc<8, NC>(p, j0, ncols, s) : launch_side_dot_rnc<2, NC>(p, j0, ncols, s);
 }
 
 static hipError_t launch_side_dot(const GemmParams& p, int ncols, hipStream_t s) {
@@ -1193,6 +1198,8 @@ hipError_t gemm_launch_bf16(const GemmParams& p, int cfg, hipStream_t s) {
     // lane has at two waves a SIMD (spills); the 128x128 tile streams the same bytes per
     // product from L2 as the bf16 256x256 tile (half-size elements)
     if (p.a_e4m3 || p.b_e4m3) return launch_pipe_epi<128, 128, 64, 64>(p, s);
+    // (measured at OPT-13B batch 64: finishing the last partial round of 256x256 tiles in
+    // 128x128 tiles of a second launch made the projections 6 % slower, not faster)
     if (pipe_tile(p) == 0) return launch_pipe_epi<256, 256, 128, 64>(p, s);
     return launch_pipe_epi<128, 128, 64, 64>(p, s);
   }
