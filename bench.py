@@ -308,6 +308,10 @@ def main():
                     help="skip the extra scoring without side path that measures its cost (for profiler runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 1 GiB device copy (counter calibration for the traffic figure)")
+    ap.add_argument("--graphs", action="store_true",
+                    help="replay zo_score's forward pass from a captured HIP graph (launch-bound small "
+                         "workloads); the timed steps then carry no per-launch events and the roofline "
+                         "comes from the eagerly launched breakdown steps")
     ap.add_argument("--generate", type=int, default=0, metavar="N",
                     help="time greedy generation of N tokens per sequence (zo_generate) instead of the ZO step")
     args = ap.parse_args()
@@ -328,6 +332,9 @@ def main():
     wl = configs.CONFIGS[args.workload]
     cfg = wl.model
     torch.cuda.set_device(0)
+    # a stream of its own (default priority): graph capture needs a stream other than the null one
+    stream = torch.cuda.Stream()
+    torch.cuda.set_stream(stream)
     model = zo.Model(cfg)
     model.init_weights(wl.model_seed)
     batch = inputs.make_batch(wl)
@@ -337,6 +344,7 @@ def main():
     if args.generate:
         generation_bench(args, wl, model, bank, batch, db)
         return
+    model.set_graphs(args.graphs)
 
     score_s = [0.0]
 
@@ -355,7 +363,8 @@ def main():
     torch.cuda.synchronize()
     score_s[0] = 0.0
     # timed region: events only around the projections (the roofline kernel)
-    zo.api.profile_begin(["gemm_base"])
+    if not args.graphs:
+        zo.api.profile_begin(["gemm_base"])
     t0 = time.perf_counter()
     marks = [t0]
     for k in range(args.steps):
@@ -365,7 +374,7 @@ def main():
     elapsed = time.perf_counter() - t0
     step_ms = sorted((b - a) * 1e3 for a, b in zip(marks, marks[1:]))
     score_timed = score_s[0]
-    prof_timed = zo.api.profile_end()
+    prof_timed = zo.api.profile_end() if not args.graphs else None
     # per-class breakdown: a few more steps with every class timed
     n_bd = max(1, min(args.steps, 5))
     zo.api.profile_begin()
@@ -383,9 +392,10 @@ def main():
     ms_step = elapsed / args.steps * 1e3
     value = probe_tokens / (ms_step / 1e3)
 
-    n_base, ms_base = prof_timed["gemm_base"]
+    # projection launch times: the timed steps' events, or with graph replay the breakdown steps'
+    n_base, ms_base = (prof_timed or prof)["gemm_base"]
     flops_step = base_gemm_flops(cfg, rows)
-    launches_per_step = n_base / args.steps
+    launches_per_step = n_base / (args.steps if prof_timed else n_bd)
     avg_launch_ms = ms_base / max(n_base, 1)
     achieved = (flops_step / launches_per_step) / (avg_launch_ms / 1e3) / 1e12 if n_base else None
     peak = {"bf16": PEAK_BF16_TFLOPS, "fp8": PEAK_FP8_TFLOPS}.get(cfg.dtype, PEAK_F32_TFLOPS)
@@ -405,7 +415,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": describe(wl), "prompts": wl.n_prompts, "candidates": len(wl.candidates),
                    "rank": wl.rank, "probe_tokens_per_step": probe_tokens, "foreground_tokens_per_step": fg_tokens,
-                   "scored_positions_per_step": int(out["n_scored"])},
+                   "scored_positions_per_step": int(out["n_scored"]), "hip_graph_replay": args.graphs},
         "steps_per_s": round(args.steps / elapsed, 4),
         "score_only_tokens_per_s": round(probe_tokens * args.steps / score_timed, 1),
         "score_share_of_step": round(score_timed / elapsed, 4),

@@ -269,6 +269,18 @@ int zo_pack(const zo_plan_t* p, const zo_batch* b, int32_t* phys_seq, int32_t* p
 int zo_score(zo_model* m, const zo_plan_t* p, const zo_bank* bank, const zo_batch* b, void* ws_dev,
              size_t ws_bytes, double* seq_logp_dev, float* tok_logp_dev, double* S_host, void* stream);
 
+/* Launch amortisation: with enable != 0, zo_score captures its forward pass (embedding,
+ * every layer's kernels and the head: several hundred launches) into a HIP graph on the
+ * call's stream and, on later calls whose workspace, token buffer, packing sizes and side
+ * geometry are the same, replays the graph instead of launching each kernel; the packing
+ * tables and side factors are rewritten before every replay, so the plan's step, seeds and
+ * candidates, the bank's contents and the batch's token values may change freely.  The
+ * results are bitwise those of the eager launches.  Needs a stream other than the null
+ * stream; per-kernel timing (zo_profile_begin) launches eagerly.  enable == 0 (the
+ * default) launches eagerly and frees the graph.  One graph per model: a model shared by
+ * concurrent zo_score calls must not use this. */
+int zo_model_set_graphs(zo_model* m, int32_t enable);
+
 /* For callers that cannot allocate device memory (code under HIP graph capture, tight
  * serving loops, harnesses that forbid allocation): zo_score with the workspace taken from
  * a scratch array of ZO_NOALLOC_SCRATCH_BYTES that the library holds on each device it

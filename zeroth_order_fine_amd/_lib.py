@@ -35,6 +35,7 @@ _SIGS = {
     "zo_weight_locate": (c_i32, [P(ModelDesc), c_i32, c_i32, P(c_sz), P(c_i64), P(c_i64), P(c_i32), P(c_i32)]),
     "zo_model_create": (c_i32, [P(ModelDesc), c_vp, c_sz, P(c_vp)]),
     "zo_model_destroy": (c_i32, [c_vp]),
+    "zo_model_set_graphs": (c_i32, [c_vp, c_i32]),
     "zo_init_weights": (c_i32, [c_vp, c_u64, c_vp]),
     "zo_plan": (c_i32, [c_vp, P(PlanDesc), P(c_vp)]),
     "zo_plan_destroy": (c_i32, [c_vp]),

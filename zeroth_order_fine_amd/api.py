@@ -88,6 +88,11 @@ class Model:
         except Exception:
             pass
 
+    def set_graphs(self, enable=True):
+        """Replay zo_score's forward pass from a captured HIP graph while shapes and buffers
+        repeat (zo_model_set_graphs)."""
+        _check(self.L.zo_model_set_graphs(self.h, 1 if enable else 0))
+
     def init_weights(self, seed):
         _check(self.L.zo_init_weights(self.h, seed, _stream()))
 

@@ -251,6 +251,24 @@ inline uint32_t weight_tag(int slot, int param) { return (1u << 30) | ((uint32_t
 }  // namespace
 
 // ---- opaque objects --------------------------------------------------------------
+// The forward launch sequence of zo_score captured as a HIP graph, with what its kernel
+// arguments were derived from (see graph_key).
+struct GraphCache {
+  bool on = false;                 // zo_model_set_graphs
+  std::vector<int64_t> key;
+  std::vector<int64_t> pending;    // the last eager call's key: captured when it repeats
+  hipGraph_t graph = nullptr;
+  hipGraphExec_t exec = nullptr;
+  void reset() {
+    if (exec) (void)hipGraphExecDestroy(exec);
+    if (graph) (void)hipGraphDestroy(graph);
+    exec = nullptr;
+    graph = nullptr;
+    key.clear();
+    pending.clear();
+  }
+};
+
 struct zo_model {
   zo_model_desc d;
   Layout lo;
@@ -259,6 +277,7 @@ struct zo_model {
   float2* rope = nullptr;   // [rope_len x head_dim/2] (cos, sin), Qwen3
   int rope_len = 0;
   int device = 0;
+  GraphCache gc;
 };
 
 struct zo_plan_s {
@@ -989,6 +1008,7 @@ int zo_model_create(const zo_model_desc* desc, void* weights_dev, size_t bytes, 
 
 int zo_model_destroy(zo_model* m) {
   if (!m) return ZO_OK;
+  m->gc.reset();
   if (m->rope) (void)hipFree(m->rope);
   delete m;
   return ZO_OK;
@@ -1310,6 +1330,26 @@ static int prepare_call(zo_model* m, const zo_plan_t* p, const zo_bank* bank, co
   return ZO_OK;
 }
 
+// Everything the kernel arguments of forward() are derived from, besides the model: the
+// workspace (whose carve follows from the sizes below), the token buffer, the packing's
+// sizes and the side geometry.  The packing tables and side factors themselves live in the
+// workspace and are rewritten before every launch, so they are not part of the key.
+static std::vector<int64_t> graph_key(const zo_plan_s& p, const Packing& pk, const SideGeom& sg, const void* ws,
+                                      size_t ws_bytes, const void* tokens) {
+  std::vector<int64_t> k = {(int64_t)(intptr_t)ws, (int64_t)ws_bytes, (int64_t)(intptr_t)tokens, pk.M, pk.n_phys,
+                            pk.n_scored, (int64_t)pk.work.size(), (int64_t)p.cdir.size(), (int64_t)p.flags,
+                            (int64_t)p.mask, sg.any, sg.E, sg.q, sg.r, sg.used, sg.ks, sg.nc, sg.ks_c};
+  for (int g = 0; g < (int)sg.group_on.size(); ++g) k.push_back(sg.group_on[g]);
+  return k;
+}
+
+int zo_model_set_graphs(zo_model* m, int32_t enable) {
+  ZO_CHECK(m, ZO_E_INVAL, "null model");
+  m->gc.reset();
+  m->gc.on = enable != 0;
+  return ZO_OK;
+}
+
 int zo_score(zo_model* m, const zo_plan_t* p, const zo_bank* bank, const zo_batch* b, void* ws_dev,
              size_t ws_bytes, double* seq_logp_dev, float* tok_logp_dev, double* S_host, void* stream) {
   ZO_CHECK(m && p && S_host, ZO_E_INVAL, "null argument");
@@ -1324,10 +1364,42 @@ int zo_score(zo_model* m, const zo_plan_t* p, const zo_bank* bank, const zo_batc
   if (rc != ZO_OK) return rc;
   const int nc = (int)p->cdir.size();
 
-  // ---- forward, head, reduce
-  if (bf) rc = forward<bf16_t>(m, *p, pk, sg, w, b->tokens_dev, s);   // bf16 and fp8 models
-  else rc = forward<float>(m, *p, pk, sg, w, b->tokens_dev, s);
-  if (rc != ZO_OK) return rc;
+  // ---- forward and head: eagerly, or replayed from the captured graph while everything its
+  // launches were derived from repeats (graph_key); the tables it reads were copied above
+  if (m->gc.on && s != nullptr && !g_prof.on) {
+    const std::vector<int64_t> key = graph_key(*p, pk, sg, ws_dev, ws_bytes, b->tokens_dev);
+    if (m->gc.exec && m->gc.key == key) {
+      ZO_HIP(hipGraphLaunch(m->gc.exec, s));
+    } else if (m->gc.pending != key) {
+      // a new key runs eagerly once (also doing any first-use set-up of the kernels) and
+      // is captured if the next call repeats it
+      rc = bf ? forward<bf16_t>(m, *p, pk, sg, w, b->tokens_dev, s) : forward<float>(m, *p, pk, sg, w, b->tokens_dev, s);
+      if (rc != ZO_OK) return rc;
+      m->gc.pending = key;
+    } else {
+      m->gc.reset();
+      ZO_HIP(hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal));
+      rc = bf ? forward<bf16_t>(m, *p, pk, sg, w, b->tokens_dev, s) : forward<float>(m, *p, pk, sg, w, b->tokens_dev, s);
+      hipGraph_t g = nullptr;
+      const hipError_t e = hipStreamEndCapture(s, &g);      // always leave capture mode
+      if (rc != ZO_OK) {
+        if (g) (void)hipGraphDestroy(g);
+        return rc;
+      }
+      if (e != hipSuccess) return fail(ZO_E_DEVICE, "graph capture: %s", hipGetErrorString(e));
+      m->gc.graph = g;
+      if (hipGraphInstantiate(&m->gc.exec, g, nullptr, nullptr, 0) != hipSuccess) {
+        m->gc.reset();
+        return fail(ZO_E_DEVICE, "graph instantiation failed");
+      }
+      m->gc.key = key;
+      ZO_HIP(hipGraphLaunch(m->gc.exec, s));
+    }
+  } else {
+    if (bf) rc = forward<bf16_t>(m, *p, pk, sg, w, b->tokens_dev, s);   // bf16 and fp8 models
+    else rc = forward<float>(m, *p, pk, sg, w, b->tokens_dev, s);
+    if (rc != ZO_OK) return rc;
+  }
   double* seq_out = seq_logp_dev ? seq_logp_dev : w.seq_logp;
   const int bn = gemm_cfg_bn(GEMM_CFG_HEAD, bf);
   ProfScope ps_red(ZO_PROF_REDUCE, s);
