@@ -284,7 +284,7 @@ def generation_bench(args, wl, model, bank, batch, db):
         "warmup": args.warmup, "ms_per_call": round(ms, 3), "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": cfg.dtype, "data": "synthetic",
         "config": {"workload": describe(wl), "sequences": n_phys, "new_tokens": n_new,
-                   "prompt_tokens": int(sum(lengths[li] for li in phys[0]))},
+                   "prompt_tokens": int(sum(lengths[li] for li in phys[0])), "hip_graph_replay": args.graphs},
         "roofline": {"kernel": "decode attention (single-query attention over the K/V cache)", "bound": "hbm",
                      "achieved": round(gbs, 1) if gbs else None, "peak": PEAK_HBM_GBS, "unit": "GB/s",
                      "frac": round(gbs / PEAK_HBM_GBS, 4) if gbs else None, "traffic": None,
@@ -341,10 +341,10 @@ def main():
     db = zo.DeviceBatch(batch)
     bank = zo.Bank(model, 2 * wl.n_dirs, wl.rank, wl.targets)
     torch.cuda.synchronize()
+    model.set_graphs(args.graphs)
     if args.generate:
         generation_bench(args, wl, model, bank, batch, db)
         return
-    model.set_graphs(args.graphs)
 
     score_s = [0.0]
 

@@ -67,3 +67,32 @@ def test_graph_replays_match_eager(name):
         assert _same(_bits(got), _bits(eager))
     torch.cuda.synchronize()
     del x
+
+
+@pytest.mark.parametrize("cfg", [SMALL_OPT_BF16, SMALL_QWEN_BF16], ids=["opt", "qwen3"])
+def test_generation_decode_steps_replayed_from_graph(cfg):
+    """zo_generate with graph replay: the decode steps after the first two run from one
+    captured graph; tokens and log-probs are bitwise those of eager launches, on two calls
+    in a row (the second replays from the start) with eager work between them."""
+    need_gpu()
+    import torch
+    import zeroth_order_fine_amd as zo
+    wl = workload(cfg, dir_seeds=(3,), n_fg=1, n_prompts=2, len_lo=5, len_hi=70)
+    batch = inputs.make_batch(wl)
+    g, ref = GpuRun(wl), GpuRun(wl)
+    stream = torch.cuda.Stream()
+    with torch.cuda.stream(stream):
+        for r in (g, ref):
+            r.update(0, np.array([0.8]), 1e-2)
+        db = zo.DeviceBatch(batch)
+        g.model.set_graphs(True)
+        for call in range(2):
+            flush("generation with graphs, call %d" % call)
+            got = zo.generate(g.model, g.plan(1), g.bank, db, 9)
+            eager = zo.generate(ref.model, ref.plan(1), ref.bank, zo.DeviceBatch(batch), 9)
+            assert np.array_equal(got["tokens"].cpu().numpy(), eager["tokens"].cpu().numpy())
+            assert np.array_equal(got["logp"].cpu().numpy().view(np.uint32), eager["logp"].cpu().numpy().view(np.uint32))
+            assert np.array_equal(got["S"], eager["S"])
+            x = torch.randn(1 << 12, device="cuda").sum()
+            torch.cuda.synchronize()
+    torch.cuda.synchronize()

@@ -277,7 +277,8 @@ struct zo_model {
   float2* rope = nullptr;   // [rope_len x head_dim/2] (cos, sin), Qwen3
   int rope_len = 0;
   int device = 0;
-  GraphCache gc;
+  GraphCache gc;       // zo_score's forward pass
+  GraphCache gcd;      // a decode step of zo_generate
 };
 
 struct zo_plan_s {
@@ -934,6 +935,53 @@ int forward(zo_model* m, const zo_plan_s& p, const Packing& pk, const SideGeom& 
 
 }  // namespace
 
+// Runs `launch` (a fixed launch sequence whose arguments follow from `key`) on stream s: a
+// new key eagerly once, captured into a graph when the next call repeats it, and replayed
+// from the graph while the key repeats.
+template <typename F>
+static int launch_cached(GraphCache& gc, const std::vector<int64_t>& key, hipStream_t s, F&& launch) {
+  if (gc.exec && gc.key == key) {
+    ZO_HIP(hipGraphLaunch(gc.exec, s));
+    return ZO_OK;
+  }
+  if (gc.pending != key) {
+    const int rc = launch();
+    if (rc == ZO_OK) gc.pending = key;
+    return rc;
+  }
+  gc.reset();
+  ZO_HIP(hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal));
+  const int rc = launch();
+  hipGraph_t g = nullptr;
+  const hipError_t e = hipStreamEndCapture(s, &g);      // always leave capture mode
+  if (rc != ZO_OK) {
+    if (g) (void)hipGraphDestroy(g);
+    return rc;
+  }
+  if (e != hipSuccess) return fail(ZO_E_DEVICE, "graph capture: %s", hipGetErrorString(e));
+  gc.graph = g;
+  if (hipGraphInstantiate(&gc.exec, g, nullptr, nullptr, 0) != hipSuccess) {
+    gc.reset();
+    return fail(ZO_E_DEVICE, "graph instantiation failed");
+  }
+  gc.key = key;
+  ZO_HIP(hipGraphLaunch(gc.exec, s));
+  return ZO_OK;
+}
+
+// Everything the kernel arguments of forward() are derived from, besides the model: the
+// workspace (whose carve follows from the sizes below), the token buffer, the packing's
+// sizes and the side geometry.  The packing tables and side factors themselves live in the
+// workspace and are rewritten before every launch, so they are not part of the key.
+static std::vector<int64_t> graph_key(const zo_plan_s& p, const Packing& pk, const SideGeom& sg, const void* ws,
+                                      size_t ws_bytes, const void* tokens) {
+  std::vector<int64_t> k = {(int64_t)(intptr_t)ws, (int64_t)ws_bytes, (int64_t)(intptr_t)tokens, pk.M, pk.n_phys,
+                            pk.n_scored, (int64_t)pk.work.size(), (int64_t)p.cdir.size(), (int64_t)p.flags,
+                            (int64_t)p.mask, sg.any, sg.E, sg.q, sg.r, sg.used, sg.ks, sg.nc, sg.ks_c};
+  for (int g = 0; g < (int)sg.group_on.size(); ++g) k.push_back(sg.group_on[g]);
+  return k;
+}
+
 // =====================================================================================
 extern "C" {
 
@@ -1009,6 +1057,7 @@ int zo_model_create(const zo_model_desc* desc, void* weights_dev, size_t bytes, 
 int zo_model_destroy(zo_model* m) {
   if (!m) return ZO_OK;
   m->gc.reset();
+  m->gcd.reset();
   if (m->rope) (void)hipFree(m->rope);
   delete m;
   return ZO_OK;
@@ -1330,22 +1379,10 @@ static int prepare_call(zo_model* m, const zo_plan_t* p, const zo_bank* bank, co
   return ZO_OK;
 }
 
-// Everything the kernel arguments of forward() are derived from, besides the model: the
-// workspace (whose carve follows from the sizes below), the token buffer, the packing's
-// sizes and the side geometry.  The packing tables and side factors themselves live in the
-// workspace and are rewritten before every launch, so they are not part of the key.
-static std::vector<int64_t> graph_key(const zo_plan_s& p, const Packing& pk, const SideGeom& sg, const void* ws,
-                                      size_t ws_bytes, const void* tokens) {
-  std::vector<int64_t> k = {(int64_t)(intptr_t)ws, (int64_t)ws_bytes, (int64_t)(intptr_t)tokens, pk.M, pk.n_phys,
-                            pk.n_scored, (int64_t)pk.work.size(), (int64_t)p.cdir.size(), (int64_t)p.flags,
-                            (int64_t)p.mask, sg.any, sg.E, sg.q, sg.r, sg.used, sg.ks, sg.nc, sg.ks_c};
-  for (int g = 0; g < (int)sg.group_on.size(); ++g) k.push_back(sg.group_on[g]);
-  return k;
-}
-
 int zo_model_set_graphs(zo_model* m, int32_t enable) {
   ZO_CHECK(m, ZO_E_INVAL, "null model");
   m->gc.reset();
+  m->gcd.reset();
   m->gc.on = enable != 0;
   return ZO_OK;
 }
@@ -1366,35 +1403,12 @@ int zo_score(zo_model* m, const zo_plan_t* p, const zo_bank* bank, const zo_batc
 
   // ---- forward and head: eagerly, or replayed from the captured graph while everything its
   // launches were derived from repeats (graph_key); the tables it reads were copied above
+  // (a new key runs eagerly once, which also does any first-use set-up of the kernels)
   if (m->gc.on && s != nullptr && !g_prof.on) {
-    const std::vector<int64_t> key = graph_key(*p, pk, sg, ws_dev, ws_bytes, b->tokens_dev);
-    if (m->gc.exec && m->gc.key == key) {
-      ZO_HIP(hipGraphLaunch(m->gc.exec, s));
-    } else if (m->gc.pending != key) {
-      // a new key runs eagerly once (also doing any first-use set-up of the kernels) and
-      // is captured if the next call repeats it
-      rc = bf ? forward<bf16_t>(m, *p, pk, sg, w, b->tokens_dev, s) : forward<float>(m, *p, pk, sg, w, b->tokens_dev, s);
-      if (rc != ZO_OK) return rc;
-      m->gc.pending = key;
-    } else {
-      m->gc.reset();
-      ZO_HIP(hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal));
-      rc = bf ? forward<bf16_t>(m, *p, pk, sg, w, b->tokens_dev, s) : forward<float>(m, *p, pk, sg, w, b->tokens_dev, s);
-      hipGraph_t g = nullptr;
-      const hipError_t e = hipStreamEndCapture(s, &g);      // always leave capture mode
-      if (rc != ZO_OK) {
-        if (g) (void)hipGraphDestroy(g);
-        return rc;
-      }
-      if (e != hipSuccess) return fail(ZO_E_DEVICE, "graph capture: %s", hipGetErrorString(e));
-      m->gc.graph = g;
-      if (hipGraphInstantiate(&m->gc.exec, g, nullptr, nullptr, 0) != hipSuccess) {
-        m->gc.reset();
-        return fail(ZO_E_DEVICE, "graph instantiation failed");
-      }
-      m->gc.key = key;
-      ZO_HIP(hipGraphLaunch(m->gc.exec, s));
-    }
+    rc = launch_cached(m->gc, graph_key(*p, pk, sg, ws_dev, ws_bytes, b->tokens_dev), s, [&]() {
+      return bf ? forward<bf16_t>(m, *p, pk, sg, w, b->tokens_dev, s) : forward<float>(m, *p, pk, sg, w, b->tokens_dev, s);
+    });
+    if (rc != ZO_OK) return rc;
   } else {
     if (bf) rc = forward<bf16_t>(m, *p, pk, sg, w, b->tokens_dev, s);   // bf16 and fp8 models
     else rc = forward<float>(m, *p, pk, sg, w, b->tokens_dev, s);
@@ -1540,8 +1554,19 @@ int zo_generate(zo_model* m, const zo_plan_t* p, const zo_bank* bank, const zo_b
     ZO_HIP(h2d(w.sc_lab_src, zeros));
     ZO_HIP(h2d(w.row_cache, cache));
     if (sg.any) ZO_HIP(hipMemsetAsync(w.as, 0, (size_t)nq * w.as_ld * act_size(d), s));   // rows change meaning
-    rc = bf ? forward<bf16_t>(m, *p, pd, sg, w, w.gen_tok, s, &decode)
-            : forward<float>(m, *p, pd, sg, w, w.gen_tok, s, &decode);
+    auto step = [&]() {
+      return bf ? forward<bf16_t>(m, *p, pd, sg, w, w.gen_tok, s, &decode)
+                : forward<float>(m, *p, pd, sg, w, w.gen_tok, s, &decode);
+    };
+    if (m->gc.on && s != nullptr && !g_prof.on) {
+      // every decode step launches the same sequence (the step's tables were copied above);
+      // only the wide / narrow form of the decode attention follows the key count
+      std::vector<int64_t> key = graph_key(*p, pd, sg, ws_dev, ws_bytes, w.gen_tok);
+      key.push_back(decode.max_keys > 512);
+      rc = launch_cached(m->gcd, key, s, step);
+    } else {
+      rc = step();
+    }
     if (rc != ZO_OK) return rc;
     ZO_HIP(launch_greedy_reduce(w.part, w.part_idx, n_tiles, nq, w.gen_tok, tokens_dev, logp_dev, n_new, j, s));
   }
