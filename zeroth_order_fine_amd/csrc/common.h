@@ -124,6 +124,15 @@ struct GemmParams {
   // side segment's Bs pre-scaled by 2^11, multiplies the sums by 2^-11 before the
   // epilogue, and writes GELU outputs as e4m3)
   int a_e4m3, b_e4m3;
+  // GELU / SwiGLU epilogues (bf16 kernels): the side input of the projection that reads this
+  // output, formed here (sf_n used factor columns, 0 = none).  Per row and group of the
+  // output columns one wave tile holds (64 for GELU, 32 for SwiGLU), the partial sums of the
+  // stored (rounded) outputs times the used V^T rows: column j of sf_n is row
+  // (j / sf_used) * sf_ks + j % sf_used of sf_vt (row pitch sf_ldv), written to
+  // sf_part [sf_groups x M x sf_n] fp32; side_part_reduce sums the groups in order.
+  int sf_n, sf_used, sf_ks, sf_groups;
+  const void* sf_vt; int64_t sf_ldv;
+  float* sf_part;
 };
 
 // Launch on `stream`; returns hipSuccess or the launch error.
@@ -286,6 +295,9 @@ hipError_t launch_attention_split(const float* qkv, int ld_qkv, bf16_t* out, int
                                   const int32_t* cu, const int32_t* work, int n_work, int hq, int hkv, int hd,
                                   hipStream_t s);
 hipError_t launch_tproj_reduce(const GemmParams& p, hipStream_t s);
+// t from the partial sums of an epilogue (sf_part, sf_groups, sf_n) in group order, then the
+// side-input store of tproj_out (p carries the tproj fields of the consuming projection)
+hipError_t launch_side_part_reduce(const GemmParams& p, hipStream_t s);
 hipError_t launch_gather_labels(const int32_t* src, const int32_t* idx, int n, int vocab, int32_t* dst,
                                 int32_t* bad, hipStream_t s);
 hipError_t launch_logp_reduce(const float2* part, int n_tiles, const float* lab_logit, int n_scored,

@@ -380,6 +380,59 @@ __device__ __forceinline__ void store_e4m3x4(e4m3_t* o, floatx4_t v) {
   *(uint32_t*)o = f32x4_to_e4m3(v[0], v[1], v[2], v[3]);
 }
 
+// The values a four-column store wrote, as the next projection reads them (bf16 or e4m3).
+template <bool F8>
+__device__ __forceinline__ floatx4_t stored4(floatx4_t v) {
+  floatx4_t r;
+  if constexpr (F8) {
+    const u32x4_t w = e4m3x8_to_bf16(make_uint2(f32x4_to_e4m3(v[0], v[1], v[2], v[3]), 0u));
+    r = floatx4_t{bf16_to_f32((bf16_t)(w[0] & 0xFFFFu)), bf16_to_f32((bf16_t)(w[0] >> 16)),
+                  bf16_to_f32((bf16_t)(w[1] & 0xFFFFu)), bf16_to_f32((bf16_t)(w[1] >> 16))};
+  } else {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) r[q] = bf16_to_f32(f32_to_bf16(v[q]));
+  }
+  return r;
+}
+
+// The used V^T values of four consecutive output columns (from col), loaded once per column
+// group and used for every row of the wave tile
+__device__ __forceinline__ void side_v4(const GemmParams& p, int col, uint2 (&e)[4]) {
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+    if (c < p.sf_n)
+      e[c] = *(const uint2*)((const bf16_t*)p.sf_vt +
+                             (int64_t)((c / p.sf_used) * p.sf_ks + c % p.sf_used) * p.sf_ldv + col);
+}
+
+// Adds y . V over four consecutive output columns to the lane's partial sums
+__device__ __forceinline__ void side_partial4(const GemmParams& p, floatx4_t y, const uint2 (&e)[4], float (&t)[4]) {
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+    if (c < p.sf_n) {
+      t[c] = fmaf(y[0], bf16_to_f32((bf16_t)(e[c].x & 0xFFFFu)), t[c]);
+      t[c] = fmaf(y[1], bf16_to_f32((bf16_t)(e[c].x >> 16)), t[c]);
+      t[c] = fmaf(y[2], bf16_to_f32((bf16_t)(e[c].y & 0xFFFFu)), t[c]);
+      t[c] = fmaf(y[3], bf16_to_f32((bf16_t)(e[c].y >> 16)), t[c]);
+    }
+}
+
+// The four lanes holding one row's columns of the wave tile (lane, +16, +32, +48) combine
+// their partial sums; the first writes the row's group partials
+template <int NC>
+__device__ __forceinline__ void side_partial_store(const GemmParams& p, int r, int grp, int lane, float (&t)[NC]) {
+#pragma unroll
+  for (int c = 0; c < NC; ++c) {
+    t[c] += __shfl_xor(t[c], 16, 64);
+    t[c] += __shfl_xor(t[c], 32, 64);
+  }
+  if (lane < 16 && r < p.M) {
+#pragma unroll
+    for (int c = 0; c < NC; ++c)
+      if (c < p.sf_n) p.sf_part[((int64_t)grp * p.M + r) * p.sf_n + c] = t[c];
+  }
+}
+
 template <int EPI, int TM, int TN, int BM, int BN, int WM, int WN, bool F8>
 __device__ __forceinline__ void epilogue_rows(const GemmParams& p, floatx4_t (&acc)[TM][TN], int m0, int n0, int wm,
                                               int wn, int lane, float* red) {
@@ -492,13 +545,19 @@ __device__ __forceinline__ void epilogue_rows(const GemmParams& p, floatx4_t (&a
   } else if constexpr (EPI == EPI_SWIGLU) {
     // packed rows: blocks of 16 gate rows then 16 up rows; output column = gate index
     const int ob = (n0 + wn * WN) / 2 + 4 * (lane >> 4);
+    const int grp = (n0 + wn * WN) / WN;              // 32 output columns a wave tile
+    float t[TM][4];
 #pragma unroll
-    for (int i = 0; i < TM; ++i) {
-      const int r = rb + i * 16;
-      if (r >= p.M) continue;
+    for (int i = 0; i < TM; ++i) t[i][0] = t[i][1] = t[i][2] = t[i][3] = 0.f;
 #pragma unroll
-      for (int jp = 0; jp < TN / 2; ++jp) {
-        if (cb + 2 * jp * 16 >= p.N) continue;                  // N is a multiple of 32 here
+    for (int jp = 0; jp < TN / 2; ++jp) {
+      if (cb + 2 * jp * 16 >= p.N) continue;                    // N is a multiple of 32 here
+      uint2 e[4];
+      if (p.sf_n) side_v4(p, ob + jp * 16, e);
+#pragma unroll
+      for (int i = 0; i < TM; ++i) {
+        const int r = rb + i * 16;
+        if (r >= p.M) continue;
         // (e4m3 main segments sum in units of 2^-11 of the result)
         constexpr float unit = F8 ? 1.0f / (float)(1 << ZO_FP8_WEIGHT_EXP) : 1.0f;
         const floatx4_t g = acc[i][2 * jp] * unit, u = acc[i][2 * jp + 1] * unit;
@@ -509,8 +568,12 @@ __device__ __forceinline__ void epilogue_rows(const GemmParams& p, floatx4_t (&a
           store_e4m3x4((e4m3_t*)p.C + (int64_t)r * p.ldc + ob + jp * 16, v);
         else
           store_bf16x4(p, (bf16_t*)p.C + (int64_t)r * p.ldc + ob + jp * 16, v);
+        if (p.sf_n) side_partial4(p, stored4<F8>(v), e, t[i]);
       }
     }
+    if (p.sf_n)
+#pragma unroll
+      for (int i = 0; i < TM; ++i) side_partial_store<4>(p, rb + i * 16, grp, lane, t[i]);   // every lane takes part
     return;
   } else {
     // a lane's four columns are all inside N or all outside (N is a multiple of 16)
@@ -519,6 +582,37 @@ __device__ __forceinline__ void epilogue_rows(const GemmParams& p, floatx4_t (&a
     for (int j = 0; j < TN; ++j)
       bias[j] = (p.bias && cb + j * 16 < p.N) ? *(const floatx4_t*)(p.bias + cb + j * 16)
                                               : floatx4_t{0.f, 0.f, 0.f, 0.f};
+    if constexpr (EPI == EPI_GELU) {
+      // column group outer, so the side input's V values are loaded once per group
+      const int grp = (n0 + wn * WN) / WN;            // 64 output columns a wave tile
+      float t[TM][4];
+#pragma unroll
+      for (int i = 0; i < TM; ++i) t[i][0] = t[i][1] = t[i][2] = t[i][3] = 0.f;
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        if (cb + j * 16 >= p.N) continue;
+        uint2 e[4];
+        if (p.sf_n) side_v4(p, cb + j * 16, e);
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+          const int r = rb + i * 16;
+          if (r >= p.M) continue;
+          constexpr float unit = F8 ? 1.0f / (float)(1 << ZO_FP8_WEIGHT_EXP) : 1.0f;
+          floatx4_t v = F8 ? acc[i][j] * unit + bias[j] : acc[i][j] + bias[j];
+#pragma unroll
+          for (int q = 0; q < 4; ++q) v[q] = gelu_fast(v[q]);
+          if constexpr (F8)            // the input of the next e4m3 projection
+            store_e4m3x4((e4m3_t*)p.C + (int64_t)r * p.ldc + cb + j * 16, v);
+          else
+            store_bf16x4(p, (bf16_t*)p.C + (int64_t)r * p.ldc + cb + j * 16, v);
+          if (p.sf_n) side_partial4(p, stored4<F8>(v), e, t[i]);
+        }
+      }
+      if (p.sf_n)
+#pragma unroll
+        for (int i = 0; i < TM; ++i) side_partial_store<4>(p, rb + i * 16, grp, lane, t[i]);   // every lane takes part
+      return;
+    }
 #pragma unroll
     for (int i = 0; i < TM; ++i) {
       const int r = rb + i * 16;
@@ -533,14 +627,6 @@ __device__ __forceinline__ void epilogue_rows(const GemmParams& p, floatx4_t (&a
           floatx4_t* hp = (floatx4_t*)(p.H + (int64_t)r * p.ldh + cb + j * 16);
           *hp = *hp + v;
         } else {
-          if constexpr (EPI == EPI_GELU) {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) v[q] = gelu_fast(v[q]);
-            if constexpr (F8) {        // the input of the next e4m3 projection
-              store_e4m3x4((e4m3_t*)p.C + (int64_t)r * p.ldc + cb + j * 16, v);
-              continue;
-            }
-          }
           if (EPI == EPI_STORE && p.c_f32)
             *(floatx4_t*)((float*)p.C + (int64_t)r * p.ldc + cb + j * 16) = v;
           else
@@ -1065,7 +1151,31 @@ side_dot_kernel(GemmParams p, int j0, int n_used) {
   }
 }
 
+// t of the projection that reads an epilogue's output: its group partials summed in order
+__global__ void side_part_reduce_kernel(GemmParams p) {
+  const int64_t n = (int64_t)p.M * p.sf_n;
+  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n; e += (int64_t)gridDim.x * blockDim.x) {
+    const int r = (int)(e / p.sf_n), c = (int)(e - (int64_t)r * p.sf_n);
+    const int cand = p.row_cand[r];
+    if (cand < 0) continue;
+    const float* pr = p.sf_part + e;                  // group-major: [groups][M][sf_n]
+    float v = 0.f;
+#pragma unroll 8
+    for (int g = 0; g < p.sf_groups; ++g) v += pr[(int64_t)g * n];   // loads in flight together, sums in order
+    tproj_out<bf16_t>(p, r, (c / p.tp_used) * p.tp_ks + c % p.tp_used, v, cand);
+  }
+}
+
 }  // namespace
+
+hipError_t launch_side_part_reduce(const GemmParams& p, hipStream_t s) {
+  const int64_t n = (int64_t)p.M * p.sf_n;
+  if (n <= 0) return hipSuccess;
+  int64_t blocks = (n + 255) / 256;
+  if (blocks > 8192) blocks = 8192;
+  hipLaunchKernelGGL(side_part_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p);
+  return hipGetLastError();
+}
 
 // Used factor columns of a side-input projection (the kind blocks times the used columns
 // of each block) when the streaming kernel serves it, else 0.

@@ -166,104 +166,126 @@ norm_kernel(const float* __restrict__ h, const int32_t* __restrict__ rows, int d
 // j % tp_used of that block; each thread sums its own elements, the wave's lanes are
 // combined by a butterfly and the four waves in order, and t goes through tproj_out like
 // the side-input projection's output.  One row per workgroup, no two-term outputs.
-template <typename T, int NC>
+// R rows per workgroup (R > 1: the thread's V^T values are loaded once into registers and
+// serve the R rows).  Launched with R = 1: at OPT-13B batch 64, R = 4 with q|k|v's six
+// columns held in registers halved the occupancy and took the norms from 6.2 to 9.5 ms per
+// step, more than the V^T reads through the caches cost.
+template <typename T, int NC, int R>
 __global__ void __launch_bounds__(NORM_THREADS)
-norm_side_kernel(const float* __restrict__ h, int d, const float* __restrict__ w, const float* __restrict__ b,
+norm_side_kernel(const float* __restrict__ h, int M, int d, const float* __restrict__ w, const float* __restrict__ b,
                  float eps, int rms, T* __restrict__ out, int64_t ld_out, GemmParams p, int n_used) {
   constexpr int NV = NORM_MAXV / 4;
+  constexpr bool HOLD = R > 1;
   __shared__ float sh[3 * (NORM_THREADS / 64)];
   __shared__ float red[NORM_THREADS / 64][NC];
-  const int m = blockIdx.x;
-  const float* x = h + (int64_t)m * d;
-  floatx4_t v[NV];
-  float s = 0.f;
-#pragma unroll
-  for (int k = 0; k < NV; ++k) {
-    const int i = 4 * (threadIdx.x + k * NORM_THREADS);
-    v[k] = i < d ? *(const floatx4_t*)(x + i) : floatx4_t{0.f, 0.f, 0.f, 0.f};
-    s += (v[k][0] + v[k][1]) + (v[k][2] + v[k][3]);
-  }
-  float mean = 0.f, scale;
-  if (!rms) {
-    float n = 0.f;
-#pragma unroll
-    for (int k = 0; k < NV; ++k) n += (4 * (threadIdx.x + k * NORM_THREADS) < d) ? 4.f : 0.f;
-    float mm = n > 0.f ? s / n : 0.f, m2 = 0.f;
-#pragma unroll
-    for (int k = 0; k < NV; ++k) {
-      const int i = 4 * (threadIdx.x + k * NORM_THREADS);
-      if (i < d) {
-        const floatx4_t c = v[k] - mm;
-        m2 += (c[0] * c[0] + c[1] * c[1]) + (c[2] * c[2] + c[3] * c[3]);
-      }
-    }
-    block_merge_moments(n, mm, m2, sh);
-    mean = mm;
-    scale = 1.0f / sqrtf(m2 / (float)d + eps);
-  } else {
-    float q = 0.f;
-#pragma unroll
-    for (int k = 0; k < NV; ++k) q += (v[k][0] * v[k][0] + v[k][1] * v[k][1]) + (v[k][2] * v[k][2] + v[k][3] * v[k][3]);
-    const float ms = block_sum(q, sh) / (float)d;
-    scale = 1.0f / sqrtf(ms + eps);
-  }
-  const int cand = p.row_cand[m];
-  T* o = out + (int64_t)m * ld_out;
-  float t[NC];
-#pragma unroll
-  for (int c = 0; c < NC; ++c) t[c] = 0.f;
   const bf16_t* vt[NC];
 #pragma unroll
   for (int c = 0; c < NC; ++c) {
     const int j = min(c, n_used - 1);
     vt[c] = (const bf16_t*)p.B + (int64_t)((j / p.tp_used) * p.tp_ks + j % p.tp_used) * p.ldb;
   }
+  uint2 vv[HOLD ? NC : 1][HOLD ? NV : 1];
+  if constexpr (HOLD) {
 #pragma unroll
-  for (int k = 0; k < NV; ++k) {
-    const int i = 4 * (threadIdx.x + k * NORM_THREADS);
-    if (i < d) {
-      floatx4_t y = (v[k] - mean) * scale * *(const floatx4_t*)(w + i);
-      if (b) y += *(const floatx4_t*)(b + i);
-      store4<T>(o + i, y);
-      if (cand >= 0) {
-        // the values the projection reads: y rounded to the output type
-        floatx4_t yr;
-        if constexpr (std::is_same<T, e4m3_t>::value) {
-          const uint32_t code = f32x4_to_e4m3(y[0], y[1], y[2], y[3]);
-          const u32x4_t wds = e4m3x8_to_bf16(make_uint2(code, 0u));
-          yr = floatx4_t{bf16_to_f32((bf16_t)(wds[0] & 0xFFFFu)), bf16_to_f32((bf16_t)(wds[0] >> 16)),
-                         bf16_to_f32((bf16_t)(wds[1] & 0xFFFFu)), bf16_to_f32((bf16_t)(wds[1] >> 16))};
-        } else {
+    for (int c = 0; c < NC; ++c)
 #pragma unroll
-          for (int q = 0; q < 4; ++q) yr[q] = bf16_to_f32(f32_to_bf16(y[q]));
+      for (int k = 0; k < NV; ++k) {
+        const int i = 4 * (threadIdx.x + k * NORM_THREADS);
+        vv[c][k] = i < d ? *(const uint2*)(vt[c] + i) : make_uint2(0u, 0u);
+      }
+  }
+  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  for (int rr = 0; rr < R; ++rr) {
+    const int m = blockIdx.x * R + rr;
+    if (m >= M) break;                               // workgroup-uniform
+    const float* x = h + (int64_t)m * d;
+    floatx4_t v[NV];
+    float s = 0.f;
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      const int i = 4 * (threadIdx.x + k * NORM_THREADS);
+      v[k] = i < d ? *(const floatx4_t*)(x + i) : floatx4_t{0.f, 0.f, 0.f, 0.f};
+      s += (v[k][0] + v[k][1]) + (v[k][2] + v[k][3]);
+    }
+    float mean = 0.f, scale;
+    if (!rms) {
+      float n = 0.f;
+#pragma unroll
+      for (int k = 0; k < NV; ++k) n += (4 * (threadIdx.x + k * NORM_THREADS) < d) ? 4.f : 0.f;
+      float mm = n > 0.f ? s / n : 0.f, m2 = 0.f;
+#pragma unroll
+      for (int k = 0; k < NV; ++k) {
+        const int i = 4 * (threadIdx.x + k * NORM_THREADS);
+        if (i < d) {
+          const floatx4_t c = v[k] - mm;
+          m2 += (c[0] * c[0] + c[1] * c[1]) + (c[2] * c[2] + c[3] * c[3]);
         }
+      }
+      block_merge_moments(n, mm, m2, sh);
+      mean = mm;
+      scale = 1.0f / sqrtf(m2 / (float)d + eps);
+    } else {
+      float q = 0.f;
 #pragma unroll
-        for (int c = 0; c < NC; ++c) {
-          const uint2 e = *(const uint2*)(vt[c] + i);
-          t[c] = fmaf(yr[0], bf16_to_f32((bf16_t)(e.x & 0xFFFFu)), t[c]);
-          t[c] = fmaf(yr[1], bf16_to_f32((bf16_t)(e.x >> 16)), t[c]);
-          t[c] = fmaf(yr[2], bf16_to_f32((bf16_t)(e.y & 0xFFFFu)), t[c]);
-          t[c] = fmaf(yr[3], bf16_to_f32((bf16_t)(e.y >> 16)), t[c]);
+      for (int k = 0; k < NV; ++k) q += (v[k][0] * v[k][0] + v[k][1] * v[k][1]) + (v[k][2] * v[k][2] + v[k][3] * v[k][3]);
+      const float ms = block_sum(q, sh) / (float)d;
+      scale = 1.0f / sqrtf(ms + eps);
+    }
+    const int cand = p.row_cand[m];
+    T* o = out + (int64_t)m * ld_out;
+    float t[NC];
+#pragma unroll
+    for (int c = 0; c < NC; ++c) t[c] = 0.f;
+#pragma unroll
+    for (int k = 0; k < NV; ++k) {
+      const int i = 4 * (threadIdx.x + k * NORM_THREADS);
+      if (i < d) {
+        floatx4_t y = (v[k] - mean) * scale * *(const floatx4_t*)(w + i);
+        if (b) y += *(const floatx4_t*)(b + i);
+        store4<T>(o + i, y);
+        if (cand >= 0) {
+          // the values the projection reads: y rounded to the output type
+          floatx4_t yr;
+          if constexpr (std::is_same<T, e4m3_t>::value) {
+            const uint32_t code = f32x4_to_e4m3(y[0], y[1], y[2], y[3]);
+            const u32x4_t wds = e4m3x8_to_bf16(make_uint2(code, 0u));
+            yr = floatx4_t{bf16_to_f32((bf16_t)(wds[0] & 0xFFFFu)), bf16_to_f32((bf16_t)(wds[0] >> 16)),
+                           bf16_to_f32((bf16_t)(wds[1] & 0xFFFFu)), bf16_to_f32((bf16_t)(wds[1] >> 16))};
+          } else {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) yr[q] = bf16_to_f32(f32_to_bf16(y[q]));
+          }
+#pragma unroll
+          for (int c = 0; c < NC; ++c) {
+            uint2 e;
+            if constexpr (HOLD) e = vv[c][k];
+            else e = *(const uint2*)(vt[c] + i);
+            t[c] = fmaf(yr[0], bf16_to_f32((bf16_t)(e.x & 0xFFFFu)), t[c]);
+            t[c] = fmaf(yr[1], bf16_to_f32((bf16_t)(e.x >> 16)), t[c]);
+            t[c] = fmaf(yr[2], bf16_to_f32((bf16_t)(e.y & 0xFFFFu)), t[c]);
+            t[c] = fmaf(yr[3], bf16_to_f32((bf16_t)(e.y >> 16)), t[c]);
+          }
         }
       }
     }
-  }
-  if (cand < 0) return;                              // workgroup-uniform: one row per workgroup
-  const int wv = threadIdx.x >> 6, lane = threadIdx.x & 63;
+    if (cand >= 0) {                                 // workgroup-uniform: one row at a time
 #pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    float a = t[c];
+      for (int c = 0; c < NC; ++c) {
+        float a = t[c];
 #pragma unroll
-    for (int sh_ = 32; sh_ >= 1; sh_ >>= 1) a += __shfl_xor(a, sh_, 64);
-    if (lane == 0) red[wv][c] = a;
-  }
-  __syncthreads();
-  if ((int)threadIdx.x < n_used) {
-    const int c = threadIdx.x;
-    float a = red[0][c];
+        for (int sh_ = 32; sh_ >= 1; sh_ >>= 1) a += __shfl_xor(a, sh_, 64);
+        if (lane == 0) red[wv][c] = a;
+      }
+      __syncthreads();
+      if ((int)threadIdx.x < n_used) {
+        const int c = threadIdx.x;
+        float a = red[0][c];
 #pragma unroll
-    for (int q = 1; q < NORM_THREADS / 64; ++q) a += red[q][c];
-    tproj_out<bf16_t>(p, m, (c / p.tp_used) * p.tp_ks + c % p.tp_used, a, cand);
+        for (int q = 1; q < NORM_THREADS / 64; ++q) a += red[q][c];
+        tproj_out<bf16_t>(p, m, (c / p.tp_used) * p.tp_ks + c % p.tp_used, a, cand);
+      }
+    }
+    __syncthreads();                                 // red and sh are reused by the next row
   }
 }
 
@@ -388,9 +410,12 @@ hipError_t launch_norm_side(const float* h, int M, int d, const float* w, const 
   if (d > NORM_THREADS * NORM_MAXV || d % 4 != 0 || ld_out % 4 != 0 || p.ldb % 4 != 0 || n_used < 1 || n_used > 16)
     return hipErrorInvalidValue;
   const int iu = rms ? 1 : 0;
-#define ZO_NORM_SIDE(NC_)                                                                                     \
-  hipLaunchKernelGGL((norm_side_kernel<T, NC_>), dim3(M), dim3(NORM_THREADS), 0, s, h, d, w, b, eps, iu, out, \
-                     ld_out, p, n_used)
+#define ZO_NORM_SIDE(NC_)                                                                                    \
+  do {                                                                                                       \
+    constexpr int R_ = 1;                                                                                    \
+    hipLaunchKernelGGL((norm_side_kernel<T, NC_, R_>), dim3((M + R_ - 1) / R_), dim3(NORM_THREADS), 0, s, h, \
+                       M, d, w, b, eps, iu, out, ld_out, p, n_used);                                        \
+  } while (0)
   if (n_used <= 2) ZO_NORM_SIDE(2);
   else if (n_used <= 4) ZO_NORM_SIDE(4);
   else if (n_used <= 6) ZO_NORM_SIDE(6);

@@ -41,6 +41,19 @@ __global__ void __launch_bounds__(256) read_kernel(const floatx4_t* __restrict__
   out[blockIdx.x * blockDim.x + threadIdx.x] = s[0] + s[1] + s[2] + s[3];
 }
 
+// R reads per write: dst[i] = src[i] + src[i + n] (+ src[i + 2n]), the read:write byte mix
+// of the norms (R = 2: fp32 in, bf16 out) and of attention (R = 3: q, k, v in, output out)
+template <int R>
+__global__ void __launch_bounds__(256) mix_kernel(const floatx4_t* __restrict__ src, floatx4_t* __restrict__ dst,
+                                                  int64_t n) {
+  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += (int64_t)gridDim.x * blockDim.x) {
+    floatx4_t v = src[i];
+#pragma unroll
+    for (int r = 1; r < R; ++r) v += src[i + r * n];
+    dst[i] = v;
+  }
+}
+
 float time_ms(void (*launch)(void*), void* arg, int reps) {
   hipEvent_t a, b;
   hipEventCreate(&a);
@@ -68,6 +81,16 @@ void launch_copy(void* p) {
   hipLaunchKernelGGL(copy_kernel, dim3(b->blocks), dim3(256), 0, 0, (const floatx4_t*)b->src, (floatx4_t*)b->dst,
                      b->n16);
 }
+void launch_mix2(void* p) {
+  Buf* b = (Buf*)p;
+  hipLaunchKernelGGL(mix_kernel<2>, dim3(b->blocks), dim3(256), 0, 0, (const floatx4_t*)b->src, (floatx4_t*)b->dst,
+                     b->n16);
+}
+void launch_mix3(void* p) {
+  Buf* b = (Buf*)p;
+  hipLaunchKernelGGL(mix_kernel<3>, dim3(b->blocks), dim3(256), 0, 0, (const floatx4_t*)b->src, (floatx4_t*)b->dst,
+                     b->n16);
+}
 void launch_read(void* p) {
   Buf* b = (Buf*)p;
   hipLaunchKernelGGL(read_kernel, dim3(b->blocks), dim3(256), 0, 0, (const floatx4_t*)b->src, (float*)b->dst,
@@ -91,6 +114,15 @@ double zo_peak_copy(const void* src, void* dst, int64_t bytes, int blocks) {
   Buf b = {(void*)src, dst, bytes / 16, blocks, 0};
   const float ms = time_ms(launch_copy, &b, 5);
   return 2.0 * (double)bytes / (ms * 1e-3) / 1e9;
+}
+
+// Streaming with `reads` (2 or 3) reads per write of `write_bytes` (multiple of 16): GB/s of
+// bytes read + written; src holds reads * write_bytes.
+double zo_peak_mix(const void* src, void* dst, int64_t write_bytes, int reads, int blocks) {
+  if (reads != 2 && reads != 3) return 0.0;
+  Buf b = {(void*)src, dst, write_bytes / 16, blocks, 0};
+  const float ms = time_ms(reads == 2 ? launch_mix2 : launch_mix3, &b, 5);
+  return (double)(reads + 1) * (double)write_bytes / (ms * 1e-3) / 1e9;
 }
 
 // Streaming read of `bytes`: GB/s; `out` holds blocks * 256 floats.

@@ -538,6 +538,7 @@ struct WsPtrs {
   unsigned char* side_begin = nullptr;
   size_t side_bytes = 0;
   float* tp_partial;
+  float* sf_part;               // partial sums of the FFN input's side input (fc1 / gate-up epilogue)
   float2* part;
   float* lab_logit;
   double *tok64, *seq_logp;
@@ -584,6 +585,14 @@ int64_t as_stride(const SideGeom& sg) {
   int64_t c = 0;
   for (int g = 0; g < 4; ++g) c = std::max(c, sg.as_cols[g]);
   return c;
+}
+
+// The side input of the last projection of the FFN (fc2 / down) formed in the epilogue of the
+// projection that writes its input (GELU / SwiGLU): bf16 and fp8 models, one-term
+// activations, at most 4 used factor columns.
+bool side_in_ffn_epilogue(const zo_model_desc& d, const zo_plan_s& p, const SideGeom& sg) {
+  return bf16_like(d) && !split_act(p) && sg.group_on.size() == 4 && sg.group_on[3] &&
+         (sg.vt_rows[3] / sg.ks_c) * (int64_t)(sg.nc * sg.r) <= 4;
 }
 
 int n_side_jobs(const zo_model_desc& d, const zo_plan_s& p, const SideGeom& sg) {
@@ -651,6 +660,10 @@ void carve(const zo_model* m, const zo_plan_s& p, const Packing& pk, const SideG
     }
     const int64_t n = std::max<int64_t>(np * M, kv_rows > 0 ? npd * std::max(pk.n_phys, 1) : 0);
     w.tp_partial = b.take<float>(std::max<int64_t>(n, 1));
+  }
+  {
+    const int64_t n1 = is_opt(d) ? F : 2 * F;           // columns of the fc1 / gate-up projection
+    w.sf_part = side_in_ffn_epilogue(d, p, sg) ? b.take<float>(M * ((n1 + 63) / 64) * 4) : nullptr;
   }
   const int bn_head = gemm_cfg_bn(GEMM_CFG_HEAD, bf16_like(d));
   const int64_t n_vt = (d.vocab + bn_head - 1) / bn_head;
@@ -895,6 +908,9 @@ int forward(zo_model* m, const zo_plan_s& p, const Packing& pk, const SideGeom& 
       ZO_HIP(norm_in(Wf(P[P_LN2W]), Wf(P[P_LN2B]), l, 2));
     }
     if (!side_in_norm(2) && (rc = tproj(l, 2, w.xa, D)) != ZO_OK) return rc;
+    // the FFN output projection's side input: in the fc1 / gate-up epilogue (not in the
+    // K-sliced decode-step projections)
+    const bool ffn_fused = w.sf_part && !(gen && gen->decode);
     {
       const int N1 = is_opt(d) ? F : 2 * F;
       GemmParams gp = proj(w.xa, W(P[P_W1]), N1, D);
@@ -902,9 +918,21 @@ int forward(zo_model* m, const zo_plan_s& p, const Packing& pk, const SideGeom& 
       gp.C = w.hid; gp.ldc = (int64_t)F * x2; gp.c_lo = sp ? F : 0;
       if (is_opt(d)) { gp.epi = EPI_GELU; gp.bias = Wf(P[P_B1]); }
       else gp.epi = EPI_SWIGLU;
+      if (ffn_fused) {
+        gp.sf_n = sg.nc * sg.r; gp.sf_used = sg.nc * sg.r; gp.sf_ks = sg.ks_c;
+        gp.sf_groups = (N1 + 63) / 64;
+        gp.sf_vt = w.vt[l * 4 + 3]; gp.sf_ldv = F;
+        gp.sf_part = w.sf_part;
+      }
       if ((rc = run_gemm(d, gp, big, s)) != ZO_OK) return rc;
+      if (ffn_fused) {
+        GemmParams rp = tproj_params(l, 3, w.hid, F);
+        rp.sf_n = gp.sf_n; rp.sf_groups = gp.sf_groups; rp.sf_part = w.sf_part;
+        ProfScope ps(ZO_PROF_GEMM_SIDE, s);
+        ZO_HIP(launch_side_part_reduce(rp, s));
+      }
     }
-    if ((rc = tproj(l, 3, w.hid, F)) != ZO_OK) return rc;
+    if (!ffn_fused && (rc = tproj(l, 3, w.hid, F)) != ZO_OK) return rc;
     {
       const TLoc& w2 = is_opt(d) ? P[P_W2] : P[P_WDOWN];
       GemmParams gp = proj(w.hid, W(w2), D, F);
