@@ -70,8 +70,9 @@ def measured_peaks():
     if not os.path.exists(path):
         return None
     L = ctypes.CDLL(path)
-    for f in (L.zo_peak_mfma_bf16, L.zo_peak_copy, L.zo_peak_read):
+    for f in (L.zo_peak_mfma_bf16, L.zo_peak_copy, L.zo_peak_read, L.zo_peak_mix):
         f.restype = ctypes.c_double
+    L.zo_peak_mix.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int]
     L.zo_peak_mfma_bf16.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int]
     L.zo_peak_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int]
     L.zo_peak_read.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int]
@@ -82,7 +83,12 @@ def measured_peaks():
     b = torch.empty_like(a)
     res = {"mfma_bf16_tflops": round(L.zo_peak_mfma_bf16(ctypes.c_void_p(out.data_ptr()), blocks, 2000), 1),
            "copy_gbs": round(L.zo_peak_copy(ctypes.c_void_p(a.data_ptr()), ctypes.c_void_p(b.data_ptr()), n, 4096), 1),
-           "read_gbs": round(L.zo_peak_read(ctypes.c_void_p(a.data_ptr()), ctypes.c_void_p(out.data_ptr()), n, 4096), 1)}
+           "read_gbs": round(L.zo_peak_read(ctypes.c_void_p(a.data_ptr()), ctypes.c_void_p(out.data_ptr()), n, 4096), 1),
+           # read:write byte mixes of the norms (2:1) and of attention (3:1)
+           "mix2_gbs": round(L.zo_peak_mix(ctypes.c_void_p(a.data_ptr()), ctypes.c_void_p(b.data_ptr()), n // 4, 2,
+                                           4096), 1),
+           "mix3_gbs": round(L.zo_peak_mix(ctypes.c_void_p(a.data_ptr()), ctypes.c_void_p(b.data_ptr()), n // 4, 3,
+                                           4096), 1)}
     del a, b, out
     torch.cuda.empty_cache()
     return res
@@ -447,8 +453,13 @@ def main():
             line["measured_peaks"] = pk
             if achieved and cfg.dtype == "bf16":
                 line["roofline"]["frac_of_measured_mfma"] = round(achieved / pk["mfma_bf16_tflops"], 4)
-            for v in hbm.values():
-                v["frac_of_measured_copy"] = round(v["achieved"] / pk["copy_gbs"], 4)
+            # each class against the streaming microbenchmark with its own read:write mix
+            matched = {"norm": "mix2_gbs", "attention": "mix3_gbs", "gemm_side": "read_gbs", "gemm_head": "read_gbs",
+                       "side_prep": "copy_gbs", "update": "copy_gbs"}
+            for k, v in hbm.items():
+                ref = matched.get(k, "copy_gbs")
+                v["matched_ceiling"] = ref
+                v["frac_of_matched_ceiling"] = round(v["achieved"] / pk[ref], 4)
     # side-path cost: the projections' time with the side columns vs a plan with no targets
     if wl.targets and not args.no_side_check:
         # scores with and without the side path, alternated so that clock drift between
