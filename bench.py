@@ -144,6 +144,15 @@ def hbm_bytes_per_step(cfg, wl, rows, scored, n_entries):
         if g in (0, 2) and cfg.dtype != "f32" and not split and len(kinds) * used <= 16:
             out["norm"] += len(tk) * used * n_in * 2 + rows * len(tk) * used * a
             continue
+        # group 3 (fc2 / down) with at most 4 used columns: the fc1 / gate-up epilogue writes
+        # per-64-column partial sums; the side-input class is then their ordered reduction
+        # (partials read once, t written once)
+        if g == 3 and cfg.dtype != "f32" and not split and used <= 4:
+            n1 = cfg.d_ffn * (1 if cfg.arch == "opt" else 2)
+            side += rows * ((n1 + 63) // 64) * used * 4 + rows * used * a
+            n_out = cfg.linear_shape(tk[0])[0]
+            prep += used * (n_in + n_out) * 2 + n_entries * r * n_out * 4
+            continue
         side += rows * n_in * ai + len(tk) * used * n_in * 2 * (3 if split else 1) + rows * len(tk) * used * a
         for k in tk:
             n_out = cfg.linear_shape(k)[0]

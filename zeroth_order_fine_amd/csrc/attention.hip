@@ -18,22 +18,47 @@
 namespace {
 
 constexpr int QB = 64;     // queries per workgroup
+#ifndef ATTN_PREFETCH
+#define ATTN_PREFETCH 1
+#endif
 constexpr int KB = 64;     // keys per LDS tile
 
+// Task of workgroup bid in a one-dimensional grid of n_work x hq: workgroups are dispatched
+// round-robin over the 8 XCDs, so each XCD is given a contiguous range of the task order
+// (key/value head, work item, query head of the group).  The query blocks of one sequence
+// and the query heads sharing a key/value head then run on one XCD at about the same time,
+// and the K / V rows the later ones read are still in that XCD's L2.
+__device__ __forceinline__ void attn_task(int bid, int n_work, int hq, int hkv, int& wi, int& h) {
+  const int total = n_work * hq;
+  const int xcd = bid & 7, local = bid >> 3;
+  const int per = total >> 3, rem = total & 7;
+  const int t = xcd < rem ? xcd * (per + 1) + local : rem * (per + 1) + (xcd - rem) * per + local;
+  const int grp = hq / hkv;
+  const int kvh = t / (n_work * grp);
+  const int r = t - kvh * n_work * grp;
+  wi = r / grp;
+  h = kvh * grp + r % grp;
+}
+
 // TO: output element type, bf16_t, or e4m3_t for the e4m3 input of an fp8 model's o-projection
+#ifndef ATTN_OCC128
+#define ATTN_OCC128 3
+#endif
 template <int HD, typename TO>
-__global__ void __launch_bounds__(256, 4)   // four waves per SIMD: the kernel waits on loads
+__global__ void __launch_bounds__(256, HD == 128 ? ATTN_OCC128 : 4)   // waves per SIMD: the kernel waits on loads
 attn_bf16_kernel(const bf16_t* __restrict__ qkv, int ld, TO* __restrict__ out, int ld_out,
-                 const int32_t* __restrict__ cu, const int32_t* __restrict__ work, int hq, int hkv, float scale_log2) {
+                 const int32_t* __restrict__ cu, const int32_t* __restrict__ work, int n_work, int hq, int hkv,
+                 float scale_log2) {
   constexpr int KS = HD / 32;        // MFMA k-steps over the head dimension
   constexpr int HB = HD / 16;        // 16-wide blocks of the head dimension
   __shared__ __align__(16) bf16_t sK[KB * HD];        // [key][hd], 16-byte chunks XOR-swizzled
   __shared__ __align__(16) bf16_t sVt[HD * (KB + 8)];  // [hd][key] (+8 pad)
   constexpr int VT_LD = KB + 8;
 
-  const int w = work[blockIdx.x];
+  int wi, h;
+  attn_task(blockIdx.x, n_work, hq, hkv, wi, h);
+  const int w = work[wi];
   const int seq = w >> 12, qblk = w & 4095;
-  const int h = blockIdx.y;
   const int kvh = h / (hq / hkv);
   const int base = cu[seq], len = cu[seq + 1] - base;
   const int q0 = qblk * QB;
@@ -59,28 +84,41 @@ attn_bf16_kernel(const bf16_t* __restrict__ qkv, int ld, TO* __restrict__ out, i
 
   const int q_last = min(q0 + QB, len) - 1;       // last valid query of the block
   const int n_kt = q_last / KB + 1;
-  for (int kt = 0; kt < n_kt; ++kt) {
-    const int k0 = kt * KB;
-    __syncthreads();
-    // stage K [64 x HD] and V^T [HD x 64]
-    constexpr int CH = HD / 8;                      // 16-byte chunks per row
-    for (int c = tid; c < KB * CH; c += 256) {
-      const int kr = c / CH, ch = c % CH;
+  // Staging of a 64-key tile: K [64 x HD] and V^T [HD x 64].  Every global load of the tile
+  // is issued before the first LDS write (one wait for all of them); with ATTN_PREFETCH the
+  // next tile's loads are issued before the current tile's products and land under them.
+  constexpr int CH = HD / 8;                        // 16-byte chunks per row
+  constexpr int NKC = KB * CH / 256;                // K chunks per thread
+  constexpr int NVG = (KB / 4) * CH;                // V^T groups (4 keys x one chunk)
+  static_assert(NKC * 256 == KB * CH && NVG <= 256, "staging shape");
+  u32x4_t kreg[NKC], vv[4];
+  auto load_tile = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < NKC; ++i) {
+      const int c = tid + i * 256, kr = c / CH, ch = c % CH;
       const int krow = base + min(k0 + kr, len - 1);
-      u32x4_t kv = *(const u32x4_t*)(qkv + (int64_t)krow * ld + kcol + ch * 8);
-      *(u32x4_t*)(sK + kr * HD + ((ch ^ (kr & SWZ)) << 3)) = kv;
+      kreg[i] = *(const u32x4_t*)(qkv + (int64_t)krow * ld + kcol + ch * 8);
     }
-    // V^T: a thread takes 4 consecutive keys of one 8-wide head-dim chunk, transposes
-    // them in registers and writes 8 rows of 4 keys (8 bytes each); the 16 lanes that
-    // share a chunk fill one 128-byte stretch of a V^T row
-    for (int c = tid; c < (KB / 4) * CH; c += 256) {
-      const int kg = c % (KB / 4), ch = c / (KB / 4);
-      u32x4_t vv[4];
+    if (tid < NVG) {
+      const int kg = tid % (KB / 4), ch = tid / (KB / 4);
 #pragma unroll
       for (int u = 0; u < 4; ++u) {
         const int krow = base + min(k0 + kg * 4 + u, len - 1);
         vv[u] = *(const u32x4_t*)(qkv + (int64_t)krow * ld + vcol + ch * 8);
       }
+    }
+  };
+  // V^T: a thread holds 4 consecutive keys of one 8-wide head-dim chunk, transposes them in
+  // registers and writes 8 rows of 4 keys (8 bytes each); the 16 lanes that share a chunk
+  // fill one 128-byte stretch of a V^T row
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int i = 0; i < NKC; ++i) {
+      const int c = tid + i * 256, kr = c / CH, ch = c % CH;
+      *(u32x4_t*)(sK + kr * HD + ((ch ^ (kr & SWZ)) << 3)) = kreg[i];
+    }
+    if (tid < NVG) {
+      const int kg = tid % (KB / 4), ch = tid / (KB / 4);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int wi = e >> 1, sh = (e & 1) * 16;
@@ -89,7 +127,15 @@ attn_bf16_kernel(const bf16_t* __restrict__ qkv, int ld, TO* __restrict__ out, i
         *(uint2*)(sVt + (ch * 8 + e) * VT_LD + kg * 4) = make_uint2(lo, hi);
       }
     }
+  };
+  if (ATTN_PREFETCH) load_tile(0);
+  for (int kt = 0; kt < n_kt; ++kt) {
+    const int k0 = kt * KB;
+    __syncthreads();                                // every wave is done with the previous tile
+    if (!ATTN_PREFETCH) load_tile(k0);
+    store_tile();
     __syncthreads();
+    if (ATTN_PREFETCH && kt + 1 < n_kt) load_tile(k0 + KB);
     // S^T[key][query] for 4 blocks of 16 keys
     floatx4_t s[4];
 #pragma unroll
@@ -103,29 +149,43 @@ attn_bf16_kernel(const bf16_t* __restrict__ qkv, int ld, TO* __restrict__ out, i
         s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ks], s[kb], 0, 0, 0);
       }
     }
-    // mask + scale (log2 domain)
+    // scale (log2 domain) and mask; a tile whose keys all precede the block's first query
+    // and lie inside the sequence needs no mask (workgroup-uniform)
     float mx = -INFINITY;
+    if (k0 + KB <= q0 + 1 && k0 + KB <= len) {
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+      for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int key = k0 + kb * 16 + 4 * g + j;
-        float v = s[kb][j] * scale_log2;
-        if (key > qi || key >= len) v = -INFINITY;
-        s[kb][j] = v;
-        mx = fmaxf(mx, v);
-      }
+        for (int j = 0; j < 4; ++j) {
+          s[kb][j] *= scale_log2;
+          mx = fmaxf(mx, s[kb][j]);
+        }
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int key = k0 + kb * 16 + 4 * g + j;
+          float v = s[kb][j] * scale_log2;
+          if (key > qi || key >= len) v = -INFINITY;
+          s[kb][j] = v;
+          mx = fmaxf(mx, v);
+        }
+    }
     mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
+    // Key 0 is unmasked for every query, so m_new is finite from the first tile on; the
+    // hardware exp2 then gives exactly 0 for masked scores (-inf) and for alpha on the first
+    // tile (m_run = -inf), and flushes results below 2^-126 (negligible probabilities) to 0.
     const float m_new = fmaxf(m_run, mx);
-    const float alpha = (m_run == -INFINITY) ? 0.f : exp2f(m_run - m_new);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
     float psum = 0.f;
     bf16x8_t pf[2];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float pv = (s[kb][j] == -INFINITY) ? 0.f : exp2f(s[kb][j] - m_new);
+        const float pv = __builtin_amdgcn_exp2f(s[kb][j] - m_new);
         psum += pv;
         pf[kb >> 1][(kb & 1) * 4 + j] = (__bf16)pv;
       }
@@ -194,7 +254,7 @@ __device__ __forceinline__ floatx4_t mfma3(bf16x8_t ah, bf16x8_t al, bf16x8_t bh
 template <int HD>
 __global__ void __launch_bounds__(256)
 attn_split_kernel(const float* __restrict__ qkv, int ld, bf16_t* __restrict__ out, int ld_out, int lo_off,
-                  const int32_t* __restrict__ cu, const int32_t* __restrict__ work, int hq, int hkv,
+                  const int32_t* __restrict__ cu, const int32_t* __restrict__ work, int n_work, int hq, int hkv,
                   float scale_log2) {
   constexpr int KS = HD / 32;
   constexpr int HB = HD / 16;
@@ -202,9 +262,10 @@ attn_split_kernel(const float* __restrict__ qkv, int ld, bf16_t* __restrict__ ou
   __shared__ __align__(16) bf16_t sK[2][KB * HD];        // hi, lo: [key][hd], 16-byte chunks XOR-swizzled
   __shared__ __align__(16) bf16_t sVt[2][HD * VT_LD];    // hi, lo: [hd][key] (+8 pad)
 
-  const int w = work[blockIdx.x];
+  int wi, h;
+  attn_task(blockIdx.x, n_work, hq, hkv, wi, h);
+  const int w = work[wi];
   const int seq = w >> 12, qblk = w & 4095;
-  const int h = blockIdx.y;
   const int kvh = h / (hq / hkv);
   const int base = cu[seq], len = cu[seq + 1] - base;
   const int q0 = qblk * QB;
@@ -233,38 +294,53 @@ attn_split_kernel(const float* __restrict__ qkv, int ld, bf16_t* __restrict__ ou
 
   const int q_last = min(q0 + QB, len) - 1;
   const int n_kt = q_last / KB + 1;
-  for (int kt = 0; kt < n_kt; ++kt) {
-    const int k0 = kt * KB;
-    __syncthreads();
-    constexpr int CH = HD / 8;                      // 8-element chunks per row
-    for (int c = tid; c < KB * CH; c += 256) {
-      const int kr = c / CH, ch = c % CH;
-      const int krow = base + min(k0 + kr, len - 1);
-      const float* src = qkv + (int64_t)krow * ld + kcol + ch * 8;
+  // staging as in the bf16 kernel: all global loads of a tile first (fp32), then the
+  // hi / lo split and the LDS writes
+  constexpr int CH = HD / 8;                        // 8-element chunks per row
+  constexpr int NKC = KB * CH / 256;                // K chunks per thread
+  constexpr int NVG = (KB / 4) * CH;                // V^T groups (4 keys x one chunk)
+  static_assert(NKC * 256 == KB * CH && NVG <= 256, "staging shape");
+  floatx4_t kreg[NKC][2], vreg[4][2];
+  auto load_tile = [&](int k0) {
+#pragma unroll
+    for (int i = 0; i < NKC; ++i) {
+      const int c = tid + i * 256, kr = c / CH, ch = c % CH;
+      const float* src = qkv + (int64_t)(base + min(k0 + kr, len - 1)) * ld + kcol + ch * 8;
+      kreg[i][0] = *(const floatx4_t*)src;
+      kreg[i][1] = *(const floatx4_t*)(src + 4);
+    }
+    if (tid < NVG) {
+      const int kg = tid % (KB / 4), ch = tid / (KB / 4);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float* src = qkv + (int64_t)(base + min(k0 + kg * 4 + u, len - 1)) * ld + vcol + ch * 8;
+        vreg[u][0] = *(const floatx4_t*)src;
+        vreg[u][1] = *(const floatx4_t*)(src + 4);
+      }
+    }
+  };
+  // V^T: 4 consecutive keys of one 8-wide head-dim chunk per thread, transposed in
+  // registers, 8-byte writes of 4 keys into 8 rows of each plane
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int i = 0; i < NKC; ++i) {
+      const int c = tid + i * 256, kr = c / CH, ch = c % CH;
       float v[8];
-      *(floatx4_t*)v = *(const floatx4_t*)src;
-      *(floatx4_t*)(v + 4) = *(const floatx4_t*)(src + 4);
+      *(floatx4_t*)v = kreg[i][0];
+      *(floatx4_t*)(v + 4) = kreg[i][1];
       bf16x8_t hi, lo;
       split8(v, hi, lo);
       const int o = kr * HD + ((ch ^ (kr & SWZ)) << 3);
       *(bf16x8_t*)(sK[0] + o) = hi;
       *(bf16x8_t*)(sK[1] + o) = lo;
     }
-    // V^T: 4 consecutive keys of one 8-wide head-dim chunk per thread, transposed in
-    // registers, 8-byte writes of 4 keys into 8 rows of each plane
-    for (int c = tid; c < (KB / 4) * CH; c += 256) {
-      const int kg = c % (KB / 4), ch = c / (KB / 4);
+    if (tid < NVG) {
+      const int kg = tid % (KB / 4), ch = tid / (KB / 4);
       bf16_t vh[4][8], vl[4][8];
 #pragma unroll
-      for (int u = 0; u < 4; ++u) {
-        const int krow = base + min(k0 + kg * 4 + u, len - 1);
-        const float* src = qkv + (int64_t)krow * ld + vcol + ch * 8;
-        float v[8];
-        *(floatx4_t*)v = *(const floatx4_t*)src;
-        *(floatx4_t*)(v + 4) = *(const floatx4_t*)(src + 4);
+      for (int u = 0; u < 4; ++u)
 #pragma unroll
-        for (int e = 0; e < 8; ++e) split_bf16(v[e], vh[u][e], vl[u][e]);
-      }
+        for (int e = 0; e < 8; ++e) split_bf16(vreg[u][e >> 2][e & 3], vh[u][e], vl[u][e]);
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const int o = (ch * 8 + e) * VT_LD + kg * 4;
@@ -274,6 +350,12 @@ attn_split_kernel(const float* __restrict__ qkv, int ld, bf16_t* __restrict__ ou
                                           (uint32_t)vl[2][e] | ((uint32_t)vl[3][e] << 16));
       }
     }
+  };
+  for (int kt = 0; kt < n_kt; ++kt) {
+    const int k0 = kt * KB;
+    __syncthreads();
+    load_tile(k0);
+    store_tile();
     __syncthreads();
     floatx4_t s[4];
 #pragma unroll
@@ -287,28 +369,39 @@ attn_split_kernel(const float* __restrict__ qkv, int ld, bf16_t* __restrict__ ou
         s[kb] = mfma3(kh, kl, qh[ks], ql[ks], s[kb]);
       }
     }
+    // scale and mask, then the softmax update, as in the bf16 kernel
     float mx = -INFINITY;
+    if (k0 + KB <= q0 + 1 && k0 + KB <= len) {
 #pragma unroll
-    for (int kb = 0; kb < 4; ++kb)
+      for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int key = k0 + kb * 16 + 4 * g + j;
-        float v = s[kb][j] * scale_log2;
-        if (key > qi || key >= len) v = -INFINITY;
-        s[kb][j] = v;
-        mx = fmaxf(mx, v);
-      }
+        for (int j = 0; j < 4; ++j) {
+          s[kb][j] *= scale_log2;
+          mx = fmaxf(mx, s[kb][j]);
+        }
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < 4; ++kb)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int key = k0 + kb * 16 + 4 * g + j;
+          float v = s[kb][j] * scale_log2;
+          if (key > qi || key >= len) v = -INFINITY;
+          s[kb][j] = v;
+          mx = fmaxf(mx, v);
+        }
+    }
     mx = fmaxf(mx, __shfl_xor(mx, 16, 64));
     mx = fmaxf(mx, __shfl_xor(mx, 32, 64));
     const float m_new = fmaxf(m_run, mx);
-    const float alpha = (m_run == -INFINITY) ? 0.f : exp2f(m_run - m_new);
+    const float alpha = __builtin_amdgcn_exp2f(m_run - m_new);
     float psum = 0.f;
     bf16x8_t ph[2], pl[2];
 #pragma unroll
     for (int kb = 0; kb < 4; ++kb)
 #pragma unroll
       for (int j = 0; j < 4; ++j) {
-        const float pv = (s[kb][j] == -INFINITY) ? 0.f : exp2f(s[kb][j] - m_new);
+        const float pv = __builtin_amdgcn_exp2f(s[kb][j] - m_new);
         psum += pv;
         bf16_t hb, lb;
         split_bf16(pv, hb, lb);
@@ -396,11 +489,12 @@ hipError_t launch_attention_bf16_to(const bf16_t* qkv, int ld_qkv, TO* out, int 
                                     const int32_t* work, int n_work, int hq, int hkv, int hd, hipStream_t s) {
   if (n_work <= 0) return hipSuccess;
   const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)hd));
-  dim3 grid(n_work, hq);
+  if ((int64_t)n_work * hq > 0x7fffffff || hq % hkv != 0) return hipErrorInvalidValue;
+  dim3 grid(n_work * hq);
   switch (hd) {
-    case 32: hipLaunchKernelGGL((attn_bf16_kernel<32, TO>), grid, dim3(256), 0, s, qkv, ld_qkv, out, ld_out, cu, work, hq, hkv, scale_log2); break;
-    case 64: hipLaunchKernelGGL((attn_bf16_kernel<64, TO>), grid, dim3(256), 0, s, qkv, ld_qkv, out, ld_out, cu, work, hq, hkv, scale_log2); break;
-    case 128: hipLaunchKernelGGL((attn_bf16_kernel<128, TO>), grid, dim3(256), 0, s, qkv, ld_qkv, out, ld_out, cu, work, hq, hkv, scale_log2); break;
+    case 32: hipLaunchKernelGGL((attn_bf16_kernel<32, TO>), grid, dim3(256), 0, s, qkv, ld_qkv, out, ld_out, cu, work, n_work, hq, hkv, scale_log2); break;
+    case 64: hipLaunchKernelGGL((attn_bf16_kernel<64, TO>), grid, dim3(256), 0, s, qkv, ld_qkv, out, ld_out, cu, work, n_work, hq, hkv, scale_log2); break;
+    case 128: hipLaunchKernelGGL((attn_bf16_kernel<128, TO>), grid, dim3(256), 0, s, qkv, ld_qkv, out, ld_out, cu, work, n_work, hq, hkv, scale_log2); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
@@ -443,11 +537,12 @@ hipError_t launch_attention_split(const float* qkv, int ld_qkv, bf16_t* out, int
   if (lo_off <= 0 || lo_off % 4 != 0 || ld_out % 4 != 0 || ld_qkv % 4 != 0) return hipErrorInvalidValue;
   if (n_work <= 0) return hipSuccess;
   const float scale_log2 = (float)(1.4426950408889634 / sqrt((double)hd));
-  dim3 grid(n_work, hq);
+  if ((int64_t)n_work * hq > 0x7fffffff || hq % hkv != 0) return hipErrorInvalidValue;
+  dim3 grid(n_work * hq);
   switch (hd) {
-    case 32: hipLaunchKernelGGL(attn_split_kernel<32>, grid, dim3(256), 0, s, qkv, ld_qkv, out, ld_out, lo_off, cu, work, hq, hkv, scale_log2); break;
-    case 64: hipLaunchKernelGGL(attn_split_kernel<64>, grid, dim3(256), 0, s, qkv, ld_qkv, out, ld_out, lo_off, cu, work, hq, hkv, scale_log2); break;
-    case 128: hipLaunchKernelGGL(attn_split_kernel<128>, grid, dim3(256), 0, s, qkv, ld_qkv, out, ld_out, lo_off, cu, work, hq, hkv, scale_log2); break;
+    case 32: hipLaunchKernelGGL(attn_split_kernel<32>, grid, dim3(256), 0, s, qkv, ld_qkv, out, ld_out, lo_off, cu, work, n_work, hq, hkv, scale_log2); break;
+    case 64: hipLaunchKernelGGL(attn_split_kernel<64>, grid, dim3(256), 0, s, qkv, ld_qkv, out, ld_out, lo_off, cu, work, n_work, hq, hkv, scale_log2); break;
+    case 128: hipLaunchKernelGGL(attn_split_kernel<128>, grid, dim3(256), 0, s, qkv, ld_qkv, out, ld_out, lo_off, cu, work, n_work, hq, hkv, scale_log2); break;
     default: return hipErrorInvalidValue;
   }
   return hipGetLastError();
