@@ -528,19 +528,19 @@ __device__ __forceinline__ void epilogue_rows(const GemmParams& p, floatx4_t (&a
   } else if constexpr (EPI == EPI_TPROJ) {
     // side input t: columns of x.[V...] kept for the bank entries, scaled by s * eps~
     // for the row's own direction, zero elsewhere (as in the register-staged epilogue)
-#pragma unroll
-    for (int i = 0; i < TM; ++i) {
+    static_for<0, TM>([&](auto i) {
       const int r = rb + i * 16;
-      if (r >= p.M) continue;
-      const int cand = p.row_cand[r];
-      if (cand < 0) continue;
-#pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        if (cb + j * 16 >= p.N) continue;
-#pragma unroll
-        for (int q = 0; q < 4; ++q) tproj_out<bf16_t>(p, r, cb + j * 16 + q, acc[i][j][q], cand);
+      const int cand = r < p.M ? p.row_cand[r] : -1;
+      if (cand >= 0) {
+        static_for<0, TN>([&](auto j) {
+          if (cb + j * 16 < p.N) {
+            static_for<0, 4>([&](auto q) {
+              tproj_out<bf16_t>(p, r, cb + j * 16 + q, acc[i][j][decltype(q)::value], cand);
+            });
+          }
+        });
       }
-    }
+    });
     return;
   } else if constexpr (EPI == EPI_SWIGLU) {
     // packed rows: blocks of 16 gate rows then 16 up rows; output column = gate index
@@ -689,6 +689,7 @@ gemm_bf16_pipe_kernel(GemmParams p) {
   const int mt = gm0 + in_g % gsize, nt = in_g / gsize;
   const int m0 = mt * BM, n0 = nt * BN;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int wave_s = __builtin_amdgcn_readfirstlane(wave);
   const int wm = wave / NWN, wn = wave % NWN;
   const int grp = (p.n_bounds > 0 && n0 >= p.bounds[0]) + (p.n_bounds > 1 && n0 >= p.bounds[1]) +
                   (p.n_bounds > 2 && n0 >= p.bounds[2]);
@@ -892,7 +893,12 @@ gemm_bf16_pipe_kernel(GemmParams p) {
     }
   }
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no LDS write outlives the workgroup
-  epilogue_rows<EPI, TM, TN, BM, BN, WM, WN, F8>(p, acc, m0, n0, wm, wn, lane, (float*)smem_raw);
+  // the epilogue's coordinates come from the wave index in a scalar register and the lane
+  // index counted afresh, so no vector register is kept live across the K loop (where every
+  // one is taken) for them
+  const int lane_e = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+  epilogue_rows<EPI, TM, TN, BM, BN, WM, WN, F8>(p, acc, m0, n0, wave_s / NWN, wave_s % NWN, lane_e,
+                                                (float*)smem_raw);
 }
 
 // ------------------------------------------------------------------------------
