@@ -549,15 +549,20 @@ __device__ __forceinline__ void epilogue_rows(const GemmParams& p, floatx4_t (&a
     float t[TM][4];
 #pragma unroll
     for (int i = 0; i < TM; ++i) t[i][0] = t[i][1] = t[i][2] = t[i][3] = 0.f;
+    // V values of the wave tile's output columns loaded once; rows outer (as in the GELU
+    // epilogue, so that a row's stores follow one another)
+    uint2 e[TN / 2][4];
+    if (p.sf_n)
 #pragma unroll
-    for (int jp = 0; jp < TN / 2; ++jp) {
-      if (cb + 2 * jp * 16 >= p.N) continue;                    // N is a multiple of 32 here
-      uint2 e[4];
-      if (p.sf_n) side_v4(p, ob + jp * 16, e);
+      for (int jp = 0; jp < TN / 2; ++jp)
+        if (cb + 2 * jp * 16 < p.N) side_v4(p, ob + jp * 16, e[jp]);
 #pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const int r = rb + i * 16;
-        if (r >= p.M) continue;
+    for (int i = 0; i < TM; ++i) {
+      const int r = rb + i * 16;
+      if (r >= p.M) continue;
+#pragma unroll
+      for (int jp = 0; jp < TN / 2; ++jp) {
+        if (cb + 2 * jp * 16 >= p.N) continue;                  // N is a multiple of 32 here
         // (e4m3 main segments sum in units of 2^-11 of the result)
         constexpr float unit = F8 ? 1.0f / (float)(1 << ZO_FP8_WEIGHT_EXP) : 1.0f;
         const floatx4_t g = acc[i][2 * jp] * unit, u = acc[i][2 * jp + 1] * unit;
@@ -568,7 +573,7 @@ __device__ __forceinline__ void epilogue_rows(const GemmParams& p, floatx4_t (&a
           store_e4m3x4((e4m3_t*)p.C + (int64_t)r * p.ldc + ob + jp * 16, v);
         else
           store_bf16x4(p, (bf16_t*)p.C + (int64_t)r * p.ldc + ob + jp * 16, v);
-        if (p.sf_n) side_partial4(p, stored4<F8>(v), e, t[i]);
+        if (p.sf_n) side_partial4(p, stored4<F8>(v), e[jp], t[i]);
       }
     }
     if (p.sf_n)
@@ -583,20 +588,25 @@ __device__ __forceinline__ void epilogue_rows(const GemmParams& p, floatx4_t (&a
       bias[j] = (p.bias && cb + j * 16 < p.N) ? *(const floatx4_t*)(p.bias + cb + j * 16)
                                               : floatx4_t{0.f, 0.f, 0.f, 0.f};
     if constexpr (EPI == EPI_GELU) {
-      // column group outer, so the side input's V values are loaded once per group
+      // the side input's V values of all the wave tile's columns are loaded once, before the
+      // rows; rows outer, so that the stores of one row's 64 columns follow one another (with
+      // the column blocks outer, the L2 wrote each output line back twice)
       const int grp = (n0 + wn * WN) / WN;            // 64 output columns a wave tile
       float t[TM][4];
 #pragma unroll
       for (int i = 0; i < TM; ++i) t[i][0] = t[i][1] = t[i][2] = t[i][3] = 0.f;
+      uint2 e[TN][4];
+      if (p.sf_n)
 #pragma unroll
-      for (int j = 0; j < TN; ++j) {
-        if (cb + j * 16 >= p.N) continue;
-        uint2 e[4];
-        if (p.sf_n) side_v4(p, cb + j * 16, e);
+        for (int j = 0; j < TN; ++j)
+          if (cb + j * 16 < p.N) side_v4(p, cb + j * 16, e[j]);
 #pragma unroll
-        for (int i = 0; i < TM; ++i) {
-          const int r = rb + i * 16;
-          if (r >= p.M) continue;
+      for (int i = 0; i < TM; ++i) {
+        const int r = rb + i * 16;
+        if (r >= p.M) continue;
+#pragma unroll
+        for (int j = 0; j < TN; ++j) {
+          if (cb + j * 16 >= p.N) continue;
           constexpr float unit = F8 ? 1.0f / (float)(1 << ZO_FP8_WEIGHT_EXP) : 1.0f;
           floatx4_t v = F8 ? acc[i][j] * unit + bias[j] : acc[i][j] + bias[j];
 #pragma unroll
@@ -605,7 +615,7 @@ __device__ __forceinline__ void epilogue_rows(const GemmParams& p, floatx4_t (&a
             store_e4m3x4((e4m3_t*)p.C + (int64_t)r * p.ldc + cb + j * 16, v);
           else
             store_bf16x4(p, (bf16_t*)p.C + (int64_t)r * p.ldc + cb + j * 16, v);
-          if (p.sf_n) side_partial4(p, stored4<F8>(v), e, t[i]);
+          if (p.sf_n) side_partial4(p, stored4<F8>(v), e[j], t[i]);
         }
       }
       if (p.sf_n)
