@@ -110,9 +110,11 @@ def group_kinds(cfg):
     return [("q", "k", "v"), ("o",), ("gate", "up"), ("down",)]
 
 
-def hbm_bytes_per_step(cfg, wl, rows, scored, n_entries):
+def hbm_bytes_per_step(cfg, wl, rows, scored, n_entries, n_shared=0):
     """Algorithmic HBM bytes per step of the bandwidth-bound kernel classes: every tensor
-    read or written once, no padding, no re-reads (the unit the HBM fractions use)."""
+    read or written once, no padding, no re-reads (the unit the HBM fractions use).
+    n_shared of the n_entries bank entries are the directions' own entries of the current
+    window, whose V is the direction's, so they add no side-input columns."""
     split = wl.act_split
     a = 2 * (2 if split else 1)          # bytes per activation element fed to a bf16 GEMM
     d, f, L = cfg.d_model, cfg.d_ffn, cfg.n_layers
@@ -122,7 +124,7 @@ def hbm_bytes_per_step(cfg, wl, rows, scored, n_entries):
         a = 4
     ai = 1 if cfg.dtype == "fp8" else a  # layer-linear inputs (e4m3 in fp8 models)
     r, q = wl.rank, wl.n_dirs
-    used = (n_entries + q) * r
+    used = (n_entries - n_shared + q) * r
     out = {}
     # embedding (+ learned positions), two norms per layer, final norm, QK-norm + RoPE
     nb = rows * d * (w * (2 if cfg.arch == "opt" else 1) + 4)
@@ -446,8 +448,11 @@ def main():
         "launches_per_step": {k: v[0] / n_bd for k, v in prof.items()},
     }
     # bandwidth-bound classes: algorithmic bytes per step / class time per step
-    n_entries = sum(1 for w in bank.keys()[1] if w >= 0)
-    hb = hbm_bytes_per_step(cfg, wl, rows, int(out["n_scored"]), n_entries)
+    seeds, wins = bank.keys()
+    n_entries = sum(1 for w in wins if w >= 0)
+    window = (args.warmup + args.steps - 1) // wl.nu
+    n_shared = sum(1 for s_, w in zip(seeds, wins) if w == window and s_ in wl.dir_seeds)
+    hb = hbm_bytes_per_step(cfg, wl, rows, int(out["n_scored"]), n_entries, n_shared)
     hbm = {}
     for k, b in hb.items():
         ms = prof[k][1] / n_bd
