@@ -63,17 +63,19 @@ def copy_calibration():
 
 def measured_peaks():
     """Ceilings measured on this GPU by the committed microbenchmarks (libzo_peaks.so): a
-    dense bf16 MFMA loop and a 1 GiB streaming copy; reported beside the published peaks."""
+    dense bf16 MFMA loop on constant and on random operands, and 1 GiB streaming copy / read
+    / mixed kernels; reported beside the published peaks."""
     import ctypes
     import torch
     path = os.path.join(ROOT, "zeroth_order_fine_amd", "libzo_peaks.so")
     if not os.path.exists(path):
         return None
     L = ctypes.CDLL(path)
-    for f in (L.zo_peak_mfma_bf16, L.zo_peak_copy, L.zo_peak_read, L.zo_peak_mix):
+    for f in (L.zo_peak_mfma_bf16, L.zo_peak_mfma_bf16_random, L.zo_peak_copy, L.zo_peak_read, L.zo_peak_mix):
         f.restype = ctypes.c_double
     L.zo_peak_mix.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int, ctypes.c_int]
     L.zo_peak_mfma_bf16.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int]
+    L.zo_peak_mfma_bf16_random.argtypes = [ctypes.c_void_p, ctypes.c_int, ctypes.c_int]
     L.zo_peak_copy.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int]
     L.zo_peak_read.argtypes = [ctypes.c_void_p, ctypes.c_void_p, ctypes.c_int64, ctypes.c_int]
     blocks = 1024
@@ -82,6 +84,9 @@ def measured_peaks():
     a = torch.ones(n // 4, dtype=torch.float32, device="cuda")
     b = torch.empty_like(a)
     res = {"mfma_bf16_tflops": round(L.zo_peak_mfma_bf16(ctypes.c_void_p(out.data_ptr()), blocks, 2000), 1),
+           # the same loop on random operands: the clock the matrix cores hold on real data
+           "mfma_bf16_random_tflops": round(L.zo_peak_mfma_bf16_random(ctypes.c_void_p(out.data_ptr()), blocks,
+                                                                       2000), 1),
            "copy_gbs": round(L.zo_peak_copy(ctypes.c_void_p(a.data_ptr()), ctypes.c_void_p(b.data_ptr()), n, 4096), 1),
            "read_gbs": round(L.zo_peak_read(ctypes.c_void_p(a.data_ptr()), ctypes.c_void_p(out.data_ptr()), n, 4096), 1),
            # read:write byte mixes of the norms (2:1) and of attention (3:1)
@@ -467,6 +472,7 @@ def main():
             line["measured_peaks"] = pk
             if achieved and cfg.dtype == "bf16":
                 line["roofline"]["frac_of_measured_mfma"] = round(achieved / pk["mfma_bf16_tflops"], 4)
+                line["roofline"]["frac_of_random_operand_mfma"] = round(achieved / pk["mfma_bf16_random_tflops"], 4)
             # each class against the streaming microbenchmark with its own read:write mix
             matched = {"norm": "mix2_gbs", "attention": "mix3_gbs", "gemm_side": "read_gbs", "gemm_head": "read_gbs",
                        "side_prep": "copy_gbs", "update": "copy_gbs"}

@@ -659,11 +659,14 @@ __device__ __forceinline__ void epilogue_rows(const GemmParams& p, floatx4_t (&a
 // the step's 2 x TM x TN MFMAs; one barrier per 64-deep step.  LDS holds
 // [A0 | A1 | B0 | B1], so the stage switch is an immediate offset of the LDS reads.
 // Within a 1 KB block (8 rows x 64 k, 128-byte rows) lane L of a load writes row L/8,
-// 16-byte chunk L%8, which holds logical chunk (L%8) ^ swz8(row): the fragment reads
-// (16 rows, one logical chunk) then fall on distinct banks.  Each output element is
+// 16-byte chunk L%8, which holds logical chunk (L%8) ^ swz8(row), swz8(row) = (row / 2) % 8:
+// a fragment read (16 consecutive rows, one logical chunk) then touches each 16-byte bank
+// group of the 256-byte LDS line once.  Measured with eight waves streaming the fragment
+// pattern: 209 bytes per clock per CU, against 118 for (row ^ row / 8) % 8 (which spreads
+// only 8-row phases) and 176 for plain contiguous 1 KB reads.  Each output element is
 // accumulated by the same MFMA sequence (k ascending, 32 per instruction) for every
 // workgroup and wave tile shape.
-__device__ __forceinline__ int swz8(int r) { return (r ^ (r >> 3)) & 7; }
+__device__ __forceinline__ int swz8(int r) { return (r >> 1) & 7; }
 
 // buffer resource over `bytes` bytes at `base` (raw addressing: offsets past the end read 0)
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void* base, int64_t bytes) {
@@ -726,8 +729,8 @@ gemm_bf16_pipe_kernel(GemmParams p) {
   // 8 * chunk for bf16) is recomputed where needed rather than kept
   auto a_row = [&](int i) { return min(m0 + (wave * IA + i) * 8 + lrow, p.M - 1); };
   auto b_row = [&](int i) { return min(n0 + (wave * IB + i) * 8 + lrow, p.N - 1); };
-  auto a_chk = [&](int i) { return (lane & 7) ^ ((lrow ^ (wave * IA + i)) & 7); };
-  auto b_chk = [&](int i) { return (lane & 7) ^ ((lrow ^ (wave * IB + i)) & 7); };
+  auto a_chk = [&](int i) { return (lane & 7) ^ swz8((wave * IA + i) * 8 + lrow); };
+  auto b_chk = [&](int i) { return (lane & 7) ^ swz8((wave * IB + i) * 8 + lrow); };
   auto a_elem = [&](int i, int ld) { return a_row(i) * ld + (a_chk(i) << 3); };
   auto b_elem = [&](int i, int ld) { return b_row(i) * ld + (b_chk(i) << 3); };
   // byte offsets: the host keeps every operand under 2^31 elements, so they fit 32 unsigned

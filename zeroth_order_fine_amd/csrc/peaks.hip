@@ -1,6 +1,8 @@
 // Microbenchmarks for the measured ceilings bench.py reports beside the published
 // peaks: a dense bf16 MFMA loop (16 independent accumulators per wave, four waves per
-// SIMD) and a streaming copy / read over a buffer much larger than the caches.  Not
+// SIMD), once on constant operands and once on random ones (the matrix cores draw more
+// power, and the clock drops, when the operand bits toggle as they do in a real product),
+// and a streaming copy / read over a buffer much larger than the caches.  Not
 // part of the method; built into a separate library that only bench.py loads.
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -21,6 +23,34 @@ __global__ void __launch_bounds__(256) mfma_loop(float* out, int iters) {
   for (int it = 0; it < iters; ++it) {
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, acc[i], 0, 0, 0);
+  }
+  float s = 0.f;
+  for (int i = 0; i < 16; ++i) s += acc[i][0] + acc[i][1] + acc[i][2] + acc[i][3];
+  out[blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
+__device__ __forceinline__ uint32_t mix32(uint32_t x) {
+  x ^= x >> 16; x *= 0x7feb352du; x ^= x >> 15; x *= 0x846ca68bu; x ^= x >> 16;
+  return x;
+}
+
+// The same loop on random operands: per lane two A fragments uniform in [-1, 1) and two B
+// fragments uniform in [-0.05, 0.05) (the ranges of normalised activations and of the
+// weights), alternated so that consecutive MFMAs see different operand bits.
+__global__ void __launch_bounds__(256) mfma_loop_random(float* out, int iters) {
+  bf16x8_t a[2], b[2];
+  for (int v = 0; v < 2; ++v)
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t h = mix32((blockIdx.x * 256u + threadIdx.x) * 977u + i * 31u + v * 7u);
+      a[v][i] = (__bf16)((float)(h & 0xffffu) / 32768.0f - 1.0f);
+      b[v][i] = (__bf16)((float)(h >> 16) / 655360.0f - 0.05f);
+    }
+  floatx4_t acc[16];
+  for (int i = 0; i < 16; ++i) acc[i] = floatx4_t{0.f, 0.f, 0.f, 0.f};
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int i = 0; i < 16; ++i)
+      acc[i] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a[i & 1], b[(i >> 1) & 1], acc[i], 0, 0, 0);
   }
   float s = 0.f;
   for (int i = 0; i < 16; ++i) s += acc[i][0] + acc[i][1] + acc[i][2] + acc[i][3];
@@ -76,6 +106,10 @@ void launch_mfma(void* p) {
   Buf* b = (Buf*)p;
   hipLaunchKernelGGL(mfma_loop, dim3(b->blocks), dim3(256), 0, 0, (float*)b->dst, b->iters);
 }
+void launch_mfma_random(void* p) {
+  Buf* b = (Buf*)p;
+  hipLaunchKernelGGL(mfma_loop_random, dim3(b->blocks), dim3(256), 0, 0, (float*)b->dst, b->iters);
+}
 void launch_copy(void* p) {
   Buf* b = (Buf*)p;
   hipLaunchKernelGGL(copy_kernel, dim3(b->blocks), dim3(256), 0, 0, (const floatx4_t*)b->src, (floatx4_t*)b->dst,
@@ -105,6 +139,14 @@ extern "C" {
 double zo_peak_mfma_bf16(void* scratch, int blocks, int iters) {
   Buf b = {nullptr, scratch, 0, blocks, iters};
   const float ms = time_ms(launch_mfma, &b, 3);
+  const double flop = (double)blocks * 4 * iters * 16 * (2.0 * 16 * 16 * 32);
+  return flop / (ms * 1e-3) / 1e12;
+}
+
+// The same on random operands (see mfma_loop_random).
+double zo_peak_mfma_bf16_random(void* scratch, int blocks, int iters) {
+  Buf b = {nullptr, scratch, 0, blocks, iters};
+  const float ms = time_ms(launch_mfma_random, &b, 3);
   const double flop = (double)blocks * 4 * iters * 16 * (2.0 * 16 * 16 * 32);
   return flop / (ms * 1e-3) / 1e12;
 }
