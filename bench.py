@@ -316,6 +316,42 @@ def generation_bench(args, wl, model, bank, batch, db):
     print(json.dumps(line), flush=True)
 
 
+def sites_bench(args, wl, model, db):
+    """The precision / cost trade-off of two-term activations at single rounding sites
+    (ZO_PLAN_SPLIT_*): for each site mask, score time and the per-sequence error against the
+    oracle's expected values for this workload (tests/golden/<workload>_step1.json)."""
+    import torch
+
+    import zeroth_order_fine_amd as zo
+    A = zo.api
+    sites = {"none": 0, "qkv_in": A.PLAN_SPLIT_QKV_IN, "attn": A.PLAN_SPLIT_ATTN, "fc1_in": A.PLAN_SPLIT_FC1_IN,
+             "fc2_in": A.PLAN_SPLIT_FC2_IN, "head": A.PLAN_SPLIT_HEAD,
+             "attn+qkv_in": A.PLAN_SPLIT_ATTN | A.PLAN_SPLIT_QKV_IN,
+             "attn+qkv_in+fc1_in": A.PLAN_SPLIT_ATTN | A.PLAN_SPLIT_QKV_IN | A.PLAN_SPLIT_FC1_IN,
+             "all": A.PLAN_ACT_SPLIT}
+    base = wl.with_(act_split=False)
+    rows = []
+    for name, bits in sites.items():
+        w = base.with_(split_sites=bits)
+        acc = accuracy_vs_golden(args.workload, w, model, db)
+        bank = zo.Bank(model, 2 * w.n_dirs, w.rank, w.targets)
+        plan = zo.Plan.from_workload(model, w, t=1)
+        zo.score(model, plan, bank, db)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(max(1, args.steps)):
+            zo.score(model, plan, bank, db)
+        torch.cuda.synchronize()
+        ms = (time.perf_counter() - t0) / max(1, args.steps) * 1e3
+        del bank, plan
+        row = {"sites": name, "flags": bits, "score_ms": round(ms, 2)}
+        if acc:
+            row.update(acc)
+        rows.append(row)
+        print(json.dumps(row), flush=True)
+    print(json.dumps({"workload": args.workload, "split_sites": rows}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -334,6 +370,9 @@ def main():
                     help="replay zo_score's forward pass from a captured HIP graph (launch-bound small "
                          "workloads); the timed steps then carry no per-launch events and the roofline "
                          "comes from the eagerly launched breakdown steps")
+    ap.add_argument("--sites", action="store_true",
+                    help="score time and accuracy against the oracle's expected values of two-term activations "
+                         "at each single rounding site (and a few combinations) instead of the ZO step")
     ap.add_argument("--generate", type=int, default=0, metavar="N",
                     help="time greedy generation of N tokens per sequence (zo_generate) instead of the ZO step")
     args = ap.parse_args()
@@ -366,6 +405,9 @@ def main():
     model.set_graphs(args.graphs)
     if args.generate:
         generation_bench(args, wl, model, bank, batch, db)
+        return
+    if args.sites:
+        sites_bench(args, wl, model, db)
         return
 
     score_s = [0.0]
@@ -539,23 +581,36 @@ def main():
             extra["score_ms_foreground_only"] = round(score_ms(bank, zo.DeviceBatch(fg)), 3)
             extra["foreground_only_tokens_per_s"] = round(fg_tokens / (extra["score_ms_foreground_only"] / 1e3), 1)
         if not wl.act_split and cfg.dtype == "bf16":
-            # the same step with two-term activations (what keeps c within 1e-2 at eps = 1e-3)
-            wl2 = wl.with_(act_split=True)
-            bank2 = zo.Bank(model, 2 * wl.n_dirs, wl.rank, wl.targets)
-            for t in range(2):
-                p2 = zo.Plan.from_workload(model, wl2, t=t)
-                zo.update(model, p2, bank2, zo.estimate(p2, zo.score(model, p2, bank2, db)["S"]), args.lr)
-            torch.cuda.synchronize()
-            a = time.perf_counter()
-            n2 = 3
-            for t in range(2, 2 + n2):
-                p2 = zo.Plan.from_workload(model, wl2, t=t)
-                zo.update(model, p2, bank2, zo.estimate(p2, zo.score(model, p2, bank2, db)["S"]), args.lr)
-            torch.cuda.synchronize()
-            ms2 = (time.perf_counter() - a) / n2 * 1e3
+            def step_ms(wl2):
+                bank2 = zo.Bank(model, 2 * wl.n_dirs, wl.rank, wl.targets)
+                for t in range(2):
+                    p2 = zo.Plan.from_workload(model, wl2, t=t)
+                    zo.update(model, p2, bank2, zo.estimate(p2, zo.score(model, p2, bank2, db)["S"]), args.lr)
+                torch.cuda.synchronize()
+                a = time.perf_counter()
+                n2 = 3
+                for t in range(2, 2 + n2):
+                    p2 = zo.Plan.from_workload(model, wl2, t=t)
+                    zo.update(model, p2, bank2, zo.estimate(p2, zo.score(model, p2, bank2, db)["S"]), args.lr)
+                torch.cuda.synchronize()
+                del bank2
+                return (time.perf_counter() - a) / n2 * 1e3
+            # the same step with two-term activations everywhere (what keeps c within 1e-2 at
+            # eps = 1e-3), and at the three rounding sites that carry most of the error here
+            # (attention, and the inputs of the q|k|v and fc1 projections; not the fc2 input)
+            ms2 = step_ms(wl.with_(act_split=True))
             extra["two_term_ms_per_step"] = round(ms2, 3)
             extra["two_term_tokens_per_s"] = round(probe_tokens / (ms2 / 1e3), 1)
-            del bank2
+            A = zo.api
+            wl3 = wl.with_(split_sites=A.PLAN_SPLIT_ATTN | A.PLAN_SPLIT_QKV_IN | A.PLAN_SPLIT_FC1_IN)
+            ms3 = step_ms(wl3)
+            three = {"flags": wl3.split_sites, "ms_per_step": round(ms3, 3),
+                     "tokens_per_s": round(probe_tokens / (ms3 / 1e3), 1)}
+            if not args.no_side_check:
+                acc3 = accuracy_vs_golden(args.workload, wl3, model, db)
+                if acc3:
+                    three["accuracy_vs_oracle"] = acc3
+            extra["split_attn_qkv_fc1"] = three
         line["other_states"] = extra
     if not args.no_side_check:
         acc = accuracy_vs_golden(args.workload, wl, model, db)

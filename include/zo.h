@@ -85,7 +85,7 @@ enum { ZO_ARCH_OPT = 0, ZO_ARCH_QWEN3 = 1 };
    the e4m3 encoding is the one of "FP8 Formats for Deep Learning", which that page's
    list of prior work names.  Requires d_model, d_ffn and n_heads * head_dim multiples
    of 128; not with
-   ZO_PLAN_ACT_SPLIT; side-input projections of at most 128 columns; zo_bank_fold
+   ZO_PLAN_ACT_SPLIT or ZO_PLAN_SPLIT_*; side-input projections of at most 128 columns; zo_bank_fold
    requantizes the folded weights to e4m3. */
 enum { ZO_DTYPE_F32 = 0, ZO_DTYPE_BF16 = 1, ZO_DTYPE_FP8 = 2 };
 enum { ZO_ROLE_PROBE = 0, ZO_ROLE_FOREGROUND = 1 };
@@ -108,7 +108,19 @@ enum { ZO_KIND_Q = 0, ZO_KIND_K = 1, ZO_KIND_V = 2, ZO_KIND_O = 3,
                                         factors, and run attention in fp32.  Twice the MFMA work of the
                                         projections; for summed long-sequence losses and deep stacks, where
                                         bf16 activation rounding alone moves a sequence's sum by more than
-                                        2e-2.  ZO_E_INVAL on fp32 models. */
+                                        2e-2.  Same as all five ZO_PLAN_SPLIT_* flags below.  ZO_E_INVAL on
+                                        fp32 and fp8 models. */
+/* The two-term expansion at one rounding site only (bf16 models; any combination; ACT_SPLIT sets
+   them all).  Each doubles the K extent of the projections that read the site (the cost is that
+   projection's share of the MFMA work) and takes the site's side-input projection and side segment
+   to three-term products: */
+#define ZO_PLAN_SPLIT_QKV_IN 8u      /* first norm output -> packed q|k|v projection */
+#define ZO_PLAN_SPLIT_ATTN 16u       /* q|k|v kept fp32, three-term attention products, attention
+                                        output -> o projection */
+#define ZO_PLAN_SPLIT_FC1_IN 32u     /* second norm output -> fc1 / gate-up projection */
+#define ZO_PLAN_SPLIT_FC2_IN 64u     /* GELU / SwiGLU output -> fc2 / down projection */
+#define ZO_PLAN_SPLIT_HEAD 128u      /* final norm output -> vocabulary head */
+#define ZO_PLAN_SPLIT_SITES 248u     /* the five flags above */
 
 /* zo_estimate flags */
 #define ZO_EST_INV_RANK 1u  /* divide c by r: the explicit 1/r of LoZO's estimator, which the
@@ -310,7 +322,7 @@ int zo_score_noalloc(zo_model* m, const zo_plan_t* p, const zo_bank* bank, const
  *   S_host:     host fp64 [n_cand] out, per candidate the sum over its sequences of the
  *               generated tokens' log-probabilities (the generative objective, for
  *               zo_estimate).
- * Sequences are in zo_pack's order.  fp32, bf16 and fp8 models; not with ZO_PLAN_ACT_SPLIT;
+ * Sequences are in zo_pack's order.  fp32, bf16 and fp8 models; not with ZO_PLAN_ACT_SPLIT or ZO_PLAN_SPLIT_*;
  * prompt length + n_new - 1 <= max_pos.  The batch's score modes are validated but not
  * used.  zo_generate_layout gives n_phys and the workspace bytes (the cache takes
  * 2 x n_layers x (sum of prompt lengths + n_phys (n_new - 1)) x n_kv_heads x head_dim

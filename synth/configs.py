@@ -68,6 +68,8 @@ class Workload:
     # products: a precision choice of the GPU path for summed long-sequence losses and deep
     # stacks; the oracle is exact either way
     act_split: bool = False
+    # the same at single rounding sites only (a mask of the library's two-term site flags)
+    split_sites: int = 0
 
     @property
     def n_dirs(self):

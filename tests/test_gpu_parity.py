@@ -99,6 +99,37 @@ def test_small_models_with_bank_and_ragged_rows(cfg, split):
         first += len(ref)
 
 
+@pytest.mark.parametrize("cfg", [SMALL_OPT_BF16, SMALL_QWEN_BF16], ids=["opt-bf16", "qwen3-bf16"])
+def test_single_split_sites(cfg):
+    """Two-term activations at one rounding site at a time (ZO_PLAN_SPLIT_*): every site alone
+    and two combinations score within the bf16 bound of the oracle, and the five site flags
+    together give bitwise the results of ZO_PLAN_ACT_SPLIT (so each site's buffers, pitches
+    and wraps are the ones the all-sites mode uses)."""
+    need_gpu()
+    import zeroth_order_fine_amd as zo
+    A = zo.api
+    sites = {"qkv": A.PLAN_SPLIT_QKV_IN, "attn": A.PLAN_SPLIT_ATTN, "fc1": A.PLAN_SPLIT_FC1_IN,
+             "fc2": A.PLAN_SPLIT_FC2_IN, "head": A.PLAN_SPLIT_HEAD,
+             "attn+fc2": A.PLAN_SPLIT_ATTN | A.PLAN_SPLIT_FC2_IN, "qkv+head": A.PLAN_SPLIT_QKV_IN | A.PLAN_SPLIT_HEAD}
+    wl = workload(cfg, dir_seeds=(3, 8), n_fg=2, n_prompts=3)
+    batch = inputs.make_batch(wl)
+    g, o = GpuRun(wl), OracleRun(wl)
+    for t in (0, 3, 5):                      # windows 0, 0, 1: a frozen entry and an active one
+        c = np.array([0.9, -1.7]) if t == 0 else np.array([-2.5, 0.4])
+        g.update(t, c, 5e-3)
+        o.update(t, c, 5e-3)
+    ref = o.score(6, batch)
+    for name, bits in sites.items():
+        out = g.score(6, batch, flags=bits)
+        err = _seq_close(out, ref, 2e-2)
+        flush("site %s: max per-sequence err %.3g" % (name, err))
+    all5 = g.score(6, batch, flags=sum(v for k, v in sites.items() if "+" not in k))
+    act = g.score(6, batch, flags=A.PLAN_ACT_SPLIT)
+    for key in ("seq_logp", "tok_logp"):
+        a, b = all5[key].cpu().numpy(), act[key].cpu().numpy()
+        assert np.array_equal(a.view(np.uint8), b.view(np.uint8)), key
+
+
 @pytest.mark.parametrize("n_prompts,len_lo", [(4, 5), (72, 100)], ids=["small-batch", "tile-switch"])
 def test_foreground_bitwise_invariance(n_prompts, len_lo):
     """Foreground rows are bitwise identical whether batched alone or alongside probes.

@@ -118,8 +118,15 @@ def test_plan_validation_errors(zlib):
     assert _plan(zlib, m, wl, nu=0)[0] == -1
     assert _plan(zlib, m, wl, cand=((1, 1),))[0] == -1
     assert _plan(zlib, m, wl, cand=((0, 2),))[0] == -1
-    assert _plan(zlib, m, wl, flags=8)[0] == -1
+    assert _plan(zlib, m, wl, flags=4)[0] == -1            # two-term activations: bf16 models only
+    assert _plan(zlib, m, wl, flags=8)[0] == -1            # and so are the single-site flags
+    assert _plan(zlib, m, wl, flags=256)[0] == -1          # unknown flag
     assert b"sign" in zlib.zo_last_error() or True
+    wb = configs.CONFIGS["opt1.3b"]
+    mb = _M(zlib, wb.model)
+    for flags in (4, 8, 16, 32, 64, 128, 248, 4 | 248, 16 | 64):
+        assert _plan(zlib, mb, wb, flags=flags)[0] == 0, flags
+    assert _plan(zlib, mb, wb, flags=256)[0] == -1
 
 
 def _batch_desc(batch):

@@ -15,6 +15,8 @@ ARCH = {"opt": 0, "qwen3": 1}
 DTYPE = {"f32": 0, "bf16": 1, "fp8": 2}
 KINDS = {"opt": ("q", "k", "v", "o", "fc1", "fc2"), "qwen3": ("q", "k", "v", "o", "gate", "up", "down")}
 PLAN_SCALE_INV_SQRT_R, PLAN_ALLOW_ZERO_EPS, PLAN_ACT_SPLIT = 1, 2, 4
+# two-term activations at single rounding sites (PLAN_ACT_SPLIT = all five)
+PLAN_SPLIT_QKV_IN, PLAN_SPLIT_ATTN, PLAN_SPLIT_FC1_IN, PLAN_SPLIT_FC2_IN, PLAN_SPLIT_HEAD = 8, 16, 32, 64, 128
 EST_INV_RANK, EST_MEAN = 1, 2
 NOALLOC_SCRATCH_BYTES = 256 << 20    # ZO_NOALLOC_SCRATCH_BYTES
 ROLE_PROBE, ROLE_FOREGROUND = 0, 1
@@ -143,7 +145,8 @@ class Plan:
     @classmethod
     def from_workload(cls, model, wl, t=0, eps=None, flags=None, candidates=None):
         if flags is None:
-            flags = (PLAN_SCALE_INV_SQRT_R if wl.scale_inv_sqrt_r else 0) | (PLAN_ACT_SPLIT if wl.act_split else 0)
+            flags = ((PLAN_SCALE_INV_SQRT_R if wl.scale_inv_sqrt_r else 0) | (PLAN_ACT_SPLIT if wl.act_split else 0)
+                     | wl.split_sites)
         return cls(model, t, wl.nu, wl.rank, wl.eps if eps is None else eps, wl.dir_seeds,
                    wl.candidates if candidates is None else candidates, wl.targets, flags)
 

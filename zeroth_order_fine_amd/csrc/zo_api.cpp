@@ -577,7 +577,18 @@ int tproj_split_decode(const zo_model_desc& d, int64_t n_cols, int64_t k) {
 }
 
 size_t act_size(const zo_model_desc& d) { return bf16_like(d) ? 2 : 4; }
-bool split_act(const zo_plan_s& p) { return (p.flags & ZO_PLAN_ACT_SPLIT) != 0; }
+// Two-term rounding sites of a plan (ZO_PLAN_ACT_SPLIT = all of them)
+uint32_t split_sites(const zo_plan_s& p) {
+  return (p.flags & ZO_PLAN_ACT_SPLIT) ? (uint32_t)ZO_PLAN_SPLIT_SITES : (p.flags & ZO_PLAN_SPLIT_SITES);
+}
+bool split_act(const zo_plan_s& p) { return split_sites(p) != 0; }
+// input of the projections of side group g (0 q|k|v, 1 o, 2 fc1 / gate-up, 3 fc2 / down)
+bool split_group(const zo_plan_s& p, int g) {
+  static const uint32_t site[4] = {ZO_PLAN_SPLIT_QKV_IN, ZO_PLAN_SPLIT_ATTN, ZO_PLAN_SPLIT_FC1_IN,
+                                   ZO_PLAN_SPLIT_FC2_IN};
+  return (split_sites(p) & site[g]) != 0;
+}
+bool split_head(const zo_plan_s& p) { return (split_sites(p) & ZO_PLAN_SPLIT_HEAD) != 0; }
 // As columns per row: the widest group.  Every group writes, for a given row, the same
 // column offsets inside each ks-wide block, so one zero fill per call keeps the
 // columns that no group writes at zero.
@@ -591,7 +602,7 @@ int64_t as_stride(const SideGeom& sg) {
 // projection that writes its input (GELU / SwiGLU): bf16 and fp8 models, one-term
 // activations, at most 4 used factor columns.
 bool side_in_ffn_epilogue(const zo_model_desc& d, const zo_plan_s& p, const SideGeom& sg) {
-  return bf16_like(d) && !split_act(p) && sg.group_on.size() == 4 && sg.group_on[3] &&
+  return bf16_like(d) && !split_group(p, 3) && sg.group_on.size() == 4 && sg.group_on[3] &&
          (sg.vt_rows[3] / sg.ks_c) * (int64_t)(sg.nc * sg.r) <= 4;
 }
 
@@ -629,15 +640,17 @@ void carve(const zo_model* m, const zo_plan_s& p, const Packing& pk, const SideG
   w.jobs = b.take<SideJob>(std::max(n_side_jobs(d, p, sg), 1));
   const int64_t D = d.d_model, F = d.d_ffn;
   const int64_t NQ = (int64_t)d.n_heads * d.head_dim, NKV = (int64_t)d.n_kv_heads * d.head_dim;
-  // two-term activations: [hi | lo] rows (x2), fp32 q|k|v, factor blocks hi | hi | lo (x3)
-  const bool sp = split_act(p);
-  const int64_t x2 = sp ? 2 : 1, x3 = sp ? 3 : 1;
+  // two-term activations at a site: [hi | lo] rows (x2), fp32 q|k|v, factor blocks
+  // hi | hi | lo (x3) of the groups that read a split site
+  auto x2g = [&](int g) -> int64_t { return split_group(p, g) ? 2 : 1; };
+  auto x3g = [&](int g) -> int64_t { return split_group(p, g) ? 3 : 1; };
+  const int64_t x2n = (split_group(p, 0) || split_group(p, 2)) ? 2 : 1;   // the two norm outputs share xa
   w.h = b.take<float>(M * D);
-  w.xa = b.take<unsigned char>(M * D * as * x2);
-  w.qkv = b.take<unsigned char>(M * (NQ + 2 * NKV) * (sp ? sizeof(float) : as));
-  w.attn = b.take<unsigned char>(M * NQ * as * x2);
-  w.hid = b.take<unsigned char>(M * F * as * x2);
-  w.as_ld = std::max<int64_t>(as_stride(sg), 1) * x2;
+  w.xa = b.take<unsigned char>(M * D * as * x2n);
+  w.qkv = b.take<unsigned char>(M * (NQ + 2 * NKV) * (split_group(p, 1) ? sizeof(float) : as));
+  w.attn = b.take<unsigned char>(M * NQ * as * x2g(1));
+  w.hid = b.take<unsigned char>(M * F * as * x2g(3));
+  w.as_ld = std::max<int64_t>(as_stride(sg), 1) * (split_act(p) ? 2 : 1);
   w.as = b.take<unsigned char>(M * w.as_ld * as);
   w.vt.assign((size_t)d.n_layers * 4, nullptr);
   w.bs.assign((size_t)d.n_layers * 4, nullptr);
@@ -646,16 +659,16 @@ void carve(const zo_model* m, const zo_plan_s& p, const Packing& pk, const SideG
   for (int l = 0; l < d.n_layers; ++l)
     for (int g = 0; g < 4; ++g)
       if (sg.group_on[g]) {
-        w.vt[l * 4 + g] = b.take<unsigned char>(sg.vt_rows[g] * sg.n_in[g] * as * x3);
-        w.bs[l * 4 + g] = b.take<unsigned char>(sg.bs_rows[g] * sg.bs_cols[g] * as * x3);
+        w.vt[l * 4 + g] = b.take<unsigned char>(sg.vt_rows[g] * sg.n_in[g] * as * x3g(g));
+        w.bs[l * 4 + g] = b.take<unsigned char>(sg.bs_rows[g] * sg.bs_cols[g] * as * x3g(g));
       }
   w.side_begin = base ? (unsigned char*)base + side0 : nullptr;
   w.side_bytes = b.off - side0;
-  w.xs = b.take<unsigned char>(S * D * as * x2);
+  w.xs = b.take<unsigned char>(S * D * as * (split_head(p) ? 2 : 1));
   {
     int64_t np = 0, npd = 0;
     for (int g = 0; g < 4; ++g) {
-      np = std::max(np, (int64_t)tproj_split(d, sg.vt_rows[g], sg.n_in[g] * x3) * sg.vt_rows[g]);
+      np = std::max(np, (int64_t)tproj_split(d, sg.vt_rows[g], sg.n_in[g] * x3g(g)) * sg.vt_rows[g]);
       npd = std::max(npd, (int64_t)tproj_split_decode(d, sg.vt_rows[g], sg.n_in[g]) * sg.vt_rows[g]);
     }
     const int64_t n = std::max<int64_t>(np * M, kv_rows > 0 ? npd * std::max(pk.n_phys, 1) : 0);
@@ -756,13 +769,19 @@ int forward(zo_model* m, const zo_plan_s& p, const Packing& pk, const SideGeom& 
   const float eps = (float)d.norm_eps;
   const bool rms = !is_opt(d);
   const int big = GEMM_CFG_BIG, narrow = GEMM_CFG_NARROW;
-  // Two-term activations (bf16 only): every projection input is [hi | lo] of width
-  // 2K and the GEMM wraps B at K; q|k|v stay fp32 for the fp32 attention; the
-  // side-input projection reads A = [hi | lo] wrapped at 2K against
-  // V^T = [hi | hi | lo] (K' = 3K), and the side segment reads As = [t_hi | t_lo]
-  // per unit wrapped at 2 units against Bs = [U_hi | U_hi | U_lo].
+  // Two-term activations (bf16 only), per site: a split projection input is [hi | lo] of
+  // width 2K and the GEMM wraps B at K; with the attention site q|k|v stay fp32 for the
+  // fp32 attention; the side-input projection of a split group reads A = [hi | lo] wrapped
+  // at 2K against V^T = [hi | hi | lo] (K' = 3K), and its side segment reads
+  // As = [t_hi | t_lo] per unit wrapped at 2 units against Bs = [U_hi | U_hi | U_lo].
   const bool sp = split_act(p);
-  const int x2 = sp ? 2 : 1, x3 = sp ? 3 : 1;
+  bool spg[4];
+  for (int g = 0; g < 4; ++g) spg[g] = split_group(p, g);
+  const bool sph = split_head(p);
+  const int xn = (spg[0] || spg[2]) ? 2 : 1;        // pitch factor of the shared norm-output rows
+  auto x3g = [&](int g) { return spg[g] ? 3 : 1; };
+  // row pitch of the input buffer of group g (K its width)
+  auto lda_of = [&](int g, int K) -> int64_t { return (int64_t)K * ((g == 0 || g == 2) ? xn : (spg[g] ? 2 : 1)); };
   int rc;
 
   if (M > 0) {
@@ -778,10 +797,11 @@ int forward(zo_model* m, const zo_plan_s& p, const Packing& pk, const SideGeom& 
   // the side input of a group formed inside the norm kernel that produces its activations
   // (bf16 and fp8 models, one-term activations, at most 16 used factor columns)
   auto side_in_norm = [&](int g) {
-    return bf && !sp && sg.group_on[g] && (sg.vt_rows[g] / sg.ks_c) * (int64_t)(sg.nc * sg.r) <= 16;
+    return bf && !spg[g] && sg.group_on[g] && (sg.vt_rows[g] / sg.ks_c) * (int64_t)(sg.nc * sg.r) <= 16;
   };
   auto tproj_params = [&](int l, int g, const void* X, int K) {
-    GemmParams gp = gemm_base(X, (int64_t)K * x2, w.vt[l * 4 + g], (int64_t)K * x3, M, (int)sg.vt_rows[g], K * x3);
+    GemmParams gp = gemm_base(X, lda_of(g, K), w.vt[l * 4 + g], (int64_t)K * x3g(g), M, (int)sg.vt_rows[g],
+                              K * x3g(g));
     gp.epi = EPI_TPROJ;
     gp.C = w.as; gp.ldc = w.as_ld;
     gp.row_cand = w.row_cand; gp.cand_dir = w.cand_dir; gp.cand_slot = w.cand_slot; gp.cand_scale = w.cand_scale;
@@ -790,23 +810,24 @@ int forward(zo_model* m, const zo_plan_s& p, const Packing& pk, const SideGeom& 
   };
   auto tproj = [&](int l, int g, const void* X, int K) -> int {
     if (!sg.group_on[g]) return ZO_OK;
-    GemmParams gp = gemm_base(X, (int64_t)K * x2, w.vt[l * 4 + g], (int64_t)K * x3, M, (int)sg.vt_rows[g], K * x3);
-    if (sp) { gp.kwa = 2 * K; gp.tp_unit = (int)sg.bs_cols[g]; }
+    GemmParams gp = gemm_base(X, lda_of(g, K), w.vt[l * 4 + g], (int64_t)K * x3g(g), M, (int)sg.vt_rows[g],
+                              K * x3g(g));
+    if (spg[g]) { gp.kwa = 2 * K; gp.tp_unit = (int)sg.bs_cols[g]; }
     gp.epi = EPI_TPROJ;
     gp.C = w.as; gp.ldc = w.as_ld;
     gp.row_cand = w.row_cand; gp.cand_dir = w.cand_dir; gp.cand_slot = w.cand_slot; gp.cand_scale = w.cand_scale;
     gp.tp_ks = sg.ks_c; gp.tp_rank = sg.r; gp.tp_entries = sg.E; gp.tp_used = sg.nc * sg.r; gp.tp_as_ks = sg.ks;
     gp.ksplit = (gen && gen->decode && !sp) ? tproj_split_decode(d, sg.vt_rows[g], K)
-                                            : tproj_split(d, sg.vt_rows[g], K * x3);
+                                            : tproj_split(d, sg.vt_rows[g], K * x3g(g));
     gp.partial = w.tp_partial;
     gp.a_e4m3 = f8;                        // fp8 models: every layer-linear input is e4m3
     return run_gemm(d, gp, narrow, s);
   };
-  // projection over activations X [M x K] (or [hi | lo]) with the exact weight B [N x K]
-  // (fp8 models: e4m3 X and e4m3 codes of B * 2^11)
-  auto proj = [&](const void* X, const void* B, int N, int K) {
-    GemmParams gp = gemm_base(X, (int64_t)K * x2, B, K, M, N, K * x2);
-    if (sp) gp.kwb = K;
+  // projection over activations X [M x K] (or [hi | lo] when `split`; row pitch lda) with the
+  // exact weight B [N x K] (fp8 models: e4m3 X and e4m3 codes of B * 2^11)
+  auto proj = [&](const void* X, int64_t lda, bool split, const void* B, int N, int K) {
+    GemmParams gp = gemm_base(X, lda, B, K, M, N, K * (split ? 2 : 1));
+    if (split) gp.kwb = K;
     gp.a_e4m3 = gp.b_e4m3 = f8;
     if (gen && gen->decode && !sp && bf) {
       // decode steps (one row per sequence): K-slices until the 128x128 tiles fill the
@@ -827,17 +848,17 @@ int forward(zo_model* m, const zo_plan_s& p, const Packing& pk, const SideGeom& 
       const int n_used = (int)(sg.vt_rows[g] / sg.ks_c) * sg.nc * sg.r;
       if (f8) return launch_norm_side<e4m3_t>(w.h, M, D, nw, nb, eps, rms, (e4m3_t*)w.xa, D, gp, n_used, s);
       if constexpr (std::is_same<T, bf16_t>::value)
-        return launch_norm_side<bf16_t>(w.h, M, D, nw, nb, eps, rms, (bf16_t*)w.xa, D, gp, n_used, s);
+        return launch_norm_side<bf16_t>(w.h, M, D, nw, nb, eps, rms, (bf16_t*)w.xa, (int64_t)D * xn, gp, n_used, s);
     }
     if (f8) return launch_norm<e4m3_t>(w.h, nullptr, M, D, nw, nb, eps, rms, (e4m3_t*)w.xa, D, 0, s);
-    return launch_norm<T>(w.h, nullptr, M, D, nw, nb, eps, rms, (T*)w.xa, (int64_t)D * x2, sp ? D : 0, s);
+    return launch_norm<T>(w.h, nullptr, M, D, nw, nb, eps, rms, (T*)w.xa, (int64_t)D * xn, spg[g] ? D : 0, s);
   };
   auto with_side = [&](GemmParams& gp, int l, int g) {
     if (!sg.group_on[g]) return;
     gp.As = w.as; gp.ldas = w.as_ld;
-    gp.Bs = w.bs[l * 4 + g]; gp.ldbs = sg.bs_cols[g] * x3;
-    gp.ks_tile = (int)sg.bs_cols[g] * x3;
-    if (sp) { gp.as_stride = 2 * (int)sg.bs_cols[g]; gp.kwas = 2 * (int)sg.bs_cols[g]; }
+    gp.Bs = w.bs[l * 4 + g]; gp.ldbs = sg.bs_cols[g] * x3g(g);
+    gp.ks_tile = (int)sg.bs_cols[g] * x3g(g);
+    if (spg[g]) { gp.as_stride = 2 * (int)sg.bs_cols[g]; gp.kwas = 2 * (int)sg.bs_cols[g]; }
   };
 
   for (int l = 0; l < d.n_layers && M > 0; ++l) {
@@ -849,15 +870,15 @@ int forward(zo_model* m, const zo_plan_s& p, const Packing& pk, const SideGeom& 
     }
     if (!side_in_norm(0) && (rc = tproj(l, 0, w.xa, D)) != ZO_OK) return rc;
     {
-      GemmParams gp = proj(w.xa, W(P[P_WQ]), NQKV, D);
+      GemmParams gp = proj(w.xa, lda_of(0, D), spg[0], W(P[P_WQ]), NQKV, D);
       with_side(gp, l, 0);
       if (sg.group_on[0]) { gp.n_bounds = 2; gp.bounds[0] = NQ; gp.bounds[1] = NQ + NKV; }
-      gp.epi = EPI_STORE; gp.bias = Wf(P[P_BQ]); gp.C = w.qkv; gp.ldc = NQKV; gp.c_f32 = sp;
+      gp.epi = EPI_STORE; gp.bias = Wf(P[P_BQ]); gp.C = w.qkv; gp.ldc = NQKV; gp.c_f32 = spg[1];
       if ((rc = run_gemm(d, gp, big, s)) != ZO_OK) return rc;
     }
     if (!is_opt(d)) {
       ProfScope ps(ZO_PROF_NORM, s);
-      if (sp)
+      if (spg[1])
         ZO_HIP(launch_qknorm_rope<float>((float*)w.qkv, M, NQKV, d.n_heads, d.n_kv_heads, d.head_dim, Wf(P[P_QNW]),
                                          Wf(P[P_KNW]), eps, m->rope, w.row_pos, s));
       else
@@ -885,7 +906,7 @@ int forward(zo_model* m, const zo_plan_s& p, const Packing& pk, const SideGeom& 
         }
         ZO_HIP(e);
       }
-      else if (sp)
+      else if (spg[1])
         ZO_HIP(launch_attention_split((const float*)w.qkv, NQKV, (bf16_t*)w.attn, 2 * NQ, NQ, w.phys_cu, w.work,
                                       (int)pk.work.size(), d.n_heads, d.n_kv_heads, d.head_dim, s));
       else if (f8)
@@ -897,7 +918,7 @@ int forward(zo_model* m, const zo_plan_s& p, const Packing& pk, const SideGeom& 
     }
     if ((rc = tproj(l, 1, w.attn, NQ)) != ZO_OK) return rc;
     {
-      GemmParams gp = proj(w.attn, W(P[P_WO]), D, NQ);
+      GemmParams gp = proj(w.attn, lda_of(1, NQ), spg[1], W(P[P_WO]), D, NQ);
       with_side(gp, l, 1);
       gp.epi = EPI_RESID; gp.bias = Wf(P[P_BO]); gp.H = w.h; gp.ldh = D;
       if ((rc = run_gemm(d, gp, big, s)) != ZO_OK) return rc;
@@ -913,9 +934,9 @@ int forward(zo_model* m, const zo_plan_s& p, const Packing& pk, const SideGeom& 
     const bool ffn_fused = w.sf_part && !(gen && gen->decode);
     {
       const int N1 = is_opt(d) ? F : 2 * F;
-      GemmParams gp = proj(w.xa, W(P[P_W1]), N1, D);
+      GemmParams gp = proj(w.xa, lda_of(2, D), spg[2], W(P[P_W1]), N1, D);
       with_side(gp, l, 2);
-      gp.C = w.hid; gp.ldc = (int64_t)F * x2; gp.c_lo = sp ? F : 0;
+      gp.C = w.hid; gp.ldc = lda_of(3, F); gp.c_lo = spg[3] ? F : 0;
       if (is_opt(d)) { gp.epi = EPI_GELU; gp.bias = Wf(P[P_B1]); }
       else gp.epi = EPI_SWIGLU;
       if (ffn_fused) {
@@ -935,7 +956,7 @@ int forward(zo_model* m, const zo_plan_s& p, const Packing& pk, const SideGeom& 
     if (!ffn_fused && (rc = tproj(l, 3, w.hid, F)) != ZO_OK) return rc;
     {
       const TLoc& w2 = is_opt(d) ? P[P_W2] : P[P_WDOWN];
-      GemmParams gp = proj(w.hid, W(w2), D, F);
+      GemmParams gp = proj(w.hid, lda_of(3, F), spg[3], W(w2), D, F);
       with_side(gp, l, 3);
       gp.epi = EPI_RESID; gp.bias = is_opt(d) ? Wf(P[P_B2]) : nullptr; gp.H = w.h; gp.ldh = D;
       if ((rc = run_gemm(d, gp, big, s)) != ZO_OK) return rc;
@@ -946,12 +967,12 @@ int forward(zo_model* m, const zo_plan_s& p, const Packing& pk, const SideGeom& 
     {
       ProfScope ps(ZO_PROF_NORM, s);
       ZO_HIP(launch_norm<T>(w.h, w.sc_row, S, D, Wf(Lo.g[G_FNW]), Wf(Lo.g[G_FNB]), eps, rms, (T*)w.xs,
-                            (int64_t)D * x2, sp ? D : 0, s));
+                            (int64_t)D * (sph ? 2 : 1), sph ? D : 0, s));
       ZO_HIP(launch_gather_labels(tokens, w.sc_lab_src, S, d.vocab, w.labels, w.bad_ids, s));
     }
     const TLoc& head = is_opt(d) ? Lo.g[G_TOK] : Lo.g[G_HEAD];
-    GemmParams gp = gemm_base(w.xs, (int64_t)D * x2, W(head), D, S, d.vocab, D * x2);
-    if (sp) gp.kwb = D;
+    GemmParams gp = gemm_base(w.xs, (int64_t)D * (sph ? 2 : 1), W(head), D, S, d.vocab, D * (sph ? 2 : 1));
+    if (sph) gp.kwb = D;
     const int bn = gemm_cfg_bn(GEMM_CFG_HEAD, bf);
     gp.epi = EPI_LMHEAD; gp.labels = w.labels; gp.part = w.part; gp.lab_logit = w.lab_logit;
     gp.part_idx = gen ? w.part_idx : nullptr;
@@ -1127,10 +1148,11 @@ int zo_plan(const zo_model* m, const zo_plan_desc* desc, zo_plan_t** out) {
   const zo_plan_desc& d = *desc;
   ZO_CHECK(d.nu >= 1, ZO_E_INVAL, "nu must be >= 1");
   ZO_CHECK(d.rank >= 1, ZO_E_INVAL, "rank must be >= 1");
-  ZO_CHECK((d.flags & ~(ZO_PLAN_SCALE_INV_SQRT_R | ZO_PLAN_ALLOW_ZERO_EPS | ZO_PLAN_ACT_SPLIT)) == 0, ZO_E_INVAL,
-           "unknown plan flag");
-  ZO_CHECK(!(d.flags & ZO_PLAN_ACT_SPLIT) || m->d.dtype == ZO_DTYPE_BF16, ZO_E_INVAL,
-           "ZO_PLAN_ACT_SPLIT applies to bf16 models only");
+  ZO_CHECK((d.flags & ~(ZO_PLAN_SCALE_INV_SQRT_R | ZO_PLAN_ALLOW_ZERO_EPS | ZO_PLAN_ACT_SPLIT |
+                        ZO_PLAN_SPLIT_SITES)) == 0,
+           ZO_E_INVAL, "unknown plan flag");
+  ZO_CHECK(!(d.flags & (ZO_PLAN_ACT_SPLIT | ZO_PLAN_SPLIT_SITES)) || m->d.dtype == ZO_DTYPE_BF16, ZO_E_INVAL,
+           "ZO_PLAN_ACT_SPLIT and ZO_PLAN_SPLIT_* apply to bf16 models only");
   ZO_CHECK(std::isfinite(d.eps) && (d.eps > 0 || (d.eps == 0 && (d.flags & ZO_PLAN_ALLOW_ZERO_EPS))), ZO_E_INVAL,
            "eps must be finite and > 0");
   ZO_CHECK(d.n_dirs >= 1 && d.dir_seeds, ZO_E_INVAL, "need at least one direction");
@@ -1333,8 +1355,6 @@ static int prepare_call(zo_model* m, const zo_plan_t* p, const zo_bank* bank, co
   if (sg.any && pk.M > 0) {
     const uint64_t win = p->window();
     const int dt = bf ? 1 : 0;
-    const bool sp = split_act(*p);
-    const int64_t x3 = sp ? 3 : 1;
     const int64_t NQ = (int64_t)d.n_heads * d.head_dim, NKV = (int64_t)d.n_kv_heads * d.head_dim;
     ZO_HIP(hipMemsetAsync(w.side_begin, 0, w.side_bytes, s));   // padding rows/columns must be zero
     ZO_HIP(hipMemsetAsync(w.as, 0, (size_t)pk.M * w.as_ld * act_size(d), s));   // columns no row writes
@@ -1343,6 +1363,8 @@ static int prepare_call(zo_model* m, const zo_plan_t* p, const zo_bank* bank, co
         if (!sg.group_on[g]) continue;
         const Group& G = sg.groups[g];
         const size_t asz = act_size(d);
+        const bool sp = split_group(*p, g);            // factor blocks hi | hi | lo
+        const int64_t x3 = sp ? 3 : 1;
         for (size_t kb = 0; kb < G.kinds.size(); ++kb) {
           const int kind = G.kinds[kb];
           if (!((p->mask >> kind) & 1u)) continue;
@@ -1483,7 +1505,7 @@ int zo_score_noalloc(zo_model* m, const zo_plan_t* p, const zo_bank* bank, const
 
 static int check_generate(const zo_model* m, const zo_plan_t* p, const zo_batch* b, int32_t n_new) {
   const zo_model_desc& d = m->d;
-  ZO_CHECK(!split_act(*p), ZO_E_INVAL, "generation: not with ZO_PLAN_ACT_SPLIT");
+  ZO_CHECK(!split_act(*p), ZO_E_INVAL, "generation: not with ZO_PLAN_ACT_SPLIT or ZO_PLAN_SPLIT_*");
   ZO_CHECK(n_new >= 1, ZO_E_INVAL, "n_new must be >= 1");
   int rc = validate_batch(d, b);
   if (rc) return rc;
