@@ -47,7 +47,7 @@ def test_host_runtime_clean_under_asan_and_ubsan():
                      (os.path.join(ROOT, "tests", "sanitize", "zo_host_driver.cpp"), drv_o)):
         r = subprocess.run([cc] + flags + san + ["-c", src, "-o", obj], capture_output=True, text=True)
         assert r.returncode == 0, r.stderr[-3000:]
-    r = subprocess.run([cc, "--offload-arch=gfx950"] + san + [drv_o, api_o] + objs + ["-o", exe],
+    r = subprocess.run([cc, "--offload-arch=gfx950"] + san + [drv_o, api_o] + objs + zbuild.ROCTX_LINK + ["-o", exe],
                        capture_output=True, text=True)
     assert r.returncode == 0, r.stderr[-3000:]
     env = dict(os.environ, ASAN_OPTIONS="detect_leaks=0:abort_on_error=0:exitcode=23",

@@ -21,6 +21,8 @@ SOURCES = ["rng.hip", "gemm.hip", "layers.hip", "attention.hip", "decode.hip", "
 PEAKS_SOURCE = "peaks.hip"
 PEAKS_OUT = os.path.join(HERE, "libzo_peaks.so")
 ARCH = "gfx950"
+ROCM_LIB = "/opt/rocm/lib"
+ROCTX_LINK = ["-L" + ROCM_LIB, "-lrocprofiler-sdk-roctx", "-Wl,-rpath," + ROCM_LIB]
 
 
 def hipcc():
@@ -56,6 +58,8 @@ def build(verbose=False):
     for out, parts in ((OUT, objs[:-1]), (PEAKS_OUT, objs[-1:])):
         tmp = out + ".tmp%d" % os.getpid()
         cmd = [cc, "--offload-arch=" + ARCH, "-shared", "-fPIC", "-o", tmp] + parts
+        if out == OUT:   # roctx ranges around the public calls
+            cmd += ROCTX_LINK
         r = subprocess.run(cmd, capture_output=True, text=True)
         if r.returncode != 0:
             raise RuntimeError("link failed:\n" + r.stderr[-4000:])

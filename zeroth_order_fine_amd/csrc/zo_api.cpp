@@ -9,6 +9,7 @@
 // Scoring" and "The System Reorganization").
 #include "../../include/zo.h"
 #include "common.h"
+#include <rocprofiler-sdk-roctx/roctx.h>
 
 #include <algorithm>
 #include <array>
@@ -27,6 +28,14 @@
 // own copy for the life of the process.  In host code `scratch` names a host-side stand-in:
 // its device address comes from hipGetSymbolAddress, once per device (scratch_init).
 static __device__ __align__(256) unsigned char scratch[ZO_NOALLOC_SCRATCH_BYTES];
+
+// A roctx range over one public call (shown by rocprofv3 --marker-trace; free otherwise)
+struct CallRange {
+  explicit CallRange(const char* name) { roctxRangePushA(name); }
+  ~CallRange() { roctxRangePop(); }
+  CallRange(const CallRange&) = delete;
+  CallRange& operator=(const CallRange&) = delete;
+};
 
 namespace {
 
@@ -1113,6 +1122,7 @@ int zo_model_destroy(zo_model* m) {
 }
 
 int zo_init_weights(zo_model* m, uint64_t seed, void* stream) {
+  CallRange range_("zo_init_weights");
   ZO_CHECK(m, ZO_E_INVAL, "null model");
   hipStream_t s = (hipStream_t)stream;
   std::vector<NormalJob> jobs;
@@ -1144,6 +1154,7 @@ int zo_init_weights(zo_model* m, uint64_t seed, void* stream) {
 }
 
 int zo_plan(const zo_model* m, const zo_plan_desc* desc, zo_plan_t** out) {
+  CallRange range_("zo_plan");
   ZO_CHECK(m && desc && out, ZO_E_INVAL, "null argument");
   const zo_plan_desc& d = *desc;
   ZO_CHECK(d.nu >= 1, ZO_E_INVAL, "nu must be >= 1");
@@ -1439,6 +1450,7 @@ int zo_model_set_graphs(zo_model* m, int32_t enable) {
 
 int zo_score(zo_model* m, const zo_plan_t* p, const zo_bank* bank, const zo_batch* b, void* ws_dev,
              size_t ws_bytes, double* seq_logp_dev, float* tok_logp_dev, double* S_host, void* stream) {
+  CallRange range_("zo_score");
   ZO_CHECK(m && p && S_host, ZO_E_INVAL, "null argument");
   hipStream_t s = (hipStream_t)stream;
   const zo_model_desc& d = m->d;
@@ -1486,6 +1498,7 @@ int zo_score(zo_model* m, const zo_plan_t* p, const zo_bank* bank, const zo_batc
 
 int zo_score_noalloc(zo_model* m, const zo_plan_t* p, const zo_bank* bank, const zo_batch* b,
                      double* seq_logp_dev, float* tok_logp_dev, double* S_host, void* stream) {
+  CallRange range_("zo_score_noalloc");
   ZO_CHECK(m && p && S_host, ZO_E_INVAL, "null argument");
   size_t need = 0;
   int rc = zo_batch_layout(m, p, bank, b, nullptr, nullptr, nullptr, &need);
@@ -1536,6 +1549,7 @@ int zo_generate_layout(const zo_model* m, const zo_plan_t* p, const zo_bank* ban
 
 int zo_generate(zo_model* m, const zo_plan_t* p, const zo_bank* bank, const zo_batch* b, int32_t n_new,
                 void* ws_dev, size_t ws_bytes, int32_t* tokens_dev, float* logp_dev, double* S_host, void* stream) {
+  CallRange range_("zo_generate");
   ZO_CHECK(m && p && tokens_dev && logp_dev && S_host, ZO_E_INVAL, "null argument");
   int rc = check_generate(m, p, b, n_new);
   if (rc) return rc;
@@ -1635,6 +1649,7 @@ int zo_generate(zo_model* m, const zo_plan_t* p, const zo_bank* bank, const zo_b
 
 int zo_estimate(const zo_plan_t* p, const double* S_host, const int64_t* n_scored, uint32_t flags,
                 double* c_out) {
+  CallRange range_("zo_estimate");
   ZO_CHECK(p && S_host && c_out, ZO_E_INVAL, "null argument");
   ZO_CHECK((flags & ~(ZO_EST_INV_RANK | ZO_EST_MEAN)) == 0, ZO_E_INVAL, "unknown estimate flag");
   ZO_CHECK(!(flags & ZO_EST_MEAN) || n_scored, ZO_E_INVAL, "ZO_EST_MEAN needs n_scored");
@@ -1666,6 +1681,7 @@ int zo_estimate(const zo_plan_t* p, const double* S_host, const int64_t* n_score
 }
 
 int zo_update(zo_model* m, const zo_plan_t* p, zo_bank* bank, const double* c_host, double lr, void* stream) {
+  CallRange range_("zo_update");
   ZO_CHECK(m && p && bank && c_host, ZO_E_INVAL, "null argument");
   ZO_CHECK(std::isfinite(lr), ZO_E_INVAL, "lr must be finite");
   if (int rc = check_objects(m, p, bank)) return rc;
@@ -1731,6 +1747,7 @@ int zo_bank_fold_size(const zo_model* m, const zo_bank* bank, size_t* bytes) {
 }
 
 int zo_bank_fold(zo_model* m, zo_bank* bank, int32_t slot, void* ws_dev, size_t ws_bytes, void* stream) {
+  CallRange range_("zo_bank_fold");
   ZO_CHECK(m && bank, ZO_E_INVAL, "null argument");
   ZO_CHECK(slot >= 0 && slot < bank->n_slots, ZO_E_INVAL, "slot %d out of range", slot);
   ZO_CHECK(bank->windows[slot] >= 0, ZO_E_STATE, "slot %d holds no entry", slot);
@@ -1785,6 +1802,7 @@ int zo_bank_fold(zo_model* m, zo_bank* bank, int32_t slot, void* ws_dev, size_t 
 
 int zo_bank_cap(zo_model* m, zo_bank* bank, const zo_plan_t* p, int32_t max_frozen, void* ws_dev, size_t ws_bytes,
                 void* stream, int32_t* n_folded) {
+  CallRange range_("zo_bank_cap");
   ZO_CHECK(m && bank && p, ZO_E_INVAL, "null argument");
   ZO_CHECK(max_frozen >= 0, ZO_E_INVAL, "max_frozen must be >= 0");
   if (int rc = check_objects(m, p, bank)) return rc;
