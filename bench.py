@@ -559,13 +559,20 @@ def main():
     if not args.no_side_check:
         # bank growth: score time with E frozen entries (windows 0 .. E-1, each a rank-r side
         # term of every probe row) besides the plan's direction
+        # (single-direction plans: each window leaves one entry; the MeZO-style workload's
+        # four rank-64 directions a window would make 16 windows a rank-4096 side path)
         growth = {}
-        for E in (0, 1, 4, 16):
+        for E in ((0, 1, 4, 16) if wl.n_dirs == 1 else ()):
             bE = zo.Bank(model, E + 2 * wl.n_dirs, wl.rank, wl.targets)
             for win in range(E):
                 zo.update(model, zo.Plan.from_workload(model, wl, t=win * wl.nu), bE, [0.5] * wl.n_dirs, args.lr)
             pE = zo.Plan.from_workload(model, wl, t=E * wl.nu)
-            zo.score(model, pE, bE, db)
+            try:
+                zo.score(model, pE, bE, db)
+            except zo.ZoError as e:      # e.g. fp8 models: side-input projections of at most 128 columns
+                growth[str(E)] = "refused: %s" % e
+                del bE
+                continue
             torch.cuda.synchronize()
             a = time.perf_counter()
             for k in range(3):
@@ -573,7 +580,8 @@ def main():
             torch.cuda.synchronize()
             growth[str(E)] = round((time.perf_counter() - a) / 3 * 1e3, 3)
             del bE
-        extra["score_ms_by_frozen_entries"] = growth
+        if growth:
+            extra["score_ms_by_frozen_entries"] = growth
         extra["score_ms_steady_bank"] = round(score_ms(bank, db), 3)
         extra["score_ms_empty_bank"] = round(score_ms(None, db), 3)
         if wl.n_fg:
