@@ -17,6 +17,13 @@
 
 namespace {
 
+// 16-byte chunk swizzle of K tile row kr (CH chunks a row): the fragment reads take one
+// logical chunk of 16 consecutive rows, which then touch every 16-byte bank group of the
+// 256-byte LDS line once (rows of 256 bytes or more: the low four bits of kr; 128-byte rows:
+// row pairs share a line, so (kr / 2) % 8)
+template <int CH>
+__device__ __forceinline__ int kswz(int kr) { return CH >= 16 ? (kr & 15) : ((kr >> 1) & (CH - 1)); }
+
 constexpr int QB = 64;     // queries per workgroup
 #ifndef ATTN_PREFETCH
 #define ATTN_PREFETCH 1
@@ -67,7 +74,6 @@ attn_bf16_kernel(const bf16_t* __restrict__ qkv, int ld, TO* __restrict__ out, i
 
   const int kcol = hq * HD + kvh * HD;
   const int vcol = hq * HD + hkv * HD + kvh * HD;
-  constexpr int SWZ = (HD / 8 < 8 ? HD / 8 : 8) - 1;   // XOR mask that stays inside a row
 
   // this lane's query (as a B-operand column): q = q0 + wave*16 + lr
   const int qi = q0 + wave * 16 + lr;
@@ -115,7 +121,7 @@ attn_bf16_kernel(const bf16_t* __restrict__ qkv, int ld, TO* __restrict__ out, i
 #pragma unroll
     for (int i = 0; i < NKC; ++i) {
       const int c = tid + i * 256, kr = c / CH, ch = c % CH;
-      *(u32x4_t*)(sK + kr * HD + ((ch ^ (kr & SWZ)) << 3)) = kreg[i];
+      *(u32x4_t*)(sK + kr * HD + ((ch ^ kswz<HD / 8>(kr)) << 3)) = kreg[i];
     }
     if (tid < NVG) {
       const int kg = tid % (KB / 4), ch = tid / (KB / 4);
@@ -145,7 +151,7 @@ attn_bf16_kernel(const bf16_t* __restrict__ qkv, int ld, TO* __restrict__ out, i
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const int ch = ks * 4 + g;
-        bf16x8_t kf = *(const bf16x8_t*)(sK + kr * HD + ((ch ^ (kr & SWZ)) << 3));
+        bf16x8_t kf = *(const bf16x8_t*)(sK + kr * HD + ((ch ^ kswz<HD / 8>(kr)) << 3));
         s[kb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(kf, qf[ks], s[kb], 0, 0, 0);
       }
     }
@@ -273,7 +279,6 @@ attn_split_kernel(const float* __restrict__ qkv, int ld, bf16_t* __restrict__ ou
   const int lr = lane & 15, g = lane >> 4;
   const int kcol = hq * HD + kvh * HD;
   const int vcol = hq * HD + hkv * HD + kvh * HD;
-  constexpr int SWZ = (HD / 8 < 8 ? HD / 8 : 8) - 1;
 
   const int qi = q0 + wave * 16 + lr;
   const int qrow = base + min(qi, len - 1);
@@ -330,7 +335,7 @@ attn_split_kernel(const float* __restrict__ qkv, int ld, bf16_t* __restrict__ ou
       *(floatx4_t*)(v + 4) = kreg[i][1];
       bf16x8_t hi, lo;
       split8(v, hi, lo);
-      const int o = kr * HD + ((ch ^ (kr & SWZ)) << 3);
+      const int o = kr * HD + ((ch ^ kswz<HD / 8>(kr)) << 3);
       *(bf16x8_t*)(sK[0] + o) = hi;
       *(bf16x8_t*)(sK[1] + o) = lo;
     }
@@ -364,7 +369,7 @@ attn_split_kernel(const float* __restrict__ qkv, int ld, bf16_t* __restrict__ ou
       const int kr = kb * 16 + lr;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        const int o = kr * HD + (((ks * 4 + g) ^ (kr & SWZ)) << 3);
+        const int o = kr * HD + (((ks * 4 + g) ^ kswz<HD / 8>(kr)) << 3);
         const bf16x8_t kh = *(const bf16x8_t*)(sK[0] + o), kl = *(const bf16x8_t*)(sK[1] + o);
         s[kb] = mfma3(kh, kl, qh[ks], ql[ks], s[kb]);
       }

@@ -129,7 +129,7 @@ struct GemmParams {
   // output columns one wave tile holds (64 for GELU, 32 for SwiGLU), the partial sums of the
   // stored (rounded) outputs times the used V^T rows: column j of sf_n is row
   // (j / sf_used) * sf_ks + j % sf_used of sf_vt (row pitch sf_ldv), written to
-  // sf_part [sf_groups x M x sf_n] fp32; side_part_reduce sums the groups in order.
+  // sf_part [M x sf_groups x sf_n] fp32; side_part_reduce sums each row's groups.
   int sf_n, sf_used, sf_ks, sf_groups;
   const void* sf_vt; int64_t sf_ldv;
   float* sf_part;
@@ -295,7 +295,7 @@ hipError_t launch_attention_split(const float* qkv, int ld_qkv, bf16_t* out, int
                                   const int32_t* cu, const int32_t* work, int n_work, int hq, int hkv, int hd,
                                   hipStream_t s);
 hipError_t launch_tproj_reduce(const GemmParams& p, hipStream_t s);
-// t from the partial sums of an epilogue (sf_part, sf_groups, sf_n) in group order, then the
+// t from the partial sums of an epilogue (sf_part, sf_groups, sf_n) in a fixed order, then the
 // side-input store of tproj_out (p carries the tproj fields of the consuming projection)
 hipError_t launch_side_part_reduce(const GemmParams& p, hipStream_t s);
 hipError_t launch_gather_labels(const int32_t* src, const int32_t* idx, int n, int vocab, int32_t* dst,

@@ -429,7 +429,7 @@ __device__ __forceinline__ void side_partial_store(const GemmParams& p, int r, i
   if (lane < 16 && r < p.M) {
 #pragma unroll
     for (int c = 0; c < NC; ++c)
-      if (c < p.sf_n) p.sf_part[((int64_t)grp * p.M + r) * p.sf_n + c] = t[c];
+      if (c < p.sf_n) p.sf_part[((int64_t)r * p.sf_groups + grp) * p.sf_n + c] = t[c];
   }
 }
 
@@ -1170,29 +1170,37 @@ side_dot_kernel(GemmParams p, int j0, int n_used) {
   }
 }
 
-// t of the projection that reads an epilogue's output: its group partials summed in order
-__global__ void side_part_reduce_kernel(GemmParams p) {
-  const int64_t n = (int64_t)p.M * p.sf_n;
-  for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < n; e += (int64_t)gridDim.x * blockDim.x) {
-    const int r = (int)(e / p.sf_n), c = (int)(e - (int64_t)r * p.sf_n);
-    const int cand = p.row_cand[r];
-    if (cand < 0) continue;
-    const float* pr = p.sf_part + e;                  // group-major: [groups][M][sf_n]
-    float v = 0.f;
-#pragma unroll 8
-    for (int g = 0; g < p.sf_groups; ++g) v += pr[(int64_t)g * n];   // loads in flight together, sums in order
-    tproj_out<bf16_t>(p, r, (c / p.tp_used) * p.tp_ks + c % p.tp_used, v, cand);
-  }
+// t of the projection that reads an epilogue's output: one wave per row sums the row's group
+// partials ([M][groups][sf_n], a row's contiguous): lane l takes groups l, l + 64, ... in order,
+// then a fixed butterfly over the lanes, so each (row, column) value is formed by the same
+// operations whatever the batch
+__global__ void __launch_bounds__(256) side_part_reduce_kernel(GemmParams p) {
+  const int r = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
+  if (r >= p.M) return;                               // wave-uniform
+  const int cand = p.row_cand[r];
+  if (cand < 0) return;
+  const float* pr = p.sf_part + (int64_t)r * p.sf_groups * p.sf_n;
+  float v[4] = {0.f, 0.f, 0.f, 0.f};
+  for (int g = lane; g < p.sf_groups; g += 64)
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      if (c < p.sf_n) v[c] += pr[g * p.sf_n + c];
+#pragma unroll
+  for (int c = 0; c < 4; ++c)
+#pragma unroll
+    for (int sh = 32; sh >= 1; sh >>= 1) v[c] += __shfl_xor(v[c], sh, 64);
+  if (lane == 0)
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      if (c < p.sf_n) tproj_out<bf16_t>(p, r, (c / p.tp_used) * p.tp_ks + c % p.tp_used, v[c], cand);
 }
 
 }  // namespace
 
 hipError_t launch_side_part_reduce(const GemmParams& p, hipStream_t s) {
-  const int64_t n = (int64_t)p.M * p.sf_n;
-  if (n <= 0) return hipSuccess;
-  int64_t blocks = (n + 255) / 256;
-  if (blocks > 8192) blocks = 8192;
-  hipLaunchKernelGGL(side_part_reduce_kernel, dim3((unsigned)blocks), dim3(256), 0, s, p);
+  if (p.M <= 0 || p.sf_n <= 0) return hipSuccess;
+  if (p.sf_n > 4) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(side_part_reduce_kernel, dim3((unsigned)((p.M + 3) / 4)), dim3(256), 0, s, p);
   return hipGetLastError();
 }
 
