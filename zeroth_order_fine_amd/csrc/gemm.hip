@@ -595,27 +595,47 @@ __device__ __forceinline__ void epilogue_rows(const GemmParams& p, floatx4_t (&a
       float t[TM][4];
 #pragma unroll
       for (int i = 0; i < TM; ++i) t[i][0] = t[i][1] = t[i][2] = t[i][3] = 0.f;
-      uint2 e[TN][4];
-      if (p.sf_n)
-#pragma unroll
-        for (int j = 0; j < TN; ++j)
-          if (cb + j * 16 < p.N) side_v4(p, cb + j * 16, e[j]);
-#pragma unroll
-      for (int i = 0; i < TM; ++i) {
-        const int r = rb + i * 16;
-        if (r >= p.M) continue;
+      if constexpr (F8) {
+        // e4m3: column blocks outer, one block's V values live at a time (holding all of
+        // them took this variant past 256 registers a lane, one wave a SIMD instead of
+        // two); a row's partial sums still take its columns in ascending order
+        constexpr float unit = 1.0f / (float)(1 << ZO_FP8_WEIGHT_EXP);   // main segments in units of 2^-11
 #pragma unroll
         for (int j = 0; j < TN; ++j) {
           if (cb + j * 16 >= p.N) continue;
-          constexpr float unit = F8 ? 1.0f / (float)(1 << ZO_FP8_WEIGHT_EXP) : 1.0f;
-          floatx4_t v = F8 ? acc[i][j] * unit + bias[j] : acc[i][j] + bias[j];
+          uint2 ej[4];
+          if (p.sf_n) side_v4(p, cb + j * 16, ej);
+          const floatx4_t bj = p.bias ? *(const floatx4_t*)(p.bias + cb + j * 16) : floatx4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-          for (int q = 0; q < 4; ++q) v[q] = gelu_fast(v[q]);
-          if constexpr (F8)            // the input of the next e4m3 projection
-            store_e4m3x4((e4m3_t*)p.C + (int64_t)r * p.ldc + cb + j * 16, v);
-          else
+          for (int i = 0; i < TM; ++i) {
+            const int r = rb + i * 16;
+            if (r >= p.M) continue;
+            floatx4_t v = acc[i][j] * unit + bj;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) v[q] = gelu_fast(v[q]);
+            store_e4m3x4((e4m3_t*)p.C + (int64_t)r * p.ldc + cb + j * 16, v);   // the next e4m3 projection's input
+            if (p.sf_n) side_partial4(p, stored4<true>(v), ej, t[i]);
+          }
+        }
+      } else {
+        uint2 e[TN][4];
+        if (p.sf_n)
+#pragma unroll
+          for (int j = 0; j < TN; ++j)
+            if (cb + j * 16 < p.N) side_v4(p, cb + j * 16, e[j]);
+#pragma unroll
+        for (int i = 0; i < TM; ++i) {
+          const int r = rb + i * 16;
+          if (r >= p.M) continue;
+#pragma unroll
+          for (int j = 0; j < TN; ++j) {
+            if (cb + j * 16 >= p.N) continue;
+            floatx4_t v = acc[i][j] + bias[j];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) v[q] = gelu_fast(v[q]);
             store_bf16x4(p, (bf16_t*)p.C + (int64_t)r * p.ldc + cb + j * 16, v);
-          if (p.sf_n) side_partial4(p, stored4<F8>(v), e[j], t[i]);
+            if (p.sf_n) side_partial4(p, stored4<false>(v), e[j], t[i]);
+          }
         }
       }
       if (p.sf_n)
