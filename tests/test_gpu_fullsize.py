@@ -100,6 +100,18 @@ def test_full_size_against_oracle(name):
     gold, wl, batch, model, bank, db, out, phys, first = _run(name)
     c_gpu = zo.estimate(zo.Plan.from_workload(model, wl, t=1), out["S"])
     seq, tok = _check(name, gold, wl, out, phys, first, 2e-2 if wl.act_split else 5e-2, c_gpu)
+    if name in ("opt13b", "qwen3-8b-mixed"):
+        # the o and fc2 / down projections run as split-tail launches at this batch (the last
+        # rounds of 256x256 tiles in K-slices dealt over every CU); the slices continue the
+        # same MFMA sequence, so the data-parallel launch gives the same bits
+        os.environ["ZO_GEMM_STREAMK"] = "0"
+        try:
+            dp = zo.score(model, zo.Plan.from_workload(model, wl, t=1), bank, db, want_tokens=True)
+        finally:
+            del os.environ["ZO_GEMM_STREAMK"]
+        assert np.array_equal(dp["seq_logp"].cpu().numpy().view(np.uint64), seq.view(np.uint64))
+        assert np.array_equal(dp["tok_logp"].cpu().numpy().view(np.uint32), tok.view(np.uint32))
+        flush("%s: split-tail and data-parallel projections bitwise equal" % name)
     if name == "qwen3-8b-mixed":
         # co-serving: the foreground rows are bitwise identical without the probes
         import zeroth_order_fine_amd as zo

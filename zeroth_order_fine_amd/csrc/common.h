@@ -133,7 +133,21 @@ struct GemmParams {
   int sf_n, sf_used, sf_ks, sf_groups;
   const void* sf_vt; int64_t sf_ldv;
   float* sf_part;
+  // Split tail of the 256x256 projection kernel (null: off).  A launch of sk_ncu persistent
+  // workgroups (one per CU) runs the last one to two rounds of tiles in K-slices dealt out
+  // evenly; slice j of a tile leaves its fp32 accumulators in the tile's sk_part buffer
+  // (256 x 256 floats; two buffers per workgroup) and sets the tile's sk_flag word to
+  // j + 1; slice j + 1 waits for it, continues the same K sequence from those accumulators
+  // and the last slice clears the word (the words are zero between launches).  sk_flag
+  // holds 2 ZO_SK_MAX_WG flag words, then ZO_SK_MAX_WG words for the XCD each workgroup
+  // ran on.  sk_err is set to 1 if a wait ever gives up, to 2 if a handover crossed XCDs.
+  float* sk_part;
+  int32_t* sk_flag;
+  int32_t* sk_err;
+  int sk_ncu;
 };
+// split-tail workgroups a workspace provides for (one per CU, at most; two buffers each)
+constexpr int ZO_SK_MAX_WG = 256;
 
 // Launch on `stream`; returns hipSuccess or the launch error.
 hipError_t gemm_launch_bf16(const GemmParams& p, int cfg, hipStream_t stream);

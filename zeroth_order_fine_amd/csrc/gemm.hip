@@ -22,6 +22,7 @@
 // sequence (same 128x64 wave tile, same K loop, no split-K).
 #include "common.h"
 #include <math.h>
+#include <stdlib.h>
 #include <type_traits>
 
 namespace {
@@ -694,7 +695,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void* base, int
   return __builtin_amdgcn_make_buffer_rsrc((void*)base, (short)0, (int)n, 0x00020000);
 }
 
-template <int BM, int BN, int WM, int WN, int EPI, bool F8>
+template <int BM, int BN, int WM, int WN, int EPI, bool F8, bool SK = false>
 __global__ void __launch_bounds__((BM / WM) * (BN / WN) * 64)
 gemm_bf16_pipe_kernel(GemmParams p) {
   constexpr int BK = 64;                               // bf16 elements of a K-step (128 bytes a row)
@@ -709,24 +710,31 @@ gemm_bf16_pipe_kernel(GemmParams p) {
   bf16_t* sm = (bf16_t*)smem_raw;                      // [A stage 0 | A stage 1 | B stage 0 | B stage 1]
 
   const int n_mt = (p.M + BM - 1) / BM, n_nt = (p.N + BN - 1) / BN;
-  int logical;
-  tile_swizzle(blockIdx.x, n_mt * n_nt, logical);
-  // groups of GM m-tiles, column-major inside a group: the ~32 tiles an XCD runs at
-  // once share a few A and B panels, so each K-step's chunks are fetched into its L2
-  // once and reused
+  // logical tile -> origin (m0, n0): groups of GM m-tiles, column-major inside a group:
+  // the ~32 tiles an XCD runs at once share a few A and B panels, so each K-step's chunks
+  // are fetched into its L2 once and reused.  a_side_off: the side-segment As columns of
+  // the kind group the column tile lies in.
   constexpr int GM = 4;
-  const int per_group = GM * n_nt;
-  const int g = logical / per_group, gm0 = g * GM;
-  const int gsize = min(GM, n_mt - gm0);
-  const int in_g = logical - g * per_group;
-  const int mt = gm0 + in_g % gsize, nt = in_g / gsize;
-  const int m0 = mt * BM, n0 = nt * BN;
+  int m0 = 0, n0 = 0, a_side_off = 0;
+  auto set_tile = [&](int logical) {
+    const int per_group = GM * n_nt;
+    const int g = logical / per_group, gm0 = g * GM;
+    const int gsize = min(GM, n_mt - gm0);
+    const int in_g = logical - g * per_group;
+    m0 = (gm0 + in_g % gsize) * BM;
+    n0 = (in_g / gsize) * BN;
+    const int grp = (p.n_bounds > 0 && n0 >= p.bounds[0]) + (p.n_bounds > 1 && n0 >= p.bounds[1]) +
+                    (p.n_bounds > 2 && n0 >= p.bounds[2]);
+    a_side_off = grp * (p.as_stride ? p.as_stride : p.ks_tile);
+  };
+  if constexpr (!SK) {
+    int logical;
+    tile_swizzle(blockIdx.x, n_mt * n_nt, logical);
+    set_tile(logical);
+  }
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int wave_s = __builtin_amdgcn_readfirstlane(wave);
   const int wm = wave / NWN, wn = wave % NWN;
-  const int grp = (p.n_bounds > 0 && n0 >= p.bounds[0]) + (p.n_bounds > 1 && n0 >= p.bounds[1]) +
-                  (p.n_bounds > 2 && n0 >= p.bounds[2]);
-  const int a_side_off = grp * (p.as_stride ? p.as_stride : p.ks_tile);
   int nkb = p.K / BKM, nk = nkb + p.ks_tile / BK;
   int kt_off = 0;                      // first K-step of this workgroup's K-slice
   if constexpr (EPI == EPI_PARTIAL) {  // split-K: the last K-slice also runs the side segment
@@ -738,8 +746,16 @@ gemm_bf16_pipe_kernel(GemmParams p) {
   const int nkwa = p.kwa ? p.kwa / BKM : (1 << 30), nkwb = p.kwb ? p.kwb / BKM : (1 << 30);
   const int nkwas = p.kwas ? p.kwas / BK : (1 << 30);
   constexpr int ESZ = F8 ? 1 : 2;                      // main-segment bytes per element
-  const __amdgpu_buffer_rsrc_t rA = raw_rsrc(p.A, (int64_t)p.M * p.lda * ESZ);
-  const __amdgpu_buffer_rsrc_t rB = raw_rsrc(p.B, (int64_t)p.N * p.ldb * ESZ);
+  // The split-tail kernel keeps the per-lane offsets tile-independent (rows of the tile, no clamp) and
+  // moves the tile origin into the buffer resources, which end at the last row (rows past
+  // it read as zero and feed only outputs that are never stored); otherwise the resources
+  // cover the whole operands and rows are clamped to the last one.
+  __amdgpu_buffer_rsrc_t rA = raw_rsrc(p.A, (int64_t)p.M * p.lda * ESZ);
+  __amdgpu_buffer_rsrc_t rB = raw_rsrc(p.B, (int64_t)p.N * p.ldb * ESZ);
+  auto set_rsrc = [&]() {
+    rA = raw_rsrc((const unsigned char*)p.A + (int64_t)m0 * p.lda * ESZ, (int64_t)(p.M - m0) * p.lda * ESZ);
+    rB = raw_rsrc((const unsigned char*)p.B + (int64_t)n0 * p.ldb * ESZ, (int64_t)(p.N - n0) * p.ldb * ESZ);
+  };
 
   // load i of this wave fills 1 KB block wave * I + i: tile row blk * 8 + lane / 8, the
   // lane's 16 bytes holding logical chunk (lane % 8) ^ swz8(row).  Byte offsets of the
@@ -756,13 +772,19 @@ gemm_bf16_pipe_kernel(GemmParams p) {
   // byte offsets: the host keeps every operand under 2^31 elements, so they fit 32 unsigned
   // bits (e4m3 operands: one byte an element, 16 elements a chunk)
   uint32_t aoff[IA], boff[IB];
-  if constexpr (F8) {
-    static_for<0, IA>([&](auto i) { aoff[i] = (uint32_t)(a_row(i) * (int)p.lda) + (uint32_t)(a_chk(i) << 4); });
-    static_for<0, IB>([&](auto i) { boff[i] = (uint32_t)(b_row(i) * (int)p.ldb) + (uint32_t)(b_chk(i) << 4); });
-  } else {
-    static_for<0, IA>([&](auto i) { aoff[i] = (uint32_t)a_elem(i, (int)p.lda) * 2u; });
-    static_for<0, IB>([&](auto i) { boff[i] = (uint32_t)b_elem(i, (int)p.ldb) * 2u; });
-  }
+  auto set_offsets = [&]() {
+    if constexpr (SK) {
+      static_for<0, IA>([&](auto i) { aoff[i] = (uint32_t)(((wave * IA + i) * 8 + lrow) * (int)p.lda + (a_chk(i) << 3)) * 2u; });
+      static_for<0, IB>([&](auto i) { boff[i] = (uint32_t)(((wave * IB + i) * 8 + lrow) * (int)p.ldb + (b_chk(i) << 3)) * 2u; });
+    } else if constexpr (F8) {
+      static_for<0, IA>([&](auto i) { aoff[i] = (uint32_t)(a_row(i) * (int)p.lda) + (uint32_t)(a_chk(i) << 4); });
+      static_for<0, IB>([&](auto i) { boff[i] = (uint32_t)(b_row(i) * (int)p.ldb) + (uint32_t)(b_chk(i) << 4); });
+    } else {
+      static_for<0, IA>([&](auto i) { aoff[i] = (uint32_t)a_elem(i, (int)p.lda) * 2u; });
+      static_for<0, IB>([&](auto i) { boff[i] = (uint32_t)b_elem(i, (int)p.ldb) * 2u; });
+    }
+  };
+  if constexpr (!SK) set_offsets();
   // K-step order: bf16 kernels run the main segment, then the side segment; the e4m3
   // kernel runs its (bf16) side segment first, so that the side operands' offsets are dead
   // before the main loop, which needs every register it has
@@ -781,6 +803,24 @@ gemm_bf16_pipe_kernel(GemmParams p) {
       static_for<0, IB>([&](auto i) {
         __builtin_amdgcn_raw_ptr_buffer_load_lds(
             rB, (__attribute__((address_space(3))) void*)(sB + (wave * IB + i) * 8 * BK), 16, boff[i], kb, 0, 0);
+      });
+    } else if constexpr (SK) {                // side segment, split-tail form
+      const __amdgpu_buffer_rsrc_t rAs =
+          raw_rsrc((const unsigned char*)p.As + (int64_t)m0 * p.ldas * 2, (int64_t)(p.M - m0) * p.ldas * 2);
+      const __amdgpu_buffer_rsrc_t rBs =
+          raw_rsrc((const unsigned char*)p.Bs + (int64_t)n0 * p.ldbs * 2, (int64_t)(p.N - n0) * p.ldbs * 2);
+      const int kk = s - nkb;
+      const int ka = ((kk >= nkwas ? kk - nkwas : kk) * BK + a_side_off) * 2;
+      const int kb = kk * BK * 2;
+      static_for<0, IA>([&](auto i) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rAs, (__attribute__((address_space(3))) void*)(sA + (wave * IA + i) * 8 * BK), 16,
+            (uint32_t)(((wave * IA + i) * 8 + lrow) * (int)p.ldas + (a_chk(i) << 3)) * 2u, ka, 0, 0);
+      });
+      static_for<0, IB>([&](auto i) {
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(
+            rBs, (__attribute__((address_space(3))) void*)(sB + (wave * IB + i) * 8 * BK), 16,
+            (uint32_t)(((wave * IB + i) * 8 + lrow) * (int)p.ldbs + (b_chk(i) << 3)) * 2u, kb, 0, 0);
       });
     } else {                                  // side segment
       const __amdgpu_buffer_rsrc_t rAs = raw_rsrc(p.As, (int64_t)p.M * p.ldas * 2);
@@ -820,9 +860,13 @@ gemm_bf16_pipe_kernel(GemmParams p) {
     static_for<0, TN>([&](auto j) { fb[u][j] = *(const bf16x8_t*)(sm + slot * BSZ + bro[u][j]); });
   };
   floatx4_t acc[TM][TN];
-  static_for<0, TM>([&](auto i) {
-    static_for<0, TN>([&](auto j) { acc[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f}; });
-  });
+  auto zero_acc = [&]() {
+    static_for<0, TM>([&](auto i) {
+      static_for<0, TN>([&](auto j) { acc[i][j] = floatx4_t{0.f, 0.f, 0.f, 0.f}; });
+    });
+  };
+  if constexpr (!SK) zero_acc();
+  int kend = nk;                                       // the current K range ends before step kend
   auto mm = [&](auto u) {
     static_for<0, TM>([&](auto i) {
       static_for<0, TN>([&](auto j) {
@@ -832,7 +876,7 @@ gemm_bf16_pipe_kernel(GemmParams p) {
   };
   constexpr int MPR = (TM * TN) / (TM + TN);           // MFMAs per interleaved LDS read
   auto step_bf16 = [&](int kt, auto slot) {
-    if (kt + 1 < nk) issue(kt + 1, std::integral_constant<int, 1 - slot>{});
+    if (kt + 1 < kend) issue(kt + 1, std::integral_constant<int, 1 - slot>{});
     rd(slot, std::integral_constant<int, 0>{});
     rd(slot, std::integral_constant<int, 1>{});
     mm(std::integral_constant<int, 0>{});
@@ -855,7 +899,7 @@ gemm_bf16_pipe_kernel(GemmParams p) {
   typedef __attribute__((ext_vector_type(8))) int i32x8_t;
   typedef __attribute__((ext_vector_type(4))) int i32x4_t;
   auto step8 = [&](int kt, auto slot, auto side) {
-    if (kt + 1 < nk) issue(kt + 1, std::integral_constant<int, 1 - slot>{});
+    if (kt + 1 < kend) issue(kt + 1, std::integral_constant<int, 1 - slot>{});
     // chunk lk + 4 = chunk lk ^ 4, so its offset is the first one's with bit 5 flipped (row
     // starts are multiples of 64 elements); only the first offsets stay in registers
     i32x8_t ga[TM], gb[TN];
@@ -899,39 +943,157 @@ gemm_bf16_pipe_kernel(GemmParams p) {
   // this wave's loads of stage kt have landed; after the barrier so have every wave's,
   // and every read of the other stage (kt - 1) is retired
   auto wait_stage = [&]() { asm volatile("s_waitcnt vmcnt(0)\n\ts_barrier" ::: "memory"); };
-  if (nk > 0) issue(0, std::integral_constant<int, 0>{});
-  if constexpr (F8) {
-    // the bf16 side segment, then the e4m3 main segment, in separate loops (stage kt in
-    // slot kt & 1)
-    int kt = 0;
-    using S0 = std::integral_constant<int, 0>;
-    using S1 = std::integral_constant<int, 1>;
-    using SIDE = std::true_type;
-    using MAIN = std::false_type;
-    for (; kt < nks; ++kt) {
-      wait_stage();
-      if (kt & 1) step8(kt, S1{}, SIDE{});
-      else step8(kt, S0{}, SIDE{});
+  using S0 = std::integral_constant<int, 0>;
+  using S1 = std::integral_constant<int, 1>;
+  // bf16 K-steps [kb, ke) of the current tile, stage kt in slot (kt - kb) & 1
+  auto kloop_bf16 = [&](int kb, int ke) {
+    kend = ke;
+    if (kb < ke) issue(kb, S0{});
+    for (int kt = kb; kt < ke; kt += 2) {
+      wait_stage(); step_bf16(kt, S0{});
+      if (kt + 1 < ke) { wait_stage(); step_bf16(kt + 1, S1{}); }
     }
-    if ((kt & 1) && kt < nk) { wait_stage(); step8(kt, S1{}, MAIN{}); ++kt; }
-    for (; kt + 1 < nk; kt += 2) {
-      wait_stage(); step8(kt, S0{}, MAIN{});
-      wait_stage(); step8(kt + 1, S1{}, MAIN{});
-    }
-    if (kt < nk) { wait_stage(); step8(kt, S0{}, MAIN{}); }
-  } else {
-    for (int kt = 0; kt < nk; kt += 2) {
-      wait_stage(); step_bf16(kt, std::integral_constant<int, 0>{});
-      if (kt + 1 < nk) { wait_stage(); step_bf16(kt + 1, std::integral_constant<int, 1>{}); }
-    }
-  }
-  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no LDS write outlives the workgroup
+  };
   // the epilogue's coordinates come from the wave index in a scalar register and the lane
   // index counted afresh, so no vector register is kept live across the K loop (where every
   // one is taken) for them
-  const int lane_e = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
-  epilogue_rows<EPI, TM, TN, BM, BN, WM, WN, F8>(p, acc, m0, n0, wave_s / NWN, wave_s % NWN, lane_e,
-                                                (float*)smem_raw);
+  auto finish = [&]() {
+    const int lane_e = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    epilogue_rows<EPI, TM, TN, BM, BN, WM, WN, F8>(p, acc, m0, n0, wave_s / NWN, wave_s % NWN, lane_e,
+                                                  (float*)smem_raw);
+  };
+  if constexpr (!SK) {
+    if constexpr (F8) {
+      // the bf16 side segment, then the e4m3 main segment, in separate loops (stage kt in
+      // slot kt & 1)
+      if (nk > 0) issue(0, S0{});
+      int kt = 0;
+      using SIDE = std::true_type;
+      using MAIN = std::false_type;
+      for (; kt < nks; ++kt) {
+        wait_stage();
+        if (kt & 1) step8(kt, S1{}, SIDE{});
+        else step8(kt, S0{}, SIDE{});
+      }
+      if ((kt & 1) && kt < nk) { wait_stage(); step8(kt, S1{}, MAIN{}); ++kt; }
+      for (; kt + 1 < nk; kt += 2) {
+        wait_stage(); step8(kt, S0{}, MAIN{});
+        wait_stage(); step8(kt + 1, S1{}, MAIN{});
+      }
+      if (kt < nk) { wait_stage(); step8(kt, S0{}, MAIN{}); }
+    } else {
+      kloop_bf16(0, nk);
+    }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // no LDS write outlives the workgroup
+    finish();
+  } else {
+    // Split tail: gridDim.x persistent workgroups, dispatched round-robin over the 8 XCDs
+    // (workgroup b on XCD b % 8, slot b / 8 of Px there).  Each XCD owns the contiguous
+    // logical tiles tile_swizzle gives it.  All but the last one to two rounds of them run
+    // as whole tiles (round r: tile r * Px + slot, as the data-parallel launch orders them).
+    // The last Tsk tiles (Px <= Tsk < 2 Px) are cut along K into S equal slices (S from 1 to
+    // 4: the fewest rounds of slices, in tiles), and the Tsk * S pieces are dealt round-robin:
+    // piece q, slice q / Tsk of tile q % Tsk, goes to slot q % Px.  A round's pieces are then
+    // mostly one slice of Px consecutive tiles, all at the same K-steps, so the XCD's L2
+    // serves them from shared panel chunks as in a whole-tile round.  Slice j > 0 of a tile
+    // starts from the fp32 accumulators slice j - 1 left in the tile's sk_part buffer (its
+    // flag then reads j) and continues the same MFMA sequence, so every element gets the bits
+    // of the whole-tile kernel; the last slice runs the epilogue and clears the flag.  A slice
+    // waits only for the previous slice of its tile, dealt to an earlier round; the wait is
+    // bounded all the same.
+    static_assert(!F8 && EPI != EPI_PARTIAL && EPI != EPI_LMHEAD && EPI != EPI_TPROJ, "split tail: projections");
+    const int Px = (int)(gridDim.x >> 3), xcd = (int)(blockIdx.x & 7), sl = (int)(blockIdx.x >> 3);
+    const int T = n_mt * n_nt, per = T >> 3, rem = T & 7;
+    const int Tx = per + (xcd < rem ? 1 : 0);
+    const int t0 = xcd < rem ? xcd * (per + 1) : rem * (per + 1) + (xcd - rem) * per;
+    const int R = Tx / Px > 0 ? Tx / Px - 1 : 0;       // whole-tile rounds
+    const int tb = t0 + R * Px;                        // first shared tile
+    const int Tsk = Tx - R * Px;                       // shared tiles
+    // S: the fewest rounds of slices, in tiles (ceil(Tsk S / Px) / S), among the S for which
+    // no slot runs two slices j and j + k (k >= 2) of one tile: a slot reads a tile's buffer
+    // at most once, so its L1 never holds a stale copy of it
+    int S = 1, best = (Tsk + Px - 1) / Px;
+    for (int c = 2; c <= 4 && nk / c >= 2; ++c) {
+      bool ok = true;
+      for (int k = 2; k < c; ++k) ok = ok && (k * Tsk) % Px != 0;
+      const int rounds = (Tsk * c + Px - 1) / Px;
+      if (ok && rounds * S < best * c) { S = c; best = rounds; }
+    }
+    const int nq = Tsk * S;
+    const int npc = R + (nq > sl ? (nq - sl + Px - 1) / Px : 0);
+    constexpr int NACC = TM * TN;
+    // accumulator image of shared tile t: [wave][block i * TN + j][lane] of 16-byte quads,
+    // coalesced 1 KB rows (the lane index counted afresh, as in the epilogue)
+    auto part_at = [&](int buf) {
+      const int ln = (int)__builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+      return (float*)((floatx4_t*)(p.sk_part + (int64_t)buf * (BM * BN)) + (int64_t)wave_s * NACC * 64 + ln);
+    };
+    auto first_thread = [&]() {
+      return wave_s == 0 && __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u)) == 0;
+    };
+    // The handover goes through the XCD's L2 (plain stores, loads that miss the L1: the buffer
+    // was never read on this CU), which holds only if producer and consumer share an XCD.
+    // Workgroups b and b + 8 do under the round-robin dispatch; each workgroup records the
+    // XCD it runs on, and a consumer that finds its producer on another XCD reports it
+    // (sk_err = 2) instead of trusting the data.
+    int32_t* const xcc_of = p.sk_flag + 2 * ZO_SK_MAX_WG;
+    const int my_xcc = __builtin_amdgcn_s_getreg((20) | (0 << 6) | ((4 - 1) << 11));   // HW_REG_XCC_ID[3:0]
+    if (first_thread()) __hip_atomic_store(xcc_of + blockIdx.x, my_xcc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+    set_offsets();                                     // tile-independent (the origin is in rA / rB)
+    for (int pc = 0; pc < npc; ++pc) {
+      int logical, kb = 0, ke = nk, j = 0, t = 0;
+      if (pc < R) {
+        logical = t0 + pc * Px + sl;
+      } else {
+        const int q = (pc - R) * Px + sl;
+        j = q / Tsk;
+        t = q - j * Tsk;
+        logical = tb + t;
+        kb = nk * j / S;
+        ke = nk * (j + 1) / S;
+      }
+      const int buf = xcd * 2 * Px + t;                // 2 Px buffers per XCD
+      set_tile(logical);
+      set_rsrc();
+      __syncthreads();                                 // the previous piece's LDS reads are done
+      if (j > 0) {
+        if (first_thread()) {
+          int n = 0;
+          while (__hip_atomic_load(p.sk_flag + buf, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != j) {
+            if (++n > (1 << 20)) { __hip_atomic_store(p.sk_err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT); break; }
+            __builtin_amdgcn_s_sleep(2);
+          }
+          // producer of slice j - 1: piece q - Tsk, slot (q - Tsk) % Px of this XCD class
+          const int prod = (((pc - R) * Px + sl - Tsk) % Px) * 8 + xcd;
+          if (__hip_atomic_load(xcc_of + prod, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) != my_xcc)
+            __hip_atomic_store(p.sk_err, 2, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        }
+        __syncthreads();
+        float* src = part_at(buf);
+        static_for<0, TM>([&](auto i) {
+          static_for<0, TN>([&](auto jj) { acc[i][jj] = *(const floatx4_t*)(src + (i * TN + jj) * 256); });
+        });
+      } else {
+        zero_acc();
+      }
+      kloop_bf16(kb, ke);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      if (pc >= R && j < S - 1) {
+        // plain stores into the XCD's L2 (no agent-scope release: it would write back the
+        // whole L2), complete before the barrier; the flag moves on after it
+        float* dst = part_at(buf);
+        static_for<0, TM>([&](auto i) {
+          static_for<0, TN>([&](auto jj) { *(floatx4_t*)(dst + (i * TN + jj) * 256) = acc[i][jj]; });
+        });
+        __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+        __syncthreads();
+        if (first_thread()) __hip_atomic_store(p.sk_flag + buf, j + 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      } else {
+        if (j > 0 && first_thread()) __hip_atomic_store(p.sk_flag + buf, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+        finish();
+      }
+    }
+  }
 }
 
 // ------------------------------------------------------------------------------
@@ -1034,6 +1196,23 @@ hipError_t launch_bf16_pipe(const GemmParams& p, hipStream_t s) {
   const int tiles = ((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN);
   const int z = EPI == EPI_PARTIAL ? p.ksplit : 1;
   hipLaunchKernelGGL((gemm_bf16_pipe_kernel<BM, BN, WM, WN, EPI, F8>), dim3(tiles, 1, z), dim3(NT), smem, s, p);
+  return hipGetLastError();
+}
+
+// Split-tail launch of the 256x256 projection kernel: p.sk_ncu persistent workgroups
+template <int EPI>
+hipError_t launch_bf16_pipe_sk(const GemmParams& p, hipStream_t s) {
+  constexpr int BM = 256, BN = 256, WM = 128, WN = 64;
+  constexpr int NT = (BM / WM) * (BN / WN) * 64;
+  const size_t smem = (size_t)2 * (BM + BN) * 64 * sizeof(bf16_t);
+  static bool attr_set = false;
+  if (!attr_set) {
+    hipError_t e = hipFuncSetAttribute((const void*)gemm_bf16_pipe_kernel<BM, BN, WM, WN, EPI, false, true>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)smem);
+    if (e != hipSuccess) return e;
+    attr_set = true;
+  }
+  hipLaunchKernelGGL((gemm_bf16_pipe_kernel<BM, BN, WM, WN, EPI, false, true>), dim3(p.sk_ncu), dim3(NT), smem, s, p);
   return hipGetLastError();
 }
 
@@ -1332,6 +1511,28 @@ int pipe_tile(const GemmParams& p) {
   return t256 >= 128 ? 0 : 1;
 }
 
+// Split tail for a 256x256-tile projection: when the workspace provides for it, every CU can
+// hold a workgroup, there is at least one whole round of tiles, and the last round of the
+// data-parallel launch would leave more than 2 % of the CU time idle.  ZO_GEMM_STREAMK=0
+// turns it off (the outputs are the same bits either way).
+bool use_streamk(const GemmParams& p) {
+  if (!p.sk_part || !p.sk_flag || !p.sk_err || p.sk_ncu < 8 || p.sk_ncu % 8 != 0 || p.sk_ncu > ZO_SK_MAX_WG)
+    return false;
+  if (p.a_e4m3 || p.b_e4m3 || p.ksplit > 1) return false;
+  // (the GELU / SwiGLU epilogues with their side-input partials would spill in the K loop
+  // beside the piece state)
+  if (p.epi != EPI_STORE && p.epi != EPI_RESID) return false;
+  // the slices' handovers pay for themselves on long K only (measured at OPT-13B batch 64:
+  // fc2, 320 K-steps, 1590 -> 1487 us; o, 80 K-steps, 431 -> 476 us)
+  if (p.K / 64 + p.ks_tile / 64 < 160) return false;
+  const char* env = getenv("ZO_GEMM_STREAMK");
+  if (env && env[0] == '0') return false;
+  const int64_t t = (int64_t)((p.M + 255) / 256) * ((p.N + 255) / 256), P = p.sk_ncu;
+  if (t < P) return false;
+  const int64_t rounds = (t + P - 1) / P;
+  return (double)(rounds * P - t) > 0.02 * (double)t;
+}
+
 hipError_t gemm_launch_bf16(const GemmParams& p, int cfg, hipStream_t s) {
   if (p.M <= 0 || p.N <= 0) return hipSuccess;
   if (cfg == GEMM_CFG_BIG) {
@@ -1357,7 +1558,13 @@ hipError_t gemm_launch_bf16(const GemmParams& p, int cfg, hipStream_t s) {
     if (p.a_e4m3 || p.b_e4m3) return launch_pipe_epi<128, 128, 64, 64>(p, s);
     // (measured at OPT-13B batch 64: finishing the last partial round of 256x256 tiles in
     // 128x128 tiles of a second launch made the projections 6 % slower, not faster)
-    if (pipe_tile(p) == 0) return launch_pipe_epi<256, 256, 128, 64>(p, s);
+    if (pipe_tile(p) == 0) {
+      if (use_streamk(p)) {
+        if (p.epi == EPI_STORE) return launch_bf16_pipe_sk<EPI_STORE>(p, s);
+        return launch_bf16_pipe_sk<EPI_RESID>(p, s);
+      }
+      return launch_pipe_epi<256, 256, 128, 64>(p, s);
+    }
     return launch_pipe_epi<128, 128, 64, 64>(p, s);
   }
   if (cfg == GEMM_CFG_NARROW) {

@@ -286,6 +286,7 @@ struct zo_model {
   float2* rope = nullptr;   // [rope_len x head_dim/2] (cos, sin), Qwen3
   int rope_len = 0;
   int device = 0;
+  int n_cu = 0;        // compute units of the device (0: unknown, no split-tail projections)
   GraphCache gc;       // zo_score's forward pass
   GraphCache gcd;      // a decode step of zo_generate
 };
@@ -537,7 +538,10 @@ struct WsPtrs {
   int32_t *row_src, *row_pos, *row_cand, *phys_cu, *phys_first, *sc_row, *sc_lab_src, *work, *labels;
   int32_t* cand_dir;
   int32_t* cand_slot;           // computed t slot of the candidate's direction
-  int32_t* bad_ids;             // set by the kernels when a token id lies outside [0, vocab)
+  int32_t* bad_ids;             // [0]: set by the kernels when a token id lies outside [0, vocab);
+                                // [1]: set by a split-tail projection whose wait gave up
+  float* sk_part = nullptr;     // split-tail projections: accumulator images and flags (null: none)
+  int32_t* sk_flag = nullptr;
   float* cand_scale;
   SideJob* jobs;
   int64_t as_ld;                // As row pitch (elements), the same for every group
@@ -625,6 +629,15 @@ int n_side_jobs(const zo_model_desc& d, const zo_plan_s& p, const SideGeom& sg) 
   return d.n_layers * kinds * per_kind;
 }
 
+// Split-tail projections (q|k|v, o and fc2 / down of bf16 models, 256x256 tiles) need room
+// for two 256 x 256 fp32 accumulator images and two flags per workgroup; reserved when the
+// widest of them spans at least one round of ZO_SK_MAX_WG tiles at this batch.
+bool sk_workspace(const zo_model_desc& d, int64_t M) {
+  if (d.dtype != ZO_DTYPE_BF16) return false;
+  const int64_t nqkv = (int64_t)(d.n_heads + 2 * d.n_kv_heads) * d.head_dim;
+  return ((M + 255) / 256) * ((std::max<int64_t>(nqkv, d.d_model) + 255) / 256) >= ZO_SK_MAX_WG;
+}
+
 // kv_rows > 0: a generation call whose caches hold kv_rows rows per layer
 void carve(const zo_model* m, const zo_plan_s& p, const Packing& pk, const SideGeom& sg, void* base, WsPtrs& w,
            int64_t kv_rows = 0) {
@@ -644,7 +657,7 @@ void carve(const zo_model* m, const zo_plan_s& p, const Packing& pk, const SideG
   w.labels = b.take<int32_t>(S);
   w.cand_dir = b.take<int32_t>(nc);
   w.cand_slot = b.take<int32_t>(nc);
-  w.bad_ids = b.take<int32_t>(1);
+  w.bad_ids = b.take<int32_t>(2);
   w.cand_scale = b.take<float>(nc);
   w.jobs = b.take<SideJob>(std::max(n_side_jobs(d, p, sg), 1));
   const int64_t D = d.d_model, F = d.d_ffn;
@@ -674,6 +687,10 @@ void carve(const zo_model* m, const zo_plan_s& p, const Packing& pk, const SideG
   w.side_begin = base ? (unsigned char*)base + side0 : nullptr;
   w.side_bytes = b.off - side0;
   w.xs = b.take<unsigned char>(S * D * as * (split_head(p) ? 2 : 1));
+  if (sk_workspace(d, pk.M)) {
+    w.sk_part = b.take<float>((int64_t)2 * ZO_SK_MAX_WG * 256 * 256);
+    w.sk_flag = b.take<int32_t>(3 * ZO_SK_MAX_WG);
+  }
   {
     int64_t np = 0, npd = 0;
     for (int g = 0; g < 4; ++g) {
@@ -838,6 +855,9 @@ int forward(zo_model* m, const zo_plan_s& p, const Packing& pk, const SideGeom& 
     GemmParams gp = gemm_base(X, lda, B, K, M, N, K * (split ? 2 : 1));
     if (split) gp.kwb = K;
     gp.a_e4m3 = gp.b_e4m3 = f8;
+    if (w.sk_part && !f8) {
+      gp.sk_part = w.sk_part; gp.sk_flag = w.sk_flag; gp.sk_err = w.bad_ids + 1; gp.sk_ncu = m->n_cu;
+    }
     if (gen && gen->decode && !sp && bf) {
       // decode steps (one row per sequence): K-slices until the 128x128 tiles fill the
       // CUs, at least four K-steps (64 bf16 or 128 e4m3 deep) a slice
@@ -1087,6 +1107,7 @@ int zo_model_create(const zo_model_desc* desc, void* weights_dev, size_t bytes, 
   m->w = (unsigned char*)weights_dev;
   m->w_bytes = bytes;
   if (hipGetDevice(&m->device) != hipSuccess) m->device = 0;
+  if (hipDeviceGetAttribute(&m->n_cu, hipDeviceAttributeMultiprocessorCount, m->device) != hipSuccess) m->n_cu = 0;
   (void)scratch_init(m->device);        // the device is current: record its scratch address
   if (!is_opt(*desc)) {
     // RoPE table: inv_freq_i = theta^(-2i/hd); angle = pos * inv_freq_i, in fp64, stored fp32
@@ -1352,7 +1373,8 @@ static int prepare_call(zo_model* m, const zo_plan_t* p, const zo_bank* bank, co
   ZO_HIP(h2d(w.sc_row, pk.sc_row.data(), pk.sc_row.size() * 4));
   ZO_HIP(h2d(w.sc_lab_src, pk.sc_lab_src.data(), pk.sc_lab_src.size() * 4));
   ZO_HIP(h2d(w.work, pk.work.data(), pk.work.size() * 4));
-  ZO_HIP(hipMemsetAsync(w.bad_ids, 0, sizeof(int32_t), s));
+  ZO_HIP(hipMemsetAsync(w.bad_ids, 0, 2 * sizeof(int32_t), s));
+  if (w.sk_flag) ZO_HIP(hipMemsetAsync(w.sk_flag, 0, 2 * ZO_SK_MAX_WG * sizeof(int32_t), s));
   std::vector<int32_t>& cslot = keep.cslot;
   cslot.assign(nc, -1);
   for (int c = 0; c < nc && !sg.dslot.empty(); ++c) cslot[c] = sg.dslot[cdir[c]];
@@ -1484,12 +1506,19 @@ int zo_score(zo_model* m, const zo_plan_t* p, const zo_bank* bank, const zo_batc
   prof_stop(ps_red.rec, s);
   ps_red.rec = -1;
   std::vector<double> seq(pk.n_phys);
-  int32_t bad = 0;
+  int32_t bad[2] = {0, 0};
   if (pk.n_phys > 0)
     ZO_HIP(hipMemcpyAsync(seq.data(), seq_out, pk.n_phys * sizeof(double), hipMemcpyDeviceToHost, s));
-  ZO_HIP(hipMemcpyAsync(&bad, w.bad_ids, sizeof bad, hipMemcpyDeviceToHost, s));
+  ZO_HIP(hipMemcpyAsync(bad, w.bad_ids, sizeof bad, hipMemcpyDeviceToHost, s));
   ZO_HIP(hipStreamSynchronize(s));
-  ZO_CHECK(!bad, ZO_E_INVAL, "a token id of the batch lies outside [0, vocab)");
+  ZO_CHECK(!bad[0], ZO_E_INVAL, "a token id of the batch lies outside [0, vocab)");
+  if (bad[1]) {
+    m->n_cu = 0;        // split-tail projections off for this model from now on
+    m->gc.reset();
+    m->gcd.reset();
+    return fail(ZO_E_DEVICE, "a split-tail projection %s; turned off for this model, call again",
+                bad[1] == 2 ? "found a handover between XCDs" : "gave up waiting for a partial tile");
+  }
   for (int c = 0; c < nc; ++c) S_host[c] = 0.0;
   for (int q = 0; q < pk.n_phys; ++q)
     if (pk.phys_cand[q] >= 0) S_host[pk.phys_cand[q]] += seq[q];
@@ -1635,11 +1664,18 @@ int zo_generate(zo_model* m, const zo_plan_t* p, const zo_bank* bank, const zo_b
     ZO_HIP(launch_greedy_reduce(w.part, w.part_idx, n_tiles, nq, w.gen_tok, tokens_dev, logp_dev, n_new, j, s));
   }
   std::vector<float> lp((size_t)nq * n_new);
-  int32_t bad = 0;
+  int32_t bad[2] = {0, 0};
   ZO_HIP(hipMemcpyAsync(lp.data(), logp_dev, lp.size() * sizeof(float), hipMemcpyDeviceToHost, s));
-  ZO_HIP(hipMemcpyAsync(&bad, w.bad_ids, sizeof bad, hipMemcpyDeviceToHost, s));
+  ZO_HIP(hipMemcpyAsync(bad, w.bad_ids, sizeof bad, hipMemcpyDeviceToHost, s));
   ZO_HIP(hipStreamSynchronize(s));
-  ZO_CHECK(!bad, ZO_E_INVAL, "a token id of the batch lies outside [0, vocab)");
+  ZO_CHECK(!bad[0], ZO_E_INVAL, "a token id of the batch lies outside [0, vocab)");
+  if (bad[1]) {
+    m->n_cu = 0;        // split-tail projections off for this model from now on
+    m->gc.reset();
+    m->gcd.reset();
+    return fail(ZO_E_DEVICE, "a split-tail projection %s; turned off for this model, call again",
+                bad[1] == 2 ? "found a handover between XCDs" : "gave up waiting for a partial tile");
+  }
   for (int c = 0; c < nc; ++c) S_host[c] = 0.0;
   for (int q = 0; q < nq; ++q)
     if (pk.phys_cand[q] >= 0)
