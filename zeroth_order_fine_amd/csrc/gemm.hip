@@ -365,15 +365,24 @@ gemm_bf16_kernel(GemmParams p) {
 // n = j*16 + 4*(lane >> 4) + q inside the wave tile, so every lane owns four
 // consecutive output columns and writes them with one 8-byte (bf16) or 16-byte
 // (fp32 residual) access.
-// four consecutive bf16 outputs (8 bytes), plus their lo terms at + c_lo when set
-__device__ __forceinline__ void store_bf16x4(const GemmParams& p, bf16_t* o, floatx4_t v) {
-  bf16_t hi[4], lo[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) split_bf16(v[q], hi[q], lo[q]);
-  *(uint2*)o = make_uint2((uint32_t)hi[0] | ((uint32_t)hi[1] << 16), (uint32_t)hi[2] | ((uint32_t)hi[3] << 16));
-  if (p.c_lo)
-    *(uint2*)(o + p.c_lo) =
-        make_uint2((uint32_t)lo[0] | ((uint32_t)lo[1] << 16), (uint32_t)lo[2] | ((uint32_t)lo[3] << 16));
+// two fp32 values rounded to bf16 (nearest even) by the packed hardware conversion, packed
+// little-endian
+typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint32_t bf16x2_rne(float a, float b) {
+  return __builtin_bit_cast(uint32_t, bf16x2v_t{(__bf16)a, (__bf16)b});
+}
+// four consecutive bf16 outputs (8 bytes), plus their lo terms at + c_lo when set; returns
+// the values written (the hi terms), as the next projection reads them
+__device__ __forceinline__ floatx4_t store_bf16x4(const GemmParams& p, bf16_t* o, floatx4_t v) {
+  const uint32_t w0 = bf16x2_rne(v[0], v[1]), w1 = bf16x2_rne(v[2], v[3]);
+  *(uint2*)o = make_uint2(w0, w1);
+  const floatx4_t hi = floatx4_t{__builtin_bit_cast(float, w0 << 16), __builtin_bit_cast(float, w0 & 0xFFFF0000u),
+                                 __builtin_bit_cast(float, w1 << 16), __builtin_bit_cast(float, w1 & 0xFFFF0000u)};
+  if (p.c_lo) {
+    const floatx4_t d = v - hi;                        // exact in fp32
+    *(uint2*)(o + p.c_lo) = make_uint2(bf16x2_rne(d[0], d[1]), bf16x2_rne(d[2], d[3]));
+  }
+  return hi;
 }
 
 // four consecutive outputs as e4m3 codes (4 bytes)
@@ -570,11 +579,13 @@ __device__ __forceinline__ void epilogue_rows(const GemmParams& p, floatx4_t (&a
         floatx4_t v;
 #pragma unroll
         for (int q = 0; q < 4; ++q) v[q] = silu_fast(g[q]) * u[q];
-        if constexpr (F8)              // the e4m3 input of the down projection
+        if constexpr (F8) {            // the e4m3 input of the down projection
           store_e4m3x4((e4m3_t*)p.C + (int64_t)r * p.ldc + ob + jp * 16, v);
-        else
-          store_bf16x4(p, (bf16_t*)p.C + (int64_t)r * p.ldc + ob + jp * 16, v);
-        if (p.sf_n) side_partial4(p, stored4<F8>(v), e[jp], t[i]);
+          if (p.sf_n) side_partial4(p, stored4<true>(v), e[jp], t[i]);
+        } else {
+          const floatx4_t y = store_bf16x4(p, (bf16_t*)p.C + (int64_t)r * p.ldc + ob + jp * 16, v);
+          if (p.sf_n) side_partial4(p, y, e[jp], t[i]);
+        }
       }
     }
     if (p.sf_n)
@@ -634,8 +645,8 @@ __device__ __forceinline__ void epilogue_rows(const GemmParams& p, floatx4_t (&a
             floatx4_t v = acc[i][j] + bias[j];
 #pragma unroll
             for (int q = 0; q < 4; ++q) v[q] = gelu_fast(v[q]);
-            store_bf16x4(p, (bf16_t*)p.C + (int64_t)r * p.ldc + cb + j * 16, v);
-            if (p.sf_n) side_partial4(p, stored4<false>(v), e[j], t[i]);
+            const floatx4_t y = store_bf16x4(p, (bf16_t*)p.C + (int64_t)r * p.ldc + cb + j * 16, v);
+            if (p.sf_n) side_partial4(p, y, e[j], t[i]);
           }
         }
       }
