@@ -227,9 +227,8 @@ attn_bf16_kernel(const bf16_t* __restrict__ qkv, int ld, TO* __restrict__ out, i
         *(uint32_t*)(orow + hb * 16 + 4 * g) =
             f32x4_to_e4m3(acc[hb][0] * inv, acc[hb][1] * inv, acc[hb][2] * inv, acc[hb][3] * inv);
       } else {
-        uint32_t w0 = (uint32_t)f32_to_bf16(acc[hb][0] * inv) | ((uint32_t)f32_to_bf16(acc[hb][1] * inv) << 16);
-        uint32_t w1 = (uint32_t)f32_to_bf16(acc[hb][2] * inv) | ((uint32_t)f32_to_bf16(acc[hb][3] * inv) << 16);
-        *(uint2*)(orow + hb * 16 + 4 * g) = make_uint2(w0, w1);
+        *(uint2*)(orow + hb * 16 + 4 * g) =
+            make_uint2(bf16x2_rne(acc[hb][0] * inv, acc[hb][1] * inv), bf16x2_rne(acc[hb][2] * inv, acc[hb][3] * inv));
       }
     }
   }

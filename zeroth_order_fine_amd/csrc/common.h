@@ -18,6 +18,14 @@ __host__ __device__ inline bf16_t f32_to_bf16(float f) {
 __host__ __device__ inline float bf16_to_f32(bf16_t b) {
   return __builtin_bit_cast(float, ((uint32_t)b) << 16);
 }
+// two fp32 values rounded to bf16 (nearest even, as f32_to_bf16) by the packed hardware
+// conversion, packed little-endian; and back
+typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
+__device__ inline uint32_t bf16x2_rne(float a, float b) {
+  return __builtin_bit_cast(uint32_t, bf16x2v_t{(__bf16)a, (__bf16)b});
+}
+__device__ inline float bf16x2_lo(uint32_t w) { return __builtin_bit_cast(float, w << 16); }
+__device__ inline float bf16x2_hi(uint32_t w) { return __builtin_bit_cast(float, w & 0xFFFF0000u); }
 // Two-term bf16 expansion of an fp32 value: hi = bf16(v), lo = bf16(v - hi).
 // v - hi is exact in fp32, so hi + lo carries 16 significant bits (relative
 // error <= 2^-17); a product with an exact bf16 weight then needs two MFMAs.

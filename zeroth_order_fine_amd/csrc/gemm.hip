@@ -365,19 +365,12 @@ gemm_bf16_kernel(GemmParams p) {
 // n = j*16 + 4*(lane >> 4) + q inside the wave tile, so every lane owns four
 // consecutive output columns and writes them with one 8-byte (bf16) or 16-byte
 // (fp32 residual) access.
-// two fp32 values rounded to bf16 (nearest even) by the packed hardware conversion, packed
-// little-endian
-typedef __bf16 bf16x2v_t __attribute__((ext_vector_type(2)));
-__device__ __forceinline__ uint32_t bf16x2_rne(float a, float b) {
-  return __builtin_bit_cast(uint32_t, bf16x2v_t{(__bf16)a, (__bf16)b});
-}
 // four consecutive bf16 outputs (8 bytes), plus their lo terms at + c_lo when set; returns
 // the values written (the hi terms), as the next projection reads them
 __device__ __forceinline__ floatx4_t store_bf16x4(const GemmParams& p, bf16_t* o, floatx4_t v) {
   const uint32_t w0 = bf16x2_rne(v[0], v[1]), w1 = bf16x2_rne(v[2], v[3]);
   *(uint2*)o = make_uint2(w0, w1);
-  const floatx4_t hi = floatx4_t{__builtin_bit_cast(float, w0 << 16), __builtin_bit_cast(float, w0 & 0xFFFF0000u),
-                                 __builtin_bit_cast(float, w1 << 16), __builtin_bit_cast(float, w1 & 0xFFFF0000u)};
+  const floatx4_t hi = floatx4_t{bf16x2_lo(w0), bf16x2_hi(w0), bf16x2_lo(w1), bf16x2_hi(w1)};
   if (p.c_lo) {
     const floatx4_t d = v - hi;                        // exact in fp32
     *(uint2*)(o + p.c_lo) = make_uint2(bf16x2_rne(d[0], d[1]), bf16x2_rne(d[2], d[3]));
@@ -420,10 +413,10 @@ __device__ __forceinline__ void side_partial4(const GemmParams& p, floatx4_t y, 
 #pragma unroll
   for (int c = 0; c < 4; ++c)
     if (c < p.sf_n) {
-      t[c] = fmaf(y[0], bf16_to_f32((bf16_t)(e[c].x & 0xFFFFu)), t[c]);
-      t[c] = fmaf(y[1], bf16_to_f32((bf16_t)(e[c].x >> 16)), t[c]);
-      t[c] = fmaf(y[2], bf16_to_f32((bf16_t)(e[c].y & 0xFFFFu)), t[c]);
-      t[c] = fmaf(y[3], bf16_to_f32((bf16_t)(e[c].y >> 16)), t[c]);
+      t[c] = fmaf(y[0], bf16x2_lo(e[c].x), t[c]);
+      t[c] = fmaf(y[1], bf16x2_hi(e[c].x), t[c]);
+      t[c] = fmaf(y[2], bf16x2_lo(e[c].y), t[c]);
+      t[c] = fmaf(y[3], bf16x2_hi(e[c].y), t[c]);
     }
 }
 

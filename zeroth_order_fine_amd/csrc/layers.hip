@@ -80,9 +80,7 @@ template <>
 __device__ __forceinline__ void store4<float>(float* o, floatx4_t y) { *(floatx4_t*)o = y; }
 template <>
 __device__ __forceinline__ void store4<bf16_t>(bf16_t* o, floatx4_t y) {
-  const uint32_t w0 = (uint32_t)f32_to_bf16(y[0]) | ((uint32_t)f32_to_bf16(y[1]) << 16);
-  const uint32_t w1 = (uint32_t)f32_to_bf16(y[2]) | ((uint32_t)f32_to_bf16(y[3]) << 16);
-  *(uint2*)o = make_uint2(w0, w1);
+  *(uint2*)o = make_uint2(bf16x2_rne(y[0], y[1]), bf16x2_rne(y[2], y[3]));
 }
 template <>
 __device__ __forceinline__ void store4<e4m3_t>(e4m3_t* o, floatx4_t y) {
@@ -90,12 +88,10 @@ __device__ __forceinline__ void store4<e4m3_t>(e4m3_t* o, floatx4_t y) {
 }
 // two-term bf16 expansion: hi at o, lo at o + lo_off
 __device__ __forceinline__ void store4_split(bf16_t* o, int lo_off, floatx4_t y) {
-  bf16_t hi[4], lo[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) split_bf16(y[q], hi[q], lo[q]);
-  *(uint2*)o = make_uint2((uint32_t)hi[0] | ((uint32_t)hi[1] << 16), (uint32_t)hi[2] | ((uint32_t)hi[3] << 16));
-  *(uint2*)(o + lo_off) =
-      make_uint2((uint32_t)lo[0] | ((uint32_t)lo[1] << 16), (uint32_t)lo[2] | ((uint32_t)lo[3] << 16));
+  const uint32_t w0 = bf16x2_rne(y[0], y[1]), w1 = bf16x2_rne(y[2], y[3]);
+  *(uint2*)o = make_uint2(w0, w1);
+  const floatx4_t d = y - floatx4_t{bf16x2_lo(w0), bf16x2_hi(w0), bf16x2_lo(w1), bf16x2_hi(w1)};   // exact
+  *(uint2*)(o + lo_off) = make_uint2(bf16x2_rne(d[0], d[1]), bf16x2_rne(d[2], d[3]));
 }
 
 template <typename T>
@@ -242,28 +238,31 @@ norm_side_kernel(const float* __restrict__ h, int M, int d, const float* __restr
       if (i < d) {
         floatx4_t y = (v[k] - mean) * scale * *(const floatx4_t*)(w + i);
         if (b) y += *(const floatx4_t*)(b + i);
-        store4<T>(o + i, y);
-        if (cand >= 0) {
-          // the values the projection reads: y rounded to the output type
-          floatx4_t yr;
-          if constexpr (std::is_same<T, e4m3_t>::value) {
+        // the values the projection reads: y rounded to the output type
+        floatx4_t yr;
+        if constexpr (std::is_same<T, e4m3_t>::value) {
+          store4<T>(o + i, y);
+          if (cand >= 0) {
             const uint32_t code = f32x4_to_e4m3(y[0], y[1], y[2], y[3]);
             const u32x4_t wds = e4m3x8_to_bf16(make_uint2(code, 0u));
             yr = floatx4_t{bf16_to_f32((bf16_t)(wds[0] & 0xFFFFu)), bf16_to_f32((bf16_t)(wds[0] >> 16)),
                            bf16_to_f32((bf16_t)(wds[1] & 0xFFFFu)), bf16_to_f32((bf16_t)(wds[1] >> 16))};
-          } else {
-#pragma unroll
-            for (int q = 0; q < 4; ++q) yr[q] = bf16_to_f32(f32_to_bf16(y[q]));
           }
+        } else {
+          const uint32_t w0 = bf16x2_rne(y[0], y[1]), w1 = bf16x2_rne(y[2], y[3]);
+          *(uint2*)(o + i) = make_uint2(w0, w1);
+          yr = floatx4_t{bf16x2_lo(w0), bf16x2_hi(w0), bf16x2_lo(w1), bf16x2_hi(w1)};
+        }
+        if (cand >= 0) {
 #pragma unroll
           for (int c = 0; c < NC; ++c) {
             uint2 e;
             if constexpr (HOLD) e = vv[c][k];
             else e = *(const uint2*)(vt[c] + i);
-            t[c] = fmaf(yr[0], bf16_to_f32((bf16_t)(e.x & 0xFFFFu)), t[c]);
-            t[c] = fmaf(yr[1], bf16_to_f32((bf16_t)(e.x >> 16)), t[c]);
-            t[c] = fmaf(yr[2], bf16_to_f32((bf16_t)(e.y & 0xFFFFu)), t[c]);
-            t[c] = fmaf(yr[3], bf16_to_f32((bf16_t)(e.y >> 16)), t[c]);
+            t[c] = fmaf(yr[0], bf16x2_lo(e.x), t[c]);
+            t[c] = fmaf(yr[1], bf16x2_hi(e.x), t[c]);
+            t[c] = fmaf(yr[2], bf16x2_lo(e.y), t[c]);
+            t[c] = fmaf(yr[3], bf16x2_hi(e.y), t[c]);
           }
         }
       }
