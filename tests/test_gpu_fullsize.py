@@ -245,3 +245,31 @@ def test_full_width_layer_cuts(case, split):
     del model, bank, db, out
     gc.collect()
     torch.cuda.empty_cache()
+
+
+def test_full_size_opt13b_graph_replays():
+    """OPT-13B batch 64 scored from a captured HIP graph: the split-tail fc2 launches (their
+    flags cleared before every call, outside the graph) and every other launch replayed give
+    bitwise the eager results, across replays and a step change of the plan."""
+    need_gpu()
+    import torch
+    import zeroth_order_fine_amd as zo
+    gold, wl, batch, model, bank, db, out, phys, first = _run("opt13b")
+    bits = lambda o: (o["seq_logp"].cpu().numpy().view(np.uint64).copy(), o["tok_logp"].cpu().numpy().view(np.uint32).copy())
+    ref1 = bits(out)
+    ref2 = bits(zo.score(model, zo.Plan.from_workload(model, wl, t=2), bank, db, want_tokens=True))
+    model.set_graphs(True)
+    stream = torch.cuda.Stream()             # graphs are captured on the call's (non-default) stream
+    try:
+        with torch.cuda.stream(stream):
+            for k, t in enumerate((1, 1, 1, 2, 1)):
+                flush("opt13b graph call %d (t=%d)" % (k, t))
+                got = bits(zo.score(model, zo.Plan.from_workload(model, wl, t=t), bank, db, want_tokens=True))
+                ref = ref1 if t == 1 else ref2
+                assert np.array_equal(got[0], ref[0]) and np.array_equal(got[1], ref[1]), (k, t)
+                torch.cuda.synchronize()
+    finally:
+        model.set_graphs(False)
+    del model, bank, db, out
+    gc.collect()
+    torch.cuda.empty_cache()
