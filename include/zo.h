@@ -277,7 +277,13 @@ int zo_pack(const zo_plan_t* p, const zo_batch* b, int32_t* phys_seq, int32_t* p
  *   tok_logp_dev  device fp32 [n_scored] or NULL: every scored log-prob in packing order
  *   S_host        host fp64 [n_cand]: S_c = sum over candidate c's sequences in packing
  *                 order (the summed label log-probs "L+/-"; loss L = -S)
- * Enqueued on `stream`; returns after synchronising that stream (S_host is valid). */
+ * Enqueued on `stream`; returns after synchronising that stream (S_host is valid).
+ * At batches of at least one round of 256x256 tiles, the long-K projections (fc2 / down,
+ * K >= 10240) run as persistent launches of one workgroup per CU whose last tiles are
+ * handed between workgroups in K-slices; they expect the GPU to themselves.  Should a
+ * handover wait give up (other kernels holding CUs for a long time) or cross XCDs, the
+ * call fails with ZO_E_DEVICE and the model stops using them (call again); setting the
+ * environment variable ZO_GEMM_STREAMK=0 keeps every projection data-parallel (same bits). */
 int zo_score(zo_model* m, const zo_plan_t* p, const zo_bank* bank, const zo_batch* b, void* ws_dev,
              size_t ws_bytes, double* seq_logp_dev, float* tok_logp_dev, double* S_host, void* stream);
 
