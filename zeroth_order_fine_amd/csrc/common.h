@@ -134,8 +134,8 @@ struct GemmParams {
   int a_e4m3, b_e4m3;
   // GELU / SwiGLU epilogues (bf16 kernels): the side input of the projection that reads this
   // output, formed here (sf_n used factor columns, 0 = none).  Per row and group of the
-  // output columns one wave tile holds (64 for GELU, 32 for SwiGLU), the partial sums of the
-  // stored (rounded) outputs times the used V^T rows: column j of sf_n is row
+  // output columns two adjacent wave tiles hold (128 for GELU, 64 for SwiGLU), the partial
+  // sums of the stored (rounded) outputs times the used V^T rows: column j of sf_n is row
   // (j / sf_used) * sf_ks + j % sf_used of sf_vt (row pitch sf_ldv), written to
   // sf_part [M x sf_groups x sf_n] fp32; side_part_reduce sums each row's groups.
   int sf_n, sf_used, sf_ks, sf_groups;

@@ -420,19 +420,38 @@ __device__ __forceinline__ void side_partial4(const GemmParams& p, floatx4_t y, 
     }
 }
 
-// The four lanes holding one row's columns of the wave tile (lane, +16, +32, +48) combine
-// their partial sums; the first writes the row's group partials
-template <int NC>
-__device__ __forceinline__ void side_partial_store(const GemmParams& p, int r, int grp, int lane, float (&t)[NC]) {
+// The side input's partial sums of a workgroup tile, per row and unit of two adjacent wave
+// tiles (128 packed output columns): the four lanes holding one row's columns of a wave tile
+// (lane, +16, +32, +48) combine, the wave tiles meet in LDS (red: [BM][NWN][4]), and each
+// unit's two wave tiles are added in order; unit u of the N extent goes to group u.  The
+// units do not depend on the workgroup tile shape (both shapes are pairs of 64-column wave
+// tiles), so a row's partials do not depend on the batch.
+template <int TM, int BM, int BN, int WM, int WN>
+__device__ __forceinline__ void side_partials_wg(const GemmParams& p, float (&t)[TM][4], int m0, int n0, int wm,
+                                                 int wn, int lane, float* red) {
+  constexpr int NWN = BN / WN, NU = NWN / 2;
+  static_assert(NWN % 2 == 0 && WN == 64, "pairs of 64-column wave tiles");
 #pragma unroll
-  for (int c = 0; c < NC; ++c) {
-    t[c] += __shfl_xor(t[c], 16, 64);
-    t[c] += __shfl_xor(t[c], 32, 64);
-  }
-  if (lane < 16 && r < p.M) {
+  for (int i = 0; i < TM; ++i)
 #pragma unroll
-    for (int c = 0; c < NC; ++c)
-      if (c < p.sf_n) p.sf_part[((int64_t)r * p.sf_groups + grp) * p.sf_n + c] = t[c];
+    for (int c = 0; c < 4; ++c) {
+      t[i][c] += __shfl_xor(t[i][c], 16, 64);
+      t[i][c] += __shfl_xor(t[i][c], 32, 64);
+    }
+  __syncthreads();                                   // every wave is past its last LDS read of the stages
+  if (lane < 16)
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+      *(floatx4_t*)(red + ((wm * WM + i * 16 + lane) * NWN + wn) * 4) = floatx4_t{t[i][0], t[i][1], t[i][2], t[i][3]};
+  __syncthreads();
+  for (int it = threadIdx.x; it < BM * NU; it += blockDim.x) {
+    const int row = it / NU, u = it - row * NU, r = m0 + row;
+    if (r >= p.M || n0 + 2 * u * WN >= p.N) continue;
+    const float* a = red + (row * NWN + 2 * u) * 4;
+    const int unit = (n0 + 2 * u * WN) / (2 * WN);
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+      if (c < p.sf_n) p.sf_part[((int64_t)r * p.sf_groups + unit) * p.sf_n + c] = a[c] + a[4 + c];
   }
 }
 
@@ -548,7 +567,6 @@ __device__ __forceinline__ void epilogue_rows(const GemmParams& p, floatx4_t (&a
   } else if constexpr (EPI == EPI_SWIGLU) {
     // packed rows: blocks of 16 gate rows then 16 up rows; output column = gate index
     const int ob = (n0 + wn * WN) / 2 + 4 * (lane >> 4);
-    const int grp = (n0 + wn * WN) / WN;              // 32 output columns a wave tile
     float t[TM][4];
 #pragma unroll
     for (int i = 0; i < TM; ++i) t[i][0] = t[i][1] = t[i][2] = t[i][3] = 0.f;
@@ -581,9 +599,7 @@ __device__ __forceinline__ void epilogue_rows(const GemmParams& p, floatx4_t (&a
         }
       }
     }
-    if (p.sf_n)
-#pragma unroll
-      for (int i = 0; i < TM; ++i) side_partial_store<4>(p, rb + i * 16, grp, lane, t[i]);   // every lane takes part
+    if (p.sf_n) side_partials_wg<TM, BM, BN, WM, WN>(p, t, m0, n0, wm, wn, lane, red);   // every thread takes part
     return;
   } else {
     // a lane's four columns are all inside N or all outside (N is a multiple of 16)
@@ -596,7 +612,6 @@ __device__ __forceinline__ void epilogue_rows(const GemmParams& p, floatx4_t (&a
       // the side input's V values of all the wave tile's columns are loaded once, before the
       // rows; rows outer, so that the stores of one row's 64 columns follow one another (with
       // the column blocks outer, the L2 wrote each output line back twice)
-      const int grp = (n0 + wn * WN) / WN;            // 64 output columns a wave tile
       float t[TM][4];
 #pragma unroll
       for (int i = 0; i < TM; ++i) t[i][0] = t[i][1] = t[i][2] = t[i][3] = 0.f;
@@ -643,9 +658,7 @@ __device__ __forceinline__ void epilogue_rows(const GemmParams& p, floatx4_t (&a
           }
         }
       }
-      if (p.sf_n)
-#pragma unroll
-        for (int i = 0; i < TM; ++i) side_partial_store<4>(p, rb + i * 16, grp, lane, t[i]);   // every lane takes part
+      if (p.sf_n) side_partials_wg<TM, BM, BN, WM, WN>(p, t, m0, n0, wm, wn, lane, red);   // every thread takes part
       return;
     }
 #pragma unroll

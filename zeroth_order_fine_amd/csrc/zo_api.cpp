@@ -702,7 +702,7 @@ void carve(const zo_model* m, const zo_plan_s& p, const Packing& pk, const SideG
   }
   {
     const int64_t n1 = is_opt(d) ? F : 2 * F;           // columns of the fc1 / gate-up projection
-    w.sf_part = side_in_ffn_epilogue(d, p, sg) ? b.take<float>(M * ((n1 + 63) / 64) * 4) : nullptr;
+    w.sf_part = side_in_ffn_epilogue(d, p, sg) ? b.take<float>(M * ((n1 + 127) / 128) * 4) : nullptr;
   }
   const int bn_head = gemm_cfg_bn(GEMM_CFG_HEAD, bf16_like(d));
   const int64_t n_vt = (d.vocab + bn_head - 1) / bn_head;
@@ -970,7 +970,7 @@ int forward(zo_model* m, const zo_plan_s& p, const Packing& pk, const SideGeom& 
       else gp.epi = EPI_SWIGLU;
       if (ffn_fused) {
         gp.sf_n = sg.nc * sg.r; gp.sf_used = sg.nc * sg.r; gp.sf_ks = sg.ks_c;
-        gp.sf_groups = (N1 + 63) / 64;
+        gp.sf_groups = (N1 + 127) / 128;                 // units of two 64-column wave tiles
         gp.sf_vt = w.vt[l * 4 + 3]; gp.sf_ldv = F;
         gp.sf_part = w.sf_part;
       }
