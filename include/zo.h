@@ -283,7 +283,7 @@ int zo_pack(const zo_plan_t* p, const zo_batch* b, int32_t* phys_seq, int32_t* p
  * handed between workgroups in K-slices; they expect the GPU to themselves.  Should a
  * handover wait give up (other kernels holding CUs for a long time) or cross XCDs, the
  * call fails with ZO_E_DEVICE and the model stops using them (call again); setting the
- * environment variable ZO_GEMM_STREAMK=0 keeps every projection data-parallel (same bits). */
+ * environment variable ZO_GEMM_SPLIT_TAIL=0 keeps every projection data-parallel (same bits). */
 int zo_score(zo_model* m, const zo_plan_t* p, const zo_bank* bank, const zo_batch* b, void* ws_dev,
              size_t ws_bytes, double* seq_logp_dev, float* tok_logp_dev, double* S_host, void* stream);
 

@@ -104,11 +104,11 @@ def test_full_size_against_oracle(name):
         # the o and fc2 / down projections run as split-tail launches at this batch (the last
         # rounds of 256x256 tiles in K-slices dealt over every CU); the slices continue the
         # same MFMA sequence, so the data-parallel launch gives the same bits
-        os.environ["ZO_GEMM_STREAMK"] = "0"
+        os.environ["ZO_GEMM_SPLIT_TAIL"] = "0"
         try:
             dp = zo.score(model, zo.Plan.from_workload(model, wl, t=1), bank, db, want_tokens=True)
         finally:
-            del os.environ["ZO_GEMM_STREAMK"]
+            del os.environ["ZO_GEMM_SPLIT_TAIL"]
         assert np.array_equal(dp["seq_logp"].cpu().numpy().view(np.uint64), seq.view(np.uint64))
         assert np.array_equal(dp["tok_logp"].cpu().numpy().view(np.uint32), tok.view(np.uint32))
         flush("%s: split-tail and data-parallel projections bitwise equal" % name)

@@ -1530,9 +1530,9 @@ int pipe_tile(const GemmParams& p) {
 
 // Split tail for a 256x256-tile projection: when the workspace provides for it, every CU can
 // hold a workgroup, there is at least one whole round of tiles, and the last round of the
-// data-parallel launch would leave more than 2 % of the CU time idle.  ZO_GEMM_STREAMK=0
+// data-parallel launch would leave more than 2 % of the CU time idle.  ZO_GEMM_SPLIT_TAIL=0
 // turns it off (the outputs are the same bits either way).
-bool use_streamk(const GemmParams& p) {
+bool use_split_tail(const GemmParams& p) {
   if (!p.sk_part || !p.sk_flag || !p.sk_err || p.sk_ncu < 8 || p.sk_ncu % 8 != 0 || p.sk_ncu > ZO_SK_MAX_WG)
     return false;
   if (p.a_e4m3 || p.b_e4m3 || p.ksplit > 1) return false;
@@ -1542,7 +1542,7 @@ bool use_streamk(const GemmParams& p) {
   // the slices' handovers pay for themselves on long K only (measured at OPT-13B batch 64:
   // fc2, 320 K-steps, 1590 -> 1487 us; o, 80 K-steps, 431 -> 476 us)
   if (p.K / 64 + p.ks_tile / 64 < 160) return false;
-  const char* env = getenv("ZO_GEMM_STREAMK");
+  const char* env = getenv("ZO_GEMM_SPLIT_TAIL");
   if (env && env[0] == '0') return false;
   const int64_t t = (int64_t)((p.M + 255) / 256) * ((p.N + 255) / 256), P = p.sk_ncu;
   if (t < P) return false;
@@ -1576,7 +1576,7 @@ hipError_t gemm_launch_bf16(const GemmParams& p, int cfg, hipStream_t s) {
     // (measured at OPT-13B batch 64: finishing the last partial round of 256x256 tiles in
     // 128x128 tiles of a second launch made the projections 6 % slower, not faster)
     if (pipe_tile(p) == 0) {
-      if (use_streamk(p)) {
+      if (use_split_tail(p)) {
         if (p.epi == EPI_STORE) return launch_bf16_pipe_sk<EPI_STORE>(p, s);
         return launch_bf16_pipe_sk<EPI_RESID>(p, s);
       }
