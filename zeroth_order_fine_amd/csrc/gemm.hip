@@ -1050,9 +1050,10 @@ gemm_bf16_pipe_kernel(GemmParams p) {
     };
     // The handover goes through the XCD's L2 (plain stores, loads that miss the L1: the buffer
     // was never read on this CU), which holds only if producer and consumer share an XCD.
-    // Workgroups b and b + 8 do under the round-robin dispatch; each workgroup records the
-    // XCD it runs on, and a consumer that finds its producer on another XCD reports it
-    // (sk_err = 2) instead of trusting the data.
+    // Workgroups whose indices agree modulo 8 do under the round-robin dispatch (a tile's
+    // slices stay within one such class); each workgroup records the XCD it runs on, and a
+    // consumer that finds its producer on another XCD reports it (sk_err = 2) instead of
+    // trusting the data.
     int32_t* const xcc_of = p.sk_flag + 2 * ZO_SK_MAX_WG;
     const int my_xcc = __builtin_amdgcn_s_getreg((20) | (0 << 6) | ((4 - 1) << 11));   // HW_REG_XCC_ID[3:0]
     if (first_thread()) __hip_atomic_store(xcc_of + blockIdx.x, my_xcc, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
